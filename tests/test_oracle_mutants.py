@@ -1,0 +1,160 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case below plants one mistake in a copy of the oracle's C source (a
+dropped term, a wrong sign, an index off by one, a transposed operand), builds
+it on the CPU, and checks that at least one pin rejects it; the unmodified
+source must pass every pin.  Nothing here touches the GPU path.
+"""
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "llref.c")
+
+# (name, original text, planted text)
+MUTANTS = [
+    ("level-0 dropped", "if (s == t) return 0;", "if (s == t) return 1;"),
+    ("bucket level off by one", "if (s >= end - size) return floor_log2(size) + 1;",
+     "if (s >= end - size) return floor_log2(size);"),
+    ("largest bucket peeled first", "int64_t size = end & (-end);",
+     "int64_t size = (int64_t)1 << floor_log2(end);"),
+    ("own gate decays own write", "double logw = 0.0; /* sum_{r=s+1}^{t} log a_r */",
+     "double logw = log_gate[ix_tok(&d, b, t, h)];"),
+    ("decay sign flipped", "double a = exp(log_a);", "double a = exp(-log_a);"),
+    ("read uses transposed state", "r += S[l * per_level + (size_t)i * dv + j] * (double)qt[i];",
+     "r += S[l * per_level + (size_t)j * dk + i] * (double)qt[i];"),
+    ("merge into wrong level", "double *dst = S + (size_t)(c + 1) * per_level;",
+     "double *dst = S + (size_t)(c > 0 ? c : 1) * per_level;"),
+    ("gdn beta dropped", "w[j] = bt * ((double)vt[j] - acc);", "w[j] = ((double)vt[j] - acc);"),
+    ("gdn u ignores decay", "double w = exp(logw) * dot_f(kt, ks, d->dk);", "double w = dot_f(kt, ks, d->dk);"),
+    ("state decayed one token too far", "double logw = 0.0; /* sum_{r=s+1}^{T-1} log a_r */",
+     "double logw = log_gate[ix_tok(&d, b, T - 1, h)];"),
+]
+
+
+def _inputs(T, L, gdn, seed=1):
+    rng = np.random.default_rng(seed)
+    B, H, dk, dv = 1, 2, 3, 5
+    q = rng.standard_normal((B, T, H, dk)).astype(np.float32)
+    k = rng.standard_normal((B, T, H, dk)).astype(np.float32)
+    if gdn:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    g = (-rng.uniform(0.001, 0.3, (B, T, H))).astype(np.float32)
+    lam = np.log1p(np.exp(rng.normal(0.54, 0.5, (B, T, H, L)))).astype(np.float32)
+    beta = (1 / (1 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32)
+    return q, k, v, g, lam, beta
+
+
+def _xor_level(t, s):
+    return (t ^ s).bit_length()
+
+
+def pin_failures(lib):
+    """Run a compact set of the pins against ``lib``; return the names that fail."""
+    fails = []
+
+    # hand-worked partition of [0,13) and the XOR characterisation
+    if list(oracle.levels_row(13, lib=lib)) != [4] * 8 + [3] * 4 + [1, 0]:
+        fails.append("partition")
+
+    T, L = 29, 6
+    for gdn in (False, True):
+        rule = oracle.RULE_GDN if gdn else oracle.RULE_MAMBA2
+        q, k, v, g, lam, beta = _inputs(T, L, gdn)
+        beta_arg = beta if gdn else None
+        # lambda == 1: textbook (gated) linear attention / gated delta rule
+        ones = np.ones_like(lam)
+        ref = np.zeros((1, T, 2, 5))
+        for h in range(2):
+            S = np.zeros((3, 5))
+            for t in range(T):
+                kt = k[0, t, h].astype(np.float64)
+                vt = v[0, t, h].astype(np.float64)
+                a = math.exp(float(g[0, t, h]))
+                if gdn:
+                    bt = float(beta[0, t, h])
+                    S = a * (np.eye(3) - bt * np.outer(kt, kt)) @ S + bt * np.outer(kt, vt)
+                else:
+                    S = a * S + np.outer(kt, vt)
+                ref[0, t, h] = S.T @ q[0, t, h].astype(np.float64)
+        for form in (oracle.fwd_direct, oracle.fwd_recurrent):
+            o = form(q, k, v, g, ones, beta_arg, rule=rule, lib=lib)
+            if not np.allclose(o, ref, rtol=1e-10, atol=1e-10):
+                fails.append(f"textbook-{form.__name__}-{rule}")
+        # two independent forms agree with random lambda
+        a = oracle.fwd_direct(q, k, v, g, lam, beta_arg, rule=rule, lib=lib)
+        b = oracle.fwd_recurrent(q, k, v, g, lam, beta_arg, rule=rule, lib=lib)
+        if not np.allclose(a, b, rtol=1e-10, atol=1e-10):
+            fails.append(f"direct-vs-recurrent-{rule}")
+        # decode from the empty state reproduces the prefill outputs
+        st = np.zeros((1, 2, L, 3, 5))
+        for t in range(T):
+            o = oracle.decode_step(st, t, q[:, t], k[:, t], v[:, t], g[:, t], lam[:, t],
+                                   beta[:, t] if gdn else None, rule=rule, lib=lib)
+            if not np.allclose(o, a[:, t], rtol=1e-10, atol=1e-10):
+                fails.append(f"decode-{rule}")
+                break
+
+    # one-hot lambda at each level against brute force over XOR buckets,
+    # and the exported state against bucket sums
+    q, k, v, g, lam, _ = _inputs(T, L, False)
+    cum = np.cumsum(g.astype(np.float64), axis=1)
+    for level in range(L):
+        lam1 = np.zeros_like(lam)
+        lam1[..., level] = 1.0
+        o = oracle.fwd_direct(q, k, v, g, lam1, lib=lib)
+        ref = np.zeros_like(o)
+        for h in range(2):
+            for t in range(T):
+                for s in range(t + 1):
+                    if _xor_level(t, s) == level:
+                        w = math.exp(cum[0, t, h] - cum[0, s, h]) * float(
+                            q[0, t, h].astype(np.float64) @ k[0, s, h].astype(np.float64))
+                        ref[0, t, h] += w * v[0, s, h].astype(np.float64)
+        if not np.allclose(o, ref, rtol=1e-10, atol=1e-10):
+            fails.append(f"one-hot-{level}")
+    st = oracle.state_direct(k, v, g, L, lib=lib)
+    ref = np.zeros_like(st)
+    for h in range(2):
+        for s in range(T):
+            ref[0, h, _xor_level(T, s)] += math.exp(cum[0, T - 1, h] - cum[0, s, h]) * np.outer(
+                k[0, s, h].astype(np.float64), v[0, s, h].astype(np.float64))
+    if not np.allclose(st, ref, rtol=1e-10, atol=1e-10):
+        fails.append("state")
+    return fails
+
+
+def _build_variant(tmp_path, name, text):
+    src = tmp_path / f"{name.replace(' ', '_')}.c"
+    src.write_text(text)
+    so = tmp_path / f"{name.replace(' ', '_')}.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", str(so), str(src), "-lm"],
+                   check=True)
+    return oracle.load(str(so))
+
+
+def test_unmodified_oracle_passes_every_pin(tmp_path):
+    with open(SRC) as f:
+        text = f.read()
+    assert pin_failures(_build_variant(tmp_path, "original", text)) == []
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new):
+    with open(SRC) as f:
+        text = f.read()
+    assert text.count(old) == 1, f"mutation site for {name!r} not found exactly once"
+    lib = _build_variant(tmp_path, name, text.replace(old, new))
+    try:
+        fails = pin_failures(lib)
+    except ValueError:
+        fails = ["raised"]
+    assert fails, f"no pin caught: {name}"

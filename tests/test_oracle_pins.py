@@ -1,0 +1,348 @@
+"""Pins for the CPU oracle: facts fixed by the pages and by the mathematics.
+
+Each test ties one part of the oracle to something other than the oracle
+itself -- a hand-worked partition from the "Log-Linear Attention" page
+(section 2.2), an independent characterisation of the Fenwick buckets, a
+textbook recurrence the method reduces to, a closed form, or brute force.
+Tiny shapes use dk != dv so that a transposed operand cannot pass.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from fenwick_tree_linear_amd import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bit_length(x):
+    return np.where(x > 0, np.floor(np.log2(np.maximum(x, 1))).astype(np.int64) + 1, 0)
+
+
+def xor_levels(t):
+    """lev(t,s) = bit_length(t XOR s): an independent characterisation of the
+    Fenwick bucket of s (the highest bit where s and t differ)."""
+    s = np.arange(t + 1, dtype=np.int64)
+    return bit_length(np.bitwise_xor(t, s))
+
+
+def tiny_inputs(B=2, T=37, H=2, dk=3, dv=5, L=None, seed=0, gdn=False, unit_norm_k=False):
+    rng = np.random.default_rng(seed)
+    L = L or (math.ceil(math.log2(T)) + 1)
+    q = rng.standard_normal((B, T, H, dk)).astype(np.float32)
+    k = rng.standard_normal((B, T, H, dk)).astype(np.float32)
+    if unit_norm_k:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    g = (-rng.uniform(0.001, 0.3, (B, T, H))).astype(np.float32)
+    lam = np.log1p(np.exp(rng.normal(0.54, 0.5, (B, T, H, L)))).astype(np.float32)
+    beta = (1 / (1 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32) if gdn else None
+    return q, k, v, g, lam, beta
+
+
+def rel_err(a, b):
+    return np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300)
+
+
+# ---------------------------------------------------------------- Fenwick map
+
+def test_levels_match_hand_worked_partitions():
+    with open(os.path.join(GOLDEN, "fenwick_partition.txt")) as f:
+        lines = [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+    assert len(lines) >= 10
+    for ln in lines:
+        head, _, rest = ln.partition(":")
+        t = int(head[2:])
+        expect = np.full(t + 1, -1, dtype=np.int64)
+        expect[t] = 0
+        for item in rest.split():
+            rng_, lev = item.split("@")
+            lo, hi = (int(x) for x in rng_.strip("[)").split(","))
+            expect[lo:hi] = int(lev)
+        assert (expect >= 0).all(), f"fixture for t={t} does not tile [0,t]"
+        np.testing.assert_array_equal(oracle.levels_row(t), expect, err_msg=f"t={t}")
+
+
+@pytest.mark.parametrize("t_hi", [2048])
+def test_levels_are_a_fenwick_partition(t_hi):
+    """Buckets are powers of two, disjoint, tile [0,t), one per set bit of t,
+    finer for recent tokens, and equal the XOR characterisation."""
+    for t in range(t_hi):
+        lev = oracle.levels_row(t).astype(np.int64)
+        assert lev[t] == 0
+        np.testing.assert_array_equal(lev, xor_levels(t))
+        if t == 0:
+            continue
+        prev = lev[:t]
+        assert (prev >= 1).all()
+        assert (np.diff(prev) <= 0).all(), "older tokens must not sit in finer buckets"
+        nonempty = 0
+        for l in range(1, int(prev.max()) + 1):
+            idx = np.nonzero(prev == l)[0]
+            if (t >> (l - 1)) & 1:
+                nonempty += 1
+                assert len(idx) == 2 ** (l - 1)
+                assert idx[-1] - idx[0] + 1 == len(idx)
+            else:
+                assert len(idx) == 0
+        assert nonempty == bin(t).count("1") <= int(math.log2(t)) + 1
+
+
+def test_levels_sampled_large_positions():
+    rng = np.random.default_rng(7)
+    for t in list(rng.integers(2 ** 12, 2 ** 16, 24)) + [2 ** 16 - 1, 2 ** 15, 33279]:
+        np.testing.assert_array_equal(oracle.levels_row(int(t)).astype(np.int64), xor_levels(int(t)))
+
+
+def test_levels_match_merge_rule_simulation():
+    """Replaying the decode merge rule on sets of tokens (merge levels 0..c,
+    c = ctz(t+1), into level c+1) yields the same buckets."""
+    buckets = {}
+    for t in range(600):
+        lev = oracle.levels_row(t)
+        for l, members in buckets.items():
+            assert sorted(members) == list(np.nonzero(lev[:t] == l)[0]), (t, l)
+        assert sum(len(m) for m in buckets.values()) == t
+        c = ((t + 1) & -(t + 1)).bit_length() - 1
+        merged = [t]
+        for l in range(1, c + 1):
+            merged += buckets.pop(l, [])
+        assert c + 1 not in buckets
+        buckets[c + 1] = merged
+
+
+# -------------------------------------------------- reductions of the method
+
+@pytest.mark.parametrize("T", [37, 64])
+def test_lambda_one_is_gated_linear_attention(T):
+    """lambda == 1 on every level: the levels re-assemble the single state of
+    gated linear attention (Mamba-2), S_t = a_t S_{t-1} + k_t v_t^T, o_t = S_t^T q_t."""
+    q, k, v, g, lam, _ = tiny_inputs(T=T)
+    lam[:] = 1.0
+    B, _, H, dk = q.shape
+    dv = v.shape[-1]
+    ref = np.zeros((B, T, H, dv))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dk, dv))
+            for t in range(T):
+                S = np.exp(float(g[b, t, h])) * S + np.outer(k[b, t, h].astype(np.float64), v[b, t, h])
+                ref[b, t, h] = S.T @ q[b, t, h]
+    assert rel_err(oracle.fwd_direct(q, k, v, g, lam), ref) < 1e-12
+    assert rel_err(oracle.fwd_recurrent(q, k, v, g, lam), ref) < 1e-12
+
+
+def test_no_decay_lambda_one_is_prefix_sum():
+    """log a == 0, lambda == 1: o_t = q_t^T sum_{s<=t} k_s v_s^T (closed form)."""
+    q, k, v, g, lam, _ = tiny_inputs(T=40)
+    g[:] = 0.0
+    lam[:] = 1.0
+    B, T, H, _ = q.shape
+    ref = np.zeros((B, T, H, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            S = np.cumsum(np.einsum("ta,tc->tac", k[b, :, h].astype(np.float64), v[b, :, h].astype(np.float64)),
+                          axis=0)
+            ref[b, :, h] = np.einsum("ta,tac->tc", q[b, :, h].astype(np.float64), S)
+    assert rel_err(oracle.fwd_direct(q, k, v, g, lam), ref) < 1e-12
+
+
+def test_first_token_closed_form():
+    """t = 0: only the token itself, o_0 = lambda_0^(0) (q_0 . k_0) v_0."""
+    q, k, v, g, lam, _ = tiny_inputs(T=8)
+    o = oracle.fwd_direct(q, k, v, g, lam)
+    ref = lam[:, 0, :, 0, None] * np.einsum("bha,bha->bh", q[:, 0], k[:, 0])[..., None] * v[:, 0]
+    np.testing.assert_allclose(o[:, 0], ref, rtol=1e-6, atol=1e-12)
+
+
+@pytest.mark.parametrize("level", range(0, 6))
+def test_one_hot_lambda_reads_one_bucket(level):
+    """lambda one-hot at level l: only the bucket of level l (brute force over
+    the XOR characterisation of the buckets) contributes."""
+    T = 40
+    q, k, v, g, lam, _ = tiny_inputs(T=T, L=7)
+    lam[:] = 0.0
+    lam[..., level] = 1.0
+    B, _, H, _ = q.shape
+    ref = np.zeros((B, T, H, v.shape[-1]))
+    cum = np.cumsum(g.astype(np.float64), axis=1)
+    for b in range(B):
+        for h in range(H):
+            for t in range(T):
+                for s in range(t + 1):
+                    if (t ^ s).bit_length() != level:
+                        continue
+                    w = math.exp(cum[b, t, h] - cum[b, s, h]) * float(q[b, t, h] @ k[b, s, h].astype(np.float64))
+                    ref[b, t, h] += w * v[b, s, h].astype(np.float64)
+    o = oracle.fwd_direct(q, k, v, g, lam)
+    assert np.max(np.abs(o - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_masked_matrix_form():
+    """Parallel (training) form of section 2.3: O = (Q K^T * M_H * D) V with
+    M_H[t,s] = lambda_t^(bit_length(t^s)), D[t,s] = exp(cum_t - cum_s) for s <= t."""
+    q, k, v, g, lam, _ = tiny_inputs(T=50, B=1, H=3)
+    B, T, H, _ = q.shape
+    o = oracle.fwd_direct(q, k, v, g, lam)
+    tt, ss = np.meshgrid(np.arange(T), np.arange(T), indexing="ij")
+    lev = bit_length(np.bitwise_xor(tt, ss))
+    for h in range(H):
+        cum = np.cumsum(g[0, :, h].astype(np.float64))
+        D = np.where(ss <= tt, np.exp(cum[:, None] - cum[None, :]), 0.0)
+        MH = np.take_along_axis(lam[0, :, h].astype(np.float64), lev, axis=1)
+        Q, K, V = (x[0, :, h].astype(np.float64) for x in (q, k, v))
+        ref = ((Q @ K.T) * MH * D) @ V
+        assert rel_err(o[0, :, h], ref) < 1e-12
+
+
+@pytest.mark.parametrize("rule", [oracle.RULE_MAMBA2, oracle.RULE_GDN])
+@pytest.mark.parametrize("T,L", [(37, 7), (64, 7), (64, 9), (1, 2)])
+def test_direct_equals_recurrent(rule, T, L):
+    """Two independent algorithms: the O(T^2) masked sum with the lowbit level
+    map, and the O(T log T) recurrence that only knows the merge rule."""
+    gdn = rule == oracle.RULE_GDN
+    q, k, v, g, lam, beta = tiny_inputs(T=T, L=L, gdn=gdn, unit_norm_k=gdn)
+    a = oracle.fwd_direct(q, k, v, g, lam, beta, rule=rule)
+    b = oracle.fwd_recurrent(q, k, v, g, lam, beta, rule=rule)
+    assert rel_err(b, a) < 1e-12
+
+
+# --------------------------------------------------------- Gated DeltaNet pins
+
+def test_gdn_lambda_one_is_gated_delta_rule():
+    """lambda == 1: the textbook gated delta rule
+    S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T, o_t = S_t^T q_t."""
+    q, k, v, g, lam, beta = tiny_inputs(T=33, gdn=True, unit_norm_k=True)
+    lam[:] = 1.0
+    B, T, H, dk = q.shape
+    ref = np.zeros((B, T, H, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dk, v.shape[-1]))
+            for t in range(T):
+                kt = k[b, t, h].astype(np.float64)
+                bt = float(beta[b, t, h])
+                S = math.exp(float(g[b, t, h])) * (np.eye(dk) - bt * np.outer(kt, kt)) @ S + bt * np.outer(
+                    kt, v[b, t, h])
+                ref[b, t, h] = S.T @ q[b, t, h]
+    assert rel_err(oracle.fwd_direct(q, k, v, g, lam, beta, rule=oracle.RULE_GDN), ref) < 1e-12
+    assert rel_err(oracle.fwd_recurrent(q, k, v, g, lam, beta, rule=oracle.RULE_GDN), ref) < 1e-12
+
+
+def test_gdn_zero_beta_writes_nothing():
+    q, k, v, g, lam, beta = tiny_inputs(T=20, gdn=True)
+    beta[:] = 0.0
+    assert np.max(np.abs(oracle.fwd_direct(q, k, v, g, lam, beta, rule=oracle.RULE_GDN))) == 0.0
+
+
+def test_gdn_one_hot_keys_keep_last_value():
+    """a == 1, beta == 1, keys drawn from a one-hot basis: the delta rule
+    overwrites the slot of each key, so with lambda == 1 and q = e_j the output
+    is the last value written under key j."""
+    T, dk, dv = 24, 4, 3
+    rng = np.random.default_rng(3)
+    keys = rng.integers(0, dk, T)
+    k = np.eye(dk, dtype=np.float32)[keys][None, :, None, :]
+    v = rng.standard_normal((1, T, 1, dv)).astype(np.float32)
+    g = np.zeros((1, T, 1), np.float32)
+    beta = np.ones((1, T, 1), np.float32)
+    lam = np.ones((1, T, 1, 6), np.float32)
+    for j in range(dk):
+        q = np.zeros((1, T, 1, dk), np.float32)
+        q[..., j] = 1.0
+        o = oracle.fwd_direct(q, k, v, g, lam, beta, rule=oracle.RULE_GDN)
+        for t in range(T):
+            last = [s for s in range(t + 1) if keys[s] == j]
+            ref = v[0, last[-1], 0] if last else np.zeros(dv)
+            np.testing.assert_allclose(o[0, t, 0], ref, atol=1e-12)
+
+
+# ------------------------------------------------------------ states, decode
+
+def bucket_state_bruteforce(k, v, g, T, L, b, h):
+    cum = np.cumsum(g[b, :T, h].astype(np.float64))
+    st = np.zeros((L, k.shape[-1], v.shape[-1]))
+    for s in range(T):
+        lev = (T ^ s).bit_length()
+        st[lev] += math.exp(cum[T - 1] - cum[s]) * np.outer(k[b, s, h].astype(np.float64), v[b, s, h])
+    return st
+
+
+@pytest.mark.parametrize("T", [1, 13, 32, 45])
+def test_state_export_is_bucket_sum(T):
+    q, k, v, g, lam, _ = tiny_inputs(T=T, L=7)
+    st_direct = oracle.state_direct(k, v, g, 7)
+    _, st_rec = oracle.fwd_recurrent(q, k, v, g, lam, want_state=True)
+    for b in range(2):
+        for h in range(2):
+            ref = bucket_state_bruteforce(k, v, g, T, 7, b, h)
+            assert np.max(np.abs(st_direct[b, h] - ref)) < 1e-12 * max(1, np.abs(ref).max())
+    assert rel_err(st_rec, st_direct) < 1e-12
+    # empty levels are exactly zero, non-empty ones are the set bits of T
+    for l in range(7):
+        nonempty = l >= 1 and (T >> (l - 1)) & 1
+        assert (np.abs(st_direct[:, :, l]).max() > 0) == bool(nonempty)
+
+
+@pytest.mark.parametrize("rule", [oracle.RULE_MAMBA2, oracle.RULE_GDN])
+def test_decode_from_empty_state_equals_prefill(rule):
+    gdn = rule == oracle.RULE_GDN
+    T, L = 45, 7
+    q, k, v, g, lam, beta = tiny_inputs(T=T, L=L, gdn=gdn, unit_norm_k=gdn)
+    o_ref = oracle.fwd_direct(q, k, v, g, lam, beta, rule=rule)
+    st = np.zeros((2, 2, L, 3, 5))
+    for t in range(T):
+        o = oracle.decode_step(st, t, q[:, t], k[:, t], v[:, t], g[:, t], lam[:, t],
+                               None if beta is None else beta[:, t], rule=rule)
+        assert rel_err(o, o_ref[:, t]) < 1e-12
+    st_ref = oracle.state_direct(k, v, g, L, beta, rule=rule)
+    assert rel_err(st, st_ref) < 1e-12
+
+
+def test_decode_resumes_from_exported_state():
+    T0, T1, L = 32, 50, 7
+    q, k, v, g, lam, _ = tiny_inputs(T=T1, L=L)
+    o_ref = oracle.fwd_direct(q, k, v, g, lam)
+    st = oracle.state_direct(k[:, :T0], v[:, :T0], g[:, :T0], L)
+    for t in range(T0, T1):
+        o = oracle.decode_step(st, t, q[:, t], k[:, t], v[:, t], g[:, t], lam[:, t])
+        assert rel_err(o, o_ref[:, t]) < 1e-12
+
+
+def test_level_count_limits_are_enforced():
+    q, k, v, g, lam, _ = tiny_inputs(T=65, L=7)  # position 64 needs level 7
+    with pytest.raises(ValueError):
+        oracle.fwd_direct(q, k, v, g, lam)
+    with pytest.raises(ValueError):
+        oracle.state_direct(k[:, :64], v[:, :64], g[:, :64], 7)  # [0,64) needs level 7
+    st = np.zeros((2, 2, 7, 3, 5))
+    with pytest.raises(ValueError):
+        oracle.decode_step(st, 63, q[:, 0], k[:, 0], v[:, 0], g[:, 0], lam[:, 0])
+
+
+# --------------------------------------------------------------- generators
+
+def test_softplus_initial_bias_is_near_one():
+    """The adaptive-decay page initialises the lambda bias to 0.54 so that
+    softplus starts near 1.0: softplus(0.54) = 0.99916."""
+    assert abs(workloads.softplus(0.54) - 0.9991627) < 1e-6
+
+
+def test_workload_generators_are_seeded_and_shaped():
+    w = workloads.with_shape(workloads.WORKLOADS["prefill-2k"], B=1, H=2, T=128)
+    a = workloads.prefill_inputs(w)
+    b = workloads.prefill_inputs(w)
+    for name in ("q", "k", "v", "log_gate", "lam"):
+        assert (a[name].float() == b[name].float()).all()
+    assert a["q"].dtype.is_floating_point and a["q"].dtype != a["log_gate"].dtype
+    assert a["lam"].shape == (1, 128, 2, w.L)
+    g = a["log_gate"]
+    assert float(g.max()) <= -0.001 and float(g.min()) >= -0.1
+    assert float(a["lam"].min()) > 0
+    for key, L in (("tiny", 9), ("prefill-2k", 12), ("prefill-16k", 15), ("gdn-8k", 14)):
+        w = workloads.WORKLOADS[key]
+        assert w.L == L == workloads.levels_for(w.T)
