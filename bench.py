@@ -1,0 +1,167 @@
+"""Prefill throughput of log-linear Mamba-2 attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = one ll_attn_fwd over the 16K-token workload (B=2, H=16, T=16384,
+dk=dv=64, bf16 q/k/v/o, fp32 gates and lambda, 15 levels, chunk 64): the whole
+hot path (ll_chunk_state, ll_fenwick_scan, ll_chunk_attn) on inputs already
+resident in HBM.  Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes_per_token_head(w) -> int:
+    """Compulsory HBM traffic of one token-head: read q, k, v, lambda, the
+    log-gate, write o."""
+    esz = 2 if w.io == "bf16" else 4
+    return (2 * w.dk + 2 * w.dv) * esz + 4 * w.L + 4
+
+
+def useful_flops_per_token_head(w) -> float:
+    """Matrix-core work the chunked form must do per token-head: the chunk's
+    own key-value state (2 dk dv), the causal half of the in-chunk scores and
+    their product with V (~ (C+1)(dk+dv)), and one q^T S read per non-empty
+    chunk-or-coarser level (2 dk dv each; on average half of the log2(T/C)
+    chunk levels are non-empty)."""
+    import math
+
+    chunk_levels = math.log2(w.T // w.C)
+    return 2 * w.dk * w.dv + (w.C + 1) * (w.dk + w.dv) + 2 * w.dk * w.dv * chunk_levels / 2
+
+
+def cpu_baseline(w) -> dict:
+    """The oracle's recurrent form on batch 0 of the workload (all heads, all
+    tokens), timed on the host cores."""
+    import oracle
+    from fenwick_tree_linear_amd import workloads as W
+
+    sw = W.with_shape(w, B=1)
+    x = W.prefill_inputs(sw)
+    np_in = {k: (None if v is None else v.float().numpy()) for k, v in x.items()}
+    lib = oracle.load()
+    t0 = time.perf_counter()
+    oracle.fwd_recurrent(np_in["q"], np_in["k"], np_in["v"], np_in["log_gate"], np_in["lam"], lib=lib)
+    dt = time.perf_counter() - t0
+    cores = min(oracle.threads(lib), sw.B * sw.H)
+    return {"value": sw.T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"recurrent O(T log T) form, batch 0 of {w.B} (all {w.H} heads x {w.T} tokens), fp64, "
+                      f"{dt:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (each (batch, head) pair is "
+              "independent, so more GPUs would shard the heads with no communication)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import fenwick_tree_linear_amd as F
+    from fenwick_tree_linear_amd import workloads as W
+
+    w = W.WORKLOADS["prefill-16k"]
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {w.name}: generating inputs on the GPU")
+    x = W.prefill_inputs(w, device=dev)
+    prob = F.LLProblem(w.B, w.T, w.H, w.dk, w.dv, w.L, w.C, F.LL_BF16, F.LL_MAMBA2)
+    ws_bytes = F.ll_attn_fwd_workspace_bytes(prob)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    o = torch.empty(w.B, w.T, w.H, w.dv, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        F.ll_attn_fwd(prob, x["q"], x["k"], x["v"], x["log_gate"], x["lam"], None, o, None, ws, ws_bytes, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    start_ev = torch.cuda.Event(enable_timing=True)
+    stop_ev = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start_ev.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop_ev.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start_ev.elapsed_time(stop_ev) / args.steps
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (events), wall {wall * 1e3 / args.steps:.1f} us")
+
+    # per-kernel durations: HIP events around every launch, on the launch stream
+    F.ll_kernel_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = F.ll_kernel_timing_read()
+    F.ll_kernel_timing_enable(False)
+    kernels = {name: round(ms / n * 1e3, 2) for name, (ms, n) in kt.items()}
+    log(f"[bench] per-kernel average us: {kernels}")
+
+    token_heads = w.B * w.T * w.H
+    alg_bytes = algorithmic_bytes_per_token_head(w) * token_heads
+    t_attn = kt["ll_chunk_attn"][0] / kt["ll_chunk_attn"][1] * 1e-3
+    achieved = alg_bytes / t_attn / 1e9
+    flops = useful_flops_per_token_head(w) * token_heads
+    tokens_per_s = w.B * w.T / (ms_per_step * 1e-3)
+
+    result = {
+        "metric": "prefill tokens/s (log-linear Mamba-2, T=16K) + % of MFMA/HBM peak",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "log-linear Mamba-2 prefill B2 H16 T16384 dk=dv=64 bf16, 15 levels, chunk 64",
+                   "global_batch": w.B, "seq_len": w.T, "heads": w.H, "head_dim": w.dk, "levels": w.L,
+                   "chunk": w.C},
+        "roofline": {"bound": "hbm", "kernel": "ll_chunk_attn", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": alg_bytes},
+        "mfma": {"useful_gflop": round(flops / 1e9, 2),
+                 "achieved_tflops_step": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+                 "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                 "frac_step": round(flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "kernels_us": kernels,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host cores")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,176 @@
+"""ctypes binding of libllattn.so: argument marshalling only.
+
+Every function named ``ll_*`` mirrors the C entry point of the same name in
+``include/ll_attn.h``; tensors are passed as device pointers and the current
+torch stream is passed as the hipStream.  Non-OK statuses raise ``LLError``
+carrying ``ll_last_error()``.  The library is loaded on first use and its
+absence is an error, never a fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LL_F32, LL_BF16 = 0, 1
+LL_MAMBA2, LL_GATED_DELTANET = 0, 1
+
+_STATUS = {0: "LL_OK", -1: "LL_ERR_NULL", -2: "LL_ERR_SHAPE", -3: "LL_ERR_DTYPE", -4: "LL_ERR_UNSUPPORTED",
+           -5: "LL_ERR_WORKSPACE", -6: "LL_ERR_POSITION", -7: "LL_ERR_HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.environ.get("LLATTN_LIB", os.path.join(_HERE, "libllattn.so"))
+
+
+class LLError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.name = _STATUS.get(status, str(status))
+        super().__init__(f"{self.name}: {message}")
+
+
+class LLProblem(ctypes.Structure):
+    """``ll_problem``: B, T, H, dk, dv, L, C, io, rule."""
+
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("dk", ctypes.c_int),
+                ("dv", ctypes.c_int), ("L", ctypes.c_int), ("C", ctypes.c_int), ("io", ctypes.c_int),
+                ("rule", ctypes.c_int)]
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libllattn.so (built by ``python -m fenwick_tree_linear_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m fenwick_tree_linear_amd.build` "
+                          "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    P, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int64
+    lib.ll_attn_fwd_workspace_bytes.argtypes = [ctypes.POINTER(LLProblem), ctypes.POINTER(sz)]
+    lib.ll_attn_fwd.argtypes = [ctypes.POINTER(LLProblem), P, P, P, P, P, P, P, P, P, sz, P]
+    lib.ll_decode_state_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.ll_decode_step.argtypes = [i32, i32, i32, i32, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P]
+    lib.ll_last_error.argtypes = []
+    lib.ll_last_error.restype = ctypes.c_char_p
+    lib.ll_kernel_timing_enable.argtypes = [i32]
+    lib.ll_kernel_timing_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(ctypes.c_int), i32, ctypes.POINTER(ctypes.c_int)]
+    for fn in ("ll_attn_fwd_workspace_bytes", "ll_attn_fwd", "ll_decode_state_bytes", "ll_decode_step",
+               "ll_kernel_timing_enable", "ll_kernel_timing_read"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def ll_last_error() -> str:
+    return load_library().ll_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise LLError(status, ll_last_error())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libllattn must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def ll_attn_fwd_workspace_bytes(problem: LLProblem) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().ll_attn_fwd_workspace_bytes(ctypes.byref(problem), ctypes.byref(out)))
+    return out.value
+
+
+def ll_attn_fwd(problem: LLProblem, q, k, v, log_gate, lam, beta, o, state_out, workspace, workspace_bytes: int,
+                stream=None) -> None:
+    _check(load_library().ll_attn_fwd(None if problem is None else ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate), _ptr(lam),
+                                      _ptr(beta), _ptr(o), _ptr(state_out), _ptr(workspace), workspace_bytes,
+                                      _stream(stream)))
+
+
+def ll_decode_state_bytes(B: int, H: int, dk: int, dv: int, L: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().ll_decode_state_bytes(B, H, dk, dv, L, ctypes.byref(out)))
+    return out.value
+
+
+def ll_decode_step(B, H, dk, dv, L, io, rule, pos, q, k, v, log_gate, lam, beta, o, state, stream=None) -> None:
+    _check(load_library().ll_decode_step(B, H, dk, dv, L, io, rule, pos, _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
+                                         _ptr(lam), _ptr(beta), _ptr(o), _ptr(state), _stream(stream)))
+
+
+def ll_kernel_timing_enable(on: bool) -> None:
+    _check(load_library().ll_kernel_timing_enable(1 if on else 0))
+
+
+def ll_kernel_timing_read() -> dict:
+    """{kernel name: (total ms, launches)} since the last read."""
+    cap = 16
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_double * cap)()
+    n_launch = (ctypes.c_int * cap)()
+    count = ctypes.c_int(0)
+    _check(load_library().ll_kernel_timing_read(names, ms, n_launch, cap, ctypes.byref(count)))
+    return {names[i].decode(): (ms[i], n_launch[i]) for i in range(min(count.value, cap))}
+
+
+# ---------------------------------------------------------------- helpers
+
+def io_code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return LL_F32
+    if dtype == torch.bfloat16:
+        return LL_BF16
+    raise TypeError(f"io dtype must be float32 or bfloat16, got {dtype}")
+
+
+def decode_state_tensor(B: int, H: int, dk: int, dv: int, L: int, device="cuda") -> torch.Tensor:
+    """A zeroed decode state (the empty prefix) as a flat fp32 tensor."""
+    n = ll_decode_state_bytes(B, H, dk, dv, L) // 4
+    return torch.zeros(n, dtype=torch.float32, device=device)
+
+
+def attn_fwd(q, k, v, log_gate, lam, beta=None, C: int = 64, rule: int = LL_MAMBA2, L: int | None = None,
+             want_output: bool = True, want_state: bool = False, workspace=None, out=None, stream=None):
+    """Allocate outputs and workspace with torch, then call ``ll_attn_fwd``.
+
+    Returns ``o`` (or None), and the exported state (flat fp32) when
+    ``want_state``.
+    """
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    L = L if L is not None else lam.shape[-1]
+    prob = LLProblem(B, T, H, dk, dv, L, C, io_code(k.dtype), rule)
+    nbytes = ll_attn_fwd_workspace_bytes(prob)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
+    o = None
+    if want_output:
+        o = out if out is not None else torch.empty(B, T, H, dv, dtype=v.dtype, device=v.device)
+    st = None
+    if want_state:
+        st = torch.empty(ll_decode_state_bytes(B, H, dk, dv, L) // 4, dtype=torch.float32, device=k.device)
+    ll_attn_fwd(prob, q, k, v, log_gate, lam, beta, o, st, workspace, workspace.numel(), stream)
+    return (o, st) if want_state else o

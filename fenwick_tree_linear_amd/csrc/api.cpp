@@ -1,0 +1,313 @@
+// api.cpp -- the C ABI of libllattn (declared in include/ll_attn.h):
+// argument validation, workspace planning and the launch sequence.  Every
+// check runs before the first HIP call, so a rejected call enqueues nothing.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <mutex>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/ll_attn.h"
+#include "ll_launch.hpp"
+
+using llattn::DecodeArgs;
+using llattn::PrefillArgs;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ll_status fail(ll_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ll_status ok() {
+  g_err[0] = '\0';
+  return LL_OK;
+}
+
+int bit_length(int64_t x) {
+  int n = 0;
+  while (x > 0) {
+    x >>= 1;
+    ++n;
+  }
+  return n;
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// bf16 matrix-core steps contract 32 values: bf16 needs d >= 32 and C >= 32
+bool supported_head(int d, ll_dtype io) {
+  if (io == LL_BF16) return d == 32 || d == 64 || d == 128;
+  return d == 16 || d == 32 || d == 64;
+}
+
+bool supported_chunk(int c, ll_dtype io) {
+  if (io == LL_BF16) return c == 32 || c == 64;
+  return c == 16 || c == 32 || c == 64;
+}
+
+constexpr int kMaxBlockChunks = 8;  // P <= 2^max_block_depth for d <= 64
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+  int P, nb, nF, LS;
+  size_t s_off, gs_off, f_off, gf_off, bytes;
+};
+
+// Validates a prefill problem and derives the block decomposition.
+ll_status plan_prefill(const ll_problem* p, bool exporting, Plan* out) {
+  if (!p) return fail(LL_ERR_NULL, "problem is NULL");
+  if (p->io != LL_F32 && p->io != LL_BF16) return fail(LL_ERR_DTYPE, "unknown io dtype %d", (int)p->io);
+  if (p->rule != LL_MAMBA2 && p->rule != LL_GATED_DELTANET)
+    return fail(LL_ERR_UNSUPPORTED, "unknown rule %d", (int)p->rule);
+  if (p->B < 1 || p->T < 1 || p->H < 1 || p->dk < 1 || p->dv < 1 || p->L < 1 || p->C < 1)
+    return fail(LL_ERR_SHAPE, "sizes must be positive (B=%d T=%d H=%d dk=%d dv=%d L=%d C=%d)", p->B, p->T, p->H,
+                p->dk, p->dv, p->L, p->C);
+  if (!is_pow2(p->C)) return fail(LL_ERR_SHAPE, "chunk size C=%d is not a power of two", p->C);
+  if (p->T % p->C != 0) return fail(LL_ERR_SHAPE, "T=%d is not a multiple of C=%d", p->T, p->C);
+  if (p->L > 62) return fail(LL_ERR_SHAPE, "L=%d levels is more than positions can use", p->L);
+  // outputs of positions t < T need levels up to bit_length(T-1)
+  const int need = bit_length((int64_t)p->T - 1) + 1;
+  if (p->L < need) return fail(LL_ERR_SHAPE, "T=%d needs at least %d levels, got L=%d", p->T, need, p->L);
+  if (exporting && bit_length(p->T) > p->L - 1)
+    return fail(LL_ERR_SHAPE, "exporting the state of [0,%d) needs at least %d levels, got L=%d", p->T,
+                bit_length(p->T) + 1, p->L);
+  if (p->rule != LL_MAMBA2)
+    return fail(LL_ERR_UNSUPPORTED, "the Gated DeltaNet write is not implemented in prefill");
+  if (p->dk != p->dv) return fail(LL_ERR_UNSUPPORTED, "dk=%d != dv=%d is not supported", p->dk, p->dv);
+  if (!supported_head(p->dk, p->io))
+    return fail(LL_ERR_UNSUPPORTED, "head size %d not supported for %s io", p->dk, p->io == LL_BF16 ? "bf16" : "fp32");
+  if (!supported_chunk(p->C, p->io))
+    return fail(LL_ERR_UNSUPPORTED, "chunk size C=%d not supported for %s io", p->C, p->io == LL_BF16 ? "bf16" : "fp32");
+  if (need > llattn::kLevelsMax)
+    return fail(LL_ERR_UNSUPPORTED, "T=%d needs %d levels; at most %d are supported", p->T, need, llattn::kLevelsMax);
+  if ((int64_t)p->B * p->H * (p->T / p->C) > ((int64_t)1 << 31) - 1)
+    return fail(LL_ERR_UNSUPPORTED, "problem too large for one launch");
+
+  const int nc = p->T / p->C;
+  const int depth_cap = 1 << llattn::max_block_depth(p->dk);
+  int P = nc & -nc;  // lowest set bit: blocks tile the chunks exactly
+  if (P > kMaxBlockChunks) P = kMaxBlockChunks;
+  if (P > depth_cap) P = depth_cap;
+  Plan pl;
+  pl.P = P;
+  pl.nb = nc / P;
+  pl.nF = pl.nb / 2;
+  pl.LS = p->L < need ? p->L : need;
+  const size_t bh = (size_t)p->B * p->H;
+  const size_t dd = (size_t)p->dk * p->dv;
+  size_t off = 0;
+  pl.s_off = off;
+  off = align256(off + bh * pl.nb * dd * sizeof(float));
+  pl.gs_off = off;
+  off = align256(off + bh * pl.nb * sizeof(float));
+  pl.f_off = off;
+  off = align256(off + bh * pl.nF * dd * sizeof(float));
+  pl.gf_off = off;
+  off = align256(off + bh * (pl.nF > 0 ? pl.nF : 1) * sizeof(float));
+  pl.bytes = off;
+  *out = pl;
+  return LL_OK;
+}
+
+// ---------------------------------------------------------- kernel timing
+enum KernelId { K_CHUNK_STATE, K_FENWICK_SCAN, K_CHUNK_ATTN, K_STATE_EXPORT, K_DECODE_STEP, K_COUNT };
+const char* const kKernelNames[K_COUNT] = {"ll_chunk_state", "ll_fenwick_scan", "ll_chunk_attn", "ll_state_export",
+                                           "ll_decode_step"};
+
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;  // free events
+  struct Pending {
+    int kernel;
+    hipEvent_t start, stop;
+  };
+  std::vector<Pending> pending;
+  double total_ms[K_COUNT] = {};
+  int launches[K_COUNT] = {};
+};
+Timing g_timing;
+
+hipEvent_t take_event() {
+  if (!g_timing.pool.empty()) {
+    hipEvent_t e = g_timing.pool.back();
+    g_timing.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launches one kernel through `fn`, bracketed by events when timing is on.
+template <typename Fn>
+hipError_t timed(int kernel, hipStream_t stream, Fn fn) {
+  std::unique_lock<std::mutex> lock(g_timing.mu, std::defer_lock);
+  if (g_timing.on) lock.lock();
+  if (!g_timing.on) return fn();
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) return fn();
+  hipEventRecord(a, stream);
+  hipError_t e = fn();
+  hipEventRecord(b, stream);
+  g_timing.pending.push_back({kernel, a, b});
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+ll_status ll_kernel_timing_enable(int on) {
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  g_timing.on = on != 0;
+  return ok();
+}
+
+ll_status ll_kernel_timing_read(const char** names, double* total_ms, int* launches, int capacity, int* count) {
+  if (!count || (capacity > 0 && (!names || !total_ms || !launches)))
+    return fail(LL_ERR_NULL, "output arrays must not be NULL");
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  for (auto& p : g_timing.pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.stop) != hipSuccess || hipEventElapsedTime(&ms, p.start, p.stop) != hipSuccess)
+      return fail(LL_ERR_HIP, "reading kernel timing events failed");
+    g_timing.total_ms[p.kernel] += ms;
+    g_timing.launches[p.kernel] += 1;
+    g_timing.pool.push_back(p.start);
+    g_timing.pool.push_back(p.stop);
+  }
+  g_timing.pending.clear();
+  int n = 0;
+  for (int kk = 0; kk < K_COUNT; ++kk) {
+    if (g_timing.launches[kk] == 0) continue;
+    if (n < capacity) {
+      names[n] = kKernelNames[kk];
+      total_ms[n] = g_timing.total_ms[kk];
+      launches[n] = g_timing.launches[kk];
+    }
+    ++n;
+    g_timing.total_ms[kk] = 0.0;
+    g_timing.launches[kk] = 0;
+  }
+  *count = n;
+  return ok();
+}
+
+const char* ll_last_error(void) { return g_err; }
+
+ll_status ll_attn_fwd_workspace_bytes(const ll_problem* p, size_t* bytes) {
+  if (!bytes) return fail(LL_ERR_NULL, "bytes is NULL");
+  Plan pl;
+  // plan as if exporting is not requested; the workspace does not depend on it
+  ll_status st = plan_prefill(p, false, &pl);
+  if (st != LL_OK) return st;
+  *bytes = pl.bytes;
+  return ok();
+}
+
+ll_status ll_attn_fwd(const ll_problem* p, const void* q, const void* k, const void* v, const float* log_gate,
+                      const float* lambda, const float* beta, void* o, void* state_out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  Plan pl;
+  ll_status st = plan_prefill(p, state_out != nullptr, &pl);
+  if (st != LL_OK) return st;
+  if (!k || !v || !log_gate) return fail(LL_ERR_NULL, "k, v and log_gate must not be NULL");
+  if (!o && !state_out) return fail(LL_ERR_NULL, "o and state_out are both NULL: nothing to compute");
+  if (o && (!q || !lambda)) return fail(LL_ERR_NULL, "q and lambda must not be NULL when o is requested");
+  if (p->rule == LL_GATED_DELTANET && !beta) return fail(LL_ERR_NULL, "beta must not be NULL for Gated DeltaNet");
+  if (workspace_bytes < pl.bytes)
+    return fail(LL_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, pl.bytes);
+  if (pl.bytes > 0 && !workspace) return fail(LL_ERR_WORKSPACE, "workspace is NULL");
+
+  char* ws = static_cast<char*>(workspace);
+  PrefillArgs a;
+  a.B = p->B;
+  a.T = p->T;
+  a.H = p->H;
+  a.L = p->L;
+  a.LS = pl.LS;
+  a.P = pl.P;
+  a.nb = pl.nb;
+  a.nF = pl.nF;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = log_gate;
+  a.lam = lambda;
+  a.o = o;
+  a.S = reinterpret_cast<float*>(ws + pl.s_off);
+  a.GS = reinterpret_cast<float*>(ws + pl.gs_off);
+  a.F = reinterpret_cast<float*>(ws + pl.f_off);
+  a.GF = reinterpret_cast<float*>(ws + pl.gf_off);
+  a.state = static_cast<float*>(state_out);
+  const int io = p->io == LL_BF16 ? 1 : 0;
+  const int D = p->dk;
+
+  const int C = p->C;
+  hipError_t e = timed(K_CHUNK_STATE, stream, [&] { return llattn::launch_block_state(io, D, C, a, stream); });
+  if (e == hipSuccess && a.nb > 1)
+    e = timed(K_FENWICK_SCAN, stream, [&] { return llattn::launch_fenwick_scan(D, a, stream); });
+  if (e == hipSuccess && o)
+    e = timed(K_CHUNK_ATTN, stream, [&] { return llattn::launch_chunk_attn(io, D, C, a, stream); });
+  if (e == hipSuccess && state_out)
+    e = timed(K_STATE_EXPORT, stream, [&] { return llattn::launch_state_export(D, C, a, stream); });
+  if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ll_status ll_decode_state_bytes(int B, int H, int dk, int dv, int L, size_t* bytes) {
+  if (!bytes) return fail(LL_ERR_NULL, "bytes is NULL");
+  if (B < 1 || H < 1 || dk < 1 || dv < 1 || L < 2)
+    return fail(LL_ERR_SHAPE, "sizes must be positive and L >= 2 (B=%d H=%d dk=%d dv=%d L=%d)", B, H, dk, dv, L);
+  *bytes = (size_t)B * H * L * ((size_t)dk * dv + 1) * sizeof(float);
+  return ok();
+}
+
+ll_status ll_decode_step(int B, int H, int dk, int dv, int L, ll_dtype io, ll_rule rule, int64_t pos, const void* q,
+                         const void* k, const void* v, const float* log_gate, const float* lambda, const float* beta,
+                         void* o, void* state, hipStream_t stream) {
+  if (io != LL_F32 && io != LL_BF16) return fail(LL_ERR_DTYPE, "unknown io dtype %d", (int)io);
+  if (rule != LL_MAMBA2 && rule != LL_GATED_DELTANET) return fail(LL_ERR_UNSUPPORTED, "unknown rule %d", (int)rule);
+  if (B < 1 || H < 1 || dk < 1 || dv < 1 || L < 2)
+    return fail(LL_ERR_SHAPE, "sizes must be positive and L >= 2 (B=%d H=%d dk=%d dv=%d L=%d)", B, H, dk, dv, L);
+  if (pos < 0) return fail(LL_ERR_POSITION, "pos=%lld is negative", (long long)pos);
+  if (L > 32) return fail(LL_ERR_UNSUPPORTED, "L=%d: at most 32 decode levels are supported", L);
+  if (pos + 1 >= ((int64_t)1 << (L - 1)))
+    return fail(LL_ERR_POSITION, "pos=%lld: the state of [0,pos+1) does not fit in L=%d levels", (long long)pos, L);
+  if (!q || !k || !v || !log_gate || !lambda || !o || !state)
+    return fail(LL_ERR_NULL, "q, k, v, log_gate, lambda, o and state must not be NULL");
+  if (rule != LL_MAMBA2) return fail(LL_ERR_UNSUPPORTED, "the Gated DeltaNet decode step is not implemented");
+  if (dk != dv) return fail(LL_ERR_UNSUPPORTED, "dk=%d != dv=%d is not supported", dk, dv);
+  if (dk != 16 && dk != 32 && dk != 64 && dk != 128) return fail(LL_ERR_UNSUPPORTED, "head size %d not supported", dk);
+  (void)beta;
+
+  DecodeArgs a;
+  a.B = B;
+  a.H = H;
+  a.L = L;
+  a.pos = pos;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = log_gate;
+  a.lam = lambda;
+  a.o = o;
+  a.state = static_cast<float*>(state);
+  const int code = io == LL_BF16 ? 1 : 0;
+  hipError_t e = timed(K_DECODE_STEP, stream, [&] { return llattn::launch_decode_step(code, dk, a, stream); });
+  if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// decode_step.hip -- one recurrent decode step ("Log-Linear Attention",
+// section 2.3: O(log T) state and work per generated token).
+//
+// Per head the state keeps one dk x dv fp32 matrix per level plus a log-scale
+// sigma (true state = exp(sigma) * S_hat), so the per-token decay of every
+// level costs one scalar add instead of a pass over the matrices.  At position
+// pos:
+//   sigma_l += log a_pos                                   (all levels)
+//   o = lambda_0 (q.k) v + sum_{l: bit l-1 of pos} lambda_l exp(sigma_l) S_hat_l^T q
+//   c = ctz(pos+1):  S_hat_{c+1} = k v^T + sum_{l=1..c} exp(sigma_l) S_hat_l,  sigma_{c+1} = 0
+// Levels 1..c are exactly the low set bits of pos, so the merge reuses the rows
+// loaded for the read; they become empty (bit clear in pos+1) and are not
+// rewritten.  Traffic per head: popcount(pos) level reads + one level write.
+#include "ll_device.hpp"
+#include "ll_launch.hpp"
+
+namespace llattn {
+
+constexpr int kDecodeLevelsMax = 32;
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
+  constexpr int NTH = (D * D / 4 < 256) ? D * D / 4 : 256;
+  constexpr int CG = D / 4;      // column groups of 4 floats
+  constexpr int RG = NTH / CG;   // row groups
+  constexpr int RPT = D / RG;    // rows per thread
+  __shared__ float qs[D], ks[D], vs[D];
+  __shared__ float lam[kDecodeLevelsMax], sig[kDecodeLevelsMax];
+  __shared__ __attribute__((aligned(16))) float red[RG][D];
+
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
+  const int L = a.L;
+  const int64_t pos = a.pos;
+  float* Sh = a.state + (int64_t)bh * L * D * D;
+  float* sigma = a.state + (int64_t)a.B * a.H * L * D * D + (int64_t)bh * L;
+
+  const T* q = static_cast<const T*>(a.q) + (int64_t)bh * D;
+  const T* k = static_cast<const T*>(a.k) + (int64_t)bh * D;
+  const T* v = static_cast<const T*>(a.v) + (int64_t)bh * D;
+  for (int x = tid; x < D; x += NTH) {
+    qs[x] = to_f32(q[x]);
+    ks[x] = to_f32(k[x]);
+    vs[x] = to_f32(v[x]);
+  }
+  const float loga = a.g[bh];
+  for (int x = tid; x < L; x += NTH) {
+    lam[x] = a.lam[(int64_t)bh * L + x];
+    sig[x] = sigma[x] + loga;
+  }
+  __syncthreads();
+
+  const int c = __ffsll((unsigned long long)(pos + 1)) - 1;
+  f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 msum[RPT];
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) msum[rr] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int l = 1; l < L; ++l) {
+    if (!((pos >> (l - 1)) & 1)) continue;
+    const float decay = __expf(sig[l]);
+    const float coef = lam[l] * decay;
+    const float* lev = Sh + (int64_t)l * D * D + 4 * cg;
+    f32x4 rows[RPT];
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr) rows[rr] = *reinterpret_cast<const f32x4*>(lev + (rr * RG + rg) * D);
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr) part += (coef * qs[rr * RG + rg]) * rows[rr];
+    if (l <= c) {
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr) msum[rr] += decay * rows[rr];
+    }
+  }
+
+  *reinterpret_cast<f32x4*>(&red[rg][4 * cg]) = part;
+  __syncthreads();
+  if (tid < D) {
+    float qk = 0.f;
+    for (int x = 0; x < D; ++x) qk += qs[x] * ks[x];
+    float acc = lam[0] * qk * vs[tid];
+    for (int r = 0; r < RG; ++r) acc += red[r][tid];
+    static_cast<T*>(a.o)[(int64_t)bh * D + tid] = from_f32<T>(acc);
+  }
+
+  // merge into level c+1 (c + 1 <= L - 1 is guaranteed by the caller)
+  float* dst = Sh + (int64_t)(c + 1) * D * D + 4 * cg;
+  const f32x4 vv = *reinterpret_cast<const f32x4*>(&vs[4 * cg]);
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) {
+    const int d = rr * RG + rg;
+    *reinterpret_cast<f32x4*>(dst + d * D) = ks[d] * vv + msum[rr];
+  }
+  for (int x = tid; x < L; x += NTH) sigma[x] = (x == c + 1) ? 0.f : sig[x];
+}
+
+template <typename T, int D>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
+  constexpr int NTH = (D * D / 4 < 256) ? D * D / 4 : 256;
+  hipLaunchKernelGGL((ll_decode_step<T, D>), dim3(a.B * a.H), dim3(NTH), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_step(int io, int D, const DecodeArgs& a, hipStream_t s) {
+  if (io == 1) {
+    switch (D) {
+      case 16: return launch_decode_t<bf16, 16>(a, s);
+      case 32: return launch_decode_t<bf16, 32>(a, s);
+      case 64: return launch_decode_t<bf16, 64>(a, s);
+      case 128: return launch_decode_t<bf16, 128>(a, s);
+    }
+  } else {
+    switch (D) {
+      case 16: return launch_decode_t<float, 16>(a, s);
+      case 32: return launch_decode_t<float, 32>(a, s);
+      case 64: return launch_decode_t<float, 64>(a, s);
+      case 128: return launch_decode_t<float, 128>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace llattn

@@ -1,0 +1,63 @@
+// ll_launch.hpp -- host-side launch interface between the C ABI (api.cpp)
+// and the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace llattn {
+
+constexpr int kLevelsMax = 24;  // levels staged per chunk: positions < 2^23
+
+// Everything one prefill needs, with the workspace already carved up.
+struct PrefillArgs {
+  int B, T, H, L;
+  int LS;    // levels staged per chunk: min(L, bit_length(T-1) + 1)
+  int P;     // chunks per block (power of two)
+  int nb;    // blocks per head = T / (C * P)
+  int nF;    // Fenwick nodes of level >= 1 per head = nb / 2
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;    // log-gates [B,T,H]
+  const float* lam;  // [B,T,H,L]
+  void* o;
+  float* S;   // [B*H, nb, D*D] decayed key-value state of each block (tile layout)
+  float* GS;  // [B*H, nb] sum of log-gates of each block
+  float* F;   // [B*H, nF, D*D] Fenwick nodes of level >= 1 (odd block index e at e/2)
+  float* GF;  // [B*H, nF]
+  float* state;  // nullable export target [B,H,L,D,D] + sigma [B,H,L]
+};
+
+struct DecodeArgs {
+  int B, H, L;
+  int64_t pos;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* lam;
+  void* o;
+  float* state;
+};
+
+// io: 0 = fp32, 1 = bf16.  Each returns hipSuccess or the launch error.
+hipError_t launch_block_state(int io, int D, int C, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_chunk_attn(int io, int D, int C, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_fenwick_scan(int D, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_state_export(int D, int C, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_decode_step(int io, int D, const DecodeArgs& a, hipStream_t s);
+
+inline int ilog2_host(int x) {
+  int r = 0;
+  while (x > 1) {
+    x >>= 1;
+    ++r;
+  }
+  return r;
+}
+
+// largest within-block Fenwick depth the chunk kernels hold in registers
+constexpr int max_block_depth(int D) { return D >= 128 ? 2 : 3; }
+
+}  // namespace llattn

@@ -14,7 +14,9 @@ Distributions (shared by every workload unless stated):
 For bf16 workloads q, k, v are drawn in fp32 and rounded to bf16 (round to
 nearest even); gates, lambda and beta stay fp32.
 
-Draw order inside one generator: q, k, v, log_gate, lambda, beta.
+Each tensor has its own generator, seeded from the workload seed and the
+tensor's index (q 0, k 1, v 2, log_gate 3, lambda 4, beta 5, one-hot level 6),
+so any subset can be drawn alone and yields the same values.
 """
 
 from __future__ import annotations
@@ -72,9 +74,9 @@ def with_shape(w: Workload, **kw) -> Workload:
     return replace(w, **kw)
 
 
-def _gen(seed: int, device) -> torch.Generator:
+def _gen(seed: int, index: int, device) -> torch.Generator:
     g = torch.Generator(device=device)
-    g.manual_seed(seed)
+    g.manual_seed(seed * 16 + index)
     return g
 
 
@@ -82,7 +84,8 @@ def _round_io(x: torch.Tensor, io: str) -> torch.Tensor:
     return x.to(torch.bfloat16) if io == "bf16" else x
 
 
-def prefill_inputs(w: Workload, device="cpu", variant: str = "default", seed: int | None = None) -> dict:
+def prefill_inputs(w: Workload, device="cpu", variant: str = "default", seed: int | None = None,
+                   parts=("q", "k", "v", "log_gate", "lam", "beta")) -> dict:
     """Inputs of one prefill over [B, T, H] tokens.
 
     variant:
@@ -91,36 +94,46 @@ def prefill_inputs(w: Workload, device="cpu", variant: str = "default", seed: in
       "slowdecay" -- log a = -U(1e-5, 1e-4);
       "deep"      -- log a == 0 and lambda one-hot at a level drawn uniformly
                      per token and head, so that every level is read alone.
+    ``parts`` selects which tensors to draw (the others are None).
     Returns q, k, v (io dtype), log_gate, lam, beta (fp32; beta None for Mamba-2).
     """
-    g = _gen(w.seed if seed is None else seed, device)
+    s = w.seed if seed is None else seed
     B, T, H = w.B, w.T, w.H
-    q = torch.randn(B, T, H, w.dk, generator=g, device=device) / math.sqrt(w.dk)
-    k = torch.randn(B, T, H, w.dk, generator=g, device=device)
-    if w.rule == GATED_DELTANET:
-        k = k / k.norm(dim=-1, keepdim=True)
-    else:
-        k = k / math.sqrt(w.dk)
-    v = torch.randn(B, T, H, w.dv, generator=g, device=device)
-    u = torch.rand(B, T, H, generator=g, device=device)
-    log_gate = -(0.001 + 0.099 * u)
-    lam = torch.nn.functional.softplus(0.54 + 0.5 * torch.randn(B, T, H, w.L, generator=g, device=device))
-    beta = None
-    if w.rule == GATED_DELTANET:
-        beta = torch.sigmoid(torch.randn(B, T, H, generator=g, device=device))
-    if variant == "nodecay":
-        log_gate = torch.zeros_like(log_gate)
-    elif variant == "slowdecay":
-        log_gate = -(1e-5 + 9e-5 * u)
-    elif variant == "deep":
-        log_gate = torch.zeros_like(log_gate)
-        hot = torch.randint(0, w.L, (B, T, H), generator=g, device=device)
-        lam = torch.nn.functional.one_hot(hot, w.L).to(torch.float32)
-    elif variant != "default":
-        raise ValueError(f"unknown variant {variant!r}")
-    return dict(q=_round_io(q, w.io), k=_round_io(k, w.io), v=_round_io(v, w.io),
-                log_gate=log_gate.contiguous(), lam=lam.contiguous(),
-                beta=None if beta is None else beta.contiguous())
+    out = dict(q=None, k=None, v=None, log_gate=None, lam=None, beta=None)
+    if "q" in parts:
+        q = torch.randn(B, T, H, w.dk, generator=_gen(s, 0, device), device=device) / math.sqrt(w.dk)
+        out["q"] = _round_io(q, w.io)
+    if "k" in parts:
+        k = torch.randn(B, T, H, w.dk, generator=_gen(s, 1, device), device=device)
+        if w.rule == GATED_DELTANET:
+            k = k / k.norm(dim=-1, keepdim=True)
+        else:
+            k = k / math.sqrt(w.dk)
+        out["k"] = _round_io(k, w.io)
+    if "v" in parts:
+        out["v"] = _round_io(torch.randn(B, T, H, w.dv, generator=_gen(s, 2, device), device=device), w.io)
+    if "log_gate" in parts:
+        u = torch.rand(B, T, H, generator=_gen(s, 3, device), device=device)
+        if variant in ("nodecay", "deep"):
+            g = torch.zeros_like(u)
+        elif variant == "slowdecay":
+            g = -(1e-5 + 9e-5 * u)
+        elif variant == "default":
+            g = -(0.001 + 0.099 * u)
+        else:
+            raise ValueError(f"unknown variant {variant!r}")
+        out["log_gate"] = g.contiguous()
+    if "lam" in parts:
+        if variant == "deep":
+            hot = torch.randint(0, w.L, (B, T, H), generator=_gen(s, 6, device), device=device)
+            lam = torch.nn.functional.one_hot(hot, w.L).to(torch.float32)
+        else:
+            z = torch.randn(B, T, H, w.L, generator=_gen(s, 4, device), device=device)
+            lam = torch.nn.functional.softplus(0.54 + 0.5 * z)
+        out["lam"] = lam.contiguous()
+    if "beta" in parts and w.rule == GATED_DELTANET:
+        out["beta"] = torch.sigmoid(torch.randn(B, T, H, generator=_gen(s, 5, device), device=device)).contiguous()
+    return out
 
 
 def decode_inputs(w: Workload, device="cpu", seed: int | None = None) -> dict:

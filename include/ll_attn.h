@@ -1,0 +1,159 @@
+/*
+ * ll_attn.h -- C ABI of libllattn.so: log-linear (Fenwick-tree) attention
+ * forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed ("Log-Linear Attention", technical summary, section 2.2):
+ *
+ *   o_t = sum_{l=0}^{L-1} lambda_t^(l) q_t^T S_t^(l)
+ *
+ * where the prefix [0,t) is split by the Fenwick-tree decomposition into
+ * disjoint power-of-two buckets (level l >= 1 holds 2^(l-1) tokens; level 0 is
+ * token t itself) and S_t^(l) is the hidden state of bucket l.  Equivalently,
+ * with 0-based tokens and lev(t,s) = bit_length(t XOR s) for s < t, lev(t,t) = 0:
+ *
+ *   o_t = sum_{s<=t} lambda_t^(lev(t,s)) * prod_{r=s+1}^{t} a_r * (q_t . k_s) * w_s
+ *
+ * The write w_s follows the host model the method is applied to (section 3):
+ *   LL_MAMBA2          w_s = v_s                (scalar-gated state, S_t = a_t S_{t-1} + k_t v_t^T)
+ *   LL_GATED_DELTANET  w_s = u_s = beta_s (v_s - a_s S_{s-1}^T k_s), the pseudo-value of the
+ *                      gated delta rule S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T;
+ *                      the level weights act on the read only.
+ * The gate is passed as log a_t (a_t in (0,1], so log a_t <= 0; positive values
+ * are accepted but can overflow exactly as the mathematics does).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensors are dense, row-major, in device memory owned by the caller.
+ *    The library never allocates, frees or synchronises.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *  - Every argument is validated before any HIP call: a non-LL_OK return
+ *    means nothing was enqueued; ll_last_error() then describes the problem.
+ *  - LL_ERR_HIP reports a failed launch.  Faults inside kernels surface at the
+ *    caller's next synchronisation of the stream.
+ *  - No C++ exception crosses this interface.  The library is thread-safe for
+ *    calls on different streams with disjoint output buffers.
+ */
+#ifndef LL_ATTN_H
+#define LL_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LL_OK = 0,
+  LL_ERR_NULL = -1,        /* a required pointer is NULL */
+  LL_ERR_SHAPE = -2,       /* sizes inconsistent (e.g. T % C != 0, too few levels) */
+  LL_ERR_DTYPE = -3,       /* unknown io dtype */
+  LL_ERR_UNSUPPORTED = -4, /* valid but not implemented (head size, chunk, rule) */
+  LL_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
+  LL_ERR_POSITION = -6,    /* decode position outside what the levels can hold */
+  LL_ERR_HIP = -7          /* a HIP launch failed */
+} ll_status;
+
+typedef enum { LL_F32 = 0, LL_BF16 = 1 } ll_dtype;
+
+typedef enum { LL_MAMBA2 = 0, LL_GATED_DELTANET = 1 } ll_rule;
+
+/*
+ * One prefill problem.
+ *   B, T, H : batch, tokens, heads.       dk, dv : key and value head sizes.
+ *   L       : number of Fenwick levels (level 0 = the token itself).  Outputs
+ *             need T <= 2^(L-1); exporting the state of [0,T) needs
+ *             T < 2^(L-1).  Levels beyond the largest used are ignored.
+ *   C       : chunk size of the chunk-parallel form (section 2.3), a power of
+ *             two with T % C == 0.  The result does not depend on C beyond
+ *             rounding.
+ *   io      : dtype of q, k, v and o.  Gates, lambda, beta and states are fp32.
+ * Implemented (LL_ERR_UNSUPPORTED otherwise): dk == dv, and
+ *   bf16 io: dk in {32, 64, 128}, C in {32, 64};
+ *   fp32 io: dk in {16, 32, 64},  C in {16, 32, 64};
+ *   T < 2^23.
+ */
+typedef struct {
+  int B, T, H, dk, dv, L, C;
+  ll_dtype io;
+  ll_rule rule;
+} ll_problem;
+
+/*
+ * Bytes of device workspace ll_attn_fwd needs for `p` (0 is possible).  The
+ * workspace holds, per head, the decayed key-value state of every aligned span
+ * of chunks and its Fenwick combination (chunk-parallel form, section 2.3).
+ * Errors: LL_ERR_NULL, and every validation error of ll_attn_fwd.
+ */
+ll_status ll_attn_fwd_workspace_bytes(const ll_problem* p, size_t* bytes);
+
+/*
+ * Chunk-parallel prefill (section 2.3, "training (parallel)": the hierarchical
+ * mask evaluated chunk by chunk with matrix multiplications).
+ *   q [B,T,H,dk], k [B,T,H,dk], v [B,T,H,dv]     io dtype
+ *   log_gate [B,T,H]        fp32, log a_t
+ *   lambda   [B,T,H,L]      fp32, per-token, per-head level weights
+ *   beta     [B,T,H]        fp32, LL_GATED_DELTANET only (NULL otherwise)
+ *   o        [B,T,H,dv]     io dtype, written (may be NULL if state_out is not)
+ *   state_out                nullable; if given, receives the per-level states
+ *                            of [0,T) in the decode-state layout (see
+ *                            ll_decode_state_bytes), decayed through token T-1
+ *                            with all log-scales 0 and empty levels zeroed.
+ *   workspace                device memory of >= ll_attn_fwd_workspace_bytes;
+ *                            contents on entry do not matter.
+ * q and lambda may be NULL when o is NULL.
+ */
+ll_status ll_attn_fwd(const ll_problem* p, const void* q, const void* k, const void* v,
+                      const float* log_gate, const float* lambda, const float* beta, void* o,
+                      void* state_out, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/*
+ * Bytes of one decode state: S_hat [B,H,L,dk,dv] fp32 followed by
+ * sigma [B,H,L] fp32.  The true per-level state is exp(sigma_l) * S_hat_l
+ * (the log-scale carries the decay lazily).  Level l >= 1 holds the bucket of
+ * size 2^(l-1) of the prefix [0,pos) when bit l-1 of pos is set; the other
+ * levels (and level 0) are ignored and may hold anything.
+ * A zero-filled state is the state of the empty prefix (pos = 0).
+ */
+ll_status ll_decode_state_bytes(int B, int H, int dk, int dv, int L, size_t* bytes);
+
+/*
+ * One recurrent decode step at position `pos` (section 2.3, "inference":
+ * O(log T) state and time per token), for all B*H heads at once.
+ *   q, k [B,H,dk], v [B,H,dv]       io dtype, the new token
+ *   log_gate [B,H], lambda [B,H,L]  fp32     beta [B,H] (LL_GATED_DELTANET only)
+ *   o [B,H,dv]                      io dtype, written
+ *   state                           in/out, the layout above, holding [0,pos) on
+ *                                   entry and [0,pos+1) on return.
+ * Requires pos + 1 < 2^(L-1) (LL_ERR_POSITION otherwise), so that the state
+ * after the step still fits.  Only LL_MAMBA2 is implemented
+ * (LL_ERR_UNSUPPORTED otherwise).
+ */
+ll_status ll_decode_step(int B, int H, int dk, int dv, int L, ll_dtype io, ll_rule rule, int64_t pos,
+                         const void* q, const void* k, const void* v, const float* log_gate,
+                         const float* lambda, const float* beta, void* o, void* state,
+                         hipStream_t stream);
+
+/* Text of the last error on the calling thread; valid until its next call. */
+const char* ll_last_error(void);
+
+/*
+ * Per-kernel timing, a measurement aid (off by default).  While enabled, each
+ * kernel that ll_attn_fwd and ll_decode_step launch is bracketed by two HIP
+ * events recorded on the call's stream.  ll_kernel_timing_read() waits for the
+ * recorded events, then reports for up to `capacity` kernels their name (a
+ * static string: "ll_chunk_state", "ll_fenwick_scan", "ll_chunk_attn",
+ * "ll_state_export", "ll_decode_step"), the summed milliseconds and the launch
+ * count, and clears the record.  Enabling creates HIP events lazily; timing
+ * adds two event records per launch, so do not time throughput with it on.
+ */
+ll_status ll_kernel_timing_enable(int on);
+ll_status ll_kernel_timing_read(const char** names, double* total_ms, int* launches, int capacity, int* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LL_ATTN_H */

@@ -57,6 +57,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
 def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     P = ctypes.c_void_p
     i32, i64 = ctypes.c_int, ctypes.c_int64
+    lib.llref_threads.argtypes = []
+    lib.llref_threads.restype = i32
     lib.llref_level.argtypes = [i64, i64]
     lib.llref_level.restype = i32
     lib.llref_levels_row.argtypes = [i64, P]
@@ -93,6 +95,11 @@ def _heads(heads):
 def _check(rc: int, what: str) -> None:
     if rc != 0:
         raise ValueError(f"{what}: {_ERRORS.get(rc, rc)}")
+
+
+def threads(lib=None) -> int:
+    """OpenMP threads the oracle's parallel loops use (over heads)."""
+    return (lib or load()).llref_threads()
 
 
 def level(t: int, s: int, lib=None) -> int:

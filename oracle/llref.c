@@ -39,6 +39,7 @@
  * Return value: 0 on success, a negative code for inconsistent arguments.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -47,6 +48,9 @@
 #define LLREF_EARG -1
 #define LLREF_ELEVELS -2
 #define LLREF_ENOMEM -3
+
+/* threads an OpenMP region of this library uses */
+int llref_threads(void) { return omp_get_max_threads(); }
 
 /* floor(log2(x)) for x >= 1 */
 static int floor_log2(int64_t x) {

@@ -1,0 +1,141 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared
+entry point, sizes its buffers as documented, and rejects bad arguments before
+touching the GPU (a rejected call enqueues nothing, so these run without one)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fenwick_tree_linear_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ll_attn.h")
+
+DUMMY = 0x1000  # a non-NULL pointer that validation must never dereference
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ll_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(
+        ["ll_attn_fwd", "ll_attn_fwd_workspace_bytes", "ll_decode_state_bytes", "ll_decode_step",
+         "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_last_error"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(F.lib_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def prob(**kw):
+    base = dict(B=2, T=16384, H=16, dk=64, dv=64, L=15, C=64, io=F.LL_BF16, rule=F.LL_MAMBA2)
+    base.update(kw)
+    return F.LLProblem(*(base[k] for k in ("B", "T", "H", "dk", "dv", "L", "C", "io", "rule")))
+
+
+def status_of(fn, *args):
+    try:
+        fn(*args)
+    except F.LLError as e:
+        return e.name, str(e)
+    return "LL_OK", ""
+
+
+def test_workspace_bytes_for_the_16k_prefill():
+    # 32 heads x 32 blocks of 8 chunks: 1024 block states + 512 Fenwick nodes
+    # of 64x64 fp32, plus their gate sums
+    n = F.ll_attn_fwd_workspace_bytes(prob())
+    assert 1536 * 64 * 64 * 4 <= n <= 1536 * 64 * 64 * 4 + 4 * 4096 + 4 * 256
+    assert n % 256 == 0
+
+
+def test_workspace_grows_with_problem():
+    a = F.ll_attn_fwd_workspace_bytes(prob(T=2048, L=12))
+    b = F.ll_attn_fwd_workspace_bytes(prob(T=4096, L=13))
+    assert 0 < a < b
+
+
+@pytest.mark.parametrize("kw,name,frag", [
+    (dict(T=16384, L=14), "LL_ERR_SHAPE", "levels"),
+    (dict(T=1000), "LL_ERR_SHAPE", "multiple"),
+    (dict(C=48), "LL_ERR_SHAPE", "power of two"),
+    (dict(C=128), "LL_ERR_UNSUPPORTED", "chunk"),
+    (dict(C=16), "LL_ERR_UNSUPPORTED", "chunk"),
+    (dict(dk=64, dv=32), "LL_ERR_UNSUPPORTED", "dk"),
+    (dict(dk=48, dv=48), "LL_ERR_UNSUPPORTED", "head size"),
+    (dict(dk=16, dv=16), "LL_ERR_UNSUPPORTED", "head size"),
+    (dict(io=7), "LL_ERR_DTYPE", "dtype"),
+    (dict(rule=5), "LL_ERR_UNSUPPORTED", "rule"),
+    (dict(B=0), "LL_ERR_SHAPE", "positive"),
+    (dict(T=2 ** 24, L=25), "LL_ERR_UNSUPPORTED", "levels"),
+])
+def test_invalid_problems_are_rejected(kw, name, frag):
+    st, msg = status_of(F.ll_attn_fwd_workspace_bytes, prob(**kw))
+    assert st == name and frag in msg, msg
+
+
+def test_fp32_supports_small_heads_and_chunks():
+    assert F.ll_attn_fwd_workspace_bytes(prob(T=256, dk=16, dv=16, L=9, C=16, io=F.LL_F32)) > 0
+
+
+def test_fwd_validation_before_any_launch():
+    p = prob()
+    ws = F.ll_attn_fwd_workspace_bytes(p)
+    D = DUMMY
+    cases = [
+        ((p, D, None, D, D, D, None, D, None, D, ws), "LL_ERR_NULL"),           # k NULL
+        ((p, D, D, D, D, D, None, None, None, D, ws), "LL_ERR_NULL"),           # nothing requested
+        ((p, None, D, D, D, D, None, D, None, D, ws), "LL_ERR_NULL"),           # q NULL with output
+        ((p, D, D, D, D, None, None, D, None, D, ws), "LL_ERR_NULL"),           # lambda NULL with output
+        ((p, D, D, D, D, D, None, D, None, D, ws - 1), "LL_ERR_WORKSPACE"),     # workspace too small
+        ((p, D, D, D, D, D, None, D, None, None, ws), "LL_ERR_WORKSPACE"),      # workspace NULL
+        ((p, D, D, D, D, D, None, D, D, D, ws), "LL_ERR_SHAPE"),                # export of [0,2^14) needs L=16
+        ((prob(rule=F.LL_GATED_DELTANET), D, D, D, D, D, None, D, None, D, ws), "LL_ERR_UNSUPPORTED"),
+        ((None, D, D, D, D, D, None, D, None, D, ws), "LL_ERR_NULL"),
+    ]
+    for args, name in cases:
+        st, msg = status_of(F.ll_attn_fwd, *args, 0)
+        assert st == name, (name, msg)
+
+
+def test_decode_state_bytes():
+    # S_hat [B,H,L,dk,dv] + sigma [B,H,L], fp32
+    assert F.ll_decode_state_bytes(64, 16, 64, 64, 17) == 64 * 16 * 17 * (64 * 64 + 1) * 4
+    assert status_of(F.ll_decode_state_bytes, 1, 1, 64, 64, 1)[0] == "LL_ERR_SHAPE"
+
+
+def test_decode_validation_before_any_launch():
+    D = DUMMY
+    good = [64, 16, 64, 64, 17, F.LL_BF16, F.LL_MAMBA2, 32768, D, D, D, D, D, None, D, D, 0]
+    # largest position whose successor state still fits: pos + 1 < 2^16
+    cases = [
+        (dict(pos=2 ** 16 - 1), "LL_ERR_POSITION"),
+        (dict(pos=-1), "LL_ERR_POSITION"),
+        (dict(L=33, pos=5), "LL_ERR_UNSUPPORTED"),
+        (dict(io=3), "LL_ERR_DTYPE"),
+        (dict(rule=F.LL_GATED_DELTANET), "LL_ERR_UNSUPPORTED"),
+        (dict(dk=64, dv=32), "LL_ERR_UNSUPPORTED"),
+        (dict(state=None), "LL_ERR_NULL"),
+        (dict(q=None), "LL_ERR_NULL"),
+    ]
+    idx = dict(B=0, H=1, dk=2, dv=3, L=4, io=5, rule=6, pos=7, q=8, k=9, v=10, g=11, lam=12, beta=13, o=14, state=15)
+    for kw, name in cases:
+        args = list(good)
+        for key, val in kw.items():
+            args[idx[key]] = val
+        st, msg = status_of(F.ll_decode_step, *args)
+        assert st == name, (kw, msg)
+
+
+def test_last_error_is_cleared_by_a_good_call():
+    status_of(F.ll_attn_fwd_workspace_bytes, prob(C=48))
+    assert F.ll_last_error() != ""
+    F.ll_attn_fwd_workspace_bytes(prob())
+    assert F.ll_last_error() == ""
