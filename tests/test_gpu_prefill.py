@@ -86,7 +86,7 @@ def test_every_level_fp32(variant):
 RAGGED = [
     # io, B, H, T, d, C, L    (T/C chunks: odd counts give one-chunk blocks)
     ("bf16", 3, 5, 320, 64, 64, 10),    # 5 chunks
-    ("bf16", 1, 2, 1536, 64, 64, 11),   # 24 chunks: 3 blocks of 8
+    ("bf16", 1, 2, 1536, 64, 64, 12),   # 24 chunks: 3 blocks of 8
     ("bf16", 2, 3, 224, 32, 32, 9),     # 7 chunks of 32, d=32
     ("bf16", 2, 2, 64, 64, 64, 7),      # a single chunk
     ("bf16", 1, 3, 320, 64, 64, 20),    # more levels than needed
