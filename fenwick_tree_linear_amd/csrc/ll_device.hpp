@@ -1,6 +1,7 @@
 // ll_device.hpp -- device-side building blocks shared by the gfx950 kernels of
-// libllattn: matrix-core (MFMA) fragments, chunk staging into LDS, the
-// in-chunk gate prefix, and the tile layout of key-value states.
+// libllattn: matrix-core (MFMA) fragments, asynchronous global->LDS staging of
+// chunk tiles, fragment reads from swizzled LDS tiles (including the gfx950
+// transposing LDS read), and the tile layout of key-value states.
 //
 // MFMA conventions (CDNA3/CDNA4 16x16 shapes, wave64):
 //   accumulator f32x4 of a 16x16 tile: lane l holds rows 4*(l/16)+i (i=0..3)
@@ -23,7 +24,10 @@ namespace llattn {
 typedef __bf16 bf16;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ int ilog2c(int x) { return 31 - __clz(x); }
 
@@ -38,28 +42,8 @@ struct Mma<bf16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   // k index carried by element e (0..7) of lane group g in step s
-  __device__ __forceinline__ static int kidx(int s, int g, int e) {
+  __device__ __forceinline__ static constexpr int kidx(int s, int g, int e) {
     return 32 * s + 16 * (e >> 2) + 4 * g + (e & 3);
-  }
-  // fragment whose k axis runs along a contiguous row (row + kidx(s, g, e))
-  __device__ __forceinline__ static Frag row_frag(const bf16* row, int s, int g) {
-    bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 32 * s + 4 * g);
-    bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 32 * s + 16 + 4 * g);
-    return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-  // same, each element multiplied by w[kidx] (w in LDS, fp32)
-  __device__ __forceinline__ static Frag row_frag_scaled(const bf16* row, const float* w, int s, int g) {
-    bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 32 * s + 4 * g);
-    bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 32 * s + 16 + 4 * g);
-    f32x4 wl = *reinterpret_cast<const f32x4*>(w + 32 * s + 4 * g);
-    f32x4 wh = *reinterpret_cast<const f32x4*>(w + 32 * s + 16 + 4 * g);
-    Frag f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f[e] = (bf16)((float)lo[e] * wl[e]);
-      f[4 + e] = (bf16)((float)hi[e] * wh[e]);
-    }
-    return f;
   }
   // fragment from accumulator tiles: tiles[t] are 16-row tiles along k
   __device__ __forceinline__ static Frag acc_frag(const f32x4* tiles, int s) {
@@ -67,8 +51,6 @@ struct Mma<bf16> {
     return Frag{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
                 (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
   }
-  // highest 16-row tile index that step s touches
-  __device__ __forceinline__ static constexpr int last_tile(int s) { return 2 * s + 1; }
   __device__ __forceinline__ static constexpr int first_tile(int s) { return 2 * s; }
 };
 
@@ -79,14 +61,8 @@ struct Mma<float> {
   __device__ __forceinline__ static f32x4 mma(Frag a, Frag b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
-  __device__ __forceinline__ static int kidx(int s, int g, int) { return 16 * (s >> 2) + 4 * g + (s & 3); }
-  __device__ __forceinline__ static Frag row_frag(const float* row, int s, int g) { return row[kidx(s, g, 0)]; }
-  __device__ __forceinline__ static Frag row_frag_scaled(const float* row, const float* w, int s, int g) {
-    const int k = kidx(s, g, 0);
-    return row[k] * w[k];
-  }
+  __device__ __forceinline__ static constexpr int kidx(int s, int g, int) { return 16 * (s >> 2) + 4 * g + (s & 3); }
   __device__ __forceinline__ static Frag acc_frag(const f32x4* tiles, int s) { return tiles[s >> 2][s & 3]; }
-  __device__ __forceinline__ static constexpr int last_tile(int s) { return s >> 2; }
   __device__ __forceinline__ static constexpr int first_tile(int s) { return s >> 2; }
 };
 
@@ -119,60 +95,87 @@ __device__ __forceinline__ int state_tile_offset(int dt, int nt, int lane) {
   return ((dt * (D / 16) + nt) * 64 + lane) * 4;
 }
 
-// --------------------------------------------------------- chunk staging
-// LDS image of one chunk of C tokens of one head.
-template <typename T, int D, int C>
-struct ChunkTiles {
-  static constexpr int RP = D + 4;  // padded row of q / k (k axis = head dim)
-  static constexpr int TP = C + 4;  // padded row of k^T / v^T (k axis = tokens)
-  T q[C][RP];
-  T k[C][RP];
-  T kt[D][TP];
-  T vt[D][TP];
-  float lam[C * kLevelsMax];
-  float gcum[C];  // inclusive prefix of log a inside the chunk
-  float wend[C];  // exp(G[C-1] - G[r]): decay from token r to the chunk end
+// ------------------------------------------------------------ LDS tiles
+// Row-major [ROWS][COLS] tile of T in LDS.  Rows are stored unpadded and the
+// 16-byte chunks of row r are permuted by XOR with (r mod chunks-per-row), so
+// that the 16 rows touched by one fragment read fall on different banks.
+template <typename T, int ROWS, int COLS>
+struct Tile {
+  static constexpr int ESZ = sizeof(T);
+  static constexpr int RB = COLS * ESZ;  // bytes per row
+  static constexpr int NCH = RB / 16;    // 16-byte chunks per row
+  static constexpr int BYTES = ROWS * RB;
+  static_assert((NCH & (NCH - 1)) == 0 && NCH >= 1, "rows must be a power-of-two number of 16-byte chunks");
+  __device__ __forceinline__ static int pos(int row, int chunk) { return chunk ^ (row & (NCH - 1)); }
+  // byte offset of element (row, col)
+  __device__ __forceinline__ static int off(int row, int col) {
+    const int byte = col * ESZ;
+    return row * RB + (pos(row, byte >> 4) << 4) + (byte & 15);
+  }
 };
 
-// Loads rows [t0, t0+C) of head (b,h) of a [B,T,H,D] tensor into LDS.
-// Row-major copy into `row` (if non-null) and transposed copy into `col`
-// (if non-null).  16-byte global loads, one row segment per thread.
-template <typename T, int D, int C, int RP, int TP>
-__device__ __forceinline__ void stage_rows(const T* __restrict__ src, int64_t row_stride, T (*row)[RP],
-                                           T (*col)[TP], int tid, int nthreads) {
-  constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
-  constexpr int VPR = D / EPV;         // vectors per row
-  for (int vi = tid; vi < C * VPR; vi += nthreads) {
-    const int r = vi / VPR, c0 = (vi % VPR) * EPV;
-    const uint4 raw = *reinterpret_cast<const uint4*>(src + r * row_stride + c0);
-    if (row) {
-      uint2* dst = reinterpret_cast<uint2*>(&row[r][c0]);
-      dst[0] = uint2{raw.x, raw.y};
-      dst[1] = uint2{raw.z, raw.w};
-    }
-    if (col) {
-      const T* e = reinterpret_cast<const T*>(&raw);
-#pragma unroll
-      for (int j = 0; j < EPV; ++j) col[c0 + j][r] = e[j];
-    }
+// Direct global->LDS copy of one tile: row r of the source starts at
+// src + r * stride (elements).  One wave instruction moves 64 x 16 bytes;
+// wave `wv` of `nw` issues instructions wv, wv+nw, ...  Completion is tracked
+// by the issuing wave's vmcnt.
+template <typename T, int ROWS, int COLS>
+__device__ __forceinline__ void tile_load_async(const T* __restrict__ src, int64_t stride, char* lds, int wv, int nw,
+                                                int lane) {
+  typedef Tile<T, ROWS, COLS> TL;
+  constexpr int NINST = TL::BYTES / 1024;
+  constexpr int RPI = 1024 / TL::RB;  // rows per instruction
+  static_assert(TL::BYTES % 1024 == 0 && 1024 % TL::RB == 0, "tile must be whole 1 KiB instructions");
+  const int rl = lane / TL::NCH, p = lane % TL::NCH;
+  for (int i = wv; i < NINST; i += nw) {
+    const int row = i * RPI + rl;
+    const int chunk = TL::pos(row, p);  // the source chunk that belongs at position p
+    const T* g = src + row * stride + chunk * (16 / TL::ESZ);
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds + i * 1024), 16, 0, 0);
   }
 }
 
-// Inclusive prefix sum of the chunk's log-gates (one wave, C <= 64 lanes),
-// and the decay of every token to the chunk end.  Reads gcum[] holding the
-// raw log-gates, rewrites it in place.  Call from one whole wave.
-template <int C>
-__device__ __forceinline__ void chunk_gate_prefix(float* gcum, float* wend, int lane) {
-  float x = lane < C ? gcum[lane] : 0.f;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
+// Direct 4-byte global->LDS copy of n scattered floats: element f (0 <= f < n)
+// comes from src_of(f) and lands at lds[f].
+template <typename F>
+__device__ __forceinline__ void scatter_load_async(float* lds, int n, int wv, int nw, int lane, F src_of) {
+  for (int base = wv * 64; base < n; base += nw * 64) {
+    const int f = base + lane;
+    if (f < n) __builtin_amdgcn_global_load_lds(src_of(f), (lds_void*)(lds + base), 4, 0, 0);
   }
-  const float total = __shfl(x, C - 1, 64);
-  if (lane < C) {
-    gcum[lane] = x;
-    wend[lane] = __expf(total - x);
+}
+
+// Fragment whose k axis runs along a row: rows/columns of the MFMA tile are
+// LDS rows `row`, k = columns kidx(s, g, .).
+template <typename T, int ROWS, int COLS>
+__device__ __forceinline__ typename Mma<T>::Frag frag_row(const char* lds, int row, int s, int g) {
+  typedef Tile<T, ROWS, COLS> TL;
+  if constexpr (sizeof(T) == 2) {
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(lds + TL::off(row, 32 * s + 4 * g));
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(lds + TL::off(row, 32 * s + 16 + 4 * g));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    return *reinterpret_cast<const float*>(lds + TL::off(row, Mma<float>::kidx(s, g, 0)));
+  }
+}
+
+// Fragment whose k axis runs down the rows (tokens): the MFMA row/column is
+// LDS column col0 + lane%16, k = rows kidx(s, lane/16, .).  For bf16 this is
+// two gfx950 transposing reads: within each 16-lane group, lane q supplies the
+// address of row base + q/4, columns col0 + 4*(q%4) .. +3, and receives
+// column col0 + q of rows base .. base+3.
+template <typename T, int ROWS, int COLS>
+__device__ __forceinline__ typename Mma<T>::Frag frag_col(const char* lds, int col0, int s, int lane) {
+  typedef Tile<T, ROWS, COLS> TL;
+  const int g = lane >> 4, q = lane & 15;
+  if constexpr (sizeof(T) == 2) {
+    const int row = 32 * s + 4 * g + (q >> 2), col = col0 + 4 * (q & 3);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds + TL::off(row, col)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds + TL::off(row + 16, col)));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 v = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  } else {
+    return *reinterpret_cast<const float*>(lds + TL::off(Mma<float>::kidx(s, g, 0), col0 + q));
   }
 }
 
