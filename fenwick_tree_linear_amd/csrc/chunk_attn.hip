@@ -195,8 +195,11 @@ __device__ __forceinline__ void node_frags(typename Mma<T>::Frag (&nf)[D / Mma<T
 // ---------------------------------------------------------------------------
 // ll_chunk_attn: one workgroup per (block J, head); wave wv owns output
 // columns [16 wv, 16 wv + 16); the P chunks of the block are visited in order.
+// The Fenwick nodes of earlier blocks are the same for every chunk of the
+// block: up to MAXH of them are converted once into MFMA B fragments in LDS,
+// any further ones are read from the workspace per chunk.
 template <typename T, int D, int C, int MAXB, int MAXH>
-__global__ void __launch_bounds__(64 * (D / 16)) ll_chunk_attn(PrefillArgs a) {
+__global__ void __launch_bounds__(64 * (D / 16)) __attribute__((amdgpu_waves_per_eu(2, 2))) ll_chunk_attn(PrefillArgs a) {
   using M = Mma<T>;
   typedef typename M::Frag Frag;
   typedef Stage<T, D, C> S;
@@ -206,48 +209,43 @@ __global__ void __launch_bounds__(64 * (D / 16)) ll_chunk_attn(PrefillArgs a) {
   constexpr int DT = D / 16, CT = C / 16;
   constexpr int KSD = D / M::KS, KSC = C / M::KS;
   constexpr int LOGC = (C == 16) ? 4 : (C == 32) ? 5 : 6;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * S::BYTES + TL::BYTES + PT::BYTES];
+  constexpr int FRAG_BYTES = 64 * (int)sizeof(Frag);     // one fragment of one wave
+  constexpr int NODE_BYTES = NW * KSD * FRAG_BYTES;       // one node, every wave's columns
+  constexpr int HOFF = 2 * S::BYTES + TL::BYTES + PT::BYTES;
+  constexpr int GOFF = HOFF + (MAXH > 0 ? MAXH : 0) * NODE_BYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[GOFF + NW * C * 4];
   char* kd = smem + 2 * S::BYTES;
   char* pt = kd + TL::BYTES;
+  char* hbuf = smem + HOFF;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g4 = lane >> 4, q16 = lane & 15;
+  float* gl = reinterpret_cast<float*>(smem + GOFF) + wv * C;  // this wave's copy of G
   const int wg = xcd_logical_id(blockIdx.x, gridDim.x);
   const int J = wg % a.nb, bh = wg / a.nb, h = bh % a.H, b = bh / a.H;
   const int logP = ilog2c(a.P);
   const int LS = a.LS;
   auto row_of = [&](int j) { return ((int64_t)b * a.T + (int64_t)(J * a.P + j) * C) * a.H + h; };
+  auto node_of = [&](int e) {
+    return (e & 1) ? a.F + ((int64_t)bh * a.nF + (e >> 1)) * D * D : a.S + ((int64_t)bh * a.nb + e) * D * D;
+  };
+  auto gamma_of = [&](int e) { return (e & 1) ? a.GF[(int64_t)bh * a.nF + (e >> 1)] : a.GS[(int64_t)bh * a.nb + e]; };
 
   issue_chunk<T, D, C>(a, row_of(0), smem, true, true, wv, NW, lane, LS);
 
   // masked-score tiles above the diagonal are never written: keep them zero
   for (int x = tid * 16; x < PT::BYTES; x += 64 * NW * 16) *reinterpret_cast<uint4*>(pt + x) = uint4{0, 0, 0, 0};
 
-  // Fenwick nodes of earlier blocks (most recent first), as bf16/fp32 MFMA
-  // B fragments of this wave's columns.  Levels past MAXH are read per chunk.
-  Frag hn[MAXH > 0 ? MAXH : 1][KSD];
-  int hlvl[MAXH > 0 ? MAXH : 1];
-  float hoff[MAXH > 0 ? MAXH : 1];
-  int nhigh = 0;
-  int rest_after;  // set bits of J whose nodes are not held in registers
-  {
+  // the first MAXH nodes (most recent first) as B fragments of each wave's columns
+  if constexpr (MAXH > 0) {
     int rest = J;
-    float dd = 0.f;  // log-decay from the node's end to the start of block J
+    for (int x = 0; x < MAXH && rest > 0; ++x) {
+      Frag nf[KSD];
+      node_frags<T, D>(nf, node_of(rest - 1), wv, lane);
 #pragma unroll
-    for (int x = 0; x < MAXH; ++x) {
-      if (rest > 0) {
-        const int e = rest - 1, l = __ffs(rest) - 1;
-        const float* node = (e & 1) ? a.F + ((int64_t)bh * a.nF + (e >> 1)) * D * D
-                                    : a.S + ((int64_t)bh * a.nb + e) * D * D;
-        const float gam = (e & 1) ? a.GF[(int64_t)bh * a.nF + (e >> 1)] : a.GS[(int64_t)bh * a.nb + e];
-        node_frags<T, D>(hn[x], node, wv, lane);
-        hlvl[x] = LOGC + logP + l + 1;
-        hoff[x] = dd;
-        dd += gam;
-        rest &= rest - 1;
-        nhigh = x + 1;
-      }
+      for (int s = 0; s < KSD; ++s)
+        *reinterpret_cast<Frag*>(hbuf + ((x * NW + wv) * KSD + s) * FRAG_BYTES + lane * (int)sizeof(Frag)) = nf[s];
+      rest &= rest - 1;
     }
-    rest_after = rest;
   }
 
   f32x4 nst[MAXB][DT];
@@ -269,6 +267,7 @@ __global__ void __launch_bounds__(64 * (D / 16)) ll_chunk_attn(PrefillArgs a) {
       issue_chunk<T, D, C>(a, row_of(j + 1), smem + ((j + 1) & 1) * S::BYTES, true, true, wv, NW, lane, LS);
 
     const float gscan = chunk_prefix<C>(reinterpret_cast<const float*>(st + S::GOFF), lane);
+    if (lane < C) gl[lane] = gscan;
     const float gsum = __shfl(gscan, C - 1, 64);
 
     Frag qf[CT][KSD];
@@ -282,39 +281,39 @@ __global__ void __launch_bounds__(64 * (D / 16)) ll_chunk_attn(PrefillArgs a) {
 #pragma unroll
     for (int rt = 0; rt < CT; ++rt)
 #pragma unroll
-    for (int ct = 0; ct <= rt; ++ct) {  // ct: source tile (column of P)
-      if ((rt * (rt + 1) / 2 + ct) % NW != wv) continue;
-      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct <= rt; ++ct) {  // ct: source tile (column of P)
+        if ((rt * (rt + 1) / 2 + ct) % NW != wv) continue;
+        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KSD; ++s) x = M::mma(frag_row<T, C, D>(st + S::KOFF, 16 * ct + q16, s, g4), qf[rt][s], x);
-      const int r = 16 * rt + q16;
-      const float gr = __shfl(gscan, r, 64);
-      float pv[4];
+        for (int s = 0; s < KSD; ++s) x = M::mma(frag_row<T, C, D>(st + S::KOFF, 16 * ct + q16, s, g4), qf[rt][s], x);
+        const int r = 16 * rt + q16;
+        const float gr = gl[r];
+        const f32x4 gs = *reinterpret_cast<const f32x4*>(gl + 16 * ct + 4 * g4);
+        float pv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int src = 16 * ct + 4 * g4 + i;
-        const float gs = __shfl(gscan, src, 64);
-        float val = 0.f;
-        if (src <= r) {
-          const int lev = (src == r) ? 0 : 32 - __clz(r ^ src);
-          val = x[i] * lamT[lev * C + r] * __expf(gr - gs);
+        for (int i = 0; i < 4; ++i) {
+          const int src = 16 * ct + 4 * g4 + i;
+          float val = 0.f;
+          if (src <= r) {
+            const int lev = (src == r) ? 0 : 32 - __clz(r ^ src);
+            val = x[i] * lamT[lev * C + r] * __expf(gr - gs[i]);
+          }
+          pv[i] = val;
         }
-        pv[i] = val;
+        char* dst = pt + PT::off(r, 16 * ct + 4 * g4);
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<bf16x4*>(dst) = bf16x4{(bf16)pv[0], (bf16)pv[1], (bf16)pv[2], (bf16)pv[3]};
+        } else {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{pv[0], pv[1], pv[2], pv[3]};
+        }
       }
-      char* dst = pt + PT::off(r, 16 * ct + 4 * g4);
-      if constexpr (sizeof(T) == 2) {
-        *reinterpret_cast<bf16x4*>(dst) = bf16x4{(bf16)pv[0], (bf16)pv[1], (bf16)pv[2], (bf16)pv[3]};
-      } else {
-        *reinterpret_cast<f32x4*>(dst) = f32x4{pv[0], pv[1], pv[2], pv[3]};
-      }
-    }
 
     // --- decayed keys for this chunk's state, and lambda of the inter-chunk
     // levels pre-multiplied by exp(G[r]) (in place; levels <= log2 C untouched)
     decay_keys<T, D, C, NW>(st + S::KOFF, kd, gscan, wv, lane);
     {
       float* lw = reinterpret_cast<float*>(st + S::LOFF);
-      const float eg = __expf(__shfl(gscan, lane & (C - 1), 64));
+      const float eg = __expf(gl[lane & (C - 1)]);
       const int n = (LS - LOGC - 1) * C;
       for (int x = tid; x < n; x += 64 * NW) lw[(LOGC + 1) * C + x] *= eg;
     }
@@ -335,27 +334,24 @@ __global__ void __launch_bounds__(64 * (D / 16)) ll_chunk_attn(PrefillArgs a) {
       }
     }
 
-    // --- earlier blocks: register-held Fenwick nodes, then the rest
-#pragma unroll
-    for (int x = 0; x < MAXH; ++x)
-      if (x < nhigh) level_read<T, D, C>(oacc, qf, hn[x], lamT, hlvl[x], __expf(gw + hoff[x]), g4);
-    if (rest_after) {
+    // --- earlier blocks: one Fenwick node per set bit of J, most recent first
+    {
       int rest = J;
-      float dd = 0.f;
-      int x = 0;
-      while (rest > 0) {
+      float dd = 0.f;  // log-decay from the node's end to the start of block J
+      for (int x = 0; rest > 0; ++x) {
         const int e = rest - 1, l = __ffs(rest) - 1;
-        const float gam = (e & 1) ? a.GF[(int64_t)bh * a.nF + (e >> 1)] : a.GS[(int64_t)bh * a.nb + e];
-        if (x >= MAXH) {
-          const float* node = (e & 1) ? a.F + ((int64_t)bh * a.nF + (e >> 1)) * D * D
-                                      : a.S + ((int64_t)bh * a.nb + e) * D * D;
-          Frag nf[KSD];
-          node_frags<T, D>(nf, node, wv, lane);
-          level_read<T, D, C>(oacc, qf, nf, lamT, LOGC + logP + l + 1, __expf(gw + dd), g4);
+        Frag nf[KSD];
+        if (x < MAXH) {
+#pragma unroll
+          for (int s = 0; s < KSD; ++s)
+            nf[s] = *reinterpret_cast<const Frag*>(hbuf + ((x * NW + wv) * KSD + s) * FRAG_BYTES +
+                                                   lane * (int)sizeof(Frag));
+        } else {
+          node_frags<T, D>(nf, node_of(e), wv, lane);
         }
-        dd += gam;
+        level_read<T, D, C>(oacc, qf, nf, lamT, LOGC + logP + l + 1, __expf(gw + dd), g4);
+        dd += gamma_of(e);
         rest &= rest - 1;
-        ++x;
       }
     }
 
@@ -426,7 +422,8 @@ static hipError_t launch_state_t(const PrefillArgs& a, hipStream_t s) {
 template <typename T, int D, int C>
 static hipError_t launch_attn_t(const PrefillArgs& a, hipStream_t s) {
   const int grid = a.B * a.H * a.nb;
-  constexpr int MAXH = D >= 128 ? 2 : 6;
+  // node fragments kept in LDS: bf16 heads up to 64 (8 KB per node at d=64)
+  constexpr int MAXH = 0;
   hipLaunchKernelGGL((ll_chunk_attn<T, D, C, max_block_depth(D), MAXH>), dim3(grid), dim3(64 * (D / 16)), 0, s, a);
   return hipGetLastError();
 }
