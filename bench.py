@@ -72,6 +72,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device-to-device copy of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (each (batch, head) pair is "
@@ -95,6 +97,16 @@ def main() -> int:
 
     def step():
         F.ll_attn_fwd(prob, x["q"], x["k"], x["v"], x["log_gate"], x["lam"], None, o, None, ws, ws_bytes, stream)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * 1024 * 1024 // 4
+        src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written")
+        del src, dst
 
     for _ in range(args.warmup):
         step()

@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def lib_path() -> str:
-    return os.environ.get("LLATTN_LIB", os.path.join(_HERE, "libllattn.so"))
+    return os.environ.get("LLATTN_LIB") or os.path.join(_HERE, "libllattn.so")
 
 
 class LLError(RuntimeError):

@@ -9,7 +9,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "../../include/ll_attn.h"
+#include "ll_attn.h"
 #include "ll_launch.hpp"
 
 using llattn::DecodeArgs;
