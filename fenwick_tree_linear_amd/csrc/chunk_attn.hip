@@ -17,138 +17,141 @@
 //                   in registers, and the block-level nodes built by
 //                   ll_fenwick_scan, each read as diag(alpha) Q N on MFMA.
 //
-// Both kernels stream their chunks through LDS with direct global->LDS loads,
-// double-buffered: chunk j+1 is in flight while chunk j is computed.  Tiles
-// keep the global row-major layout; the operands that contract over tokens
-// (V, and the decayed K for the state) are read with the transposing LDS
-// read, so no transposed copy is ever written.
+// Chunks stream through LDS with direct global->LDS loads issued one chunk
+// ahead.  Tiles keep the global row-major layout; the operands that contract
+// over tokens (V, and K for the state) are read with the transposing LDS
+// read, and the per-token decay of the state update is applied to the V
+// fragments in registers, so no transposed or rescaled tile is ever written.
 #include "ll_device.hpp"
 #include "ll_launch.hpp"
 
 namespace llattn {
 
-// Per-chunk staging area of one pipeline stage.
-template <typename T, int D, int C>
-struct Stage {
-  typedef Tile<T, C, D> Row;  // q, k, v: [C][D]
-  static constexpr int QOFF = 0;
-  static constexpr int KOFF = QOFF + Row::BYTES;
-  static constexpr int VOFF = KOFF + Row::BYTES;
-  static constexpr int LOFF = VOFF + Row::BYTES;            // lambda^T [kLevelsMax][C] fp32
-  static constexpr int GOFF = LOFF + kLevelsMax * C * 4;    // raw log-gates [C] fp32
-  static constexpr int BYTES = GOFF + C * 4;
-};
+// DPP move of a float within a wave (lanes without a source read 0).
+template <int CTRL, int ROW_MASK, bool ZERO_FILL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, ZERO_FILL));
+}
 
-// Shared prologue of one chunk: the in-chunk inclusive prefix G of the
-// log-gates (every wave computes it; lane r holds G[r]).
+// In-chunk inclusive prefix G of the log-gates (every wave computes it; lane
+// r holds G[r]).  DPP shifts inside each 16-lane row, then the last lane of
+// each row is broadcast to the rows above it: no LDS round trips.
 template <int C>
 __device__ __forceinline__ float chunk_prefix(const float* gates, int lane) {
   float x = lane < C ? gates[lane] : 0.f;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  x += dpp_f32<0x111, 0xf, true>(x);  // row_shr:1
+  x += dpp_f32<0x112, 0xf, true>(x);  // row_shr:2
+  x += dpp_f32<0x114, 0xf, true>(x);  // row_shr:4
+  x += dpp_f32<0x118, 0xf, true>(x);  // row_shr:8
+  if (C > 16) x += dpp_f32<0x142, 0xa, false>(x);  // row_bcast:15 into rows 1 and 3
+  if (C > 32) x += dpp_f32<0x143, 0xc, false>(x);  // row_bcast:31 into rows 2 and 3
   return x;
 }
 
-// Writes kd[r][:] = k[r][:] * exp(G[C-1] - G[r]) (the key decayed to the chunk
-// end) for the rows of wave wv.  Elementwise per row, so it works on LDS
-// positions directly (the swizzle is the same in both tiles).
-template <typename T, int D, int C, int NW>
-__device__ __forceinline__ void decay_keys(const char* k, char* kd, float gscan, int wv, int lane) {
-  typedef Tile<T, C, D> TL;
-  constexpr int RPW = C / NW;                       // rows per wave
-  constexpr int CPL = RPW * TL::NCH / 64;           // 16-byte chunks per lane
-  static_assert(CPL >= 1 && (RPW * TL::NCH) % 64 == 0, "decay pass shape");
-  const float glast = __shfl(gscan, C - 1, 64);
+// Multiplies element e of a fragment whose k axis is tokens by w[token(e)].
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::Frag scale_tokens(typename Mma<T>::Frag f, const float* w, int s, int g) {
+  if constexpr (sizeof(T) == 2) {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(w + 32 * s + 4 * g);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(w + 32 * s + 16 + 4 * g);
+    bf16x8 r;
 #pragma unroll
-  for (int u = 0; u < CPL; ++u) {
-    const int ci = lane + 64 * u;
-    const int row = wv * RPW + ci / TL::NCH;
-    const int byte = row * TL::RB + (ci % TL::NCH) * 16;
-    const float w = __expf(glast - __shfl(gscan, row, 64));
-    const uint4 raw = *reinterpret_cast<const uint4*>(k + byte);
-    uint4 outv;
-    if constexpr (sizeof(T) == 2) {
-      const bf16x8 x = __builtin_bit_cast(bf16x8, raw);
-      bf16x8 y;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = (bf16)((float)x[e] * w);
-      outv = __builtin_bit_cast(uint4, y);
-    } else {
-      const f32x4 x = __builtin_bit_cast(f32x4, raw);
-      outv = __builtin_bit_cast(uint4, x * w);
+    for (int e = 0; e < 4; ++e) {
+      r[e] = (bf16)((float)f[e] * lo[e]);
+      r[4 + e] = (bf16)((float)f[4 + e] * hi[e]);
     }
-    *reinterpret_cast<uint4*>(kd + byte) = outv;
+    return r;
+  } else {
+    return f * w[Mma<float>::kidx(s, g, 0)];
   }
 }
 
+// Direct loads of chunk rows [row0, row0 + C) of one head.
 template <typename T, int D, int C>
-__device__ __forceinline__ void issue_chunk(const PrefillArgs& a, int64_t row0, char* st, bool with_q, bool with_lam,
-                                            int wv, int nw, int lane, int LS) {
-  typedef Stage<T, D, C> S;
-  const int64_t rs = (int64_t)a.H * D;
-  if (with_q) tile_load_async<T, C, D>(static_cast<const T*>(a.q) + row0 * D, rs, st + S::QOFF, wv, nw, lane);
-  tile_load_async<T, C, D>(static_cast<const T*>(a.k) + row0 * D, rs, st + S::KOFF, wv, nw, lane);
-  tile_load_async<T, C, D>(static_cast<const T*>(a.v) + row0 * D, rs, st + S::VOFF, wv, nw, lane);
+__device__ __forceinline__ void issue_rows(const void* src, const PrefillArgs& a, int64_t row0, char* lds, int wv,
+                                           int nw, int lane) {
+  tile_load_async<T, C, D>(static_cast<const T*>(src) + row0 * D, (int64_t)a.H * D, lds, wv, nw, lane);
+}
+
+template <int C>
+__device__ __forceinline__ void issue_gates(const PrefillArgs& a, int64_t row0, float* lds, int wv, int nw, int lane) {
   const float* g = a.g + row0;
-  scatter_load_async(reinterpret_cast<float*>(st + S::GOFF), C, wv, nw, lane,
-                     [&](int f) { return g + (int64_t)f * a.H; });
-  if (with_lam) {
-    // lambda^T[l][r] = lambda[token r][l]
-    const float* lam = a.lam + row0 * a.L;
-    const int64_t ls = (int64_t)a.H * a.L;
-    scatter_load_async(reinterpret_cast<float*>(st + S::LOFF), LS * C, wv, nw, lane,
-                       [&](int f) { return lam + (f % C) * ls + f / C; });
-  }
+  scatter_load_async(lds, C, wv, nw, lane, [&](int f) { return g + (int64_t)f * a.H; });
+}
+
+// lambda rows of the chunk, row-major [C][LS]: consecutive lanes read
+// consecutive floats of one token's level weights.
+// (f / LS uses a multiply-high by ceil(2^32 / LS): exact for f * LS < 2^32.)
+template <int C>
+__device__ __forceinline__ void issue_lambda(const PrefillArgs& a, int64_t row0, float* lds, int LS, unsigned ls_magic,
+                                             int wv, int nw, int lane) {
+  const float* lam = a.lam + row0 * a.L;
+  const int64_t ls = (int64_t)a.H * a.L;
+  scatter_load_async(lds, LS * C, wv, nw, lane, [&](int f) {
+    const int r = (int)__umulhi((unsigned)f, ls_magic);
+    return lam + r * ls + (f - r * LS);
+  });
 }
 
 // ---------------------------------------------------------------------------
 // ll_chunk_state: one workgroup per (block J, head), one wave per 16 state
 // columns.  Writes S[bh, J] (tile layout) and GS[bh, J].
 template <typename T, int D, int C>
+struct StateSmem {
+  typedef Tile<T, C, D> TL;
+  static constexpr int KOFF = 0, VOFF = TL::BYTES, GOFF = 2 * TL::BYTES;
+  static constexpr int STAGE = GOFF + C * 4;
+  static constexpr int WOFF = 2 * STAGE;  // per-wave decay-to-end weights [NW][C]
+  static constexpr int BYTES = WOFF + (D / 16) * C * 4;
+};
+
+template <typename T, int D, int C>
 __global__ void __launch_bounds__(64 * (D / 16)) ll_chunk_state(PrefillArgs a) {
   using M = Mma<T>;
-  typedef Stage<T, D, C> S;
-  typedef Tile<T, C, D> TL;
+  typedef StateSmem<T, D, C> L;
   constexpr int NW = D / 16;
   constexpr int DT = D / 16;
   constexpr int KSC = C / M::KS;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * S::BYTES + TL::BYTES];
-  char* kd = smem + 2 * S::BYTES;  // decayed keys of the current chunk
+  __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g4 = lane >> 4;
+  float* wl = reinterpret_cast<float*>(smem + L::WOFF) + wv * C;
   const int wg = xcd_logical_id(blockIdx.x, gridDim.x);
   const int J = wg % a.nb, bh = wg / a.nb, h = bh % a.H, b = bh / a.H;
   auto row_of = [&](int j) { return ((int64_t)b * a.T + (int64_t)(J * a.P + j) * C) * a.H + h; };
+  auto issue = [&](int j) {
+    char* st = smem + (j & 1) * L::STAGE;
+    issue_rows<T, D, C>(a.k, a, row_of(j), st + L::KOFF, wv, NW, lane);
+    issue_rows<T, D, C>(a.v, a, row_of(j), st + L::VOFF, wv, NW, lane);
+    issue_gates<C>(a, row_of(j), reinterpret_cast<float*>(st + L::GOFF), wv, NW, lane);
+  };
 
   f32x4 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float gblk = 0.f;
 
-  issue_chunk<T, D, C>(a, row_of(0), smem, false, false, wv, NW, lane, 0);
+  issue(0);
   for (int j = 0; j < a.P; ++j) {
-    char* st = smem + (j & 1) * S::BYTES;
+    const char* st = smem + (j & 1) * L::STAGE;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk j have landed
-    __syncthreads();                // every wave's loads have; chunk j-1 is done
-    if (j + 1 < a.P) issue_chunk<T, D, C>(a, row_of(j + 1), smem + ((j + 1) & 1) * S::BYTES, false, false, wv, NW,
-                                          lane, 0);
-    const float gscan = chunk_prefix<C>(reinterpret_cast<const float*>(st + S::GOFF), lane);
+    __syncthreads();                // every wave's have; chunk j-1 is done everywhere
+    if (j + 1 < a.P) issue(j + 1);
+    const float gscan = chunk_prefix<C>(reinterpret_cast<const float*>(st + L::GOFF), lane);
     const float gsum = __shfl(gscan, C - 1, 64);
-    decay_keys<T, D, C, NW>(st + S::KOFF, kd, gscan, wv, lane);
-    __syncthreads();
+    if (lane < C) wl[lane] = __expf(gsum - gscan);
 
+    // H_j[:, cols] = sum_r k_r (w_r v_r)^T, w_r = exp(G[C-1] - G[r])
     typename M::Frag vf[KSC];
 #pragma unroll
-    for (int s = 0; s < KSC; ++s) vf[s] = frag_col<T, C, D>(st + S::VOFF, 16 * wv, s, lane);
+    for (int s = 0; s < KSC; ++s) vf[s] = scale_tokens<T>(frag_col<T, C, D>(st + L::VOFF, 16 * wv, s, lane), wl, s, g4);
     const float carry = __expf(gsum);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       f32x4 x = acc[dt] * carry;
 #pragma unroll
-      for (int s = 0; s < KSC; ++s) x = M::mma(frag_col<T, C, D>(kd, 16 * dt, s, lane), vf[s], x);
+      for (int s = 0; s < KSC; ++s) x = M::mma(frag_col<T, C, D>(st + L::KOFF, 16 * dt, s, lane), vf[s], x);
       acc[dt] = x;
     }
     gblk += gsum;
@@ -161,13 +164,13 @@ __global__ void __launch_bounds__(64 * (D / 16)) ll_chunk_state(PrefillArgs a) {
 }
 
 // Adds diag(alpha) (Q N) to oacc, N given as MFMA B fragments (k = head dim,
-// n = this wave's 16 columns), alpha_r = lamT[lvl][r] * scale for the rows
+// n = this wave's 16 columns), alpha_r = lamT[r] * scale for the rows
 // r = 16*rt + 4*(lane/16) + i this lane holds.
 template <typename T, int D, int C>
 __device__ __forceinline__ void level_read(f32x4 (&oacc)[C / 16],
                                            const typename Mma<T>::Frag (&qf)[C / 16][D / Mma<T>::KS],
                                            const typename Mma<T>::Frag (&nf)[D / Mma<T>::KS], const float* lamT,
-                                           int lvl, float scale, int g4) {
+                                           float scale, int g4) {
   using M = Mma<T>;
   constexpr int CT = C / 16, KSD = D / M::KS;
 #pragma unroll
@@ -175,7 +178,7 @@ __device__ __forceinline__ void level_read(f32x4 (&oacc)[C / 16],
     f32x4 tmp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KSD; ++s) tmp = M::mma(qf[rt][s], nf[s], tmp);
-    const f32x4 al = *reinterpret_cast<const f32x4*>(lamT + lvl * C + 16 * rt + 4 * g4);
+    const f32x4 al = *reinterpret_cast<const f32x4*>(lamT + 16 * rt + 4 * g4);
     oacc[rt] += (al * scale) * tmp;
   }
 }
@@ -192,45 +195,88 @@ __device__ __forceinline__ void node_frags(typename Mma<T>::Frag (&nf)[D / Mma<T
   for (int s = 0; s < KSD; ++s) nf[s] = M::acc_frag(t, s);
 }
 
+// Dynamic LDS layout of ll_chunk_attn (byte offsets; LS = staged levels).
+template <typename T, int D, int C, int MAXH, bool QDB>
+struct AttnLayout {
+  typedef Tile<T, C, D> TL;
+  typedef Tile<T, C, C> PT;
+  static constexpr int NW = D / 16;
+  static constexpr int LOGC = (C == 16) ? 4 : (C == 32) ? 5 : 6;
+  static constexpr int FRAG_BYTES = 64 * (int)sizeof(typename Mma<T>::Frag);
+  static constexpr int NODE_BYTES = NW * (D / Mma<T>::KS) * FRAG_BYTES;
+  int k, v, lraw, g, stage;  // per-stage offsets and stage size
+  int q, p, lt, gw, h, total;  // q: in the stage when double-buffered (QDB)
+  __host__ __device__ explicit AttnLayout(int LS) {
+    k = 0;
+    v = k + TL::BYTES;
+    g = v + TL::BYTES;
+    lraw = g + C * 4;                      // lambda rows [C][LS]
+    stage = lraw + ((C * LS * 4 + 15) & ~15);
+    if (QDB) {
+      q = stage;
+      stage += TL::BYTES;
+      p = 2 * stage;
+    } else {
+      q = 2 * stage;                       // single q tile, refilled after the mid-chunk barrier
+      p = q + TL::BYTES;
+    }
+    // p: masked scores [C][C]
+    lt = p + PT::BYTES;                    // inter-chunk lambda^T, scaled [LS-LOGC-1][C]
+    const int nlt = LS > LOGC + 1 ? LS - LOGC - 1 : 0;
+    gw = lt + nlt * C * 4;                 // per-wave G and decay-to-end [NW][2][C]
+    h = gw + NW * 2 * C * 4;               // MAXH nodes as B fragments
+    total = h + MAXH * NODE_BYTES;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // ll_chunk_attn: one workgroup per (block J, head); wave wv owns output
 // columns [16 wv, 16 wv + 16); the P chunks of the block are visited in order.
 // The Fenwick nodes of earlier blocks are the same for every chunk of the
 // block: up to MAXH of them are converted once into MFMA B fragments in LDS,
 // any further ones are read from the workspace per chunk.
-template <typename T, int D, int C, int MAXB, int MAXH>
-__global__ void __launch_bounds__(64 * (D / 16)) __attribute__((amdgpu_waves_per_eu(2, 2))) ll_chunk_attn(PrefillArgs a) {
+template <typename T, int D, int C, int MAXB, int MAXH, bool QDB>
+__global__ void __launch_bounds__(64 * (D / 16)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+ll_chunk_attn(PrefillArgs a) {
   using M = Mma<T>;
   typedef typename M::Frag Frag;
-  typedef Stage<T, D, C> S;
-  typedef Tile<T, C, D> TL;
-  typedef Tile<T, C, C> PT;  // masked scores P[r][s]
+  typedef AttnLayout<T, D, C, MAXH, QDB> Lay;
+  typedef Tile<T, C, C> PT;
   constexpr int NW = D / 16;
   constexpr int DT = D / 16, CT = C / 16;
   constexpr int KSD = D / M::KS, KSC = C / M::KS;
-  constexpr int LOGC = (C == 16) ? 4 : (C == 32) ? 5 : 6;
-  constexpr int FRAG_BYTES = 64 * (int)sizeof(Frag);     // one fragment of one wave
-  constexpr int NODE_BYTES = NW * KSD * FRAG_BYTES;       // one node, every wave's columns
-  constexpr int HOFF = 2 * S::BYTES + TL::BYTES + PT::BYTES;
-  constexpr int GOFF = HOFF + (MAXH > 0 ? MAXH : 0) * NODE_BYTES;
-  __shared__ __attribute__((aligned(1024))) char smem[GOFF + NW * C * 4];
-  char* kd = smem + 2 * S::BYTES;
-  char* pt = kd + TL::BYTES;
-  char* hbuf = smem + HOFF;
+  constexpr int LOGC = Lay::LOGC;
+  constexpr int FRAG_BYTES = Lay::FRAG_BYTES;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
 
+  const int LS = a.LS;
+  const unsigned ls_magic = (unsigned)((0x100000000ull + LS - 1) / LS);
+  const Lay lay(LS);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g4 = lane >> 4, q16 = lane & 15;
-  float* gl = reinterpret_cast<float*>(smem + GOFF) + wv * C;  // this wave's copy of G
+  float* gl = reinterpret_cast<float*>(smem + lay.gw) + wv * 2 * C;  // this wave's G
+  float* wl = gl + C;                                                // and exp(G[C-1] - G)
+  float* lt = reinterpret_cast<float*>(smem + lay.lt);
+  char* pt = smem + lay.p;
+  char* hbuf = smem + lay.h;
   const int wg = xcd_logical_id(blockIdx.x, gridDim.x);
   const int J = wg % a.nb, bh = wg / a.nb, h = bh % a.H, b = bh / a.H;
   const int logP = ilog2c(a.P);
-  const int LS = a.LS;
   auto row_of = [&](int j) { return ((int64_t)b * a.T + (int64_t)(J * a.P + j) * C) * a.H + h; };
   auto node_of = [&](int e) {
     return (e & 1) ? a.F + ((int64_t)bh * a.nF + (e >> 1)) * D * D : a.S + ((int64_t)bh * a.nb + e) * D * D;
   };
   auto gamma_of = [&](int e) { return (e & 1) ? a.GF[(int64_t)bh * a.nF + (e >> 1)] : a.GS[(int64_t)bh * a.nb + e]; };
+  auto issue_kvl = [&](int j) {
+    char* st = smem + (j & 1) * lay.stage;
+    issue_rows<T, D, C>(a.k, a, row_of(j), st + lay.k, wv, NW, lane);
+    issue_rows<T, D, C>(a.v, a, row_of(j), st + lay.v, wv, NW, lane);
+    issue_gates<C>(a, row_of(j), reinterpret_cast<float*>(st + lay.g), wv, NW, lane);
+    issue_lambda<C>(a, row_of(j), reinterpret_cast<float*>(st + lay.lraw), LS, ls_magic, wv, NW, lane);
+    if (QDB) issue_rows<T, D, C>(a.q, a, row_of(j), st + lay.q, wv, NW, lane);
+  };
 
-  issue_chunk<T, D, C>(a, row_of(0), smem, true, true, wv, NW, lane, LS);
+  issue_kvl(0);
+  if (!QDB) issue_rows<T, D, C>(a.q, a, row_of(0), smem + lay.q, wv, NW, lane);
 
   // masked-score tiles above the diagonal are never written: keep them zero
   for (int x = tid * 16; x < PT::BYTES; x += 64 * NW * 16) *reinterpret_cast<uint4*>(pt + x) = uint4{0, 0, 0, 0};
@@ -259,22 +305,25 @@ __global__ void __launch_bounds__(64 * (D / 16)) __attribute__((amdgpu_waves_per
   float gw = 0.f;  // log-decay from the start of block J to the current chunk
 
   for (int j = 0; j < a.P; ++j) {
-    char* st = smem + (j & 1) * S::BYTES;
-    const float* lamT = reinterpret_cast<const float*>(st + S::LOFF);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (j + 1 < a.P)
-      issue_chunk<T, D, C>(a, row_of(j + 1), smem + ((j + 1) & 1) * S::BYTES, true, true, wv, NW, lane, LS);
+    const char* st = smem + (j & 1) * lay.stage;
+    const float* lraw = reinterpret_cast<const float*>(st + lay.lraw);
+    const char* qt = QDB ? st + lay.q : smem + lay.q;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk j (and q) have landed
+    lds_barrier();                  // every wave's have; chunk j-1 is done everywhere
+    if (j + 1 < a.P) issue_kvl(j + 1);
 
-    const float gscan = chunk_prefix<C>(reinterpret_cast<const float*>(st + S::GOFF), lane);
-    if (lane < C) gl[lane] = gscan;
+    const float gscan = chunk_prefix<C>(reinterpret_cast<const float*>(st + lay.g), lane);
     const float gsum = __shfl(gscan, C - 1, 64);
+    if (lane < C) {
+      gl[lane] = gscan;
+      wl[lane] = __expf(gsum - gscan);
+    }
 
     Frag qf[CT][KSD];
 #pragma unroll
     for (int rt = 0; rt < CT; ++rt)
 #pragma unroll
-      for (int s = 0; s < KSD; ++s) qf[rt][s] = frag_row<T, C, D>(st + S::QOFF, 16 * rt + q16, s, g4);
+      for (int s = 0; s < KSD; ++s) qf[rt][s] = frag_row<T, C, D>(qt, 16 * rt + q16, s, g4);
 
     // --- intra-chunk scores, this wave's share of the causal tiles:
     // P[r][s] = (q_r . k_s) lambda_r^(lev(r,s)) exp(G[r] - G[s]), s <= r
@@ -285,7 +334,7 @@ __global__ void __launch_bounds__(64 * (D / 16)) __attribute__((amdgpu_waves_per
         if ((rt * (rt + 1) / 2 + ct) % NW != wv) continue;
         f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KSD; ++s) x = M::mma(frag_row<T, C, D>(st + S::KOFF, 16 * ct + q16, s, g4), qf[rt][s], x);
+        for (int s = 0; s < KSD; ++s) x = M::mma(frag_row<T, C, D>(st + lay.k, 16 * ct + q16, s, g4), qf[rt][s], x);
         const int r = 16 * rt + q16;
         const float gr = gl[r];
         const f32x4 gs = *reinterpret_cast<const f32x4*>(gl + 16 * ct + 4 * g4);
@@ -296,7 +345,7 @@ __global__ void __launch_bounds__(64 * (D / 16)) __attribute__((amdgpu_waves_per
           float val = 0.f;
           if (src <= r) {
             const int lev = (src == r) ? 0 : 32 - __clz(r ^ src);
-            val = x[i] * lamT[lev * C + r] * __expf(gr - gs[i]);
+            val = x[i] * lraw[r * LS + lev] * __expf(gr - gs[i]);
           }
           pv[i] = val;
         }
@@ -308,16 +357,18 @@ __global__ void __launch_bounds__(64 * (D / 16)) __attribute__((amdgpu_waves_per
         }
       }
 
-    // --- decayed keys for this chunk's state, and lambda of the inter-chunk
-    // levels pre-multiplied by exp(G[r]) (in place; levels <= log2 C untouched)
-    decay_keys<T, D, C, NW>(st + S::KOFF, kd, gscan, wv, lane);
+    // --- lambda of the inter-chunk levels, transposed to [level][r] and
+    // pre-multiplied by exp(G[r])
     {
-      float* lw = reinterpret_cast<float*>(st + S::LOFF);
       const float eg = __expf(gl[lane & (C - 1)]);
       const int n = (LS - LOGC - 1) * C;
-      for (int x = tid; x < n; x += 64 * NW) lw[(LOGC + 1) * C + x] *= eg;
+      for (int x = tid; x < n; x += 64 * NW) {
+        const int l = LOGC + 1 + x / C, r = x % C;
+        lt[x] = lraw[r * LS + l] * eg;
+      }
     }
-    __syncthreads();
+    lds_barrier();  // P and lambda^T visible; the loads of chunk j+1 keep flying
+    if (!QDB && j + 1 < a.P) issue_rows<T, D, C>(a.q, a, row_of(j + 1), smem + lay.q, wv, NW, lane);
 
     f32x4 oacc[CT];
 #pragma unroll
@@ -330,7 +381,7 @@ __global__ void __launch_bounds__(64 * (D / 16)) __attribute__((amdgpu_waves_per
         Frag nf[KSD];
 #pragma unroll
         for (int s = 0; s < KSD; ++s) nf[s] = M::acc_frag(nst[m - 1], s);
-        level_read<T, D, C>(oacc, qf, nf, lamT, LOGC + m, __expf(sig[m]), g4);
+        level_read<T, D, C>(oacc, qf, nf, lt + (m - 1) * C, __expf(sig[m]), g4);
       }
     }
 
@@ -349,7 +400,7 @@ __global__ void __launch_bounds__(64 * (D / 16)) __attribute__((amdgpu_waves_per
         } else {
           node_frags<T, D>(nf, node_of(e), wv, lane);
         }
-        level_read<T, D, C>(oacc, qf, nf, lamT, LOGC + logP + l + 1, __expf(gw + dd), g4);
+        level_read<T, D, C>(oacc, qf, nf, lt + (logP + l) * C, __expf(gw + dd), g4);
         dd += gamma_of(e);
         rest &= rest - 1;
       }
@@ -358,7 +409,7 @@ __global__ void __launch_bounds__(64 * (D / 16)) __attribute__((amdgpu_waves_per
     // --- intra-chunk: O += P V for this wave's columns
     Frag vf[KSC];
 #pragma unroll
-    for (int s = 0; s < KSC; ++s) vf[s] = frag_col<T, C, D>(st + S::VOFF, 16 * wv, s, lane);
+    for (int s = 0; s < KSC; ++s) vf[s] = frag_col<T, C, D>(st + lay.v, 16 * wv, s, lane);
 #pragma unroll
     for (int rt = 0; rt < CT; ++rt)
 #pragma unroll
@@ -382,12 +433,14 @@ __global__ void __launch_bounds__(64 * (D / 16)) __attribute__((amdgpu_waves_per
     for (int m = 1; m <= MAXB; ++m) sig[m] += gsum;
     gw += gsum;
     if (j + 1 < a.P) {
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) vf[s] = scale_tokens<T>(vf[s], wl, s, g4);
       f32x4 merged[DT];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KSC; ++s) x = M::mma(frag_col<T, C, D>(kd, 16 * dt, s, lane), vf[s], x);
+        for (int s = 0; s < KSC; ++s) x = M::mma(frag_col<T, C, D>(st + lay.k, 16 * dt, s, lane), vf[s], x);
         merged[dt] = x;
       }
       const int c = __ffs(j + 1) - 1;
@@ -421,10 +474,20 @@ static hipError_t launch_state_t(const PrefillArgs& a, hipStream_t s) {
 
 template <typename T, int D, int C>
 static hipError_t launch_attn_t(const PrefillArgs& a, hipStream_t s) {
-  const int grid = a.B * a.H * a.nb;
-  // node fragments kept in LDS: bf16 heads up to 64 (8 KB per node at d=64)
+  // node fragments kept in LDS (bf16 heads up to 64: 8 KB per node at d=64)
   constexpr int MAXH = 0;
-  hipLaunchKernelGGL((ll_chunk_attn<T, D, C, max_block_depth(D), MAXH>), dim3(grid), dim3(64 * (D / 16)), 0, s, a);
+  constexpr bool QDB = false;
+  auto kern = ll_chunk_attn<T, D, C, max_block_depth(D), MAXH, QDB>;
+  const AttnLayout<T, D, C, MAXH, QDB> lay(a.LS);
+  static int configured = 0;  // dynamic LDS above 64 KiB must be allowed per kernel
+  if (lay.total > configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lay.total);
+    if (e != hipSuccess) return e;
+    configured = lay.total;
+  }
+  const int grid = a.B * a.H * a.nb;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * (D / 16)), lay.total, s, a);
   return hipGetLastError();
 }
 

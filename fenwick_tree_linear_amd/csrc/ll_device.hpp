@@ -31,6 +31,15 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ int ilog2c(int x) { return 31 - __clz(x); }
 
+// Workgroup barrier that orders LDS accesses only.  Unlike __syncthreads()
+// it does not wait for this wave's outstanding global loads, so direct
+// global->LDS loads of the next chunk stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <typename T>
 struct Mma;
 
