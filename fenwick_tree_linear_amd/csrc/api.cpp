@@ -88,6 +88,9 @@ ll_status plan_prefill(const ll_problem* p, bool exporting, Plan* out) {
     return fail(LL_ERR_UNSUPPORTED, "head size %d not supported for %s io", p->dk, p->io == LL_BF16 ? "bf16" : "fp32");
   if (!supported_chunk(p->C, p->io))
     return fail(LL_ERR_UNSUPPORTED, "chunk size C=%d not supported for %s io", p->C, p->io == LL_BF16 ? "bf16" : "fp32");
+  if ((size_t)p->C * p->dk * (p->io == LL_BF16 ? 2 : 4) > (size_t)llattn::kAttnTileBytesMax)
+    return fail(LL_ERR_UNSUPPORTED, "a chunk tile of C=%d x d=%d %s values exceeds %d bytes", p->C, p->dk,
+                p->io == LL_BF16 ? "bf16" : "fp32", llattn::kAttnTileBytesMax);
   if (need > llattn::kLevelsMax)
     return fail(LL_ERR_UNSUPPORTED, "T=%d needs %d levels; at most %d are supported", p->T, need, llattn::kLevelsMax);
   if ((int64_t)p->B * p->H * (p->T / p->C) > ((int64_t)1 << 31) - 1)

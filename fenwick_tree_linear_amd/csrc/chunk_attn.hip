@@ -22,6 +22,8 @@
 // over tokens (V, and K for the state) are read with the transposing LDS
 // read, and the per-token decay of the state update is applied to the V
 // fragments in registers, so no transposed or rescaled tile is ever written.
+#include <type_traits>
+
 #include "ll_device.hpp"
 #include "ll_launch.hpp"
 
@@ -115,7 +117,7 @@ __global__ void __launch_bounds__(64 * (D / 16)) ll_chunk_state(PrefillArgs a) {
   constexpr int KSC = C / M::KS;
   __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g4 = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6), g4 = lane >> 4;
   float* wl = reinterpret_cast<float*>(smem + L::WOFF) + wv * C;
   const int wg = xcd_logical_id(blockIdx.x, gridDim.x);
   const int J = wg % a.nb, bh = wg / a.nb, h = bh % a.H, b = bh / a.H;
@@ -143,15 +145,22 @@ __global__ void __launch_bounds__(64 * (D / 16)) ll_chunk_state(PrefillArgs a) {
     if (lane < C) wl[lane] = __expf(gsum - gscan);
 
     // H_j[:, cols] = sum_r k_r (w_r v_r)^T, w_r = exp(G[C-1] - G[r])
-    typename M::Frag vf[KSC];
+    typename M::Frag vf[KSC], kf[DT][KSC];
 #pragma unroll
-    for (int s = 0; s < KSC; ++s) vf[s] = scale_tokens<T>(frag_col<T, C, D>(st + L::VOFF, 16 * wv, s, lane), wl, s, g4);
+    for (int s = 0; s < KSC; ++s) vf[s] = frag_col<T, C, D>(st + L::VOFF, 16 * wv, s, lane);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) kf[dt][s] = frag_col<T, C, D>(st + L::KOFF, 16 * dt, s, lane);
+    lds_wait(vf, kf);
+#pragma unroll
+    for (int s = 0; s < KSC; ++s) vf[s] = scale_tokens<T>(vf[s], wl, s, g4);
     const float carry = __expf(gsum);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       f32x4 x = acc[dt] * carry;
 #pragma unroll
-      for (int s = 0; s < KSC; ++s) x = M::mma(frag_col<T, C, D>(st + L::KOFF, 16 * dt, s, lane), vf[s], x);
+      for (int s = 0; s < KSC; ++s) x = M::mma(kf[dt][s], vf[s], x);
       acc[dt] = x;
     }
     gblk += gsum;
@@ -163,101 +172,99 @@ __global__ void __launch_bounds__(64 * (D / 16)) ll_chunk_state(PrefillArgs a) {
   if (tid == 0) a.GS[(int64_t)bh * a.nb + J] = gblk;
 }
 
-// Adds diag(alpha) (Q N) to oacc, N given as MFMA B fragments (k = head dim,
-// n = this wave's 16 columns), alpha_r = lamT[r] * scale for the rows
-// r = 16*rt + 4*(lane/16) + i this lane holds.
-template <typename T, int D, int C>
-__device__ __forceinline__ void level_read(f32x4 (&oacc)[C / 16],
-                                           const typename Mma<T>::Frag (&qf)[C / 16][D / Mma<T>::KS],
-                                           const typename Mma<T>::Frag (&nf)[D / Mma<T>::KS], const float* lamT,
-                                           float scale, int g4) {
-  using M = Mma<T>;
-  constexpr int CT = C / 16, KSD = D / M::KS;
-#pragma unroll
-  for (int rt = 0; rt < CT; ++rt) {
-    f32x4 tmp = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KSD; ++s) tmp = M::mma(qf[rt][s], nf[s], tmp);
-    const f32x4 al = *reinterpret_cast<const f32x4*>(lamT + 16 * rt + 4 * g4);
-    oacc[rt] += (al * scale) * tmp;
-  }
-}
-
+// MFMA A fragments (row = state column n of this wave's 16, k = head dim d)
+// of a dk x dv state stored in tile layout.
 template <typename T, int D>
-__device__ __forceinline__ void node_frags(typename Mma<T>::Frag (&nf)[D / Mma<T>::KS], const float* node, int wv,
+__device__ __forceinline__ void node_frags(typename Mma<T>::Frag (&nf)[D / Mma<T>::KS], const float* node, int wc,
                                            int lane) {
   using M = Mma<T>;
   constexpr int DT = D / 16, KSD = D / M::KS;
   f32x4 t[DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) t[dt] = *reinterpret_cast<const f32x4*>(node + state_tile_offset<D>(dt, wv, lane));
+  for (int dt = 0; dt < DT; ++dt) t[dt] = *reinterpret_cast<const f32x4*>(node + state_tile_offset<D>(dt, wc, lane));
 #pragma unroll
   for (int s = 0; s < KSD; ++s) nf[s] = M::acc_frag(t, s);
 }
 
-// Dynamic LDS layout of ll_chunk_attn (byte offsets; LS = staged levels).
-template <typename T, int D, int C, int MAXH, bool QDB>
+// Wave arrangement of ll_chunk_attn: D/16 column tiles x RH row groups
+// (at most 8 waves, so that each keeps up to 256 registers).  With two row
+// groups, group wr takes row tiles wr and CT-1-wr, so both get the same
+// share of the causal triangle.
+template <int D, int C>
+struct AttnWaves {
+  static constexpr int NCT = D / 16;                        // output column tiles
+  static constexpr int CT = C / 16;                         // 16-row tiles of a chunk
+  static constexpr int RH = (CT >= 2 && NCT <= 4) ? 2 : 1;  // row groups
+  static constexpr int NRT = CT / RH;                       // row tiles per wave
+  static constexpr int NW = NCT * RH;                       // waves per workgroup
+  static_assert(RH == 1 || NRT <= 2, "row pairing covers up to four row tiles");
+  __host__ __device__ static constexpr int row_tile(int i, int wr) {
+    return RH == 1 ? i : ((i & 1) ? CT - 1 - wr : wr);
+  }
+};
+
+// Dynamic LDS layout of ll_chunk_attn (byte offsets; LS = staged levels):
+// three staging buffers of chunk tiles, two buffers of masked scores and two
+// of decay-scaled keys (chunk parity), and per-wave prefix arrays.
+template <typename T, int D, int C>
 struct AttnLayout {
   typedef Tile<T, C, D> TL;
   typedef Tile<T, C, C> PT;
-  static constexpr int NW = D / 16;
-  static constexpr int LOGC = (C == 16) ? 4 : (C == 32) ? 5 : 6;
-  static constexpr int FRAG_BYTES = 64 * (int)sizeof(typename Mma<T>::Frag);
-  static constexpr int NODE_BYTES = NW * (D / Mma<T>::KS) * FRAG_BYTES;
-  int k, v, lraw, g, stage;  // per-stage offsets and stage size
-  int q, p, lt, gw, h, total;  // q: in the stage when double-buffered (QDB)
+  static constexpr int NS = 3;
+  int q, k, v, g, lraw, stage;  // per-stage offsets and stage size
+  int p, kw, gw, total;
   __host__ __device__ explicit AttnLayout(int LS) {
-    k = 0;
+    q = 0;
+    k = q + TL::BYTES;
     v = k + TL::BYTES;
     g = v + TL::BYTES;
-    lraw = g + C * 4;                      // lambda rows [C][LS]
-    stage = lraw + ((C * LS * 4 + 15) & ~15);
-    if (QDB) {
-      q = stage;
-      stage += TL::BYTES;
-      p = 2 * stage;
-    } else {
-      q = 2 * stage;                       // single q tile, refilled after the mid-chunk barrier
-      p = q + TL::BYTES;
-    }
-    // p: masked scores [C][C]
-    lt = p + PT::BYTES;                    // inter-chunk lambda^T, scaled [LS-LOGC-1][C]
-    const int nlt = LS > LOGC + 1 ? LS - LOGC - 1 : 0;
-    gw = lt + nlt * C * 4;                 // per-wave G and decay-to-end [NW][2][C]
-    h = gw + NW * 2 * C * 4;               // MAXH nodes as B fragments
-    total = h + MAXH * NODE_BYTES;
+    lraw = g + C * 4;  // lambda rows [C][LS]
+    stage = (lraw + C * LS * 4 + 255) & ~255;
+    p = NS * stage;             // masked scores P[r][s], [2][C][C]
+    kw = p + 2 * PT::BYTES;     // K with rows scaled by e^{G[C-1] - G_s}, [2][C][D]
+    gw = kw + 2 * TL::BYTES;    // per wave and chunk parity: G, e^{G[C-1]-G}, e^{G[tile end]-G}
+    total = gw + AttnWaves<D, C>::NW * 2 * 3 * C * 4;
   }
 };
 
 // ---------------------------------------------------------------------------
-// ll_chunk_attn: one workgroup per (block J, head); wave wv owns output
-// columns [16 wv, 16 wv + 16); the P chunks of the block are visited in order.
-// The Fenwick nodes of earlier blocks are the same for every chunk of the
-// block: up to MAXH of them are converted once into MFMA B fragments in LDS,
+// ll_chunk_attn: one workgroup per (block J, head) with D/16 x RH waves: wave
+// (wc, wr) owns output columns [16 wc, 16 wc + 16) of NRT row tiles.  The P
+// chunks of the block are visited in order as a pipeline: while chunk j is
+// read out, the workgroup prepares chunk j+1 (its masked in-chunk scores and
+// its decay-scaled keys, each tile made once) and chunk j+2 is in flight
+// from HBM.  One barrier per chunk hands all of it over.
+//
+// Every product is formed transposed, O^T[n][r]: a lane then holds one token
+// row r and four output columns, so the per-row weights lambda_r^l e^{G_r}
+// are per-lane scalars and the output leaves as 4-element vector stores.  The
+// Fenwick nodes of earlier blocks are the same for every chunk of the block:
+// up to MAXH of them stay in registers as MFMA fragments for the whole block,
 // any further ones are read from the workspace per chunk.
-template <typename T, int D, int C, int MAXB, int MAXH, bool QDB>
-__global__ void __launch_bounds__(64 * (D / 16)) __attribute__((amdgpu_waves_per_eu(2, 2)))
-ll_chunk_attn(PrefillArgs a) {
+template <typename T, int D, int C, int MAXB, int MAXH>
+__global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(PrefillArgs a) {
   using M = Mma<T>;
   typedef typename M::Frag Frag;
-  typedef AttnLayout<T, D, C, MAXH, QDB> Lay;
+  typedef AttnLayout<T, D, C> Lay;
+  typedef AttnWaves<D, C> W;
+  typedef Tile<T, C, D> TL;
   typedef Tile<T, C, C> PT;
-  constexpr int NW = D / 16;
-  constexpr int DT = D / 16, CT = C / 16;
+  typedef typename std::conditional<sizeof(T) == 2, bf16x4, f32x4>::type Vec4;  // 4 values of T
+  constexpr int NW = W::NW, NCT = W::NCT, NRT = W::NRT, CT = W::CT;
+  constexpr int DT = D / 16;
   constexpr int KSD = D / M::KS, KSC = C / M::KS;
-  constexpr int LOGC = Lay::LOGC;
-  constexpr int FRAG_BYTES = Lay::FRAG_BYTES;
+  constexpr int LOGC = (C == 16) ? 4 : (C == 32) ? 5 : 6;
+  constexpr int NS = Lay::NS;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int LS = a.LS;
   const unsigned ls_magic = (unsigned)((0x100000000ull + LS - 1) / LS);
   const Lay lay(LS);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g4 = lane >> 4, q16 = lane & 15;
-  float* gl = reinterpret_cast<float*>(smem + lay.gw) + wv * 2 * C;  // this wave's G
-  float* wl = gl + C;                                                // and exp(G[C-1] - G)
-  float* lt = reinterpret_cast<float*>(smem + lay.lt);
-  char* pt = smem + lay.p;
-  char* hbuf = smem + lay.h;
+  // the wave index is made a scalar so that every branch on it is a uniform
+  // jump: an MFMA must never sit under a partial or empty EXEC mask
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, q16 = lane & 15;
+  const int wc = wv % NCT, wr = wv / NCT;
   const int wg = xcd_logical_id(blockIdx.x, gridDim.x);
   const int J = wg % a.nb, bh = wg / a.nb, h = bh % a.H, b = bh / a.H;
   const int logP = ilog2c(a.P);
@@ -266,201 +273,302 @@ ll_chunk_attn(PrefillArgs a) {
     return (e & 1) ? a.F + ((int64_t)bh * a.nF + (e >> 1)) * D * D : a.S + ((int64_t)bh * a.nb + e) * D * D;
   };
   auto gamma_of = [&](int e) { return (e & 1) ? a.GF[(int64_t)bh * a.nF + (e >> 1)] : a.GS[(int64_t)bh * a.nb + e]; };
-  auto issue_kvl = [&](int j) {
-    char* st = smem + (j & 1) * lay.stage;
+  auto stage_of = [&](int j) { return smem + (j % NS) * lay.stage; };
+  // this wave's prefix arrays for chunk parity p: G, e^{G[C-1]-G}, e^{G[end of 16-token tile]-G}
+  auto garr = [&](int j) { return reinterpret_cast<float*>(smem + lay.gw) + (wv * 2 + (j & 1)) * 3 * C; };
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    char* st = stage_of(j);
+    issue_rows<T, D, C>(a.q, a, row_of(j), st + lay.q, wv, NW, lane);
     issue_rows<T, D, C>(a.k, a, row_of(j), st + lay.k, wv, NW, lane);
     issue_rows<T, D, C>(a.v, a, row_of(j), st + lay.v, wv, NW, lane);
     issue_gates<C>(a, row_of(j), reinterpret_cast<float*>(st + lay.g), wv, NW, lane);
     issue_lambda<C>(a, row_of(j), reinterpret_cast<float*>(st + lay.lraw), LS, ls_magic, wv, NW, lane);
-    if (QDB) issue_rows<T, D, C>(a.q, a, row_of(j), st + lay.q, wv, NW, lane);
   };
 
-  issue_kvl(0);
-  if (!QDB) issue_rows<T, D, C>(a.q, a, row_of(0), smem + lay.q, wv, NW, lane);
-
-  // masked-score tiles above the diagonal are never written: keep them zero
-  for (int x = tid * 16; x < PT::BYTES; x += 64 * NW * 16) *reinterpret_cast<uint4*>(pt + x) = uint4{0, 0, 0, 0};
-
-  // the first MAXH nodes (most recent first) as B fragments of each wave's columns
-  if constexpr (MAXH > 0) {
-    int rest = J;
-    for (int x = 0; x < MAXH && rest > 0; ++x) {
-      Frag nf[KSD];
-      node_frags<T, D>(nf, node_of(rest - 1), wv, lane);
-#pragma unroll
-      for (int s = 0; s < KSD; ++s)
-        *reinterpret_cast<Frag*>(hbuf + ((x * NW + wv) * KSD + s) * FRAG_BYTES + lane * (int)sizeof(Frag)) = nf[s];
-      rest &= rest - 1;
-    }
-  }
-
-  f32x4 nst[MAXB][DT];
-  float sig[MAXB + 1];
-#pragma unroll
-  for (int m = 0; m < MAXB; ++m)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) nst[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int m = 0; m <= MAXB; ++m) sig[m] = 0.f;
-  float gw = 0.f;  // log-decay from the start of block J to the current chunk
-
-  for (int j = 0; j < a.P; ++j) {
-    const char* st = smem + (j & 1) * lay.stage;
+  // Prepares chunk j for its read-out: the in-chunk prefix G of the log-gates
+  // (every wave keeps its own copy), the masked scores
+  // P[r][s] = (q_r . k_s) lambda_r^(lev(r,s)) e^{G_r - G_s} for s <= r (each
+  // 16x16 tile made by one wave) and the keys scaled by e^{G[C-1] - G_s}.
+  // Below the diagonal the decay splits at the end e of the source tile,
+  // e^{G_r - G_e} e^{G_e - G_s}: both factors are at most one.
+  auto prepare = [&](int j) __attribute__((always_inline)) {
+    const char* st = stage_of(j);
     const float* lraw = reinterpret_cast<const float*>(st + lay.lraw);
-    const char* qt = QDB ? st + lay.q : smem + lay.q;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk j (and q) have landed
-    lds_barrier();                  // every wave's have; chunk j-1 is done everywhere
-    if (j + 1 < a.P) issue_kvl(j + 1);
-
+    float* gl = garr(j);
+    float* wl = gl + C;
+    float* es = wl + C;
     const float gscan = chunk_prefix<C>(reinterpret_cast<const float*>(st + lay.g), lane);
     const float gsum = __shfl(gscan, C - 1, 64);
+    const float gend = __shfl(gscan, lane | 15, 64);
     if (lane < C) {
       gl[lane] = gscan;
       wl[lane] = __expf(gsum - gscan);
+      es[lane] = __expf(gend - gscan);
     }
-
-    Frag qf[CT][KSD];
+    char* pt = smem + lay.p + (j & 1) * PT::BYTES;
 #pragma unroll
     for (int rt = 0; rt < CT; ++rt)
 #pragma unroll
-      for (int s = 0; s < KSD; ++s) qf[rt][s] = frag_row<T, C, D>(qt, 16 * rt + q16, s, g4);
-
-    // --- intra-chunk scores, this wave's share of the causal tiles:
-    // P[r][s] = (q_r . k_s) lambda_r^(lev(r,s)) exp(G[r] - G[s]), s <= r
-#pragma unroll
-    for (int rt = 0; rt < CT; ++rt)
-#pragma unroll
-      for (int ct = 0; ct <= rt; ++ct) {  // ct: source tile (column of P)
+      for (int ct = 0; ct <= rt; ++ct) {
         if ((rt * (rt + 1) / 2 + ct) % NW != wv) continue;
+        const int r = 16 * rt + q16;  // lane: row r, sources 16 ct + 4 (lane/16) .. + 3
         f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KSD; ++s) x = M::mma(frag_row<T, C, D>(st + lay.k, 16 * ct + q16, s, g4), qf[rt][s], x);
-        const int r = 16 * rt + q16;
+        for (int s = 0; s < KSD; ++s)
+          x = M::mma(frag_row<T, C, D>(st + lay.k, 16 * ct + q16, s, g4), frag_row<T, C, D>(st + lay.q, r, s, g4), x);
+        const float* lr = lraw + r * LS;
         const float gr = gl[r];
-        const f32x4 gs = *reinterpret_cast<const f32x4*>(gl + 16 * ct + 4 * g4);
-        float pv[4];
+        f32x4 pv;
+        if (ct < rt) {  // one level for the whole row: 4 + bit_length(rt ^ ct)
+          const float w = lr[4 + 32 - __clz(rt ^ ct)] * __expf(gr - gl[16 * ct + 15]);
+          pv = x * w * *reinterpret_cast<const f32x4*>(es + 16 * ct + 4 * g4);
+        } else {
+          const f32x4 gs = *reinterpret_cast<const f32x4*>(gl + 16 * ct + 4 * g4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int src = 16 * ct + 4 * g4 + i;
-          float val = 0.f;
-          if (src <= r) {
-            const int lev = (src == r) ? 0 : 32 - __clz(r ^ src);
-            val = x[i] * lraw[r * LS + lev] * __expf(gr - gs[i]);
+          for (int e = 0; e < 4; ++e) {
+            const int src = 4 * g4 + e;  // source position inside the tile; the row is q16
+            pv[e] = (src <= q16) ? x[e] * lr[32 - __clz(q16 ^ src)] * __expf(gr - gs[e]) : 0.f;
           }
-          pv[i] = val;
         }
-        char* dst = pt + PT::off(r, 16 * ct + 4 * g4);
-        if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<bf16x4*>(dst) = bf16x4{(bf16)pv[0], (bf16)pv[1], (bf16)pv[2], (bf16)pv[3]};
-        } else {
-          *reinterpret_cast<f32x4*>(dst) = f32x4{pv[0], pv[1], pv[2], pv[3]};
+        Vec4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = (T)pv[e];
+        *reinterpret_cast<Vec4*>(pt + PT::off(r, 16 * ct + 4 * g4)) = out;
+      }
+    // decay-scaled keys: the same swizzled positions, each 16-byte piece of a
+    // row scaled by that row's weight
+    char* kw = smem + lay.kw + (j & 1) * TL::BYTES;
+    constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte piece
+    for (int x = tid; x < TL::BYTES / 16; x += 64 * NW) {
+      const int row = x / TL::NCH;
+      const float w = wl[row];
+      const Vec4* src = reinterpret_cast<const Vec4*>(st + lay.k + x * 16);
+      Vec4* dst = reinterpret_cast<Vec4*>(kw + x * 16);
+#pragma unroll
+      for (int u = 0; u < EPC / 4; ++u) {
+        const Vec4 kv = src[u];
+        Vec4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (T)((float)kv[e] * w);
+        dst[u] = o;
+      }
+    }
+  };
+
+  // masked-score tiles above the diagonal are never written: keep them zero
+  for (int x = tid * 16; x < 2 * PT::BYTES; x += 64 * NW * 16)
+    *reinterpret_cast<uint4*>(smem + lay.p + x) = uint4{0, 0, 0, 0};
+  issue(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  if (a.P > 1) issue(1);
+  lds_barrier();  // chunk 0 has landed for every wave; the zeroed tiles are visible
+  prepare(0);
+
+  // The chunk loop, compiled once per row group so that every row-tile
+  // index in it is a constant and the work of a chunk is straight-line code.
+  auto run = [&](auto row_group) __attribute__((always_inline)) {
+    constexpr int WR = decltype(row_group)::value;
+    // (all per-wave state is declared in here, so that it stays in registers)
+    // the first MAXH Fenwick nodes of earlier blocks (most recent first): A
+    // fragments of this wave's columns, their level and their decay offset
+    Frag hn[MAXH > 0 ? MAXH : 1][KSD];
+    int hlv[MAXH > 0 ? MAXH : 1];
+    float hdd[MAXH > 0 ? MAXH : 1];
+    int rest_far = J;  // set bits of J whose nodes are not held in registers
+    float dd_far = 0.f;
+#pragma unroll
+    for (int x = 0; x < MAXH; ++x) {
+      hlv[x] = -1;
+      hdd[x] = 0.f;
+      if (rest_far > 0) {
+        const int e = rest_far - 1;
+        node_frags<T, D>(hn[x], node_of(e), wc, lane);
+        hlv[x] = LOGC + 1 + logP + __ffs(rest_far) - 1;  // token level of the node
+        hdd[x] = dd_far;
+        dd_far += gamma_of(e);
+        rest_far &= rest_far - 1;
+      }
+    }
+
+    f32x4 nst[MAXB][DT];
+    float sig[MAXB + 1];
+#pragma unroll
+    for (int m = 0; m < MAXB; ++m)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) nst[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m <= MAXB; ++m) sig[m] = 0.f;
+    float gw = 0.f;  // log-decay from the start of block J to the current chunk
+
+    // Output rows of a chunk leave at the start of the following chunk, next
+    // to the loads it issues: the wait at the top of each chunk then finds
+    // both the loads and the stores one whole chunk old.
+    Vec4 ov[NRT];
+    auto store_out = [&](int jj) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NRT; ++i) {
+        const int r = 16 * W::row_tile(i, WR) + q16;  // lane: row r, columns 16 wc + 4 (lane/16) .. + 3
+        T* o = static_cast<T*>(a.o) + (row_of(jj) + (int64_t)r * a.H) * D + 16 * wc + 4 * g4;
+        *reinterpret_cast<Vec4*>(o) = ov[i];
+      }
+    };
+
+    for (int j = 0; j < a.P; ++j) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk j+1 and stores of chunk j-2 are done
+      lds_barrier();                  // chunk j prepared and chunk j+1 landed everywhere; chunk j-1 done
+      if (j > 0) store_out(j - 1);
+      if (j + 2 < a.P) issue(j + 2);
+      if (j + 1 < a.P) prepare(j + 1);
+
+      const char* st = stage_of(j);
+      const float* lraw = reinterpret_cast<const float*>(st + lay.lraw);
+      const float* gl = garr(j);
+      const float gsum = gl[C - 1];
+
+      // per row tile: Q fragments (index r, k = head dim), the row's lambda
+      // weights times e^{G_r} for every inter-chunk level this chunk reads
+      Frag qf[NRT][KSD];
+      const float* lr[NRT];
+      float egr[NRT], alw[NRT][MAXB], alh[NRT][MAXH > 0 ? MAXH : 1];
+#pragma unroll
+      for (int i = 0; i < NRT; ++i) {
+        const int r = 16 * W::row_tile(i, WR) + q16;
+#pragma unroll
+        for (int s = 0; s < KSD; ++s) qf[i][s] = frag_row<T, C, D>(st + lay.q, r, s, g4);
+        lr[i] = lraw + r * LS;
+        egr[i] = __expf(gl[r]);
+#pragma unroll
+        for (int m = 1; m <= MAXB; ++m) alw[i][m - 1] = lr[i][min(LOGC + m, LS - 1)] * egr[i];
+#pragma unroll
+        for (int x = 0; x < MAXH; ++x) alh[i][x] = lr[i][max(hlv[x], 0)] * egr[i];
+      }
+
+      // --- intra-chunk: O^T += V^T P^T
+      Frag vf[KSC];
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) vf[s] = frag_col<T, C, D>(st + lay.v, 16 * wc, s, lane);
+      const char* pt = smem + lay.p + (j & 1) * PT::BYTES;
+      Frag pf[NRT][KSC];
+#pragma unroll
+      for (int i = 0; i < NRT; ++i)
+#pragma unroll
+        for (int s = 0; s < KSC; ++s) pf[i][s] = frag_row<T, C, C>(pt, 16 * W::row_tile(i, WR) + q16, s, g4);
+      lds_wait(vf);
+      f32x4 oacc[NRT];
+#pragma unroll
+      for (int i = 0; i < NRT; ++i) {
+        oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KSC; ++s)
+          if (M::first_tile(s) <= W::row_tile(i, WR)) oacc[i] = M::mma(vf[s], pf[i][s], oacc[i]);
+      }
+
+      // --- inter-chunk levels: O^T += diag(alpha) N^T Q^T, alpha_r = lambda_r^l e^{G_r} x scale
+      auto level_read = [&](const Frag(&nf)[KSD], const float(&al)[NRT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NRT; ++i) {
+          f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KSD; ++s) t = M::mma(nf[s], qf[i][s], t);
+          oacc[i] += al[i] * t;
         }
-      }
-
-    // --- lambda of the inter-chunk levels, transposed to [level][r] and
-    // pre-multiplied by exp(G[r])
-    {
-      const float eg = __expf(gl[lane & (C - 1)]);
-      const int n = (LS - LOGC - 1) * C;
-      for (int x = tid; x < n; x += 64 * NW) {
-        const int l = LOGC + 1 + x / C, r = x % C;
-        lt[x] = lraw[r * LS + l] * eg;
-      }
-    }
-    lds_barrier();  // P and lambda^T visible; the loads of chunk j+1 keep flying
-    if (!QDB && j + 1 < a.P) issue_rows<T, D, C>(a.q, a, row_of(j + 1), smem + lay.q, wv, NW, lane);
-
-    f32x4 oacc[CT];
-#pragma unroll
-    for (int rt = 0; rt < CT; ++rt) oacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // --- within-block levels LOGC+1 .. LOGC+logP
-#pragma unroll
-    for (int m = 1; m <= MAXB; ++m) {
-      if (m <= logP && ((j >> (m - 1)) & 1)) {
-        Frag nf[KSD];
-#pragma unroll
-        for (int s = 0; s < KSD; ++s) nf[s] = M::acc_frag(nst[m - 1], s);
-        level_read<T, D, C>(oacc, qf, nf, lt + (m - 1) * C, __expf(sig[m]), g4);
-      }
-    }
-
-    // --- earlier blocks: one Fenwick node per set bit of J, most recent first
-    {
-      int rest = J;
-      float dd = 0.f;  // log-decay from the node's end to the start of block J
-      for (int x = 0; rest > 0; ++x) {
-        const int e = rest - 1, l = __ffs(rest) - 1;
-        Frag nf[KSD];
-        if (x < MAXH) {
-#pragma unroll
-          for (int s = 0; s < KSD; ++s)
-            nf[s] = *reinterpret_cast<const Frag*>(hbuf + ((x * NW + wv) * KSD + s) * FRAG_BYTES +
-                                                   lane * (int)sizeof(Frag));
-        } else {
-          node_frags<T, D>(nf, node_of(e), wv, lane);
-        }
-        level_read<T, D, C>(oacc, qf, nf, lt + (logP + l) * C, __expf(gw + dd), g4);
-        dd += gamma_of(e);
-        rest &= rest - 1;
-      }
-    }
-
-    // --- intra-chunk: O += P V for this wave's columns
-    Frag vf[KSC];
-#pragma unroll
-    for (int s = 0; s < KSC; ++s) vf[s] = frag_col<T, C, D>(st + lay.v, 16 * wv, s, lane);
-#pragma unroll
-    for (int rt = 0; rt < CT; ++rt)
-#pragma unroll
-      for (int s = 0; s < KSC; ++s)
-        if (M::first_tile(s) <= rt) oacc[rt] = M::mma(frag_row<T, C, C>(pt, 16 * rt + q16, s, g4), vf[s], oacc[rt]);
-
-    // --- store this chunk's output rows (this wave's 16 columns)
-    {
-      T* o = static_cast<T*>(a.o) + row_of(j) * D + 16 * wv + q16;
-      const int64_t rs = (int64_t)a.H * D;
-#pragma unroll
-      for (int rt = 0; rt < CT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[(16 * rt + 4 * g4 + i) * rs] = from_f32<T>(oacc[rt][i]);
-    }
-
-    // --- this chunk's own decayed key-value state, then the merge rule of
-    // the within-block Fenwick levels (levels 1..c and the chunk become level
-    // c+1, c = ctz(j+1))
-#pragma unroll
-    for (int m = 1; m <= MAXB; ++m) sig[m] += gsum;
-    gw += gsum;
-    if (j + 1 < a.P) {
-#pragma unroll
-      for (int s = 0; s < KSC; ++s) vf[s] = scale_tokens<T>(vf[s], wl, s, g4);
-      f32x4 merged[DT];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KSC; ++s) x = M::mma(frag_col<T, C, D>(st + lay.k, 16 * dt, s, lane), vf[s], x);
-        merged[dt] = x;
-      }
-      const int c = __ffs(j + 1) - 1;
+      };
+      // within-block levels LOGC+1 .. LOGC+logP
 #pragma unroll
       for (int m = 1; m <= MAXB; ++m) {
-        if (m <= c) {
+        if (m <= logP && ((j >> (m - 1)) & 1)) {
+          Frag nf[KSD];
+#pragma unroll
+          for (int s = 0; s < KSD; ++s) nf[s] = M::acc_frag(nst[m - 1], s);
           const float sc = __expf(sig[m]);
+          float al[NRT];
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) merged[dt] += sc * nst[m - 1][dt];
+          for (int i = 0; i < NRT; ++i) al[i] = alw[i][m - 1] * sc;
+          level_read(nf, al);
         }
       }
+      // earlier blocks: one Fenwick node per set bit of J, most recent first
 #pragma unroll
-      for (int m = 1; m <= MAXB; ++m) {
-        if (m == c + 1) {
+      for (int x = 0; x < MAXH; ++x) {
+        if (hlv[x] >= 0) {
+          const float sc = __expf(gw + hdd[x]);
+          float al[NRT];
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) nst[m - 1][dt] = merged[dt];
-          sig[m] = 0.f;
+          for (int i = 0; i < NRT; ++i) al[i] = alh[i][x] * sc;
+          level_read(hn[x], al);
+        }
+      }
+      {
+        int rest = rest_far;
+        float dd = dd_far;
+        while (rest > 0) {
+          const int e = rest - 1;
+          Frag nf[KSD];
+          node_frags<T, D>(nf, node_of(e), wc, lane);
+          const int lev = LOGC + 1 + logP + __ffs(rest) - 1;
+          const float sc = __expf(gw + dd);
+          float al[NRT];
+#pragma unroll
+          for (int i = 0; i < NRT; ++i) al[i] = lr[i][lev] * egr[i] * sc;
+          level_read(nf, al);
+          dd += gamma_of(e);
+          rest &= rest - 1;
+        }
+      }
+
+      // --- the output rows, stored at the start of the next chunk
+#pragma unroll
+      for (int i = 0; i < NRT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[i][e] = (T)oacc[i][e];
+
+      // --- this chunk's own decayed key-value state K_w^T V (keys scaled by
+      // e^{G[C-1] - G_s}), then the merge rule of the within-block Fenwick
+      // levels (levels 1..c and the chunk become level c+1, c = ctz(j+1))
+#pragma unroll
+      for (int m = 1; m <= MAXB; ++m) sig[m] += gsum;
+      gw += gsum;
+      if (j + 1 < a.P) {
+        const char* kw = smem + lay.kw + (j & 1) * TL::BYTES;
+        Frag kf[DT][KSC];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int s = 0; s < KSC; ++s) kf[dt][s] = frag_col<T, C, D>(kw, 16 * dt, s, lane);
+        lds_wait(kf);
+        f32x4 merged[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KSC; ++s) x = M::mma(kf[dt][s], vf[s], x);
+          merged[dt] = x;
+        }
+        const int c = __ffs(j + 1) - 1;
+#pragma unroll
+        for (int m = 1; m <= MAXB; ++m) {
+          if (m <= c) {
+            const float sc = __expf(sig[m]);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) merged[dt] += sc * nst[m - 1][dt];
+          }
+        }
+#pragma unroll
+        for (int m = 1; m <= MAXB; ++m) {
+          if (m == c + 1) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) nst[m - 1][dt] = merged[dt];
+            sig[m] = 0.f;
+          }
         }
       }
     }
+    store_out(a.P - 1);
+  };
+  if (W::RH == 1 || wr == 0) {
+    run(std::integral_constant<int, 0>{});
+  } else {
+    run(std::integral_constant<int, W::RH - 1>{});
   }
 }
 
@@ -474,21 +582,24 @@ static hipError_t launch_state_t(const PrefillArgs& a, hipStream_t s) {
 
 template <typename T, int D, int C>
 static hipError_t launch_attn_t(const PrefillArgs& a, hipStream_t s) {
-  // node fragments kept in LDS (bf16 heads up to 64: 8 KB per node at d=64)
-  constexpr int MAXH = 0;
-  constexpr bool QDB = false;
-  auto kern = ll_chunk_attn<T, D, C, max_block_depth(D), MAXH, QDB>;
-  const AttnLayout<T, D, C, MAXH, QDB> lay(a.LS);
-  static int configured = 0;  // dynamic LDS above 64 KiB must be allowed per kernel
-  if (lay.total > configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lay.total);
-    if (e != hipSuccess) return e;
-    configured = lay.total;
+  if constexpr (C * D * (int)sizeof(T) > kAttnTileBytesMax) {
+    return hipErrorInvalidValue;  // rejected by the shape checks before launch
+  } else {
+    // Fenwick nodes of earlier blocks held in registers (5 cover up to 32 blocks per head)
+    constexpr int MAXH = (sizeof(T) == 2 && D <= 64) ? 5 : 0;
+    auto kern = ll_chunk_attn<T, D, C, max_block_depth(D), MAXH>;
+    const AttnLayout<T, D, C> lay(a.LS);
+    static int configured = 0;  // dynamic LDS above 64 KiB must be allowed per kernel
+    if (lay.total > configured) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lay.total);
+      if (e != hipSuccess) return e;
+      configured = lay.total;
+    }
+    const int grid = a.B * a.H * a.nb;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * AttnWaves<D, C>::NW), lay.total, s, a);
+    return hipGetLastError();
   }
-  const int grid = a.B * a.H * a.nb;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * (D / 16)), lay.total, s, a);
-  return hipGetLastError();
 }
 
 // bf16 MFMA steps contract 32 values, so bf16 needs C >= 32 and D >= 32

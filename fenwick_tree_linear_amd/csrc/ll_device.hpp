@@ -33,12 +33,11 @@ __device__ __forceinline__ int ilog2c(int x) { return 31 - __clz(x); }
 
 // Workgroup barrier that orders LDS accesses only.  Unlike __syncthreads()
 // it does not wait for this wave's outstanding global loads, so direct
-// global->LDS loads of the next chunk stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
+// global->LDS loads of the next chunk stay in flight across it.  (A release
+// fence on LDS would wait for them too: the compiler counts direct loads as
+// pending LDS writes.)  Only this wave's own LDS operations are drained; the
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <typename T>
 struct Mma;
@@ -167,19 +166,51 @@ __device__ __forceinline__ typename Mma<T>::Frag frag_row(const char* lds, int r
   }
 }
 
+// gfx950 transposing LDS read (ds_read_b64_tr_b16), issued as inline
+// assembly.  Through the builtin, the compiler makes every such read wait for
+// all outstanding direct global->LDS loads, since it cannot tell that they
+// fill another buffer; that would serialise the next chunk's loads with the
+// current chunk's work.  The compiler does not track this read: call
+// lds_wait() on the result before using it.
+__device__ __forceinline__ i16x4 ds_read_tr16(const char* lds) {
+  i16x4 r;
+  const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+
+// Waits for this wave's LDS reads issued through inline assembly; the
+// values passed in (arrays of fragments) are not used before the wait.
+template <typename F, int N>
+__device__ __forceinline__ void lds_pin(F (&f)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(f[i]));
+}
+template <typename F, int N, int M>
+__device__ __forceinline__ void lds_pin(F (&f)[N][M]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) lds_pin(f[i]);
+}
+template <typename... A>
+__device__ __forceinline__ void lds_wait(A&... arrays) {
+  asm volatile("s_waitcnt lgkmcnt(0)");
+  (lds_pin(arrays), ...);
+}
+
 // Fragment whose k axis runs down the rows (tokens): the MFMA row/column is
 // LDS column col0 + lane%16, k = rows kidx(s, lane/16, .).  For bf16 this is
 // two gfx950 transposing reads: within each 16-lane group, lane q supplies the
 // address of row base + q/4, columns col0 + 4*(q%4) .. +3, and receives
-// column col0 + q of rows base .. base+3.
+// column col0 + q of rows base .. base+3.  The bf16 result must pass through
+// lds_wait() before use.
 template <typename T, int ROWS, int COLS>
 __device__ __forceinline__ typename Mma<T>::Frag frag_col(const char* lds, int col0, int s, int lane) {
   typedef Tile<T, ROWS, COLS> TL;
   const int g = lane >> 4, q = lane & 15;
   if constexpr (sizeof(T) == 2) {
     const int row = 32 * s + 4 * g + (q >> 2), col = col0 + 4 * (q & 3);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds + TL::off(row, col)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds + TL::off(row + 16, col)));
+    const i16x4 lo = ds_read_tr16(lds + TL::off(row, col));
+    const i16x4 hi = ds_read_tr16(lds + TL::off(row + 16, col));
     typedef short i16x8 __attribute__((ext_vector_type(8)));
     const i16x8 v = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);

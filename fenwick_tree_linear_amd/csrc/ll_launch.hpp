@@ -8,6 +8,8 @@
 namespace llattn {
 
 constexpr int kLevelsMax = 24;  // levels staged per chunk: positions < 2^23
+// Largest chunk tile (C x d values) of the staged prefill pipeline, in bytes.
+constexpr int kAttnTileBytesMax = 8192;
 
 // Everything one prefill needs, with the workspace already carved up.
 struct PrefillArgs {

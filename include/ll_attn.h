@@ -72,6 +72,8 @@ typedef enum { LL_MAMBA2 = 0, LL_GATED_DELTANET = 1 } ll_rule;
  * Implemented (LL_ERR_UNSUPPORTED otherwise): dk == dv, and
  *   bf16 io: dk in {32, 64, 128}, C in {32, 64};
  *   fp32 io: dk in {16, 32, 64},  C in {16, 32, 64};
+ *   a chunk tile of C x dk values within 8 KiB (bf16: C = 64 with dk <= 64,
+ *   C = 32 with any dk; fp32: C x dk <= 2048);
  *   T < 2^23.
  */
 typedef struct {

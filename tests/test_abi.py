@@ -71,6 +71,8 @@ def test_workspace_grows_with_problem():
     (dict(dk=64, dv=32), "LL_ERR_UNSUPPORTED", "dk"),
     (dict(dk=48, dv=48), "LL_ERR_UNSUPPORTED", "head size"),
     (dict(dk=16, dv=16), "LL_ERR_UNSUPPORTED", "head size"),
+    (dict(dk=128, dv=128), "LL_ERR_UNSUPPORTED", "exceeds"),
+    (dict(io=F.LL_F32, dk=64, dv=64, C=64), "LL_ERR_UNSUPPORTED", "exceeds"),
     (dict(io=7), "LL_ERR_DTYPE", "dtype"),
     (dict(rule=5), "LL_ERR_UNSUPPORTED", "rule"),
     (dict(B=0), "LL_ERR_SHAPE", "positive"),

@@ -90,7 +90,7 @@ RAGGED = [
     ("bf16", 2, 3, 224, 32, 32, 9),     # 7 chunks of 32, d=32
     ("bf16", 2, 2, 64, 64, 64, 7),      # a single chunk
     ("bf16", 1, 3, 320, 64, 64, 20),    # more levels than needed
-    ("bf16", 1, 2, 1024, 128, 64, 11),  # d=128
+    ("bf16", 1, 2, 1024, 128, 32, 11),  # d=128 (chunks of 32)
     ("f32", 2, 3, 48, 16, 16, 7),       # 3 chunks of 16
     ("f32", 1, 1, 16, 16, 16, 5),       # a single fp32 chunk
     ("f32", 1, 2, 96, 64, 32, 8),       # d=64 fp32
