@@ -50,6 +50,18 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _check_no_undefined_kernels(lib: str) -> None:
+    """A kernel whose host stub the compiler did not emit links silently and
+    only fails when the library is loaded: refuse such a library here."""
+    readelf = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "llvm-readelf")
+    r = subprocess.run([readelf, "--dyn-syms", "-W", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"llvm-readelf failed on {lib}:\n{r.stderr}")
+    missing = [line.split()[-1] for line in r.stdout.splitlines() if " UND " in line and "llattn" in line]
+    if missing:
+        raise RuntimeError("undefined kernel symbols in the built library: " + ", ".join(missing))
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
@@ -59,6 +71,7 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    _check_no_undefined_kernels(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -69,32 +69,68 @@ __device__ __forceinline__ typename Mma<T>::Frag scale_tokens(typename Mma<T>::F
   }
 }
 
-// Direct loads of chunk rows [row0, row0 + C) of one head.
-template <typename T, int D, int C>
-__device__ __forceinline__ void issue_rows(const void* src, const PrefillArgs& a, int64_t row0, char* lds, int wv,
-                                           int nw, int lane) {
-  tile_load_async<T, C, D>(static_cast<const T*>(src) + row0 * D, (int64_t)a.H * D, lds, wv, nw, lane);
+// The direct global->LDS loads one wave issues for a chunk of one head.  The
+// per-lane byte offsets (from the chunk's first row) are the same for every
+// chunk and are computed once; per chunk only the scalar base pointers move.
+//   tiles : C rows of D values at a stride of H*D, 1 KiB per instruction,
+//           landing in the swizzled Tile layout (instruction i of the tile is
+//           issued by wave i % NW)
+//   gates : C floats at a stride of H (wave 0)
+//   lambda: the first LS of the L level weights of each row, row-major [C][LS]
+//           in LDS, 64 consecutive floats per instruction (instruction k by
+//           wave k % NW)
+__device__ __forceinline__ void load_lds16(const char* src, char* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, 0);
 }
 
-template <int C>
-__device__ __forceinline__ void issue_gates(const PrefillArgs& a, int64_t row0, float* lds, int wv, int nw, int lane) {
-  const float* g = a.g + row0;
-  scatter_load_async(lds, C, wv, nw, lane, [&](int f) { return g + (int64_t)f * a.H; });
-}
+template <typename T, int D, int C, int NW>
+struct ChunkLoads {
+  typedef Tile<T, C, D> TL;
+  static constexpr int NINST = TL::BYTES / 1024;
+  static constexpr int TPW = (NINST + NW - 1) / NW;                        // tile instructions per wave
+  static constexpr int LPW = (C * kLevelsMax + 64 * NW - 1) / (64 * NW);   // lambda instructions per wave, at most
+  static_assert(TL::BYTES % 1024 == 0 && 1024 % TL::RB == 0, "tile must be whole 1 KiB instructions");
+  uint32_t tile_off[TPW], lam_off[LPW], gate_off;
+  int lam_n;  // lambda floats per chunk, C * LS
 
-// lambda rows of the chunk, row-major [C][LS]: consecutive lanes read
-// consecutive floats of one token's level weights.
-// (f / LS uses a multiply-high by ceil(2^32 / LS): exact for f * LS < 2^32.)
-template <int C>
-__device__ __forceinline__ void issue_lambda(const PrefillArgs& a, int64_t row0, float* lds, int LS, unsigned ls_magic,
-                                             int wv, int nw, int lane) {
-  const float* lam = a.lam + row0 * a.L;
-  const int64_t ls = (int64_t)a.H * a.L;
-  scatter_load_async(lds, LS * C, wv, nw, lane, [&](int f) {
-    const int r = (int)__umulhi((unsigned)f, ls_magic);
-    return lam + r * ls + (f - r * LS);
-  });
-}
+  __device__ __forceinline__ void init(int wv, int lane, int H, int L, int LS) {
+    constexpr int RPI = 1024 / TL::RB;  // rows per instruction
+    const int rl = lane / TL::NCH, p = lane % TL::NCH;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int row = (wv + k * NW) * RPI + rl;
+      tile_off[k] = (uint32_t)(row * H * D * (int)sizeof(T) + TL::pos(row, p) * 16);
+    }
+    lam_n = C * LS;
+#pragma unroll
+    for (int k = 0; k < LPW; ++k) {
+      const int f = (wv + k * NW) * 64 + lane, r = f / LS;
+      lam_off[k] = (uint32_t)((r * H * L + (f - r * LS)) * 4);
+    }
+    gate_off = (uint32_t)(lane * H * 4);
+  }
+  __device__ __forceinline__ void tiles(const void* tensor, int64_t row0, char* lds, int wv) const {
+    const char* base = static_cast<const char*>(tensor) + row0 * D * (int64_t)sizeof(T);
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int i = wv + k * NW;
+      if (i < NINST) load_lds16(base + tile_off[k], lds + i * 1024);
+    }
+  }
+  __device__ __forceinline__ void gates(const float* g, int64_t row0, float* lds, int wv, int lane) const {
+    if (wv == 0 && lane < C)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(g + row0) + gate_off, (lds_void*)lds, 4, 0, 0);
+  }
+  __device__ __forceinline__ void lambda(const float* lam, int64_t row0, int L, float* lds, int wv, int lane) const {
+    const char* base = reinterpret_cast<const char*>(lam + row0 * L);
+#pragma unroll
+    for (int k = 0; k < LPW; ++k) {
+      const int first = (wv + k * NW) * 64;
+      if (first < lam_n && first + lane < lam_n)
+        __builtin_amdgcn_global_load_lds(base + lam_off[k], (lds_void*)(lds + first), 4, 0, 0);
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------
 // ll_chunk_state: one workgroup per (block J, head), one wave per 16 state
@@ -122,11 +158,13 @@ __global__ void __launch_bounds__(64 * (D / 16)) ll_chunk_state(PrefillArgs a) {
   const int wg = xcd_logical_id(blockIdx.x, gridDim.x);
   const int J = wg % a.nb, bh = wg / a.nb, h = bh % a.H, b = bh / a.H;
   auto row_of = [&](int j) { return ((int64_t)b * a.T + (int64_t)(J * a.P + j) * C) * a.H + h; };
+  ChunkLoads<T, D, C, NW> ld;
+  ld.init(wv, lane, a.H, a.L, a.LS);
   auto issue = [&](int j) {
     char* st = smem + (j & 1) * L::STAGE;
-    issue_rows<T, D, C>(a.k, a, row_of(j), st + L::KOFF, wv, NW, lane);
-    issue_rows<T, D, C>(a.v, a, row_of(j), st + L::VOFF, wv, NW, lane);
-    issue_gates<C>(a, row_of(j), reinterpret_cast<float*>(st + L::GOFF), wv, NW, lane);
+    ld.tiles(a.k, row_of(j), st + L::KOFF, wv);
+    ld.tiles(a.v, row_of(j), st + L::VOFF, wv);
+    ld.gates(a.g, row_of(j), reinterpret_cast<float*>(st + L::GOFF), wv, lane);
   };
 
   f32x4 acc[DT];
@@ -258,7 +296,6 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int LS = a.LS;
-  const unsigned ls_magic = (unsigned)((0x100000000ull + LS - 1) / LS);
   const Lay lay(LS);
   // the wave index is made a scalar so that every branch on it is a uniform
   // jump: an MFMA must never sit under a partial or empty EXEC mask
@@ -276,13 +313,16 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
   auto stage_of = [&](int j) { return smem + (j % NS) * lay.stage; };
   // this wave's prefix arrays for chunk parity p: G, e^{G[C-1]-G}, e^{G[end of 16-token tile]-G}
   auto garr = [&](int j) { return reinterpret_cast<float*>(smem + lay.gw) + (wv * 2 + (j & 1)) * 3 * C; };
+  ChunkLoads<T, D, C, NW> ld;
+  ld.init(wv, lane, a.H, a.L, LS);
   auto issue = [&](int j) __attribute__((always_inline)) {
     char* st = stage_of(j);
-    issue_rows<T, D, C>(a.q, a, row_of(j), st + lay.q, wv, NW, lane);
-    issue_rows<T, D, C>(a.k, a, row_of(j), st + lay.k, wv, NW, lane);
-    issue_rows<T, D, C>(a.v, a, row_of(j), st + lay.v, wv, NW, lane);
-    issue_gates<C>(a, row_of(j), reinterpret_cast<float*>(st + lay.g), wv, NW, lane);
-    issue_lambda<C>(a, row_of(j), reinterpret_cast<float*>(st + lay.lraw), LS, ls_magic, wv, NW, lane);
+    const int64_t row0 = row_of(j);
+    ld.tiles(a.q, row0, st + lay.q, wv);
+    ld.tiles(a.k, row0, st + lay.k, wv);
+    ld.tiles(a.v, row0, st + lay.v, wv);
+    ld.gates(a.g, row0, reinterpret_cast<float*>(st + lay.g), wv, lane);
+    ld.lambda(a.lam, row0, a.L, reinterpret_cast<float*>(st + lay.lraw), wv, lane);
   };
 
   // Prepares chunk j for its read-out: the in-chunk prefix G of the log-gates
@@ -305,36 +345,39 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
       wl[lane] = __expf(gsum - gscan);
       es[lane] = __expf(gend - gscan);
     }
+    // the causal tiles t = rt (rt+1)/2 + ct are dealt to the waves in turn
     char* pt = smem + lay.p + (j & 1) * PT::BYTES;
+    constexpr int NT = CT * (CT + 1) / 2, NSLOT = (NT + NW - 1) / NW;
 #pragma unroll
-    for (int rt = 0; rt < CT; ++rt)
+    for (int k = 0; k < NSLOT; ++k) {
+      const int t = wv + k * NW;
+      if (t >= NT) break;
+      int rt = 0;
 #pragma unroll
-      for (int ct = 0; ct <= rt; ++ct) {
-        if ((rt * (rt + 1) / 2 + ct) % NW != wv) continue;
-        const int r = 16 * rt + q16;  // lane: row r, sources 16 ct + 4 (lane/16) .. + 3
-        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 1; u < CT; ++u) rt += (t >= u * (u + 1) / 2) ? 1 : 0;
+      const int ct = t - rt * (rt + 1) / 2;
+      const int r = 16 * rt + q16;  // lane: row r, sources 16 ct + 4 (lane/16) .. + 3
+      const float* lr = lraw + r * LS;
+      Frag kf[KSD], qf[KSD];
 #pragma unroll
-        for (int s = 0; s < KSD; ++s)
-          x = M::mma(frag_row<T, C, D>(st + lay.k, 16 * ct + q16, s, g4), frag_row<T, C, D>(st + lay.q, r, s, g4), x);
-        const float* lr = lraw + r * LS;
-        const float gr = gl[r];
-        f32x4 pv;
-        if (ct < rt) {  // one level for the whole row: 4 + bit_length(rt ^ ct)
-          const float w = lr[4 + 32 - __clz(rt ^ ct)] * __expf(gr - gl[16 * ct + 15]);
-          pv = x * w * *reinterpret_cast<const f32x4*>(es + 16 * ct + 4 * g4);
-        } else {
-          const f32x4 gs = *reinterpret_cast<const f32x4*>(gl + 16 * ct + 4 * g4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int src = 4 * g4 + e;  // source position inside the tile; the row is q16
-            pv[e] = (src <= q16) ? x[e] * lr[32 - __clz(q16 ^ src)] * __expf(gr - gs[e]) : 0.f;
-          }
-        }
-        Vec4 out;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) out[e] = (T)pv[e];
-        *reinterpret_cast<Vec4*>(pt + PT::off(r, 16 * ct + 4 * g4)) = out;
+      for (int s = 0; s < KSD; ++s) {
+        kf[s] = frag_row<T, C, D>(st + lay.k, 16 * ct + q16, s, g4);
+        qf[s] = frag_row<T, C, D>(st + lay.q, r, s, g4);
       }
+      const f32x4 gs = *reinterpret_cast<const f32x4*>(gl + 16 * ct + 4 * g4);
+      const float gr = gl[r];
+      float lam[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lam[e] = lr[32 - __clz(r ^ (16 * ct + 4 * g4 + e))];  // level of (r, s)
+      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSD; ++s) x = M::mma(kf[s], qf[s], x);
+      Vec4 out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        out[e] = (T)((16 * ct + 4 * g4 + e <= r) ? x[e] * lam[e] * __expf(gr - gs[e]) : 0.f);
+      *reinterpret_cast<Vec4*>(pt + PT::off(r, 16 * ct + 4 * g4)) = out;
+    }
     // decay-scaled keys: the same swizzled positions, each 16-byte piece of a
     // row scaled by that row's weight
     char* kw = smem + lay.kw + (j & 1) * TL::BYTES;
@@ -565,10 +608,14 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
     }
     store_out(a.P - 1);
   };
-  if (W::RH == 1 || wr == 0) {
+  if constexpr (W::RH == 1) {
     run(std::integral_constant<int, 0>{});
   } else {
-    run(std::integral_constant<int, W::RH - 1>{});
+    if (wr == 0) {
+      run(std::integral_constant<int, 0>{});
+    } else {
+      run(std::integral_constant<int, 1>{});
+    }
   }
 }
 

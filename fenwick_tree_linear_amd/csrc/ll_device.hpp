@@ -122,36 +122,6 @@ struct Tile {
   }
 };
 
-// Direct global->LDS copy of one tile: row r of the source starts at
-// src + r * stride (elements).  One wave instruction moves 64 x 16 bytes;
-// wave `wv` of `nw` issues instructions wv, wv+nw, ...  Completion is tracked
-// by the issuing wave's vmcnt.
-template <typename T, int ROWS, int COLS>
-__device__ __forceinline__ void tile_load_async(const T* __restrict__ src, int64_t stride, char* lds, int wv, int nw,
-                                                int lane) {
-  typedef Tile<T, ROWS, COLS> TL;
-  constexpr int NINST = TL::BYTES / 1024;
-  constexpr int RPI = 1024 / TL::RB;  // rows per instruction
-  static_assert(TL::BYTES % 1024 == 0 && 1024 % TL::RB == 0, "tile must be whole 1 KiB instructions");
-  const int rl = lane / TL::NCH, p = lane % TL::NCH;
-  for (int i = wv; i < NINST; i += nw) {
-    const int row = i * RPI + rl;
-    const int chunk = TL::pos(row, p);  // the source chunk that belongs at position p
-    const T* g = src + row * stride + chunk * (16 / TL::ESZ);
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds + i * 1024), 16, 0, 0);
-  }
-}
-
-// Direct 4-byte global->LDS copy of n scattered floats: element f (0 <= f < n)
-// comes from src_of(f) and lands at lds[f].
-template <typename F>
-__device__ __forceinline__ void scatter_load_async(float* lds, int n, int wv, int nw, int lane, F src_of) {
-  for (int base = wv * 64; base < n; base += nw * 64) {
-    const int f = base + lane;
-    if (f < n) __builtin_amdgcn_global_load_lds(src_of(f), (lds_void*)(lds + base), 4, 0, 0);
-  }
-}
-
 // Fragment whose k axis runs along a row: rows/columns of the MFMA tile are
 // LDS rows `row`, k = columns kidx(s, g, .).
 template <typename T, int ROWS, int COLS>
