@@ -92,12 +92,60 @@ def cpu_baseline(w, min_seconds: float = 10.0) -> dict:
                       f"fp64, {runs} runs in {dt:.1f} s"}
 
 
+def decode_bench(steps: int) -> dict:
+    """ll_decode_step on the decode workload (B64 H16 d64 bf16, 17 levels): ``steps`` tokens at
+    positions 32768.. from a resident per-level state (random values; the step's cost does not
+    depend on them), one launch per token, timed with HIP events on the launch stream."""
+    import torch
+
+    import fenwick_tree_linear_amd as F
+    from fenwick_tree_linear_amd import workloads as W
+
+    w = W.WORKLOADS["decode-32k"]
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    state = F.decode_state_tensor(w.B, w.H, w.dk, w.dv, w.L, device=dev)
+    nmat = w.B * w.H * w.L * w.dk * w.dv
+    state[:nmat].normal_(0.0, 0.05, generator=gen)
+    x = W.decode_inputs(W.with_shape(w, steps=1), device=dev)
+    q, k, v = (x[n][0].contiguous() for n in ("q", "k", "v"))
+    g, lam = x["log_gate"][0].contiguous(), x["lam"][0].contiguous()
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(pos):
+        F.ll_decode_step(w.B, w.H, w.dk, w.dv, w.L, F.LL_BF16, F.LL_MAMBA2, pos, q, k, v, g, lam, None, o, state, stream)
+
+    for i in range(8):
+        step(w.T + i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        step(w.T + i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(stop) * 1e3 / steps
+    mask = (1 << (w.L - 1)) - 1
+    level_bytes = w.dk * w.dv * 4
+    per_head = sum((bin((w.T + i) & mask).count("1") + 1) * level_bytes for i in range(steps)) / steps
+    io_bytes = (4 * w.dk * 2 + 4 + 2 * w.L * 4)  # q, k, v, o; gate; lambda; sigma read + written
+    bytes_per_step = w.B * w.H * (per_head + io_bytes)
+    achieved = bytes_per_step / (us * 1e-6) / 1e9
+    return {"workload": "ll_decode_step B64 H16 d64 bf16, 17 levels, positions 32768.." + str(w.T + steps - 1),
+            "us_per_step": round(us, 2), "tokens_per_s": round(w.B / (us * 1e-6), 1),
+            "bytes_per_step": int(bytes_per_step), "achieved_GBs": round(achieved, 1), "peak_GBs": HBM_PEAK_GBS,
+            "frac": round(achieved / HBM_PEAK_GBS, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=512,
+                    help="also time this many ll_decode_step tokens on the decode workload (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -194,6 +242,9 @@ def main() -> int:
         "kernels_us": kernels,
         "cpu_baseline": None,
     }
+    if args.decode_steps:
+        result["decode"] = decode_bench(args.decode_steps)
+        log(f"[bench] decode: {result['decode']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores")
         result["cpu_baseline"] = cpu_baseline(w)

@@ -24,6 +24,8 @@ __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
   constexpr int CG = D / 4;      // column groups of 4 floats
   constexpr int RG = NTH / CG;   // row groups
   constexpr int RPT = D / RG;    // rows per thread
+  // levels whose rows are in flight together (at most 16 f32x4 rows per thread)
+  constexpr int kDecodeBatch = RPT >= 16 ? 1 : (16 / RPT < 4 ? 16 / RPT : 4);
   __shared__ float qs[D], ks[D], vs[D];
   __shared__ float lam[kDecodeLevelsMax], sig[kDecodeLevelsMax];
   __shared__ __attribute__((aligned(16))) float red[RG][D];
@@ -56,19 +58,36 @@ __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
 #pragma unroll
   for (int rr = 0; rr < RPT; ++rr) msum[rr] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int l = 1; l < L; ++l) {
-    if (!((pos >> (l - 1)) & 1)) continue;
-    const float decay = __expf(sig[l]);
-    const float coef = lam[l] * decay;
-    const float* lev = Sh + (int64_t)l * D * D + 4 * cg;
-    f32x4 rows[RPT];
+  // non-empty levels l >= 1 are the set bits l-1 of pos; their rows are
+  // loaded kDecodeBatch levels at a time, all in flight before any is used
+  uint64_t bits = (uint64_t)pos & ((L - 1 >= 64) ? ~0ull : ((1ull << (L - 1)) - 1));
+  while (bits) {
+    int lv[kDecodeBatch];
 #pragma unroll
-    for (int rr = 0; rr < RPT; ++rr) rows[rr] = *reinterpret_cast<const f32x4*>(lev + (rr * RG + rg) * D);
+    for (int u = 0; u < kDecodeBatch; ++u) {
+      lv[u] = bits ? __ffsll((unsigned long long)bits) : 0;  // level = bit index + 1; 0 = none
+      bits &= bits - 1;
+    }
+    f32x4 rows[kDecodeBatch][RPT];
 #pragma unroll
-    for (int rr = 0; rr < RPT; ++rr) part += (coef * qs[rr * RG + rg]) * rows[rr];
-    if (l <= c) {
+    for (int u = 0; u < kDecodeBatch; ++u) {
+      if (lv[u] == 0) continue;
+      const float* lev = Sh + (int64_t)lv[u] * D * D + 4 * cg;
 #pragma unroll
-      for (int rr = 0; rr < RPT; ++rr) msum[rr] += decay * rows[rr];
+      for (int rr = 0; rr < RPT; ++rr) rows[u][rr] = *reinterpret_cast<const f32x4*>(lev + (rr * RG + rg) * D);
+    }
+#pragma unroll
+    for (int u = 0; u < kDecodeBatch; ++u) {
+      if (lv[u] == 0) continue;
+      const int l = lv[u];
+      const float decay = __expf(sig[l]);
+      const float coef = lam[l] * decay;
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr) part += (coef * qs[rr * RG + rg]) * rows[u][rr];
+      if (l <= c) {
+#pragma unroll
+        for (int rr = 0; rr < RPT; ++rr) msum[rr] += decay * rows[u][rr];
+      }
     }
   }
 
