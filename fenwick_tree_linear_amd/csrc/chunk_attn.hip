@@ -51,6 +51,12 @@ __device__ __forceinline__ float chunk_prefix(const float* gates, int lane) {
   return x;
 }
 
+// j mod 3 for 0 <= j < 16 from a table of 2-bit entries (no division).
+__device__ __forceinline__ int mod3_small(int j) {
+  constexpr unsigned kTable = 0x24924924u;  // entry j = bits [2j, 2j+1]: 0,1,2,0,1,2,...
+  return (int)((kTable >> (2 * j)) & 3u);
+}
+
 // Multiplies element e of a fragment whose k axis is tokens by w[token(e)].
 template <typename T>
 __device__ __forceinline__ typename Mma<T>::Frag scale_tokens(typename Mma<T>::Frag f, const float* w, int s, int g) {
@@ -157,7 +163,8 @@ __global__ void __launch_bounds__(64 * (D / 16)) ll_chunk_state(PrefillArgs a) {
   float* wl = reinterpret_cast<float*>(smem + L::WOFF) + wv * C;
   const int wg = xcd_logical_id(blockIdx.x, gridDim.x);
   const int J = wg % a.nb, bh = wg / a.nb, h = bh % a.H, b = bh / a.H;
-  auto row_of = [&](int j) { return ((int64_t)b * a.T + (int64_t)(J * a.P + j) * C) * a.H + h; };
+  const int64_t row_blk = ((int64_t)b * a.T + (int64_t)J * a.P * C) * a.H + h;  // first row of the block
+  auto row_of = [&](int j) { return row_blk + (int64_t)(j * C * a.H); };
   ChunkLoads<T, D, C, NW> ld;
   ld.init(wv, lane, a.H, a.L, a.LS);
   auto issue = [&](int j) {
@@ -302,17 +309,22 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, q16 = lane & 15;
   const int wc = wv % NCT, wr = wv / NCT;
+  // This workgroup's work items: consecutive (block J, head) pairs, item
+  // i = head * nb + J, walked as one stream of steps t = (item k) * P + chunk j.
   const int wg = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int J = wg % a.nb, bh = wg / a.nb, h = bh % a.H, b = bh / a.H;
+  const int nitems = a.B * a.H * a.nb;
+  const int item0 = (int)((int64_t)wg * nitems / gridDim.x);
+  const int nsteps = ((int)((int64_t)(wg + 1) * nitems / gridDim.x) - item0) * a.P;
   const int logP = ilog2c(a.P);
-  auto row_of = [&](int j) { return ((int64_t)b * a.T + (int64_t)(J * a.P + j) * C) * a.H + h; };
-  auto node_of = [&](int e) {
-    return (e & 1) ? a.F + ((int64_t)bh * a.nF + (e >> 1)) * D * D : a.S + ((int64_t)bh * a.nb + e) * D * D;
+  const int row_step = C * a.H;  // rows per chunk
+  auto row_of = [&](int t) {     // first row of step t
+    const int item = item0 + (t >> logP), J = item % a.nb, bh = item / a.nb;
+    return ((int64_t)(bh / a.H) * a.T + (int64_t)J * a.P * C) * a.H + bh % a.H + (int64_t)((t & (a.P - 1)) * row_step);
   };
-  auto gamma_of = [&](int e) { return (e & 1) ? a.GF[(int64_t)bh * a.nF + (e >> 1)] : a.GS[(int64_t)bh * a.nb + e]; };
-  auto stage_of = [&](int j) { return smem + (j % NS) * lay.stage; };
-  // this wave's prefix arrays for chunk parity p: G, e^{G[C-1]-G}, e^{G[end of 16-token tile]-G}
-  auto garr = [&](int j) { return reinterpret_cast<float*>(smem + lay.gw) + (wv * 2 + (j & 1)) * 3 * C; };
+  static_assert(NS == 3, "the staging ring is three buffers");
+  auto stage_of = [&](int t) { return smem + (t % NS) * lay.stage; };
+  // this wave's prefix arrays for step parity: G, e^{G[C-1]-G}, e^{G[end of 16-token tile]-G}
+  auto garr = [&](int t) { return reinterpret_cast<float*>(smem + lay.gw) + (wv * 2 + (t & 1)) * 3 * C; };
   ChunkLoads<T, D, C, NW> ld;
   ld.init(wv, lane, a.H, a.L, LS);
   auto issue = [&](int j) __attribute__((always_inline)) {
@@ -403,8 +415,8 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
     *reinterpret_cast<uint4*>(smem + lay.p + x) = uint4{0, 0, 0, 0};
   issue(0);
   __builtin_amdgcn_s_waitcnt(0);
-  if (a.P > 1) issue(1);
-  lds_barrier();  // chunk 0 has landed for every wave; the zeroed tiles are visible
+  if (nsteps > 1) issue(1);
+  lds_barrier();  // step 0 has landed for every wave; the zeroed tiles are visible
   prepare(0);
 
   // The chunk loop, compiled once per row group so that every row-tile
@@ -412,36 +424,50 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
   auto run = [&](auto row_group) __attribute__((always_inline)) {
     constexpr int WR = decltype(row_group)::value;
     // (all per-wave state is declared in here, so that it stays in registers)
-    // the first MAXH Fenwick nodes of earlier blocks (most recent first): A
-    // fragments of this wave's columns, their level and their decay offset
+    // Per item: the first MAXH Fenwick nodes of earlier blocks (most recent
+    // first) as A fragments of this wave's columns, with their level and decay
+    // offset; the within-block Fenwick states and their log-scales.
     Frag hn[MAXH > 0 ? MAXH : 1][KSD];
     int hlv[MAXH > 0 ? MAXH : 1];
     float hdd[MAXH > 0 ? MAXH : 1];
-    int rest_far = J;  // set bits of J whose nodes are not held in registers
+    int rest_far = 0;  // set bits of J whose nodes are not held in registers
     float dd_far = 0.f;
-#pragma unroll
-    for (int x = 0; x < MAXH; ++x) {
-      hlv[x] = -1;
-      hdd[x] = 0.f;
-      if (rest_far > 0) {
-        const int e = rest_far - 1;
-        node_frags<T, D>(hn[x], node_of(e), wc, lane);
-        hlv[x] = LOGC + 1 + logP + __ffs(rest_far) - 1;  // token level of the node
-        hdd[x] = dd_far;
-        dd_far += gamma_of(e);
-        rest_far &= rest_far - 1;
-      }
-    }
-
+    int bh = 0;
     f32x4 nst[MAXB][DT];
     float sig[MAXB + 1];
-#pragma unroll
-    for (int m = 0; m < MAXB; ++m)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) nst[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m <= MAXB; ++m) sig[m] = 0.f;
     float gw = 0.f;  // log-decay from the start of block J to the current chunk
+    auto node_of = [&](int e) {
+      return (e & 1) ? a.F + ((int64_t)bh * a.nF + (e >> 1)) * D * D : a.S + ((int64_t)bh * a.nb + e) * D * D;
+    };
+    auto gamma_of = [&](int e) {
+      return (e & 1) ? a.GF[(int64_t)bh * a.nF + (e >> 1)] : a.GS[(int64_t)bh * a.nb + e];
+    };
+    auto start_item = [&](int item) __attribute__((always_inline)) {
+      const int J = item % a.nb;
+      bh = item / a.nb;
+      rest_far = J;
+      dd_far = 0.f;
+#pragma unroll
+      for (int x = 0; x < MAXH; ++x) {
+        hlv[x] = -1;
+        hdd[x] = 0.f;
+        if (rest_far > 0) {
+          const int e = rest_far - 1;
+          node_frags<T, D>(hn[x], node_of(e), wc, lane);
+          hlv[x] = LOGC + 1 + logP + __ffs(rest_far) - 1;  // token level of the node
+          hdd[x] = dd_far;
+          dd_far += gamma_of(e);
+          rest_far &= rest_far - 1;
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MAXB; ++m)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) nst[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m <= MAXB; ++m) sig[m] = 0.f;
+      gw = 0.f;
+    };
 
     // Output rows of a chunk leave at the start of the following chunk, next
     // to the loads it issues: the wait at the top of each chunk then finds
@@ -456,16 +482,18 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
       }
     };
 
-    for (int j = 0; j < a.P; ++j) {
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk j+1 and stores of chunk j-2 are done
-      lds_barrier();                  // chunk j prepared and chunk j+1 landed everywhere; chunk j-1 done
-      if (j > 0) store_out(j - 1);
-      if (j + 2 < a.P) issue(j + 2);
-      if (j + 1 < a.P) prepare(j + 1);
+    for (int t = 0; t < nsteps; ++t) {
+      const int j = t & (a.P - 1);    // chunk within the item's block
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of step t+1 and stores of step t-2 are done
+      lds_barrier();                  // step t prepared and step t+1 landed everywhere; step t-1 done
+      if (j == 0) start_item(item0 + (t >> logP));  // node loads ahead of this step's stores and loads
+      if (t > 0) store_out(t - 1);
+      if (t + 2 < nsteps) issue(t + 2);
+      if (t + 1 < nsteps) prepare(t + 1);
 
-      const char* st = stage_of(j);
+      const char* st = stage_of(t);
       const float* lraw = reinterpret_cast<const float*>(st + lay.lraw);
-      const float* gl = garr(j);
+      const float* gl = garr(t);
       const float gsum = gl[C - 1];
 
       // per row tile: Q fragments (index r, k = head dim), the row's lambda
@@ -490,7 +518,7 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
       Frag vf[KSC];
 #pragma unroll
       for (int s = 0; s < KSC; ++s) vf[s] = frag_col<T, C, D>(st + lay.v, 16 * wc, s, lane);
-      const char* pt = smem + lay.p + (j & 1) * PT::BYTES;
+      const char* pt = smem + lay.p + (t & 1) * PT::BYTES;
       Frag pf[NRT][KSC];
 #pragma unroll
       for (int i = 0; i < NRT; ++i)
@@ -572,7 +600,7 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
       for (int m = 1; m <= MAXB; ++m) sig[m] += gsum;
       gw += gsum;
       if (j + 1 < a.P) {
-        const char* kw = smem + lay.kw + (j & 1) * TL::BYTES;
+        const char* kw = smem + lay.kw + (t & 1) * TL::BYTES;
         Frag kf[DT][KSC];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -606,7 +634,7 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
         }
       }
     }
-    store_out(a.P - 1);
+    store_out(nsteps - 1);
   };
   if constexpr (W::RH == 1) {
     run(std::integral_constant<int, 0>{});
@@ -643,7 +671,22 @@ static hipError_t launch_attn_t(const PrefillArgs& a, hipStream_t s) {
       if (e != hipSuccess) return e;
       configured = lay.total;
     }
-    const int grid = a.B * a.H * a.nb;
+    // persistent: as many workgroups as fit on the device at once, each
+    // walking a run of consecutive (block, head) items
+    static int slots = 0, slots_lds = -1;
+    if (slots_lds != lay.total) {
+      int dev = 0, cus = 0, per_cu = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
+                                                         64 * AttnWaves<D, C>::NW, lay.total);
+      if (e != hipSuccess) return e;
+      slots = cus * (per_cu > 0 ? per_cu : 1);
+      slots_lds = lay.total;
+    }
+    const int items = a.B * a.H * a.nb;
+    const int grid = items < slots ? items : slots;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * AttnWaves<D, C>::NW), lay.total, s, a);
     return hipGetLastError();
   }

@@ -105,16 +105,19 @@ __device__ __forceinline__ int state_tile_offset(int dt, int nt, int lane) {
 
 // ------------------------------------------------------------ LDS tiles
 // Row-major [ROWS][COLS] tile of T in LDS.  Rows are stored unpadded and the
-// 16-byte chunks of row r are permuted by XOR with (r mod chunks-per-row), so
-// that the 16 rows touched by one fragment read fall on different banks.
+// 16-byte chunks of row r are permuted by XOR with a function of r, so that
+// the 16 rows touched by one fragment read fall on different banks: the 64
+// four-byte banks span 256 bytes, i.e. RP = 256 / row-bytes rows, and rows
+// r and r + RP would collide, so the XOR key is (r / RP) mod chunks-per-row.
 template <typename T, int ROWS, int COLS>
 struct Tile {
   static constexpr int ESZ = sizeof(T);
   static constexpr int RB = COLS * ESZ;  // bytes per row
   static constexpr int NCH = RB / 16;    // 16-byte chunks per row
   static constexpr int BYTES = ROWS * RB;
+  static constexpr int RP = RB >= 256 ? 1 : 256 / RB;  // rows per bank sweep
   static_assert((NCH & (NCH - 1)) == 0 && NCH >= 1, "rows must be a power-of-two number of 16-byte chunks");
-  __device__ __forceinline__ static int pos(int row, int chunk) { return chunk ^ (row & (NCH - 1)); }
+  __device__ __forceinline__ static int pos(int row, int chunk) { return chunk ^ ((row / RP) & (NCH - 1)); }
   // byte offset of element (row, col)
   __device__ __forceinline__ static int off(int row, int col) {
     const int byte = col * ESZ;
