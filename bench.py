@@ -138,6 +138,50 @@ def decode_bench(steps: int) -> dict:
             "frac": round(achieved / HBM_PEAK_GBS, 4)}
 
 
+def gdn_bench(steps: int) -> dict:
+    """ll_attn_fwd with the Gated DeltaNet write on its 8K-token workload (B2 H16 T8192 d128 bf16,
+    14 levels, chunk 64): whole-step time and per-kernel averages, both from HIP events on the
+    launch stream, inputs resident in HBM."""
+    import torch
+
+    import fenwick_tree_linear_amd as F
+    from fenwick_tree_linear_amd import workloads as W
+
+    w = W.WORKLOADS["gdn-8k"]
+    dev = torch.device("cuda:0")
+    x = W.prefill_inputs(w, device=dev)
+    prob = F.LLProblem(w.B, w.T, w.H, w.dk, w.dv, w.L, w.C, F.LL_BF16, F.LL_GATED_DELTANET)
+    ws_bytes = F.ll_attn_fwd_workspace_bytes(prob)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    o = torch.empty(w.B, w.T, w.H, w.dv, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        F.ll_attn_fwd(prob, x["q"], x["k"], x["v"], x["log_gate"], x["lam"], x["beta"], o, None, ws, ws_bytes,
+                      stream)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    F.ll_kernel_timing_read()  # drop anything counted before
+    F.ll_kernel_timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kt = F.ll_kernel_timing_read()
+    F.ll_kernel_timing_enable(False)
+    return {"workload": "gated-deltanet prefill B2 H16 T8192 dk=dv=128 bf16, 14 levels, chunk 64",
+            "ms_per_step": round(ms, 5), "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
+            "kernels_us": {name: round(t / n * 1e3, 2) for name, (t, n) in kt.items()}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +190,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=512,
                     help="also time this many ll_decode_step tokens on the decode workload (0: skip)")
+    ap.add_argument("--gdn-steps", type=int, default=20,
+                    help="also time this many Gated DeltaNet prefill steps on its 8K-token workload (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -245,6 +291,9 @@ def main() -> int:
     if args.decode_steps:
         result["decode"] = decode_bench(args.decode_steps)
         log(f"[bench] decode: {result['decode']}")
+    if args.gdn_steps:
+        result["gdn"] = gdn_bench(args.gdn_steps)
+        log(f"[bench] gdn: {result['gdn']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores")
         result["cpu_baseline"] = cpu_baseline(w)

@@ -13,6 +13,7 @@
 #include "ll_launch.hpp"
 
 using llattn::DecodeArgs;
+using llattn::GdnArgs;
 using llattn::PrefillArgs;
 
 namespace {
@@ -59,8 +60,11 @@ constexpr int kMaxBlockChunks = 8;  // P <= 2^max_block_depth for d <= 64
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
+  int Cr;  // chunk size of the log-linear read (C, or smaller for Gated DeltaNet when a tile would not fit)
   int P, nb, nF, LS;
-  size_t s_off, gs_off, f_off, gf_off, bytes;
+  size_t s_off, gs_off, f_off, gf_off;
+  size_t w_off, up_off, u_off;  // Gated DeltaNet: W, U' and the pseudo-values U
+  size_t bytes;
 };
 
 // Validates a prefill problem and derives the block decomposition.
@@ -81,27 +85,32 @@ ll_status plan_prefill(const ll_problem* p, bool exporting, Plan* out) {
   if (exporting && bit_length(p->T) > p->L - 1)
     return fail(LL_ERR_SHAPE, "exporting the state of [0,%d) needs at least %d levels, got L=%d", p->T,
                 bit_length(p->T) + 1, p->L);
-  if (p->rule != LL_MAMBA2)
-    return fail(LL_ERR_UNSUPPORTED, "the Gated DeltaNet write is not implemented in prefill");
   if (p->dk != p->dv) return fail(LL_ERR_UNSUPPORTED, "dk=%d != dv=%d is not supported", p->dk, p->dv);
   if (!supported_head(p->dk, p->io))
     return fail(LL_ERR_UNSUPPORTED, "head size %d not supported for %s io", p->dk, p->io == LL_BF16 ? "bf16" : "fp32");
   if (!supported_chunk(p->C, p->io))
     return fail(LL_ERR_UNSUPPORTED, "chunk size C=%d not supported for %s io", p->C, p->io == LL_BF16 ? "bf16" : "fp32");
-  if ((size_t)p->C * p->dk * (p->io == LL_BF16 ? 2 : 4) > (size_t)llattn::kAttnTileBytesMax)
-    return fail(LL_ERR_UNSUPPORTED, "a chunk tile of C=%d x d=%d %s values exceeds %d bytes", p->C, p->dk,
+  const size_t esz = p->io == LL_BF16 ? 2 : 4;
+  int Cr = p->C;
+  if (p->rule == LL_GATED_DELTANET) {
+    // the pseudo-value pass works on chunks of C; the read may use smaller ones
+    while ((size_t)Cr * p->dk * esz > (size_t)llattn::kAttnTileBytesMax && supported_chunk(Cr / 2, p->io)) Cr /= 2;
+  }
+  if ((size_t)Cr * p->dk * esz > (size_t)llattn::kAttnTileBytesMax)
+    return fail(LL_ERR_UNSUPPORTED, "a chunk tile of C=%d x d=%d %s values exceeds %d bytes", Cr, p->dk,
                 p->io == LL_BF16 ? "bf16" : "fp32", llattn::kAttnTileBytesMax);
   if (need > llattn::kLevelsMax)
     return fail(LL_ERR_UNSUPPORTED, "T=%d needs %d levels; at most %d are supported", p->T, need, llattn::kLevelsMax);
   if ((int64_t)p->B * p->H * (p->T / p->C) > ((int64_t)1 << 31) - 1)
     return fail(LL_ERR_UNSUPPORTED, "problem too large for one launch");
 
-  const int nc = p->T / p->C;
+  const int nc = p->T / Cr;
   const int depth_cap = 1 << llattn::max_block_depth(p->dk);
   int P = nc & -nc;  // lowest set bit: blocks tile the chunks exactly
   if (P > kMaxBlockChunks) P = kMaxBlockChunks;
   if (P > depth_cap) P = depth_cap;
   Plan pl;
+  pl.Cr = Cr;
   pl.P = P;
   pl.nb = nc / P;
   pl.nF = pl.nb / 2;
@@ -117,15 +126,26 @@ ll_status plan_prefill(const ll_problem* p, bool exporting, Plan* out) {
   off = align256(off + bh * pl.nF * dd * sizeof(float));
   pl.gf_off = off;
   off = align256(off + bh * (pl.nF > 0 ? pl.nF : 1) * sizeof(float));
+  pl.w_off = pl.up_off = pl.u_off = 0;
+  if (p->rule == LL_GATED_DELTANET) {
+    const size_t rows = (size_t)p->B * p->T * p->H * p->dk * esz;
+    pl.w_off = off;
+    off = align256(off + rows);
+    pl.up_off = off;
+    off = align256(off + rows);
+    pl.u_off = off;
+    off = align256(off + rows);
+  }
   pl.bytes = off;
   *out = pl;
   return LL_OK;
 }
 
 // ---------------------------------------------------------- kernel timing
-enum KernelId { K_CHUNK_STATE, K_FENWICK_SCAN, K_CHUNK_ATTN, K_STATE_EXPORT, K_DECODE_STEP, K_COUNT };
+enum KernelId { K_CHUNK_STATE, K_FENWICK_SCAN, K_CHUNK_ATTN, K_STATE_EXPORT, K_DECODE_STEP, K_GDN_WY, K_GDN_STATE,
+                K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"ll_chunk_state", "ll_fenwick_scan", "ll_chunk_attn", "ll_state_export",
-                                           "ll_decode_step"};
+                                           "ll_decode_step", "ll_gdn_wy",       "ll_gdn_state"};
 
 struct Timing {
   std::mutex mu;
@@ -160,9 +180,17 @@ hipError_t timed(int kernel, hipStream_t stream, Fn fn) {
   if (!g_timing.on) return fn();
   hipEvent_t a = take_event(), b = take_event();
   if (!a || !b) return fn();
-  hipEventRecord(a, stream);
+  if (hipEventRecord(a, stream) != hipSuccess) {  // no timing for this launch
+    g_timing.pool.push_back(a);
+    g_timing.pool.push_back(b);
+    return fn();
+  }
   hipError_t e = fn();
-  hipEventRecord(b, stream);
+  if (hipEventRecord(b, stream) != hipSuccess) {
+    g_timing.pool.push_back(a);
+    g_timing.pool.push_back(b);
+    return e;
+  }
   g_timing.pending.push_back({kernel, a, b});
   return e;
 }
@@ -245,7 +273,7 @@ ll_status ll_attn_fwd(const ll_problem* p, const void* q, const void* k, const v
   a.nF = pl.nF;
   a.q = q;
   a.k = k;
-  a.v = v;
+  a.v = p->rule == LL_GATED_DELTANET ? static_cast<const void*>(ws + pl.u_off) : v;
   a.g = log_gate;
   a.lam = lambda;
   a.o = o;
@@ -257,8 +285,26 @@ ll_status ll_attn_fwd(const ll_problem* p, const void* q, const void* k, const v
   const int io = p->io == LL_BF16 ? 1 : 0;
   const int D = p->dk;
 
-  const int C = p->C;
-  hipError_t e = timed(K_CHUNK_STATE, stream, [&] { return llattn::launch_block_state(io, D, C, a, stream); });
+  hipError_t e = hipSuccess;
+  if (p->rule == LL_GATED_DELTANET) {
+    // the pseudo-values U of the delta rule, then the read of (q, k, U)
+    GdnArgs gd;
+    gd.B = p->B;
+    gd.T = p->T;
+    gd.H = p->H;
+    gd.k = k;
+    gd.v = v;
+    gd.g = log_gate;
+    gd.beta = beta;
+    gd.W = ws + pl.w_off;
+    gd.Up = ws + pl.up_off;
+    gd.U = ws + pl.u_off;
+    e = timed(K_GDN_WY, stream, [&] { return llattn::launch_gdn_wy(io, D, p->C, gd, stream); });
+    if (e == hipSuccess) e = timed(K_GDN_STATE, stream, [&] { return llattn::launch_gdn_state(io, D, p->C, gd, stream); });
+  }
+  const int C = pl.Cr;
+  if (e == hipSuccess)
+    e = timed(K_CHUNK_STATE, stream, [&] { return llattn::launch_block_state(io, D, C, a, stream); });
   if (e == hipSuccess && a.nb > 1)
     e = timed(K_FENWICK_SCAN, stream, [&] { return llattn::launch_fenwick_scan(D, a, stream); });
   if (e == hipSuccess && o)
@@ -290,11 +336,9 @@ ll_status ll_decode_step(int B, int H, int dk, int dv, int L, ll_dtype io, ll_ru
     return fail(LL_ERR_POSITION, "pos=%lld: the state of [0,pos+1) does not fit in L=%d levels", (long long)pos, L);
   if (!q || !k || !v || !log_gate || !lambda || !o || !state)
     return fail(LL_ERR_NULL, "q, k, v, log_gate, lambda, o and state must not be NULL");
-  if (rule != LL_MAMBA2) return fail(LL_ERR_UNSUPPORTED, "the Gated DeltaNet decode step is not implemented");
+  if (rule == LL_GATED_DELTANET && !beta) return fail(LL_ERR_NULL, "beta must not be NULL for Gated DeltaNet");
   if (dk != dv) return fail(LL_ERR_UNSUPPORTED, "dk=%d != dv=%d is not supported", dk, dv);
   if (dk != 16 && dk != 32 && dk != 64 && dk != 128) return fail(LL_ERR_UNSUPPORTED, "head size %d not supported", dk);
-  (void)beta;
-
   DecodeArgs a;
   a.B = B;
   a.H = H;
@@ -305,6 +349,7 @@ ll_status ll_decode_step(int B, int H, int dk, int dv, int L, ll_dtype io, ll_ru
   a.v = v;
   a.g = log_gate;
   a.lam = lambda;
+  a.beta = rule == LL_GATED_DELTANET ? beta : nullptr;
   a.o = o;
   a.state = static_cast<float*>(state);
   const int code = io == LL_BF16 ? 1 : 0;

@@ -8,6 +8,10 @@
 //   sigma_l += log a_pos                                   (all levels)
 //   o = lambda_0 (q.k) v + sum_{l: bit l-1 of pos} lambda_l exp(sigma_l) S_hat_l^T q
 //   c = ctz(pos+1):  S_hat_{c+1} = k v^T + sum_{l=1..c} exp(sigma_l) S_hat_l,  sigma_{c+1} = 0
+// For the Gated DeltaNet write the token writes its pseudo-value
+//   u = beta (v - sum_l exp(sigma_l) S_hat_l^T k)
+// (the levels partition the prefix, so their sum is the plain gated state) in
+// place of v, in the level-0 term of o and in the merge.
 // Levels 1..c are exactly the low set bits of pos, so the merge reuses the rows
 // loaded for the read; they become empty (bit clear in pos+1) and are not
 // rewritten.  Traffic per head: popcount(pos) level reads + one level write.
@@ -26,9 +30,10 @@ __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
   constexpr int RPT = D / RG;    // rows per thread
   // levels whose rows are in flight together (at most 16 f32x4 rows per thread)
   constexpr int kDecodeBatch = RPT >= 16 ? 1 : (16 / RPT < 4 ? 16 / RPT : 4);
-  __shared__ float qs[D], ks[D], vs[D];
+  __shared__ float qs[D], ks[D], vs[D], us[D];
   __shared__ float lam[kDecodeLevelsMax], sig[kDecodeLevelsMax];
   __shared__ __attribute__((aligned(16))) float red[RG][D];
+  __shared__ __attribute__((aligned(16))) float redk[RG][D];  // Gated DeltaNet: the levels read by k
 
   const int bh = blockIdx.x;
   const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
@@ -53,7 +58,9 @@ __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
   __syncthreads();
 
   const int c = __ffsll((unsigned long long)(pos + 1)) - 1;
+  const bool gdn = a.beta != nullptr;
   f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 kpart = f32x4{0.f, 0.f, 0.f, 0.f};  // Gated DeltaNet: sum_l e^{sigma_l} S_hat_l^T k
   f32x4 msum[RPT];
 #pragma unroll
   for (int rr = 0; rr < RPT; ++rr) msum[rr] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -84,6 +91,10 @@ __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
       const float coef = lam[l] * decay;
 #pragma unroll
       for (int rr = 0; rr < RPT; ++rr) part += (coef * qs[rr * RG + rg]) * rows[u][rr];
+      if (gdn) {
+#pragma unroll
+        for (int rr = 0; rr < RPT; ++rr) kpart += (decay * ks[rr * RG + rg]) * rows[u][rr];
+      }
       if (l <= c) {
 #pragma unroll
         for (int rr = 0; rr < RPT; ++rr) msum[rr] += decay * rows[u][rr];
@@ -92,18 +103,29 @@ __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
   }
 
   *reinterpret_cast<f32x4*>(&red[rg][4 * cg]) = part;
+  if (gdn) *reinterpret_cast<f32x4*>(&redk[rg][4 * cg]) = kpart;
   __syncthreads();
   if (tid < D) {
     float qk = 0.f;
     for (int x = 0; x < D; ++x) qk += qs[x] * ks[x];
-    float acc = lam[0] * qk * vs[tid];
+    float acc = 0.f;
     for (int r = 0; r < RG; ++r) acc += red[r][tid];
-    static_cast<T*>(a.o)[(int64_t)bh * D + tid] = from_f32<T>(acc);
+    // the value this token writes: v, or for Gated DeltaNet its pseudo-value
+    // u = beta (v - S^T k) with S the decayed plain state (the sum of all levels)
+    float u = vs[tid];
+    if (gdn) {
+      float sk = 0.f;
+      for (int r = 0; r < RG; ++r) sk += redk[r][tid];
+      u = a.beta[bh] * (vs[tid] - sk);
+      us[tid] = u;
+    }
+    static_cast<T*>(a.o)[(int64_t)bh * D + tid] = from_f32<T>(lam[0] * qk * u + acc);
   }
+  if (gdn) __syncthreads();
 
   // merge into level c+1 (c + 1 <= L - 1 is guaranteed by the caller)
   float* dst = Sh + (int64_t)(c + 1) * D * D + 4 * cg;
-  const f32x4 vv = *reinterpret_cast<const f32x4*>(&vs[4 * cg]);
+  const f32x4 vv = *reinterpret_cast<const f32x4*>(gdn ? &us[4 * cg] : &vs[4 * cg]);
 #pragma unroll
   for (int rr = 0; rr < RPT; ++rr) {
     const int d = rr * RG + rg;

@@ -83,6 +83,27 @@ __device__ __forceinline__ T from_f32(float x) {
   return (T)x;
 }
 
+// DPP move of a float within a wave (lanes without a source read 0).
+template <int CTRL, int ROW_MASK, bool ZERO_FILL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, ZERO_FILL));
+}
+
+// Inclusive prefix sum over lanes 0..C-1 of a wave (C <= 64; lanes at or past C
+// must hold 0).  DPP shifts inside each 16-lane row, then the last lane of each
+// row is broadcast to the rows above it: no LDS round trips.
+template <int C>
+__device__ __forceinline__ float chunk_scan(float x) {
+  x += dpp_f32<0x111, 0xf, true>(x);  // row_shr:1
+  x += dpp_f32<0x112, 0xf, true>(x);  // row_shr:2
+  x += dpp_f32<0x114, 0xf, true>(x);  // row_shr:4
+  x += dpp_f32<0x118, 0xf, true>(x);  // row_shr:8
+  if (C > 16) x += dpp_f32<0x142, 0xa, false>(x);  // row_bcast:15 into rows 1 and 3
+  if (C > 32) x += dpp_f32<0x143, 0xc, false>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 // ---------------------------------------------------------------- XCD order
 // Workgroup ids are dealt round-robin to the 8 XCDs of the chip; each XCD
 // has its own L2.  Renumber so that consecutive logical ids (the blocks of
@@ -191,5 +212,86 @@ __device__ __forceinline__ typename Mma<T>::Frag frag_col(const char* lds, int c
     return *reinterpret_cast<const float*>(lds + TL::off(Mma<float>::kidx(s, g, 0), col0 + q));
   }
 }
+
+// Multiplies element e of a fragment whose k axis is tokens by w[token(e)].
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::Frag scale_tokens(typename Mma<T>::Frag f, const float* w, int s, int g) {
+  if constexpr (sizeof(T) == 2) {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(w + 32 * s + 4 * g);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(w + 32 * s + 16 + 4 * g);
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] = (bf16)((float)f[e] * lo[e]);
+      r[4 + e] = (bf16)((float)f[4 + e] * hi[e]);
+    }
+    return r;
+  } else {
+    return f * w[Mma<float>::kidx(s, g, 0)];
+  }
+}
+
+// The direct global->LDS loads one wave issues for a chunk of one head.  The
+// per-lane byte offsets (from the chunk's first row) are the same for every
+// chunk and are computed once; per chunk only the scalar base pointers move.
+//   tiles : C rows of D values at a stride of H*D, 1 KiB per instruction,
+//           landing in the swizzled Tile layout (instruction i of the tile is
+//           issued by wave i % NW)
+//   gates : C floats at a stride of H (wave 0)
+//   lambda: the first LS of the L level weights of each row, row-major [C][LS]
+//           in LDS, 64 consecutive floats per instruction (instruction k by
+//           wave k % NW)
+__device__ __forceinline__ void load_lds16(const char* src, char* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, 0);
+}
+
+template <typename T, int D, int C, int NW>
+struct ChunkLoads {
+  typedef Tile<T, C, D> TL;
+  static constexpr int NINST = TL::BYTES / 1024;
+  static constexpr int TPW = (NINST + NW - 1) / NW;                        // tile instructions per wave
+  static constexpr int LPW = (C * kLevelsMax + 64 * NW - 1) / (64 * NW);   // lambda instructions per wave, at most
+  static_assert(TL::BYTES % 1024 == 0 && 1024 % TL::RB == 0, "tile must be whole 1 KiB instructions");
+  uint32_t tile_off[TPW], lam_off[LPW], gate_off;
+  int lam_n;  // lambda floats per chunk, C * LS
+
+  __device__ __forceinline__ void init(int wv, int lane, int H, int L, int LS) {
+    constexpr int RPI = 1024 / TL::RB;  // rows per instruction
+    const int rl = lane / TL::NCH, p = lane % TL::NCH;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int row = (wv + k * NW) * RPI + rl;
+      tile_off[k] = (uint32_t)(row * H * D * (int)sizeof(T) + TL::pos(row, p) * 16);
+    }
+    lam_n = C * LS;
+#pragma unroll
+    for (int k = 0; k < LPW; ++k) {
+      const int f = (wv + k * NW) * 64 + lane, r = f / LS;
+      lam_off[k] = (uint32_t)((r * H * L + (f - r * LS)) * 4);
+    }
+    gate_off = (uint32_t)(lane * H * 4);
+  }
+  __device__ __forceinline__ void tiles(const void* tensor, int64_t row0, char* lds, int wv) const {
+    const char* base = static_cast<const char*>(tensor) + row0 * D * (int64_t)sizeof(T);
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int i = wv + k * NW;
+      if (i < NINST) load_lds16(base + tile_off[k], lds + i * 1024);
+    }
+  }
+  __device__ __forceinline__ void gates(const float* g, int64_t row0, float* lds, int wv, int lane) const {
+    if (wv == 0 && lane < C)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(g + row0) + gate_off, (lds_void*)lds, 4, 0, 0);
+  }
+  __device__ __forceinline__ void lambda(const float* lam, int64_t row0, int L, float* lds, int wv, int lane) const {
+    const char* base = reinterpret_cast<const char*>(lam + row0 * L);
+#pragma unroll
+    for (int k = 0; k < LPW; ++k) {
+      const int first = (wv + k * NW) * 64;
+      if (first < lam_n && first + lane < lam_n)
+        __builtin_amdgcn_global_load_lds(base + lam_off[k], (lds_void*)(lds + first), 4, 0, 0);
+    }
+  }
+};
 
 }  // namespace llattn

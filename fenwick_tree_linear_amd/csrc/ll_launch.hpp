@@ -39,8 +39,21 @@ struct DecodeArgs {
   const void* v;
   const float* g;
   const float* lam;
+  const float* beta;  // Gated DeltaNet write strength [B,H]; NULL for the Mamba-2 write
   void* o;
   float* state;
+};
+
+// The Gated DeltaNet pseudo-value pass of a prefill (rows [B,T,H,D] in io dtype).
+struct GdnArgs {
+  int B, T, H;
+  const void* k;
+  const void* v;
+  const float* g;     // log-gates [B,T,H]
+  const float* beta;  // [B,T,H]
+  void* W;            // (I + L)^-1 diag(beta e^G) K per chunk
+  void* Up;           // (I + L)^-1 diag(beta) V per chunk
+  void* U;            // pseudo-values, the values the log-linear read uses
 };
 
 // io: 0 = fp32, 1 = bf16.  Each returns hipSuccess or the launch error.
@@ -49,6 +62,8 @@ hipError_t launch_chunk_attn(int io, int D, int C, const PrefillArgs& a, hipStre
 hipError_t launch_fenwick_scan(int D, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_state_export(int D, int C, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode_step(int io, int D, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_gdn_wy(int io, int D, int C, const GdnArgs& a, hipStream_t s);
+hipError_t launch_gdn_state(int io, int D, int C, const GdnArgs& a, hipStream_t s);
 
 inline int ilog2_host(int x) {
   int r = 0;

@@ -42,7 +42,8 @@ def gpu_prefill(x, C, L, want_output=True, want_state=False, dev_inputs=None):
     """Runs ll_attn_fwd on cuda copies of the inputs ``x``; returns numpy o
     (and the decode-layout state split into S_hat, sigma)."""
     d = dev_inputs if dev_inputs is not None else to_dev(x)
-    res = F.attn_fwd(d["q"], d["k"], d["v"], d["log_gate"], d["lam"], d.get("beta"), C=C, L=L,
+    rule = F.LL_MAMBA2 if d.get("beta") is None else F.LL_GATED_DELTANET
+    res = F.attn_fwd(d["q"], d["k"], d["v"], d["log_gate"], d["lam"], d.get("beta"), C=C, L=L, rule=rule,
                      want_output=want_output, want_state=want_state)
     torch.cuda.synchronize()
     if want_state:
@@ -65,6 +66,10 @@ def true_state(s_hat, sigma):
     return np.exp(sigma)[..., None, None] * s_hat
 
 
+def oracle_rule(x):
+    return oracle.RULE_MAMBA2 if x.get("beta") is None else oracle.RULE_GDN
+
+
 def oracle_prefill(x, heads=None, t_range=None):
     return oracle.fwd_direct(np32(x["q"]), np32(x["k"]), np32(x["v"]), np32(x["log_gate"]), np32(x["lam"]),
-                             np32(x.get("beta")), heads=heads, t_range=t_range)
+                             np32(x.get("beta")), rule=oracle_rule(x), heads=heads, t_range=t_range)

@@ -56,6 +56,16 @@ def test_workspace_bytes_for_the_16k_prefill():
     assert n % 256 == 0
 
 
+def test_gdn_workspace_holds_three_row_buffers():
+    """The Gated DeltaNet pass adds W, U' and the pseudo-values U, each [B,T,H,d] in the io dtype;
+    d=128 bf16 with C=64 is accepted (the read then uses chunks of 32)."""
+    m = F.ll_attn_fwd_workspace_bytes(prob(T=2048, L=12))
+    g = F.ll_attn_fwd_workspace_bytes(prob(T=2048, L=12, rule=F.LL_GATED_DELTANET))
+    rows = 2 * 2048 * 16 * 64 * 2
+    assert 3 * rows <= g - m <= 3 * rows + 3 * 256
+    assert F.ll_attn_fwd_workspace_bytes(prob(T=8192, L=14, dk=128, dv=128, rule=F.LL_GATED_DELTANET)) > 0
+
+
 def test_workspace_grows_with_problem():
     a = F.ll_attn_fwd_workspace_bytes(prob(T=2048, L=12))
     b = F.ll_attn_fwd_workspace_bytes(prob(T=4096, L=13))
@@ -99,7 +109,7 @@ def test_fwd_validation_before_any_launch():
         ((p, D, D, D, D, D, None, D, None, D, ws - 1), "LL_ERR_WORKSPACE"),     # workspace too small
         ((p, D, D, D, D, D, None, D, None, None, ws), "LL_ERR_WORKSPACE"),      # workspace NULL
         ((p, D, D, D, D, D, None, D, D, D, ws), "LL_ERR_SHAPE"),                # export of [0,2^14) needs L=16
-        ((prob(rule=F.LL_GATED_DELTANET), D, D, D, D, D, None, D, None, D, ws), "LL_ERR_UNSUPPORTED"),
+        ((prob(rule=F.LL_GATED_DELTANET), D, D, D, D, D, None, D, None, D, ws), "LL_ERR_NULL"),  # GDN needs beta
         ((None, D, D, D, D, D, None, D, None, D, ws), "LL_ERR_NULL"),
     ]
     for args, name in cases:
@@ -122,7 +132,7 @@ def test_decode_validation_before_any_launch():
         (dict(pos=-1), "LL_ERR_POSITION"),
         (dict(L=33, pos=5), "LL_ERR_UNSUPPORTED"),
         (dict(io=3), "LL_ERR_DTYPE"),
-        (dict(rule=F.LL_GATED_DELTANET), "LL_ERR_UNSUPPORTED"),
+        (dict(rule=F.LL_GATED_DELTANET), "LL_ERR_NULL"),  # Gated DeltaNet needs beta
         (dict(dk=64, dv=32), "LL_ERR_UNSUPPORTED"),
         (dict(state=None), "LL_ERR_NULL"),
         (dict(q=None), "LL_ERR_NULL"),
