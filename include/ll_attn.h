@@ -73,7 +73,10 @@ typedef enum { LL_MAMBA2 = 0, LL_GATED_DELTANET = 1 } ll_rule;
  *   bf16 io: dk in {32, 64, 128}, C in {32, 64};
  *   fp32 io: dk in {16, 32, 64},  C in {16, 32, 64};
  *   a chunk tile of C x dk values within 8 KiB (bf16: C = 64 with dk <= 64,
- *   C = 32 with any dk; fp32: C x dk <= 2048);
+ *   C = 32 with any dk; fp32: C x dk <= 2048) -- for LL_GATED_DELTANET this
+ *   binds the read only: the pseudo-value pass runs at C and the read at the
+ *   largest supported chunk dividing C whose tile fits (bf16 dk = 128 with
+ *   C = 64 reads at 32), so every (dk, C) pair listed above is accepted;
  *   T < 2^23.
  */
 typedef struct {
@@ -85,7 +88,10 @@ typedef struct {
 /*
  * Bytes of device workspace ll_attn_fwd needs for `p` (0 is possible).  The
  * workspace holds, per head, the decayed key-value state of every aligned span
- * of chunks and its Fenwick combination (chunk-parallel form, section 2.3).
+ * of chunks and its Fenwick combination (chunk-parallel form, section 2.3);
+ * for LL_GATED_DELTANET also three [B,T,H,dv] io-dtype row buffers: the
+ * per-chunk WY factors (I + L)^-1 diag(beta e^G) K and (I + L)^-1 diag(beta) V
+ * and the pseudo-values u the read runs on.
  * Errors: LL_ERR_NULL, and every validation error of ll_attn_fwd.
  */
 ll_status ll_attn_fwd_workspace_bytes(const ll_problem* p, size_t* bytes);
@@ -96,7 +102,9 @@ ll_status ll_attn_fwd_workspace_bytes(const ll_problem* p, size_t* bytes);
  *   q [B,T,H,dk], k [B,T,H,dk], v [B,T,H,dv]     io dtype
  *   log_gate [B,T,H]        fp32, log a_t
  *   lambda   [B,T,H,L]      fp32, per-token, per-head level weights
- *   beta     [B,T,H]        fp32, LL_GATED_DELTANET only (NULL otherwise)
+ *   beta     [B,T,H]        fp32, LL_GATED_DELTANET only (ignored otherwise);
+ *                            the write strength, normally in (0, 1]; any finite
+ *                            value is accepted
  *   o        [B,T,H,dv]     io dtype, written (may be NULL if state_out is not)
  *   state_out                nullable; if given, receives the per-level states
  *                            of [0,T) in the decode-state layout (see
@@ -130,8 +138,11 @@ ll_status ll_decode_state_bytes(int B, int H, int dk, int dv, int L, size_t* byt
  *   state                           in/out, the layout above, holding [0,pos) on
  *                                   entry and [0,pos+1) on return.
  * Requires pos + 1 < 2^(L-1) (LL_ERR_POSITION otherwise), so that the state
- * after the step still fits.  Only LL_MAMBA2 is implemented
- * (LL_ERR_UNSUPPORTED otherwise).
+ * after the step still fits.  For LL_GATED_DELTANET beta must not be NULL
+ * (LL_ERR_NULL); the step forms the pseudo-value u = beta (v - S^T k), with S
+ * the sum of the live levels decayed through a_pos, reads with it, and
+ * writes k u^T.
+ * A state exported by ll_attn_fwd with the same rule resumes exactly.
  */
 ll_status ll_decode_step(int B, int H, int dk, int dv, int L, ll_dtype io, ll_rule rule, int64_t pos,
                          const void* q, const void* k, const void* v, const float* log_gate,
@@ -147,7 +158,8 @@ const char* ll_last_error(void);
  * events recorded on the call's stream.  ll_kernel_timing_read() waits for the
  * recorded events, then reports for up to `capacity` kernels their name (a
  * static string: "ll_chunk_state", "ll_fenwick_scan", "ll_chunk_attn",
- * "ll_state_export", "ll_decode_step"), the summed milliseconds and the launch
+ * "ll_state_export", "ll_decode_step", "ll_gdn_wy", "ll_gdn_state"), the
+ * summed milliseconds and the launch
  * count, and clears the record.  Enabling creates HIP events lazily; timing
  * adds two event records per launch, so do not time throughput with it on.
  */
