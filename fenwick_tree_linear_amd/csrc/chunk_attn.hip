@@ -152,6 +152,37 @@ struct AttnWaves {
   }
 };
 
+// Walks consecutive work items item = (b H + h) nb + J (block J of head
+// (b, h)) without dividing per step: one division when it starts, then
+// carries.  `row` is the first [B,T,H] row of the item's block.
+struct ItemWalk {
+  int J, h, b;
+  int64_t row;
+  __device__ __forceinline__ void set_row(const PrefillArgs& a, int C) {
+    row = ((int64_t)b * a.T + (int64_t)J * a.P * C) * a.H + h;
+  }
+  __device__ __forceinline__ void start(int item, const PrefillArgs& a, int C) {
+    J = item % a.nb;
+    const int bh = item / a.nb;
+    h = bh % a.H;
+    b = bh / a.H;
+    set_row(a, C);
+  }
+  __device__ __forceinline__ void next(const PrefillArgs& a, int C) {
+    if (++J < a.nb) {
+      row += (int64_t)a.P * C * a.H;
+      return;
+    }
+    J = 0;
+    if (++h == a.H) {
+      h = 0;
+      ++b;
+    }
+    set_row(a, C);
+  }
+  __device__ __forceinline__ int bh(const PrefillArgs& a) const { return b * a.H + h; }
+};
+
 // Dynamic LDS layout of ll_chunk_attn (byte offsets; LS = staged levels):
 // three staging buffers of chunk tiles, two buffers of masked scores and two
 // of decay-scaled keys (chunk parity), and per-wave prefix arrays.
@@ -221,24 +252,41 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
   const int nsteps = ((int)((int64_t)(wg + 1) * nitems / gridDim.x) - item0) * a.P;
   const int logP = ilog2c(a.P);
   const int row_step = C * a.H;  // rows per chunk
-  auto row_of = [&](int t) {     // first row of step t
-    const int item = item0 + (t >> logP), J = item % a.nb, bh = item / a.nb;
-    return ((int64_t)(bh / a.H) * a.T + (int64_t)J * a.P * C) * a.H + bh % a.H + (int64_t)((t & (a.P - 1)) * row_step);
-  };
+  // Steps are loaded, read out and stored in order, each by its own cursor
+  // over the items; a cursor moves on at the first chunk of every item after
+  // its first.
+  ItemWalk load_at, store_at, read_at;
+  load_at.start(item0, a, C);
+  store_at = load_at;
+  read_at = load_at;
+  auto row_in = [&](const ItemWalk& w, int t) { return w.row + (int64_t)((t & (a.P - 1)) * row_step); };
   static_assert(NS == 3, "the staging ring is three buffers");
   auto stage_of = [&](int t) { return smem + (t % NS) * lay.stage; };
   // this wave's prefix arrays for step parity: G, e^{G[C-1]-G}, e^{G[end of 16-token tile]-G}
   auto garr = [&](int t) { return reinterpret_cast<float*>(smem + lay.gw) + (wv * 2 + (t & 1)) * 3 * C; };
   ChunkLoads<T, D, C, NW> ld;
   ld.init(wv, lane, a.H, a.L, LS);
-  auto issue = [&](int j) __attribute__((always_inline)) {
+  // The loads of a step go out in three parts (q and gates, k and lambda, v),
+  // so that inside the chunk loop they can be spread between pieces of compute
+  // instead of queueing up at the memory pipeline all at once.
+  auto issue_part = [&](int j, int part) __attribute__((always_inline)) {
     char* st = stage_of(j);
-    const int64_t row0 = row_of(j);
-    ld.tiles(a.q, row0, st + lay.q, wv);
-    ld.tiles(a.k, row0, st + lay.k, wv);
-    ld.tiles(a.v, row0, st + lay.v, wv);
-    ld.gates(a.g, row0, reinterpret_cast<float*>(st + lay.g), wv, lane);
-    ld.lambda(a.lam, row0, a.L, reinterpret_cast<float*>(st + lay.lraw), wv, lane);
+    if (part == 0 && j > 0 && (j & (a.P - 1)) == 0) load_at.next(a, C);
+    const int64_t row0 = row_in(load_at, j);
+    if (part == 0) {
+      ld.tiles(a.q, row0, st + lay.q, wv);
+      ld.gates(a.g, row0, reinterpret_cast<float*>(st + lay.g), wv, lane);
+    } else if (part == 1) {
+      ld.tiles(a.k, row0, st + lay.k, wv);
+      ld.lambda(a.lam, row0, a.L, reinterpret_cast<float*>(st + lay.lraw), wv, lane);
+    } else {
+      ld.tiles(a.v, row0, st + lay.v, wv);
+    }
+  };
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    issue_part(j, 0);
+    issue_part(j, 1);
+    issue_part(j, 2);
   };
 
   // Prepares chunk j for its read-out: the in-chunk prefix G of the log-gates
@@ -337,6 +385,7 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
     int rest_far = 0;  // set bits of J whose nodes are not held in registers
     float dd_far = 0.f;
     int bh = 0;
+    bool first_item = true;
     f32x4 nst[MAXB][DT];
     float sig[MAXB + 1];
     float gw = 0.f;  // log-decay from the start of block J to the current chunk
@@ -346,10 +395,11 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
     auto gamma_of = [&](int e) {
       return (e & 1) ? a.GF[(int64_t)bh * a.nF + (e >> 1)] : a.GS[(int64_t)bh * a.nb + e];
     };
-    auto start_item = [&](int item) __attribute__((always_inline)) {
-      const int J = item % a.nb;
-      bh = item / a.nb;
-      rest_far = J;
+    auto start_item = [&]() __attribute__((always_inline)) {
+      if (!first_item) read_at.next(a, C);
+      first_item = false;
+      bh = read_at.bh(a);
+      rest_far = read_at.J;
       dd_far = 0.f;
 #pragma unroll
       for (int x = 0; x < MAXH; ++x) {
@@ -373,27 +423,35 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
       gw = 0.f;
     };
 
-    // Output rows of a chunk leave at the start of the following chunk, next
-    // to the loads it issues: the wait at the top of each chunk then finds
-    // both the loads and the stores one whole chunk old.
+    // Output rows of a step leave during the following step, so the wait at
+    // the top of each step finds the stores most of a step old.
     Vec4 ov[NRT];
     auto store_out = [&](int jj) __attribute__((always_inline)) {
+      if (jj > 0 && (jj & (a.P - 1)) == 0) store_at.next(a, C);
+      const int64_t row0 = row_in(store_at, jj);
 #pragma unroll
       for (int i = 0; i < NRT; ++i) {
         const int r = 16 * W::row_tile(i, WR) + q16;  // lane: row r, columns 16 wc + 4 (lane/16) .. + 3
-        T* o = static_cast<T*>(a.o) + (row_of(jj) + (int64_t)r * a.H) * D + 16 * wc + 4 * g4;
+        T* o = static_cast<T*>(a.o) + (row0 + (int64_t)r * a.H) * D + 16 * wc + 4 * g4;
         *reinterpret_cast<Vec4*>(o) = ov[i];
       }
     };
 
+    // Every step starts with one barrier.  The two row groups share each SIMD
+    // (one wave of each), so they take the step's halves in opposite orders:
+    // one prepares step t+1 and then reads out step t, the other the reverse,
+    // and the waves of a SIMD are in different phases most of the time.  The
+    // read-out issues the second and third part of step t+2's loads on the way.
     for (int t = 0; t < nsteps; ++t) {
       const int j = t & (a.P - 1);    // chunk within the item's block
       __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of step t+1 and stores of step t-2 are done
       lds_barrier();                  // step t prepared and step t+1 landed everywhere; step t-1 done
-      if (j == 0) start_item(item0 + (t >> logP));  // node loads ahead of this step's stores and loads
+      if (j == 0) start_item();       // node loads ahead of this step's other memory traffic
+      if constexpr (WR == 0) {
+        if (t + 1 < nsteps) prepare(t + 1);
+      }
       if (t > 0) store_out(t - 1);
-      if (t + 2 < nsteps) issue(t + 2);
-      if (t + 1 < nsteps) prepare(t + 1);
+      if (t + 2 < nsteps) issue_part(t + 2, 0);
 
       const char* st = stage_of(t);
       const float* lraw = reinterpret_cast<const float*>(st + lay.lraw);
@@ -438,14 +496,26 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
           if (M::first_tile(s) <= W::row_tile(i, WR)) oacc[i] = M::mma(vf[s], pf[i][s], oacc[i]);
       }
 
-      // --- inter-chunk levels: O^T += diag(alpha) N^T Q^T, alpha_r = lambda_r^l e^{G_r} x scale
+      if (t + 2 < nsteps) issue_part(t + 2, 1);
+
+      // --- inter-chunk levels: O^T += diag(alpha) N^T Q^T, alpha_r = lambda_r^l e^{G_r} x scale.
+      // A level's product is weighted into O only when the next level comes
+      // (or at the end), so no level waits right away for its own products.
+      f32x4 pend[NRT];
+      float pal[NRT];
+#pragma unroll
+      for (int i = 0; i < NRT; ++i) {
+        pend[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        pal[i] = 0.f;
+      }
       auto level_read = [&](const Frag(&nf)[KSD], const float(&al)[NRT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NRT; ++i) {
-          f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+          oacc[i] += pal[i] * pend[i];
+          pal[i] = al[i];
+          pend[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < KSD; ++s) t = M::mma(nf[s], qf[i][s], t);
-          oacc[i] += al[i] * t;
+          for (int s = 0; s < KSD; ++s) pend[i] = M::mma(nf[s], qf[i][s], pend[i]);
         }
       };
       // within-block levels LOGC+1 .. LOGC+logP
@@ -491,11 +561,15 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
         }
       }
 
-      // --- the output rows, stored at the start of the next chunk
+      if (t + 2 < nsteps) issue_part(t + 2, 2);
+
+      // --- the output rows, stored during the next step
 #pragma unroll
-      for (int i = 0; i < NRT; ++i)
+      for (int i = 0; i < NRT; ++i) {
+        oacc[i] += pal[i] * pend[i];
 #pragma unroll
         for (int e = 0; e < 4; ++e) ov[i][e] = (T)oacc[i][e];
+      }
 
       // --- this chunk's own decayed key-value state K_w^T V (keys scaled by
       // e^{G[C-1] - G_s}), then the merge rule of the within-block Fenwick
@@ -510,16 +584,11 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int s = 0; s < KSC; ++s) kf[dt][s] = frag_col<T, C, D>(kw, 16 * dt, s, lane);
-        lds_wait(kf);
+        // the merged levels are summed first and enter as the accumulator
+        const int c = __ffs(j + 1) - 1;
         f32x4 merged[DT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < KSC; ++s) x = M::mma(kf[dt][s], vf[s], x);
-          merged[dt] = x;
-        }
-        const int c = __ffs(j + 1) - 1;
+        for (int dt = 0; dt < DT; ++dt) merged[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 1; m <= MAXB; ++m) {
           if (m <= c) {
@@ -528,6 +597,11 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
             for (int dt = 0; dt < DT; ++dt) merged[dt] += sc * nst[m - 1][dt];
           }
         }
+        lds_wait(kf);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int s = 0; s < KSC; ++s) merged[dt] = M::mma(kf[dt][s], vf[s], merged[dt]);
 #pragma unroll
         for (int m = 1; m <= MAXB; ++m) {
           if (m == c + 1) {
@@ -536,6 +610,9 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
             sig[m] = 0.f;
           }
         }
+      }
+      if constexpr (WR != 0) {
+        if (t + 1 < nsteps) prepare(t + 1);
       }
     }
     store_out(nsteps - 1);
