@@ -309,17 +309,27 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
       wl[lane] = __expf(gsum - gscan);
       es[lane] = __expf(gend - gscan);
     }
-    // the causal tiles t = rt (rt+1)/2 + ct are dealt to the waves in turn
+    // The causal 16x16 score tiles, the CT diagonal ones first and then the
+    // ones below the diagonal, are dealt to the waves in turn: the costlier
+    // tiles land on the first row group, which prepares at the start of a step.
+    // Below the diagonal every pair (r, s) of a tile has the same level and the
+    // decay splits at the end e of the source tile, e^{G_r - G_e} e^{G_e - G_s}:
+    // one weight per lane and one per source column.
     char* pt = smem + lay.p + (j & 1) * PT::BYTES;
     constexpr int NT = CT * (CT + 1) / 2, NSLOT = (NT + NW - 1) / NW;
 #pragma unroll
     for (int k = 0; k < NSLOT; ++k) {
-      const int t = wv + k * NW;
-      if (t >= NT) break;
-      int rt = 0;
+      const int item = k * NW + wv;
+      if (item >= NT) continue;
+      const bool diag = item < CT;
+      int rt = item, ct = item;
+      if (!diag) {  // below-diagonal tile o = rt (rt-1)/2 + ct, ct < rt
+        const int o = item - CT;
+        rt = 1;
 #pragma unroll
-      for (int u = 1; u < CT; ++u) rt += (t >= u * (u + 1) / 2) ? 1 : 0;
-      const int ct = t - rt * (rt + 1) / 2;
+        for (int u = 2; u < CT; ++u) rt += (o >= u * (u - 1) / 2) ? 1 : 0;
+        ct = o - rt * (rt - 1) / 2;
+      }
       const int r = 16 * rt + q16;  // lane: row r, sources 16 ct + 4 (lane/16) .. + 3
       const float* lr = lraw + r * LS;
       Frag kf[KSD], qf[KSD];
@@ -328,25 +338,37 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
         kf[s] = frag_row<T, C, D>(st + lay.k, 16 * ct + q16, s, g4);
         qf[s] = frag_row<T, C, D>(st + lay.q, r, s, g4);
       }
-      const f32x4 gs = *reinterpret_cast<const f32x4*>(gl + 16 * ct + 4 * g4);
       const float gr = gl[r];
-      float lam[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) lam[e] = lr[32 - __clz(r ^ (16 * ct + 4 * g4 + e))];  // level of (r, s)
       f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KSD; ++s) x = M::mma(kf[s], qf[s], x);
       Vec4 out;
+      if (diag) {
+        const f32x4 gs = *reinterpret_cast<const f32x4*>(gl + 16 * ct + 4 * g4);
+        float lam[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        out[e] = (T)((16 * ct + 4 * g4 + e <= r) ? x[e] * lam[e] * __expf(gr - gs[e]) : 0.f);
+        for (int e = 0; e < 4; ++e) lam[e] = lr[32 - __clz(r ^ (16 * ct + 4 * g4 + e))];  // level of (r, s)
+#pragma unroll
+        for (int s = 0; s < KSD; ++s) x = M::mma(kf[s], qf[s], x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          out[e] = (T)((4 * g4 + e <= q16) ? x[e] * lam[e] * __expf(gr - gs[e]) : 0.f);
+      } else {
+        const f32x4 ess = *reinterpret_cast<const f32x4*>(es + 16 * ct + 4 * g4);
+        const float wrow = lr[4 + 32 - __clz(rt ^ ct)] * __expf(gr - gl[16 * ct + 15]);
+#pragma unroll
+        for (int s = 0; s < KSD; ++s) x = M::mma(kf[s], qf[s], x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = (T)(x[e] * wrow * ess[e]);
+      }
       *reinterpret_cast<Vec4*>(pt + PT::off(r, 16 * ct + 4 * g4)) = out;
     }
     // decay-scaled keys: the same swizzled positions, each 16-byte piece of a
     // row scaled by that row's weight
     char* kw = smem + lay.kw + (j & 1) * TL::BYTES;
     constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte piece
-    for (int x = tid; x < TL::BYTES / 16; x += 64 * NW) {
+    // (by the first row group alone: the other one prepares at the end of a
+    // step, where it is the last to reach the next barrier)
+    if (W::RH == 2 && wr != 0) return;
+    for (int x = tid; x < TL::BYTES / 16; x += 64 * NCT) {
       const int row = x / TL::NCH;
       const float w = wl[row];
       const Vec4* src = reinterpret_cast<const Vec4*>(st + lay.k + x * 16);
