@@ -463,7 +463,7 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
     // (one wave of each), so they take the step's halves in opposite orders:
     // one prepares step t+1 and then reads out step t, the other the reverse,
     // and the waves of a SIMD are in different phases most of the time.  The
-    // read-out issues the second and third part of step t+2's loads on the way.
+    // read-out issues the rest of step t+2's loads after its first products.
     for (int t = 0; t < nsteps; ++t) {
       const int j = t & (a.P - 1);    // chunk within the item's block
       __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of step t+1 and stores of step t-2 are done
@@ -518,7 +518,10 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
           if (M::first_tile(s) <= W::row_tile(i, WR)) oacc[i] = M::mma(vf[s], pf[i][s], oacc[i]);
       }
 
-      if (t + 2 < nsteps) issue_part(t + 2, 1);
+      if (t + 2 < nsteps) {
+        issue_part(t + 2, 1);
+        issue_part(t + 2, 2);
+      }
 
       // --- inter-chunk levels: O^T += diag(alpha) N^T Q^T, alpha_r = lambda_r^l e^{G_r} x scale.
       // A level's product is weighted into O only when the next level comes
@@ -583,7 +586,6 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
         }
       }
 
-      if (t + 2 < nsteps) issue_part(t + 2, 2);
 
       // --- the output rows, stored during the next step
 #pragma unroll
