@@ -15,35 +15,62 @@
 // W = (I + L)^-1 diag(beta e^G) K (the WY form), and
 //   S_{i+1} = e^{g_i} S_i + sum_r e^{g_i - G_r} k_r u_r^T   (g_i = G_{C-1}).
 //
-// ll_gdn_wy    : one workgroup per (chunk, head): L on MFMA, then U' and W by
-//                forward substitution, one thread per column of [V | K].
+// ll_gdn_wy    : one workgroup per (chunk, head): L on MFMA, (I + L)^-1 by
+//                16x16 blocks on fp32 MFMA, then U' and W as MFMA products.
 // ll_gdn_state : one workgroup per (head, 16 state columns): the serial pass
 //                over the chunks, U = U' - W S_i and the state update on MFMA,
 //                writing the pseudo-values U.
+#include <type_traits>
+
 #include "ll_device.hpp"
 #include "ll_launch.hpp"
 
 namespace llattn {
 
 // ---------------------------------------------------------------------------
+// ll_gdn_wy: one workgroup of four waves per (chunk, head).
+//   1. K and V rows land in LDS (direct loads); wave 0 scans the gates.
+//   2. L: the causal 16x16 tiles of K K^T on MFMA, weighted by
+//      beta_r e^{G_r - G_s} and masked to s < r, fp32 in LDS.
+//   3. T = (I + L)^-1 by blocks of 16: the diagonal blocks by forward
+//      substitution (one lane per column), then the blocks below by
+//      T_ij = -T_ii sum_{j<=k<i} L_ik T_kj, one block distance at a time, on
+//      fp32 MFMA.
+//   4. W^T = K^T (T diag(beta e^G))^T and U'^T = V^T (T diag(beta))^T on MFMA,
+//      each lane ending with four consecutive features of one token.  For
+//      bf16 io the scaled T is split into a bf16 head and a bf16 remainder,
+//      so that the products keep T to about 16 bits.
 template <typename T, int D, int C>
 struct WySmem {
   typedef Tile<T, C, D> TL;
+  static constexpr int TS = C + 4;  // fp32 row stride of L and T (16-byte rows, rows 4 banks apart)
   static constexpr int KOFF = 0, VOFF = TL::BYTES;
-  static constexpr int LOFF = 2 * TL::BYTES;  // L [C][C] fp32
-  static constexpr int GOFF = LOFF + C * C * 4;
-  static constexpr int BOFF = GOFF + C * 4;
-  static constexpr int BYTES = BOFF + C * 4;
-  static constexpr int NT = 2 * D < 64 ? 64 : 2 * D;  // one thread per column of [V | K]
+  static constexpr int LOFF = 2 * TL::BYTES;  // L [C][TS] fp32
+  static constexpr int TOFF = LOFF + C * TS * 4;  // T [C][TS] fp32
+  static constexpr int GOFF = TOFF + C * TS * 4;  // G [C]
+  static constexpr int BOFF = GOFF + C * 4;        // beta [C]
+  static constexpr int SOFF = BOFF + C * 4;        // beta e^G [C]
+  static constexpr int BYTES = SOFF + C * 4;
+  static constexpr int NW = 4;
 };
 
+// C += X Y for 16x16 fp32 blocks X, Y in LDS (row strides in floats), on
+// the fp32 MFMA; the result is in accumulator layout (lane: rows 4 (lane/16)
+// + e of column lane%16).
+__device__ __forceinline__ f32x4 mm16(const float* X, int xs, const float* Y, int ys, f32x4 c, int q16, int g4) {
+  const f32x4 xa = *reinterpret_cast<const f32x4*>(X + q16 * xs + 4 * g4);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[s], Y[(4 * g4 + s) * ys + q16], c, 0, 0, 0);
+  return c;
+}
+
 template <typename T, int D, int C>
-__global__ void __launch_bounds__((WySmem<T, D, C>::NT)) ll_gdn_wy(GdnArgs a) {
+__global__ void __launch_bounds__(256) ll_gdn_wy(GdnArgs a) {
   using M = Mma<T>;
   typedef WySmem<T, D, C> SM;
   typedef Tile<T, C, D> TL;
-  constexpr int NT = SM::NT, NW = NT / 64, CT = C / 16, KSD = D / M::KS;
-  constexpr int EPP = 16 / (int)sizeof(T);  // elements per 16-byte piece
+  typedef typename std::conditional<sizeof(T) == 2, bf16x4, f32x4>::type Vec4;
+  constexpr int NW = SM::NW, CT = C / 16, DT = D / 16, KSD = D / M::KS, TS = SM::TS;
   __shared__ __attribute__((aligned(1024))) char smem[SM::BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, q16 = lane & 15;
@@ -51,31 +78,33 @@ __global__ void __launch_bounds__((WySmem<T, D, C>::NT)) ll_gdn_wy(GdnArgs a) {
   const int wg = xcd_logical_id(blockIdx.x, gridDim.x);
   const int i = wg % nc, bh = wg / nc, h = bh % a.H, b = bh / a.H;
   const int64_t row0 = ((int64_t)b * a.T + (int64_t)i * C) * a.H + h;  // row of the chunk's first token
-
-  // K and V rows into swizzled tiles
-  const T* kg = static_cast<const T*>(a.k);
-  const T* vg = static_cast<const T*>(a.v);
-  for (int x = tid; x < C * TL::NCH; x += NT) {
-    const int r = x / TL::NCH, c = x % TL::NCH;
-    const int64_t src = (row0 + (int64_t)r * a.H) * D + c * EPP;
-    const int dst = r * TL::RB + TL::pos(r, c) * 16;
-    *reinterpret_cast<uint4*>(smem + SM::KOFF + dst) = *reinterpret_cast<const uint4*>(kg + src);
-    *reinterpret_cast<uint4*>(smem + SM::VOFF + dst) = *reinterpret_cast<const uint4*>(vg + src);
-  }
+  float* Lm = reinterpret_cast<float*>(smem + SM::LOFF);
+  float* Tm = reinterpret_cast<float*>(smem + SM::TOFF);
   float* gl = reinterpret_cast<float*>(smem + SM::GOFF);
   float* bl = reinterpret_cast<float*>(smem + SM::BOFF);
-  float* Lm = reinterpret_cast<float*>(smem + SM::LOFF);
+  float* sl = reinterpret_cast<float*>(smem + SM::SOFF);
+
+  // 1. K and V tiles; gates and write strengths
+  {
+    ChunkLoads<T, D, C, NW> ld;
+    ld.init(wv, lane, a.H, 1, 1);
+    ld.tiles(a.k, row0, smem + SM::KOFF, wv);
+    ld.tiles(a.v, row0, smem + SM::VOFF, wv);
+  }
   if (wv == 0) {
     const float G = chunk_scan<C>(lane < C ? a.g[row0 + (int64_t)lane * a.H] : 0.f);
     if (lane < C) {
+      const float bt = a.beta[row0 + (int64_t)lane * a.H];
       gl[lane] = G;
-      bl[lane] = a.beta[row0 + (int64_t)lane * a.H];
+      bl[lane] = bt;
+      sl[lane] = bt * __expf(G);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // L: the causal 16x16 tiles of K K^T dealt to the waves; lane holds row
-  // r = 16 rt + lane%16 and sources s = 16 ct + 4 (lane/16) + e
+  // 2. L[r][s] = beta_r e^{G_r - G_s} (k_r . k_s) for s < r; lane: row r =
+  // 16 rt + lane%16, sources 16 ct + 4 (lane/16) + e
   for (int t = wv; t < CT * (CT + 1) / 2; t += NW) {
     int rt = 0;
 #pragma unroll
@@ -88,33 +117,134 @@ __global__ void __launch_bounds__((WySmem<T, D, C>::NT)) ll_gdn_wy(GdnArgs a) {
       x = M::mma(frag_row<T, C, D>(smem + SM::KOFF, 16 * ct + q16, s, g4),
                  frag_row<T, C, D>(smem + SM::KOFF, r, s, g4), x);
     const float br = bl[r], gr = gl[r];
+    const f32x4 gs = *reinterpret_cast<const f32x4*>(gl + 16 * ct + 4 * g4);
+    f32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = (16 * ct + 4 * g4 + e < r) ? br * __expf(gr - gs[e]) * x[e] : 0.f;
+    *reinterpret_cast<f32x4*>(Lm + r * TS + 16 * ct + 4 * g4) = y;
+  }
+  __syncthreads();
+
+  // 3a. diagonal blocks T_ww = (I + L_ww)^-1, lane column c = lane%16 (the
+  // four lane groups compute the same column; each writes four rows).  A
+  // wave with an even block also zeroes the block to its right, which the
+  // 32-wide MFMA steps below read.
+  if (wv < CT) {
+    const float* Lb = Lm + 16 * wv * TS + 16 * wv;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == q16) ? 1.f : 0.f;
+#pragma unroll
+      for (int s4 = 0; s4 < r; s4 += 4) {
+        const f32x4 l = *reinterpret_cast<const f32x4*>(Lb + r * TS + s4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (s4 + e < r) acc -= l[e] * x[s4 + e];
+      }
+      x[r] = acc;
+    }
+    float* Tb = Tm + 16 * wv * TS + 16 * wv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int s = 16 * ct + 4 * g4 + e;
-      Lm[r * C + s] = s < r ? br * __expf(gr - gl[s]) * x[e] : 0.f;
+      Tb[(4 * g4 + e) * TS + q16] = x[4 * g4 + e];
+      if ((wv & 1) == 0 && wv + 1 < CT) Tb[(4 * g4 + e) * TS + 16 + q16] = 0.f;
     }
   }
   __syncthreads();
 
-  // forward substitution (I + L) X = B, one column per thread: columns
-  // [0, D) of diag(beta) V give U', columns [D, 2D) of diag(beta e^G) K give W
-  if (tid < 2 * D) {
-    const bool is_w = tid >= D;
-    const int c = is_w ? tid - D : tid;
-    const char* src = smem + (is_w ? SM::KOFF : SM::VOFF);
-    float x[C];
+  // 3b. blocks below the diagonal, by distance d: T_ij = -T_ii sum_k L_ik T_kj
+  for (int d = 1; d < CT; ++d) {
+    if (wv < CT - d) {
+      const int bi = wv + d, bj = wv;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k = bj; k < bi; ++k) acc = mm16(Lm + 16 * bi * TS + 16 * k, TS, Tm + 16 * k * TS + 16 * bj, TS, acc, q16, g4);
+      float* Tij = Tm + 16 * bi * TS + 16 * bj;
 #pragma unroll
-    for (int r = 0; r < C; ++r) {
-      float acc = to_f32(*reinterpret_cast<const T*>(src + TL::off(r, c))) * bl[r];
-      if (is_w) acc *= __expf(gl[r]);
-      const float* Lr = Lm + r * C;
+      for (int e = 0; e < 4; ++e) Tij[(4 * g4 + e) * TS + q16] = acc[e];  // the sum, read back just below
+      f32x4 y = mm16(Tm + 16 * bi * TS + 16 * bi, TS, Tij, TS, f32x4{0.f, 0.f, 0.f, 0.f}, q16, g4);
 #pragma unroll
-      for (int s = 0; s < r; ++s) acc -= Lr[s] * x[s];
-      x[r] = acc;
+      for (int e = 0; e < 4; ++e) Tij[(4 * g4 + e) * TS + q16] = -y[e];
     }
-    T* dst = static_cast<T*>(is_w ? a.W : a.Up);
+    __syncthreads();
+  }
+
+  // 4. outputs: wave w takes token tile w % CT and every (NW/CT)-th column
+  // tile; lane: token r = 16 tt + lane%16, features 16 nt + 4 (lane/16) + e
+  constexpr int WPT = NW / CT;  // waves per token tile
+  const int tt = wv % CT, r = 16 * tt + q16;
+  T* Wg = static_cast<T*>(a.W);
+  T* Ug = static_cast<T*>(a.Up);
+  if constexpr (sizeof(T) == 2) {
+    constexpr int KSC = C / 32;
+    const int nks = tt / 2 + 1;  // 32-token steps that reach token tile tt
+    bf16x8 uh[KSC], ul[KSC], wh[KSC], wl[KSC];
 #pragma unroll
-    for (int r = 0; r < C; ++r) dst[(row0 + (int64_t)r * a.H) * D + c] = from_f32<T>(x[r]);
+    for (int s = 0; s < KSC; ++s) {
+      if (s < nks) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int k0 = 32 * s + 16 * half + 4 * g4;
+          const f32x4 tv = *reinterpret_cast<const f32x4*>(Tm + r * TS + k0);
+          const f32x4 bv = *reinterpret_cast<const f32x4*>(bl + k0);
+          const f32x4 sv = *reinterpret_cast<const f32x4*>(sl + k0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float u = tv[e] * bv[e], w = tv[e] * sv[e];
+            const bf16 u0 = (bf16)u, w0 = (bf16)w;
+            uh[s][4 * half + e] = u0;
+            ul[s][4 * half + e] = (bf16)(u - (float)u0);
+            wh[s][4 * half + e] = w0;
+            wl[s][4 * half + e] = (bf16)(w - (float)w0);
+          }
+        }
+      }
+    }
+    for (int nt = wv / CT; nt < DT; nt += WPT) {
+      bf16x8 kf[KSC], vf[KSC];
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) {
+        kf[s] = frag_col<T, C, D>(smem + SM::KOFF, 16 * nt, s, lane);
+        vf[s] = frag_col<T, C, D>(smem + SM::VOFF, 16 * nt, s, lane);
+      }
+      lds_wait(kf, vf);
+      f32x4 ow = f32x4{0.f, 0.f, 0.f, 0.f}, ou = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) {
+        if (s < nks) {
+          ow = M::mma(kf[s], wh[s], ow);
+          ow = M::mma(kf[s], wl[s], ow);
+          ou = M::mma(vf[s], uh[s], ou);
+          ou = M::mma(vf[s], ul[s], ou);
+        }
+      }
+      const int64_t o = (row0 + (int64_t)r * a.H) * D + 16 * nt + 4 * g4;
+      *reinterpret_cast<Vec4*>(Wg + o) = Vec4{(T)ow[0], (T)ow[1], (T)ow[2], (T)ow[3]};
+      *reinterpret_cast<Vec4*>(Ug + o) = Vec4{(T)ou[0], (T)ou[1], (T)ou[2], (T)ou[3]};
+    }
+  } else {
+    constexpr int KSC = C / 4;
+    const int nks = 4 * (tt + 1);  // 4-token steps that reach token tile tt
+    float ub[KSC], wb[KSC];
+#pragma unroll
+    for (int s = 0; s < KSC; ++s) {
+      const int k = M::kidx(s, g4, 0);
+      ub[s] = Tm[r * TS + k] * bl[k];
+      wb[s] = Tm[r * TS + k] * sl[k];
+    }
+    for (int nt = wv / CT; nt < DT; nt += WPT) {
+      f32x4 ow = f32x4{0.f, 0.f, 0.f, 0.f}, ou = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) {
+        if (s < nks) {
+          ow = M::mma(frag_col<T, C, D>(smem + SM::KOFF, 16 * nt, s, lane), wb[s], ow);
+          ou = M::mma(frag_col<T, C, D>(smem + SM::VOFF, 16 * nt, s, lane), ub[s], ou);
+        }
+      }
+      const int64_t o = (row0 + (int64_t)r * a.H) * D + 16 * nt + 4 * g4;
+      *reinterpret_cast<Vec4*>(Wg + o) = ow;
+      *reinterpret_cast<Vec4*>(Ug + o) = ou;
+    }
   }
 }
 
@@ -248,7 +378,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) ll_gdn_state(GdnArgs a) {
 template <typename T, int D, int C>
 static hipError_t launch_wy_t(const GdnArgs& a, hipStream_t s) {
   const int grid = a.B * a.H * (a.T / C);
-  hipLaunchKernelGGL((ll_gdn_wy<T, D, C>), dim3(grid), dim3(WySmem<T, D, C>::NT), 0, s, a);
+  hipLaunchKernelGGL((ll_gdn_wy<T, D, C>), dim3(grid), dim3(64 * WySmem<T, D, C>::NW), 0, s, a);
   return hipGetLastError();
 }
 
