@@ -17,41 +17,48 @@ namespace llattn {
 
 constexpr int kScanDepth = 20;  // up to 2^20 blocks per head
 
-// One thread per (head, state element); walks the blocks of its head in
-// order, keeping the pending node of every level in registers (the same merge
-// rule as a decode step, at block granularity).  The block states are read in
-// batches of kScanBatch, all in flight at once: consecutive lanes read
-// consecutive floats of one state, so every load instruction moves 256 bytes.
+// One thread per (head, four consecutive state elements); walks the blocks
+// of its head in order, keeping the pending node of every level in registers
+// (the same merge rule as a decode step, at block granularity).  The block
+// states are read in batches of kScanBatch, all in flight at once:
+// consecutive lanes read consecutive 16-byte pieces of one state, so every
+// load and store instruction moves 1 KiB.
 constexpr int kScanBatch = 32;  // a power of two
 
 template <int D>
 __global__ void __launch_bounds__(256) ll_fenwick_scan(PrefillArgs a) {
-  constexpr int G = D * D;  // floats per state
+  constexpr int G = D * D / 4;  // 16-byte pieces per state
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (int64_t)a.B * a.H * G) return;
   const int bh = (int)(gid / G), el = (int)(gid % G);
-  const float* __restrict__ S = a.S + (int64_t)bh * a.nb * G + el;
+  const f32x4* __restrict__ S = reinterpret_cast<const f32x4*>(a.S) + (int64_t)bh * a.nb * G + el;
   const float* __restrict__ GS = a.GS + (int64_t)bh * a.nb;
-  float* __restrict__ F = a.F + (int64_t)bh * a.nF * G + el;
+  f32x4* __restrict__ F = reinterpret_cast<f32x4*>(a.F) + (int64_t)bh * a.nF * G + el;
   float* __restrict__ GF = a.GF + (int64_t)bh * a.nF;
 
-  float stack[kScanDepth], gstack[kScanDepth];
+  f32x4 stack[kScanDepth];
+  float gstack[kScanDepth];
 #pragma unroll
-  for (int l = 0; l < kScanDepth; ++l) stack[l] = gstack[l] = 0.f;
+  for (int l = 0; l < kScanDepth; ++l) {
+    stack[l] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gstack[l] = 0.f;
+  }
 
   for (int e0 = 0; e0 < a.nb; e0 += kScanBatch) {
-    float in[kScanBatch], gin[kScanBatch];
+    f32x4 in[kScanBatch];
+    float gin[kScanBatch];
 #pragma unroll
     for (int u = 0; u < kScanBatch; ++u) {
       const int e = e0 + u;
-      in[u] = e < a.nb ? S[(int64_t)e * G] : 0.f;
+      in[u] = e < a.nb ? S[(int64_t)e * G] : f32x4{0.f, 0.f, 0.f, 0.f};
       gin[u] = e < a.nb ? GS[e] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < kScanBatch; ++u) {
       const int e = e0 + u;
       if (e >= a.nb) break;
-      float cur = in[u], gc = gin[u];
+      f32x4 cur = in[u];
+      float gc = gin[u];
       // e0 is a multiple of the batch, so below its last step ctz(e+1) is a
       // compile-time constant and the level updates are straight-line code
       const int z = (u + 1 < kScanBatch) ? __builtin_ctz(u + 1) : __ffs(e + 1) - 1;
@@ -128,7 +135,7 @@ __global__ void __launch_bounds__(256) ll_state_export(PrefillArgs a, int logCP)
 }
 
 hipError_t launch_fenwick_scan(int D, const PrefillArgs& a, hipStream_t s) {
-  const int64_t threads = (int64_t)a.B * a.H * D * D;
+  const int64_t threads = (int64_t)a.B * a.H * D * D / 4;
   const int grid = (int)((threads + 255) / 256);
   switch (D) {
     case 16: hipLaunchKernelGGL((ll_fenwick_scan<16>), dim3(grid), dim3(256), 0, s, a); break;
