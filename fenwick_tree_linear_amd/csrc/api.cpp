@@ -62,7 +62,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
   int Cr;  // chunk size of the log-linear read (C, or smaller for Gated DeltaNet when a tile would not fit)
   int P, nb, nF, LS;
-  size_t s_off, gs_off, f_off, gf_off;
+  size_t s_off, gs_off, f_off, gf_off, n16_off;
   size_t w_off, up_off, u_off;  // Gated DeltaNet: W, U' and the pseudo-values U
   size_t bytes;
 };
@@ -126,6 +126,11 @@ ll_status plan_prefill(const ll_problem* p, bool exporting, Plan* out) {
   off = align256(off + bh * pl.nF * dd * sizeof(float));
   pl.gf_off = off;
   off = align256(off + bh * (pl.nF > 0 ? pl.nF : 1) * sizeof(float));
+  pl.n16_off = 0;
+  if (llattn::node_copies(p->io == LL_BF16 ? 1 : 0, p->dk) && pl.nb > 1) {  // bf16 copies of the nodes the read takes
+    pl.n16_off = off;
+    off = align256(off + bh * pl.nb * dd * 2);
+  }
   pl.w_off = pl.up_off = pl.u_off = 0;
   if (p->rule == LL_GATED_DELTANET) {
     const size_t rows = (size_t)p->B * p->T * p->H * p->dk * esz;
@@ -281,6 +286,8 @@ ll_status ll_attn_fwd(const ll_problem* p, const void* q, const void* k, const v
   a.GS = reinterpret_cast<float*>(ws + pl.gs_off);
   a.F = reinterpret_cast<float*>(ws + pl.f_off);
   a.GF = reinterpret_cast<float*>(ws + pl.gf_off);
+  a.N16 = (llattn::node_copies(p->io == LL_BF16 ? 1 : 0, p->dk) && pl.nb > 1) ? static_cast<void*>(ws + pl.n16_off)
+                                                                                : nullptr;
   a.state = static_cast<float*>(state_out);
   const int io = p->io == LL_BF16 ? 1 : 0;
   const int D = p->dk;

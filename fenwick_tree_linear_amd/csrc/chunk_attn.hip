@@ -414,6 +414,18 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
     auto node_of = [&](int e) {
       return (e & 1) ? a.F + ((int64_t)bh * a.nF + (e >> 1)) * D * D : a.S + ((int64_t)bh * a.nb + e) * D * D;
     };
+    // MFMA fragments of node e for this wave's columns: from the bf16 copies
+    // in fragment order where they exist (one 16-byte load per fragment),
+    // else from the fp32 nodes
+    auto load_node = [&](Frag(&nf)[KSD], int e) __attribute__((always_inline)) {
+      if constexpr (node_copies(sizeof(T) == 2 ? 1 : 0, D)) {
+        const bf16x8* src = static_cast<const bf16x8*>(a.N16) + ((int64_t)bh * a.nb + e) * (D * D / 8) + wc * KSD * 64 + lane;
+#pragma unroll
+        for (int s = 0; s < KSD; ++s) nf[s] = src[s * 64];
+      } else {
+        node_frags<T, D>(nf, node_of(e), wc, lane);
+      }
+    };
     auto gamma_of = [&](int e) {
       return (e & 1) ? a.GF[(int64_t)bh * a.nF + (e >> 1)] : a.GS[(int64_t)bh * a.nb + e];
     };
@@ -429,7 +441,7 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
         hdd[x] = 0.f;
         if (rest_far > 0) {
           const int e = rest_far - 1;
-          node_frags<T, D>(hn[x], node_of(e), wc, lane);
+          load_node(hn[x], e);
           hlv[x] = LOGC + 1 + logP + __ffs(rest_far) - 1;  // token level of the node
           hdd[x] = dd_far;
           dd_far += gamma_of(e);
@@ -574,7 +586,7 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
         while (rest > 0) {
           const int e = rest - 1;
           Frag nf[KSD];
-          node_frags<T, D>(nf, node_of(e), wc, lane);
+          load_node(nf, e);
           const int lev = LOGC + 1 + logP + __ffs(rest) - 1;
           const float sc = __expf(gw + dd);
           float al[NRT];

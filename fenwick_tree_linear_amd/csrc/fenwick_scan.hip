@@ -30,11 +30,28 @@ __global__ void __launch_bounds__(256) ll_fenwick_scan(PrefillArgs a) {
   constexpr int G = D * D / 4;  // 16-byte pieces per state
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (int64_t)a.B * a.H * G) return;
-  const int bh = (int)(gid / G), el = (int)(gid % G);
+  const int bh = (int)(gid / G), w = (int)(gid % G);
+  // With the bf16 copy (below) threads are ordered by its layout, w = ((nt
+  // KSD + s) 64 + l) 2 + h: the thread takes lane l of tile (2s + h, nt) of
+  // the state tile layout, so a wave reads and writes fp32 as two runs of 512
+  // bytes and writes its bf16 copy as one run of 512 bytes.  Without it, w is
+  // the tile layout itself (runs of 1 KiB).
+  int el = w;
+  if (D >= 32 && a.N16) {
+    constexpr int NCT = D / 16, KSD = D >= 32 ? D / 32 : 1;
+    const int h = w & 1, l = (w >> 1) & 63, f = w >> 7, nt = f / KSD, st = f % KSD;
+    el = ((2 * st + h) * NCT + nt) * 64 + l;
+  }
   const f32x4* __restrict__ S = reinterpret_cast<const f32x4*>(a.S) + (int64_t)bh * a.nb * G + el;
   const float* __restrict__ GS = a.GS + (int64_t)bh * a.nb;
   f32x4* __restrict__ F = reinterpret_cast<f32x4*>(a.F) + (int64_t)bh * a.nF * G + el;
   float* __restrict__ GF = a.GF + (int64_t)bh * a.nF;
+  // bf16 copy of every node in MFMA fragment order: this thread's four values
+  // are half h of lane l's fragment s for wave column nt
+  bf16x4* N16 = nullptr;
+  if constexpr (D >= 32) {
+    if (a.N16) N16 = static_cast<bf16x4*>(a.N16) + (int64_t)bh * a.nb * G + w;
+  }
 
   f32x4 stack[kScanDepth];
   float gstack[kScanDepth];
@@ -73,6 +90,7 @@ __global__ void __launch_bounds__(256) ll_fenwick_scan(PrefillArgs a) {
         F[(int64_t)(e >> 1) * G] = cur;
         if (el == 0) GF[e >> 1] = gc;
       }
+      if (N16) N16[(int64_t)e * G] = bf16x4{(bf16)cur[0], (bf16)cur[1], (bf16)cur[2], (bf16)cur[3]};
 #pragma unroll
       for (int l = 0; l < kScanDepth; ++l) {
         if (l == z) {

@@ -28,6 +28,10 @@ struct PrefillArgs {
   float* GS;  // [B*H, nb] sum of log-gates of each block
   float* F;   // [B*H, nF, D*D] Fenwick nodes of level >= 1 (odd block index e at e/2)
   float* GF;  // [B*H, nF]
+  // with node_copies(): every Fenwick node (index e: S[e] for even e, F[e/2]
+  // for odd e) as bf16 MFMA A fragments, [B*H, nb, D/16 wave columns, D/32
+  // steps, 64 lanes, 8]; NULL otherwise
+  void* N16;
   float* state;  // nullable export target [B,H,L,D,D] + sigma [B,H,L]
 };
 
@@ -76,5 +80,10 @@ inline int ilog2_host(int x) {
 
 // largest within-block Fenwick depth the chunk kernels hold in registers
 constexpr int max_block_depth(int D) { return D >= 128 ? 2 : 3; }
+
+// Whether the read takes the block-level Fenwick nodes from bf16 copies in
+// fragment order (PrefillArgs::N16): for bf16 io at head sizes where no node
+// is held in registers across a block, so that every chunk reads its nodes.
+constexpr bool node_copies(int io, int D) { return io == 1 && D > 64; }
 
 }  // namespace llattn
