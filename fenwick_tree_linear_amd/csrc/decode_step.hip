@@ -28,10 +28,13 @@ __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
   constexpr int CG = D / 4;      // column groups of 4 floats
   constexpr int RG = NTH / CG;   // row groups
   constexpr int RPT = D / RG;    // rows per thread
-  // levels whose rows are in flight together (at most 16 f32x4 rows per thread)
-  constexpr int kDecodeBatch = RPT >= 16 ? 1 : (16 / RPT < 4 ? 16 / RPT : 4);
+  // levels whose rows are in flight together (at most 20 f32x4 rows per
+  // thread, so that four workgroups fit a CU: all heads of the 32K decode
+  // workload in one round)
+  constexpr int kDecodeBatch = RPT >= 20 ? 1 : (20 / RPT < 5 ? 20 / RPT : 5);
   __shared__ float qs[D], ks[D], vs[D], us[D];
   __shared__ float lam[kDecodeLevelsMax], sig[kDecodeLevelsMax];
+  __shared__ float qk_s;
   __shared__ __attribute__((aligned(16))) float red[RG][D];
   __shared__ __attribute__((aligned(16))) float redk[RG][D];  // Gated DeltaNet: the levels read by k
 
@@ -41,14 +44,41 @@ __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
   const int64_t pos = a.pos;
   float* Sh = a.state + (int64_t)bh * L * D * D;
   float* sigma = a.state + (int64_t)a.B * a.H * L * D * D + (int64_t)bh * L;
+  const int c = __ffsll((unsigned long long)(pos + 1)) - 1;
+  const bool gdn = a.beta != nullptr;
+
+  // Non-empty levels l >= 1 are the set bits l-1 of pos.  The rows of the
+  // first kDecodeBatch of them are put in flight before anything else, so
+  // their latency overlaps the loads of the token's q, k, v and weights.
+  uint64_t bits = (uint64_t)pos & ((L - 1 >= 64) ? ~0ull : ((1ull << (L - 1)) - 1));
+  int lv[kDecodeBatch];
+  f32x4 rows[kDecodeBatch][RPT];
+#pragma unroll
+  for (int u = 0; u < kDecodeBatch; ++u) {
+    lv[u] = bits ? __ffsll((unsigned long long)bits) : 0;  // level = bit index + 1; 0 = none
+    bits &= bits - 1;
+    if (lv[u] == 0) continue;
+    const float* lev = Sh + (int64_t)lv[u] * D * D + 4 * cg;
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr) rows[u][rr] = *reinterpret_cast<const f32x4*>(lev + (rr * RG + rg) * D);
+  }
 
   const T* q = static_cast<const T*>(a.q) + (int64_t)bh * D;
   const T* k = static_cast<const T*>(a.k) + (int64_t)bh * D;
   const T* v = static_cast<const T*>(a.v) + (int64_t)bh * D;
-  for (int x = tid; x < D; x += NTH) {
-    qs[x] = to_f32(q[x]);
-    ks[x] = to_f32(k[x]);
-    vs[x] = to_f32(v[x]);
+  if (tid < 64) {
+    // q.k by one wave: lane x holds q_x k_x (+ q_{x+64} k_{x+64}), then a butterfly
+    float pk = 0.f;
+    for (int x = tid; x < D; x += 64) {
+      const float qx = to_f32(q[x]), kx = to_f32(k[x]);
+      qs[x] = qx;
+      ks[x] = kx;
+      vs[x] = to_f32(v[x]);
+      pk += qx * kx;
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) pk += __shfl_xor(pk, m, 64);
+    if (tid == 0) qk_s = pk;
   }
   const float loga = a.g[bh];
   for (int x = tid; x < L; x += NTH) {
@@ -57,32 +87,12 @@ __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
   }
   __syncthreads();
 
-  const int c = __ffsll((unsigned long long)(pos + 1)) - 1;
-  const bool gdn = a.beta != nullptr;
   f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 kpart = f32x4{0.f, 0.f, 0.f, 0.f};  // Gated DeltaNet: sum_l e^{sigma_l} S_hat_l^T k
   f32x4 msum[RPT];
 #pragma unroll
   for (int rr = 0; rr < RPT; ++rr) msum[rr] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // non-empty levels l >= 1 are the set bits l-1 of pos; their rows are
-  // loaded kDecodeBatch levels at a time, all in flight before any is used
-  uint64_t bits = (uint64_t)pos & ((L - 1 >= 64) ? ~0ull : ((1ull << (L - 1)) - 1));
-  while (bits) {
-    int lv[kDecodeBatch];
-#pragma unroll
-    for (int u = 0; u < kDecodeBatch; ++u) {
-      lv[u] = bits ? __ffsll((unsigned long long)bits) : 0;  // level = bit index + 1; 0 = none
-      bits &= bits - 1;
-    }
-    f32x4 rows[kDecodeBatch][RPT];
-#pragma unroll
-    for (int u = 0; u < kDecodeBatch; ++u) {
-      if (lv[u] == 0) continue;
-      const float* lev = Sh + (int64_t)lv[u] * D * D + 4 * cg;
-#pragma unroll
-      for (int rr = 0; rr < RPT; ++rr) rows[u][rr] = *reinterpret_cast<const f32x4*>(lev + (rr * RG + rg) * D);
-    }
+  for (;;) {
 #pragma unroll
     for (int u = 0; u < kDecodeBatch; ++u) {
       if (lv[u] == 0) continue;
@@ -100,14 +110,23 @@ __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
         for (int rr = 0; rr < RPT; ++rr) msum[rr] += decay * rows[u][rr];
       }
     }
+    if (!bits) break;
+    // further levels (more than kDecodeBatch set bits), a batch at a time
+#pragma unroll
+    for (int u = 0; u < kDecodeBatch; ++u) {
+      lv[u] = bits ? __ffsll((unsigned long long)bits) : 0;
+      bits &= bits - 1;
+      if (lv[u] == 0) continue;
+      const float* lev = Sh + (int64_t)lv[u] * D * D + 4 * cg;
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr) rows[u][rr] = *reinterpret_cast<const f32x4*>(lev + (rr * RG + rg) * D);
+    }
   }
 
   *reinterpret_cast<f32x4*>(&red[rg][4 * cg]) = part;
   if (gdn) *reinterpret_cast<f32x4*>(&redk[rg][4 * cg]) = kpart;
   __syncthreads();
   if (tid < D) {
-    float qk = 0.f;
-    for (int x = 0; x < D; ++x) qk += qs[x] * ks[x];
     float acc = 0.f;
     for (int r = 0; r < RG; ++r) acc += red[r][tid];
     // the value this token writes: v, or for Gated DeltaNet its pseudo-value
@@ -119,7 +138,7 @@ __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
       u = a.beta[bh] * (vs[tid] - sk);
       us[tid] = u;
     }
-    static_cast<T*>(a.o)[(int64_t)bh * D + tid] = from_f32<T>(lam[0] * qk * u + acc);
+    static_cast<T*>(a.o)[(int64_t)bh * D + tid] = from_f32<T>(lam[0] * qk_s * u + acc);
   }
   if (gdn) __syncthreads();
 
