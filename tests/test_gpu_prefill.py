@@ -65,6 +65,20 @@ def test_prefill_16k_sampled():
         check(f"prefill-16k tokens [{lo},{hi})", o[:, lo:hi], ref[:, lo:hi], "bf16")
 
 
+@pytest.mark.parametrize("io,T,d,C,L", [("bf16", 32768, 64, 64, 16), ("bf16", 16384, 32, 32, 15)])
+def test_many_blocks_no_decay(io, T, d, C, L):
+    """64 blocks of 8 chunks per head: block 63 has six earlier-block Fenwick
+    nodes, one more than the read holds in registers, so its last node comes
+    through the per-chunk path.  No decay, so every node carries weight."""
+    w = W.Workload("many blocks", W.MAMBA2, 1, 2, T, d, d, L, C, io, 31 + d)
+    x = W.prefill_inputs(w, variant="nodecay")
+    o = gpu_prefill(x, C, L)
+    assert np.isfinite(o).all()
+    for lo, hi in ((T - 64, T), (T * 47 // 64, T * 47 // 64 + 32)):
+        ref = oracle_prefill(x, t_range=(lo, hi))
+        check(f"{io} T{T} d{d} C{C} no decay, tokens [{lo},{hi})", o[:, lo:hi], ref[:, lo:hi], io)
+
+
 @pytest.mark.parametrize("variant", ["nodecay", "slowdecay", "deep"])
 def test_every_level_bf16(variant):
     """Inputs under which high levels carry weight (no or slow decay), and
