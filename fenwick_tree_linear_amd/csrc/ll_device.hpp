@@ -126,10 +126,13 @@ __device__ __forceinline__ int state_tile_offset(int dt, int nt, int lane) {
 
 // ------------------------------------------------------------ LDS tiles
 // Row-major [ROWS][COLS] tile of T in LDS.  Rows are stored unpadded and the
-// 16-byte chunks of row r are permuted by XOR with a function of r, so that
-// the 16 rows touched by one fragment read fall on different banks: the 64
-// four-byte banks span 256 bytes, i.e. RP = 256 / row-bytes rows, and rows
-// r and r + RP would collide, so the XOR key is (r / RP) mod chunks-per-row.
+// 16-byte chunks of row r are permuted by XOR with a key of r, so that the
+// accesses of a fragment read spread over the 64 four-byte banks (256 bytes,
+// RP = 256 / row-bytes rows).  The key is x = (r / RP) mod chunks-per-row
+// with its bits rotated left by one: x alone keeps the 16 rows of a row-wise
+// fragment read apart, and the rotation also keeps apart the rows r and r + 2
+// that one 16-lane group of a transposing read takes the same two chunks of
+// (with x alone they collided, two-way).
 template <typename T, int ROWS, int COLS>
 struct Tile {
   static constexpr int ESZ = sizeof(T);
@@ -137,8 +140,17 @@ struct Tile {
   static constexpr int NCH = RB / 16;    // 16-byte chunks per row
   static constexpr int BYTES = ROWS * RB;
   static constexpr int RP = RB >= 256 ? 1 : 256 / RB;  // rows per bank sweep
+  static constexpr int KB = NCH >= 16 ? 4 : NCH >= 8 ? 3 : NCH >= 4 ? 2 : NCH >= 2 ? 1 : 0;  // key bits
   static_assert((NCH & (NCH - 1)) == 0 && NCH >= 1, "rows must be a power-of-two number of 16-byte chunks");
-  __device__ __forceinline__ static int pos(int row, int chunk) { return chunk ^ ((row / RP) & (NCH - 1)); }
+  __device__ __forceinline__ static int key(int row) {
+    const int x = (row / RP) & (NCH - 1);
+    if constexpr (KB > 1) {
+      return ((x << 1) | (x >> (KB - 1))) & (NCH - 1);
+    } else {
+      return x;
+    }
+  }
+  __device__ __forceinline__ static int pos(int row, int chunk) { return chunk ^ key(row); }
   // byte offset of element (row, col)
   __device__ __forceinline__ static int off(int row, int col) {
     const int byte = col * ESZ;
