@@ -192,6 +192,8 @@ def main() -> int:
                     help="also time this many ll_decode_step tokens on the decode workload (0: skip)")
     ap.add_argument("--gdn-steps", type=int, default=20,
                     help="also time this many Gated DeltaNet prefill steps on its 8K-token workload (0: skip)")
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="also time this many single steps with the last-level cache flushed before each (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -245,6 +247,26 @@ def main() -> int:
     ms_per_step = start_ev.elapsed_time(stop_ev) / args.steps
     log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (events), wall {wall * 1e3 / args.steps:.1f} us")
 
+    # cold: the 256 MB last-level cache flushed by writing a 512 MiB buffer
+    # before each of a few individually timed steps (median reported)
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    cold_ms = []
+    for r in range(args.cold_reps):
+        flush.fill_(float(r))
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_ev.record(stream)
+        step()
+        b_ev.record(stream)
+        torch.cuda.synchronize()
+        cold_ms.append(a_ev.elapsed_time(b_ev))
+    del flush
+    cold = None
+    if cold_ms:
+        med = sorted(cold_ms)[len(cold_ms) // 2]
+        cold = {"ms_per_step_median": round(med, 5), "tokens_per_s": round(w.B * w.T / (med * 1e-3), 1),
+                "reps": len(cold_ms), "flush_bytes": 512 * 1024 * 1024}
+        log(f"[bench] cold (last-level cache flushed): median {med * 1e3:.1f} us/step over {len(cold_ms)} steps")
+
     # per-kernel durations: HIP events around every launch, on the launch stream
     F.ll_kernel_timing_enable(True)
     for _ in range(args.steps):
@@ -286,6 +308,7 @@ def main() -> int:
                  "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                  "frac_step": round(flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
         "kernels_us": kernels,
+        "cold": cold,
         "cpu_baseline": None,
     }
     if args.decode_steps:
