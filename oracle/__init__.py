@@ -7,9 +7,11 @@ with it.
 
 The arithmetic lives in ``llref.c`` (plain C, fp64, OpenMP over heads); this
 module builds it with gcc and wraps it for numpy arrays.  Every function states
-the passage of the "Log-Linear Attention" page (technical summary, section 2)
-that it evaluates; the pins that tie it to the page and to the mathematics are
-in ``tests/test_oracle_pins.py``.
+the passage it evaluates: of the "Log-Linear Attention" page (technical
+summary, section 2) for the attention itself, of the "Adaptive memory decay for
+log-linear attention" page (section "Method") for the level-weight MLP.  The
+pins that tie it to the pages and to the mathematics are in
+``tests/test_oracle_pins.py``.
 """
 
 from __future__ import annotations
@@ -71,6 +73,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.llref_fwd_recurrent.restype = i32
     lib.llref_decode_step.argtypes = [i32] * 6 + [i64] + [P] * 8
     lib.llref_decode_step.restype = i32
+    lib.llref_lambda_mlp.argtypes = [i64, i32, i32] + [P] * 5
+    lib.llref_lambda_mlp.restype = i32
     return lib
 
 
@@ -186,3 +190,23 @@ def decode_step(state, pos, q, k, v, log_gate, lam, beta=None, rule=RULE_MAMBA2,
                                            _ptr(lam), _ptr(beta), _ptr(o), _ptr(state))
     _check(rc, "llref_decode_step")
     return o
+
+
+def lambda_mlp(d, w1, w2, bias, lib=None) -> np.ndarray:
+    """Level weights from the adaptive-decay MLP ("Adaptive memory decay for
+    log-linear attention", section "Method", LambdaMLPSoftplus):
+    ``lambda = softplus((d W1) W2 + b)`` per token and head, fp64.
+
+    ``d`` [..., L] (any leading axes), ``w1`` [L, hidden], ``w2`` [hidden, L],
+    ``bias`` [L]; returns lambda with the shape of ``d``.
+    """
+    d, w1, w2, bias = map(_f32, (d, w1, w2, bias))
+    L = d.shape[-1]
+    hidden = w1.shape[1]
+    if w1.shape != (L, hidden) or w2.shape != (hidden, L) or bias.shape != (L,):
+        raise ValueError("lambda_mlp: inconsistent arguments")
+    rows = d.size // L
+    lam = np.empty(d.shape, dtype=np.float64)
+    rc = (lib or load()).llref_lambda_mlp(rows, L, hidden, _ptr(d), _ptr(w1), _ptr(w2), _ptr(bias), _ptr(lam))
+    _check(rc, "llref_lambda_mlp")
+    return lam

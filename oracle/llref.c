@@ -14,9 +14,12 @@
  *     [0,t) is split into at most L = O(log T) disjoint buckets by the Fenwick
  *     decomposition;
  *   - 2.3: a recurrent form with O(log T) state for decoding;
- *   - section 3: applied to Mamba-2 and Gated DeltaNet "keeping their structure".
+ *   - section 3: applied to Mamba-2 and Gated DeltaNet with their structure kept.
  *
- * Readings taken where the page is silent (each is listed in the design doc):
+ * The level weights may come from the adaptive-decay MLP of "Adaptive memory
+ * decay for log-linear attention" (section "Method"): llref_lambda_mlp.
+ *
+ * Readings taken where the page is silent:
  *   - tokens are 0-based; bucket level 0 is the token itself; a bucket of level
  *     l >= 1 holds 2^(l-1) tokens;
  *   - Mamba-2 write: S_t = a_t S_{t-1} + k_t v_t^T, so source s reaches position
@@ -425,6 +428,47 @@ int llref_decode_step(int B, int H, int dk, int dv, int L, int rule, int64_t pos
                     beta ? beta[i] : 0.0, state + (size_t)i * L * per_level,
                     o + (size_t)i * dv, scratch, 1);
     free(scratch);
+  }
+  if (bad) return LLREF_ENOMEM;
+  return LLREF_OK;
+}
+
+/*
+ * The level weights from the adaptive-decay MLP ("Adaptive memory decay for
+ * log-linear attention", section "Method", LambdaMLPSoftplus): for every token
+ * and head, with d the baseline's per-level representation,
+ *   h = d W1            (d [L], W1 [L][hidden])
+ *   z = h W2 + b        (W2 [hidden][L], b [L])
+ *   lambda = softplus(z) = log(1 + e^z)
+ * in that order, layer by layer, in double precision.  softplus is evaluated
+ * as max(z, 0) + log1p(e^-|z|), which is log(1 + e^z) without overflow.
+ * d and lambda are [rows][L] (rows = B*T*H, or B*H for one decode step).
+ */
+int llref_lambda_mlp(int64_t rows, int L, int hidden, const float *d, const float *w1,
+                     const float *w2, const float *bias, double *lambda) {
+  if (rows < 0 || L < 1 || hidden < 1) return LLREF_EARG;
+  if (rows > 0 && (!d || !w1 || !w2 || !bias || !lambda)) return LLREF_EARG;
+  int bad = 0;
+
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t r = 0; r < rows; r++) {
+    double *h = (double *)malloc(sizeof(double) * hidden);
+    if (!h) {
+      bad |= 2;
+      continue;
+    }
+    const float *dr = d + r * L;
+    for (int j = 0; j < hidden; j++) {
+      double acc = 0.0;
+      for (int m = 0; m < L; m++) acc += (double)dr[m] * (double)w1[(size_t)m * hidden + j];
+      h[j] = acc;
+    }
+    for (int l = 0; l < L; l++) {
+      double z = (double)bias[l];
+      for (int j = 0; j < hidden; j++) z += h[j] * (double)w2[(size_t)j * L + l];
+      lambda[r * L + l] = (z > 0.0 ? z : 0.0) + log1p(exp(-fabs(z)));
+    }
+    free(h);
   }
   if (bad) return LLREF_ENOMEM;
   return LLREF_OK;

@@ -36,6 +36,12 @@ MUTANTS = [
     ("gdn u ignores decay", "double w = exp(logw) * dot_f(kt, ks, d->dk);", "double w = dot_f(kt, ks, d->dk);"),
     ("state decayed one token too far", "double logw = 0.0; /* sum_{r=s+1}^{T-1} log a_r */",
      "double logw = log_gate[ix_tok(&d, b, T - 1, h)];"),
+    ("mlp W1 read transposed", "acc += (double)dr[m] * (double)w1[(size_t)m * hidden + j];",
+     "acc += (double)dr[m] * (double)w1[(size_t)j * L + m];"),
+    ("mlp bias dropped", "double z = (double)bias[l];", "double z = 0.0;"),
+    ("mlp hidden layer activated", "h[j] = acc;", "h[j] = acc > 0.0 ? acc : 0.0;"),
+    ("mlp softplus replaced by exp", "lambda[r * L + l] = (z > 0.0 ? z : 0.0) + log1p(exp(-fabs(z)));",
+     "lambda[r * L + l] = exp(z);"),
 ]
 
 
@@ -129,6 +135,28 @@ def pin_failures(lib):
                 k[0, s, h].astype(np.float64), v[0, s, h].astype(np.float64))
     if not np.allclose(st, ref, rtol=1e-10, atol=1e-10):
         fails.append("state")
+
+    # the level-weight MLP: a hand-worked case, the identity special case and
+    # linearity of the pre-activation
+    d = np.array([[1.0, 2.0]])
+    w1 = np.array([[1, 0, 2, -1], [0, 1, -1, 1]], dtype=np.float64)
+    w2 = np.array([[1, 0], [-1, 0], [5, 7], [1, 10]], dtype=np.float64)
+    lam = oracle.lambda_mlp(d, w1, w2, np.array([0.0, 20.0]), lib=lib)
+    if not (abs(lam[0, 0] - math.log(2.0)) < 1e-15 and abs(lam[0, 1] - 30.0) < 1e-12):
+        fails.append("mlp-hand")
+    x = np.array([[-3.0, -0.5, 0.0, 0.5, 3.0]])
+    if not np.allclose(oracle.lambda_mlp(x, np.eye(5), np.eye(5), np.zeros(5), lib=lib), np.logaddexp(0.0, x),
+                       rtol=1e-14, atol=0):
+        fails.append("mlp-identity")
+    rng = np.random.default_rng(2)
+    w1 = rng.standard_normal((3, 6)).astype(np.float32)
+    w2 = rng.standard_normal((6, 3)).astype(np.float32)
+    b = rng.standard_normal(3).astype(np.float32)
+    d1 = rng.standard_normal((4, 3)).astype(np.float32)
+    pre1 = np.log(np.expm1(oracle.lambda_mlp(d1, w1, w2, b, lib=lib))) - b
+    pre2 = np.log(np.expm1(oracle.lambda_mlp(-d1, w1, w2, b, lib=lib))) - b
+    if not np.allclose(pre1, -pre2, atol=1e-8):
+        fails.append("mlp-linear")
     return fails
 
 

@@ -324,6 +324,84 @@ def test_level_count_limits_are_enforced():
         oracle.decode_step(st, 63, q[:, 0], k[:, 0], v[:, 0], g[:, 0], lam[:, 0])
 
 
+# ------------------------------------------------- level-weight MLP (adaptive decay)
+
+def test_lambda_mlp_initialisation_gives_near_one():
+    """The adaptive-decay page starts W2 at zero and the bias at 0.54, so every
+    weight starts at softplus(0.54), about 1.0, whatever d and W1 are."""
+    rng = np.random.default_rng(3)
+    L = 6
+    d = rng.standard_normal((5, 7, L))
+    w1 = rng.standard_normal((L, 2 * L))
+    lam = oracle.lambda_mlp(d, w1, np.zeros((2 * L, L)), np.full(L, 0.54))
+    assert lam.shape == d.shape
+    assert np.all(np.abs(lam - 1.0) < 1e-3)
+    assert np.allclose(lam, 0.9991627, atol=1e-7)
+
+
+def test_lambda_mlp_hand_worked_example():
+    """L = 2, hidden 4, worked by hand: h = d W1 = [1, 2, 0, 1];
+    h W2 = [1 - 2 + 0 + 1, 0 + 0 + 0 + 10] = [0, 10]; plus b = [0, 20] gives
+    z = [0, 30]; softplus(0) = ln 2, softplus(30) = 30 + ln(1 + e^-30)."""
+    d = np.array([[1.0, 2.0]])
+    w1 = np.array([[1, 0, 2, -1], [0, 1, -1, 1]], dtype=np.float64)
+    w2 = np.array([[1, 0], [-1, 0], [5, 7], [1, 10]], dtype=np.float64)
+    lam = oracle.lambda_mlp(d, w1, w2, np.array([0.0, 20.0]))
+    assert abs(lam[0, 0] - math.log(2.0)) < 1e-15
+    assert abs(lam[0, 1] - 30.0) < 1e-12
+
+
+def test_lambda_mlp_identity_layers_are_softplus():
+    """With W1 = W2 = I (hidden = L) the MLP is softplus(d + b) elementwise:
+    numpy's logaddexp(0, x) is that function, and it is exact far out on both
+    sides (softplus(x) -> e^x for x -> -inf, -> x for x -> +inf, no overflow)."""
+    L = 5
+    d = np.array([[-800.0, -40.0, 0.0, 3.0, 800.0], [0.5, -0.5, 2.0, -2.0, 1e-3]])
+    b = np.array([0.0, 0.0, 0.0, 0.25, 0.0])
+    lam = oracle.lambda_mlp(d, np.eye(L), np.eye(L), b)
+    ref = np.logaddexp(0.0, d.astype(np.float32).astype(np.float64) + b)
+    assert np.allclose(lam, ref, rtol=1e-14, atol=0)
+    assert lam[0, 0] == 0.0 or lam[0, 0] < 1e-300
+    assert abs(lam[0, 1] - math.exp(-40.0)) < 1e-30
+    assert lam[0, 4] == 800.0
+
+
+def test_lambda_mlp_pre_activation_is_linear_in_d():
+    """Between the input and the softplus the two layers are linear maps plus
+    one bias: inverting softplus (log(e^y - 1)) and removing b leaves a map
+    that is additive and homogeneous in d, and equals d W1 W2."""
+    rng = np.random.default_rng(11)
+    L, hid = 7, 14
+    w1 = (rng.standard_normal((L, hid)) / math.sqrt(L)).astype(np.float32)
+    w2 = (rng.standard_normal((hid, L)) * 0.3).astype(np.float32)
+    b = rng.normal(0.54, 0.2, L).astype(np.float32)
+    d1 = rng.standard_normal((4, L)).astype(np.float32)
+    d2 = rng.standard_normal((4, L)).astype(np.float32)
+
+    def pre(d):
+        return np.log(np.expm1(oracle.lambda_mlp(d, w1, w2, b))) - b.astype(np.float64)
+
+    p1, p2, p12 = pre(d1), pre(d2), pre(d1 + d2)
+    assert np.allclose(p12, p1 + p2, atol=1e-9)
+    assert np.allclose(pre(2 * d1), 2 * p1, atol=1e-9)
+    assert np.allclose(p1, d1.astype(np.float64) @ w1.astype(np.float64) @ w2.astype(np.float64), atol=1e-9)
+    assert np.allclose(pre(np.zeros_like(d1)), 0.0, atol=1e-12)
+
+
+def test_lambda_mlp_acts_per_row():
+    """Each token and head is mapped on its own: permuting rows permutes the
+    output, and leading axes do not matter."""
+    rng = np.random.default_rng(5)
+    L = 4
+    w1, w2, b = rng.standard_normal((L, 8)), rng.standard_normal((8, L)), rng.standard_normal(L)
+    d = rng.standard_normal((3, 6, L))
+    lam = oracle.lambda_mlp(d, w1, w2, b)
+    perm = rng.permutation(18)
+    flat = oracle.lambda_mlp(d.reshape(18, L)[perm], w1, w2, b)
+    assert np.array_equal(flat, lam.reshape(18, L)[perm])
+    assert np.all(lam > 0)
+
+
 # --------------------------------------------------------------- generators
 
 def test_softplus_initial_bias_is_near_one():
