@@ -138,6 +138,63 @@ def decode_bench(steps: int) -> dict:
             "frac": round(achieved / HBM_PEAK_GBS, 4)}
 
 
+MFMA_FP32_PEAK_TFLOPS = 157.3  # dense fp32 matrix cores
+
+
+def lambda_mlp_bench(reps: int) -> dict:
+    """ll_lambda_mlp (the adaptive-decay level-weight MLP, hidden 2L) over every row of the 16K
+    prefill (2 x 16384 x 16 rows of 15 levels), back to back, HIP events on the launch stream;
+    then the prefill step with the MLP in front of ll_attn_fwd."""
+    import torch
+
+    import fenwick_tree_linear_amd as F
+    from fenwick_tree_linear_amd import workloads as W
+
+    w = W.WORKLOADS["prefill-16k"]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    m = W.lambda_mlp_inputs((w.B, w.T, w.H), w.L, seed=w.seed, device=dev)
+    rows, L, hidden = w.B * w.T * w.H, w.L, m["w1"].shape[1]
+    lam = torch.empty_like(m["d"])
+
+    def mlp():
+        F.ll_lambda_mlp(rows, L, hidden, m["d"], m["w1"], m["w2"], m["bias"], lam, stream)
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    ms = timed(mlp, reps)
+    nbytes = rows * L * 4 * 2 + (2 * L * hidden + L) * 4
+    flops = 4 * rows * L * hidden
+    x = W.prefill_inputs(w, device=dev, parts=("q", "k", "v", "log_gate"))
+    prob = F.LLProblem(w.B, w.T, w.H, w.dk, w.dv, w.L, w.C, F.LL_BF16, F.LL_MAMBA2)
+    ws_bytes = F.ll_attn_fwd_workspace_bytes(prob)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    o = torch.empty(w.B, w.T, w.H, w.dv, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        mlp()
+        F.ll_attn_fwd(prob, x["q"], x["k"], x["v"], x["log_gate"], lam, None, o, None, ws, ws_bytes, stream)
+
+    step_ms = timed(step, reps)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"ll_lambda_mlp {rows} rows (B2 T16384 H16), L={L}, hidden={hidden}, fp32",
+            "us_per_launch": round(ms * 1e3, 2), "bytes": nbytes, "achieved_GBs": round(gbs, 1),
+            "peak_GBs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "fp32_mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 2), "fp32_mfma_peak_tflops": MFMA_FP32_PEAK_TFLOPS,
+            "prefill_with_mlp": {"ms_per_step": round(step_ms, 5),
+                                 "tokens_per_s": round(w.B * w.T / (step_ms * 1e-3), 1)}}
+
+
 def gdn_bench(steps: int) -> dict:
     """ll_attn_fwd with the Gated DeltaNet write on its 8K-token workload (B2 H16 T8192 d128 bf16,
     14 levels, chunk 64): whole-step time and per-kernel averages, both from HIP events on the
@@ -192,6 +249,8 @@ def main() -> int:
                     help="also time this many ll_decode_step tokens on the decode workload (0: skip)")
     ap.add_argument("--gdn-steps", type=int, default=20,
                     help="also time this many Gated DeltaNet prefill steps on its 8K-token workload (0: skip)")
+    ap.add_argument("--mlp-reps", type=int, default=50,
+                    help="also time this many ll_lambda_mlp launches over the 16K workload's rows (0: skip)")
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="also time this many single steps with the last-level cache flushed before each (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -317,6 +376,9 @@ def main() -> int:
     if args.gdn_steps:
         result["gdn"] = gdn_bench(args.gdn_steps)
         log(f"[bench] gdn: {result['gdn']}")
+    if args.mlp_reps:
+        result["lambda_mlp"] = lambda_mlp_bench(args.mlp_reps)
+        log(f"[bench] lambda mlp: {result['lambda_mlp']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores")
         result["cpu_baseline"] = cpu_baseline(w)

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     LLProblem,
     attn_fwd,
     decode_state_tensor,
+    lambda_mlp,
     lib_path,
     ll_attn_fwd,
     ll_attn_fwd_workspace_bytes,
@@ -23,6 +24,7 @@ from .binding import (  # noqa: F401
     ll_decode_step,
     ll_kernel_timing_enable,
     ll_kernel_timing_read,
+    ll_lambda_mlp,
     ll_last_error,
     load_library,
 )

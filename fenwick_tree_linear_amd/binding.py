@@ -65,8 +65,9 @@ def load_library() -> ctypes.CDLL:
     lib.ll_kernel_timing_enable.argtypes = [i32]
     lib.ll_kernel_timing_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_int), i32, ctypes.POINTER(ctypes.c_int)]
+    lib.ll_lambda_mlp.argtypes = [i64, i32, i32, P, P, P, P, P, P]
     for fn in ("ll_attn_fwd_workspace_bytes", "ll_attn_fwd", "ll_decode_state_bytes", "ll_decode_step",
-               "ll_kernel_timing_enable", "ll_kernel_timing_read"):
+               "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -119,6 +120,11 @@ def ll_decode_state_bytes(B: int, H: int, dk: int, dv: int, L: int) -> int:
 def ll_decode_step(B, H, dk, dv, L, io, rule, pos, q, k, v, log_gate, lam, beta, o, state, stream=None) -> None:
     _check(load_library().ll_decode_step(B, H, dk, dv, L, io, rule, pos, _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
                                          _ptr(lam), _ptr(beta), _ptr(o), _ptr(state), _stream(stream)))
+
+
+def ll_lambda_mlp(rows: int, L: int, hidden: int, d, w1, w2, bias, lam, stream=None) -> None:
+    _check(load_library().ll_lambda_mlp(rows, L, hidden, _ptr(d), _ptr(w1), _ptr(w2), _ptr(bias), _ptr(lam),
+                                        _stream(stream)))
 
 
 def ll_kernel_timing_enable(on: bool) -> None:
@@ -174,3 +180,18 @@ def attn_fwd(q, k, v, log_gate, lam, beta=None, C: int = 64, rule: int = LL_MAMB
         st = torch.empty(ll_decode_state_bytes(B, H, dk, dv, L) // 4, dtype=torch.float32, device=k.device)
     ll_attn_fwd(prob, q, k, v, log_gate, lam, beta, o, st, workspace, workspace.numel(), stream)
     return (o, st) if want_state else o
+
+
+def lambda_mlp(d, w1, w2, bias, out=None, stream=None):
+    """Level weights softplus((d W1) W2 + b) for every row of ``d`` [..., L]
+    (fp32 on the GPU); returns a tensor shaped like ``d``."""
+    L = d.shape[-1]
+    hidden = w1.shape[1]
+    if tuple(w1.shape) != (L, hidden) or tuple(w2.shape) != (hidden, L) or tuple(bias.shape) != (L,):
+        raise ValueError("lambda_mlp: w1 [L, hidden], w2 [hidden, L] and bias [L] must match d [..., L]")
+    for t in (d, w1, w2, bias):
+        if t.dtype != torch.float32:
+            raise TypeError("lambda_mlp takes fp32 tensors")
+    lam = out if out is not None else torch.empty_like(d)
+    ll_lambda_mlp(d.numel() // L, L, hidden, d, w1, w2, bias, lam, stream)
+    return lam

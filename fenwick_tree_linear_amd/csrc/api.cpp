@@ -148,9 +148,9 @@ ll_status plan_prefill(const ll_problem* p, bool exporting, Plan* out) {
 
 // ---------------------------------------------------------- kernel timing
 enum KernelId { K_CHUNK_STATE, K_FENWICK_SCAN, K_CHUNK_ATTN, K_STATE_EXPORT, K_DECODE_STEP, K_GDN_WY, K_GDN_STATE,
-                K_COUNT };
+                K_LAMBDA_MLP, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"ll_chunk_state", "ll_fenwick_scan", "ll_chunk_attn", "ll_state_export",
-                                           "ll_decode_step", "ll_gdn_wy",       "ll_gdn_state"};
+                                           "ll_decode_step", "ll_gdn_wy",       "ll_gdn_state",   "ll_lambda_mlp"};
 
 struct Timing {
   std::mutex mu;
@@ -361,6 +361,23 @@ ll_status ll_decode_step(int B, int H, int dk, int dv, int L, ll_dtype io, ll_ru
   a.state = static_cast<float*>(state);
   const int code = io == LL_BF16 ? 1 : 0;
   hipError_t e = timed(K_DECODE_STEP, stream, [&] { return llattn::launch_decode_step(code, dk, a, stream); });
+  if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ll_status ll_lambda_mlp(int64_t rows, int L, int hidden, const float* d, const float* w1, const float* w2,
+                        const float* bias, float* lambda, hipStream_t stream) {
+  if (rows < 0 || L < 1 || hidden < 1)
+    return fail(LL_ERR_SHAPE, "rows must be >= 0, L and hidden >= 1 (rows=%lld L=%d hidden=%d)", (long long)rows, L,
+                hidden);
+  if (L > 32 || hidden > 64)
+    return fail(LL_ERR_UNSUPPORTED, "L=%d, hidden=%d: at most 32 levels and 64 hidden units are supported", L, hidden);
+  if (rows > ((int64_t)1 << 36)) return fail(LL_ERR_UNSUPPORTED, "rows=%lld is too many for one launch", (long long)rows);
+  if (rows == 0) return ok();  // nothing to compute
+  if (!d || !w1 || !w2 || !bias || !lambda) return fail(LL_ERR_NULL, "d, w1, w2, bias and lambda must not be NULL");
+  if ((const float*)lambda == d) return fail(LL_ERR_SHAPE, "lambda must not alias d");
+  hipError_t e = timed(K_LAMBDA_MLP, stream,
+                       [&] { return llattn::launch_lambda_mlp(rows, L, hidden, d, w1, w2, bias, lambda, stream); });
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -17,20 +17,34 @@ namespace llattn {
 
 constexpr int kScanDepth = 20;  // up to 2^20 blocks per head
 
-// One thread per (head, four consecutive state elements); walks the blocks
-// of its head in order, keeping the pending node of every level in registers
-// (the same merge rule as a decode step, at block granularity).  The block
-// states are read in batches of kScanBatch, all in flight at once:
-// consecutive lanes read consecutive 16-byte pieces of one state, so every
-// load and store instruction moves 1 KiB.
-constexpr int kScanBatch = 32;  // a power of two
+// One thread per (head, four consecutive state elements, segment): the
+// blocks of a head are split into NS aligned segments of 2^seg_log blocks, and
+// each thread walks its segment in order, keeping the pending node of every
+// level in registers (the same merge rule as a decode step, at block
+// granularity).  The block states are read in batches of BATCH, all in flight
+// at once: consecutive lanes read consecutive 16-byte pieces of one state, so
+// every load and store instruction moves 1 KiB.
+//
+// A node whose run of blocks stays inside one segment is finished by that
+// segment's thread.  The node at the last block of segment s covers
+// 2^ctz(s+1) whole segments: the segment totals meet in LDS and the thread of
+// segment s combines them, newest first, with the same merge rule.  Splitting
+// into segments puts NS times more loads in flight when there are few heads.
+constexpr int kScanThreads = 256;
 
-template <int D>
-__global__ void __launch_bounds__(256) ll_fenwick_scan(PrefillArgs a) {
+template <int D, int NS, int BATCH>
+__global__ void __launch_bounds__(kScanThreads) ll_fenwick_scan(PrefillArgs a, int seg_log) {
   constexpr int G = D * D / 4;  // 16-byte pieces per state
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)a.B * a.H * G) return;
-  const int bh = (int)(gid / G), w = (int)(gid % G);
+  constexpr int PW = kScanThreads / NS;  // pieces per workgroup, a multiple of the wave size
+  static_assert(PW % 64 == 0, "a wave must stay inside one segment");
+  __shared__ f32x4 tot[NS > 1 ? NS : 1][PW];
+  __shared__ float gtot[NS > 1 ? NS : 1][PW];
+  const int seg = threadIdx.x / PW, wl = threadIdx.x % PW;
+  // the same head-to-XCD placement as ll_chunk_state (consecutive logical
+  // workgroups on one XCD), so block states are read where they were written
+  const int64_t piece = (int64_t)xcd_logical_id(blockIdx.x, gridDim.x) * PW + wl;
+  const bool active = piece < (int64_t)a.B * a.H * G;
+  const int bh = active ? (int)(piece / G) : 0, w = active ? (int)(piece % G) : 0;
   // With the bf16 copy (below) threads are ordered by its layout, w = ((nt
   // KSD + s) 64 + l) 2 + h: the thread takes lane l of tile (2s + h, nt) of
   // the state tile layout, so a wave reads and writes fp32 as two runs of 512
@@ -61,30 +75,41 @@ __global__ void __launch_bounds__(256) ll_fenwick_scan(PrefillArgs a) {
     gstack[l] = 0.f;
   }
 
-  for (int e0 = 0; e0 < a.nb; e0 += kScanBatch) {
-    f32x4 in[kScanBatch];
-    float gin[kScanBatch];
+  // this thread's blocks [e_begin, e_end); with one segment, all of them
+  const int e_begin = NS > 1 ? seg << seg_log : 0;
+  const int e_last = NS > 1 ? e_begin + (1 << seg_log) - 1 : -1;  // the segment's last block
+  const int e_end = NS > 1 ? min(e_last + 1, a.nb) : a.nb;
+  f32x4 total = f32x4{0.f, 0.f, 0.f, 0.f};
+  float gtotal = 0.f;
+  for (int e0 = e_begin; active && e0 < e_end; e0 += BATCH) {
+    f32x4 in[BATCH];
+    float gin[BATCH];
 #pragma unroll
-    for (int u = 0; u < kScanBatch; ++u) {
+    for (int u = 0; u < BATCH; ++u) {
       const int e = e0 + u;
-      in[u] = e < a.nb ? S[(int64_t)e * G] : f32x4{0.f, 0.f, 0.f, 0.f};
-      gin[u] = e < a.nb ? GS[e] : 0.f;
+      in[u] = e < e_end ? S[(int64_t)e * G] : f32x4{0.f, 0.f, 0.f, 0.f};
+      gin[u] = e < e_end ? GS[e] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < kScanBatch; ++u) {
+    for (int u = 0; u < BATCH; ++u) {
       const int e = e0 + u;
-      if (e >= a.nb) break;
+      if (e >= e_end) break;
       f32x4 cur = in[u];
       float gc = gin[u];
       // e0 is a multiple of the batch, so below its last step ctz(e+1) is a
       // compile-time constant and the level updates are straight-line code
-      const int z = (u + 1 < kScanBatch) ? __builtin_ctz(u + 1) : __ffs(e + 1) - 1;
+      const int z = (u + 1 < BATCH) ? __builtin_ctz(u + 1) : __ffs(e + 1) - 1;
 #pragma unroll
       for (int l = 0; l < kScanDepth; ++l) {
         if (l < z) {
           cur = __expf(gc) * stack[l] + cur;
           gc += gstack[l];
         }
+      }
+      if (e == e_last) {  // the whole segment: finished across segments below
+        total = cur;
+        gtotal = gc;
+        break;
       }
       if (z > 0) {
         F[(int64_t)(e >> 1) * G] = cur;
@@ -98,6 +123,24 @@ __global__ void __launch_bounds__(256) ll_fenwick_scan(PrefillArgs a) {
           gstack[l] = gc;
         }
       }
+    }
+  }
+  if constexpr (NS > 1) {
+    tot[seg][wl] = total;
+    gtot[seg][wl] = gtotal;
+    __syncthreads();
+    if (active && e_last < a.nb) {
+      // node at e_last: segments seg + 1 - 2^m .. seg, m = ctz(seg + 1)
+      const int first = seg + 1 - (1 << __builtin_ctz(seg + 1));
+      f32x4 cur = total;
+      float gc = gtotal;
+      for (int j = seg - 1; j >= first; --j) {
+        cur = __expf(gc) * tot[j][wl] + cur;
+        gc += gtot[j][wl];
+      }
+      F[(int64_t)(e_last >> 1) * G] = cur;
+      if (el == 0) GF[e_last >> 1] = gc;
+      if (N16) N16[(int64_t)e_last * G] = bf16x4{(bf16)cur[0], (bf16)cur[1], (bf16)cur[2], (bf16)cur[3]};
     }
   }
 }
@@ -152,17 +195,41 @@ __global__ void __launch_bounds__(256) ll_state_export(PrefillArgs a, int logCP)
   }
 }
 
-hipError_t launch_fenwick_scan(int D, const PrefillArgs& a, hipStream_t s) {
-  const int64_t threads = (int64_t)a.B * a.H * D * D / 4;
-  const int grid = (int)((threads + 255) / 256);
-  switch (D) {
-    case 16: hipLaunchKernelGGL((ll_fenwick_scan<16>), dim3(grid), dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((ll_fenwick_scan<32>), dim3(grid), dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((ll_fenwick_scan<64>), dim3(grid), dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((ll_fenwick_scan<128>), dim3(grid), dim3(256), 0, s, a); break;
-    default: return hipErrorInvalidValue;
+// Segments per head: enough threads to keep every CU loading (up to 2^17),
+// each segment at least 8 blocks; the batch is at most the segment.
+template <int D>
+hipError_t launch_scan_d(const PrefillArgs& a, hipStream_t s) {
+  constexpr int G = D * D / 4;
+  const int64_t pieces = (int64_t)a.B * a.H * G;
+  int ns = 1;
+  while (ns < 4 && pieces * ns < ((int64_t)1 << 17) && (a.nb + 2 * ns - 1) / (2 * ns) >= 8) ns *= 2;
+  int seg_log = 0;
+  while ((int64_t)ns << seg_log < a.nb) ++seg_log;
+  const int batch = ns == 1 ? 32 : (seg_log >= 5 ? 32 : (seg_log >= 4 ? 16 : 8));
+  const int grid = (int)((pieces + kScanThreads / ns - 1) / (kScanThreads / ns));
+  const dim3 g(grid), b(kScanThreads);
+  if (ns == 1) {
+    hipLaunchKernelGGL((ll_fenwick_scan<D, 1, 32>), g, b, 0, s, a, 30);
+  } else if (ns == 2) {
+    if (batch == 32) hipLaunchKernelGGL((ll_fenwick_scan<D, 2, 32>), g, b, 0, s, a, seg_log);
+    else if (batch == 16) hipLaunchKernelGGL((ll_fenwick_scan<D, 2, 16>), g, b, 0, s, a, seg_log);
+    else hipLaunchKernelGGL((ll_fenwick_scan<D, 2, 8>), g, b, 0, s, a, seg_log);
+  } else {
+    if (batch == 32) hipLaunchKernelGGL((ll_fenwick_scan<D, 4, 32>), g, b, 0, s, a, seg_log);
+    else if (batch == 16) hipLaunchKernelGGL((ll_fenwick_scan<D, 4, 16>), g, b, 0, s, a, seg_log);
+    else hipLaunchKernelGGL((ll_fenwick_scan<D, 4, 8>), g, b, 0, s, a, seg_log);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_fenwick_scan(int D, const PrefillArgs& a, hipStream_t s) {
+  switch (D) {
+    case 16: return launch_scan_d<16>(a, s);
+    case 32: return launch_scan_d<32>(a, s);
+    case 64: return launch_scan_d<64>(a, s);
+    case 128: return launch_scan_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_state_export(int D, int C, const PrefillArgs& a, hipStream_t s) {

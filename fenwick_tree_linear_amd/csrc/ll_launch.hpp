@@ -68,6 +68,8 @@ hipError_t launch_state_export(int D, int C, const PrefillArgs& a, hipStream_t s
 hipError_t launch_decode_step(int io, int D, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_gdn_wy(int io, int D, int C, const GdnArgs& a, hipStream_t s);
 hipError_t launch_gdn_state(int io, int D, int C, const GdnArgs& a, hipStream_t s);
+hipError_t launch_lambda_mlp(int64_t rows, int L, int hidden, const float* d, const float* w1, const float* w2,
+                             const float* bias, float* lam, hipStream_t s);
 
 inline int ilog2_host(int x) {
   int r = 0;

@@ -15,8 +15,16 @@ For bf16 workloads q, k, v are drawn in fp32 and rounded to bf16 (round to
 nearest even); gates, lambda and beta stay fp32.
 
 Each tensor has its own generator, seeded from the workload seed and the
-tensor's index (q 0, k 1, v 2, log_gate 3, lambda 4, beta 5, one-hot level 6),
-so any subset can be drawn alone and yields the same values.
+tensor's index (q 0, k 1, v 2, log_gate 3, lambda 4, beta 5, one-hot level 6;
+the level-weight MLP: d 7, W1 8, W2 9, bias 10), so any subset can be drawn
+alone and yields the same values.
+
+Level-weight MLP inputs (the adaptive-decay page's lambda producer, hidden
+size 2L): d ~ N(0, 1) per token, head and level; W1 ~ N(0, 1/L);
+W2 ~ N(0, 0.25/hidden); bias = 0.54 + 0.25 N(0, 1).  The page starts training
+from W2 = 0 and bias 0.54 (every weight softplus(0.54), about 1); the random
+W2 and bias stand in for a trained MLP, so that the weights differ per token
+and level (mostly between 0.4 and 2).
 """
 
 from __future__ import annotations
@@ -155,3 +163,14 @@ def decode_inputs(w: Workload, device="cpu", seed: int | None = None) -> dict:
 def softplus(x: float) -> float:
     """log(1 + e^x), the activation that produces lambda."""
     return math.log1p(math.exp(x))
+
+
+def lambda_mlp_inputs(lead: tuple, L: int, hidden: int | None = None, seed: int = 0, device="cpu") -> dict:
+    """Inputs of the level-weight MLP: d [*lead, L] and weights W1 [L, hidden],
+    W2 [hidden, L], bias [L] (fp32; hidden defaults to 2L)."""
+    hidden = 2 * L if hidden is None else hidden
+    d = torch.randn(*lead, L, generator=_gen(seed, 7, device), device=device)
+    w1 = torch.randn(L, hidden, generator=_gen(seed, 8, device), device=device) / math.sqrt(L)
+    w2 = torch.randn(hidden, L, generator=_gen(seed, 9, device), device=device) * (0.5 / math.sqrt(hidden))
+    bias = 0.54 + 0.25 * torch.randn(L, generator=_gen(seed, 10, device), device=device)
+    return dict(d=d.contiguous(), w1=w1.contiguous(), w2=w2.contiguous(), bias=bias.contiguous())

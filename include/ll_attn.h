@@ -149,6 +149,26 @@ ll_status ll_decode_step(int B, int H, int dk, int dv, int L, ll_dtype io, ll_ru
                          const float* lambda, const float* beta, void* o, void* state,
                          hipStream_t stream);
 
+/*
+ * Level weights from the adaptive-decay MLP ("Adaptive memory decay for
+ * log-linear attention", section "Method", LambdaMLPSoftplus), the producer of
+ * the `lambda` argument above: for every row (a token and head),
+ *   h = d W1,   lambda = softplus(h W2 + b),   softplus(z) = log(1 + e^z),
+ * so every level of every token and head gets its own non-negative weight.
+ *   d      [rows, L]        fp32, the per-level representation of each row
+ *                           (rows = B*T*H for a prefill, B*H for a decode step;
+ *                           row-major, so [B,T,H,L] is already this layout)
+ *   w1     [L, hidden]      fp32, first layer (no bias)
+ *   w2     [hidden, L]      fp32, second layer
+ *   bias   [L]              fp32
+ *   lambda [rows, L]        fp32, written; must not overlap d
+ * The page uses hidden = 2L; implemented for 1 <= L <= 32, 1 <= hidden <= 64
+ * (LL_ERR_UNSUPPORTED otherwise).  Computed in fp32 on the matrix cores.
+ * rows == 0 enqueues nothing (pointers may then be NULL).
+ */
+ll_status ll_lambda_mlp(int64_t rows, int L, int hidden, const float* d, const float* w1, const float* w2,
+                        const float* bias, float* lambda, hipStream_t stream);
+
 /* Text of the last error on the calling thread; valid until its next call. */
 const char* ll_last_error(void);
 
@@ -158,8 +178,8 @@ const char* ll_last_error(void);
  * events recorded on the call's stream.  ll_kernel_timing_read() waits for the
  * recorded events, then reports for up to `capacity` kernels their name (a
  * static string: "ll_chunk_state", "ll_fenwick_scan", "ll_chunk_attn",
- * "ll_state_export", "ll_decode_step", "ll_gdn_wy", "ll_gdn_state"), the
- * summed milliseconds and the launch
+ * "ll_state_export", "ll_decode_step", "ll_gdn_wy", "ll_gdn_state",
+ * "ll_lambda_mlp"), the summed milliseconds and the launch
  * count, and clears the record.  Enabling creates HIP events lazily; timing
  * adds two event records per launch, so do not time throughput with it on.
  */

@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["ll_attn_fwd", "ll_attn_fwd_workspace_bytes", "ll_decode_state_bytes", "ll_decode_step",
-         "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_last_error"])
+         "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp", "ll_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -156,3 +156,26 @@ def test_last_error_is_cleared_by_a_good_call():
     assert F.ll_last_error() != ""
     F.ll_attn_fwd_workspace_bytes(prob())
     assert F.ll_last_error() == ""
+
+
+def test_lambda_mlp_validation_before_any_launch():
+    D = DUMMY
+    good = dict(rows=1024, L=15, hidden=30, d=D, w1=D, w2=D + 64, bias=D + 128, lam=D + 4096)
+    cases = [
+        (dict(rows=-1), "LL_ERR_SHAPE"),
+        (dict(L=0), "LL_ERR_SHAPE"),
+        (dict(hidden=0), "LL_ERR_SHAPE"),
+        (dict(L=33), "LL_ERR_UNSUPPORTED"),
+        (dict(hidden=65), "LL_ERR_UNSUPPORTED"),
+        (dict(rows=2 ** 40), "LL_ERR_UNSUPPORTED"),
+        (dict(d=None), "LL_ERR_NULL"),
+        (dict(bias=None), "LL_ERR_NULL"),
+        (dict(lam=None), "LL_ERR_NULL"),
+        (dict(lam=D), "LL_ERR_SHAPE"),  # lambda over d
+        (dict(rows=0, d=None, w1=None, w2=None, bias=None, lam=None), "LL_OK"),  # nothing to do
+    ]
+    order = ("rows", "L", "hidden", "d", "w1", "w2", "bias", "lam")
+    for kw, name in cases:
+        a = dict(good, **kw)
+        st, msg = status_of(F.ll_lambda_mlp, *(a[k] for k in order), 0)
+        assert st == name, (kw, msg)

@@ -166,3 +166,19 @@ def test_bitwise_deterministic(prefill_2k):
     a = gpu_prefill(x, 64, w.L, dev_inputs=d)
     b = gpu_prefill(x, 64, w.L, dev_inputs=d)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("T", [15872, 16384])
+def test_state_export_many_blocks(T):
+    """At 31 and 32 blocks of 8 chunks per head the Fenwick scan splits each
+    head's blocks into segments; the exported states then include nodes that
+    combine several segments (slow decay, so every level carries weight)."""
+    w = W.Workload("export many blocks", W.MAMBA2, 1, 2, T, 64, 64, 16, 64, "bf16", 17 + T)
+    x = W.prefill_inputs(w, variant="slowdecay", parts=("k", "v", "log_gate"))
+    _, (s_hat, sigma) = gpu_prefill(x, 64, 16, want_output=False, want_state=True)
+    ref = oracle.state_direct(np32(x["k"]), np32(x["v"]), np32(x["log_gate"]), 16)
+    for lvl in range(16):
+        if lvl >= 1 and (T >> (lvl - 1)) & 1:
+            err = rel_err(true_state(s_hat[:, :, lvl], sigma[:, :, lvl]), ref[:, :, lvl])
+            say(f"[prefill] export T{T} level {lvl}: state rel err {err:.3e}")
+            assert err <= TOL["bf16"], lvl
