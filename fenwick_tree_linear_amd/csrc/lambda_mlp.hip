@@ -6,8 +6,7 @@
 // W1 [L][hidden], W2 [hidden][L], b [L] shared by all rows.
 //
 // One wave per 64 rows.  The rows are a dense [rows][L] fp32 array, so a wave
-// loads its 64 L floats with coalesced 256-byte instructions into LDS (row
-// stride padded so that the column reads below hit distinct banks), and
+// copies its 64 L floats with coalesced 256-byte instructions into LDS, and
 // stores the weights back the same way.  Both layers run on the fp32 matrix
 // cores (v_mfma_f32_16x16x4_f32) with L and hidden padded to 16:
 //   layer 1, transposed: h^T tile (16 hidden x 16 rows) = W1^T d^T, so that
@@ -23,9 +22,10 @@ namespace llattn {
 
 constexpr int kMlpWaves = 4;  // waves (of 64 rows each) per workgroup
 
-// softplus(z) = log(1 + e^z), as max(z, 0) + log1p(e^-|z|) so that large |z|
-// neither overflows nor cancels
-__device__ __forceinline__ float softplus_f32(float z) { return fmaxf(z, 0.f) + log1pf(__expf(-fabsf(z))); }
+// softplus(z) = log(1 + e^z), as max(z, 0) + log(1 + e^-|z|) so that large |z|
+// neither overflows nor cancels; rounding 1 + x (x in (0, 1]) to fp32 costs at
+// most 2^-24 in absolute terms, far below the weights' own size
+__device__ __forceinline__ float softplus_f32(float z) { return fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z))); }
 
 // LT = ceil(L / 16) level tiles, HT = ceil(hidden / 16) hidden tiles
 template <int LT, int HT>
@@ -35,21 +35,22 @@ __global__ void __launch_bounds__(64 * kMlpWaves) ll_lambda_mlp(int64_t rows, in
                                                                  const float* __restrict__ w2,
                                                                  const float* __restrict__ bias,
                                                                  float* __restrict__ lam) {
-  constexpr int LP = 16 * LT;   // padded levels
-  constexpr int RS = LP + 1;    // LDS row stride (odd: column reads are conflict-free)
+  constexpr int LP = 16 * LT;  // padded levels
   typedef Mma<float> M;
-  __shared__ float tile[kMlpWaves][64 * RS];
+  // a straight copy of the wave's rows, [64][L] (odd L: the column reads
+  // below hit distinct banks; even L at most two-way)
+  __shared__ float tile[kMlpWaves][64 * LP];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;  // fragment column and lane group
   float* t = tile[wave];
   const int64_t row0 = ((int64_t)blockIdx.x * kMlpWaves + wave) * 64;
   if (row0 >= rows) return;  // whole waves only; no workgroup barrier below
-  const int nrow = rows - row0 < 64 ? (int)(rows - row0) : 64;
+  const int nel = (rows - row0 < 64 ? (int)(rows - row0) : 64) * L;  // floats of this wave's rows
 
   // weights as MFMA fragments.  Layer 1 (A = W1^T, k = level): step s of
   // hidden tile n gives lane l W1[4s + g][16n + c].  Layer 2 (B = W2, k =
   // hidden in the accumulator order of layer 1): step s gives lane l
-  // W2[M::kidx(s, g)][16lt + c].
+  // W2[M::kidx(s, g)][16lt + c].  Zero in the padding.
   float a1[HT][4 * LT], b2[LT][4 * HT];
 #pragma unroll
   for (int n = 0; n < HT; ++n)
@@ -69,25 +70,23 @@ __global__ void __launch_bounds__(64 * kMlpWaves) ll_lambda_mlp(int64_t rows, in
 #pragma unroll
   for (int lt = 0; lt < LT; ++lt) bvec[lt] = 16 * lt + c < L ? bias[16 * lt + c] : 0.f;
 
-  // stage the wave's rows: element i = lane + 64 j of the contiguous block is
-  // row i / L, level i % L (tracked incrementally); padding levels are zero
+  // the wave's rows: coalesced 256-byte loads (element i = lane + 64 j of the
+  // rows' contiguous floats), all issued before the first LDS write.  Rows
+  // past the end are left unset: every row of both products depends on its
+  // own row of d only, and they are never stored.
   {
     const float* src = d + row0 * L;
-    const int n = nrow * L;
-    int r = lane / L, col = lane % L;
-    const int dr = 64 / L, dc = 64 % L;
-    for (int i = lane; i < n; i += 64) {
-      t[r * RS + col] = src[i];
-      r += dr;
-      col += dc;
-      if (col >= L) {
-        col -= L;
-        ++r;
-      }
+    float v[LP];
+#pragma unroll
+    for (int j = 0; j < LP; ++j) {
+      const int i = lane + 64 * j;
+      if (j < L && i < nel) v[j] = src[i];
     }
-    for (int col2 = L; col2 < LP; ++col2) t[lane * RS + col2] = 0.f;
-    if (lane >= nrow)
-      for (int col2 = 0; col2 < L; ++col2) t[lane * RS + col2] = 0.f;
+#pragma unroll
+    for (int j = 0; j < LP; ++j) {
+      const int i = lane + 64 * j;
+      if (j < L && i < nel) t[i] = v[j];
+    }
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
   __builtin_amdgcn_wave_barrier();
@@ -96,12 +95,13 @@ __global__ void __launch_bounds__(64 * kMlpWaves) ll_lambda_mlp(int64_t rows, in
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     // layer 1: h^T (hidden x rows) = W1^T d^T; B operand lane l = d[16rt + c][4s + g]
+    const float* drow = t + (16 * rt + c) * L + g;
     f32x4 h[HT];
 #pragma unroll
     for (int n = 0; n < HT; ++n) h[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4 * LT; ++s) {
-      const float bd = t[(16 * rt + c) * RS + 4 * s + g];
+      const float bd = 4 * s + g < L ? drow[4 * s] : 0.f;
 #pragma unroll
       for (int n = 0; n < HT; ++n) h[n] = M::mma(a1[n][s], bd, h[n]);
     }
@@ -114,31 +114,30 @@ __global__ void __launch_bounds__(64 * kMlpWaves) ll_lambda_mlp(int64_t rows, in
       z[rt][lt] = acc;
     }
   }
-  __builtin_amdgcn_wave_barrier();  // every lane's reads of the staged rows are issued before they are overwritten
+  __builtin_amdgcn_wave_barrier();  // the staged rows are read before they are overwritten
   __builtin_amdgcn_s_waitcnt(0xc07f);
-  // z[rt][lt][i] = z[16rt + 4g + i][16lt + c]: bias, softplus, back into the tile
+  // z[rt][lt][i] = z[16rt + 4g + i][16lt + c]: bias, softplus, back into the
+  // tile in the rows' own layout
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int lt = 0; lt < LT; ++lt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) t[(16 * rt + 4 * g + i) * RS + 16 * lt + c] = softplus_f32(z[rt][lt][i] + bvec[lt]);
+      for (int i = 0; i < 4; ++i)
+        if (16 * lt + c < L) t[(16 * rt + 4 * g + i) * L + 16 * lt + c] = softplus_f32(z[rt][lt][i] + bvec[lt]);
   __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_wave_barrier();
-  {
-    float* dst = lam + row0 * L;
-    const int n = nrow * L;
-    int r = lane / L, col = lane % L;
-    const int dr = 64 / L, dc = 64 % L;
-    for (int i = lane; i < n; i += 64) {
-      dst[i] = t[r * RS + col];
-      r += dr;
-      col += dc;
-      if (col >= L) {
-        col -= L;
-        ++r;
-      }
-    }
+  float* dst = lam + row0 * L;
+  float o[LP];
+#pragma unroll
+  for (int j = 0; j < LP; ++j) {
+    const int i = lane + 64 * j;
+    if (j < L && i < nel) o[j] = t[i];
+  }
+#pragma unroll
+  for (int j = 0; j < LP; ++j) {
+    const int i = lane + 64 * j;
+    if (j < L && i < nel) dst[i] = o[j];
   }
 }
 
