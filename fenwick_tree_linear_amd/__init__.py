@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     ll_attn_fwd_workspace_bytes,
     ll_decode_state_bytes,
     ll_decode_step,
+    ll_decode_step_ragged,
     ll_kernel_timing_enable,
     ll_kernel_timing_read,
     ll_lambda_mlp,

@@ -66,8 +66,9 @@ def load_library() -> ctypes.CDLL:
     lib.ll_kernel_timing_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_int), i32, ctypes.POINTER(ctypes.c_int)]
     lib.ll_lambda_mlp.argtypes = [i64, i32, i32, P, P, P, P, P, P]
+    lib.ll_decode_step_ragged.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
     for fn in ("ll_attn_fwd_workspace_bytes", "ll_attn_fwd", "ll_decode_state_bytes", "ll_decode_step",
-               "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp"):
+               "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp", "ll_decode_step_ragged"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -125,6 +126,16 @@ def ll_decode_step(B, H, dk, dv, L, io, rule, pos, q, k, v, log_gate, lam, beta,
 def ll_lambda_mlp(rows: int, L: int, hidden: int, d, w1, w2, bias, lam, stream=None) -> None:
     _check(load_library().ll_lambda_mlp(rows, L, hidden, _ptr(d), _ptr(w1), _ptr(w2), _ptr(bias), _ptr(lam),
                                         _stream(stream)))
+
+
+def ll_decode_step_ragged(B, H, dk, dv, L, io, rule, pos, q, k, v, log_gate, lam, beta, o, state,
+                          stream=None) -> None:
+    """``pos``: int64 device tensor [B], one position per sequence."""
+    if isinstance(pos, torch.Tensor) and pos.dtype != torch.int64:
+        raise TypeError("pos must be an int64 tensor")
+    _check(load_library().ll_decode_step_ragged(B, H, dk, dv, L, io, rule, _ptr(pos), _ptr(q), _ptr(k), _ptr(v),
+                                                _ptr(log_gate), _ptr(lam), _ptr(beta), _ptr(o), _ptr(state),
+                                                _stream(stream)))
 
 
 def ll_kernel_timing_enable(on: bool) -> None:

@@ -330,27 +330,34 @@ ll_status ll_decode_state_bytes(int B, int H, int dk, int dv, int L, size_t* byt
   return ok();
 }
 
-ll_status ll_decode_step(int B, int H, int dk, int dv, int L, ll_dtype io, ll_rule rule, int64_t pos, const void* q,
-                         const void* k, const void* v, const float* log_gate, const float* lambda, const float* beta,
-                         void* o, void* state, hipStream_t stream) {
+namespace {
+
+// Shared by both decode entry points: everything but the position.
+ll_status check_decode(int B, int H, int dk, int dv, int L, ll_dtype io, ll_rule rule, const void* q, const void* k,
+                       const void* v, const float* log_gate, const float* lambda, const float* beta, void* o,
+                       void* state) {
   if (io != LL_F32 && io != LL_BF16) return fail(LL_ERR_DTYPE, "unknown io dtype %d", (int)io);
   if (rule != LL_MAMBA2 && rule != LL_GATED_DELTANET) return fail(LL_ERR_UNSUPPORTED, "unknown rule %d", (int)rule);
   if (B < 1 || H < 1 || dk < 1 || dv < 1 || L < 2)
     return fail(LL_ERR_SHAPE, "sizes must be positive and L >= 2 (B=%d H=%d dk=%d dv=%d L=%d)", B, H, dk, dv, L);
-  if (pos < 0) return fail(LL_ERR_POSITION, "pos=%lld is negative", (long long)pos);
   if (L > 32) return fail(LL_ERR_UNSUPPORTED, "L=%d: at most 32 decode levels are supported", L);
-  if (pos + 1 >= ((int64_t)1 << (L - 1)))
-    return fail(LL_ERR_POSITION, "pos=%lld: the state of [0,pos+1) does not fit in L=%d levels", (long long)pos, L);
   if (!q || !k || !v || !log_gate || !lambda || !o || !state)
     return fail(LL_ERR_NULL, "q, k, v, log_gate, lambda, o and state must not be NULL");
   if (rule == LL_GATED_DELTANET && !beta) return fail(LL_ERR_NULL, "beta must not be NULL for Gated DeltaNet");
   if (dk != dv) return fail(LL_ERR_UNSUPPORTED, "dk=%d != dv=%d is not supported", dk, dv);
   if (dk != 16 && dk != 32 && dk != 64 && dk != 128) return fail(LL_ERR_UNSUPPORTED, "head size %d not supported", dk);
+  return LL_OK;
+}
+
+ll_status launch_decode(int B, int H, int dk, int L, ll_dtype io, ll_rule rule, int64_t pos, const int64_t* pos_dev,
+                        const void* q, const void* k, const void* v, const float* log_gate, const float* lambda,
+                        const float* beta, void* o, void* state, hipStream_t stream) {
   DecodeArgs a;
   a.B = B;
   a.H = H;
   a.L = L;
   a.pos = pos;
+  a.pos_dev = pos_dev;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -363,6 +370,28 @@ ll_status ll_decode_step(int B, int H, int dk, int dv, int L, ll_dtype io, ll_ru
   hipError_t e = timed(K_DECODE_STEP, stream, [&] { return llattn::launch_decode_step(code, dk, a, stream); });
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+ll_status ll_decode_step(int B, int H, int dk, int dv, int L, ll_dtype io, ll_rule rule, int64_t pos, const void* q,
+                         const void* k, const void* v, const float* log_gate, const float* lambda, const float* beta,
+                         void* o, void* state, hipStream_t stream) {
+  ll_status st = check_decode(B, H, dk, dv, L, io, rule, q, k, v, log_gate, lambda, beta, o, state);
+  if (st != LL_OK) return st;
+  if (pos < 0) return fail(LL_ERR_POSITION, "pos=%lld is negative", (long long)pos);
+  if (pos + 1 >= ((int64_t)1 << (L - 1)))
+    return fail(LL_ERR_POSITION, "pos=%lld: the state of [0,pos+1) does not fit in L=%d levels", (long long)pos, L);
+  return launch_decode(B, H, dk, L, io, rule, pos, nullptr, q, k, v, log_gate, lambda, beta, o, state, stream);
+}
+
+ll_status ll_decode_step_ragged(int B, int H, int dk, int dv, int L, ll_dtype io, ll_rule rule, const int64_t* pos,
+                                const void* q, const void* k, const void* v, const float* log_gate,
+                                const float* lambda, const float* beta, void* o, void* state, hipStream_t stream) {
+  ll_status st = check_decode(B, H, dk, dv, L, io, rule, q, k, v, log_gate, lambda, beta, o, state);
+  if (st != LL_OK) return st;
+  if (!pos) return fail(LL_ERR_NULL, "pos must not be NULL");
+  return launch_decode(B, H, dk, L, io, rule, 0, pos, q, k, v, log_gate, lambda, beta, o, state, stream);
 }
 
 ll_status ll_lambda_mlp(int64_t rows, int L, int hidden, const float* d, const float* w1, const float* w2,

@@ -15,6 +15,9 @@
 // Levels 1..c are exactly the low set bits of pos, so the merge reuses the rows
 // loaded for the read; they become empty (bit clear in pos+1) and are not
 // rewritten.  Traffic per head: popcount(pos) level reads + one level write.
+// Sequences of a batch may sit at different positions (read per sequence from
+// device memory): each workgroup is one head of one sequence, so nothing else
+// changes.
 #include "ll_device.hpp"
 #include "ll_launch.hpp"
 
@@ -41,9 +44,16 @@ __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
   const int bh = blockIdx.x;
   const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
   const int L = a.L;
-  const int64_t pos = a.pos;
   float* Sh = a.state + (int64_t)bh * L * D * D;
   float* sigma = a.state + (int64_t)a.B * a.H * L * D * D + (int64_t)bh * L;
+  // one position for the batch (checked by the host), or one per sequence
+  // from device memory: a position whose successor state would not fit in L
+  // levels (or a negative one) gives NaN outputs and leaves the state as it is
+  const int64_t pos = a.pos_dev ? a.pos_dev[bh / a.H] : a.pos;
+  if (pos < 0 || pos + 1 >= ((int64_t)1 << (L - 1))) {
+    for (int x = tid; x < D; x += NTH) static_cast<T*>(a.o)[(int64_t)bh * D + x] = from_f32<T>(__builtin_nanf(""));
+    return;  // the whole workgroup: pos is the same for every thread
+  }
   const int c = __ffsll((unsigned long long)(pos + 1)) - 1;
   const bool gdn = a.beta != nullptr;
 
@@ -142,7 +152,7 @@ __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
   }
   if (gdn) __syncthreads();
 
-  // merge into level c+1 (c + 1 <= L - 1 is guaranteed by the caller)
+  // merge into level c+1 (c + 1 <= L - 1 by the position check above)
   float* dst = Sh + (int64_t)(c + 1) * D * D + 4 * cg;
   const f32x4 vv = *reinterpret_cast<const f32x4*>(gdn ? &us[4 * cg] : &vs[4 * cg]);
 #pragma unroll

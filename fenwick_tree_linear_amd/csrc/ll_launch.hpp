@@ -37,7 +37,8 @@ struct PrefillArgs {
 
 struct DecodeArgs {
   int B, H, L;
-  int64_t pos;
+  int64_t pos;             // the position of every sequence, unless pos_dev is given
+  const int64_t* pos_dev;  // nullable: device [B], one position per sequence
   const void* q;
   const void* k;
   const void* v;

@@ -169,6 +169,23 @@ ll_status ll_decode_step(int B, int H, int dk, int dv, int L, ll_dtype io, ll_ru
 ll_status ll_lambda_mlp(int64_t rows, int L, int hidden, const float* d, const float* w1, const float* w2,
                         const float* bias, float* lambda, hipStream_t stream);
 
+/*
+ * The decode step for a batch whose sequences sit at different positions
+ * (section 2.3, "inference", one token per sequence), for continuous batching:
+ * as ll_decode_step, with
+ *   pos [B]   int64 in device memory: the position of each sequence, read by
+ *             the kernel (so a captured or replayed launch follows the values
+ *             in memory); the caller advances them.
+ * Positions are not visible to the host, so they are checked on the device:
+ * a sequence with pos < 0 or pos + 1 >= 2^(L-1) gets NaN in every output of
+ * its heads and its state is left unchanged.  Every other argument is
+ * validated on the host as for ll_decode_step (LL_ERR_NULL for a NULL pos).
+ */
+ll_status ll_decode_step_ragged(int B, int H, int dk, int dv, int L, ll_dtype io, ll_rule rule, const int64_t* pos,
+                                const void* q, const void* k, const void* v, const float* log_gate,
+                                const float* lambda, const float* beta, void* o, void* state,
+                                hipStream_t stream);
+
 /* Text of the last error on the calling thread; valid until its next call. */
 const char* ll_last_error(void);
 

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["ll_attn_fwd", "ll_attn_fwd_workspace_bytes", "ll_decode_state_bytes", "ll_decode_step",
+        ["ll_attn_fwd", "ll_attn_fwd_workspace_bytes", "ll_decode_state_bytes", "ll_decode_step", "ll_decode_step_ragged",
          "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp", "ll_last_error"])
 
 
@@ -178,4 +178,27 @@ def test_lambda_mlp_validation_before_any_launch():
     for kw, name in cases:
         a = dict(good, **kw)
         st, msg = status_of(F.ll_lambda_mlp, *(a[k] for k in order), 0)
+        assert st == name, (kw, msg)
+
+
+def test_ragged_decode_validation_before_any_launch():
+    D = DUMMY
+    good = [64, 16, 64, 64, 17, F.LL_BF16, F.LL_MAMBA2, D, D, D, D, D, D, None, D, D, 0]
+    cases = [
+        (dict(pos=None), "LL_ERR_NULL"),
+        (dict(L=33), "LL_ERR_UNSUPPORTED"),
+        (dict(L=1), "LL_ERR_SHAPE"),
+        (dict(io=3), "LL_ERR_DTYPE"),
+        (dict(rule=F.LL_GATED_DELTANET), "LL_ERR_NULL"),
+        (dict(dk=64, dv=32), "LL_ERR_UNSUPPORTED"),
+        (dict(dk=48, dv=48), "LL_ERR_UNSUPPORTED"),
+        (dict(state=None), "LL_ERR_NULL"),
+        (dict(o=None), "LL_ERR_NULL"),
+    ]
+    idx = dict(B=0, H=1, dk=2, dv=3, L=4, io=5, rule=6, pos=7, q=8, k=9, v=10, g=11, lam=12, beta=13, o=14, state=15)
+    for kw, name in cases:
+        args = list(good)
+        for key, val in kw.items():
+            args[idx[key]] = val
+        st, msg = status_of(F.ll_decode_step_ragged, *args)
         assert st == name, (kw, msg)
