@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     lambda_mlp,
     lib_path,
     ll_attn_fwd,
+    ll_attn_fwd_from_state,
     ll_attn_fwd_workspace_bytes,
     ll_decode_state_bytes,
     ll_decode_step,

@@ -66,9 +66,10 @@ def load_library() -> ctypes.CDLL:
     lib.ll_kernel_timing_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_int), i32, ctypes.POINTER(ctypes.c_int)]
     lib.ll_lambda_mlp.argtypes = [i64, i32, i32, P, P, P, P, P, P]
+    lib.ll_attn_fwd_from_state.argtypes = [ctypes.POINTER(LLProblem), i64, P, P, P, P, P, P, P, P, P, P, sz, P]
     lib.ll_decode_step_ragged.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
     for fn in ("ll_attn_fwd_workspace_bytes", "ll_attn_fwd", "ll_decode_state_bytes", "ll_decode_step",
-               "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp", "ll_decode_step_ragged"):
+               "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp", "ll_decode_step_ragged", "ll_attn_fwd_from_state"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -110,6 +111,14 @@ def ll_attn_fwd(problem: LLProblem, q, k, v, log_gate, lam, beta, o, state_out, 
     _check(load_library().ll_attn_fwd(None if problem is None else ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate), _ptr(lam),
                                       _ptr(beta), _ptr(o), _ptr(state_out), _ptr(workspace), workspace_bytes,
                                       _stream(stream)))
+
+
+def ll_attn_fwd_from_state(problem: LLProblem, pos0: int, state_in, q, k, v, log_gate, lam, beta, o, state_out,
+                           workspace, workspace_bytes: int, stream=None) -> None:
+    _check(load_library().ll_attn_fwd_from_state(None if problem is None else ctypes.byref(problem), pos0,
+                                                 _ptr(state_in), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
+                                                 _ptr(lam), _ptr(beta), _ptr(o), _ptr(state_out), _ptr(workspace),
+                                                 workspace_bytes, _stream(stream)))
 
 
 def ll_decode_state_bytes(B: int, H: int, dk: int, dv: int, L: int) -> int:
@@ -170,11 +179,15 @@ def decode_state_tensor(B: int, H: int, dk: int, dv: int, L: int, device="cuda")
 
 
 def attn_fwd(q, k, v, log_gate, lam, beta=None, C: int = 64, rule: int = LL_MAMBA2, L: int | None = None,
-             want_output: bool = True, want_state: bool = False, workspace=None, out=None, stream=None):
-    """Allocate outputs and workspace with torch, then call ``ll_attn_fwd``.
+             want_output: bool = True, want_state: bool = False, workspace=None, out=None, stream=None,
+             pos0: int = 0, state_in=None, state_out=None):
+    """Allocate outputs and workspace with torch, then call ``ll_attn_fwd``
+    (or ``ll_attn_fwd_from_state`` for a segment starting at ``pos0`` after
+    the per-level states ``state_in``).
 
     Returns ``o`` (or None), and the exported state (flat fp32) when
-    ``want_state``.
+    ``want_state`` (written into ``state_out`` if given, which may be
+    ``state_in``).
     """
     B, T, H, dk = k.shape
     dv = v.shape[-1]
@@ -188,8 +201,13 @@ def attn_fwd(q, k, v, log_gate, lam, beta=None, C: int = 64, rule: int = LL_MAMB
         o = out if out is not None else torch.empty(B, T, H, dv, dtype=v.dtype, device=v.device)
     st = None
     if want_state:
-        st = torch.empty(ll_decode_state_bytes(B, H, dk, dv, L) // 4, dtype=torch.float32, device=k.device)
-    ll_attn_fwd(prob, q, k, v, log_gate, lam, beta, o, st, workspace, workspace.numel(), stream)
+        st = state_out if state_out is not None else torch.empty(ll_decode_state_bytes(B, H, dk, dv, L) // 4,
+                                                                  dtype=torch.float32, device=k.device)
+    if pos0 or state_in is not None:
+        ll_attn_fwd_from_state(prob, pos0, state_in, q, k, v, log_gate, lam, beta, o, st, workspace,
+                               workspace.numel(), stream)
+    else:
+        ll_attn_fwd(prob, q, k, v, log_gate, lam, beta, o, st, workspace, workspace.numel(), stream)
     return (o, st) if want_state else o
 
 

@@ -148,9 +148,9 @@ ll_status plan_prefill(const ll_problem* p, bool exporting, Plan* out) {
 
 // ---------------------------------------------------------- kernel timing
 enum KernelId { K_CHUNK_STATE, K_FENWICK_SCAN, K_CHUNK_ATTN, K_STATE_EXPORT, K_DECODE_STEP, K_GDN_WY, K_GDN_STATE,
-                K_LAMBDA_MLP, K_COUNT };
+                K_LAMBDA_MLP, K_PRIOR_READ, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"ll_chunk_state", "ll_fenwick_scan", "ll_chunk_attn", "ll_state_export",
-                                           "ll_decode_step", "ll_gdn_wy",       "ll_gdn_state",   "ll_lambda_mlp"};
+                                           "ll_decode_step", "ll_gdn_wy",       "ll_gdn_state",   "ll_lambda_mlp", "ll_prior_read"};
 
 struct Timing {
   std::mutex mu;
@@ -252,12 +252,33 @@ ll_status ll_attn_fwd_workspace_bytes(const ll_problem* p, size_t* bytes) {
   return ok();
 }
 
-ll_status ll_attn_fwd(const ll_problem* p, const void* q, const void* k, const void* v, const float* log_gate,
-                      const float* lambda, const float* beta, void* o, void* state_out, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// Both prefill entry points: a segment at positions pos0 .. pos0 + T - 1 whose
+// earlier positions (if any) are summarised by state_in.
+ll_status run_prefill(const ll_problem* p, int64_t pos0, const float* state_in, const void* q, const void* k,
+                      const void* v, const float* log_gate, const float* lambda, const float* beta, void* o,
+                      void* state_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Plan pl;
   ll_status st = plan_prefill(p, state_out != nullptr, &pl);
   if (st != LL_OK) return st;
+  if (pos0 < 0) return fail(LL_ERR_POSITION, "pos0=%lld is negative", (long long)pos0);
+  if (pos0 > 0) {
+    if (!state_in) return fail(LL_ERR_NULL, "state_in must not be NULL when pos0 > 0");
+    if (p->rule != LL_MAMBA2)
+      return fail(LL_ERR_UNSUPPORTED, "a prefill from a state is implemented for the Mamba-2 write only");
+    if ((pos0 & -pos0) < p->T)
+      return fail(LL_ERR_POSITION, "pos0=%lld: the segment of T=%d tokens must fit below the lowest set bit of pos0",
+                  (long long)pos0, p->T);
+    if (pos0 > ((int64_t)1 << 61)) return fail(LL_ERR_POSITION, "pos0=%lld is too large", (long long)pos0);
+    const int64_t end = pos0 + p->T;
+    if (bit_length(end - 1) + 1 > p->L)
+      return fail(LL_ERR_SHAPE, "positions up to %lld need at least %d levels, got L=%d", (long long)(end - 1),
+                  bit_length(end - 1) + 1, p->L);
+    if (state_out && bit_length(end) > p->L - 1)
+      return fail(LL_ERR_SHAPE, "exporting the state of [0,%lld) needs at least %d levels, got L=%d", (long long)end,
+                  bit_length(end) + 1, p->L);
+  }
   if (!k || !v || !log_gate) return fail(LL_ERR_NULL, "k, v and log_gate must not be NULL");
   if (!o && !state_out) return fail(LL_ERR_NULL, "o and state_out are both NULL: nothing to compute");
   if (o && (!q || !lambda)) return fail(LL_ERR_NULL, "q and lambda must not be NULL when o is requested");
@@ -289,6 +310,8 @@ ll_status ll_attn_fwd(const ll_problem* p, const void* q, const void* k, const v
   a.N16 = (llattn::node_copies(p->io == LL_BF16 ? 1 : 0, p->dk) && pl.nb > 1) ? static_cast<void*>(ws + pl.n16_off)
                                                                                 : nullptr;
   a.state = static_cast<float*>(state_out);
+  a.state_in = pos0 > 0 ? state_in : nullptr;
+  a.pos0 = pos0;
   const int io = p->io == LL_BF16 ? 1 : 0;
   const int D = p->dk;
 
@@ -316,10 +339,28 @@ ll_status ll_attn_fwd(const ll_problem* p, const void* q, const void* k, const v
     e = timed(K_FENWICK_SCAN, stream, [&] { return llattn::launch_fenwick_scan(D, a, stream); });
   if (e == hipSuccess && o)
     e = timed(K_CHUNK_ATTN, stream, [&] { return llattn::launch_chunk_attn(io, D, C, a, stream); });
+  if (e == hipSuccess && o && pos0 > 0)
+    e = timed(K_PRIOR_READ, stream, [&] { return llattn::launch_prior_read(io, D, C, a, stream); });
   if (e == hipSuccess && state_out)
     e = timed(K_STATE_EXPORT, stream, [&] { return llattn::launch_state_export(D, C, a, stream); });
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+ll_status ll_attn_fwd(const ll_problem* p, const void* q, const void* k, const void* v, const float* log_gate,
+                      const float* lambda, const float* beta, void* o, void* state_out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  return run_prefill(p, 0, nullptr, q, k, v, log_gate, lambda, beta, o, state_out, workspace, workspace_bytes, stream);
+}
+
+ll_status ll_attn_fwd_from_state(const ll_problem* p, int64_t pos0, const float* state_in, const void* q,
+                                 const void* k, const void* v, const float* log_gate, const float* lambda,
+                                 const float* beta, void* o, void* state_out, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  return run_prefill(p, pos0, state_in, q, k, v, log_gate, lambda, beta, o, state_out, workspace, workspace_bytes,
+                     stream);
 }
 
 ll_status ll_decode_state_bytes(int B, int H, int dk, int dv, int L, size_t* bytes) {

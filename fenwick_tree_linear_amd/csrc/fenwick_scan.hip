@@ -145,11 +145,18 @@ __global__ void __launch_bounds__(kScanThreads) ll_fenwick_scan(PrefillArgs a, i
   }
 }
 
-// Export of the per-level states of [0,T) in the decode layout: for each set
-// bit z of nb the node covering the aligned run of blocks ending at
-// (nb with bits below z cleared) - 1, decayed to the last token; token level
-// log2(C) + log2(P) + z + 1.  Other levels are written as zeros; all
-// log-scales are 0.
+// Export of the per-level states in the decode layout.  Segment from
+// position 0: for each set bit z of nb the node covering the aligned run of
+// blocks ending at (nb with bits below z cleared) - 1, decayed to the last
+// token; token level log2(C) + log2(P) + z + 1.  After a prior state (pos0 >
+// 0, T <= lowbit(pos0)): the levels of pos0 + T -- the prior levels decayed
+// through the segment (e^{sigma + segment gate sum} S_hat), and when
+// T == lowbit(pos0) the carry: the segment's bucket merged with the run of
+// prior levels from level log2(T) + 1 up into the next free level.  Every
+// written level is a true state (its log-scale is 0, written by
+// ll_sigma_zero after this kernel, since other workgroups still read the
+// prior log-scales); the other levels are zeroed.  Each thread reads all its
+// prior elements before it writes any, so the prior state may be the output.
 template <int D>
 __global__ void __launch_bounds__(256) ll_state_export(PrefillArgs a, int logCP) {
   constexpr int G = D * D / 4;
@@ -160,15 +167,11 @@ __global__ void __launch_bounds__(256) ll_state_export(PrefillArgs a, int logCP)
   const int dt = tile / (D / 16), nt = tile % (D / 16);
   const int d0 = 16 * dt + 4 * (lane >> 4), n = 16 * nt + (lane & 15);
   float* out = a.state + (int64_t)bh * a.L * D * D;
-
-  uint64_t written = 0;
-  int rest = a.nb;
-  float dd = 0.f;
-  while (rest > 0) {
-    const int e = rest - 1;
-    const int z = __ffs(rest) - 1;
-    f32x4 val;
-    float gam;
+  auto put = [&](int lvl, f32x4 v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[(int64_t)lvl * D * D + (d0 + i) * D + n] = v[i];
+  };
+  auto node = [&](int e, f32x4& val, float& gam) {
     if (e & 1) {
       val = reinterpret_cast<const f32x4*>(a.F)[((int64_t)bh * a.nF + (e >> 1)) * G + grp];
       gam = a.GF[(int64_t)bh * a.nF + (e >> 1)];
@@ -176,23 +179,77 @@ __global__ void __launch_bounds__(256) ll_state_export(PrefillArgs a, int logCP)
       val = reinterpret_cast<const f32x4*>(a.S)[((int64_t)bh * a.nb + e) * G + grp];
       gam = a.GS[(int64_t)bh * a.nb + e];
     }
+  };
+
+  // the segment's gate sum (over the set bits of nb: the nodes tile the blocks)
+  float gseg = 0.f;
+  for (int rest = a.nb; rest > 0; rest &= rest - 1) {
+    const int e = rest - 1;
+    gseg += (e & 1) ? a.GF[(int64_t)bh * a.nF + (e >> 1)] : a.GS[(int64_t)bh * a.nb + e];
+  }
+
+  uint64_t written = 0;
+  const int segtop = logCP + 31 - __clz(a.nb) + 1;  // level of the segment's largest bucket
+  const uint64_t prior = (uint64_t)a.pos0;
+  // carry: T == lowbit(pos0), i.e. bit segtop - 1 of pos0 is set (nb is then a power of two)
+  const bool carry = prior != 0 && ((prior >> (segtop - 1)) & 1);
+  f32x4 merged = f32x4{0.f, 0.f, 0.f, 0.f};
+  int carry_lvl = 0;
+  if (prior != 0) {
+    const float* Sp = a.state_in + (int64_t)bh * a.L * D * D;
+    const float* sp = a.state_in + (int64_t)a.B * a.H * a.L * D * D + (int64_t)bh * a.L;
+    int run_end = 0;  // levels segtop .. run_end - 1 are the carried run
+    if (carry) {
+      run_end = segtop;
+      while (run_end <= 62 && ((prior >> (run_end - 1)) & 1)) ++run_end;
+      carry_lvl = run_end;
+    }
+    for (uint64_t bits = prior; bits; bits &= bits - 1) {
+      const int lvl = __ffsll((unsigned long long)bits);
+      const float sc = __expf(sp[lvl] + gseg);
+      f32x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = sc * Sp[(int64_t)lvl * D * D + (d0 + i) * D + n];
+      if (carry && lvl >= segtop && lvl < run_end) {
+        merged += v;
+      } else {
+        put(lvl, v);
+        written |= 1ull << lvl;
+      }
+    }
+  }
+
+  float dd = 0.f;
+  for (int rest = a.nb; rest > 0; rest &= rest - 1) {
+    const int e = rest - 1;
+    const int z = __ffs(rest) - 1;
+    f32x4 val;
+    float gam;
+    node(e, val, gam);
     const int lvl = logCP + z + 1;
     const float sc = __expf(dd);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[(int64_t)lvl * D * D + (d0 + i) * D + n] = sc * val[i];
-    written |= 1ull << lvl;
+    if (carry) {
+      merged += sc * val;  // the only bucket: nb is a power of two
+    } else {
+      put(lvl, sc * val);
+      written |= 1ull << lvl;
+    }
     dd += gam;
-    rest &= rest - 1;
+  }
+  if (carry) {
+    put(carry_lvl, merged);
+    written |= 1ull << carry_lvl;
   }
   for (int lvl = 0; lvl < a.L; ++lvl) {
     if ((written >> lvl) & 1) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[(int64_t)lvl * D * D + (d0 + i) * D + n] = 0.f;
+    put(lvl, f32x4{0.f, 0.f, 0.f, 0.f});
   }
-  if (grp == 0) {
-    float* sigma = a.state + (int64_t)a.B * a.H * a.L * D * D + (int64_t)bh * a.L;
-    for (int lvl = 0; lvl < a.L; ++lvl) sigma[lvl] = 0.f;
-  }
+}
+
+// Log-scales of an exported state: all zero (true states).
+__global__ void __launch_bounds__(256) ll_sigma_zero(float* sigma, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) sigma[i] = 0.f;
 }
 
 // Segments per head: enough threads to keep every CU loading (up to 2^17),
@@ -243,6 +300,11 @@ hipError_t launch_state_export(int D, int C, const PrefillArgs& a, hipStream_t s
     case 128: hipLaunchKernelGGL((ll_state_export<128>), dim3(grid), dim3(256), 0, s, a, logCP); break;
     default: return hipErrorInvalidValue;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t ns = (int64_t)a.B * a.H * a.L;
+  float* sigma = a.state + (int64_t)a.B * a.H * a.L * D * D;
+  hipLaunchKernelGGL(ll_sigma_zero, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, s, sigma, ns);
   return hipGetLastError();
 }
 

@@ -33,6 +33,10 @@ struct PrefillArgs {
   // steps, 64 lanes, 8]; NULL otherwise
   void* N16;
   float* state;  // nullable export target [B,H,L,D,D] + sigma [B,H,L]
+  // prefill from a state: the per-level states of the positions before the
+  // segment in the decode layout, and the segment's first position (0: none)
+  const float* state_in;
+  int64_t pos0;
 };
 
 struct DecodeArgs {
@@ -66,6 +70,7 @@ hipError_t launch_block_state(int io, int D, int C, const PrefillArgs& a, hipStr
 hipError_t launch_chunk_attn(int io, int D, int C, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_fenwick_scan(int D, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_state_export(int D, int C, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prior_read(int io, int D, int C, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode_step(int io, int D, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_gdn_wy(int io, int D, int C, const GdnArgs& a, hipStream_t s);
 hipError_t launch_gdn_state(int io, int D, int C, const GdnArgs& a, hipStream_t s);

@@ -120,6 +120,28 @@ ll_status ll_attn_fwd(const ll_problem* p, const void* q, const void* k, const v
                       hipStream_t stream);
 
 /*
+ * Prefill of a segment that continues a sequence (section 2.2 and 2.3: the
+ * buckets of positions before the segment are carried as per-level states),
+ * for chunked prefill: tokens pos0 .. pos0 + T - 1, with the per-level
+ * states of [0, pos0) in `state_in` (the decode-state layout below, e.g. the
+ * export of the previous segment).  Everything else as ll_attn_fwd, whose
+ * workspace size applies; o receives the outputs of the segment's tokens and
+ * state_out (nullable) the states of [0, pos0 + T).  state_out may be
+ * state_in (updated in place); no other overlap is allowed.
+ * Requires (LL_ERR_POSITION otherwise) pos0 >= 0 and, for pos0 > 0,
+ * T <= lowbit(pos0): the segment then never splits a prior bucket, and each
+ * of its tokens sees the prior states at the set bits of pos0, above all of
+ * the segment's own levels.  Outputs need pos0 + T <= 2^(L-1), exporting
+ * pos0 + T < 2^(L-1) (LL_ERR_SHAPE).  pos0 > 0 is implemented for LL_MAMBA2
+ * (LL_ERR_UNSUPPORTED otherwise) and needs state_in (LL_ERR_NULL);
+ * pos0 == 0 is ll_attn_fwd (state_in ignored).
+ */
+ll_status ll_attn_fwd_from_state(const ll_problem* p, int64_t pos0, const float* state_in, const void* q,
+                                 const void* k, const void* v, const float* log_gate, const float* lambda,
+                                 const float* beta, void* o, void* state_out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Bytes of one decode state: S_hat [B,H,L,dk,dv] fp32 followed by
  * sigma [B,H,L] fp32.  The true per-level state is exp(sigma_l) * S_hat_l
  * (the log-scale carries the decay lazily).  Level l >= 1 holds the bucket of
@@ -196,7 +218,7 @@ const char* ll_last_error(void);
  * recorded events, then reports for up to `capacity` kernels their name (a
  * static string: "ll_chunk_state", "ll_fenwick_scan", "ll_chunk_attn",
  * "ll_state_export", "ll_decode_step", "ll_gdn_wy", "ll_gdn_state",
- * "ll_lambda_mlp"), the summed milliseconds and the launch
+ * "ll_lambda_mlp", "ll_prior_read"), the summed milliseconds and the launch
  * count, and clears the record.  Enabling creates HIP events lazily; timing
  * adds two event records per launch, so do not time throughput with it on.
  */

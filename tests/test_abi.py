@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["ll_attn_fwd", "ll_attn_fwd_workspace_bytes", "ll_decode_state_bytes", "ll_decode_step", "ll_decode_step_ragged",
+        ["ll_attn_fwd", "ll_attn_fwd_from_state", "ll_attn_fwd_workspace_bytes", "ll_decode_state_bytes", "ll_decode_step", "ll_decode_step_ragged",
          "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp", "ll_last_error"])
 
 
@@ -202,3 +202,21 @@ def test_ragged_decode_validation_before_any_launch():
             args[idx[key]] = val
         st, msg = status_of(F.ll_decode_step_ragged, *args)
         assert st == name, (kw, msg)
+
+
+def test_prefill_from_state_validation_before_any_launch():
+    D = DUMMY
+    ws = F.ll_attn_fwd_workspace_bytes(prob(T=2048, L=16))
+
+    def call(p, pos0, state_in=D, o=D, state_out=None, beta=None):
+        return status_of(F.ll_attn_fwd_from_state, p, pos0, state_in, D, D, D, D, D, beta, o, state_out, D, ws, 0)
+
+    assert call(prob(T=2048, L=16), -1)[0] == "LL_ERR_POSITION"
+    assert call(prob(T=2048, L=16), 1024)[0] == "LL_ERR_POSITION"  # segment longer than lowbit(pos0)
+    assert call(prob(T=2048, L=16), 3 * 1024)[0] == "LL_ERR_POSITION"
+    assert call(prob(T=2048, L=16), 2048, state_in=None)[0] == "LL_ERR_NULL"
+    assert call(prob(T=2048, L=16, rule=F.LL_GATED_DELTANET), 2048, beta=D)[0] == "LL_ERR_UNSUPPORTED"
+    # outputs up to position 2^15 - 1 fit 16 levels; the state of [0, 2^15) needs 17
+    assert call(prob(T=2048, L=16), 2 ** 15 - 2048, state_out=D)[0] == "LL_ERR_SHAPE"
+    assert call(prob(T=2048, L=16), 2 ** 15, state_out=None)[0] == "LL_ERR_SHAPE"
+    assert call(prob(T=2048, L=13), 2048 * 3)[0] == "LL_ERR_SHAPE"  # position 8191 needs 14 levels
