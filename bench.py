@@ -138,6 +138,116 @@ def decode_bench(steps: int) -> dict:
             "frac": round(achieved / HBM_PEAK_GBS, 4)}
 
 
+def ragged_decode_bench(steps: int) -> dict:
+    """ll_decode_step_ragged on the decode workload's shape (B64 H16 d64 bf16, 17 levels) with the
+    64 sequences at different positions (32768 + 37 b, so their non-empty levels differ), all
+    advanced by one token per step on the device; HIP events on the launch stream."""
+    import torch
+
+    import fenwick_tree_linear_amd as F
+    from fenwick_tree_linear_amd import workloads as W
+
+    w = W.WORKLOADS["decode-32k"]
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    state = F.decode_state_tensor(w.B, w.H, w.dk, w.dv, w.L, device=dev)
+    nmat = w.B * w.H * w.L * w.dk * w.dv
+    state[:nmat].normal_(0.0, 0.05, generator=gen)
+    x = W.decode_inputs(W.with_shape(w, steps=1), device=dev)
+    q, k, v = (x[n][0].contiguous() for n in ("q", "k", "v"))
+    g, lam = x["log_gate"][0].contiguous(), x["lam"][0].contiguous()
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    start_pos = [w.T + 37 * b for b in range(w.B)]
+    pos = torch.tensor(start_pos, dtype=torch.int64, device=dev)
+
+    def step():
+        F.ll_decode_step_ragged(w.B, w.H, w.dk, w.dv, w.L, F.LL_BF16, F.LL_MAMBA2, pos, q, k, v, g, lam, None, o,
+                                state, stream)
+        pos.add_(1)
+
+    for _ in range(8):
+        step()
+    torch.cuda.synchronize()
+    first = [p + 8 for p in start_pos]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(stop) * 1e3 / steps  # includes the position increment (a tiny torch kernel)
+    mask = (1 << (w.L - 1)) - 1
+    level_bytes = w.dk * w.dv * 4
+    io_bytes = (4 * w.dk * 2 + 4 + 2 * w.L * 4 + 8)
+    total = sum(w.H * ((bin((p + i) & mask).count("1") + 1) * level_bytes + io_bytes)
+                for p in first for i in range(steps)) / steps
+    achieved = total / (us * 1e-6) / 1e9
+    return {"workload": "ll_decode_step_ragged B64 H16 d64 bf16, 17 levels, sequence b at position 32768 + 37 b",
+            "us_per_step": round(us, 2), "tokens_per_s": round(w.B / (us * 1e-6), 1),
+            "bytes_per_step": int(total), "achieved_GBs": round(achieved, 1), "peak_GBs": HBM_PEAK_GBS,
+            "frac": round(achieved / HBM_PEAK_GBS, 4)}
+
+
+def from_state_bench(reps: int) -> dict:
+    """ll_attn_fwd_from_state on the second half of the 16K prefill (tokens 8192..16383 of
+    B2 H16 d64 bf16, 15 levels, chunk 64) after the per-level state of the first half (its one
+    bucket, level 14): whole-call time and per-kernel averages (HIP events on the launch stream);
+    ll_prior_read's algorithmic bytes: q read, o read and written, the one level's weight and the
+    gates per token-head, and the prior level once per head."""
+    import torch
+
+    import fenwick_tree_linear_amd as F
+    from fenwick_tree_linear_amd import workloads as W
+
+    w = W.WORKLOADS["prefill-16k"]
+    T0 = w.T // 2
+    dev = torch.device("cuda:0")
+    x = W.prefill_inputs(w, device=dev)
+    half = {k: (None if v is None else v[:, T0:].contiguous()) for k, v in x.items()}
+    first = {k: (None if v is None else v[:, :T0].contiguous()) for k, v in x.items()}
+    state = F.decode_state_tensor(w.B, w.H, w.dk, w.dv, w.L, device=dev)
+    prob0 = F.LLProblem(w.B, T0, w.H, w.dk, w.dv, w.L, w.C, F.LL_BF16, F.LL_MAMBA2)
+    ws_bytes = F.ll_attn_fwd_workspace_bytes(prob0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    o = torch.empty(w.B, T0, w.H, w.dv, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    F.ll_attn_fwd(prob0, first["q"], first["k"], first["v"], first["log_gate"], first["lam"], None, o, state, ws,
+                  ws_bytes, stream)
+
+    def step():
+        F.ll_attn_fwd_from_state(prob0, T0, state, half["q"], half["k"], half["v"], half["log_gate"], half["lam"],
+                                 None, o, None, ws, ws_bytes, stream)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    F.ll_kernel_timing_read()
+    F.ll_kernel_timing_enable(True)
+    for _ in range(reps):
+        step()
+    torch.cuda.synchronize()
+    kt = F.ll_kernel_timing_read()
+    F.ll_kernel_timing_enable(False)
+    kernels = {name: round(t / n * 1e3, 2) for name, (t, n) in kt.items()}
+    th = w.B * T0 * w.H
+    prior_bytes = th * (w.dk * 2 + 2 * w.dv * 2 + 4 + 4) + w.B * w.H * w.dk * w.dv * 4
+    t_prior = kt["ll_prior_read"][0] / kt["ll_prior_read"][1] * 1e-3
+    gbs = prior_bytes / t_prior / 1e9
+    return {"workload": "ll_attn_fwd_from_state B2 H16 d64 bf16, 15 levels, chunk 64: tokens 8192..16383 after "
+                        "the state of 0..8191",
+            "ms_per_step": round(ms, 5), "tokens_per_s": round(w.B * T0 / (ms * 1e-3), 1), "kernels_us": kernels,
+            "prior_read": {"bytes": int(prior_bytes), "achieved_GBs": round(gbs, 1), "peak_GBs": HBM_PEAK_GBS,
+                           "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
 MFMA_FP32_PEAK_TFLOPS = 157.3  # dense fp32 matrix cores
 
 
@@ -249,6 +359,10 @@ def main() -> int:
                     help="also time this many ll_decode_step tokens on the decode workload (0: skip)")
     ap.add_argument("--gdn-steps", type=int, default=20,
                     help="also time this many Gated DeltaNet prefill steps on its 8K-token workload (0: skip)")
+    ap.add_argument("--ragged-steps", type=int, default=512,
+                    help="also time this many ll_decode_step_ragged steps with per-sequence positions (0: skip)")
+    ap.add_argument("--from-state-reps", type=int, default=20,
+                    help="also time this many prefills of the 16K workload's second half from a state (0: skip)")
     ap.add_argument("--mlp-reps", type=int, default=50,
                     help="also time this many ll_lambda_mlp launches over the 16K workload's rows (0: skip)")
     ap.add_argument("--cold-reps", type=int, default=10,
@@ -376,6 +490,12 @@ def main() -> int:
     if args.gdn_steps:
         result["gdn"] = gdn_bench(args.gdn_steps)
         log(f"[bench] gdn: {result['gdn']}")
+    if args.ragged_steps:
+        result["ragged_decode"] = ragged_decode_bench(args.ragged_steps)
+        log(f"[bench] ragged decode: {result['ragged_decode']}")
+    if args.from_state_reps:
+        result["from_state"] = from_state_bench(args.from_state_reps)
+        log(f"[bench] prefill from a state: {result['from_state']}")
     if args.mlp_reps:
         result["lambda_mlp"] = lambda_mlp_bench(args.mlp_reps)
         log(f"[bench] lambda mlp: {result['lambda_mlp']}")
