@@ -265,8 +265,6 @@ ll_status run_prefill(const ll_problem* p, int64_t pos0, const float* state_in, 
   if (pos0 < 0) return fail(LL_ERR_POSITION, "pos0=%lld is negative", (long long)pos0);
   if (pos0 > 0) {
     if (!state_in) return fail(LL_ERR_NULL, "state_in must not be NULL when pos0 > 0");
-    if (p->rule != LL_MAMBA2)
-      return fail(LL_ERR_UNSUPPORTED, "a prefill from a state is implemented for the Mamba-2 write only");
     if ((pos0 & -pos0) < p->T)
       return fail(LL_ERR_POSITION, "pos0=%lld: the segment of T=%d tokens must fit below the lowest set bit of pos0",
                   (long long)pos0, p->T);
@@ -329,6 +327,9 @@ ll_status run_prefill(const ll_problem* p, int64_t pos0, const float* state_in, 
     gd.W = ws + pl.w_off;
     gd.Up = ws + pl.up_off;
     gd.U = ws + pl.u_off;
+    gd.L = p->L;
+    gd.state_in = a.state_in;
+    gd.pos0 = a.pos0;
     e = timed(K_GDN_WY, stream, [&] { return llattn::launch_gdn_wy(io, D, p->C, gd, stream); });
     if (e == hipSuccess) e = timed(K_GDN_STATE, stream, [&] { return llattn::launch_gdn_state(io, D, p->C, gd, stream); });
   }

@@ -300,10 +300,43 @@ __global__ void __launch_bounds__(64 * (C / 16)) ll_gdn_state(GdnArgs a) {
     gn = lane < C ? a.g[row_of(i) + (int64_t)lane * a.H] : 0.f;
   };
 
+  // S_0: zero, or after a prior state the plain gated state of [0, pos0),
+  // the sum of its levels' true states (the buckets partition the prefix)
   f32x4 st[ODT];
 #pragma unroll
   for (int o = 0; o < ODT; ++o) st[o] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (a.pos0 > 0) {
+    const float* Sh = a.state_in + (int64_t)bh * a.L * D * D;
+    const float* sg = a.state_in + (int64_t)a.B * a.H * a.L * D * D + (int64_t)bh * a.L;
+    for (uint64_t bits = (uint64_t)a.pos0; bits; bits &= bits - 1) {
+      const int lvl = __ffsll((unsigned long long)bits);
+      const float sc = __expf(sg[lvl]);
+#pragma unroll
+      for (int o = 0; o < ODT; ++o) {
+        const int dt = wv + o * NW;
+        if (dt >= DT) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[o][e] += sc * Sh[(int64_t)lvl * D * D + (16 * dt + 4 * g4 + e) * D + n0 + q16];
+      }
+    }
+  }
   for (int x = tid; x < KSD * 64; x += 64 * NW) sf[x] = Frag{};
+  if (a.pos0 > 0) {
+    __syncthreads();  // the zero fill is complete before the tiles are published into it
+#pragma unroll
+    for (int o = 0; o < ODT; ++o) {
+      const int dt = wv + o * NW;
+      if (dt >= DT) continue;
+      if constexpr (sizeof(T) == 2) {
+        bf16* f = reinterpret_cast<bf16*>(&sf[(dt >> 1) * 64 + lane]) + 4 * (dt & 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = (bf16)st[o][e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) reinterpret_cast<float*>(sf)[(4 * dt + e) * 64 + lane] = st[o][e];
+      }
+    }
+  }
 
   issue(0);
   fetch(0);

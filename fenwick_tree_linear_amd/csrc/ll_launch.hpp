@@ -63,6 +63,11 @@ struct GdnArgs {
   void* W;            // (I + L)^-1 diag(beta e^G) K per chunk
   void* Up;           // (I + L)^-1 diag(beta) V per chunk
   void* U;            // pseudo-values, the values the log-linear read uses
+  // a segment continuing a sequence: the per-level states of [0, pos0) in the
+  // decode layout (L levels); the chunk recurrence starts from their sum
+  int L;
+  const float* state_in;
+  int64_t pos0;
 };
 
 // io: 0 = fp32, 1 = bf16.  Each returns hipSuccess or the launch error.

@@ -132,9 +132,10 @@ ll_status ll_attn_fwd(const ll_problem* p, const void* q, const void* k, const v
  * T <= lowbit(pos0): the segment then never splits a prior bucket, and each
  * of its tokens sees the prior states at the set bits of pos0, above all of
  * the segment's own levels.  Outputs need pos0 + T <= 2^(L-1), exporting
- * pos0 + T < 2^(L-1) (LL_ERR_SHAPE).  pos0 > 0 is implemented for LL_MAMBA2
- * (LL_ERR_UNSUPPORTED otherwise) and needs state_in (LL_ERR_NULL);
- * pos0 == 0 is ll_attn_fwd (state_in ignored).
+ * pos0 + T < 2^(L-1) (LL_ERR_SHAPE).  pos0 > 0 needs state_in (LL_ERR_NULL);
+ * pos0 == 0 is ll_attn_fwd (state_in ignored).  For LL_GATED_DELTANET the
+ * pseudo-values of the segment continue the delta rule from the prior plain
+ * state, the sum of the prior levels (they partition [0, pos0)).
  */
 ll_status ll_attn_fwd_from_state(const ll_problem* p, int64_t pos0, const float* state_in, const void* q,
                                  const void* k, const void* v, const float* log_gate, const float* lambda,

@@ -215,7 +215,7 @@ def test_prefill_from_state_validation_before_any_launch():
     assert call(prob(T=2048, L=16), 1024)[0] == "LL_ERR_POSITION"  # segment longer than lowbit(pos0)
     assert call(prob(T=2048, L=16), 3 * 1024)[0] == "LL_ERR_POSITION"
     assert call(prob(T=2048, L=16), 2048, state_in=None)[0] == "LL_ERR_NULL"
-    assert call(prob(T=2048, L=16, rule=F.LL_GATED_DELTANET), 2048, beta=D)[0] == "LL_ERR_UNSUPPORTED"
+    assert call(prob(T=2048, L=16, rule=F.LL_GATED_DELTANET), 2048, beta=None)[0] == "LL_ERR_NULL"
     # outputs up to position 2^15 - 1 fit 16 levels; the state of [0, 2^15) needs 17
     assert call(prob(T=2048, L=16), 2 ** 15 - 2048, state_out=D)[0] == "LL_ERR_SHAPE"
     assert call(prob(T=2048, L=16), 2 ** 15, state_out=None)[0] == "LL_ERR_SHAPE"

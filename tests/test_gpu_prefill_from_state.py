@@ -3,7 +3,8 @@ states (ll_attn_fwd_from_state), chained segment by segment with the state
 updated in place, against the oracle's direct form over the whole sequence
 and its bucket states.
 
-Segment boundaries cover both cases of the export: the segment's bucket
+Both write rules (for Gated DeltaNet the pseudo-value pass continues from the
+prior plain state).  Segment boundaries cover both cases of the export: the segment's bucket
 merging with a run of prior levels (pos0 = 512, 1536 with 512-token
 segments) and prior levels kept beside the segment's own (pos0 = 1024; a
 1536-token segment after 2048).  Tolerance: max|o - ref| / max|ref| <= 1e-4
@@ -31,26 +32,32 @@ def chained_prefill(x, cuts, C, L):
     outs = []
     for lo, hi in zip(cuts[:-1], cuts[1:]):
         seg = {k: (None if v is None else v[:, lo:hi].contiguous()) for k, v in d.items()}
-        o, _ = F.attn_fwd(seg["q"], seg["k"], seg["v"], seg["log_gate"], seg["lam"], C=C, L=L, want_state=True,
-                          pos0=lo, state_in=state if lo > 0 else None, state_out=state)
+        rule = F.LL_MAMBA2 if seg.get("beta") is None else F.LL_GATED_DELTANET
+        o, _ = F.attn_fwd(seg["q"], seg["k"], seg["v"], seg["log_gate"], seg["lam"], seg.get("beta"), C=C, L=L,
+                          rule=rule, want_state=True, pos0=lo, state_in=state if lo > 0 else None, state_out=state)
         outs.append(o)
     torch.cuda.synchronize()
     return np.concatenate([np32(o) for o in outs], axis=1), state
 
 
-@pytest.mark.parametrize("io,d,C,seg,variant", [("bf16", 64, 64, 512, "slowdecay"), ("bf16", 64, 64, 512, "default"),
-                                                ("f32", 32, 32, 128, "slowdecay"), ("bf16", 128, 32, 256, "nodecay")])
-def test_chained_segments_match_whole_sequence(io, d, C, seg, variant):
+@pytest.mark.parametrize("io,d,C,seg,variant,rule", [
+    ("bf16", 64, 64, 512, "slowdecay", W.MAMBA2), ("bf16", 64, 64, 512, "default", W.MAMBA2),
+    ("f32", 32, 32, 128, "slowdecay", W.MAMBA2), ("bf16", 128, 32, 256, "nodecay", W.MAMBA2),
+    ("bf16", 64, 64, 512, "slowdecay", W.GATED_DELTANET), ("f32", 32, 16, 64, "slowdecay", W.GATED_DELTANET),
+    ("bf16", 128, 64, 256, "slowdecay", W.GATED_DELTANET)])
+def test_chained_segments_match_whole_sequence(io, d, C, seg, variant, rule):
     N, L = 4 * seg, 13
-    w = W.Workload("chained", W.MAMBA2, 1, 3, N, d, d, L, C, io, 90 + d + seg)
+    w = W.Workload("chained", rule, 1, 3, N, d, d, L, C, io, 90 + d + seg)
     x = W.prefill_inputs(w, variant=variant)
     cuts = [0, seg, 2 * seg, 3 * seg, 4 * seg]
     o, state = chained_prefill(x, cuts, C, L)
     err = rel_err(o, oracle_prefill(x))
-    say(f"[from state] {io} d{d} C{C} segments of {seg} ({variant}): output rel err {err:.3e} (tol {TOL[io]:g})")
+    say(f"[from state] rule {rule} {io} d{d} C{C} segments of {seg} ({variant}): output rel err {err:.3e} "
+        f"(tol {TOL[io]:g})")
     assert err <= TOL[io]
     s_hat, sigma = split_state(state, w.B, w.H, L, d, d)
-    ref = oracle.state_direct(np32(x["k"]), np32(x["v"]), np32(x["log_gate"]), L)
+    ref = oracle.state_direct(np32(x["k"]), np32(x["v"]), np32(x["log_gate"]), L, beta=np32(x["beta"]),
+                              rule=oracle.RULE_GDN if rule == W.GATED_DELTANET else oracle.RULE_MAMBA2)
     live = [l for l in range(1, L) if (N >> (l - 1)) & 1]
     assert (sigma == 0).all()
     err = rel_err(true_state(s_hat, sigma)[:, :, live], ref[:, :, live])
