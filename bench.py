@@ -248,6 +248,44 @@ def from_state_bench(reps: int) -> dict:
                            "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
+def measured_peaks() -> dict:
+    """What this machine reaches on plain library work, as context for the spec-sheet peaks: a 1 GiB
+    device-to-device copy (HBM read + write, beyond the 256 MB last-level cache) and an
+    8192 x 8192 x 8192 bf16 matrix product through torch (hipBLASLt), each the median of 5."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def median_ms(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b))
+        return sorted(out)[len(out) // 2]
+
+    n = 1 << 28  # fp32 elements: 1 GiB
+    src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    ms = median_ms(lambda: dst.copy_(src))
+    copy_gbs = 2 * n * 4 / (ms * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    x = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+    y = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+    ms = median_ms(lambda: torch.mm(x, y))
+    gemm_tflops = 2 * m ** 3 / (ms * 1e-3) / 1e12
+    del x, y
+    return {"copy_1GiB_GBs": round(copy_gbs, 1), "bf16_gemm_8192_TFLOPs": round(gemm_tflops, 1),
+            "hbm_spec_GBs": HBM_PEAK_GBS, "bf16_mfma_spec_TFLOPs": MFMA_BF16_PEAK_TFLOPS}
+
+
 MFMA_FP32_PEAK_TFLOPS = 157.3  # dense fp32 matrix cores
 
 
@@ -367,6 +405,7 @@ def main() -> int:
                     help="also time this many ll_lambda_mlp launches over the 16K workload's rows (0: skip)")
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="also time this many single steps with the last-level cache flushed before each (0: skip)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy and GEMM rates")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -499,6 +538,9 @@ def main() -> int:
     if args.mlp_reps:
         result["lambda_mlp"] = lambda_mlp_bench(args.mlp_reps)
         log(f"[bench] lambda mlp: {result['lambda_mlp']}")
+    if not args.no_peaks:
+        result["measured_peaks"] = measured_peaks()
+        log(f"[bench] measured peaks: {result['measured_peaks']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores")
         result["cpu_baseline"] = cpu_baseline(w)
