@@ -88,3 +88,23 @@ def test_prefill_with_mlp_level_weights(io, d, C):
     err = rel_err(o, oracle_prefill(x))
     say(f"[lambda-mlp] prefill {io} d{d} C{C} with MLP weights: rel err {err:.3e} (tol {TOL[io]:g})")
     assert err <= TOL[io]
+
+
+def test_lambda_mlp_unaligned_rows():
+    """Rows and weights not on 16-byte boundaries (views one float into larger
+    buffers) take the 4-byte path and give the same values."""
+    rows, L, hidden = 640, 15, 30
+    x = W.lambda_mlp_inputs((rows,), L, hidden, seed=13)
+    ref = ref_lambda(x)
+    d = to_dev(x)
+    buf = torch.empty(rows * L + 1, dtype=torch.float32, device="cuda")
+    buf[1:] = d["d"].reshape(-1)
+    din = buf[1:].view(rows, L)
+    out = torch.empty(rows * L + 1, dtype=torch.float32, device="cuda")
+    lam = F.lambda_mlp(din, d["w1"], d["w2"], d["bias"], out=out[1:].view(rows, L))
+    torch.cuda.synchronize()
+    err = rel_err(np32(lam), ref)
+    say(f"[lambda-mlp] unaligned rows: rel err {err:.3e}")
+    assert err <= MLP_TOL
+    aligned = np32(F.lambda_mlp(d["d"], d["w1"], d["w2"], d["bias"]))
+    assert np.array_equal(np32(lam), aligned)
