@@ -9,7 +9,9 @@ The arithmetic lives in ``llref.c`` (plain C, fp64, OpenMP over heads); this
 module builds it with gcc and wraps it for numpy arrays.  Every function states
 the passage it evaluates: of the "Log-Linear Attention" page (technical
 summary, section 2) for the attention itself, of the "Adaptive memory decay for
-log-linear attention" page (section "Method") for the level-weight MLP.  The
+log-linear attention" page (section "Method") for the level-weight MLP, of the
+curvature-conditioned query page (section 2, "Mechanism") for the query
+contraction.  The
 pins that tie it to the pages and to the mathematics are in
 ``tests/test_oracle_pins.py``.
 """
@@ -75,6 +77,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.llref_decode_step.restype = i32
     lib.llref_lambda_mlp.argtypes = [i64, i32, i32] + [P] * 5
     lib.llref_lambda_mlp.restype = i32
+    lib.llref_ccq_query.argtypes = [i32] * 4 + [P] * 5
+    lib.llref_ccq_query.restype = i32
     return lib
 
 
@@ -210,3 +214,20 @@ def lambda_mlp(d, w1, w2, bias, lib=None) -> np.ndarray:
     rc = (lib or load()).llref_lambda_mlp(rows, L, hidden, _ptr(d), _ptr(w1), _ptr(w2), _ptr(bias), _ptr(lam))
     _check(rc, "llref_lambda_mlp")
     return lam
+
+
+def ccq_query(q, k, w, b, lib=None) -> np.ndarray:
+    """Curvature-conditioned query (the curvature-conditioned query page,
+    section 2, "Mechanism"): q_clean = q_t - sigmoid(w_h . q_t + b_h) Sigma_t q_t
+    with Sigma_t the plain covariance of keys 0..t, per token and head, fp64.
+
+    ``q``, ``k`` [B,T,H,dk], ``w`` [H,dk], ``b`` [H]; returns q_clean [B,T,H,dk].
+    """
+    q, k, w, b = map(_f32, (q, k, w, b))
+    B, T, H, dk = q.shape
+    if k.shape != q.shape or w.shape != (H, dk) or b.shape != (H,):
+        raise ValueError("ccq_query: inconsistent arguments")
+    out = np.empty(q.shape, dtype=np.float64)
+    _check((lib or load()).llref_ccq_query(B, T, H, dk, _ptr(q), _ptr(k), _ptr(w), _ptr(b), _ptr(out)),
+           "llref_ccq_query")
+    return out

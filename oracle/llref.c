@@ -473,3 +473,63 @@ int llref_lambda_mlp(int64_t rows, int L, int hidden, const float *d, const floa
   if (bad) return LLREF_ENOMEM;
   return LLREF_OK;
 }
+
+/*
+ * The curvature-conditioned query ("Don't read everything: curvature-
+ * conditioned query for linear attention", section 2, "Mechanism"): before the
+ * read, each query is contracted along the directions where the keys seen so
+ * far are dense,
+ *   mu_t    = (1/(t+1)) sum_{j<=t} k_j                      (running key mean)
+ *   Sigma_t = (1/(t+1)) sum_{j<=t} k_j k_j^T - mu_t mu_t^T    (running key covariance)
+ *   gamma_t = sigmoid(w_h . q_t + b_h)                         (query-conditioned gate)
+ *   q_clean = q_t - gamma_t Sigma_t q_t
+ * per token t and head h.  Readings taken where the page is silent: the
+ * running covariance is the plain (population) covariance of keys 0..t, with
+ * no decay; the gate has one weight vector and bias per head.  The running
+ * sums are kept in double precision and Sigma_t is formed token by token.
+ * q, k: [B][T][H][dk]; w: [H][dk]; b: [H]; q_clean: [B][T][H][dk].
+ */
+int llref_ccq_query(int B, int T, int H, int dk, const float *q, const float *k, const float *w,
+                    const float *b, double *q_clean) {
+  if (B < 1 || T < 0 || H < 1 || dk < 1) return LLREF_EARG;
+  if (T > 0 && (!q || !k || !w || !b || !q_clean)) return LLREF_EARG;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic) reduction(| : bad)
+  for (int bh = 0; bh < B * H; bh++) {
+    const int bb = bh / H, h = bh % H;
+    double *ksum = (double *)calloc((size_t)dk, sizeof(double));
+    double *kk = (double *)calloc((size_t)dk * dk, sizeof(double));
+    double *sig = (double *)malloc(sizeof(double) * dk * dk);
+    if (!ksum || !kk || !sig) {
+      bad |= 2;
+      free(ksum);
+      free(kk);
+      free(sig);
+      continue;
+    }
+    for (int t = 0; t < T; t++) {
+      const size_t row = ((size_t)bb * T + t) * H + h;
+      const float *kt = k + row * dk, *qt = q + row * dk;
+      for (int i = 0; i < dk; i++) {
+        ksum[i] += kt[i];
+        for (int j = 0; j < dk; j++) kk[(size_t)i * dk + j] += (double)kt[i] * kt[j];
+      }
+      const double n = (double)(t + 1);
+      for (int i = 0; i < dk; i++)
+        for (int j = 0; j < dk; j++) sig[(size_t)i * dk + j] = kk[(size_t)i * dk + j] / n - (ksum[i] / n) * (ksum[j] / n);
+      double z = b[h];
+      for (int i = 0; i < dk; i++) z += (double)w[(size_t)h * dk + i] * qt[i];
+      const double gamma = 1.0 / (1.0 + exp(-z));
+      for (int i = 0; i < dk; i++) {
+        double sq = 0.0;
+        for (int j = 0; j < dk; j++) sq += sig[(size_t)i * dk + j] * qt[j];
+        q_clean[row * dk + i] = qt[i] - gamma * sq;
+      }
+    }
+    free(ksum);
+    free(kk);
+    free(sig);
+  }
+  if (bad) return LLREF_ENOMEM;
+  return LLREF_OK;
+}

@@ -42,6 +42,12 @@ MUTANTS = [
     ("mlp hidden layer activated", "h[j] = acc;", "h[j] = acc > 0.0 ? acc : 0.0;"),
     ("mlp softplus replaced by exp", "lambda[r * L + l] = (z > 0.0 ? z : 0.0) + log1p(exp(-fabs(z)));",
      "lambda[r * L + l] = exp(z);"),
+    ("ccq mean term dropped", "sig[(size_t)i * dk + j] = kk[(size_t)i * dk + j] / n - (ksum[i] / n) * (ksum[j] / n);",
+     "sig[(size_t)i * dk + j] = kk[(size_t)i * dk + j] / n;"),
+    ("ccq covariance over t, not t + 1", "const double n = (double)(t + 1);", "const double n = (double)(t > 0 ? t : 1);"),
+    ("ccq gate sign flipped", "const double gamma = 1.0 / (1.0 + exp(-z));", "const double gamma = 1.0 / (1.0 + exp(z));"),
+    ("ccq query expanded, not contracted", "q_clean[row * dk + i] = qt[i] - gamma * sq;",
+     "q_clean[row * dk + i] = qt[i] + gamma * sq;"),
 ]
 
 
@@ -157,7 +163,46 @@ def pin_failures(lib):
     pre2 = np.log(np.expm1(oracle.lambda_mlp(-d1, w1, w2, b, lib=lib))) - b
     if not np.allclose(pre1, -pre2, atol=1e-8):
         fails.append("mlp-linear")
+
+    # the curvature-conditioned query: numpy's population covariance, and a
+    # hand-worked two-token case
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((1, 6, 2, 3)).astype(np.float32)
+    k = rng.standard_normal((1, 6, 2, 3)).astype(np.float32)
+    w = rng.standard_normal((2, 3)).astype(np.float32)
+    b = rng.standard_normal(2).astype(np.float32)
+    qc = oracle.ccq_query(q, k, w, b, lib=lib)
+    ref = _ccq_numpy(q, k, w, b)
+    if not np.allclose(qc, ref, rtol=1e-10, atol=1e-12):
+        fails.append("ccq-numpy")
+    qh, kh = _ccq_hand()
+    if not np.allclose(oracle.ccq_query(qh, kh, np.zeros((1, 2)), np.zeros(1), lib=lib)[0, 1, 0], [1.0, 3.0],
+                       atol=1e-14):
+        fails.append("ccq-hand")
     return fails
+
+
+def _ccq_numpy(q, k, w, b):
+    """q - sigmoid(w.q + b) Cov(k_0..k_t) q with numpy's population covariance."""
+    B, T, H, dk = q.shape
+    out = np.zeros((B, T, H, dk))
+    for bb in range(B):
+        for h in range(H):
+            for t in range(T):
+                ks = k[bb, :t + 1, h].astype(np.float64)
+                cov = np.cov(ks.T, bias=True).reshape(dk, dk) if t > 0 else np.zeros((dk, dk))
+                qt = q[bb, t, h].astype(np.float64)
+                g = 1.0 / (1.0 + math.exp(-(float(w[h].astype(np.float64) @ qt) + float(b[h]))))
+                out[bb, t, h] = qt - g * (cov @ qt)
+    return out
+
+
+def _ccq_hand():
+    """Keys (1, 0) then (-1, 0): at t = 1 the mean is 0 and the covariance
+    diag(1, 0); with w = 0, b = 0 the gate is 1/2, so q = (2, 3) becomes (1, 3)."""
+    q = np.array([[[[5.0, 5.0]], [[2.0, 3.0]]]], dtype=np.float32)
+    k = np.array([[[[1.0, 0.0]], [[-1.0, 0.0]]]], dtype=np.float32)
+    return q, k
 
 
 def _build_variant(tmp_path, name, text):

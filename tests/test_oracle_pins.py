@@ -402,6 +402,62 @@ def test_lambda_mlp_acts_per_row():
     assert np.all(lam > 0)
 
 
+# --------------------------------------- curvature-conditioned query (CCQ)
+
+def _ccq_inputs(T=9, H=2, dk=4, seed=0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((2, T, H, dk)).astype(np.float32)
+    k = rng.standard_normal((2, T, H, dk)).astype(np.float32)
+    w = rng.standard_normal((H, dk)).astype(np.float32)
+    b = rng.standard_normal(H).astype(np.float32)
+    return q, k, w, b
+
+
+def test_ccq_first_token_is_unchanged():
+    """One key has zero covariance: q_clean_0 = q_0."""
+    q, k, w, b = _ccq_inputs()
+    qc = oracle.ccq_query(q, k, w, b)
+    assert np.array_equal(qc[:, 0], q[:, 0].astype(np.float64))
+
+
+def test_ccq_matches_numpy_population_covariance():
+    """Sigma_t is the plain covariance of keys 0..t (numpy's np.cov with
+    bias=True), the gate sigmoid(w_h . q_t + b_h)."""
+    q, k, w, b = _ccq_inputs(T=7, H=2, dk=3, seed=8)
+    qc = oracle.ccq_query(q, k, w, b)
+    for bb in range(2):
+        for h in range(2):
+            for t in range(1, 7):
+                cov = np.cov(k[bb, :t + 1, h].astype(np.float64).T, bias=True)
+                qt = q[bb, t, h].astype(np.float64)
+                g = 1.0 / (1.0 + math.exp(-(float(w[h].astype(np.float64) @ qt) + float(b[h]))))
+                assert np.allclose(qc[bb, t, h], qt - g * cov @ qt, rtol=1e-12, atol=1e-12)
+
+
+def test_ccq_hand_worked_example():
+    """Keys (1, 0) then (-1, 0): mean 0, covariance diag(1, 0) at t = 1; with
+    w = 0 and b = 0 the gate is 1/2, so q = (2, 3) becomes (2 - 1, 3) = (1, 3)."""
+    q = np.array([[[[5.0, 5.0]], [[2.0, 3.0]]]], dtype=np.float32)
+    k = np.array([[[[1.0, 0.0]], [[-1.0, 0.0]]]], dtype=np.float32)
+    qc = oracle.ccq_query(q, k, np.zeros((1, 2)), np.zeros(1))
+    assert np.allclose(qc[0, 1, 0], [1.0, 3.0], atol=1e-15)
+    assert np.allclose(qc[0, 0, 0], [5.0, 5.0], atol=0)
+
+
+def test_ccq_special_cases():
+    """A closed gate (b -> -inf) or keys that never change (zero covariance)
+    leave q unchanged; the contraction never increases q . q_clean beyond
+    q . q (Sigma is positive semi-definite)."""
+    q, k, w, b = _ccq_inputs(seed=3)
+    qc = oracle.ccq_query(q, k, np.zeros_like(w), np.full_like(b, -80.0))
+    assert np.allclose(qc, q, rtol=0, atol=1e-30)
+    same = np.broadcast_to(k[:, :1], k.shape).copy()
+    assert np.allclose(oracle.ccq_query(q, same, w, b), q, rtol=0, atol=1e-12)
+    qc = oracle.ccq_query(q, k, w, b)
+    qq = np.einsum("bthd,bthd->bth", q.astype(np.float64), q.astype(np.float64))
+    assert (np.einsum("bthd,bthd->bth", q.astype(np.float64), qc) <= qq + 1e-12).all()
+
+
 # --------------------------------------------------------------- generators
 
 def test_softplus_initial_bias_is_near_one():
