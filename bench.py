@@ -286,6 +286,63 @@ def measured_peaks() -> dict:
             "hbm_spec_GBs": HBM_PEAK_GBS, "bf16_mfma_spec_TFLOPs": MFMA_BF16_PEAK_TFLOPS}
 
 
+def ccq_bench(reps: int) -> dict:
+    """ll_ccq_query (the curvature-conditioned query) on the 16K prefill's q and k (B2 H16 T16384
+    d64 bf16): per-call time and per-kernel averages (HIP events on the launch stream), then the
+    prefill step that reads with the contracted queries."""
+    import torch
+
+    import fenwick_tree_linear_amd as F
+    from fenwick_tree_linear_amd import workloads as W
+
+    w = W.WORKLOADS["prefill-16k"]
+    dev = torch.device("cuda:0")
+    x = W.prefill_inputs(w, device=dev)
+    g = W.ccq_inputs(w.H, w.dk, seed=w.seed, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    nbytes = F.ll_ccq_query_workspace_bytes(w.B, w.T, w.H, w.dk, F.LL_BF16)
+    cws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    qc = torch.empty_like(x["q"])
+    prob = F.LLProblem(w.B, w.T, w.H, w.dk, w.dv, w.L, w.C, F.LL_BF16, F.LL_MAMBA2)
+    ws_bytes = F.ll_attn_fwd_workspace_bytes(prob)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    o = torch.empty(w.B, w.T, w.H, w.dv, dtype=torch.bfloat16, device=dev)
+
+    def ccq():
+        F.ll_ccq_query(w.B, w.T, w.H, w.dk, F.LL_BF16, x["q"], x["k"], g["w"], g["b"], qc, cws, nbytes, stream)
+
+    def step():
+        ccq()
+        F.ll_attn_fwd(prob, qc, x["k"], x["v"], x["log_gate"], x["lam"], None, o, None, ws, ws_bytes, stream)
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    ms = timed(ccq, reps)
+    F.ll_kernel_timing_read()
+    F.ll_kernel_timing_enable(True)
+    for _ in range(reps):
+        ccq()
+    torch.cuda.synchronize()
+    kt = F.ll_kernel_timing_read()
+    F.ll_kernel_timing_enable(False)
+    step_ms = timed(step, reps)
+    return {"workload": "ll_ccq_query B2 H16 T16384 d64 bf16 (running key covariance from two all-ones, "
+                        "no-decay prefills)",
+            "ms_per_call": round(ms, 5), "kernels_us": {k: round(t / n * 1e3, 2) for k, (t, n) in kt.items()},
+            "prefill_with_ccq": {"ms_per_step": round(step_ms, 5),
+                                 "tokens_per_s": round(w.B * w.T / (step_ms * 1e-3), 1)}}
+
+
 MFMA_FP32_PEAK_TFLOPS = 157.3  # dense fp32 matrix cores
 
 
@@ -401,6 +458,8 @@ def main() -> int:
                     help="also time this many ll_decode_step_ragged steps with per-sequence positions (0: skip)")
     ap.add_argument("--from-state-reps", type=int, default=20,
                     help="also time this many prefills of the 16K workload's second half from a state (0: skip)")
+    ap.add_argument("--ccq-reps", type=int, default=10,
+                    help="also time this many curvature-conditioned query calls on the 16K workload (0: skip)")
     ap.add_argument("--mlp-reps", type=int, default=50,
                     help="also time this many ll_lambda_mlp launches over the 16K workload's rows (0: skip)")
     ap.add_argument("--cold-reps", type=int, default=10,
@@ -535,6 +594,9 @@ def main() -> int:
     if args.from_state_reps:
         result["from_state"] = from_state_bench(args.from_state_reps)
         log(f"[bench] prefill from a state: {result['from_state']}")
+    if args.ccq_reps:
+        result["ccq"] = ccq_bench(args.ccq_reps)
+        log(f"[bench] curvature-conditioned query: {result['ccq']}")
     if args.mlp_reps:
         result["lambda_mlp"] = lambda_mlp_bench(args.mlp_reps)
         log(f"[bench] lambda mlp: {result['lambda_mlp']}")

@@ -15,12 +15,15 @@ from .binding import (  # noqa: F401
     LLError,
     LLProblem,
     attn_fwd,
+    ccq_query,
     decode_state_tensor,
     lambda_mlp,
     lib_path,
     ll_attn_fwd,
     ll_attn_fwd_from_state,
     ll_attn_fwd_workspace_bytes,
+    ll_ccq_query,
+    ll_ccq_query_workspace_bytes,
     ll_decode_state_bytes,
     ll_decode_step,
     ll_decode_step_ragged,

@@ -67,9 +67,12 @@ def load_library() -> ctypes.CDLL:
                                           ctypes.POINTER(ctypes.c_int), i32, ctypes.POINTER(ctypes.c_int)]
     lib.ll_lambda_mlp.argtypes = [i64, i32, i32, P, P, P, P, P, P]
     lib.ll_attn_fwd_from_state.argtypes = [ctypes.POINTER(LLProblem), i64, P, P, P, P, P, P, P, P, P, P, sz, P]
+    lib.ll_ccq_query_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.ll_ccq_query.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, sz, P]
     lib.ll_decode_step_ragged.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
     for fn in ("ll_attn_fwd_workspace_bytes", "ll_attn_fwd", "ll_decode_state_bytes", "ll_decode_step",
-               "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp", "ll_decode_step_ragged", "ll_attn_fwd_from_state"):
+               "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp", "ll_decode_step_ragged", "ll_attn_fwd_from_state",
+               "ll_ccq_query_workspace_bytes", "ll_ccq_query"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -145,6 +148,17 @@ def ll_decode_step_ragged(B, H, dk, dv, L, io, rule, pos, q, k, v, log_gate, lam
     _check(load_library().ll_decode_step_ragged(B, H, dk, dv, L, io, rule, _ptr(pos), _ptr(q), _ptr(k), _ptr(v),
                                                 _ptr(log_gate), _ptr(lam), _ptr(beta), _ptr(o), _ptr(state),
                                                 _stream(stream)))
+
+
+def ll_ccq_query_workspace_bytes(B: int, T: int, H: int, dk: int, io: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().ll_ccq_query_workspace_bytes(B, T, H, dk, io, ctypes.byref(out)))
+    return out.value
+
+
+def ll_ccq_query(B, T, H, dk, io, q, k, w, b, q_clean, workspace, workspace_bytes: int, stream=None) -> None:
+    _check(load_library().ll_ccq_query(B, T, H, dk, io, _ptr(q), _ptr(k), _ptr(w), _ptr(b), _ptr(q_clean),
+                                       _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def ll_kernel_timing_enable(on: bool) -> None:
@@ -224,3 +238,16 @@ def lambda_mlp(d, w1, w2, bias, out=None, stream=None):
     lam = out if out is not None else torch.empty_like(d)
     ll_lambda_mlp(d.numel() // L, L, hidden, d, w1, w2, bias, lam, stream)
     return lam
+
+
+def ccq_query(q, k, w, b, out=None, workspace=None, stream=None):
+    """The curvature-conditioned query q - sigmoid(w_h . q + b_h) Cov(k_0..k_t) q
+    for q, k [B,T,H,dk] (io dtype), w [H,dk], b [H] (fp32); returns q_clean."""
+    B, T, H, dk = q.shape
+    io = io_code(q.dtype)
+    nbytes = ll_ccq_query_workspace_bytes(B, T, H, dk, io)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    qc = out if out is not None else torch.empty_like(q)
+    ll_ccq_query(B, T, H, dk, io, q, k, w, b, qc, workspace, workspace.numel(), stream)
+    return qc

@@ -148,9 +148,9 @@ ll_status plan_prefill(const ll_problem* p, bool exporting, Plan* out) {
 
 // ---------------------------------------------------------- kernel timing
 enum KernelId { K_CHUNK_STATE, K_FENWICK_SCAN, K_CHUNK_ATTN, K_STATE_EXPORT, K_DECODE_STEP, K_GDN_WY, K_GDN_STATE,
-                K_LAMBDA_MLP, K_PRIOR_READ, K_COUNT };
+                K_LAMBDA_MLP, K_PRIOR_READ, K_CCQ, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"ll_chunk_state", "ll_fenwick_scan", "ll_chunk_attn", "ll_state_export",
-                                           "ll_decode_step", "ll_gdn_wy",       "ll_gdn_state",   "ll_lambda_mlp", "ll_prior_read"};
+                                           "ll_decode_step", "ll_gdn_wy",       "ll_gdn_state",   "ll_lambda_mlp", "ll_prior_read", "ll_ccq"};
 
 struct Timing {
   std::mutex mu;
@@ -449,6 +449,102 @@ ll_status ll_lambda_mlp(int64_t rows, int L, int hidden, const float* d, const f
   if ((const float*)lambda == d) return fail(LL_ERR_SHAPE, "lambda must not alias d");
   hipError_t e = timed(K_LAMBDA_MLP, stream,
                        [&] { return llattn::launch_lambda_mlp(rows, L, hidden, d, w1, w2, bias, lambda, stream); });
+  if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+namespace {
+
+// The curvature-conditioned query: two prefills with all level weights 1 and
+// no decay give the running sums it needs; their buffers, then the prefill
+// workspace.
+struct CcqPlan {
+  ll_problem p;
+  size_t ones_off, zeros_off, e0_off, kkq_off, ksum_off, fwd_off, fwd_bytes, bytes;
+};
+
+ll_status plan_ccq(int B, int T, int H, int dk, ll_dtype io, CcqPlan* out) {
+  if (io != LL_F32 && io != LL_BF16) return fail(LL_ERR_DTYPE, "unknown io dtype %d", (int)io);
+  if (B < 1 || T < 1 || H < 1 || dk < 1)
+    return fail(LL_ERR_SHAPE, "sizes must be positive (B=%d T=%d H=%d dk=%d)", B, T, H, dk);
+  if (!supported_head(dk, io))
+    return fail(LL_ERR_UNSUPPORTED, "head size %d not supported for %s io", dk, io == LL_BF16 ? "bf16" : "fp32");
+  const size_t esz = io == LL_BF16 ? 2 : 4;
+  int C = 0;
+  for (int c : {64, 32, 16})
+    if (!C && supported_chunk(c, io) && T % c == 0 && (size_t)c * dk * esz <= (size_t)llattn::kAttnTileBytesMax) C = c;
+  if (!C) return fail(LL_ERR_UNSUPPORTED, "T=%d is not a multiple of a supported chunk size for head size %d", T, dk);
+  CcqPlan c;
+  c.p.B = B;
+  c.p.T = T;
+  c.p.H = H;
+  c.p.dk = c.p.dv = dk;
+  c.p.L = bit_length((int64_t)T - 1) + 1;
+  if (c.p.L < 2) c.p.L = 2;
+  c.p.C = C;
+  c.p.io = io;
+  c.p.rule = LL_MAMBA2;
+  Plan pl;
+  ll_status st = plan_prefill(&c.p, false, &pl);
+  if (st != LL_OK) return st;
+  const size_t rows = (size_t)B * T * H;
+  size_t off = 0;
+  c.ones_off = off;
+  off = align256(off + rows * c.p.L * 4);
+  c.zeros_off = off;
+  off = align256(off + rows * 4);
+  c.e0_off = off;
+  off = align256(off + rows * dk * esz);
+  c.kkq_off = off;
+  off = align256(off + rows * dk * esz);
+  c.ksum_off = off;
+  off = align256(off + rows * dk * esz);
+  c.fwd_off = off;
+  c.fwd_bytes = pl.bytes;
+  c.bytes = off + pl.bytes;
+  *out = c;
+  return LL_OK;
+}
+
+}  // namespace
+
+ll_status ll_ccq_query_workspace_bytes(int B, int T, int H, int dk, ll_dtype io, size_t* bytes) {
+  if (!bytes) return fail(LL_ERR_NULL, "bytes is NULL");
+  CcqPlan c;
+  ll_status st = plan_ccq(B, T, H, dk, io, &c);
+  if (st != LL_OK) return st;
+  *bytes = c.bytes;
+  return ok();
+}
+
+ll_status ll_ccq_query(int B, int T, int H, int dk, ll_dtype io, const void* q, const void* k, const float* w,
+                       const float* b, void* q_clean, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  CcqPlan c;
+  ll_status st = plan_ccq(B, T, H, dk, io, &c);
+  if (st != LL_OK) return st;
+  if (!q || !k || !w || !b || !q_clean) return fail(LL_ERR_NULL, "q, k, w, b and q_clean must not be NULL");
+  if (workspace_bytes < c.bytes)
+    return fail(LL_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, c.bytes);
+  if (!workspace) return fail(LL_ERR_WORKSPACE, "workspace is NULL");
+  char* ws = static_cast<char*>(workspace);
+  float* ones = reinterpret_cast<float*>(ws + c.ones_off);
+  float* zeros = reinterpret_cast<float*>(ws + c.zeros_off);
+  void* e0 = ws + c.e0_off;
+  void* kkq = ws + c.kkq_off;
+  void* ksum = ws + c.ksum_off;
+  const int code = io == LL_BF16 ? 1 : 0;
+  hipError_t e = timed(K_CCQ, stream, [&] {
+    return llattn::launch_ccq_fill(code, (int64_t)B * T * H, c.p.L, dk, ones, zeros, e0, stream);
+  });
+  if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  // sum_{j<=t} (k_j . q_t) k_j and sum_{j<=t} k_j
+  st = run_prefill(&c.p, 0, nullptr, q, k, k, zeros, ones, nullptr, kkq, nullptr, ws + c.fwd_off, c.fwd_bytes, stream);
+  if (st != LL_OK) return st;
+  st = run_prefill(&c.p, 0, nullptr, e0, e0, k, zeros, ones, nullptr, ksum, nullptr, ws + c.fwd_off, c.fwd_bytes,
+                   stream);
+  if (st != LL_OK) return st;
+  e = timed(K_CCQ, stream,
+            [&] { return llattn::launch_ccq_combine(code, dk, B, T, H, q, kkq, ksum, w, b, q_clean, stream); });
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -76,6 +76,9 @@ hipError_t launch_chunk_attn(int io, int D, int C, const PrefillArgs& a, hipStre
 hipError_t launch_fenwick_scan(int D, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_state_export(int D, int C, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prior_read(int io, int D, int C, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_ccq_fill(int io, int64_t rows, int L, int D, float* ones, float* zeros, void* e0, hipStream_t s);
+hipError_t launch_ccq_combine(int io, int D, int B, int T, int H, const void* q, const void* kkq, const void* ksum,
+                              const float* w, const float* b, void* qc, hipStream_t s);
 hipError_t launch_decode_step(int io, int D, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_gdn_wy(int io, int D, int C, const GdnArgs& a, hipStream_t s);
 hipError_t launch_gdn_state(int io, int D, int C, const GdnArgs& a, hipStream_t s);

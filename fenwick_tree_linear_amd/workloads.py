@@ -16,8 +16,9 @@ nearest even); gates, lambda and beta stay fp32.
 
 Each tensor has its own generator, seeded from the workload seed and the
 tensor's index (q 0, k 1, v 2, log_gate 3, lambda 4, beta 5, one-hot level 6;
-the level-weight MLP: d 7, W1 8, W2 9, bias 10), so any subset can be drawn
-alone and yields the same values.
+the level-weight MLP: d 7, W1 8, W2 9, bias 10; the query-contraction gate:
+w 11, b 12, dense key direction 13), so any subset can be drawn alone and
+yields the same values.
 
 Level-weight MLP inputs (the adaptive-decay page's lambda producer, hidden
 size 2L): d ~ N(0, 1) per token, head and level; W1 ~ N(0, 1/L);
@@ -174,3 +175,23 @@ def lambda_mlp_inputs(lead: tuple, L: int, hidden: int | None = None, seed: int 
     w2 = torch.randn(hidden, L, generator=_gen(seed, 9, device), device=device) * (0.5 / math.sqrt(hidden))
     bias = 0.54 + 0.25 * torch.randn(L, generator=_gen(seed, 10, device), device=device)
     return dict(d=d.contiguous(), w1=w1.contiguous(), w2=w2.contiguous(), bias=bias.contiguous())
+
+
+def ccq_inputs(H: int, dk: int, seed: int = 0, device="cpu") -> dict:
+    """Gate of the curvature-conditioned query per head: w [H, dk] ~ N(0, 1/dk),
+    b [H] ~ N(0, 1) (fp32)."""
+    w = torch.randn(H, dk, generator=_gen(seed, 11, device), device=device) / math.sqrt(dk)
+    b = torch.randn(H, generator=_gen(seed, 12, device), device=device)
+    return dict(w=w.contiguous(), b=b.contiguous())
+
+
+def with_dense_key_direction(k: torch.Tensor, scale: float = 3.0, seed: int = 0) -> torch.Tensor:
+    """Keys with one crowded direction per head: k + scale N(0, 1) u_h, u_h a
+    random unit vector of head h (zero mean, so the running covariance has an
+    eigenvalue near scale^2 along u_h).  Returned in k's dtype."""
+    B, T, H, dk = k.shape
+    g = _gen(seed, 13, "cpu")
+    u = torch.randn(H, dk, generator=g)
+    u = u / u.norm(dim=-1, keepdim=True)
+    a = torch.randn(B, T, H, 1, generator=g) * scale
+    return (k.float().cpu() + a * u).to(k.dtype).to(k.device)

@@ -209,6 +209,28 @@ ll_status ll_decode_step_ragged(int B, int H, int dk, int dv, int L, ll_dtype io
                                 const float* lambda, const float* beta, void* o, void* state,
                                 hipStream_t stream);
 
+/*
+ * The curvature-conditioned query ("Don't read everything: curvature-
+ * conditioned query for linear attention", section 2, "Mechanism"), a
+ * read-side correction applied before the read:
+ *   q_clean_t = q_t - gamma_t Sigma_t q_t,   gamma_t = sigmoid(w_h . q_t + b_h),
+ *   Sigma_t   = the covariance of keys 0..t of the head (population, no decay).
+ * Pass q_clean as q to ll_attn_fwd: the contraction then applies to the read of
+ * every level.
+ *   q, k [B,T,H,dk]  io dtype        w [H,dk], b [H]  fp32, the gate of each head
+ *   q_clean [B,T,H,dk]  io dtype, written (may be q itself)
+ *   workspace  device memory of >= ll_ccq_query_workspace_bytes; contents on
+ *              entry do not matter.
+ * The running sums come from two chunk-parallel prefills with every level
+ * weight 1 and no decay.  Implemented for the head sizes of ll_attn_fwd and T
+ * a multiple of a supported chunk size (16 for fp32, 32 for bf16), T < 2^23
+ * (LL_ERR_UNSUPPORTED otherwise).
+ */
+ll_status ll_ccq_query_workspace_bytes(int B, int T, int H, int dk, ll_dtype io, size_t* bytes);
+ll_status ll_ccq_query(int B, int T, int H, int dk, ll_dtype io, const void* q, const void* k, const float* w,
+                       const float* b, void* q_clean, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
 /* Text of the last error on the calling thread; valid until its next call. */
 const char* ll_last_error(void);
 
@@ -219,7 +241,7 @@ const char* ll_last_error(void);
  * recorded events, then reports for up to `capacity` kernels their name (a
  * static string: "ll_chunk_state", "ll_fenwick_scan", "ll_chunk_attn",
  * "ll_state_export", "ll_decode_step", "ll_gdn_wy", "ll_gdn_state",
- * "ll_lambda_mlp", "ll_prior_read"), the summed milliseconds and the launch
+ * "ll_lambda_mlp", "ll_prior_read", "ll_ccq"), the summed milliseconds and the launch
  * count, and clears the record.  Enabling creates HIP events lazily; timing
  * adds two event records per launch, so do not time throughput with it on.
  */

@@ -24,7 +24,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["ll_attn_fwd", "ll_attn_fwd_from_state", "ll_attn_fwd_workspace_bytes", "ll_decode_state_bytes", "ll_decode_step", "ll_decode_step_ragged",
+        ["ll_attn_fwd", "ll_attn_fwd_from_state", "ll_attn_fwd_workspace_bytes", "ll_ccq_query",
+         "ll_ccq_query_workspace_bytes", "ll_decode_state_bytes", "ll_decode_step", "ll_decode_step_ragged",
          "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp", "ll_last_error"])
 
 
@@ -220,3 +221,23 @@ def test_prefill_from_state_validation_before_any_launch():
     assert call(prob(T=2048, L=16), 2 ** 15 - 2048, state_out=D)[0] == "LL_ERR_SHAPE"
     assert call(prob(T=2048, L=16), 2 ** 15, state_out=None)[0] == "LL_ERR_SHAPE"
     assert call(prob(T=2048, L=13), 2048 * 3)[0] == "LL_ERR_SHAPE"  # position 8191 needs 14 levels
+
+
+def test_ccq_validation_before_any_launch():
+    D = DUMMY
+    n = F.ll_ccq_query_workspace_bytes(2, 16384, 16, 64, F.LL_BF16)
+    # two prefills' running sums: ones [rows, 15] fp32, zeros, e0, kkq, ksum (bf16 rows) + prefill workspace
+    rows = 2 * 16384 * 16
+    assert n >= rows * 15 * 4 + rows * 4 + 3 * rows * 64 * 2 + F.ll_attn_fwd_workspace_bytes(prob())
+
+    def call(B=2, T=16384, H=16, dk=64, io=F.LL_BF16, q=D, k=D, w=D, b=D, qc=D, ws=D, wsb=n):
+        return status_of(F.ll_ccq_query, B, T, H, dk, io, q, k, w, b, qc, ws, wsb, 0)[0]
+
+    assert call(T=100) == "LL_ERR_UNSUPPORTED"  # no supported chunk divides 100
+    assert call(dk=48) == "LL_ERR_UNSUPPORTED"
+    assert call(io=7) == "LL_ERR_DTYPE"
+    assert call(B=0) == "LL_ERR_SHAPE"
+    assert call(w=None) == "LL_ERR_NULL"
+    assert call(qc=None) == "LL_ERR_NULL"
+    assert call(wsb=n - 1) == "LL_ERR_WORKSPACE"
+    assert call(ws=None) == "LL_ERR_WORKSPACE"
