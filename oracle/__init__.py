@@ -79,6 +79,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.llref_lambda_mlp.restype = i32
     lib.llref_ccq_query.argtypes = [i32] * 4 + [P] * 5
     lib.llref_ccq_query.restype = i32
+    lib.llref_bwd_direct.argtypes = [i32] * 6 + [P] * 11
+    lib.llref_bwd_direct.restype = i32
     return lib
 
 
@@ -230,4 +232,21 @@ def ccq_query(q, k, w, b, lib=None) -> np.ndarray:
     out = np.empty(q.shape, dtype=np.float64)
     _check((lib or load()).llref_ccq_query(B, T, H, dk, _ptr(q), _ptr(k), _ptr(w), _ptr(b), _ptr(out)),
            "llref_ccq_query")
+    return out
+
+
+def bwd_direct(q, k, v, log_gate, lam, dO, lib=None) -> dict:
+    """Gradients of the Mamba-2 log-linear read ("Log-Linear Attention",
+    sections 2.2-2.3, masked form) for a loss with gradient dO at o, from the
+    definition term by term, fp64.  Returns dq, dk, dv, dlog_gate, dlambda."""
+    q, k, v, g, lam, dO = map(_f32, (q, k, v, log_gate, lam, dO))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    out = dict(dq=np.empty((B, T, H, dk)), dk=np.empty((B, T, H, dk)), dv=np.empty((B, T, H, dv)),
+               dlog_gate=np.empty((B, T, H)), dlambda=np.empty((B, T, H, L)))
+    rc = (lib or load()).llref_bwd_direct(B, T, H, dk, dv, L, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(lam),
+                                          _ptr(dO), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                          _ptr(out["dlog_gate"]), _ptr(out["dlambda"]))
+    _check(rc, "llref_bwd_direct")
     return out

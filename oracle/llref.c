@@ -533,3 +533,74 @@ int llref_ccq_query(int B, int T, int H, int dk, const float *q, const float *k,
   if (bad) return LLREF_ENOMEM;
   return LLREF_OK;
 }
+
+/*
+ * Gradients of the Mamba-2 log-linear read (the masked form of sections 2.2
+ * and 2.3) for a loss whose gradient with respect to o is dO, from the
+ * definition term by term.  With, for each pair s <= t,
+ *   w  = prod_{r=s+1}^{t} a_r,   lam = lambda_t^(lev(t,s)),
+ *   P  = q_t . k_s,              A   = dO_t . v_s,
+ * the pair contributes lam w P v_s to o_t, hence
+ *   dq_t += lam w A k_s,  dk_s += lam w A q_t,  dv_s += lam w P dO_t,
+ *   dlambda_t^(lev) += w P A,
+ * and, for s < t, lam w P A to dG_t and minus that to dG_s, where
+ * G_t = sum_{r<=t} log a_r (w = e^{G_t - G_s}); then
+ *   dlog_gate_r = sum_{t >= r} dG_t.
+ * Inputs as llref_fwd_direct (Mamba-2 write); outputs in double, same
+ * layouts: dq, dk [B][T][H][dk], dv [B][T][H][dv], dlog_gate [B][T][H],
+ * dlambda [B][T][H][L].
+ */
+int llref_bwd_direct(int B, int T, int H, int dk, int dv, int L, const float *q, const float *k,
+                     const float *v, const float *log_gate, const float *lambda, const float *dO,
+                     double *dq, double *dk_out, double *dv_out, double *dlog_gate, double *dlambda) {
+  if (B < 1 || T < 1 || H < 1 || dk < 1 || dv < 1) return LLREF_EARG;
+  if (!q || !k || !v || !log_gate || !lambda || !dO) return LLREF_EARG;
+  if (!dq || !dk_out || !dv_out || !dlog_gate || !dlambda) return LLREF_EARG;
+  if (!levels_cover(T, L)) return LLREF_ELEVELS;
+  const dims_t d = {B, T, H, dk, dv, L};
+  memset(dq, 0, sizeof(double) * (size_t)B * T * H * dk);
+  memset(dk_out, 0, sizeof(double) * (size_t)B * T * H * dk);
+  memset(dv_out, 0, sizeof(double) * (size_t)B * T * H * dv);
+  memset(dlambda, 0, sizeof(double) * (size_t)B * T * H * L);
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic) reduction(| : bad)
+  for (int bh = 0; bh < B * H; bh++) {
+    const int b = bh / H, h = bh % H;
+    double *dG = (double *)calloc((size_t)T, sizeof(double));
+    if (!dG) {
+      bad |= 2;
+      continue;
+    }
+    for (int64_t t = 0; t < T; t++) {
+      const size_t it = ix_tok(&d, b, t, h);
+      const float *qt = q + it * dk, *dOt = dO + it * dv;
+      double logw = 0.0; /* log w: the log-gates of tokens s+1..t */
+      for (int64_t s = t; s >= 0; s--) {
+        const size_t is = ix_tok(&d, b, s, h);
+        const float *ks = k + is * dk, *vs = v + is * dv;
+        const int lev = llref_level(t, s);
+        const double w = exp(logw), lam = lambda[it * L + lev];
+        const double P = dot_f(qt, ks, dk), A = dot_f(dOt, vs, dv);
+        for (int i = 0; i < dk; i++) {
+          dq[it * dk + i] += lam * w * A * ks[i];
+          dk_out[is * dk + i] += lam * w * A * qt[i];
+        }
+        for (int j = 0; j < dv; j++) dv_out[is * dv + j] += lam * w * P * dOt[j];
+        dlambda[it * L + lev] += w * P * A;
+        if (s < t) {
+          dG[t] += lam * w * P * A;
+          dG[s] -= lam * w * P * A;
+        }
+        logw += log_gate[is];
+      }
+    }
+    double acc = 0.0;
+    for (int64_t r = T - 1; r >= 0; r--) {
+      acc += dG[r];
+      dlog_gate[ix_tok(&d, b, r, h)] = acc;
+    }
+    free(dG);
+  }
+  if (bad) return LLREF_ENOMEM;
+  return LLREF_OK;
+}

@@ -48,6 +48,11 @@ MUTANTS = [
     ("ccq gate sign flipped", "const double gamma = 1.0 / (1.0 + exp(-z));", "const double gamma = 1.0 / (1.0 + exp(z));"),
     ("ccq query expanded, not contracted", "q_clean[row * dk + i] = qt[i] - gamma * sq;",
      "q_clean[row * dk + i] = qt[i] + gamma * sq;"),
+    ("bwd dk without the level weight", "dk_out[is * dk + i] += lam * w * A * qt[i];",
+     "dk_out[is * dk + i] += w * A * qt[i];"),
+    ("bwd gate gradient with the wrong sign at the source", "dG[s] -= lam * w * P * A;", "dG[s] += lam * w * P * A;"),
+    ("bwd gate gradient summed forward", "for (int64_t r = T - 1; r >= 0; r--) {",
+     "for (int64_t r = 0; r < T; r++) {"),
 ]
 
 
@@ -175,6 +180,28 @@ def pin_failures(lib):
     ref = _ccq_numpy(q, k, w, b)
     if not np.allclose(qc, ref, rtol=1e-10, atol=1e-12):
         fails.append("ccq-numpy")
+    # the backward: central differences of the forward's loss on a few coordinates
+    rng = np.random.default_rng(6)
+    T, H, d, L = 10, 1, 2, 5
+    xb = {n: rng.standard_normal((1, T, H, d)).astype(np.float32) for n in ("q", "k", "v")}
+    xb["g"] = (-rng.uniform(0.01, 0.3, (1, T, H))).astype(np.float32)
+    xb["lam"] = rng.uniform(0.5, 1.5, (1, T, H, L)).astype(np.float32)
+    dO = rng.standard_normal((1, T, H, d)).astype(np.float32)
+    gr = oracle.bwd_direct(xb["q"], xb["k"], xb["v"], xb["g"], xb["lam"], dO, lib=lib)
+
+    def loss(x):
+        return float(np.sum(oracle.fwd_direct(x["q"], x["k"], x["v"], x["g"], x["lam"], lib=lib) * dO))
+
+    for name, key, idx in (("k", "dk", (0, 2, 0, 1)), ("g", "dlog_gate", (0, 3, 0)), ("g", "dlog_gate", (0, 7, 0)),
+                           ("q", "dq", (0, 8, 0, 0)), ("v", "dv", (0, 1, 0, 1)), ("lam", "dlambda", (0, 9, 0, 2))):
+        xp = {kk: vv.copy() for kk, vv in xb.items()}
+        xm = {kk: vv.copy() for kk, vv in xb.items()}
+        xp[name][idx] += np.float32(1e-3)
+        xm[name][idx] -= np.float32(1e-3)
+        fd = (loss(xp) - loss(xm)) / (float(xp[name][idx]) - float(xm[name][idx]))
+        if abs(fd - gr[key][idx]) > 1e-6 * (1 + abs(fd)):
+            fails.append("bwd-" + key)
+            break
     qh, kh = _ccq_hand()
     if not np.allclose(oracle.ccq_query(qh, kh, np.zeros((1, 2)), np.zeros(1), lib=lib)[0, 1, 0], [1.0, 3.0],
                        atol=1e-14):

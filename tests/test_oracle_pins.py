@@ -402,6 +402,63 @@ def test_lambda_mlp_acts_per_row():
     assert np.all(lam > 0)
 
 
+# ------------------------------------------------ backward (gradients)
+
+def _bwd_inputs(T=12, H=2, d=3, L=5, seed=0):
+    rng = np.random.default_rng(seed)
+    q, k, v, dO = (rng.standard_normal((1, T, H, d)).astype(np.float32) for _ in range(4))
+    g = (-rng.uniform(0.01, 0.3, (1, T, H))).astype(np.float32)
+    lam = rng.uniform(0.5, 1.5, (1, T, H, L)).astype(np.float32)
+    return dict(q=q, k=k, v=v, log_gate=g, lam=lam), dO
+
+
+def _loss(x, dO):
+    o = oracle.fwd_direct(x["q"], x["k"], x["v"], x["log_gate"], x["lam"])
+    return float(np.sum(o * dO.astype(np.float64)))
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "lam", "log_gate"])
+def test_bwd_matches_finite_differences(name):
+    """Every gradient coordinate against a central difference of the forward
+    oracle's loss sum(dO * o); the step actually taken in fp32 is used as the
+    denominator.  The loss is linear in each single coordinate of q, k, v and
+    lambda (so the difference is exact up to rounding) and smooth in the gates."""
+    x, dO = _bwd_inputs()
+    grads = oracle.bwd_direct(x["q"], x["k"], x["v"], x["log_gate"], x["lam"], dO)
+    g = grads["d" + name if name != "lam" else "dlambda"]
+    base = x[name]
+    h = 1e-3 if name == "log_gate" else 0.05
+    for idx in np.ndindex(base.shape):
+        xp = {kk: vv.copy() for kk, vv in x.items()}
+        xm = {kk: vv.copy() for kk, vv in x.items()}
+        xp[name][idx] = base[idx] + np.float32(h)
+        xm[name][idx] = base[idx] - np.float32(h)
+        step = float(xp[name][idx]) - float(xm[name][idx])
+        fd = (_loss(xp, dO) - _loss(xm, dO)) / step
+        assert abs(fd - g[idx]) <= 1e-6 * (1.0 + abs(fd)), (name, idx, fd, g[idx])
+
+
+def test_bwd_first_gate_has_no_gradient():
+    """a_0 multiplies no weight (every decay runs over r = s+1..t >= 1)."""
+    x, dO = _bwd_inputs(seed=2)
+    g = oracle.bwd_direct(x["q"], x["k"], x["v"], x["log_gate"], x["lam"], dO)["dlog_gate"]
+    assert np.all(np.abs(g[:, 0]) < 1e-12)
+    assert np.any(np.abs(g[:, 1:]) > 1e-3)
+
+
+def test_bwd_level_weight_gradient_is_the_bucket_read():
+    """dlambda_t^(l) = dO_t . (the read of bucket l alone), the forward with
+    lambda one-hot at level l."""
+    x, dO = _bwd_inputs(seed=3)
+    dlam = oracle.bwd_direct(x["q"], x["k"], x["v"], x["log_gate"], x["lam"], dO)["dlambda"]
+    L = x["lam"].shape[-1]
+    for lvl in range(L):
+        hot = np.zeros_like(x["lam"])
+        hot[..., lvl] = 1.0
+        o = oracle.fwd_direct(x["q"], x["k"], x["v"], x["log_gate"], hot)
+        assert np.allclose(dlam[..., lvl], np.sum(o * dO.astype(np.float64), axis=-1), rtol=1e-12, atol=1e-12)
+
+
 # --------------------------------------- curvature-conditioned query (CCQ)
 
 def _ccq_inputs(T=9, H=2, dk=4, seed=0):
