@@ -14,11 +14,14 @@ from .binding import (  # noqa: F401
     LL_MAMBA2,
     LLError,
     LLProblem,
+    attn_bwd,
     attn_fwd,
     ccq_query,
     decode_state_tensor,
     lambda_mlp,
     lib_path,
+    ll_attn_bwd,
+    ll_attn_bwd_workspace_bytes,
     ll_attn_fwd,
     ll_attn_fwd_from_state,
     ll_attn_fwd_workspace_bytes,

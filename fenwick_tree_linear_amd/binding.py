@@ -69,10 +69,12 @@ def load_library() -> ctypes.CDLL:
     lib.ll_attn_fwd_from_state.argtypes = [ctypes.POINTER(LLProblem), i64, P, P, P, P, P, P, P, P, P, P, sz, P]
     lib.ll_ccq_query_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.ll_ccq_query.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, sz, P]
+    lib.ll_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(LLProblem), ctypes.POINTER(sz)]
+    lib.ll_attn_bwd.argtypes = [ctypes.POINTER(LLProblem)] + [P] * 13 + [sz, P]
     lib.ll_decode_step_ragged.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
     for fn in ("ll_attn_fwd_workspace_bytes", "ll_attn_fwd", "ll_decode_state_bytes", "ll_decode_step",
                "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp", "ll_decode_step_ragged", "ll_attn_fwd_from_state",
-               "ll_ccq_query_workspace_bytes", "ll_ccq_query"):
+               "ll_ccq_query_workspace_bytes", "ll_ccq_query", "ll_attn_bwd_workspace_bytes", "ll_attn_bwd"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -159,6 +161,20 @@ def ll_ccq_query_workspace_bytes(B: int, T: int, H: int, dk: int, io: int) -> in
 def ll_ccq_query(B, T, H, dk, io, q, k, w, b, q_clean, workspace, workspace_bytes: int, stream=None) -> None:
     _check(load_library().ll_ccq_query(B, T, H, dk, io, _ptr(q), _ptr(k), _ptr(w), _ptr(b), _ptr(q_clean),
                                        _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def ll_attn_bwd_workspace_bytes(problem: LLProblem) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().ll_attn_bwd_workspace_bytes(ctypes.byref(problem), ctypes.byref(out)))
+    return out.value
+
+
+def ll_attn_bwd(problem: LLProblem, q, k, v, log_gate, lam, o, dO, dq, dk, dv, dlog_gate, dlam, workspace,
+                workspace_bytes: int, stream=None) -> None:
+    _check(load_library().ll_attn_bwd(None if problem is None else ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(log_gate), _ptr(lam), _ptr(o), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
+                                      _ptr(dlog_gate), _ptr(dlam), _ptr(workspace), workspace_bytes,
+                                      _stream(stream)))
 
 
 def ll_kernel_timing_enable(on: bool) -> None:
@@ -251,3 +267,20 @@ def ccq_query(q, k, w, b, out=None, workspace=None, stream=None):
     qc = out if out is not None else torch.empty_like(q)
     ll_ccq_query(B, T, H, dk, io, q, k, w, b, qc, workspace, workspace.numel(), stream)
     return qc
+
+
+def attn_bwd(q, k, v, log_gate, lam, o, dO, C: int = 64, L: int | None = None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv, dlog_gate, dlambda) of the Mamba-2 prefill for
+    the output gradient dO; allocates outputs and workspace with torch."""
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    L = L if L is not None else lam.shape[-1]
+    prob = LLProblem(B, T, H, dk, dv, L, C, io_code(k.dtype), LL_MAMBA2)
+    nbytes = ll_attn_bwd_workspace_bytes(prob)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
+    dq, dkk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty_like(log_gate)
+    dl = torch.empty_like(lam)
+    ll_attn_bwd(prob, q, k, v, log_gate, lam, o, dO, dq, dkk, dvv, dg, dl, workspace, workspace.numel(), stream)
+    return dict(dq=dq, dk=dkk, dv=dvv, dlog_gate=dg, dlambda=dl)

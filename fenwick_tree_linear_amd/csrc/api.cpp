@@ -148,9 +148,9 @@ ll_status plan_prefill(const ll_problem* p, bool exporting, Plan* out) {
 
 // ---------------------------------------------------------- kernel timing
 enum KernelId { K_CHUNK_STATE, K_FENWICK_SCAN, K_CHUNK_ATTN, K_STATE_EXPORT, K_DECODE_STEP, K_GDN_WY, K_GDN_STATE,
-                K_LAMBDA_MLP, K_PRIOR_READ, K_CCQ, K_COUNT };
+                K_LAMBDA_MLP, K_PRIOR_READ, K_CCQ, K_BWD, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"ll_chunk_state", "ll_fenwick_scan", "ll_chunk_attn", "ll_state_export",
-                                           "ll_decode_step", "ll_gdn_wy",       "ll_gdn_state",   "ll_lambda_mlp", "ll_prior_read", "ll_ccq"};
+                                           "ll_decode_step", "ll_gdn_wy",       "ll_gdn_state",   "ll_lambda_mlp", "ll_prior_read", "ll_ccq", "ll_bwd"};
 
 struct Timing {
   std::mutex mu;
@@ -545,6 +545,147 @@ ll_status ll_ccq_query(int B, int T, int H, int dk, ll_dtype io, const void* q, 
   if (st != LL_OK) return st;
   e = timed(K_CCQ, stream,
             [&] { return llattn::launch_ccq_combine(code, dk, B, T, H, q, kkq, ksum, w, b, q_clean, stream); });
+  if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+namespace {
+
+// The backward pass: buffers of the reversed-time reads, then the prefill
+// workspace (sized for the padded length Tp, which also covers T).
+struct BwdPlan {
+  ll_problem p, pp;  // the forward problem at T and at Tp
+  int Tp, LS;
+  size_t qr_off, kr_off, vr_off, dor_off, y_off, gr_off, hot_off, adk_off, adv_off, fwd_off, fwd_bytes, bytes;
+};
+
+ll_status plan_bwd(const ll_problem* p, BwdPlan* out) {
+  Plan pl;
+  ll_status st = plan_prefill(p, false, &pl);
+  if (st != LL_OK) return st;
+  if (p->rule != LL_MAMBA2) return fail(LL_ERR_UNSUPPORTED, "the backward pass is implemented for the Mamba-2 write");
+  BwdPlan c;
+  c.p = *p;
+  int Tp = 1;
+  while (Tp < p->T) Tp <<= 1;
+  c.Tp = Tp;
+  c.pp = *p;
+  c.pp.T = Tp;
+  c.LS = pl.LS;
+  Plan plp;
+  st = plan_prefill(&c.pp, false, &plp);
+  if (st != LL_OK) return st;
+  const size_t esz = p->io == LL_BF16 ? 2 : 4;
+  const size_t rowsP = (size_t)p->B * Tp * p->H, rows = (size_t)p->B * p->T * p->H;
+  const size_t d = (size_t)p->dk;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  c.qr_off = take(rowsP * d * esz);
+  c.kr_off = take(rowsP * d * esz);
+  c.vr_off = take(rowsP * d * esz);
+  c.dor_off = take(rowsP * d * esz);
+  c.y_off = take(rowsP * d * esz);
+  c.gr_off = take(rowsP * 4);
+  c.hot_off = take(rowsP * p->L * 4);
+  c.adk_off = take(rows * d * 4);
+  c.adv_off = take(rows * d * 4);
+  c.fwd_off = off;
+  c.fwd_bytes = plp.bytes > pl.bytes ? plp.bytes : pl.bytes;
+  c.bytes = off + c.fwd_bytes;
+  *out = c;
+  return LL_OK;
+}
+
+}  // namespace
+
+ll_status ll_attn_bwd_workspace_bytes(const ll_problem* p, size_t* bytes) {
+  if (!bytes) return fail(LL_ERR_NULL, "bytes is NULL");
+  BwdPlan c;
+  ll_status st = plan_bwd(p, &c);
+  if (st != LL_OK) return st;
+  *bytes = c.bytes;
+  return ok();
+}
+
+ll_status ll_attn_bwd(const ll_problem* p, const void* q, const void* k, const void* v, const float* log_gate,
+                      const float* lambda, const void* o, const void* dO, void* dq, void* dk, void* dv,
+                      float* dlog_gate, float* dlambda, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  BwdPlan c;
+  ll_status st = plan_bwd(p, &c);
+  if (st != LL_OK) return st;
+  if (!q || !k || !v || !log_gate || !lambda || !o || !dO)
+    return fail(LL_ERR_NULL, "q, k, v, log_gate, lambda, o and dO must not be NULL");
+  if (!dq || !dk || !dv || !dlog_gate || !dlambda)
+    return fail(LL_ERR_NULL, "dq, dk, dv, dlog_gate and dlambda must not be NULL");
+  if (workspace_bytes < c.bytes)
+    return fail(LL_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, c.bytes);
+  if (!workspace) return fail(LL_ERR_WORKSPACE, "workspace is NULL");
+  char* ws = static_cast<char*>(workspace);
+  void* qr = ws + c.qr_off;
+  void* kr = ws + c.kr_off;
+  void* vr = ws + c.vr_off;
+  void* dOr = ws + c.dor_off;
+  void* Y = ws + c.y_off;
+  float* gr = reinterpret_cast<float*>(ws + c.gr_off);
+  float* hot = reinterpret_cast<float*>(ws + c.hot_off);
+  float* adk = reinterpret_cast<float*>(ws + c.adk_off);
+  float* adv = reinterpret_cast<float*>(ws + c.adv_off);
+  void* fws = ws + c.fwd_off;
+  llattn::BwdArgs a;
+  a.B = p->B;
+  a.T = p->T;
+  a.Tp = c.Tp;
+  a.H = p->H;
+  a.D = p->dk;
+  a.L = p->L;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = log_gate;
+  a.lam = lambda;
+  a.o = o;
+  a.dO = dO;
+  a.dk = dk;
+  a.dv = dv;
+  a.dlog_gate = dlog_gate;
+  a.dlambda = dlambda;
+  const int io = p->io == LL_BF16 ? 1 : 0;
+  const int64_t rowsP = (int64_t)p->B * c.Tp * p->H;
+  hipError_t e = hipSuccess;
+  auto step = [&](auto fn) {
+    if (e == hipSuccess) e = timed(K_BWD, stream, fn);
+  };
+  // dq: the forward with (q, k, v) := (dO, v, k)
+  st = run_prefill(p, 0, nullptr, dO, v, k, log_gate, lambda, nullptr, dq, nullptr, fws, c.fwd_bytes, stream);
+  if (st != LL_OK) return st;
+  step([&] { return llattn::launch_bwd_reverse(io, a, qr, kr, vr, gr, stream); });
+  for (int lvl = 0; lvl < c.LS && e == hipSuccess; ++lvl) {
+    step([&] { return llattn::launch_bwd_onehot(rowsP, p->L, lvl, hot, stream); });
+    if (e != hipSuccess) break;
+    // dlambda at this level: dO . (the level's read alone)
+    st = run_prefill(p, 0, nullptr, q, k, v, log_gate, hot, nullptr, Y, nullptr, fws, c.fwd_bytes, stream);
+    if (st != LL_OK) return st;
+    step([&] { return llattn::launch_bwd_rowdot(io, a, Y, lvl, stream); });
+    // dv and dk: reads in reversed time with lambda^(l) dO as the later token's side
+    step([&] { return llattn::launch_bwd_scale_rev(io, a, lvl, dOr, stream); });
+    if (e != hipSuccess) break;
+    st = run_prefill(&c.pp, 0, nullptr, kr, qr, dOr, gr, hot, nullptr, Y, nullptr, fws, c.fwd_bytes, stream);
+    if (st != LL_OK) return st;
+    step([&] { return llattn::launch_bwd_accum_rev(io, a, Y, adv, lvl == 0, stream); });
+    if (e != hipSuccess) break;
+    st = run_prefill(&c.pp, 0, nullptr, vr, dOr, qr, gr, hot, nullptr, Y, nullptr, fws, c.fwd_bytes, stream);
+    if (st != LL_OK) return st;
+    step([&] { return llattn::launch_bwd_accum_rev(io, a, Y, adk, lvl == 0, stream); });
+  }
+  // levels no position reaches carry no gradient
+  for (int lvl = c.LS; lvl < p->L; ++lvl) step([&] { return llattn::launch_bwd_rowdot(io, a, nullptr, lvl, stream); });
+  step([&] { return llattn::launch_bwd_cast(io, a, adk, adv, stream); });
+  step([&] { return llattn::launch_bwd_gate(io, a, adk, stream); });
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

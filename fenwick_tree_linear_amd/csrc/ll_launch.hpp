@@ -70,12 +70,35 @@ struct GdnArgs {
   int64_t pos0;
 };
 
+// The elementwise parts of the backward pass (Tp: T rounded up to a power of two).
+struct BwdArgs {
+  int B, T, Tp, H, D, L;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* lam;
+  const void* o;
+  const void* dO;
+  void* dk;
+  void* dv;
+  float* dlog_gate;
+  float* dlambda;
+};
+
 // io: 0 = fp32, 1 = bf16.  Each returns hipSuccess or the launch error.
 hipError_t launch_block_state(int io, int D, int C, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_chunk_attn(int io, int D, int C, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_fenwick_scan(int D, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_state_export(int D, int C, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prior_read(int io, int D, int C, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_bwd_reverse(int io, const BwdArgs& a, void* qr, void* kr, void* vr, float* gr, hipStream_t s);
+hipError_t launch_bwd_scale_rev(int io, const BwdArgs& a, int lvl, void* dOr, hipStream_t s);
+hipError_t launch_bwd_onehot(int64_t rows, int L, int lvl, float* w, hipStream_t s);
+hipError_t launch_bwd_accum_rev(int io, const BwdArgs& a, const void* Y, float* acc, int first, hipStream_t s);
+hipError_t launch_bwd_rowdot(int io, const BwdArgs& a, const void* Y, int lvl, hipStream_t s);
+hipError_t launch_bwd_cast(int io, const BwdArgs& a, const float* acc_dk, const float* acc_dv, hipStream_t s);
+hipError_t launch_bwd_gate(int io, const BwdArgs& a, const float* acc_dk, hipStream_t s);
 hipError_t launch_ccq_fill(int io, int64_t rows, int L, int D, float* ones, float* zeros, void* e0, hipStream_t s);
 hipError_t launch_ccq_combine(int io, int D, int B, int T, int H, const void* q, const void* kkq, const void* ksum,
                               const float* w, const float* b, void* qc, hipStream_t s);

@@ -231,6 +231,28 @@ ll_status ll_ccq_query(int B, int T, int H, int dk, ll_dtype io, const void* q, 
                        const float* b, void* q_clean, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/*
+ * Backward pass of the prefill for the LL_MAMBA2 write (training): given the
+ * forward's inputs, its output o and the gradient dO of a loss at o, writes
+ * the gradients of that loss with respect to every input:
+ *   dq, dk [B,T,H,dk], dv [B,T,H,dv]   io dtype
+ *   dlog_gate [B,T,H], dlambda [B,T,H,L]   fp32
+ * The gradients of the masked form (section 2.3) are evaluated with the
+ * chunk-parallel forward itself: dq is the forward with (q, k, v) :=
+ * (dO, v, k); dlambda at level l is dO . (the level-l read); dk and dv are the
+ * reads of reversed time, one level at a time with the level weight folded
+ * into dO (3 x levels + 1 forward passes, so about that many times the
+ * forward's cost); dlog_gate_r = sum_{t >= r} (dO_t . o_t - k_t . dk_t).
+ * Shapes as ll_attn_fwd (LL_ERR_UNSUPPORTED for LL_GATED_DELTANET); the
+ * workspace holds reversed copies of q, k, v and dO padded to a power of
+ * two, fp32 accumulators of dk and dv and the forward's workspace.
+ */
+ll_status ll_attn_bwd_workspace_bytes(const ll_problem* p, size_t* bytes);
+ll_status ll_attn_bwd(const ll_problem* p, const void* q, const void* k, const void* v, const float* log_gate,
+                      const float* lambda, const void* o, const void* dO, void* dq, void* dk, void* dv,
+                      float* dlog_gate, float* dlambda, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
 /* Text of the last error on the calling thread; valid until its next call. */
 const char* ll_last_error(void);
 
@@ -241,7 +263,7 @@ const char* ll_last_error(void);
  * recorded events, then reports for up to `capacity` kernels their name (a
  * static string: "ll_chunk_state", "ll_fenwick_scan", "ll_chunk_attn",
  * "ll_state_export", "ll_decode_step", "ll_gdn_wy", "ll_gdn_state",
- * "ll_lambda_mlp", "ll_prior_read", "ll_ccq"), the summed milliseconds and the launch
+ * "ll_lambda_mlp", "ll_prior_read", "ll_ccq", "ll_bwd"), the summed milliseconds and the launch
  * count, and clears the record.  Enabling creates HIP events lazily; timing
  * adds two event records per launch, so do not time throughput with it on.
  */

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["ll_attn_fwd", "ll_attn_fwd_from_state", "ll_attn_fwd_workspace_bytes", "ll_ccq_query",
+        ["ll_attn_bwd", "ll_attn_bwd_workspace_bytes", "ll_attn_fwd", "ll_attn_fwd_from_state", "ll_attn_fwd_workspace_bytes", "ll_ccq_query",
          "ll_ccq_query_workspace_bytes", "ll_decode_state_bytes", "ll_decode_step", "ll_decode_step_ragged",
          "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp", "ll_last_error"])
 
@@ -241,3 +241,22 @@ def test_ccq_validation_before_any_launch():
     assert call(qc=None) == "LL_ERR_NULL"
     assert call(wsb=n - 1) == "LL_ERR_WORKSPACE"
     assert call(ws=None) == "LL_ERR_WORKSPACE"
+
+
+def test_bwd_validation_before_any_launch():
+    D = DUMMY
+    n = F.ll_attn_bwd_workspace_bytes(prob(T=2048, L=12))
+    assert n >= 2 * 2048 * 16 * 64 * (5 * 2 + 2 * 4)  # reversed rows, accumulators
+    # T = 1536 pads to 2048 for the reversed reads (five padded bf16 row buffers)
+    assert F.ll_attn_bwd_workspace_bytes(prob(T=1536, L=12)) >= 5 * 2 * 2048 * 16 * 64 * 2
+
+    def call(p, q=D, o=D, dO=D, dq=D, dlam=D, ws=D, wsb=n):
+        return status_of(F.ll_attn_bwd, p, q, D, D, D, D, o, dO, dq, D, D, D, dlam, ws, wsb, 0)[0]
+
+    assert call(prob(T=2048, L=12, rule=F.LL_GATED_DELTANET)) == "LL_ERR_UNSUPPORTED"
+    assert call(prob(T=2048, L=11)) == "LL_ERR_SHAPE"
+    assert call(prob(T=2048, L=12, C=48)) == "LL_ERR_SHAPE"
+    assert call(prob(T=2048, L=12), o=None) == "LL_ERR_NULL"
+    assert call(prob(T=2048, L=12), dlam=None) == "LL_ERR_NULL"
+    assert call(prob(T=2048, L=12), wsb=n - 1) == "LL_ERR_WORKSPACE"
+    assert call(prob(T=2048, L=12), ws=None) == "LL_ERR_WORKSPACE"
