@@ -343,6 +343,62 @@ def ccq_bench(reps: int) -> dict:
                                  "tokens_per_s": round(w.B * w.T / (step_ms * 1e-3), 1)}}
 
 
+def bwd_bench(reps: int) -> dict:
+    """ll_attn_bwd on the 2K prefill's shape (B4 H16 T2048 d64 bf16, 12 levels, chunk 64): time per
+    backward call (HIP events on the launch stream) and per-kernel averages, beside the forward's."""
+    import torch
+
+    import fenwick_tree_linear_amd as F
+    from fenwick_tree_linear_amd import workloads as W
+
+    w = W.WORKLOADS["prefill-2k"]
+    dev = torch.device("cuda:0")
+    x = W.prefill_inputs(w, device=dev)
+    dO = torch.randn(w.B, w.T, w.H, w.dv, device=dev, generator=torch.Generator(device=dev).manual_seed(7)).to(
+        torch.bfloat16)
+    stream = torch.cuda.current_stream(dev)
+    prob = F.LLProblem(w.B, w.T, w.H, w.dk, w.dv, w.L, w.C, F.LL_BF16, F.LL_MAMBA2)
+    fws_bytes = F.ll_attn_fwd_workspace_bytes(prob)
+    fws = torch.empty(fws_bytes, dtype=torch.uint8, device=dev)
+    o = torch.empty(w.B, w.T, w.H, w.dv, dtype=torch.bfloat16, device=dev)
+    bws_bytes = F.ll_attn_bwd_workspace_bytes(prob)
+    bws = torch.empty(bws_bytes, dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
+    dg, dl = torch.empty_like(x["log_gate"]), torch.empty_like(x["lam"])
+
+    def fwd():
+        F.ll_attn_fwd(prob, x["q"], x["k"], x["v"], x["log_gate"], x["lam"], None, o, None, fws, fws_bytes, stream)
+
+    def bwd():
+        F.ll_attn_bwd(prob, x["q"], x["k"], x["v"], x["log_gate"], x["lam"], o, dO, dq, dk, dv, dg, dl, bws,
+                      bws_bytes, stream)
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    f_ms = timed(fwd, reps)
+    b_ms = timed(bwd, reps)
+    F.ll_kernel_timing_read()
+    F.ll_kernel_timing_enable(True)
+    bwd()
+    torch.cuda.synchronize()
+    kt = F.ll_kernel_timing_read()
+    F.ll_kernel_timing_enable(False)
+    return {"workload": "ll_attn_bwd B4 H16 T2048 d64 bf16, 12 levels, chunk 64 (Mamba-2)",
+            "fwd_ms": round(f_ms, 5), "bwd_ms": round(b_ms, 5), "bwd_over_fwd": round(b_ms / f_ms, 1),
+            "tokens_per_s": round(w.B * w.T / (b_ms * 1e-3), 1),
+            "kernels_in_one_call": {k: {"ms": round(t, 4), "launches": n} for k, (t, n) in kt.items()}}
+
+
 MFMA_FP32_PEAK_TFLOPS = 157.3  # dense fp32 matrix cores
 
 
@@ -458,6 +514,8 @@ def main() -> int:
                     help="also time this many ll_decode_step_ragged steps with per-sequence positions (0: skip)")
     ap.add_argument("--from-state-reps", type=int, default=20,
                     help="also time this many prefills of the 16K workload's second half from a state (0: skip)")
+    ap.add_argument("--bwd-reps", type=int, default=5,
+                    help="also time this many backward passes on the 2K prefill's shape (0: skip)")
     ap.add_argument("--ccq-reps", type=int, default=10,
                     help="also time this many curvature-conditioned query calls on the 16K workload (0: skip)")
     ap.add_argument("--mlp-reps", type=int, default=50,
@@ -594,6 +652,9 @@ def main() -> int:
     if args.from_state_reps:
         result["from_state"] = from_state_bench(args.from_state_reps)
         log(f"[bench] prefill from a state: {result['from_state']}")
+    if args.bwd_reps:
+        result["backward"] = bwd_bench(args.bwd_reps)
+        log(f"[bench] backward: {result['backward']}")
     if args.ccq_reps:
         result["ccq"] = ccq_bench(args.ccq_reps)
         log(f"[bench] curvature-conditioned query: {result['ccq']}")

@@ -685,7 +685,7 @@ ll_status ll_attn_bwd(const ll_problem* p, const void* q, const void* k, const v
   // levels no position reaches carry no gradient
   for (int lvl = c.LS; lvl < p->L; ++lvl) step([&] { return llattn::launch_bwd_rowdot(io, a, nullptr, lvl, stream); });
   step([&] { return llattn::launch_bwd_cast(io, a, adk, adv, stream); });
-  step([&] { return llattn::launch_bwd_gate(io, a, adk, stream); });
+  step([&] { return llattn::launch_bwd_gate(io, a, adk, gr, stream); });  // gr is free again: dG per row
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -13,6 +13,8 @@
 //   dlog_gate_r   = sum_{t >= r} (dO_t . o_t - k_t . dk_t).
 // The kernels here do the reversal, the weighting, the accumulation and the
 // gate gradient; all are elementwise or per-row.
+#include <type_traits>
+
 #include "ll_device.hpp"
 #include "ll_launch.hpp"
 
@@ -25,25 +27,37 @@ static int grid_for(int64_t n) {
 #define LL_GRID_STRIDE(i, n) \
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (n); i += (int64_t)gridDim.x * blockDim.x)
 
+// Elementwise kernels take four consecutive values of a row per thread; the
+// row index splits into (b, position, h) once per thread.
+template <typename T>
+using Vec4Of = typename std::conditional<sizeof(T) == 2, bf16x4, f32x4>::type;
+
 // qr, kr, vr [B,Tp,H,D] = rows of q, k, v at t = Tp-1-t' (zero past T);
-// gr [B,Tp,H] = log a at T_p - t' (the shift that makes a forward decay over
+// gr [B,Tp,H] = log a at Tp - t' (the shift that makes a forward decay over
 // t'+1..s' equal the original decay over s+1..t), zero where out of range.
 template <typename T>
 __global__ void __launch_bounds__(256) ll_bwd_reverse(BwdArgs a, T* qr, T* kr, T* vr, float* gr) {
-  const int64_t n = (int64_t)a.B * a.Tp * a.H * a.D;
+  typedef Vec4Of<T> V;
+  const int G4 = a.D / 4;
+  const int64_t n = (int64_t)a.B * a.Tp * a.H * G4;
   LL_GRID_STRIDE(i, n) {
-    const int x = (int)(i % a.D);
-    const int64_t row = i / a.D;
+    const int x4 = (int)(i % G4);
+    const int64_t row = i / G4;
     const int h = (int)(row % a.H);
-    const int tp = (int)((row / a.H) % a.Tp);
-    const int b = (int)(row / ((int64_t)a.H * a.Tp));
+    const int64_t bt = row / a.H;
+    const int tp = (int)(bt % a.Tp), b = (int)(bt / a.Tp);
     const int t = a.Tp - 1 - tp;
-    const int64_t src = (((int64_t)b * a.T + t) * a.H + h) * a.D + x;
-    const bool ok = t < a.T;
-    qr[i] = ok ? static_cast<const T*>(a.q)[src] : from_f32<T>(0.f);
-    kr[i] = ok ? static_cast<const T*>(a.k)[src] : from_f32<T>(0.f);
-    vr[i] = ok ? static_cast<const T*>(a.v)[src] : from_f32<T>(0.f);
-    if (x == 0) {
+    V zq = {}, zk = {}, zv = {};
+    if (t < a.T) {
+      const int64_t src = (((int64_t)b * a.T + t) * a.H + h) * G4 + x4;
+      zq = static_cast<const V*>(a.q)[src];
+      zk = static_cast<const V*>(a.k)[src];
+      zv = static_cast<const V*>(a.v)[src];
+    }
+    reinterpret_cast<V*>(qr)[i] = zq;
+    reinterpret_cast<V*>(kr)[i] = zk;
+    reinterpret_cast<V*>(vr)[i] = zv;
+    if (x4 == 0) {
       const int tg = a.Tp - tp;
       gr[row] = (tp >= 1 && tg < a.T) ? a.g[((int64_t)b * a.T + tg) * a.H + h] : 0.f;
     }
@@ -53,20 +67,25 @@ __global__ void __launch_bounds__(256) ll_bwd_reverse(BwdArgs a, T* qr, T* kr, T
 // dOr [B,Tp,H,D] = lambda^(l)_t dO_t at t = Tp-1-t' (zero past T)
 template <typename T>
 __global__ void __launch_bounds__(256) ll_bwd_scale_rev(BwdArgs a, int lvl, T* dOr) {
-  const int64_t n = (int64_t)a.B * a.Tp * a.H * a.D;
+  typedef Vec4Of<T> V;
+  const int G4 = a.D / 4;
+  const int64_t n = (int64_t)a.B * a.Tp * a.H * G4;
   LL_GRID_STRIDE(i, n) {
-    const int x = (int)(i % a.D);
-    const int64_t row = i / a.D;
+    const int x4 = (int)(i % G4);
+    const int64_t row = i / G4;
     const int h = (int)(row % a.H);
-    const int tp = (int)((row / a.H) % a.Tp);
-    const int b = (int)(row / ((int64_t)a.H * a.Tp));
+    const int64_t bt = row / a.H;
+    const int tp = (int)(bt % a.Tp), b = (int)(bt / a.Tp);
     const int t = a.Tp - 1 - tp;
-    float val = 0.f;
+    V out = {};
     if (t < a.T) {
       const int64_t r = ((int64_t)b * a.T + t) * a.H + h;
-      val = a.lam[r * a.L + lvl] * to_f32(static_cast<const T*>(a.dO)[r * a.D + x]);
+      const float w = a.lam[r * a.L + lvl];
+      const V d = static_cast<const V*>(a.dO)[r * G4 + x4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] = from_f32<T>(w * to_f32(d[e]));
     }
-    dOr[i] = from_f32<T>(val);
+    reinterpret_cast<V*>(dOr)[i] = out;
   }
 }
 
@@ -78,61 +97,71 @@ __global__ void __launch_bounds__(256) ll_bwd_onehot(int64_t rows, int L, int lv
 // acc [B,T,H,D] (+)= Y at t' = Tp-1-t
 template <typename T>
 __global__ void __launch_bounds__(256) ll_bwd_accum_rev(BwdArgs a, const T* Y, float* acc, int first) {
-  const int64_t n = (int64_t)a.B * a.T * a.H * a.D;
+  typedef Vec4Of<T> V;
+  const int G4 = a.D / 4;
+  const int64_t n = (int64_t)a.B * a.T * a.H * G4;
   LL_GRID_STRIDE(i, n) {
-    const int x = (int)(i % a.D);
-    const int64_t row = i / a.D;
+    const int x4 = (int)(i % G4);
+    const int64_t row = i / G4;
     const int h = (int)(row % a.H);
-    const int t = (int)((row / a.H) % a.T);
-    const int b = (int)(row / ((int64_t)a.H * a.T));
-    const float y = to_f32(Y[(((int64_t)b * a.Tp + (a.Tp - 1 - t)) * a.H + h) * a.D + x]);
-    acc[i] = first ? y : acc[i] + y;
+    const int64_t bt = row / a.H;
+    const int t = (int)(bt % a.T), b = (int)(bt / a.T);
+    const V y = reinterpret_cast<const V*>(Y)[(((int64_t)b * a.Tp + (a.Tp - 1 - t)) * a.H + h) * G4 + x4];
+    f32x4 cur = first ? f32x4{0.f, 0.f, 0.f, 0.f} : reinterpret_cast<const f32x4*>(acc)[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cur[e] += to_f32(y[e]);
+    reinterpret_cast<f32x4*>(acc)[i] = cur;
   }
 }
 
-// dlambda[row][lvl] = Y_row . dO_row (Y: [B,T,H,D]); zero when Y is NULL
+// Dot products of rows, one wave per row (lanes over the row):
+// out[row * stride + col] = sum_x X1 Y1 (- X2 Y2 when X2 is given; Y2 fp32).
 template <typename T>
-__global__ void __launch_bounds__(256) ll_bwd_rowdot(BwdArgs a, const T* Y, int lvl) {
-  const int64_t rows = (int64_t)a.B * a.T * a.H;
-  LL_GRID_STRIDE(r, rows) {
-    float s = 0.f;
-    if (Y)
-      for (int x = 0; x < a.D; ++x) s += to_f32(Y[r * a.D + x]) * to_f32(static_cast<const T*>(a.dO)[r * a.D + x]);
-    a.dlambda[r * a.L + lvl] = s;
-  }
+__global__ void __launch_bounds__(256) ll_bwd_rowdot(int64_t rows, int D, const T* X1, const T* Y1, const T* X2,
+                                                     const float* Y2, float* out, int stride, int col) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float s = 0.f;
+  if (X1)
+    for (int x = lane; x < D; x += 64) {
+      s += to_f32(X1[row * D + x]) * to_f32(Y1[row * D + x]);
+      if (X2) s -= to_f32(X2[row * D + x]) * Y2[row * D + x];
+    }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+  if (lane == 0) out[row * stride + col] = s;
 }
 
 // dk, dv in the io dtype from their fp32 accumulators
 template <typename T>
 __global__ void __launch_bounds__(256) ll_bwd_cast(BwdArgs a, const float* acc_dk, const float* acc_dv) {
-  const int64_t n = (int64_t)a.B * a.T * a.H * a.D;
+  typedef Vec4Of<T> V;
+  const int64_t n = (int64_t)a.B * a.T * a.H * a.D / 4;
   LL_GRID_STRIDE(i, n) {
-    static_cast<T*>(a.dk)[i] = from_f32<T>(acc_dk[i]);
-    static_cast<T*>(a.dv)[i] = from_f32<T>(acc_dv[i]);
+    const f32x4 x = reinterpret_cast<const f32x4*>(acc_dk)[i], y = reinterpret_cast<const f32x4*>(acc_dv)[i];
+    V ok, ov;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ok[e] = from_f32<T>(x[e]);
+      ov[e] = from_f32<T>(y[e]);
+    }
+    static_cast<V*>(a.dk)[i] = ok;
+    static_cast<V*>(a.dv)[i] = ov;
   }
 }
 
-// One workgroup per head: dG_t = dO_t . o_t - k_t . dk_t, then the suffix sum
-// dlog_gate_r = sum_{t >= r} dG_t, walking the tokens from the end in tiles of
-// 256 with the running sum carried between tiles.
-template <typename T>
-__global__ void __launch_bounds__(256) ll_bwd_gate(BwdArgs a, const float* acc_dk) {
+// One workgroup per head: dlog_gate_r = sum_{t >= r} dG_t, walking the tokens
+// from the end in tiles of 256 with the running sum carried between tiles.
+__global__ void __launch_bounds__(256) ll_bwd_suffix(BwdArgs a, const float* dG) {
   __shared__ float sbuf[256];
   const int bh = blockIdx.x, h = bh % a.H, b = bh / a.H;
   const int tid = threadIdx.x;
   float carry = 0.f;
   for (int t0 = a.T - 256; t0 > -256; t0 -= 256) {
     const int t = t0 + (255 - tid);  // thread 0 takes the latest token of the tile
-    float dg = 0.f;
-    if (t >= 0 && t < a.T) {
-      const int64_t r = ((int64_t)b * a.T + t) * a.H + h;
-      for (int x = 0; x < a.D; ++x) {
-        dg += to_f32(static_cast<const T*>(a.dO)[r * a.D + x]) * to_f32(static_cast<const T*>(a.o)[r * a.D + x]);
-        dg -= to_f32(static_cast<const T*>(a.k)[r * a.D + x]) * acc_dk[r * a.D + x];
-      }
-    }
-    // inclusive scan over threads 0..255 (tokens from latest to earliest)
-    sbuf[tid] = dg;
+    const int64_t r = ((int64_t)b * a.T + t) * a.H + h;
+    sbuf[tid] = (t >= 0) ? dG[r] : 0.f;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
       const float add = tid >= off ? sbuf[tid - off] : 0.f;
@@ -140,7 +169,7 @@ __global__ void __launch_bounds__(256) ll_bwd_gate(BwdArgs a, const float* acc_d
       sbuf[tid] += add;
       __syncthreads();
     }
-    if (t >= 0 && t < a.T) a.dlog_gate[((int64_t)b * a.T + t) * a.H + h] = carry + sbuf[tid];
+    if (t >= 0) a.dlog_gate[r] = carry + sbuf[tid];
     carry += sbuf[255];
     __syncthreads();
   }
@@ -158,14 +187,14 @@ __global__ void __launch_bounds__(256) ll_bwd_gate(BwdArgs a, const float* acc_d
   } while (0)
 
 hipError_t launch_bwd_reverse(int io, const BwdArgs& a, void* qr, void* kr, void* vr, float* gr, hipStream_t s) {
-  const int grid = grid_for((int64_t)a.B * a.Tp * a.H * a.D);
+  const int grid = grid_for((int64_t)a.B * a.Tp * a.H * a.D / 4);
   LL_BWD_IO(io, hipLaunchKernelGGL(ll_bwd_reverse<TT>, dim3(grid), dim3(256), 0, s, a, static_cast<TT*>(qr),
                                    static_cast<TT*>(kr), static_cast<TT*>(vr), gr));
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_scale_rev(int io, const BwdArgs& a, int lvl, void* dOr, hipStream_t s) {
-  const int grid = grid_for((int64_t)a.B * a.Tp * a.H * a.D);
+  const int grid = grid_for((int64_t)a.B * a.Tp * a.H * a.D / 4);
   LL_BWD_IO(io, hipLaunchKernelGGL(ll_bwd_scale_rev<TT>, dim3(grid), dim3(256), 0, s, a, lvl, static_cast<TT*>(dOr)));
   return hipGetLastError();
 }
@@ -176,26 +205,35 @@ hipError_t launch_bwd_onehot(int64_t rows, int L, int lvl, float* w, hipStream_t
 }
 
 hipError_t launch_bwd_accum_rev(int io, const BwdArgs& a, const void* Y, float* acc, int first, hipStream_t s) {
-  const int grid = grid_for((int64_t)a.B * a.T * a.H * a.D);
+  const int grid = grid_for((int64_t)a.B * a.T * a.H * a.D / 4);
   LL_BWD_IO(io, hipLaunchKernelGGL(ll_bwd_accum_rev<TT>, dim3(grid), dim3(256), 0, s, a, static_cast<const TT*>(Y),
                                    acc, first));
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_rowdot(int io, const BwdArgs& a, const void* Y, int lvl, hipStream_t s) {
-  const int grid = grid_for((int64_t)a.B * a.T * a.H);
-  LL_BWD_IO(io, hipLaunchKernelGGL(ll_bwd_rowdot<TT>, dim3(grid), dim3(256), 0, s, a, static_cast<const TT*>(Y), lvl));
+  const int64_t rows = (int64_t)a.B * a.T * a.H;
+  LL_BWD_IO(io, hipLaunchKernelGGL(ll_bwd_rowdot<TT>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, rows, a.D,
+                                   static_cast<const TT*>(Y), static_cast<const TT*>(a.dO), (const TT*)nullptr,
+                                   (const float*)nullptr, a.dlambda, a.L, lvl));
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_cast(int io, const BwdArgs& a, const float* acc_dk, const float* acc_dv, hipStream_t s) {
-  const int grid = grid_for((int64_t)a.B * a.T * a.H * a.D);
+  const int grid = grid_for((int64_t)a.B * a.T * a.H * a.D / 4);
   LL_BWD_IO(io, hipLaunchKernelGGL(ll_bwd_cast<TT>, dim3(grid), dim3(256), 0, s, a, acc_dk, acc_dv));
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_gate(int io, const BwdArgs& a, const float* acc_dk, hipStream_t s) {
-  LL_BWD_IO(io, hipLaunchKernelGGL(ll_bwd_gate<TT>, dim3(a.B * a.H), dim3(256), 0, s, a, acc_dk));
+hipError_t launch_bwd_gate(int io, const BwdArgs& a, const float* acc_dk, float* dG, hipStream_t s) {
+  // dG_t = dO_t . o_t - k_t . dk_t per row, then the suffix sums per head
+  const int64_t rows = (int64_t)a.B * a.T * a.H;
+  LL_BWD_IO(io, hipLaunchKernelGGL(ll_bwd_rowdot<TT>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, rows, a.D,
+                                   static_cast<const TT*>(a.dO), static_cast<const TT*>(a.o),
+                                   static_cast<const TT*>(a.k), acc_dk, dG, 1, 0));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ll_bwd_suffix, dim3(a.B * a.H), dim3(256), 0, s, a, dG);
   return hipGetLastError();
 }
 

@@ -98,7 +98,7 @@ hipError_t launch_bwd_onehot(int64_t rows, int L, int lvl, float* w, hipStream_t
 hipError_t launch_bwd_accum_rev(int io, const BwdArgs& a, const void* Y, float* acc, int first, hipStream_t s);
 hipError_t launch_bwd_rowdot(int io, const BwdArgs& a, const void* Y, int lvl, hipStream_t s);
 hipError_t launch_bwd_cast(int io, const BwdArgs& a, const float* acc_dk, const float* acc_dv, hipStream_t s);
-hipError_t launch_bwd_gate(int io, const BwdArgs& a, const float* acc_dk, hipStream_t s);
+hipError_t launch_bwd_gate(int io, const BwdArgs& a, const float* acc_dk, float* dG, hipStream_t s);
 hipError_t launch_ccq_fill(int io, int64_t rows, int L, int D, float* ones, float* zeros, void* e0, hipStream_t s);
 hipError_t launch_ccq_combine(int io, int D, int B, int T, int H, const void* q, const void* kkq, const void* ksum,
                               const float* w, const float* b, void* qc, hipStream_t s);
