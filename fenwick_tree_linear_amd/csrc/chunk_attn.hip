@@ -22,6 +22,7 @@
 // over tokens (V, and K for the state) are read with the transposing LDS
 // read, and the per-token decay of the state update is applied to the V
 // fragments in registers, so no transposed or rescaled tile is ever written.
+#include <mutex>
 #include <type_traits>
 
 #include "ll_device.hpp"
@@ -681,29 +682,38 @@ static hipError_t launch_attn_t(const PrefillArgs& a, hipStream_t s) {
     constexpr int MAXH = (sizeof(T) == 2 && D <= 64) ? 5 : 0;
     auto kern = ll_chunk_attn<T, D, C, max_block_depth(D), MAXH>;
     const AttnLayout<T, D, C> lay(a.LS);
-    static int configured = 0;  // dynamic LDS above 64 KiB must be allowed per kernel
-    if (lay.total > configured) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, lay.total);
-      if (e != hipSuccess) return e;
-      configured = lay.total;
-    }
-    // persistent: as many workgroups as fit on the device at once, each
-    // walking a run of consecutive (block, head) items
-    static int slots = 0, slots_lds = -1;
-    if (slots_lds != lay.total) {
-      int dev = 0, cus = 0, per_cu = 0;
-      hipError_t e = hipGetDevice(&dev);
-      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-      if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
-                                                         64 * AttnWaves<D, C>::NW, lay.total);
-      if (e != hipSuccess) return e;
-      slots = cus * (per_cu > 0 ? per_cu : 1);
-      slots_lds = lay.total;
+    // Per kernel instance: the dynamic LDS allowed (above 64 KiB it must be
+    // raised explicitly) and the number of workgroups that fit the device at
+    // once for that LDS size, kept under a lock (calls may come from several
+    // threads).
+    static std::mutex mu;
+    static int configured = 0, slots = 0, slots_lds = -1;
+    int grid_slots = 0;
+    {
+      std::lock_guard<std::mutex> lock(mu);
+      if (lay.total > configured) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lay.total);
+        if (e != hipSuccess) return e;
+        configured = lay.total;
+      }
+      // persistent: as many workgroups as fit on the device at once, each
+      // walking a run of consecutive (block, head) items
+      if (slots_lds != lay.total) {
+        int dev = 0, cus = 0, per_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess)
+          e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
+                                                           64 * AttnWaves<D, C>::NW, lay.total);
+        if (e != hipSuccess) return e;
+        slots = cus * (per_cu > 0 ? per_cu : 1);
+        slots_lds = lay.total;
+      }
+      grid_slots = slots;
     }
     const int items = a.B * a.H * a.nb;
-    const int grid = items < slots ? items : slots;
+    const int grid = items < grid_slots ? items : grid_slots;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * AttnWaves<D, C>::NW), lay.total, s, a);
     return hipGetLastError();
   }
