@@ -574,7 +574,7 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start_ev.elapsed_time(stop_ev) / args.steps
-    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (events), wall {wall * 1e3 / args.steps:.1f} us")
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (events), wall {wall * 1e6 / args.steps:.1f} us/step")
 
     # cold: the 256 MB last-level cache flushed by writing a 512 MiB buffer
     # before each of a few individually timed steps (median reported)
