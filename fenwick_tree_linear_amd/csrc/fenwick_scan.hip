@@ -253,7 +253,9 @@ __global__ void __launch_bounds__(256) ll_sigma_zero(float* sigma, int64_t n) {
 }
 
 // Segments per head: enough threads to keep every CU loading (up to 2^17),
-// each segment at least 8 blocks; the batch is at most the segment.
+// each segment at least 8 blocks.  With segments the batch is 8 blocks (a
+// segment takes several): the larger batches of the one-segment walk do not
+// fit in registers next to the segment bookkeeping and spill.
 template <int D>
 hipError_t launch_scan_d(const PrefillArgs& a, hipStream_t s) {
   constexpr int G = D * D / 4;
@@ -262,19 +264,14 @@ hipError_t launch_scan_d(const PrefillArgs& a, hipStream_t s) {
   while (ns < 4 && pieces * ns < ((int64_t)1 << 17) && (a.nb + 2 * ns - 1) / (2 * ns) >= 8) ns *= 2;
   int seg_log = 0;
   while ((int64_t)ns << seg_log < a.nb) ++seg_log;
-  const int batch = ns == 1 ? 32 : (seg_log >= 5 ? 32 : (seg_log >= 4 ? 16 : 8));
   const int grid = (int)((pieces + kScanThreads / ns - 1) / (kScanThreads / ns));
   const dim3 g(grid), b(kScanThreads);
   if (ns == 1) {
     hipLaunchKernelGGL((ll_fenwick_scan<D, 1, 32>), g, b, 0, s, a, 30);
   } else if (ns == 2) {
-    if (batch == 32) hipLaunchKernelGGL((ll_fenwick_scan<D, 2, 32>), g, b, 0, s, a, seg_log);
-    else if (batch == 16) hipLaunchKernelGGL((ll_fenwick_scan<D, 2, 16>), g, b, 0, s, a, seg_log);
-    else hipLaunchKernelGGL((ll_fenwick_scan<D, 2, 8>), g, b, 0, s, a, seg_log);
+    hipLaunchKernelGGL((ll_fenwick_scan<D, 2, 8>), g, b, 0, s, a, seg_log);
   } else {
-    if (batch == 32) hipLaunchKernelGGL((ll_fenwick_scan<D, 4, 32>), g, b, 0, s, a, seg_log);
-    else if (batch == 16) hipLaunchKernelGGL((ll_fenwick_scan<D, 4, 16>), g, b, 0, s, a, seg_log);
-    else hipLaunchKernelGGL((ll_fenwick_scan<D, 4, 8>), g, b, 0, s, a, seg_log);
+    hipLaunchKernelGGL((ll_fenwick_scan<D, 4, 8>), g, b, 0, s, a, seg_log);
   }
   return hipGetLastError();
 }
