@@ -55,7 +55,7 @@ bool supported_chunk(int c, ll_dtype io) {
   return c == 16 || c == 32 || c == 64;
 }
 
-constexpr int kMaxBlockChunks = 8;  // P <= 2^max_block_depth for d <= 64
+constexpr int kMaxBlockChunks = 8;  // P <= 2^max_block_depth
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 

@@ -678,9 +678,10 @@ static hipError_t launch_attn_t(const PrefillArgs& a, hipStream_t s) {
   if constexpr (C * D * (int)sizeof(T) > kAttnTileBytesMax) {
     return hipErrorInvalidValue;  // rejected by the shape checks before launch
   } else {
-    // Fenwick nodes of earlier blocks held in registers (5 cover up to 32 blocks per head; at
-    // d = 128 one, the most recent: more spill)
-    constexpr int MAXH = (sizeof(T) == 2) ? (D <= 64 ? 5 : 1) : 0;
+    // Fenwick nodes of earlier blocks held in registers (5 cover up to 32 blocks per head).  At
+    // d = 128 the within-block nodes of 8-chunk blocks already fill the register budget, so
+    // every earlier block's node is read from LDS (holding even one spills).
+    constexpr int MAXH = (sizeof(T) == 2) ? (D <= 64 ? 5 : 0) : 0;
     auto kern = ll_chunk_attn<T, D, C, max_block_depth(D), MAXH>;
     const AttnLayout<T, D, C> lay(a.LS);
     // Per kernel instance: the dynamic LDS allowed (above 64 KiB it must be

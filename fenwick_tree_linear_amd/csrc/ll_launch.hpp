@@ -118,7 +118,7 @@ inline int ilog2_host(int x) {
 }
 
 // largest within-block Fenwick depth the chunk kernels hold in registers
-constexpr int max_block_depth(int D) { return D >= 128 ? 2 : 3; }
+constexpr int max_block_depth(int /*D*/) { return 3; }
 
 // Whether the read takes the block-level Fenwick nodes from bf16 copies in
 // fragment order (PrefillArgs::N16): for bf16 io at head sizes where no node

@@ -56,9 +56,9 @@ def test_workspace_bytes_for_the_16k_prefill():
     assert 1536 * 64 * 64 * 4 <= n <= 1536 * 64 * 64 * 4 + 4 * 4096 + 4 * 256
     assert n % 256 == 0
     # at d = 128 (bf16) the read takes the nodes from a bf16 copy of all of them:
-    # 32 heads x 64 blocks of 4 chunks of 32 -> 2048 states, 1024 nodes, 2048 copies
+    # 32 heads x 32 blocks of 8 chunks of 32 -> 1024 states, 512 nodes, 1024 copies
     m = F.ll_attn_fwd_workspace_bytes(prob(T=8192, L=14, dk=128, dv=128, C=32))
-    base = 3072 * 128 * 128 * 4 + 2048 * 128 * 128 * 2
+    base = 1536 * 128 * 128 * 4 + 1024 * 128 * 128 * 2
     assert base <= m <= base + 4 * 4096 + 5 * 256
 
 
