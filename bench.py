@@ -336,8 +336,8 @@ def ccq_bench(reps: int) -> dict:
     kt = F.ll_kernel_timing_read()
     F.ll_kernel_timing_enable(False)
     step_ms = timed(step, reps)
-    return {"workload": "ll_ccq_query B2 H16 T16384 d64 bf16 (running key covariance from two all-ones, "
-                        "no-decay prefills)",
+    return {"workload": "ll_ccq_query B2 H16 T16384 d64 bf16 (running second moment from an all-ones, "
+                        "no-decay prefill; running key sum from a chunked fp32 prefix sum)",
             "ms_per_call": round(ms, 5), "kernels_us": {k: round(t / n * 1e3, 2) for k, (t, n) in kt.items()},
             "prefill_with_ccq": {"ms_per_step": round(step_ms, 5),
                                  "tokens_per_s": round(w.B * w.T / (step_ms * 1e-3), 1)}}

@@ -460,7 +460,7 @@ namespace {
 // workspace.
 struct CcqPlan {
   ll_problem p;
-  size_t ones_off, zeros_off, e0_off, kkq_off, ksum_off, fwd_off, fwd_bytes, bytes;
+  size_t ones_off, zeros_off, kkq_off, csum_off, fwd_off, fwd_bytes, bytes;
 };
 
 ll_status plan_ccq(int B, int T, int H, int dk, ll_dtype io, CcqPlan* out) {
@@ -493,12 +493,10 @@ ll_status plan_ccq(int B, int T, int H, int dk, ll_dtype io, CcqPlan* out) {
   off = align256(off + rows * c.p.L * 4);
   c.zeros_off = off;
   off = align256(off + rows * 4);
-  c.e0_off = off;
-  off = align256(off + rows * dk * esz);
   c.kkq_off = off;
   off = align256(off + rows * dk * esz);
-  c.ksum_off = off;
-  off = align256(off + rows * dk * esz);
+  c.csum_off = off;  // per-chunk key sums, [B,H,T/C,dk] fp32
+  off = align256(off + (size_t)B * H * (T / C) * dk * 4);
   c.fwd_off = off;
   c.fwd_bytes = pl.bytes;
   c.bytes = off + pl.bytes;
@@ -529,22 +527,20 @@ ll_status ll_ccq_query(int B, int T, int H, int dk, ll_dtype io, const void* q, 
   char* ws = static_cast<char*>(workspace);
   float* ones = reinterpret_cast<float*>(ws + c.ones_off);
   float* zeros = reinterpret_cast<float*>(ws + c.zeros_off);
-  void* e0 = ws + c.e0_off;
   void* kkq = ws + c.kkq_off;
-  void* ksum = ws + c.ksum_off;
+  float* csum = reinterpret_cast<float*>(ws + c.csum_off);
   const int code = io == LL_BF16 ? 1 : 0;
-  hipError_t e = timed(K_CCQ, stream, [&] {
-    return llattn::launch_ccq_fill(code, (int64_t)B * T * H, c.p.L, dk, ones, zeros, e0, stream);
-  });
+  hipError_t e = timed(K_CCQ, stream, [&] { return llattn::launch_ccq_fill((int64_t)B * T * H, c.p.L, ones, zeros, stream); });
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  // sum_{j<=t} (k_j . q_t) k_j and sum_{j<=t} k_j
+  // sum_{j<=t} (k_j . q_t) k_j
   st = run_prefill(&c.p, 0, nullptr, q, k, k, zeros, ones, nullptr, kkq, nullptr, ws + c.fwd_off, c.fwd_bytes, stream);
   if (st != LL_OK) return st;
-  st = run_prefill(&c.p, 0, nullptr, e0, e0, k, zeros, ones, nullptr, ksum, nullptr, ws + c.fwd_off, c.fwd_bytes,
-                   stream);
-  if (st != LL_OK) return st;
-  e = timed(K_CCQ, stream,
-            [&] { return llattn::launch_ccq_combine(code, dk, B, T, H, q, kkq, ksum, w, b, q_clean, stream); });
+  // sum_{j<=t} k_j: chunk sums and their prefix over the chunks, the rest in the combine
+  e = timed(K_CCQ, stream, [&] { return llattn::launch_ccq_ksum(code, dk, B, T, H, c.p.C, k, csum, stream); });
+  if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  e = timed(K_CCQ, stream, [&] {
+    return llattn::launch_ccq_combine(code, dk, B, T, H, c.p.C, q, k, kkq, csum, w, b, q_clean, stream);
+  });
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -99,9 +99,11 @@ hipError_t launch_bwd_accum_rev(int io, const BwdArgs& a, const void* Y, float* 
 hipError_t launch_bwd_rowdot(int io, const BwdArgs& a, const void* Y, int lvl, hipStream_t s);
 hipError_t launch_bwd_cast(int io, const BwdArgs& a, const float* acc_dk, const float* acc_dv, hipStream_t s);
 hipError_t launch_bwd_gate(int io, const BwdArgs& a, const float* acc_dk, float* dG, hipStream_t s);
-hipError_t launch_ccq_fill(int io, int64_t rows, int L, int D, float* ones, float* zeros, void* e0, hipStream_t s);
-hipError_t launch_ccq_combine(int io, int D, int B, int T, int H, const void* q, const void* kkq, const void* ksum,
-                              const float* w, const float* b, void* qc, hipStream_t s);
+hipError_t launch_ccq_fill(int64_t rows, int L, float* ones, float* zeros, hipStream_t s);
+hipError_t launch_ccq_ksum(int io, int D, int B, int T, int H, int CS, const void* k, float* csum, hipStream_t s);
+hipError_t launch_ccq_combine(int io, int D, int B, int T, int H, int CS, const void* q, const void* k,
+                              const void* kkq, const float* csum, const float* w, const float* b, void* qc,
+                              hipStream_t s);
 hipError_t launch_decode_step(int io, int D, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_gdn_wy(int io, int D, int C, const GdnArgs& a, hipStream_t s);
 hipError_t launch_gdn_state(int io, int D, int C, const GdnArgs& a, hipStream_t s);

@@ -221,8 +221,9 @@ ll_status ll_decode_step_ragged(int B, int H, int dk, int dv, int L, ll_dtype io
  *   q_clean [B,T,H,dk]  io dtype, written (may be q itself)
  *   workspace  device memory of >= ll_ccq_query_workspace_bytes; contents on
  *              entry do not matter.
- * The running sums come from two chunk-parallel prefills with every level
- * weight 1 and no decay.  Implemented for the head sizes of ll_attn_fwd and T
+ * The running second moment comes from a chunk-parallel prefill with every
+ * level weight 1 and no decay, the running key sum from a chunked fp32
+ * prefix sum.  Implemented for the head sizes of ll_attn_fwd and T
  * a multiple of a supported chunk size (16 for fp32, 32 for bf16), T < 2^23
  * (LL_ERR_UNSUPPORTED otherwise).
  */

@@ -226,9 +226,11 @@ def test_prefill_from_state_validation_before_any_launch():
 def test_ccq_validation_before_any_launch():
     D = DUMMY
     n = F.ll_ccq_query_workspace_bytes(2, 16384, 16, 64, F.LL_BF16)
-    # two prefills' running sums: ones [rows, 15] fp32, zeros, e0, kkq, ksum (bf16 rows) + prefill workspace
+    # the prefill's inputs ones [rows, 15] and zeros (fp32), its output kkq (bf16 rows), the
+    # per-chunk key sums [2, 16, 256, 64] fp32 and the prefill workspace
     rows = 2 * 16384 * 16
-    assert n >= rows * 15 * 4 + rows * 4 + 3 * rows * 64 * 2 + F.ll_attn_fwd_workspace_bytes(prob())
+    need = rows * 15 * 4 + rows * 4 + rows * 64 * 2 + 2 * 16 * 256 * 64 * 4 + F.ll_attn_fwd_workspace_bytes(prob())
+    assert need <= n <= need + 5 * 256
 
     def call(B=2, T=16384, H=16, dk=64, io=F.LL_BF16, q=D, k=D, w=D, b=D, qc=D, ws=D, wsb=n):
         return status_of(F.ll_ccq_query, B, T, H, dk, io, q, k, w, b, qc, ws, wsb, 0)[0]
