@@ -114,23 +114,33 @@ __global__ void __launch_bounds__(256) ll_bwd_accum_rev(BwdArgs a, const T* Y, f
   }
 }
 
-// Dot products of rows, one wave per row (lanes over the row):
-// out[row * stride + col] = sum_x X1 Y1 (- X2 Y2 when X2 is given; Y2 fp32).
+// Dot products of rows, D/4 lanes per row (four elements a lane, D/4 a power
+// of two <= 64, so a row's lanes are an aligned group of the wave):
+// out[row * stride + col] = sum_x X1 Y1 (- X2 Y2 when X2 is given; Y2 fp32);
+// 0 when X1 is null.
 template <typename T>
 __global__ void __launch_bounds__(256) ll_bwd_rowdot(int64_t rows, int D, const T* X1, const T* Y1, const T* X2,
                                                      const float* Y2, float* out, int stride, int col) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  typedef Vec4Of<T> V;
+  const int G4 = D / 4;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / G4;
+  const int x4 = (int)(gid % G4);
   float s = 0.f;
-  if (X1)
-    for (int x = lane; x < D; x += 64) {
-      s += to_f32(X1[row * D + x]) * to_f32(Y1[row * D + x]);
-      if (X2) s -= to_f32(X2[row * D + x]) * Y2[row * D + x];
-    }
+  if (row < rows && X1) {
+    const int64_t i = row * G4 + x4;
+    const V x = reinterpret_cast<const V*>(X1)[i], y = reinterpret_cast<const V*>(Y1)[i];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
-  if (lane == 0) out[row * stride + col] = s;
+    for (int e = 0; e < 4; ++e) s += to_f32(x[e]) * to_f32(y[e]);
+    if (X2) {
+      const V x2 = reinterpret_cast<const V*>(X2)[i];
+      const f32x4 y2 = reinterpret_cast<const f32x4*>(Y2)[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s -= to_f32(x2[e]) * y2[e];
+    }
+  }
+  for (int m = G4 >> 1; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+  if (row < rows && x4 == 0) out[row * stride + col] = s;
 }
 
 // dk, dv in the io dtype from their fp32 accumulators
@@ -211,9 +221,11 @@ hipError_t launch_bwd_accum_rev(int io, const BwdArgs& a, const void* Y, float* 
   return hipGetLastError();
 }
 
+static unsigned rowdot_blocks(int64_t rows, int D) { return (unsigned)((rows * (D / 4) + 255) / 256); }
+
 hipError_t launch_bwd_rowdot(int io, const BwdArgs& a, const void* Y, int lvl, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.T * a.H;
-  LL_BWD_IO(io, hipLaunchKernelGGL(ll_bwd_rowdot<TT>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, rows, a.D,
+  LL_BWD_IO(io, hipLaunchKernelGGL(ll_bwd_rowdot<TT>, dim3(rowdot_blocks(rows, a.D)), dim3(256), 0, s, rows, a.D,
                                    static_cast<const TT*>(Y), static_cast<const TT*>(a.dO), (const TT*)nullptr,
                                    (const float*)nullptr, a.dlambda, a.L, lvl));
   return hipGetLastError();
@@ -228,7 +240,7 @@ hipError_t launch_bwd_cast(int io, const BwdArgs& a, const float* acc_dk, const 
 hipError_t launch_bwd_gate(int io, const BwdArgs& a, const float* acc_dk, float* dG, hipStream_t s) {
   // dG_t = dO_t . o_t - k_t . dk_t per row, then the suffix sums per head
   const int64_t rows = (int64_t)a.B * a.T * a.H;
-  LL_BWD_IO(io, hipLaunchKernelGGL(ll_bwd_rowdot<TT>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, rows, a.D,
+  LL_BWD_IO(io, hipLaunchKernelGGL(ll_bwd_rowdot<TT>, dim3(rowdot_blocks(rows, a.D)), dim3(256), 0, s, rows, a.D,
                                    static_cast<const TT*>(a.dO), static_cast<const TT*>(a.o),
                                    static_cast<const TT*>(a.k), acc_dk, dG, 1, 0));
   hipError_t e = hipGetLastError();
