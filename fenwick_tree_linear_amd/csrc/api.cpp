@@ -552,7 +552,7 @@ namespace {
 struct BwdPlan {
   ll_problem p, pp;  // the forward problem at T and at Tp
   int Tp, LS;
-  size_t qr_off, kr_off, vr_off, dor_off, y_off, gr_off, hot_off, adk_off, adv_off, fwd_off, fwd_bytes, bytes;
+  size_t qr_off, kr_off, vr_off, dor_off, y_off, ylv_off, ylv_stride, gr_off, hot_off, adk_off, fwd_off, fwd_bytes, bytes;
 };
 
 ll_status plan_bwd(const ll_problem* p, BwdPlan* out) {
@@ -585,10 +585,12 @@ ll_status plan_bwd(const ll_problem* p, BwdPlan* out) {
   c.vr_off = take(rowsP * d * esz);
   c.dor_off = take(rowsP * d * esz);
   c.y_off = take(rowsP * d * esz);
+  // the reversed reads of every level present, kept until their sum: dv's and dk's per level
+  c.ylv_stride = align256(rowsP * d * esz);
+  c.ylv_off = take(2 * (size_t)c.LS * c.ylv_stride);
   c.gr_off = take(rowsP * 4);
   c.hot_off = take(rowsP * p->L * 4);
   c.adk_off = take(rows * d * 4);
-  c.adv_off = take(rows * d * 4);
   c.fwd_off = off;
   c.fwd_bytes = plp.bytes > pl.bytes ? plp.bytes : pl.bytes;
   c.bytes = off + c.fwd_bytes;
@@ -629,8 +631,8 @@ ll_status ll_attn_bwd(const ll_problem* p, const void* q, const void* k, const v
   void* Y = ws + c.y_off;
   float* gr = reinterpret_cast<float*>(ws + c.gr_off);
   float* hot = reinterpret_cast<float*>(ws + c.hot_off);
+  char* ylv = ws + c.ylv_off;
   float* adk = reinterpret_cast<float*>(ws + c.adk_off);
-  float* adv = reinterpret_cast<float*>(ws + c.adv_off);
   void* fws = ws + c.fwd_off;
   llattn::BwdArgs a;
   a.B = p->B;
@@ -670,17 +672,19 @@ ll_status ll_attn_bwd(const ll_problem* p, const void* q, const void* k, const v
     // dv and dk: reads in reversed time with lambda^(l) dO as the later token's side
     step([&] { return llattn::launch_bwd_scale_rev(io, a, lvl, dOr, stream); });
     if (e != hipSuccess) break;
-    st = run_prefill(&c.pp, 0, nullptr, kr, qr, dOr, gr, hot, nullptr, Y, nullptr, fws, c.fwd_bytes, stream);
-    if (st != LL_OK) return st;
-    step([&] { return llattn::launch_bwd_accum_rev(io, a, Y, adv, lvl == 0, stream); });
     if (e != hipSuccess) break;
-    st = run_prefill(&c.pp, 0, nullptr, vr, dOr, qr, gr, hot, nullptr, Y, nullptr, fws, c.fwd_bytes, stream);
+    void* ydv = ylv + (2 * (size_t)lvl) * c.ylv_stride;
+    void* ydk = ylv + (2 * (size_t)lvl + 1) * c.ylv_stride;
+    st = run_prefill(&c.pp, 0, nullptr, kr, qr, dOr, gr, hot, nullptr, ydv, nullptr, fws, c.fwd_bytes, stream);
     if (st != LL_OK) return st;
-    step([&] { return llattn::launch_bwd_accum_rev(io, a, Y, adk, lvl == 0, stream); });
+    st = run_prefill(&c.pp, 0, nullptr, vr, dOr, qr, gr, hot, nullptr, ydk, nullptr, fws, c.fwd_bytes, stream);
+    if (st != LL_OK) return st;
   }
   // levels no position reaches carry no gradient
   for (int lvl = c.LS; lvl < p->L; ++lvl) step([&] { return llattn::launch_bwd_rowdot(io, a, nullptr, lvl, stream); });
-  step([&] { return llattn::launch_bwd_cast(io, a, adk, adv, stream); });
+  step([&] {
+    return llattn::launch_bwd_sum_rev(io, a, ylv, (int64_t)(c.ylv_stride / (io ? 2 : 4)), c.LS, adk, stream);
+  });
   step([&] { return llattn::launch_bwd_gate(io, a, adk, gr, stream); });  // gr is free again: dG per row
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -94,9 +94,12 @@ __global__ void __launch_bounds__(256) ll_bwd_onehot(int64_t rows, int L, int lv
   LL_GRID_STRIDE(i, rows * L) w[i] = (int)(i % L) == lvl ? 1.f : 0.f;
 }
 
-// acc [B,T,H,D] (+)= Y at t' = Tp-1-t
+// The reversed-time reads of every level, summed: level l's dv read is the
+// buffer Y + 2 l ystride and its dk read Y + (2 l + 1) ystride, each [B,Tp,H,D]
+// in reversed time.  Writes dv, dk at t = Tp-1-t' in the io dtype (levels
+// added in order in fp32) and the fp32 sum for dk, which the gate uses.
 template <typename T>
-__global__ void __launch_bounds__(256) ll_bwd_accum_rev(BwdArgs a, const T* Y, float* acc, int first) {
+__global__ void __launch_bounds__(256) ll_bwd_sum_rev(BwdArgs a, const T* Y, int64_t ystride, int LS, float* acc_dk) {
   typedef Vec4Of<T> V;
   const int G4 = a.D / 4;
   const int64_t n = (int64_t)a.B * a.T * a.H * G4;
@@ -106,11 +109,27 @@ __global__ void __launch_bounds__(256) ll_bwd_accum_rev(BwdArgs a, const T* Y, f
     const int h = (int)(row % a.H);
     const int64_t bt = row / a.H;
     const int t = (int)(bt % a.T), b = (int)(bt / a.T);
-    const V y = reinterpret_cast<const V*>(Y)[(((int64_t)b * a.Tp + (a.Tp - 1 - t)) * a.H + h) * G4 + x4];
-    f32x4 cur = first ? f32x4{0.f, 0.f, 0.f, 0.f} : reinterpret_cast<const f32x4*>(acc)[i];
+    const int64_t src = (((int64_t)b * a.Tp + (a.Tp - 1 - t)) * a.H + h) * G4 + x4;
+    f32x4 sv = f32x4{0.f, 0.f, 0.f, 0.f}, sk = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int l = 0; l < LS; ++l) {
+      const V yv = reinterpret_cast<const V*>(Y + 2 * l * ystride)[src];
+      const V yk = reinterpret_cast<const V*>(Y + (2 * l + 1) * ystride)[src];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) cur[e] += to_f32(y[e]);
-    reinterpret_cast<f32x4*>(acc)[i] = cur;
+      for (int e = 0; e < 4; ++e) {
+        sv[e] += to_f32(yv[e]);
+        sk[e] += to_f32(yk[e]);
+      }
+    }
+    V ok, ov;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ok[e] = from_f32<T>(sk[e]);
+      ov[e] = from_f32<T>(sv[e]);
+    }
+    reinterpret_cast<f32x4*>(acc_dk)[i] = sk;
+    static_cast<V*>(a.dk)[i] = ok;
+    static_cast<V*>(a.dv)[i] = ov;
   }
 }
 
@@ -141,24 +160,6 @@ __global__ void __launch_bounds__(256) ll_bwd_rowdot(int64_t rows, int D, const 
   }
   for (int m = G4 >> 1; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
   if (row < rows && x4 == 0) out[row * stride + col] = s;
-}
-
-// dk, dv in the io dtype from their fp32 accumulators
-template <typename T>
-__global__ void __launch_bounds__(256) ll_bwd_cast(BwdArgs a, const float* acc_dk, const float* acc_dv) {
-  typedef Vec4Of<T> V;
-  const int64_t n = (int64_t)a.B * a.T * a.H * a.D / 4;
-  LL_GRID_STRIDE(i, n) {
-    const f32x4 x = reinterpret_cast<const f32x4*>(acc_dk)[i], y = reinterpret_cast<const f32x4*>(acc_dv)[i];
-    V ok, ov;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ok[e] = from_f32<T>(x[e]);
-      ov[e] = from_f32<T>(y[e]);
-    }
-    static_cast<V*>(a.dk)[i] = ok;
-    static_cast<V*>(a.dv)[i] = ov;
-  }
 }
 
 // One workgroup per head: dlog_gate_r = sum_{t >= r} dG_t, walking the tokens
@@ -214,10 +215,11 @@ hipError_t launch_bwd_onehot(int64_t rows, int L, int lvl, float* w, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_accum_rev(int io, const BwdArgs& a, const void* Y, float* acc, int first, hipStream_t s) {
+hipError_t launch_bwd_sum_rev(int io, const BwdArgs& a, const void* Y, int64_t ystride, int LS, float* acc_dk,
+                             hipStream_t s) {
   const int grid = grid_for((int64_t)a.B * a.T * a.H * a.D / 4);
-  LL_BWD_IO(io, hipLaunchKernelGGL(ll_bwd_accum_rev<TT>, dim3(grid), dim3(256), 0, s, a, static_cast<const TT*>(Y),
-                                   acc, first));
+  LL_BWD_IO(io, hipLaunchKernelGGL(ll_bwd_sum_rev<TT>, dim3(grid), dim3(256), 0, s, a, static_cast<const TT*>(Y),
+                                   ystride, LS, acc_dk));
   return hipGetLastError();
 }
 
@@ -228,12 +230,6 @@ hipError_t launch_bwd_rowdot(int io, const BwdArgs& a, const void* Y, int lvl, h
   LL_BWD_IO(io, hipLaunchKernelGGL(ll_bwd_rowdot<TT>, dim3(rowdot_blocks(rows, a.D)), dim3(256), 0, s, rows, a.D,
                                    static_cast<const TT*>(Y), static_cast<const TT*>(a.dO), (const TT*)nullptr,
                                    (const float*)nullptr, a.dlambda, a.L, lvl));
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_cast(int io, const BwdArgs& a, const float* acc_dk, const float* acc_dv, hipStream_t s) {
-  const int grid = grid_for((int64_t)a.B * a.T * a.H * a.D / 4);
-  LL_BWD_IO(io, hipLaunchKernelGGL(ll_bwd_cast<TT>, dim3(grid), dim3(256), 0, s, a, acc_dk, acc_dv));
   return hipGetLastError();
 }
 

@@ -95,9 +95,9 @@ hipError_t launch_prior_read(int io, int D, int C, const PrefillArgs& a, hipStre
 hipError_t launch_bwd_reverse(int io, const BwdArgs& a, void* qr, void* kr, void* vr, float* gr, hipStream_t s);
 hipError_t launch_bwd_scale_rev(int io, const BwdArgs& a, int lvl, void* dOr, hipStream_t s);
 hipError_t launch_bwd_onehot(int64_t rows, int L, int lvl, float* w, hipStream_t s);
-hipError_t launch_bwd_accum_rev(int io, const BwdArgs& a, const void* Y, float* acc, int first, hipStream_t s);
+hipError_t launch_bwd_sum_rev(int io, const BwdArgs& a, const void* Y, int64_t ystride, int LS, float* acc_dk,
+                             hipStream_t s);
 hipError_t launch_bwd_rowdot(int io, const BwdArgs& a, const void* Y, int lvl, hipStream_t s);
-hipError_t launch_bwd_cast(int io, const BwdArgs& a, const float* acc_dk, const float* acc_dv, hipStream_t s);
 hipError_t launch_bwd_gate(int io, const BwdArgs& a, const float* acc_dk, float* dG, hipStream_t s);
 hipError_t launch_ccq_fill(int64_t rows, int L, float* ones, float* zeros, hipStream_t s);
 hipError_t launch_ccq_ksum(int io, int D, int B, int T, int H, int CS, const void* k, float* csum, hipStream_t s);

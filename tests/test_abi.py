@@ -248,9 +248,10 @@ def test_ccq_validation_before_any_launch():
 def test_bwd_validation_before_any_launch():
     D = DUMMY
     n = F.ll_attn_bwd_workspace_bytes(prob(T=2048, L=12))
-    assert n >= 2 * 2048 * 16 * 64 * (5 * 2 + 2 * 4)  # reversed rows, accumulators
-    # T = 1536 pads to 2048 for the reversed reads (five padded bf16 row buffers)
-    assert F.ll_attn_bwd_workspace_bytes(prob(T=1536, L=12)) >= 5 * 2 * 2048 * 16 * 64 * 2
+    # five reversed bf16 row buffers, the dv and dk reads of all 12 levels, an fp32 dk
+    assert n >= 2 * 2048 * 16 * 64 * ((5 + 2 * 12) * 2 + 4)
+    # T = 1536 pads to 2048 for the reversed reads (29 padded bf16 row buffers)
+    assert F.ll_attn_bwd_workspace_bytes(prob(T=1536, L=12)) >= 29 * 2 * 2048 * 16 * 64 * 2
 
     def call(p, q=D, o=D, dO=D, dq=D, dlam=D, ws=D, wsb=n):
         return status_of(F.ll_attn_bwd, p, q, D, D, D, D, o, dO, dq, D, D, D, dlam, ws, wsb, 0)[0]
