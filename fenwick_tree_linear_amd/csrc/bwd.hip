@@ -94,6 +94,14 @@ __global__ void __launch_bounds__(256) ll_bwd_onehot(int64_t rows, int L, int lv
   LL_GRID_STRIDE(i, rows * L) w[i] = (int)(i % L) == lvl ? 1.f : 0.f;
 }
 
+// Moves the one of a one-hot [rows, L] from level lvl - 1 to level lvl.
+__global__ void __launch_bounds__(256) ll_bwd_onehot_next(int64_t rows, int L, int lvl, float* w) {
+  LL_GRID_STRIDE(r, rows) {
+    w[r * L + lvl - 1] = 0.f;
+    w[r * L + lvl] = 1.f;
+  }
+}
+
 // The reversed-time reads of every level, summed: level l's dv read is the
 // buffer Y + 2 l ystride and its dk read Y + (2 l + 1) ystride, each [B,Tp,H,D]
 // in reversed time.  Writes dv, dk at t = Tp-1-t' in the io dtype (levels
@@ -211,7 +219,11 @@ hipError_t launch_bwd_scale_rev(int io, const BwdArgs& a, int lvl, void* dOr, hi
 }
 
 hipError_t launch_bwd_onehot(int64_t rows, int L, int lvl, float* w, hipStream_t s) {
-  hipLaunchKernelGGL(ll_bwd_onehot, dim3(grid_for(rows * L)), dim3(256), 0, s, rows, L, lvl, w);
+  // the levels are taken in order: after level 0 only two columns change
+  if (lvl > 0 && lvl < L)
+    hipLaunchKernelGGL(ll_bwd_onehot_next, dim3(grid_for(rows)), dim3(256), 0, s, rows, L, lvl, w);
+  else
+    hipLaunchKernelGGL(ll_bwd_onehot, dim3(grid_for(rows * L)), dim3(256), 0, s, rows, L, lvl, w);
   return hipGetLastError();
 }
 

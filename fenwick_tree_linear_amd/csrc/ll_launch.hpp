@@ -94,6 +94,7 @@ hipError_t launch_state_export(int D, int C, const PrefillArgs& a, hipStream_t s
 hipError_t launch_prior_read(int io, int D, int C, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_bwd_reverse(int io, const BwdArgs& a, void* qr, void* kr, void* vr, float* gr, hipStream_t s);
 hipError_t launch_bwd_scale_rev(int io, const BwdArgs& a, int lvl, void* dOr, hipStream_t s);
+// one-hot level weights at lvl; for lvl > 0, w must hold the one-hot at lvl - 1
 hipError_t launch_bwd_onehot(int64_t rows, int L, int lvl, float* w, hipStream_t s);
 hipError_t launch_bwd_sum_rev(int io, const BwdArgs& a, const void* Y, int64_t ystride, int LS, float* acc_dk,
                              hipStream_t s);
