@@ -256,9 +256,15 @@ namespace {
 
 // Both prefill entry points: a segment at positions pos0 .. pos0 + T - 1 whose
 // earlier positions (if any) are summarised by state_in.
+// reuse_states: the workspace already holds the block states and Fenwick nodes
+// of this (k, v, log_gate) from the previous call (a Mamba-2 read with other
+// q or level weights); only the read runs.
 ll_status run_prefill(const ll_problem* p, int64_t pos0, const float* state_in, const void* q, const void* k,
                       const void* v, const float* log_gate, const float* lambda, const float* beta, void* o,
-                      void* state_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      void* state_out, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                      bool reuse_states = false) {
+  if (reuse_states && (p->rule != LL_MAMBA2 || pos0 != 0 || state_out))
+    return fail(LL_ERR_UNSUPPORTED, "reusing block states is only for a plain Mamba-2 read");
   Plan pl;
   ll_status st = plan_prefill(p, state_out != nullptr, &pl);
   if (st != LL_OK) return st;
@@ -334,9 +340,9 @@ ll_status run_prefill(const ll_problem* p, int64_t pos0, const float* state_in, 
     if (e == hipSuccess) e = timed(K_GDN_STATE, stream, [&] { return llattn::launch_gdn_state(io, D, p->C, gd, stream); });
   }
   const int C = pl.Cr;
-  if (e == hipSuccess)
+  if (e == hipSuccess && !reuse_states)
     e = timed(K_CHUNK_STATE, stream, [&] { return llattn::launch_block_state(io, D, C, a, stream); });
-  if (e == hipSuccess && a.nb > 1)
+  if (e == hipSuccess && a.nb > 1 && !reuse_states)
     e = timed(K_FENWICK_SCAN, stream, [&] { return llattn::launch_fenwick_scan(D, a, stream); });
   if (e == hipSuccess && o)
     e = timed(K_CHUNK_ATTN, stream, [&] { return llattn::launch_chunk_attn(io, D, C, a, stream); });
@@ -552,7 +558,8 @@ namespace {
 struct BwdPlan {
   ll_problem p, pp;  // the forward problem at T and at Tp
   int Tp, LS;
-  size_t qr_off, kr_off, vr_off, dor_off, y_off, ylv_off, ylv_stride, gr_off, hot_off, adk_off, fwd_off, fwd_bytes, bytes;
+  size_t qr_off, kr_off, vr_off, dor_off, y_off, ylv_off, ylv_stride, gr_off, hot_off, adk_off, fwl_off, fwl_bytes,
+      fwd_off, fwd_bytes, bytes;
 };
 
 ll_status plan_bwd(const ll_problem* p, BwdPlan* out) {
@@ -591,6 +598,9 @@ ll_status plan_bwd(const ll_problem* p, BwdPlan* out) {
   c.gr_off = take(rowsP * 4);
   c.hot_off = take(rowsP * p->L * 4);
   c.adk_off = take(rows * d * 4);
+  // the forward's block states and nodes of (k, v), kept for the reads of every level
+  c.fwl_bytes = pl.bytes;
+  c.fwl_off = take(pl.bytes);
   c.fwd_off = off;
   c.fwd_bytes = plp.bytes > pl.bytes ? plp.bytes : pl.bytes;
   c.bytes = off + c.fwd_bytes;
@@ -665,13 +675,14 @@ ll_status ll_attn_bwd(const ll_problem* p, const void* q, const void* k, const v
   for (int lvl = 0; lvl < c.LS && e == hipSuccess; ++lvl) {
     step([&] { return llattn::launch_bwd_onehot(rowsP, p->L, lvl, hot, stream); });
     if (e != hipSuccess) break;
-    // dlambda at this level: dO . (the level's read alone)
-    st = run_prefill(p, 0, nullptr, q, k, v, log_gate, hot, nullptr, Y, nullptr, fws, c.fwd_bytes, stream);
+    // dlambda at this level: dO . (the level's read alone); the block states and
+    // nodes of (k, v) are the same for every level, built once in their own workspace
+    st = run_prefill(p, 0, nullptr, q, k, v, log_gate, hot, nullptr, Y, nullptr, ws + c.fwl_off, c.fwl_bytes, stream,
+                     lvl > 0);
     if (st != LL_OK) return st;
     step([&] { return llattn::launch_bwd_rowdot(io, a, Y, lvl, stream); });
     // dv and dk: reads in reversed time with lambda^(l) dO as the later token's side
     step([&] { return llattn::launch_bwd_scale_rev(io, a, lvl, dOr, stream); });
-    if (e != hipSuccess) break;
     if (e != hipSuccess) break;
     void* ydv = ylv + (2 * (size_t)lvl) * c.ylv_stride;
     void* ydk = ylv + (2 * (size_t)lvl + 1) * c.ylv_stride;

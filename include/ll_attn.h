@@ -247,7 +247,9 @@ ll_status ll_ccq_query(int B, int T, int H, int dk, ll_dtype io, const void* q, 
  * Shapes as ll_attn_fwd (LL_ERR_UNSUPPORTED for LL_GATED_DELTANET); the
  * workspace holds reversed copies of q, k, v and dO padded to a power of
  * two, the reversed dk and dv reads of every level (2 x levels row buffers,
- * summed at the end), an fp32 dk and the forward's workspace.
+ * summed at the end), an fp32 dk, the forward's workspace for the reversed
+ * reads and one more that keeps the block states of (k, v) for the level
+ * reads.
  */
 ll_status ll_attn_bwd_workspace_bytes(const ll_problem* p, size_t* bytes);
 ll_status ll_attn_bwd(const ll_problem* p, const void* q, const void* k, const void* v, const float* log_gate,
