@@ -29,7 +29,9 @@ namespace llattn {
 
 // ---------------------------------------------------------------------------
 // ll_gdn_wy: one workgroup of four waves per (chunk, head).
-//   1. K and V rows land in LDS (direct loads); wave 0 scans the gates.
+//   1. K rows land in LDS (direct loads); wave 0 scans the gates.  V is
+//      loaded only for step 4, into the space of L (at d = 128 and C = 64 this
+//      keeps the workgroup at 51 KB of LDS: three per CU instead of two).
 //   2. L: the causal 16x16 tiles of K K^T on MFMA, weighted by
 //      beta_r e^{G_r - G_s} and masked to s < r, fp32 in LDS.
 //   3. T = (I + L)^-1 by blocks of 16: the diagonal blocks by forward
@@ -44,9 +46,11 @@ template <typename T, int D, int C>
 struct WySmem {
   typedef Tile<T, C, D> TL;
   static constexpr int TS = C + 4;  // fp32 row stride of L and T (16-byte rows, rows 4 banks apart)
-  static constexpr int KOFF = 0, VOFF = TL::BYTES;
-  static constexpr int LOFF = 2 * TL::BYTES;  // L [C][TS] fp32
-  static constexpr int TOFF = LOFF + C * TS * 4;  // T [C][TS] fp32
+  static constexpr int LREG = ((C * TS * 4 > TL::BYTES ? C * TS * 4 : TL::BYTES) + 1023) / 1024 * 1024;
+  static constexpr int KOFF = 0;
+  static constexpr int LOFF = TL::BYTES;  // L [C][TS] fp32; V lands here once L is no longer read
+  static constexpr int VOFF = LOFF;
+  static constexpr int TOFF = LOFF + LREG;  // T [C][TS] fp32
   static constexpr int GOFF = TOFF + C * TS * 4;  // G [C]
   static constexpr int BOFF = GOFF + C * 4;        // beta [C]
   static constexpr int SOFF = BOFF + C * 4;        // beta e^G [C]
@@ -89,7 +93,6 @@ __global__ void __launch_bounds__(256) ll_gdn_wy(GdnArgs a) {
     ChunkLoads<T, D, C, NW> ld;
     ld.init(wv, lane, a.H, 1, 1);
     ld.tiles(a.k, row0, smem + SM::KOFF, wv);
-    ld.tiles(a.v, row0, smem + SM::VOFF, wv);
   }
   if (wv == 0) {
     const float G = chunk_scan<C>(lane < C ? a.g[row0 + (int64_t)lane * a.H] : 0.f);
@@ -168,6 +171,14 @@ __global__ void __launch_bounds__(256) ll_gdn_wy(GdnArgs a) {
     }
     __syncthreads();
   }
+
+  {
+    ChunkLoads<T, D, C, NW> ld;
+    ld.init(wv, lane, a.H, 1, 1);
+    ld.tiles(a.v, row0, smem + SM::VOFF, wv);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
   // 4. outputs: wave w takes token tile w % CT and every (NW/CT)-th column
   // tile; lane: token r = 16 tt + lane%16, features 16 nt + 4 (lane/16) + e
