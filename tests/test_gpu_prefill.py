@@ -105,6 +105,8 @@ RAGGED = [
     ("bf16", 2, 2, 64, 64, 64, 7),      # a single chunk
     ("bf16", 1, 3, 320, 64, 64, 20),    # more levels than needed
     ("bf16", 1, 2, 1024, 128, 32, 11),  # d=128 (chunks of 32)
+    ("bf16", 1, 1, 4096, 128, 32, 13),  # d=128: 16 blocks of 8 chunks, 4 block-level node levels
+    ("bf16", 1, 1, 1568, 128, 32, 12),  # d=128: 49 chunks, one-chunk blocks
     ("f32", 2, 3, 48, 16, 16, 7),       # 3 chunks of 16
     ("f32", 1, 1, 16, 16, 16, 5),       # a single fp32 chunk
     ("f32", 1, 2, 96, 64, 32, 8),       # d=64 fp32
@@ -119,7 +121,8 @@ def test_ragged_and_degenerate_shapes(io, B, H, T, d, C, L):
 
 
 @pytest.mark.parametrize("io,T,d,C,L", [("bf16", 1536, 64, 64, 12), ("bf16", 2048, 64, 64, 13),
-                                        ("f32", 208, 16, 16, 9), ("bf16", 320, 32, 32, 10)])
+                                        ("f32", 208, 16, 16, 9), ("bf16", 320, 32, 32, 10),
+                                        ("bf16", 1280, 128, 32, 12)])
 def test_state_export_matches_bucket_states(io, T, d, C, L):
     """The exported per-level states of [0,T) (decayed through token T-1) equal
     the oracle's bucket sums; empty levels are zero and log-scales 0."""
