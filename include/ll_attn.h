@@ -242,8 +242,9 @@ ll_status ll_ccq_query(int B, int T, int H, int dk, ll_dtype io, const void* q, 
  * chunk-parallel forward itself: dq is the forward with (q, k, v) :=
  * (dO, v, k); dlambda at level l is dO . (the level-l read); dk and dv are the
  * reads of reversed time, one level at a time with the level weight folded
- * into dO (3 x levels + 1 forward passes, so about that many times the
- * forward's cost); dlog_gate_r = sum_{t >= r} (dO_t . o_t - k_t . dk_t).
+ * into dO (3 x levels + 1 forward reads, the level reads for dlambda sharing
+ * one build of the block states: roughly 40 times the forward's cost at 12
+ * levels); dlog_gate_r = sum_{t >= r} (dO_t . o_t - k_t . dk_t).
  * Shapes as ll_attn_fwd (LL_ERR_UNSUPPORTED for LL_GATED_DELTANET); the
  * workspace holds reversed copies of q, k, v and dO padded to a power of
  * two, the reversed dk and dv reads of every level (2 x levels row buffers,
