@@ -497,7 +497,34 @@ def gdn_bench(steps: int) -> dict:
     F.ll_kernel_timing_enable(False)
     return {"workload": "gated-deltanet prefill B2 H16 T8192 dk=dv=128 bf16, 14 levels, chunk 64",
             "ms_per_step": round(ms, 5), "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
-            "kernels_us": {name: round(t / n * 1e3, 2) for name, (t, n) in kt.items()}}
+            "kernels_us": {name: round(t / n * 1e3, 2) for name, (t, n) in kt.items()},
+            "hbm": gdn_hbm_fractions(w, kt)}
+
+
+def gdn_hbm_fractions(w, kt) -> dict:
+    """Algorithmic HBM bytes of each Gated DeltaNet prefill kernel on this workload and the rate
+    they give at the kernel's measured average time, as a fraction of the 8 TB/s peak.  The read
+    runs at chunk 32 (the bf16 d = 128 tile) in blocks of 8 chunks; its bytes count q, k, U, the
+    level weights, gates and o, not the re-reads of earlier blocks' nodes."""
+    rows = w.B * w.T * w.H
+    rb = w.dk * 2  # one bf16 row
+    nb = w.T // (32 * 8)  # blocks per head
+    heads = w.B * w.H
+    node = w.dk * w.dv * 4
+    alg = {
+        "ll_gdn_wy": 4 * rows * rb + 2 * rows * 4,            # k, v, gates, beta in; W, U' out
+        "ll_gdn_state": 4 * rows * rb + rows * 4,             # W, k, U', gates in; U out
+        "ll_chunk_state": 2 * rows * rb + rows * 4 + heads * nb * node,  # k, U, gates in; block states out
+        "ll_fenwick_scan": heads * nb * node + heads * (nb // 2) * node + heads * nb * node // 2,
+        "ll_chunk_attn": 4 * rows * rb + rows * (w.L + 1) * 4,  # q, k, U, lambda, gates in; o out
+    }
+    out = {}
+    for name, nbytes in alg.items():
+        if name in kt and kt[name][1]:
+            us = kt[name][0] / kt[name][1] * 1e3
+            out[name] = {"bytes": nbytes, "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                         "frac": round(nbytes / (us * 1e-6) / 8e12, 4)}
+    return out
 
 
 def main() -> int:
