@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     ll_attn_bwd_workspace_bytes,
     ll_attn_fwd,
     ll_attn_fwd_from_state,
+    ll_attn_fwd_noalloc,
     ll_attn_fwd_workspace_bytes,
     ll_ccq_query,
     ll_ccq_query_workspace_bytes,

@@ -66,6 +66,7 @@ def load_library() -> ctypes.CDLL:
     lib.ll_kernel_timing_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_int), i32, ctypes.POINTER(ctypes.c_int)]
     lib.ll_lambda_mlp.argtypes = [i64, i32, i32, P, P, P, P, P, P]
+    lib.ll_attn_fwd_noalloc.argtypes = [ctypes.POINTER(LLProblem), P, P, P, P, P, P, P, P, P]
     lib.ll_attn_fwd_from_state.argtypes = [ctypes.POINTER(LLProblem), i64, P, P, P, P, P, P, P, P, P, P, sz, P]
     lib.ll_ccq_query_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.ll_ccq_query.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, sz, P]
@@ -73,7 +74,7 @@ def load_library() -> ctypes.CDLL:
     lib.ll_attn_bwd.argtypes = [ctypes.POINTER(LLProblem)] + [P] * 13 + [sz, P]
     lib.ll_decode_step_ragged.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
     for fn in ("ll_attn_fwd_workspace_bytes", "ll_attn_fwd", "ll_decode_state_bytes", "ll_decode_step",
-               "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp", "ll_decode_step_ragged", "ll_attn_fwd_from_state",
+               "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp", "ll_attn_fwd_noalloc", "ll_decode_step_ragged", "ll_attn_fwd_from_state",
                "ll_ccq_query_workspace_bytes", "ll_ccq_query", "ll_attn_bwd_workspace_bytes", "ll_attn_bwd"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -116,6 +117,12 @@ def ll_attn_fwd(problem: LLProblem, q, k, v, log_gate, lam, beta, o, state_out, 
     _check(load_library().ll_attn_fwd(None if problem is None else ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate), _ptr(lam),
                                       _ptr(beta), _ptr(o), _ptr(state_out), _ptr(workspace), workspace_bytes,
                                       _stream(stream)))
+
+
+def ll_attn_fwd_noalloc(problem: LLProblem, q, k, v, log_gate, lam, beta, o, state_out, stream=None) -> None:
+    _check(load_library().ll_attn_fwd_noalloc(None if problem is None else ctypes.byref(problem), _ptr(q), _ptr(k),
+                                              _ptr(v), _ptr(log_gate), _ptr(lam), _ptr(beta), _ptr(o),
+                                              _ptr(state_out), _stream(stream)))
 
 
 def ll_attn_fwd_from_state(problem: LLProblem, pos0: int, state_in, q, k, v, log_gate, lam, beta, o, state_out,

@@ -252,7 +252,37 @@ ll_status ll_attn_fwd_workspace_bytes(const ll_problem* p, size_t* bytes) {
   return ok();
 }
 
+// ------------------------------------------------------ allocation-free prefill
+// The workspace of ll_attn_fwd_noalloc: one copy of this array on every GPU the
+// library runs on, alive until the process ends.  In host code its name is only
+// a stand-in for the device symbol; host code uses the device address that
+// hipGetSymbolAddress returns for the current device, never the name itself.
+static __device__ __align__(256) char scratch[LL_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept.
+ll_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LL_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LL_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail(LL_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    if (!ptr) return fail(LL_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LL_OK;
+}
 
 // Both prefill entry points: a segment at positions pos0 .. pos0 + T - 1 whose
 // earlier positions (if any) are summarised by state_in.
@@ -262,7 +292,7 @@ namespace {
 ll_status run_prefill(const ll_problem* p, int64_t pos0, const float* state_in, const void* q, const void* k,
                       const void* v, const float* log_gate, const float* lambda, const float* beta, void* o,
                       void* state_out, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                      bool reuse_states = false) {
+                      bool reuse_states = false, bool noalloc = false) {
   if (reuse_states && (p->rule != LL_MAMBA2 || pos0 != 0 || state_out))
     return fail(LL_ERR_UNSUPPORTED, "reusing block states is only for a plain Mamba-2 read");
   Plan pl;
@@ -287,9 +317,19 @@ ll_status run_prefill(const ll_problem* p, int64_t pos0, const float* state_in, 
   if (!o && !state_out) return fail(LL_ERR_NULL, "o and state_out are both NULL: nothing to compute");
   if (o && (!q || !lambda)) return fail(LL_ERR_NULL, "q and lambda must not be NULL when o is requested");
   if (p->rule == LL_GATED_DELTANET && !beta) return fail(LL_ERR_NULL, "beta must not be NULL for Gated DeltaNet");
-  if (workspace_bytes < pl.bytes)
-    return fail(LL_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, pl.bytes);
-  if (pl.bytes > 0 && !workspace) return fail(LL_ERR_WORKSPACE, "workspace is NULL");
+  if (noalloc) {
+    if (pl.bytes > LL_NOALLOC_SCRATCH_BYTES)
+      return fail(LL_ERR_WORKSPACE, "this problem needs %zu bytes of workspace; the allocation-free prefill has %zu",
+                  pl.bytes, (size_t)LL_NOALLOC_SCRATCH_BYTES);
+    // validation is over: only now touch the device, for the scratch address
+    st = scratch_of_current_device(&workspace);
+    if (st != LL_OK) return st;
+  } else {
+    if (workspace_bytes < pl.bytes)
+      return fail(LL_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes,
+                  pl.bytes);
+    if (pl.bytes > 0 && !workspace) return fail(LL_ERR_WORKSPACE, "workspace is NULL");
+  }
 
   char* ws = static_cast<char*>(workspace);
   PrefillArgs a;
@@ -360,6 +400,11 @@ ll_status ll_attn_fwd(const ll_problem* p, const void* q, const void* k, const v
                       const float* lambda, const float* beta, void* o, void* state_out, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
   return run_prefill(p, 0, nullptr, q, k, v, log_gate, lambda, beta, o, state_out, workspace, workspace_bytes, stream);
+}
+
+ll_status ll_attn_fwd_noalloc(const ll_problem* p, const void* q, const void* k, const void* v, const float* log_gate,
+                              const float* lambda, const float* beta, void* o, void* state_out, hipStream_t stream) {
+  return run_prefill(p, 0, nullptr, q, k, v, log_gate, lambda, beta, o, state_out, nullptr, 0, stream, false, true);
 }
 
 ll_status ll_attn_fwd_from_state(const ll_problem* p, int64_t pos0, const float* state_in, const void* q,

@@ -120,6 +120,32 @@ ll_status ll_attn_fwd(const ll_problem* p, const void* q, const void* k, const v
                       hipStream_t stream);
 
 /*
+ * ll_attn_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and arguments without the workspace, which comes from a
+ * scratch array inside the library instead.
+ *   - The array holds LL_NOALLOC_SCRATCH_BYTES (64 MiB); a problem whose
+ *     ll_attn_fwd_workspace_bytes exceeds it is rejected with
+ *     LL_ERR_WORKSPACE before anything is enqueued.  64 MiB covers the
+ *     LL_MAMBA2 prefill of 2 x 16 heads x 16384 tokens at dk = dv = 64
+ *     (25 MB); the LL_GATED_DELTANET row buffers rarely fit.
+ *   - Each GPU the library runs on holds its own copy of the array from the
+ *     first call made with it current until the process ends; that first
+ *     call also looks up the array's device address.
+ *   - No part of the scratch needs to start at zero: every call writes all
+ *     of it that it reads.  Nothing is allocated or freed by any call.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (on different streams, or from several threads without
+ *     ordering) race on it and give undefined results.  Calls in one stream
+ *     are ordered and safe.
+ * The caller still owns and passes every input and output.
+ */
+#define LL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ll_status ll_attn_fwd_noalloc(const ll_problem* p, const void* q, const void* k, const void* v,
+                              const float* log_gate, const float* lambda, const float* beta, void* o,
+                              void* state_out, hipStream_t stream);
+
+/*
  * Prefill of a segment that continues a sequence (section 2.2 and 2.3: the
  * buckets of positions before the segment are carried as per-level states),
  * for chunked prefill: tokens pos0 .. pos0 + T - 1, with the per-level

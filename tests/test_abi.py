@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["ll_attn_bwd", "ll_attn_bwd_workspace_bytes", "ll_attn_fwd", "ll_attn_fwd_from_state", "ll_attn_fwd_workspace_bytes", "ll_ccq_query",
+        ["ll_attn_bwd", "ll_attn_bwd_workspace_bytes", "ll_attn_fwd", "ll_attn_fwd_from_state", "ll_attn_fwd_noalloc", "ll_attn_fwd_workspace_bytes", "ll_ccq_query",
          "ll_ccq_query_workspace_bytes", "ll_decode_state_bytes", "ll_decode_step", "ll_decode_step_ragged",
          "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp", "ll_last_error"])
 
@@ -263,3 +263,21 @@ def test_bwd_validation_before_any_launch():
     assert call(prob(T=2048, L=12), dlam=None) == "LL_ERR_NULL"
     assert call(prob(T=2048, L=12), wsb=n - 1) == "LL_ERR_WORKSPACE"
     assert call(prob(T=2048, L=12), ws=None) == "LL_ERR_WORKSPACE"
+
+
+def test_noalloc_validation_before_any_launch():
+    """The allocation-free prefill validates like ll_attn_fwd, and rejects a
+    problem whose workspace exceeds its 64 MiB scratch before touching the GPU."""
+    d = DUMMY
+    args = (d, d, d, d, d, None, d, None)
+    big = prob(B=8)  # 8 x 16 heads x 16384 tokens: 100 MB of block states and nodes
+    assert F.ll_attn_fwd_workspace_bytes(prob()) <= 64 << 20
+    assert F.ll_attn_fwd_workspace_bytes(big) > 64 << 20
+    name, msg = status_of(F.ll_attn_fwd_noalloc, big, *args)
+    assert name == "LL_ERR_WORKSPACE" and "allocation-free" in msg
+    gdn = prob(T=8192, L=14, dk=128, dv=128, rule=F.LL_GATED_DELTANET)
+    assert status_of(F.ll_attn_fwd_noalloc, gdn, d, d, d, d, d, d, d, None)[0] == "LL_ERR_WORKSPACE"
+    assert status_of(F.ll_attn_fwd_noalloc, prob(C=48), *args)[0] == "LL_ERR_SHAPE"
+    assert status_of(F.ll_attn_fwd_noalloc, prob(), d, None, d, d, d, None, d, None)[0] == "LL_ERR_NULL"
+    assert status_of(F.ll_attn_fwd_noalloc, None, *args)[0] == "LL_ERR_NULL"
+    assert status_of(F.ll_attn_fwd_noalloc, prob(rule=F.LL_GATED_DELTANET), *args)[0] == "LL_ERR_NULL"
