@@ -77,9 +77,23 @@ def cpu_baseline(w, min_seconds: float = 10.0) -> dict:
     import oracle
     from fenwick_tree_linear_amd import workloads as W
 
+    import platform
+    import tempfile
+
     x = W.prefill_inputs(w)
     np_in = {k: (None if v is None else v.float().numpy()) for k, v in x.items()}
-    lib = oracle.load()
+    # a copy of the oracle built for this host's own instruction set
+    tmpdir = tempfile.mkdtemp(prefix="llref_native_")
+    lib = oracle.load(oracle.build(os.path.join(tmpdir, "libllref_native.so"), opt_flags=("-O3", "-march=native")))
+    cpu_model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     runs, dt = 0, 0.0
     while dt < min_seconds:
         t0 = time.perf_counter()
@@ -89,7 +103,9 @@ def cpu_baseline(w, min_seconds: float = 10.0) -> dict:
     cores = min(oracle.threads(lib), w.B * w.H)
     return {"value": runs * w.B * w.T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"recurrent O(T log T) form over the whole workload ({w.B} x {w.H} heads x {w.T} tokens), "
-                      f"fp64, {runs} runs in {dt:.1f} s"}
+                      f"fp64, {runs} runs in {dt:.1f} s",
+            "build": "gcc -O3 -march=native -std=c11 -fopenmp", "cpu_model": cpu_model, "nproc": os.cpu_count(),
+            "omp_threads": oracle.threads(lib)}
 
 
 def decode_bench(steps: int) -> dict:

@@ -100,6 +100,81 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
+_IO_DTYPES = {LL_F32: torch.float32, LL_BF16: torch.bfloat16}
+
+
+def _io_dtype(io: int):
+    return _IO_DTYPES.get(io)  # None for an unknown code: the library reports LL_ERR_DTYPE
+
+
+def _validate(*specs) -> None:
+    """Checks every tensor argument against the ABI's layout before the library
+    is called: the C ABI sees only pointers, so a host tensor, a tensor on
+    another device, a wrong dtype or a short buffer would otherwise reach a
+    kernel.  Each spec is (name, tensor, element count, dtype); plain integers
+    (raw device addresses) and None pass through unchecked (the library checks
+    NULLs).  A count or dtype of None is not checked."""
+    tensors = []
+    for name, t, numel, dtype in specs:  # layout first, then where the memory is
+        if t is None or isinstance(t, int):
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor or a device address, got {type(t).__name__}")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if numel is not None and t.numel() != numel:
+            raise ValueError(f"{name} must hold {numel} elements for this problem, got {t.numel()} "
+                             f"(shape {tuple(t.shape)})")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        tensors.append((name, t))
+    device = None
+    for name, t in tensors:
+        if not t.is_cuda:
+            raise ValueError(f"{name} is on {t.device}: libllattn takes device memory only")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"{name} is on {t.device}, other arguments on {device}")
+    if device is not None and device.index is not None and device.index != torch.cuda.current_device():
+        raise ValueError(f"arguments are on {device} but the current device is cuda:{torch.cuda.current_device()}")
+
+
+def _workspace_spec(workspace, workspace_bytes: int):
+    if isinstance(workspace, torch.Tensor) and workspace.numel() * workspace.element_size() < workspace_bytes:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                         f"fewer than the {workspace_bytes} passed as its size")
+    return ("workspace", workspace, None, None)
+
+
+def _state_elems(B: int, H: int, dk: int, dv: int, L: int) -> int:
+    # S_hat [B,H,L,dk,dv] then sigma [B,H,L], fp32 (ll_decode_state_bytes / 4)
+    return B * H * L * (dk * dv + 1)
+
+
+def _prefill_specs(p: LLProblem, q, k, v, log_gate, lam, beta, o):
+    if p is None:
+        return []
+    io = _io_dtype(p.io)
+    rows = p.B * p.T * p.H
+    specs = [("q", q, rows * p.dk, io), ("k", k, rows * p.dk, io), ("v", v, rows * p.dv, io),
+             ("log_gate", log_gate, rows, torch.float32), ("lambda", lam, rows * p.L, torch.float32),
+             ("o", o, rows * p.dv, io)]
+    if p.rule == LL_GATED_DELTANET:
+        specs.append(("beta", beta, rows, torch.float32))
+    return specs
+
+
+def _decode_specs(B, H, dk, dv, L, io, rule, q, k, v, log_gate, lam, beta, o, state):
+    dt = _io_dtype(io)
+    specs = [("q", q, B * H * dk, dt), ("k", k, B * H * dk, dt), ("v", v, B * H * dv, dt),
+             ("log_gate", log_gate, B * H, torch.float32), ("lambda", lam, B * H * L, torch.float32),
+             ("o", o, B * H * dv, dt), ("state", state, _state_elems(B, H, dk, dv, L), torch.float32)]
+    if rule == LL_GATED_DELTANET:
+        specs.append(("beta", beta, B * H, torch.float32))
+    return specs
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
@@ -114,12 +189,19 @@ def ll_attn_fwd_workspace_bytes(problem: LLProblem) -> int:
 
 def ll_attn_fwd(problem: LLProblem, q, k, v, log_gate, lam, beta, o, state_out, workspace, workspace_bytes: int,
                 stream=None) -> None:
+    p = problem
+    _validate(*_prefill_specs(p, q, k, v, log_gate, lam, beta, o),
+              *([("state_out", state_out, _state_elems(p.B, p.H, p.dk, p.dv, p.L), torch.float32)] if p else []),
+              _workspace_spec(workspace, workspace_bytes))
     _check(load_library().ll_attn_fwd(None if problem is None else ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate), _ptr(lam),
                                       _ptr(beta), _ptr(o), _ptr(state_out), _ptr(workspace), workspace_bytes,
                                       _stream(stream)))
 
 
 def ll_attn_fwd_noalloc(problem: LLProblem, q, k, v, log_gate, lam, beta, o, state_out, stream=None) -> None:
+    p = problem
+    _validate(*_prefill_specs(p, q, k, v, log_gate, lam, beta, o),
+              *([("state_out", state_out, _state_elems(p.B, p.H, p.dk, p.dv, p.L), torch.float32)] if p else []))
     _check(load_library().ll_attn_fwd_noalloc(None if problem is None else ctypes.byref(problem), _ptr(q), _ptr(k),
                                               _ptr(v), _ptr(log_gate), _ptr(lam), _ptr(beta), _ptr(o),
                                               _ptr(state_out), _stream(stream)))
@@ -127,6 +209,12 @@ def ll_attn_fwd_noalloc(problem: LLProblem, q, k, v, log_gate, lam, beta, o, sta
 
 def ll_attn_fwd_from_state(problem: LLProblem, pos0: int, state_in, q, k, v, log_gate, lam, beta, o, state_out,
                            workspace, workspace_bytes: int, stream=None) -> None:
+    p = problem
+    n_state = _state_elems(p.B, p.H, p.dk, p.dv, p.L) if p else None
+    _validate(*_prefill_specs(p, q, k, v, log_gate, lam, beta, o),
+              *([("state_in", state_in, n_state, torch.float32), ("state_out", state_out, n_state, torch.float32)]
+                if p else []),
+              _workspace_spec(workspace, workspace_bytes))
     _check(load_library().ll_attn_fwd_from_state(None if problem is None else ctypes.byref(problem), pos0,
                                                  _ptr(state_in), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
                                                  _ptr(lam), _ptr(beta), _ptr(o), _ptr(state_out), _ptr(workspace),
@@ -140,11 +228,15 @@ def ll_decode_state_bytes(B: int, H: int, dk: int, dv: int, L: int) -> int:
 
 
 def ll_decode_step(B, H, dk, dv, L, io, rule, pos, q, k, v, log_gate, lam, beta, o, state, stream=None) -> None:
+    _validate(*_decode_specs(B, H, dk, dv, L, io, rule, q, k, v, log_gate, lam, beta, o, state))
     _check(load_library().ll_decode_step(B, H, dk, dv, L, io, rule, pos, _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
                                          _ptr(lam), _ptr(beta), _ptr(o), _ptr(state), _stream(stream)))
 
 
 def ll_lambda_mlp(rows: int, L: int, hidden: int, d, w1, w2, bias, lam, stream=None) -> None:
+    f32 = torch.float32
+    _validate(("d", d, rows * L, f32), ("w1", w1, L * hidden, f32), ("w2", w2, hidden * L, f32),
+              ("bias", bias, L, f32), ("lambda", lam, rows * L, f32))
     _check(load_library().ll_lambda_mlp(rows, L, hidden, _ptr(d), _ptr(w1), _ptr(w2), _ptr(bias), _ptr(lam),
                                         _stream(stream)))
 
@@ -152,8 +244,8 @@ def ll_lambda_mlp(rows: int, L: int, hidden: int, d, w1, w2, bias, lam, stream=N
 def ll_decode_step_ragged(B, H, dk, dv, L, io, rule, pos, q, k, v, log_gate, lam, beta, o, state,
                           stream=None) -> None:
     """``pos``: int64 device tensor [B], one position per sequence."""
-    if isinstance(pos, torch.Tensor) and pos.dtype != torch.int64:
-        raise TypeError("pos must be an int64 tensor")
+    _validate(("pos", pos, B, torch.int64), *_decode_specs(B, H, dk, dv, L, io, rule, q, k, v, log_gate, lam, beta,
+                                                           o, state))
     _check(load_library().ll_decode_step_ragged(B, H, dk, dv, L, io, rule, _ptr(pos), _ptr(q), _ptr(k), _ptr(v),
                                                 _ptr(log_gate), _ptr(lam), _ptr(beta), _ptr(o), _ptr(state),
                                                 _stream(stream)))
@@ -166,6 +258,9 @@ def ll_ccq_query_workspace_bytes(B: int, T: int, H: int, dk: int, io: int) -> in
 
 
 def ll_ccq_query(B, T, H, dk, io, q, k, w, b, q_clean, workspace, workspace_bytes: int, stream=None) -> None:
+    dt, n = _io_dtype(io), B * T * H * dk
+    _validate(("q", q, n, dt), ("k", k, n, dt), ("w", w, H * dk, torch.float32), ("b", b, H, torch.float32),
+              ("q_clean", q_clean, n, dt), _workspace_spec(workspace, workspace_bytes))
     _check(load_library().ll_ccq_query(B, T, H, dk, io, _ptr(q), _ptr(k), _ptr(w), _ptr(b), _ptr(q_clean),
                                        _ptr(workspace), workspace_bytes, _stream(stream)))
 
@@ -178,6 +273,13 @@ def ll_attn_bwd_workspace_bytes(problem: LLProblem) -> int:
 
 def ll_attn_bwd(problem: LLProblem, q, k, v, log_gate, lam, o, dO, dq, dk, dv, dlog_gate, dlam, workspace,
                 workspace_bytes: int, stream=None) -> None:
+    p = problem
+    if p is not None:
+        io, rows, f32 = _io_dtype(p.io), p.B * p.T * p.H, torch.float32
+        _validate(*_prefill_specs(p, q, k, v, log_gate, lam, None, o), ("dO", dO, rows * p.dv, io),
+                  ("dq", dq, rows * p.dk, io), ("dk", dk, rows * p.dk, io), ("dv", dv, rows * p.dv, io),
+                  ("dlog_gate", dlog_gate, rows, f32), ("dlambda", dlam, rows * p.L, f32),
+                  _workspace_spec(workspace, workspace_bytes))
     _check(load_library().ll_attn_bwd(None if problem is None else ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v),
                                       _ptr(log_gate), _ptr(lam), _ptr(o), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
                                       _ptr(dlog_gate), _ptr(dlam), _ptr(workspace), workspace_bytes,

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -154,7 +155,7 @@ const char* const kKernelNames[K_COUNT] = {"ll_chunk_state", "ll_fenwick_scan", 
 
 struct Timing {
   std::mutex mu;
-  bool on = false;
+  std::atomic<bool> on{false};  // read without the lock on every launch
   std::vector<hipEvent_t> pool;  // free events
   struct Pending {
     int kernel;
@@ -180,9 +181,9 @@ hipEvent_t take_event() {
 // Launches one kernel through `fn`, bracketed by events when timing is on.
 template <typename Fn>
 hipError_t timed(int kernel, hipStream_t stream, Fn fn) {
-  std::unique_lock<std::mutex> lock(g_timing.mu, std::defer_lock);
-  if (g_timing.on) lock.lock();
-  if (!g_timing.on) return fn();
+  if (!g_timing.on.load(std::memory_order_acquire)) return fn();
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  if (!g_timing.on.load(std::memory_order_relaxed)) return fn();  // switched off meanwhile
   hipEvent_t a = take_event(), b = take_event();
   if (!a || !b) return fn();
   if (hipEventRecord(a, stream) != hipSuccess) {  // no timing for this launch
@@ -206,7 +207,7 @@ extern "C" {
 
 ll_status ll_kernel_timing_enable(int on) {
   std::lock_guard<std::mutex> lock(g_timing.mu);
-  g_timing.on = on != 0;
+  g_timing.on.store(on != 0, std::memory_order_release);
   return ok();
 }
 

@@ -281,3 +281,80 @@ def test_noalloc_validation_before_any_launch():
     assert status_of(F.ll_attn_fwd_noalloc, prob(), d, None, d, d, d, None, d, None)[0] == "LL_ERR_NULL"
     assert status_of(F.ll_attn_fwd_noalloc, None, *args)[0] == "LL_ERR_NULL"
     assert status_of(F.ll_attn_fwd_noalloc, prob(rule=F.LL_GATED_DELTANET), *args)[0] == "LL_ERR_NULL"
+
+
+# ------------------------------------------------ binding argument checks
+
+@pytest.fixture
+def no_library(monkeypatch):
+    """Any call that reaches the library fails the test: the binding's checks
+    must raise first."""
+    from fenwick_tree_linear_amd import binding
+
+    def refuse():
+        raise AssertionError("the library was called")
+
+    monkeypatch.setattr(binding, "load_library", refuse)
+
+
+def _prefill_tensors(p, io=None):
+    import torch
+
+    dt = io or (torch.bfloat16 if p.io == F.LL_BF16 else torch.float32)
+    rows = (p.B, p.T, p.H)
+    return dict(q=torch.zeros(*rows, p.dk, dtype=dt), k=torch.zeros(*rows, p.dk, dtype=dt),
+                v=torch.zeros(*rows, p.dv, dtype=dt), log_gate=torch.zeros(*rows), lam=torch.zeros(*rows, p.L),
+                beta=torch.zeros(*rows), o=torch.zeros(*rows, p.dv, dtype=dt))
+
+
+def test_binding_rejects_host_tensors(no_library):
+    import torch
+
+    p = prob(B=1, T=256, H=2, L=9)
+    x = _prefill_tensors(p)
+    with pytest.raises(ValueError, match="device memory only"):
+        F.ll_attn_fwd(p, x["q"], x["k"], x["v"], x["log_gate"], x["lam"], None, x["o"], None, DUMMY, 0)
+    with pytest.raises(ValueError, match="device memory only"):
+        F.ll_attn_fwd_noalloc(p, x["q"], x["k"], x["v"], x["log_gate"], x["lam"], None, x["o"], None)
+    # the int64 positions of the ragged decode step, on the host
+    with pytest.raises(ValueError, match="device memory only"):
+        F.ll_decode_step_ragged(2, 2, 64, 64, 9, F.LL_BF16, F.LL_MAMBA2, torch.zeros(2, dtype=torch.int64),
+                                DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, None, DUMMY, DUMMY)
+
+
+def test_binding_rejects_wrong_dtypes_and_sizes(no_library):
+    import torch
+
+    p = prob(B=1, T=256, H=2, L=9)
+    x = _prefill_tensors(p)
+    args = lambda **kw: [kw.get(n, x[n]) for n in ("q", "k", "v", "log_gate", "lam")]
+    # q in another dtype than the problem's io
+    with pytest.raises(TypeError, match="q must be torch.bfloat16"):
+        F.ll_attn_fwd(p, *args(q=x["q"].float()), None, x["o"], None, DUMMY, 0)
+    # lambda with one level too few, a short gate, an fp32 o for bf16 io
+    with pytest.raises(ValueError, match="lambda must hold"):
+        F.ll_attn_fwd(p, *args(lam=x["lam"][..., :-1].contiguous()), None, x["o"], None, DUMMY, 0)
+    with pytest.raises(ValueError, match="log_gate must hold"):
+        F.ll_attn_fwd(p, *args(log_gate=x["log_gate"][:, :-1].contiguous()), None, x["o"], None, DUMMY, 0)
+    with pytest.raises(TypeError, match="o must be"):
+        F.ll_attn_fwd(p, *args(), None, x["o"].float(), None, DUMMY, 0)
+    # the Gated DeltaNet write strength, short
+    g = prob(B=1, T=256, H=2, L=9, rule=F.LL_GATED_DELTANET)
+    with pytest.raises(ValueError, match="beta must hold"):
+        F.ll_attn_fwd(g, *args(), x["beta"][:, :-1].contiguous(), x["o"], None, DUMMY, 0)
+    # a state buffer of the wrong size, a workspace smaller than the size passed
+    with pytest.raises(ValueError, match="state_out must hold"):
+        F.ll_attn_fwd(p, *args(), None, x["o"], torch.zeros(10), DUMMY, 0)
+    with pytest.raises(ValueError, match="workspace holds"):
+        F.ll_attn_fwd(p, *args(), None, x["o"], None, torch.zeros(16, dtype=torch.uint8), 1 << 20)
+    # decode: a short state, a pos of the wrong dtype
+    with pytest.raises(ValueError, match="state must hold"):
+        F.ll_decode_step(2, 2, 64, 64, 9, F.LL_BF16, F.LL_MAMBA2, 5, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, None,
+                         DUMMY, torch.zeros(100))
+    with pytest.raises(TypeError, match="pos must be torch.int64"):
+        F.ll_decode_step_ragged(2, 2, 64, 64, 9, F.LL_BF16, F.LL_MAMBA2, torch.zeros(2, dtype=torch.int32),
+                                DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, None, DUMMY, DUMMY)
+    # the level-weight MLP with a transposed-size W2 buffer
+    with pytest.raises(ValueError, match="w2 must hold"):
+        F.ll_lambda_mlp(4, 15, 30, torch.zeros(4, 15), torch.zeros(15, 30), torch.zeros(29, 15), torch.zeros(15),
+                        torch.zeros(4, 15))
