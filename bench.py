@@ -108,7 +108,7 @@ def cpu_baseline(w, min_seconds: float = 10.0) -> dict:
             "omp_threads": oracle.threads(lib)}
 
 
-def decode_bench(steps: int) -> dict:
+def decode_bench(steps: int, cold_reps: int = 10) -> dict:
     """ll_decode_step on the decode workload (B64 H16 d64 bf16, 17 levels): ``steps`` tokens at
     positions 32768.. from a resident per-level state (random values; the step's cost does not
     depend on them), one launch per token, timed with HIP events on the launch stream."""
@@ -144,14 +144,38 @@ def decode_bench(steps: int) -> dict:
     us = start.elapsed_time(stop) * 1e3 / steps
     mask = (1 << (w.L - 1)) - 1
     level_bytes = w.dk * w.dv * 4
-    per_head = sum((bin((w.T + i) & mask).count("1") + 1) * level_bytes for i in range(steps)) / steps
     io_bytes = (4 * w.dk * 2 + 4 + 2 * w.L * 4)  # q, k, v, o; gate; lambda; sigma read + written
-    bytes_per_step = w.B * w.H * (per_head + io_bytes)
+
+    def step_bytes(pos):  # the non-empty levels read, the merged level written, the token's I/O
+        return w.B * w.H * ((bin(pos & mask).count("1") + 1) * level_bytes + io_bytes)
+
+    bytes_per_step = sum(step_bytes(w.T + i) for i in range(steps)) / steps
     achieved = bytes_per_step / (us * 1e-6) / 1e9
-    return {"workload": "ll_decode_step B64 H16 d64 bf16, 17 levels, positions 32768.." + str(w.T + steps - 1),
-            "us_per_step": round(us, 2), "tokens_per_s": round(w.B / (us * 1e-6), 1),
-            "bytes_per_step": int(bytes_per_step), "achieved_GBs": round(achieved, 1), "peak_GBs": HBM_PEAK_GBS,
-            "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    # cold: single steps, each after a 512 MiB write that leaves none of the state in the
+    # 256 MB last-level cache (median of ``cold_reps``; positions continue where the run above ended)
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    cold = []
+    for r in range(cold_reps):
+        flush.fill_(float(r))
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_ev.record(stream)
+        step(w.T + steps + r)
+        b_ev.record(stream)
+        torch.cuda.synchronize()
+        cold.append((a_ev.elapsed_time(b_ev) * 1e3, step_bytes(w.T + steps + r)))
+    del flush
+    out = {"workload": "ll_decode_step B64 H16 d64 bf16, 17 levels, positions 32768.." + str(w.T + steps - 1),
+           "us_per_step": round(us, 2), "tokens_per_s": round(w.B / (us * 1e-6), 1),
+           "bytes_per_step": int(bytes_per_step), "achieved_GBs": round(achieved, 1), "peak_GBs": HBM_PEAK_GBS,
+           "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    if cold:
+        cold.sort()
+        c_us, c_bytes = cold[len(cold) // 2]
+        out["cold"] = {"us_per_step_median": round(c_us, 2), "bytes": int(c_bytes),
+                       "achieved_GBs": round(c_bytes / (c_us * 1e-6) / 1e9, 1),
+                       "frac": round(c_bytes / (c_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "reps": len(cold),
+                       "note": "one step after a 512 MiB write; includes the launch of a lone kernel"}
+    return out
 
 
 def ragged_decode_bench(steps: int) -> dict:
@@ -514,14 +538,26 @@ def gdn_bench(steps: int) -> dict:
     return {"workload": "gated-deltanet prefill B2 H16 T8192 dk=dv=128 bf16, 14 levels, chunk 64",
             "ms_per_step": round(ms, 5), "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
             "kernels_us": {name: round(t / n * 1e3, 2) for name, (t, n) in kt.items()},
-            "hbm": gdn_hbm_fractions(w, kt)}
+            "algorithmic_bytes": gdn_algorithmic_bytes(w),
+            "algorithmic_frac": round(gdn_algorithmic_bytes(w) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel_io": gdn_hbm_fractions(w, kt)}
+
+
+def gdn_algorithmic_bytes(w) -> int:
+    """Compulsory HBM traffic of the Gated DeltaNet prefill: q, k, v read and o written (bf16), the
+    gate, beta and the level weights read (fp32)."""
+    rows = w.B * w.T * w.H
+    return rows * (2 * w.dk + 2 * w.dv) * 2 + rows * (w.L + 2) * 4
 
 
 def gdn_hbm_fractions(w, kt) -> dict:
-    """Algorithmic HBM bytes of each Gated DeltaNet prefill kernel on this workload and the rate
-    they give at the kernel's measured average time, as a fraction of the 8 TB/s peak.  The read
-    runs at chunk 32 (the bf16 d = 128 tile) in blocks of 8 chunks; its bytes count q, k, U, the
-    level weights, gates and o, not the re-reads of earlier blocks' nodes."""
+    """Kernel I/O bytes of each Gated DeltaNet prefill kernel on this workload (what each kernel of
+    this design must read and write, including the design's own intermediates W, U', U, the block
+    states and the Fenwick nodes, but not the bf16 node copies or re-reads of earlier blocks' nodes)
+    and the rate they give at the kernel's measured average time, as a fraction of the 8 TB/s peak.
+    These are not the step's algorithmic bytes: those are the compulsory inputs and outputs (q, k, v,
+    gates, beta, lambda read, o written), reported beside them.  The read runs at chunk 32 (the bf16
+    d = 128 tile) in blocks of 8 chunks."""
     rows = w.B * w.T * w.H
     rb = w.dk * 2  # one bf16 row
     nb = w.T // (32 * 8)  # blocks per head
@@ -531,7 +567,7 @@ def gdn_hbm_fractions(w, kt) -> dict:
         "ll_gdn_wy": 4 * rows * rb + 2 * rows * 4,            # k, v, gates, beta in; W, U' out
         "ll_gdn_state": 4 * rows * rb + rows * 4,             # W, k, U', gates in; U out
         "ll_chunk_state": 2 * rows * rb + rows * 4 + heads * nb * node,  # k, U, gates in; block states out
-        "ll_fenwick_scan": heads * nb * node + heads * (nb // 2) * node + heads * nb * node // 2,
+        "ll_fenwick_scan": heads * nb * node + heads * (nb // 2) * node,  # block states read, nodes written
         "ll_chunk_attn": 4 * rows * rb + rows * (w.L + 1) * 4,  # q, k, U, lambda, gates in; o out
     }
     out = {}
@@ -651,6 +687,13 @@ def main() -> int:
 
     token_heads = w.B * w.T * w.H
     alg_bytes = algorithmic_bytes_per_token_head(w) * token_heads
+    # ll_fenwick_scan: the block states it must read and the level >= 1 nodes it writes
+    # (blocks of 8 chunks: 32 per head, 16 nodes; 64 x 64 fp32 each)
+    nb = w.T // (w.C * 8)
+    scan_bytes = w.B * w.H * (nb + nb // 2) * w.dk * w.dv * 4
+    t_scan = kt["ll_fenwick_scan"][0] / kt["ll_fenwick_scan"][1] * 1e-3
+    scan = {"bytes": scan_bytes, "us": round(t_scan * 1e6, 2), "achieved_GBs": round(scan_bytes / t_scan / 1e9, 1),
+            "frac": round(scan_bytes / t_scan / 1e9 / HBM_PEAK_GBS, 4)}
     t_attn = kt["ll_chunk_attn"][0] / kt["ll_chunk_attn"][1] * 1e-3
     achieved = alg_bytes / t_attn / 1e9
     flops = useful_flops_per_token_head(w) * token_heads
@@ -680,11 +723,12 @@ def main() -> int:
                  "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                  "frac_step": round(flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
         "kernels_us": kernels,
+        "scan": scan,
         "cold": cold,
         "cpu_baseline": None,
     }
     if args.decode_steps:
-        result["decode"] = decode_bench(args.decode_steps)
+        result["decode"] = decode_bench(args.decode_steps, args.cold_reps)
         log(f"[bench] decode: {result['decode']}")
     if args.gdn_steps:
         result["gdn"] = gdn_bench(args.gdn_steps)

@@ -3,6 +3,7 @@
 // check runs before the first HIP call, so a rejected call enqueues nothing.
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include <atomic>
 #include <mutex>
@@ -45,6 +46,17 @@ int bit_length(int64_t x) {
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// Enum arguments arrive from C callers as plain ints and may hold any value;
+// they are read as ints, so that checking an out-of-range value is defined
+// behaviour (loading it through the enum type would not be, in C++).
+template <typename E>
+int enum_value(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "the ABI's enums are int-sized");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 // bf16 matrix-core steps contract 32 values: bf16 needs d >= 32 and C >= 32
 bool supported_head(int d, ll_dtype io) {
   if (io == LL_BF16) return d == 32 || d == 64 || d == 128;
@@ -71,9 +83,9 @@ struct Plan {
 // Validates a prefill problem and derives the block decomposition.
 ll_status plan_prefill(const ll_problem* p, bool exporting, Plan* out) {
   if (!p) return fail(LL_ERR_NULL, "problem is NULL");
-  if (p->io != LL_F32 && p->io != LL_BF16) return fail(LL_ERR_DTYPE, "unknown io dtype %d", (int)p->io);
-  if (p->rule != LL_MAMBA2 && p->rule != LL_GATED_DELTANET)
-    return fail(LL_ERR_UNSUPPORTED, "unknown rule %d", (int)p->rule);
+  const int io_v = enum_value(p->io), rule_v = enum_value(p->rule);
+  if (io_v != LL_F32 && io_v != LL_BF16) return fail(LL_ERR_DTYPE, "unknown io dtype %d", io_v);
+  if (rule_v != LL_MAMBA2 && rule_v != LL_GATED_DELTANET) return fail(LL_ERR_UNSUPPORTED, "unknown rule %d", rule_v);
   if (p->B < 1 || p->T < 1 || p->H < 1 || p->dk < 1 || p->dv < 1 || p->L < 1 || p->C < 1)
     return fail(LL_ERR_SHAPE, "sizes must be positive (B=%d T=%d H=%d dk=%d dv=%d L=%d C=%d)", p->B, p->T, p->H,
                 p->dk, p->dv, p->L, p->C);
@@ -185,7 +197,11 @@ hipError_t timed(int kernel, hipStream_t stream, Fn fn) {
   std::lock_guard<std::mutex> lock(g_timing.mu);
   if (!g_timing.on.load(std::memory_order_relaxed)) return fn();  // switched off meanwhile
   hipEvent_t a = take_event(), b = take_event();
-  if (!a || !b) return fn();
+  if (!a || !b) {  // no timing for this launch; keep whichever event was made
+    if (a) g_timing.pool.push_back(a);
+    if (b) g_timing.pool.push_back(b);
+    return fn();
+  }
   if (hipEventRecord(a, stream) != hipSuccess) {  // no timing for this launch
     g_timing.pool.push_back(a);
     g_timing.pool.push_back(b);
@@ -430,8 +446,9 @@ namespace {
 ll_status check_decode(int B, int H, int dk, int dv, int L, ll_dtype io, ll_rule rule, const void* q, const void* k,
                        const void* v, const float* log_gate, const float* lambda, const float* beta, void* o,
                        void* state) {
-  if (io != LL_F32 && io != LL_BF16) return fail(LL_ERR_DTYPE, "unknown io dtype %d", (int)io);
-  if (rule != LL_MAMBA2 && rule != LL_GATED_DELTANET) return fail(LL_ERR_UNSUPPORTED, "unknown rule %d", (int)rule);
+  const int io_v = enum_value(io), rule_v = enum_value(rule);
+  if (io_v != LL_F32 && io_v != LL_BF16) return fail(LL_ERR_DTYPE, "unknown io dtype %d", io_v);
+  if (rule_v != LL_MAMBA2 && rule_v != LL_GATED_DELTANET) return fail(LL_ERR_UNSUPPORTED, "unknown rule %d", rule_v);
   if (B < 1 || H < 1 || dk < 1 || dv < 1 || L < 2)
     return fail(LL_ERR_SHAPE, "sizes must be positive and L >= 2 (B=%d H=%d dk=%d dv=%d L=%d)", B, H, dk, dv, L);
   if (L > 32) return fail(LL_ERR_UNSUPPORTED, "L=%d: at most 32 decode levels are supported", L);
@@ -516,7 +533,8 @@ struct CcqPlan {
 };
 
 ll_status plan_ccq(int B, int T, int H, int dk, ll_dtype io, CcqPlan* out) {
-  if (io != LL_F32 && io != LL_BF16) return fail(LL_ERR_DTYPE, "unknown io dtype %d", (int)io);
+  const int io_v = enum_value(io);
+  if (io_v != LL_F32 && io_v != LL_BF16) return fail(LL_ERR_DTYPE, "unknown io dtype %d", io_v);
   if (B < 1 || T < 1 || H < 1 || dk < 1)
     return fail(LL_ERR_SHAPE, "sizes must be positive (B=%d T=%d H=%d dk=%d)", B, T, H, dk);
   if (!supported_head(dk, io))

@@ -169,6 +169,9 @@ ll_status ll_attn_fwd_from_state(const ll_problem* p, int64_t pos0, const float*
                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Size of the state the recurrent form carries between tokens ("Log-Linear
+ * Attention", section 2.3, "inference": one hidden state per Fenwick level,
+ * O(log T) of them, each dk x dv).
  * Bytes of one decode state: S_hat [B,H,L,dk,dv] fp32 followed by
  * sigma [B,H,L] fp32.  The true per-level state is exp(sigma_l) * S_hat_l
  * (the log-scale carries the decay lazily).  Level l >= 1 holds the bucket of
