@@ -17,9 +17,9 @@
 //
 // ll_gdn_wy    : one workgroup per (chunk, head): L on MFMA, (I + L)^-1 by
 //                16x16 blocks on fp32 MFMA, then U' and W as MFMA products.
-// ll_gdn_state : one workgroup per (head, 16 state columns): the serial pass
-//                over the chunks, U = U' - W S_i and the state update on MFMA,
-//                writing the pseudo-values U.
+// ll_gdn_state : the serial pass over the chunks, one wave per 16 state
+//                columns holding them in registers: U = U' - W S_i and the
+//                state update on MFMA, writing the pseudo-values U.
 #include <type_traits>
 
 #include "ll_device.hpp"
@@ -260,62 +260,217 @@ __global__ void __launch_bounds__(256) ll_gdn_wy(GdnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// ll_gdn_state: the serial pass over the chunks of a head.  Each wave owns 16
+// state columns for the whole pass, with all D rows of its columns of S in
+// registers (fp32, accumulator layout), and computes per chunk
+//   U    = U' - W S_i                     (C x 16, on MFMA: W from LDS, S_i
+//                                          from its own accumulator tiles)
+//   S_{i+1} = e^{g} S_i + K^T diag(e^{g - G}) U   (D x 16: K from LDS, U from
+//                                          its own accumulator tiles)
+// The accumulator layout of a 16x16 tile is the k-operand layout of the next
+// product (the MFMA k order of ll_device.hpp), so neither S nor U makes a
+// trip through LDS and the two products of a chunk need no barrier; only the
+// staged W, K and U' tiles are shared.  Reading the A operands from LDS is
+// what bounds a step (one 16-byte fragment per lane per MFMA), so a
+// workgroup holds few waves (two, 32 columns) and a head is spread over
+// D / 32 workgroups, each staging W and K once per chunk.  W, K, U' (the
+// workgroup's columns) and each wave's copy of the gates are staged NS - 1
+// chunks ahead with direct global->LDS loads; one barrier a chunk.
 template <typename T, int D, int C>
 struct GstSmem {
+  static constexpr int NWV = D >= 32 ? 2 : 1;  // compute waves per workgroup, 16 columns each
+  static constexpr int NCOL = 16 * NWV;
   typedef Tile<T, C, D> TL;
-  typedef Tile<T, C, 16> UL;
-  typedef typename Mma<T>::Frag Frag;
-  static constexpr int NW = C / 16, KSD = D / Mma<T>::KS;
-  static constexpr int WOFF = 0, KOFF = TL::BYTES, STAGE = 2 * TL::BYTES;  // W and K tiles, two stages
-  static constexpr int UOFF = 2 * STAGE;                                   // U of this slice [C][16]
-  static constexpr int SFOFF = UOFF + UL::BYTES;                           // S as B fragments [KSD][64]
-  static constexpr int WLOFF = SFOFF + KSD * 64 * (int)sizeof(Frag);        // per wave e^{g - G} [NW][C]
-  static constexpr int BYTES = WLOFF + NW * C * 4;
+  typedef Tile<T, C, NCOL> UT;
+  static constexpr int NSTAGE = 2;  // loads one chunk ahead
+  // each staged tensor's stages are adjacent ([W0 W1][K0 K1][U'0 U'1]), so
+  // that a stage's base is a small constant the LDS instructions carry as
+  // their immediate offset and one register per lane address serves both
+  static constexpr int WOFF = 0, KOFF = NSTAGE * TL::BYTES, UPOFF = 2 * NSTAGE * TL::BYTES;
+  static constexpr int GOFF = UPOFF + NSTAGE * UT::BYTES;  // per stage: the chunk's gates [C]
+  // per stage: e^{g - G_r} for the chunk's rows, then e^{g} (g the chunk's
+  // gate sum), made by the memory wave
+  static constexpr int WLOFF = GOFF + NSTAGE * C * 4, WLSTRIDE = C + 4;
+  // per compute wave its U columns [C][16], two buffers (chunk parity),
+  // written by the compute waves and stored to HBM by the memory wave
+  static constexpr int UTILE = C * 16 * (int)sizeof(T);
+  static constexpr int UOOFF = WLOFF + NSTAGE * WLSTRIDE * 4;
+  static constexpr int BYTES = UOOFF + 2 * NWV * UTILE;
 };
 
+// Buffer loads straight into LDS of a [ROWS][COLS] tile taken from rows of a
+// wider tensor (row stride in bytes given at run time), into the swizzled
+// Tile layout; 1 KiB per instruction, instruction i issued by wave i % NW.
+// The per-lane byte offsets from the tile's first element are fixed; the
+// tile's base is the buffer resource's, so moving to the next chunk costs
+// only scalar work.
+template <typename T, int ROWS, int COLS, int NW>
+struct TileLoads {
+  typedef Tile<T, ROWS, COLS> TL;
+  static constexpr int NINST = TL::BYTES / 1024;
+  static constexpr int TPW = (NINST + NW - 1) / NW;
+  static_assert(TL::BYTES % 1024 == 0 && 1024 % TL::RB == 0, "tile must be whole 1 KiB instructions");
+  uint32_t off[TPW];
+  __device__ __forceinline__ void init(int wv, int lane, int64_t row_stride_bytes) {
+    constexpr int RPI = 1024 / TL::RB;
+    const int rl = lane / TL::NCH, p = lane % TL::NCH;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int row = (wv + k * NW) * RPI + rl;
+      off[k] = (uint32_t)(row * row_stride_bytes + TL::pos(row, p) * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, char* lds, int wv) const {
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int i = wv + k * NW;
+      if (i < NINST) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + i * 1024), 16, off[k], 0, 0, 0);
+    }
+  }
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes from LDS through inline assembly, with the wait in the same
+// block: a plain read made the compiler wait first for every outstanding
+// load into LDS, which fill other buffers.
+__device__ __forceinline__ u32x4 lds_read16_now(const char* lds) {
+  u32x4 r;
+  const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+
+// A raw buffer resource over `bytes` bytes from `base` (gfx9 descriptor:
+// stride 0, range-checked against the byte count).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 template <typename T, int D, int C>
-__global__ void __launch_bounds__(64 * (C / 16)) ll_gdn_state(GdnArgs a) {
+__global__ void __launch_bounds__((64 * (GstSmem<T, D, C>::NWV + 1))) ll_gdn_state(GdnArgs a) {
   using M = Mma<T>;
   typedef GstSmem<T, D, C> SM;
   typedef typename M::Frag Frag;
-  typedef Tile<T, C, D> TL;
-  typedef Tile<T, C, 16> UL;
-  constexpr int NW = SM::NW, DT = D / 16, KSD = SM::KSD, KSC = C / M::KS;
-  constexpr int ODT = (DT + NW - 1) / NW;  // state tiles owned per wave (at most)
+  typedef typename SM::TL TL;
+  typedef typename SM::UT UT;
+  constexpr int NW = SM::NWV, NCOL = SM::NCOL, CT = C / 16, DT = D / 16;
+  constexpr int KSD = D / M::KS, KSC = C / M::KS;
+  static_assert(SM::NSTAGE == 2, "the step loop is unrolled over two stages");
   __shared__ __attribute__((aligned(1024))) char smem[SM::BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wv >= 0 && wv <= NW);  // NW compute waves and the memory wave
   const int g4 = lane >> 4, q16 = lane & 15;
+  constexpr int NSL = D / NCOL;  // workgroups per head
   const int wg = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int slice = wg % DT, bh = wg / DT, h = bh % a.H, b = bh / a.H;
-  const int n0 = 16 * slice;
+  const int slice = wg % NSL, bh = wg / NSL, h = bh % a.H, b = bh / a.H;
+  const int n0 = NCOL * slice;  // the workgroup's first state column
   const int nc = a.T / C;
-  auto row_of = [&](int i) { return ((int64_t)b * a.T + (int64_t)i * C) * a.H + h; };
-  Frag* sf = reinterpret_cast<Frag*>(smem + SM::SFOFF);
-  float* wl = reinterpret_cast<float*>(smem + SM::WLOFF) + wv * C;
-  char* ut = smem + SM::UOFF;
+  const int64_t rstride = (int64_t)a.H * D;         // elements between consecutive tokens of a head
+  const int64_t row0 = (int64_t)b * a.T * a.H + h;  // [B,T,H] row of the head's first token
+  const int64_t chunk_rows = (int64_t)C * a.H;
+  const uint32_t io_bytes = (uint32_t)(chunk_rows * D * (int64_t)sizeof(T)), g_bytes = (uint32_t)(chunk_rows * 4);
+  constexpr int EPP = 16 / (int)sizeof(T);       // elements per 16-byte piece
+  constexpr int UPIECES = SM::UTILE / 16;        // per compute wave and chunk
+  constexpr int SPL = (NW * UPIECES + 63) / 64;  // U pieces per lane of the memory wave
 
-  ChunkLoads<T, D, C, NW> ld;
-  ld.init(wv, lane, a.H, 1, 1);
-  auto issue = [&](int i) {
-    char* st = smem + (i & 1) * SM::STAGE;
-    ld.tiles(a.W, row_of(i), st + SM::WOFF, wv);
-    ld.tiles(a.k, row_of(i), st + SM::KOFF, wv);
-  };
-  // this wave's rows 16 wv + 4 (lane/16) + e of U' (column n0 + lane%16), and the gate of row lane
-  T upn[4];
-  float gn = 0.f;
-  auto fetch = [&](int i) {
-    const T* up = static_cast<const T*>(a.Up);
+  // The memory wave (the last one) moves all data: per step i, after the
+  // barrier, it issues the loads of chunk i + 1 (the gates first), stores the
+  // U of chunk i - 1 from LDS, makes chunk i + 1's decay factors once its
+  // gates have landed, and waits for the rest of its loads before the next
+  // barrier.  The compute waves issue no global memory operation: the
+  // barrier alone tells them a chunk is staged, and no store's latency is
+  // ever in their way.
+  if (wv == NW) {
+    TileLoads<T, C, D, 1> lt;
+    lt.init(0, lane, rstride * (int64_t)sizeof(T));
+    TileLoads<T, C, NCOL, 1> lu;
+    lu.init(0, lane, rstride * (int64_t)sizeof(T));
+    constexpr int NLOAD = 2 * TileLoads<T, C, D, 1>::NINST + TileLoads<T, C, NCOL, 1>::NINST;  // after the gates
+    constexpr int AFTER_GATES = NLOAD + SPL;
+    static_assert(AFTER_GATES <= 63, "wait count out of range");
+    const uint32_t goff = (uint32_t)(lane * a.H * 4);
+    const char* gW = static_cast<const char*>(a.W) + row0 * D * (int64_t)sizeof(T);
+    const char* gK = static_cast<const char*>(a.k) + row0 * D * (int64_t)sizeof(T);
+    const char* gU = static_cast<const char*>(a.Up) + (row0 * D + n0) * (int64_t)sizeof(T);
+    const char* gG = reinterpret_cast<const char*>(a.g + row0);
+    const char* gUo = reinterpret_cast<const char*>(static_cast<T*>(a.U) + row0 * D + n0);
+    uint32_t uoff[SPL];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) upn[e] = up[(row_of(i) + (int64_t)(16 * wv + 4 * g4 + e) * a.H) * D + n0 + q16];
-    gn = lane < C ? a.g[row_of(i) + (int64_t)lane * a.H] : 0.f;
-  };
+    for (int k = 0; k < SPL; ++k) {
+      const int p = lane + 64 * k, cw = p / UPIECES, lp = p % UPIECES, r = lp / (16 / EPP), c = lp % (16 / EPP);
+      uoff[k] = (uint32_t)(((int64_t)r * rstride + 16 * cw + c * EPP) * (int64_t)sizeof(T));
+    }
+    auto issue = [&](int si) __attribute__((always_inline)) {
+      if (lane < C)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(gG, g_bytes), (lds_void*)(smem + SM::GOFF + si * C * 4), 4,
+                                                 goff, 0, 0, 0);
+      lt.issue(buffer_rsrc(gW, io_bytes), smem + SM::WOFF + si * TL::BYTES, 0);
+      lt.issue(buffer_rsrc(gK, io_bytes), smem + SM::KOFF + si * TL::BYTES, 0);
+      lu.issue(buffer_rsrc(gU, io_bytes), smem + SM::UPOFF + si * UT::BYTES, 0);
+      gW += io_bytes;
+      gK += io_bytes;
+      gU += io_bytes;
+      gG += g_bytes;
+    };
+    // the decay factors of the chunk in stage si, from its landed gates
+    auto factors = [&](int si) __attribute__((always_inline)) {
+      const float* gl = reinterpret_cast<const float*>(smem + SM::GOFF + si * C * 4);
+      float* wlo = reinterpret_cast<float*>(smem + SM::WLOFF) + si * SM::WLSTRIDE;
+      const float G = chunk_scan<C>(lane < C ? gl[lane] : 0.f);
+      const float gsum = __shfl(G, C - 1, 64);
+      if (lane < C) wlo[lane] = __expf(gsum - G);
+      if (lane == 0) wlo[C] = __expf(gsum);
+    };
+    auto store_tile = [&](int i) __attribute__((always_inline)) {
+      const __amdgpu_buffer_rsrc_t ur = buffer_rsrc(gUo + (int64_t)i * io_bytes, io_bytes);
+      const char* tiles = smem + SM::UOOFF + (i & 1) * NW * SM::UTILE;
+#pragma unroll
+      for (int k = 0; k < SPL; ++k) {
+        const int p = lane + 64 * k;
+        if ((NW * UPIECES) % 64 == 0 || p < NW * UPIECES) {
+          const int cw = p / UPIECES, lp = p % UPIECES;
+          const u32x4 v = lds_read16_now(tiles + cw * SM::UTILE + lp * 16);
+          __builtin_amdgcn_raw_buffer_store_b128(v, ur, uoff[k], 0, 0);
+        }
+      }
+    };
+    issue(0);
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+    factors(0);
+    for (int i = 0; i < nc; ++i) {
+      lds_barrier();  // chunk i staged with its factors; the compute waves start step i
+      if (i + 1 < nc) issue((i + 1) & 1);
+      if (i > 0) store_tile(i - 1);
+      if (i + 1 < nc) {
+        // The gates went out first: once at most the tiles and the stores
+        // issued after them are outstanding, the gates have landed; once at
+        // most the stores are, the tiles have.  (Operations retire in issue
+        // order; the first step issues no stores.)
+        if (i > 0) {
+          __builtin_amdgcn_s_waitcnt(0xF70 | (AFTER_GATES & 15) | ((AFTER_GATES >> 4) << 14));
+          factors((i + 1) & 1);
+          __builtin_amdgcn_s_waitcnt(0xF70 | (SPL & 15) | ((SPL >> 4) << 14));
+        } else {
+          __builtin_amdgcn_s_waitcnt(0xF70 | (NLOAD & 15) | ((NLOAD >> 4) << 14));
+          factors(1);
+          __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+        }
+      }
+    }
+    lds_barrier();  // after the compute waves' last step
+    store_tile(nc - 1);
+    return;
+  }
 
+  // The compute waves: each owns 16 state columns, all D rows of them in
+  // registers.
+  const int col = n0 + 16 * wv + q16;  // this lane's state column
   // S_0: zero, or after a prior state the plain gated state of [0, pos0),
   // the sum of its levels' true states (the buckets partition the prefix)
-  f32x4 st[ODT];
+  f32x4 st[DT];
 #pragma unroll
-  for (int o = 0; o < ODT; ++o) st[o] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < DT; ++dt) st[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (a.pos0 > 0) {
     const float* Sh = a.state_in + (int64_t)bh * a.L * D * D;
     const float* sg = a.state_in + (int64_t)a.B * a.H * a.L * D * D + (int64_t)bh * a.L;
@@ -323,99 +478,102 @@ __global__ void __launch_bounds__(64 * (C / 16)) ll_gdn_state(GdnArgs a) {
       const int lvl = __ffsll((unsigned long long)bits);
       const float sc = __expf(sg[lvl]);
 #pragma unroll
-      for (int o = 0; o < ODT; ++o) {
-        const int dt = wv + o * NW;
-        if (dt >= DT) continue;
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st[o][e] += sc * Sh[(int64_t)lvl * D * D + (16 * dt + 4 * g4 + e) * D + n0 + q16];
-      }
-    }
-  }
-  for (int x = tid; x < KSD * 64; x += 64 * NW) sf[x] = Frag{};
-  if (a.pos0 > 0) {
-    __syncthreads();  // the zero fill is complete before the tiles are published into it
-#pragma unroll
-    for (int o = 0; o < ODT; ++o) {
-      const int dt = wv + o * NW;
-      if (dt >= DT) continue;
-      if constexpr (sizeof(T) == 2) {
-        bf16* f = reinterpret_cast<bf16*>(&sf[(dt >> 1) * 64 + lane]) + 4 * (dt & 1);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = (bf16)st[o][e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) reinterpret_cast<float*>(sf)[(4 * dt + e) * 64 + lane] = st[o][e];
-      }
+        for (int e = 0; e < 4; ++e) st[dt][e] += sc * Sh[(int64_t)lvl * D * D + (16 * dt + 4 * g4 + e) * D + col];
     }
   }
 
-  issue(0);
-  fetch(0);
-  for (int i = 0; i < nc; ++i) {
-    const char* stg = smem + (i & 1) * SM::STAGE;
-    T up[4];
+  // One chunk step on stage SI (a compile-time constant in each copy).
+  auto step = [&](auto stage_const) __attribute__((always_inline)) {
+    constexpr int SI = decltype(stage_const)::value;
+    const char* sw = smem + SM::WOFF + SI * TL::BYTES;
+    const char* sk = smem + SM::KOFF + SI * TL::BYTES;
+    const char* su = smem + SM::UPOFF + SI * UT::BYTES;
+    const float* wl = reinterpret_cast<const float*>(smem + SM::WLOFF) + SI * SM::WLSTRIDE;
+    lds_barrier();  // chunk i is staged with its decay factors; every wave is done with chunk i-1
+    // The LDS reads of the first product go out at once: the A fragments of
+    // W and U' in accumulator order; those of K^T follow as soon as the first
+    // product is issued (holding both sets at once would push the wave past
+    // the architectural registers).
+    Frag wf[CT][KSD], kf[DT][KSC];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) up[e] = upn[e];
-    const float gv = gn;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk i (and its U' rows) have landed
-    lds_barrier();                  // every wave's have; S_i is in sf; chunk i-1 is done everywhere
-    if (i + 1 < nc) {
-      issue(i + 1);
-      fetch(i + 1);
+    for (int rt = 0; rt < CT; ++rt)
+#pragma unroll
+      for (int s = 0; s < KSD; ++s) wf[rt][s] = frag_row<T, C, D>(sw, 16 * rt + q16, s, g4);
+    float up[CT][4];
+    i16x4 rr[CT];
+    if constexpr (sizeof(T) == 2) {
+      // one transposing read gives rows base..base+3 of this lane's column
+#pragma unroll
+      for (int rt = 0; rt < CT; ++rt)
+        rr[rt] = ds_read_tr16(su + UT::off(16 * rt + 4 * g4 + (q16 >> 2), 16 * wv + 4 * (q16 & 3)));
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < CT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) up[rt][e] = *reinterpret_cast<const float*>(su + UT::off(16 * rt + 4 * g4 + e, 16 * wv + q16));
     }
-    const float G = chunk_scan<C>(gv);
-    const float gsum = __shfl(G, C - 1, 64);
-    if (lane < C) wl[lane] = __expf(gsum - G);
+    // the k operand S_i from this wave's own state tiles
+    Frag sb[KSD];
+#pragma unroll
+    for (int s = 0; s < KSD; ++s) sb[s] = M::acc_frag(st, s);
+    lds_wait(rr);
 
-    // U rows of this wave: U' - W S_i
-    f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+    // U = U' - W S_i
+    f32x4 ut[CT];
 #pragma unroll
-    for (int s = 0; s < KSD; ++s) x = M::mma(frag_row<T, C, D>(stg + SM::WOFF, 16 * wv + q16, s, g4), sf[s * 64 + lane], x);
-    T* ug = static_cast<T*>(a.U);
+    for (int rt = 0; rt < CT; ++rt) ut[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * wv + 4 * g4 + e;
-      const T u = from_f32<T>(to_f32(up[e]) - x[e]);
-      ug[(row_of(i) + (int64_t)r * a.H) * D + n0 + q16] = u;
-      *reinterpret_cast<T*>(ut + UL::off(r, q16)) = u;
-    }
-    lds_barrier();  // U of the chunk complete
-
-    // S_{i+1} = e^{g} S_i + K^T diag(e^{g - G}) U for the state tiles this wave owns
-    Frag uf[KSC];
+    for (int s = 0; s < KSD; ++s)
 #pragma unroll
-    for (int s = 0; s < KSC; ++s) uf[s] = frag_col<T, C, 16>(ut, 0, s, lane);
-    Frag kf[ODT][KSC];
+      for (int rt = 0; rt < CT; ++rt) ut[rt] = M::mma(wf[rt][s], sb[s], ut[rt]);
 #pragma unroll
-    for (int o = 0; o < ODT; ++o) {
-      const int dt = wv + o * NW;
-      if (dt < DT)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int s = 0; s < KSC; ++s) kf[o][s] = frag_col<T, C, D>(stg + SM::KOFF, 16 * dt, s, lane);
-    }
-    lds_wait(uf, kf);
+      for (int s = 0; s < KSC; ++s) kf[dt][s] = frag_col<T, C, D>(sk, 16 * dt, s, lane);
+    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int s = 0; s < KSC; ++s) uf[s] = scale_tokens<T>(uf[s], wl, s, g4);
-    const float carry = __expf(gsum);
+      for (int rt = 0; rt < CT; ++rt) {
+        const bf16x4 v = __builtin_bit_cast(bf16x4, rr[rt]);
 #pragma unroll
-    for (int o = 0; o < ODT; ++o) {
-      const int dt = wv + o * NW;
-      if (dt >= DT) continue;
-      f32x4 y = st[o] * carry;
-#pragma unroll
-      for (int s = 0; s < KSC; ++s) y = M::mma(kf[o][s], uf[s], y);
-      st[o] = y;
-      // publish the tile as part of the B fragments of S (k = state row d)
-      if constexpr (sizeof(T) == 2) {
-        bf16* f = reinterpret_cast<bf16*>(&sf[(dt >> 1) * 64 + lane]) + 4 * (dt & 1);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = (bf16)y[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) reinterpret_cast<float*>(sf)[(4 * dt + e) * 64 + lane] = y[e];
+        for (int e = 0; e < 4; ++e) up[rt][e] = (float)v[e];
       }
     }
+    // U (rounded to the io type, as the read will see it) into this wave's
+    // LDS tile for the memory wave; its rows scaled by e^{g - G} become the k
+    // operand of the state update
+    T* uo = reinterpret_cast<T*>(smem + SM::UOOFF + (SI * NW + wv) * SM::UTILE);
+#pragma unroll
+    for (int rt = 0; rt < CT; ++rt) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(wl + 16 * rt + 4 * g4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const T u = from_f32<T>(up[rt][e] - ut[rt][e]);
+        uo[(16 * rt + 4 * g4 + e) * 16 + q16] = u;
+        ut[rt][e] = to_f32(u) * w[e];
+      }
+    }
+    Frag ub[KSC];
+#pragma unroll
+    for (int s = 0; s < KSC; ++s) ub[s] = M::acc_frag(ut, s);
+    const float carry = wl[C];
+    lds_wait(kf);
+
+    // S_{i+1} = e^{g} S_i + K^T diag(e^{g - G}) U
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st[dt] *= carry;
+#pragma unroll
+    for (int s = 0; s < KSC; ++s)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) st[dt] = M::mma(kf[dt][s], ub[s], st[dt]);
+  };
+
+  for (int i = 0; i < nc; i += 2) {
+    step(std::integral_constant<int, 0>{});
+    if (i + 1 < nc) step(std::integral_constant<int, 1>{});
   }
+  lds_barrier();  // the last chunk's U is in LDS for the memory wave
 }
 
 // ---------------------------------------------------------------------------
@@ -428,8 +586,9 @@ static hipError_t launch_wy_t(const GdnArgs& a, hipStream_t s) {
 
 template <typename T, int D, int C>
 static hipError_t launch_gst_t(const GdnArgs& a, hipStream_t s) {
-  const int grid = a.B * a.H * (D / 16);
-  hipLaunchKernelGGL((ll_gdn_state<T, D, C>), dim3(grid), dim3(64 * (C / 16)), 0, s, a);
+  typedef GstSmem<T, D, C> SM;
+  const int grid = a.B * a.H * (D / SM::NCOL);
+  hipLaunchKernelGGL((ll_gdn_state<T, D, C>), dim3(grid), dim3(64 * (SM::NWV + 1)), 0, s, a);
   return hipGetLastError();
 }
 
@@ -458,6 +617,29 @@ static hipError_t launch_gst_t(const GdnArgs& a, hipStream_t s) {
       default: return hipErrorInvalidValue;                                    \
     }                                                                          \
   }
+
+// Every instance the dispatch can launch, instantiated explicitly: the host
+// pass did not emit launch stubs for some implicitly instantiated instances of
+// the state pass (the library would then fail to load).
+#define LL_GDN_INSTANCES(T, D, C)                                  \
+  template __global__ void ll_gdn_wy<T, D, C>(GdnArgs);           \
+  template __global__ void ll_gdn_state<T, D, C>(GdnArgs);
+LL_GDN_INSTANCES(bf16, 32, 32)
+LL_GDN_INSTANCES(bf16, 32, 64)
+LL_GDN_INSTANCES(bf16, 64, 32)
+LL_GDN_INSTANCES(bf16, 64, 64)
+LL_GDN_INSTANCES(bf16, 128, 32)
+LL_GDN_INSTANCES(bf16, 128, 64)
+LL_GDN_INSTANCES(float, 16, 16)
+LL_GDN_INSTANCES(float, 16, 32)
+LL_GDN_INSTANCES(float, 16, 64)
+LL_GDN_INSTANCES(float, 32, 16)
+LL_GDN_INSTANCES(float, 32, 32)
+LL_GDN_INSTANCES(float, 32, 64)
+LL_GDN_INSTANCES(float, 64, 16)
+LL_GDN_INSTANCES(float, 64, 32)
+LL_GDN_INSTANCES(float, 64, 64)
+#undef LL_GDN_INSTANCES
 
 hipError_t launch_gdn_wy(int io, int D, int C, const GdnArgs& a, hipStream_t s) { LL_GDN_DISPATCH(launch_wy_t) }
 
