@@ -617,13 +617,14 @@ ll_status ll_ccq_query(int B, int T, int H, int dk, ll_dtype io, const void* q, 
 
 namespace {
 
-// The backward pass: buffers of the reversed-time reads, then the prefill
-// workspace (sized for the padded length Tp, which also covers T).
+// The backward pass: the forward's block states and nodes of (k, v) (the
+// workspace of the dq read first, then of (k, v)), the per-row dot products of
+// the gate gradient, the block shares of the reverse bucket states and the
+// chunk-level states of one walk per workgroup.
 struct BwdPlan {
-  ll_problem p, pp;  // the forward problem at T and at Tp
-  int Tp, LS;
-  size_t qr_off, kr_off, vr_off, dor_off, y_off, ylv_off, ylv_stride, gr_off, hot_off, adk_off, fwl_off, fwl_bytes,
-      fwd_off, fwd_bytes, bytes;
+  Plan pl;
+  int nbl;  // block levels: bit_length(nb - 1)
+  size_t fwd_off, doo_off, xdv_off, w_off, scratch_off, bytes;
 };
 
 ll_status plan_bwd(const ll_problem* p, BwdPlan* out) {
@@ -632,42 +633,22 @@ ll_status plan_bwd(const ll_problem* p, BwdPlan* out) {
   if (st != LL_OK) return st;
   if (p->rule != LL_MAMBA2) return fail(LL_ERR_UNSUPPORTED, "the backward pass is implemented for the Mamba-2 write");
   BwdPlan c;
-  c.p = *p;
-  int Tp = 1;
-  while (Tp < p->T) Tp <<= 1;
-  c.Tp = Tp;
-  c.pp = *p;
-  c.pp.T = Tp;
-  c.LS = pl.LS;
-  Plan plp;
-  st = plan_prefill(&c.pp, false, &plp);
-  if (st != LL_OK) return st;
-  const size_t esz = p->io == LL_BF16 ? 2 : 4;
-  const size_t rowsP = (size_t)p->B * Tp * p->H, rows = (size_t)p->B * p->T * p->H;
-  const size_t d = (size_t)p->dk;
+  c.pl = pl;
+  c.nbl = bit_length((int64_t)pl.nb - 1);
+  const size_t bh = (size_t)p->B * p->H, rows = (size_t)p->B * p->T * p->H;
+  const size_t dd = (size_t)p->dk * p->dv;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
     off = align256(off + bytes);
     return at;
   };
-  c.qr_off = take(rowsP * d * esz);
-  c.kr_off = take(rowsP * d * esz);
-  c.vr_off = take(rowsP * d * esz);
-  c.dor_off = take(rowsP * d * esz);
-  c.y_off = take(rowsP * d * esz);
-  // the reversed reads of every level present, kept until their sum: dv's and dk's per level
-  c.ylv_stride = align256(rowsP * d * esz);
-  c.ylv_off = take(2 * (size_t)c.LS * c.ylv_stride);
-  c.gr_off = take(rowsP * 4);
-  c.hot_off = take(rowsP * p->L * 4);
-  c.adk_off = take(rows * d * 4);
-  // the forward's block states and nodes of (k, v), kept for the reads of every level
-  c.fwl_bytes = pl.bytes;
-  c.fwl_off = take(pl.bytes);
-  c.fwd_off = off;
-  c.fwd_bytes = plp.bytes > pl.bytes ? plp.bytes : pl.bytes;
-  c.bytes = off + c.fwd_bytes;
+  c.fwd_off = take(pl.bytes);
+  c.doo_off = take(rows * 4);
+  c.xdv_off = take(rows * 4);
+  c.w_off = take(bh * pl.nb * (size_t)c.nbl * dd * 4);
+  c.scratch_off = take(bh * pl.nb * (size_t)llattn::max_block_depth(p->dk) * dd * 4);
+  c.bytes = off;
   *out = c;
   return LL_OK;
 }
@@ -687,80 +668,88 @@ ll_status ll_attn_bwd(const ll_problem* p, const void* q, const void* k, const v
                       const float* lambda, const void* o, const void* dO, void* dq, void* dk, void* dv,
                       float* dlog_gate, float* dlambda, void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
+  (void)o;  // dO . o is formed from the level gradients: sum_l lambda^l dlambda^l
   BwdPlan c;
   ll_status st = plan_bwd(p, &c);
   if (st != LL_OK) return st;
-  if (!q || !k || !v || !log_gate || !lambda || !o || !dO)
-    return fail(LL_ERR_NULL, "q, k, v, log_gate, lambda, o and dO must not be NULL");
+  if (!q || !k || !v || !log_gate || !lambda || !dO)
+    return fail(LL_ERR_NULL, "q, k, v, log_gate, lambda and dO must not be NULL");
   if (!dq || !dk || !dv || !dlog_gate || !dlambda)
     return fail(LL_ERR_NULL, "dq, dk, dv, dlog_gate and dlambda must not be NULL");
   if (workspace_bytes < c.bytes)
     return fail(LL_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, c.bytes);
   if (!workspace) return fail(LL_ERR_WORKSPACE, "workspace is NULL");
   char* ws = static_cast<char*>(workspace);
-  void* qr = ws + c.qr_off;
-  void* kr = ws + c.kr_off;
-  void* vr = ws + c.vr_off;
-  void* dOr = ws + c.dor_off;
-  void* Y = ws + c.y_off;
-  float* gr = reinterpret_cast<float*>(ws + c.gr_off);
-  float* hot = reinterpret_cast<float*>(ws + c.hot_off);
-  char* ylv = ws + c.ylv_off;
-  float* adk = reinterpret_cast<float*>(ws + c.adk_off);
-  void* fws = ws + c.fwd_off;
+  const Plan& pl = c.pl;
+  const int io = p->io == LL_BF16 ? 1 : 0;
+  const int D = p->dk;
+
+  // dq: the forward read with (q, k, v) := (dO, v, k)
+  st = run_prefill(p, 0, nullptr, dO, v, k, log_gate, lambda, nullptr, dq, nullptr, ws + c.fwd_off, pl.bytes, stream);
+  if (st != LL_OK) return st;
+
+  // the forward's block states and Fenwick nodes of (k, v), in the same workspace
+  PrefillArgs f;
+  f.B = p->B;
+  f.T = p->T;
+  f.H = p->H;
+  f.L = p->L;
+  f.LS = pl.LS;
+  f.P = pl.P;
+  f.nb = pl.nb;
+  f.nF = pl.nF;
+  f.q = nullptr;
+  f.k = k;
+  f.v = v;
+  f.g = log_gate;
+  f.lam = lambda;
+  f.o = nullptr;
+  f.S = reinterpret_cast<float*>(ws + c.fwd_off + pl.s_off);
+  f.GS = reinterpret_cast<float*>(ws + c.fwd_off + pl.gs_off);
+  f.F = reinterpret_cast<float*>(ws + c.fwd_off + pl.f_off);
+  f.GF = reinterpret_cast<float*>(ws + c.fwd_off + pl.gf_off);
+  f.N16 = nullptr;
+  f.state = nullptr;
+  f.state_in = nullptr;
+  f.pos0 = 0;
+  hipError_t e = timed(K_BWD, stream, [&] { return llattn::launch_block_state(io, D, pl.Cr, f, stream); });
+  if (e == hipSuccess && pl.nb > 1) e = timed(K_BWD, stream, [&] { return llattn::launch_fenwick_scan(D, f, stream); });
+  if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+
   llattn::BwdArgs a;
   a.B = p->B;
   a.T = p->T;
-  a.Tp = c.Tp;
   a.H = p->H;
-  a.D = p->dk;
+  a.D = D;
   a.L = p->L;
   a.q = q;
   a.k = k;
   a.v = v;
   a.g = log_gate;
   a.lam = lambda;
-  a.o = o;
   a.dO = dO;
   a.dk = dk;
   a.dv = dv;
   a.dlog_gate = dlog_gate;
   a.dlambda = dlambda;
-  const int io = p->io == LL_BF16 ? 1 : 0;
-  const int64_t rowsP = (int64_t)p->B * c.Tp * p->H;
-  hipError_t e = hipSuccess;
-  auto step = [&](auto fn) {
-    if (e == hipSuccess) e = timed(K_BWD, stream, fn);
-  };
-  // dq: the forward with (q, k, v) := (dO, v, k)
-  st = run_prefill(p, 0, nullptr, dO, v, k, log_gate, lambda, nullptr, dq, nullptr, fws, c.fwd_bytes, stream);
-  if (st != LL_OK) return st;
-  step([&] { return llattn::launch_bwd_reverse(io, a, qr, kr, vr, gr, stream); });
-  for (int lvl = 0; lvl < c.LS && e == hipSuccess; ++lvl) {
-    step([&] { return llattn::launch_bwd_onehot(rowsP, p->L, lvl, hot, stream); });
-    if (e != hipSuccess) break;
-    // dlambda at this level: dO . (the level's read alone); the block states and
-    // nodes of (k, v) are the same for every level, built once in their own workspace
-    st = run_prefill(p, 0, nullptr, q, k, v, log_gate, hot, nullptr, Y, nullptr, ws + c.fwl_off, c.fwl_bytes, stream,
-                     lvl > 0);
-    if (st != LL_OK) return st;
-    step([&] { return llattn::launch_bwd_rowdot(io, a, Y, lvl, stream); });
-    // dv and dk: reads in reversed time with lambda^(l) dO as the later token's side
-    step([&] { return llattn::launch_bwd_scale_rev(io, a, lvl, dOr, stream); });
-    if (e != hipSuccess) break;
-    void* ydv = ylv + (2 * (size_t)lvl) * c.ylv_stride;
-    void* ydk = ylv + (2 * (size_t)lvl + 1) * c.ylv_stride;
-    st = run_prefill(&c.pp, 0, nullptr, kr, qr, dOr, gr, hot, nullptr, ydv, nullptr, fws, c.fwd_bytes, stream);
-    if (st != LL_OK) return st;
-    st = run_prefill(&c.pp, 0, nullptr, vr, dOr, qr, gr, hot, nullptr, ydk, nullptr, fws, c.fwd_bytes, stream);
-    if (st != LL_OK) return st;
-  }
-  // levels no position reaches carry no gradient
-  for (int lvl = c.LS; lvl < p->L; ++lvl) step([&] { return llattn::launch_bwd_rowdot(io, a, nullptr, lvl, stream); });
-  step([&] {
-    return llattn::launch_bwd_sum_rev(io, a, ylv, (int64_t)(c.ylv_stride / (io ? 2 : 4)), c.LS, adk, stream);
-  });
-  step([&] { return llattn::launch_bwd_gate(io, a, adk, gr, stream); });  // gr is free again: dG per row
+  llattn::BwdFwdNodes n;
+  n.nb = pl.nb;
+  n.nF = pl.nF;
+  n.P = pl.P;
+  n.LS = pl.LS;
+  n.S = f.S;
+  n.GS = f.GS;
+  n.F = f.F;
+  n.GF = f.GF;
+  llattn::BwdWork w;
+  w.dOo = reinterpret_cast<float*>(ws + c.doo_off);
+  w.xdv = reinterpret_cast<float*>(ws + c.xdv_off);
+  w.W = reinterpret_cast<float*>(ws + c.w_off);
+  w.nbl = c.nbl;
+  w.scratch = reinterpret_cast<float*>(ws + c.scratch_off);
+  // levels; reverse states and dv; reverse states and dk; the gate
+  for (int pass = 0; pass < 6 && e == hipSuccess; ++pass)
+    e = timed(K_BWD, stream, [&] { return llattn::launch_bwd_native(io, D, pl.Cr, a, n, w, pass, stream); });
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

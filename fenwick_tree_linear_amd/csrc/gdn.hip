@@ -329,8 +329,6 @@ struct TileLoads {
   }
 };
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 // 16 bytes from LDS through inline assembly, with the wait in the same
 // block: a plain read made the compiler wait first for every outstanding
 // load into LDS, which fill other buffers.
@@ -339,12 +337,6 @@ __device__ __forceinline__ u32x4 lds_read16_now(const char* lds) {
   const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(addr) : "memory");
   return r;
-}
-
-// A raw buffer resource over `bytes` bytes from `base` (gfx9 descriptor:
-// stride 0, range-checked against the byte count).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 template <typename T, int D, int C>

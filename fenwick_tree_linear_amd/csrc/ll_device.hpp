@@ -124,6 +124,22 @@ __device__ __forceinline__ int state_tile_offset(int dt, int nt, int lane) {
   return ((dt * (D / 16) + nt) * 64 + lane) * 4;
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// A raw buffer resource over `bytes` bytes from `base` (gfx9 descriptor:
+// stride 0, range-checked against the byte count).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Tile (dt, nt) of an fp32 state through a buffer resource over the state.
+// The tile's byte offset is the scalar offset of the load, so reading many
+// tiles needs no 64-bit address per tile.
+template <int D>
+__device__ __forceinline__ f32x4 load_state_tile(__amdgpu_buffer_rsrc_t r, int dt, int nt, int lane) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, (dt * (D / 16) + nt) * 1024, 0));
+}
+
 // ------------------------------------------------------------ LDS tiles
 // Row-major [ROWS][COLS] tile of T in LDS.  Rows are stored unpadded and the
 // 16-byte chunks of row r are permuted by XOR with a key of r, so that the

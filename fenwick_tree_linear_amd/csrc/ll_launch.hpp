@@ -70,20 +70,38 @@ struct GdnArgs {
   int64_t pos0;
 };
 
-// The elementwise parts of the backward pass (Tp: T rounded up to a power of two).
+// Inputs and outputs of the backward pass.
 struct BwdArgs {
-  int B, T, Tp, H, D, L;
+  int B, T, H, D, L;
   const void* q;
   const void* k;
   const void* v;
   const float* g;
   const float* lam;
-  const void* o;
   const void* dO;
   void* dk;
   void* dv;
   float* dlog_gate;
   float* dlambda;
+};
+
+// The forward's block decomposition of (k, v) that the backward reads: block
+// states S/GS and Fenwick nodes F/GF as PrefillArgs holds them.
+struct BwdFwdNodes {
+  int nb, nF, P, LS;
+  const float* S;
+  const float* GS;
+  const float* F;
+  const float* GF;
+};
+
+// Scratch of the backward kernels.
+struct BwdWork {
+  float* dOo;      // [B,T,H] dO_t . o_t
+  float* xdv;      // [B,T,H] v_t . dv_t (= k_t . dk_t)
+  float* W;        // [B*H, nb, nbl, D*D] block shares of the reverse bucket states
+  int nbl;         // block levels: bit_length(nb - 1)
+  float* scratch;  // [B*H*nb, max_block_depth, D*D] chunk-level states of one walk
 };
 
 // io: 0 = fp32, 1 = bf16.  Each returns hipSuccess or the launch error.
@@ -92,14 +110,10 @@ hipError_t launch_chunk_attn(int io, int D, int C, const PrefillArgs& a, hipStre
 hipError_t launch_fenwick_scan(int D, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_state_export(int D, int C, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prior_read(int io, int D, int C, const PrefillArgs& a, hipStream_t s);
-hipError_t launch_bwd_reverse(int io, const BwdArgs& a, void* qr, void* kr, void* vr, float* gr, hipStream_t s);
-hipError_t launch_bwd_scale_rev(int io, const BwdArgs& a, int lvl, void* dOr, hipStream_t s);
-// one-hot level weights at lvl; for lvl > 0, w must hold the one-hot at lvl - 1
-hipError_t launch_bwd_onehot(int64_t rows, int L, int lvl, float* w, hipStream_t s);
-hipError_t launch_bwd_sum_rev(int io, const BwdArgs& a, const void* Y, int64_t ystride, int LS, float* acc_dk,
+// pass: 0 levels (dlambda, dO.o), 1 reverse states of (q, dO), 2 dv, 3 reverse
+// states of (dO, q), 4 dk, 5 dlog_gate
+hipError_t launch_bwd_native(int io, int D, int C, const BwdArgs& a, const BwdFwdNodes& n, const BwdWork& w, int pass,
                              hipStream_t s);
-hipError_t launch_bwd_rowdot(int io, const BwdArgs& a, const void* Y, int lvl, hipStream_t s);
-hipError_t launch_bwd_gate(int io, const BwdArgs& a, const float* acc_dk, float* dG, hipStream_t s);
 hipError_t launch_ccq_fill(int64_t rows, int L, float* ones, float* zeros, hipStream_t s);
 hipError_t launch_ccq_ksum(int io, int D, int B, int T, int H, int CS, const void* k, float* csum, hipStream_t s);
 hipError_t launch_ccq_combine(int io, int D, int B, int T, int H, int CS, const void* q, const void* k,

@@ -263,23 +263,27 @@ ll_status ll_ccq_query(int B, int T, int H, int dk, ll_dtype io, const void* q, 
 
 /*
  * Backward pass of the prefill for the LL_MAMBA2 write (training): given the
- * forward's inputs, its output o and the gradient dO of a loss at o, writes
- * the gradients of that loss with respect to every input:
+ * forward's inputs and the gradient dO of a loss at the output o, writes the
+ * gradients of that loss with respect to every input ("Log-Linear Attention",
+ * section 2.3: the masked form, whose pair weights are differentiated term by
+ * term; section 3 trains through it):
  *   dq, dk [B,T,H,dk], dv [B,T,H,dv]   io dtype
  *   dlog_gate [B,T,H], dlambda [B,T,H,L]   fp32
- * The gradients of the masked form (section 2.3) are evaluated with the
- * chunk-parallel forward itself: dq is the forward with (q, k, v) :=
- * (dO, v, k); dlambda at level l is dO . (the level-l read); dk and dv are the
- * reads of reversed time, one level at a time with the level weight folded
- * into dO (3 x levels + 1 forward reads, the level reads for dlambda sharing
- * one build of the block states: roughly 40 times the forward's cost at 12
- * levels); dlog_gate_r = sum_{t >= r} (dO_t . o_t - k_t . dk_t).
- * Shapes as ll_attn_fwd (LL_ERR_UNSUPPORTED for LL_GATED_DELTANET); the
- * workspace holds reversed copies of q, k, v and dO padded to a power of
- * two, the reversed dk and dv reads of every level (2 x levels row buffers,
- * summed at the end), an fp32 dk, the forward's workspace for the reversed
- * reads and one more that keeps the block states of (k, v) for the level
- * reads.
+ * With M[t,s] = lambda_t^{lev(t,s)} e^{G_t - G_s} for s <= t (G the running
+ * sum of log_gate):
+ *   dq_t = sum_s M[t,s] (dO_t . v_s) k_s      (the forward read of (dO, v, k))
+ *   dv_s = sum_t M[t,s] (q_t . k_s) dO_t,     dk_s = sum_t M[t,s] (dO_t . v_s) q_t
+ *   dlambda_t^l = sum over s at level l of e^{G_t - G_s} (q_t . k_s)(dO_t . v_s)
+ *   dlog_gate_r = sum_{t >= r} (dO_t . o_t - k_t . dk_t)
+ * dv and dk come from reads in which each source gathers the later tokens of
+ * the one Fenwick bucket it reads at every level; dO . o and k . dk enter the
+ * gate gradient in fp32, as sum_l lambda^l dlambda^l and v . dv.  `o` is not
+ * read (it may be NULL).  Shapes as ll_attn_fwd (LL_ERR_UNSUPPORTED for
+ * LL_GATED_DELTANET).  The workspace holds the forward's block states and
+ * Fenwick nodes (of the dq read, then of (k, v)), two fp32 values per row, a
+ * dk x dv fp32 state per block and block level (bit_length(blocks - 1) of them),
+ * and max-depth chunk-level states per block; its contents on entry do not
+ * matter.  Kernels run on `stream`, in order; the call returns after launching.
  */
 ll_status ll_attn_bwd_workspace_bytes(const ll_problem* p, size_t* bytes);
 ll_status ll_attn_bwd(const ll_problem* p, const void* q, const void* k, const void* v, const float* log_gate,
@@ -292,7 +296,7 @@ const char* ll_last_error(void);
 
 /*
  * Per-kernel timing, a measurement aid (off by default).  While enabled, each
- * kernel that ll_attn_fwd and ll_decode_step launch is bracketed by two HIP
+ * kernel that the entry points launch is bracketed by two HIP
  * events recorded on the call's stream.  ll_kernel_timing_read() waits for the
  * recorded events, then reports for up to `capacity` kernels their name (a
  * static string: "ll_chunk_state", "ll_fenwick_scan", "ll_chunk_attn",

@@ -12,12 +12,9 @@ hipError_t launch_chunk_attn(int, int, int, const PrefillArgs&, hipStream_t) { S
 hipError_t launch_fenwick_scan(int, const PrefillArgs&, hipStream_t) { STUB; }
 hipError_t launch_state_export(int, int, const PrefillArgs&, hipStream_t) { STUB; }
 hipError_t launch_prior_read(int, int, int, const PrefillArgs&, hipStream_t) { STUB; }
-hipError_t launch_bwd_reverse(int, const BwdArgs&, void*, void*, void*, float*, hipStream_t) { STUB; }
-hipError_t launch_bwd_scale_rev(int, const BwdArgs&, int, void*, hipStream_t) { STUB; }
-hipError_t launch_bwd_onehot(int64_t, int, int, float*, hipStream_t) { STUB; }
-hipError_t launch_bwd_sum_rev(int, const BwdArgs&, const void*, int64_t, int, float*, hipStream_t) { STUB; }
-hipError_t launch_bwd_rowdot(int, const BwdArgs&, const void*, int, hipStream_t) { STUB; }
-hipError_t launch_bwd_gate(int, const BwdArgs&, const float*, float*, hipStream_t) { STUB; }
+hipError_t launch_bwd_native(int, int, int, const BwdArgs&, const BwdFwdNodes&, const BwdWork&, int, hipStream_t) {
+  STUB;
+}
 hipError_t launch_ccq_fill(int64_t, int, float*, float*, hipStream_t) { STUB; }
 hipError_t launch_ccq_ksum(int, int, int, int, int, int, const void*, float*, hipStream_t) { STUB; }
 hipError_t launch_ccq_combine(int, int, int, int, int, int, const void*, const void*, const void*, const float*,

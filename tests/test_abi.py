@@ -248,10 +248,16 @@ def test_ccq_validation_before_any_launch():
 def test_bwd_validation_before_any_launch():
     D = DUMMY
     n = F.ll_attn_bwd_workspace_bytes(prob(T=2048, L=12))
-    # five reversed bf16 row buffers, the dv and dk reads of all 12 levels, an fp32 dk
-    assert n >= 2 * 2048 * 16 * 64 * ((5 + 2 * 12) * 2 + 4)
-    # T = 1536 pads to 2048 for the reversed reads (29 padded bf16 row buffers)
-    assert F.ll_attn_bwd_workspace_bytes(prob(T=1536, L=12)) >= 29 * 2 * 2048 * 16 * 64 * 2
+    # the forward's workspace, dO.o and v.dv per row (fp32), the block shares of the
+    # reverse bucket states (4 blocks of 8 chunks per head: 2 block levels) and 3
+    # chunk-level states per block, all fp32 64 x 64
+    def need(T, L, nb, nbl):
+        rows, heads, state = 2 * T * 16, 2 * 16, 64 * 64 * 4
+        return F.ll_attn_fwd_workspace_bytes(prob(T=T, L=L)) + 2 * rows * 4 + heads * nb * (nbl + 3) * state
+
+    assert need(2048, 12, 4, 2) <= n <= need(2048, 12, 4, 2) + 4 * 256
+    m = F.ll_attn_bwd_workspace_bytes(prob(T=4096, L=13))  # 8 blocks: 3 block levels
+    assert need(4096, 13, 8, 3) <= m <= need(4096, 13, 8, 3) + 4 * 256
 
     def call(p, q=D, o=D, dO=D, dq=D, dlam=D, ws=D, wsb=n):
         return status_of(F.ll_attn_bwd, p, q, D, D, D, D, o, dO, dq, D, D, D, dlam, ws, wsb, 0)[0]
@@ -259,7 +265,8 @@ def test_bwd_validation_before_any_launch():
     assert call(prob(T=2048, L=12, rule=F.LL_GATED_DELTANET)) == "LL_ERR_UNSUPPORTED"
     assert call(prob(T=2048, L=11)) == "LL_ERR_SHAPE"
     assert call(prob(T=2048, L=12, C=48)) == "LL_ERR_SHAPE"
-    assert call(prob(T=2048, L=12), o=None) == "LL_ERR_NULL"
+    assert call(prob(T=2048, L=12), dO=None) == "LL_ERR_NULL"
+    assert call(prob(T=2048, L=12), dq=None) == "LL_ERR_NULL"
     assert call(prob(T=2048, L=12), dlam=None) == "LL_ERR_NULL"
     assert call(prob(T=2048, L=12), wsb=n - 1) == "LL_ERR_WORKSPACE"
     assert call(prob(T=2048, L=12), ws=None) == "LL_ERR_WORKSPACE"

@@ -2,6 +2,11 @@
 gradients from the definition (themselves pinned by central differences of the
 forward oracle).  Every gradient tensor is compared element by element:
 max|g - ref| / max|ref| <= 1e-4 (fp32 io), 2e-2 (bf16 io).
+
+The cases cover one block per head (T = C P), several blocks (block-level
+reverse buckets, a block count that is not a power of two), blocks of one and
+two chunks, and the 2048-token bf16 shape the benchmark times (d 64, C 64,
+12 levels), where the gate gradient's suffix sums run longest.
 """
 
 import numpy as np
@@ -23,6 +28,11 @@ CASES = [
     ("bf16", 2, 4, 512, 64, 64, 10, "default"),
     ("bf16", 1, 2, 320, 64, 64, 10, "slowdecay"),  # padded to 512
     ("bf16", 1, 2, 256, 128, 32, 9, "default"),
+    ("f32", 1, 2, 1024, 32, 16, 11, "default"),     # 8 blocks of 8 chunks
+    ("f32", 1, 3, 384, 16, 32, 10, "slowdecay"),    # 3 blocks of 4 chunks
+    ("bf16", 2, 2, 384, 32, 64, 10, "default"),     # 3 blocks of 2 chunks
+    ("bf16", 1, 2, 1536, 128, 32, 12, "slowdecay"), # 6 blocks of 8 chunks
+    ("bf16", 1, 4, 2048, 64, 64, 12, "default"),    # 4 blocks of 8 chunks
 ]
 
 
