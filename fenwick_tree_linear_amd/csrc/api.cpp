@@ -617,14 +617,14 @@ ll_status ll_ccq_query(int B, int T, int H, int dk, ll_dtype io, const void* q, 
 
 namespace {
 
-// The backward pass: the forward's block states and nodes of (k, v) (the
-// workspace of the dq read first, then of (k, v)), the per-row dot products of
-// the gate gradient, the block shares of the reverse bucket states and the
-// chunk-level states of one walk per workgroup.
+// The backward pass: the forward's block states and Fenwick nodes of (v, k),
+// the per-row terms of the gate gradient, the reverse bucket states (block
+// shares, then bucket sums, and their transposes), the per-block gate sums,
+// and the chunk-level states of the walks where they do not fit in LDS.
 struct BwdPlan {
   Plan pl;
   int nbl;  // block levels: bit_length(nb - 1)
-  size_t fwd_off, doo_off, xdv_off, w_off, scratch_off, bytes;
+  size_t fwd_off, doo_off, din_off, w_off, wt_off, bt_off, scratch_off, bytes;
 };
 
 ll_status plan_bwd(const ll_problem* p, BwdPlan* out) {
@@ -645,9 +645,12 @@ ll_status plan_bwd(const ll_problem* p, BwdPlan* out) {
   };
   c.fwd_off = take(pl.bytes);
   c.doo_off = take(rows * 4);
-  c.xdv_off = take(rows * 4);
+  c.din_off = take(rows * 4);
   c.w_off = take(bh * pl.nb * (size_t)c.nbl * dd * 4);
-  c.scratch_off = take(bh * pl.nb * (size_t)llattn::max_block_depth(p->dk) * dd * 4);
+  c.wt_off = take(bh * pl.nb * (size_t)c.nbl * dd * 4);
+  c.bt_off = take(bh * pl.nb * 4);
+  c.scratch_off = take(llattn::bwd_states_in_lds(p->dk) ? 0
+                                                        : bh * pl.nb * (size_t)llattn::max_block_depth(p->dk) * dd * 4);
   c.bytes = off;
   *out = c;
   return LL_OK;
@@ -684,11 +687,8 @@ ll_status ll_attn_bwd(const ll_problem* p, const void* q, const void* k, const v
   const int io = p->io == LL_BF16 ? 1 : 0;
   const int D = p->dk;
 
-  // dq: the forward read with (q, k, v) := (dO, v, k)
-  st = run_prefill(p, 0, nullptr, dO, v, k, log_gate, lambda, nullptr, dq, nullptr, ws + c.fwd_off, pl.bytes, stream);
-  if (st != LL_OK) return st;
-
-  // the forward's block states and Fenwick nodes of (k, v), in the same workspace
+  // the forward's block states and Fenwick nodes of (v, k): the transposed
+  // states of (k, v), which the forward walk reads as S dO
   PrefillArgs f;
   f.B = p->B;
   f.T = p->T;
@@ -699,8 +699,8 @@ ll_status ll_attn_bwd(const ll_problem* p, const void* q, const void* k, const v
   f.nb = pl.nb;
   f.nF = pl.nF;
   f.q = nullptr;
-  f.k = k;
-  f.v = v;
+  f.k = v;
+  f.v = k;
   f.g = log_gate;
   f.lam = lambda;
   f.o = nullptr;
@@ -728,6 +728,7 @@ ll_status ll_attn_bwd(const ll_problem* p, const void* q, const void* k, const v
   a.g = log_gate;
   a.lam = lambda;
   a.dO = dO;
+  a.dq = dq;
   a.dk = dk;
   a.dv = dv;
   a.dlog_gate = dlog_gate;
@@ -743,12 +744,14 @@ ll_status ll_attn_bwd(const ll_problem* p, const void* q, const void* k, const v
   n.GF = f.GF;
   llattn::BwdWork w;
   w.dOo = reinterpret_cast<float*>(ws + c.doo_off);
-  w.xdv = reinterpret_cast<float*>(ws + c.xdv_off);
+  w.din = reinterpret_cast<float*>(ws + c.din_off);
   w.W = reinterpret_cast<float*>(ws + c.w_off);
+  w.WT = reinterpret_cast<float*>(ws + c.wt_off);
+  w.BT = reinterpret_cast<float*>(ws + c.bt_off);
   w.nbl = c.nbl;
-  w.scratch = reinterpret_cast<float*>(ws + c.scratch_off);
-  // levels; reverse states and dv; reverse states and dk; the gate
-  for (int pass = 0; pass < 6 && e == hipSuccess; ++pass)
+  w.scratch = llattn::bwd_states_in_lds(D) ? nullptr : reinterpret_cast<float*>(ws + c.scratch_off);
+  // the forward walk; the reverse bucket states; the reverse walk; the gate's later blocks
+  for (int pass = 0; pass < 4 && e == hipSuccess; ++pass)
     e = timed(K_BWD, stream, [&] { return llattn::launch_bwd_native(io, D, pl.Cr, a, n, w, pass, stream); });
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

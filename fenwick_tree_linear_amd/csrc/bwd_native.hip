@@ -4,29 +4,37 @@
 //
 // With pair weights M[t,s] = lambda_t^{lev(t,s)} e^{G_t - G_s} (s <= t, G the
 // inclusive prefix of log a) and E[t,s] = e^{G_t - G_s} (q_t . k_s)(dO_t . v_s):
-//   dq_t        = sum_s M[t,s] (dO_t . v_s) k_s        (the forward read with
-//                                                      (q,k,v) := (dO,v,k))
-//   dlambda_t^l = sum_{s: lev(t,s) = l} E[t,s]                   (ll_bwd_levels)
-//   dv_s        = sum_{t >= s} M[t,s] (q_t . k_s) dO_t           (ll_bwd_revread)
-//   dk_s        = sum_{t >= s} M[t,s] (dO_t . v_s) q_t           (the same, roles swapped)
-//   dlog_gate_r = sum_{s < r <= t} E[t,s] lambda_t^{lev(t,s)}   (the pairs the gate of r decays)
-// The gate gradient splits by pairs: those inside one chunk give, per chunk,
-// sum_{t >= r} (row sum of t) - sum_{s >= r} (column sum of s) over the chunk's
-// exact fp32 pair terms (ll_bwd_levels); those across chunks give the suffix
-// sum over all later tokens of dO_t . o_t^x - v_t . dv_t^x, the parts of
-// dO . o and v . dv (= k . dk) that come from other chunks (ll_bwd_gate).  Only
-// the cross-chunk parts, small where the gates decay within a chunk, run
-// through the long suffix sum.
+//   dlambda_t^l = sum_{s: lev(t,s) = l} E[t,s]
+//   dq_t        = sum_s M[t,s] (dO_t . v_s) k_s
+//   dv_s        = sum_{t >= s} M[t,s] (q_t . k_s) dO_t
+//   dk_s        = sum_{t >= s} M[t,s] (dO_t . v_s) q_t
+//   dlog_gate_r = sum_{s < r <= t} lambda_t^{lev(t,s)} E[t,s]   (the pairs the gate of r decays)
 //
-// The reverse sums: for a source s, the targets t at level l >= 1 form one
-// aligned bucket X, the sibling right after the aligned group of s, and every
-// aligned bucket is read at exactly one level (log2 |X| + 1).  So each bucket
-// keeps one state R_X = sum_{t in X} lambda_t^{lev(X)} e^{G_t - G_{X0-1}} q_t dO_t^T
-// (X0 its first token), and dv_s = sum_X e^{G_{X0-1} - G_s} R_X^T k_s plus
-// the in-chunk part.  Inside a block of chunks, a walk over the chunks from
-// the last to the first keeps the chunk-level buckets (ll_bwd_revread); above
-// it, ll_bwd_rev_state forms each block's share of the buckets it belongs to
-// and ll_bwd_rev_scan sums the shares into bucket states.
+// Forward walk (ll_bwd_fwalk): with S the Fenwick state of a bucket of
+// sources (sum e^{..} k_s v_s^T), one product u = S dO_t per level gives both
+// dlambda_t^l = e^{..} q_t . u and the level's share lambda_t^l e^{..} u of
+// dq_t.  The states are kept transposed (S^T, sum v_s k_s^T), so that the
+// product is a plain read of the tile layout; the block-level nodes are the
+// forward's block states and Fenwick nodes built from (v, k).
+//
+// Reverse walk (ll_bwd_rwalk): for a source s, the targets t at level l >= 1
+// form one aligned bucket X, the sibling right after the aligned group of s,
+// and every bucket is read at exactly one level (log2 |X| + 1).  One state per
+// bucket, R_X = sum_{t in X} lambda_t^{lev(X)} e^{G_t - G_{X0-1}} q_t dO_t^T
+// (X0 its first token), gives both dv_s += e^{G_{X0-1} - G_s} R_X^T k_s and
+// dk_s += e^{G_{X0-1} - G_s} R_X v_s.  Chunk-level buckets are built during
+// the walk (from the last chunk to the first); block-level buckets come from
+// ll_bwd_rev_state (each block's share) and ll_bwd_rev_scan (their sums).
+//
+// The gate gradient splits by pairs: those inside one chunk give, per chunk,
+// sum_{t >= r} (row sum of t) - sum_{s >= r} (column sum of s) over the
+// chunk's exact fp32 pair terms (forward walk); those across chunks give the
+// suffix sum over later tokens of dO_t . o_t^x - v_t . dv_t^x, the parts of
+// dO . o and v . dv (= k . dk) that come from other chunks (the reverse walk
+// sums within the block, ll_bwd_gate_add adds the later blocks).  Only the
+// cross-chunk parts, small where the gates decay within a chunk, run through
+// the long suffix sum.
+#include <mutex>
 #include <type_traits>
 
 #include "ll_device.hpp"
@@ -36,52 +44,51 @@ namespace llattn {
 
 namespace {
 
-// Staged chunk of the backward kernels: four [C][D] io tiles (row-major,
-// swizzled), the gates and the level weights of the chunk's rows.
-template <typename T, int D, int C>
-struct BwdStage {
-  typedef Tile<T, C, D> TL;
-  static constexpr int NWT = 8;  // weight rows
-  static constexpr int A = 0, B = TL::BYTES, X = 2 * TL::BYTES, Y = 3 * TL::BYTES;
-  static constexpr int G = 4 * TL::BYTES;   // gates [C]
-  static constexpr int GP = G + C * 4;      // in-chunk inclusive prefix of the gates [C]
-  static constexpr int WT = GP + C * 4;     // per-token weight rows [NWT][C]
-  static constexpr int LAM = WT + NWT * C * 4;  // level weights [C][kLevelsMax]
-  static constexpr int XIN = LAM + C * kLevelsMax * 4;  // in-chunk column sums per wave [C/16][C]
-  static constexpr int DOI = XIN + (C / 16) * C * 4;    // in-chunk row sums [C]
-  static constexpr int BYTES = DOI + C * 4;
+constexpr int logc_of(int C) { return C == 16 ? 4 : C == 32 ? 5 : 6; }
+
+// An fp32 D x D state in LDS: the tile layout (16x16 tiles, accumulator order)
+// with 4 floats of padding after every 16 lanes of a tile, so that reading a
+// tile across (one float per lane, ds_read_b32) touches distinct banks.
+template <int D>
+struct PadState {
+  static constexpr int DT = D / 16;
+  static constexpr int TS = 4 * 68;  // floats per tile
+  static constexpr int FLOATS = DT * DT * TS;
+  // float offset of the four floats lane `ln` holds in tile (tr, tc)
+  __device__ __forceinline__ static int off(int tr, int tc, int ln) { return (tr * DT + tc) * TS + 4 * ln + 4 * (ln >> 4); }
 };
 
-// Stages the gate prefix: wave 0 scans, every thread may read it after the
-// caller's next barrier.  Returns the chunk's gate sum (every wave).
-template <int C>
-__device__ __forceinline__ float stage_prefix(const float* gl, float* gp, int wv, int lane) {
-  const float G = chunk_scan<C>(lane < C ? gl[lane] : 0.f);
-  if (wv == 0 && lane < C) gp[lane] = G;
-  return __shfl(G, C - 1, 64);
+// A fragments of a state X in the tile layout: rows = column 16 tc + lane%16
+// of X, k = the rows of X.  ld(tr, tc) returns this lane's four floats of
+// tile (tr, tc).
+template <typename T, int D, typename Ld>
+__device__ __forceinline__ void col_frags(typename Mma<T>::Frag (&nf)[D / Mma<T>::KS], int tc, Ld ld) {
+  f32x4 t[D / 16];
+#pragma unroll
+  for (int tr = 0; tr < D / 16; ++tr) t[tr] = ld(tr, tc);
+#pragma unroll
+  for (int s = 0; s < D / Mma<T>::KS; ++s) nf[s] = Mma<T>::acc_frag(t, s);
 }
 
-// Loads rows row0 .. row0 + (C-1) H of a [*, D] io tensor into a swizzled tile
-// (16-byte pieces; all threads of the workgroup take part).
-template <typename T, int D, int C>
-__device__ __forceinline__ void stage_tile(const void* src, int64_t row0, int H, char* lds, int tid, int nthreads) {
-  typedef Tile<T, C, D> TL;
-  constexpr int EPP = 16 / (int)sizeof(T);
-  for (int x = tid; x < TL::BYTES / 16; x += nthreads) {
-    const int r = x / TL::NCH, c = x % TL::NCH;
-    const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const T*>(src) + (row0 + (int64_t)r * H) * D + c * EPP);
-    *reinterpret_cast<uint4*>(lds + r * TL::RB + (TL::pos(r, c) << 4)) = v;
-  }
-}
-
-// Gates and the first LS level weights of the chunk's rows.
-template <int C>
-__device__ __forceinline__ void stage_gates(const float* g, const float* lam, int64_t row0, int H, int L, int LS,
-                                            float* gl, float* ll, int tid, int nthreads) {
-  for (int x = tid; x < C; x += nthreads) gl[x] = g[row0 + (int64_t)x * H];
-  for (int x = tid; x < C * LS; x += nthreads) {
-    const int r = x / LS, l = x % LS;
-    ll[r * kLevelsMax + l] = lam[(row0 + (int64_t)r * H) * L + l];
+// A fragments of a state X: rows = row 16 tr + lane%16 of X, k = the columns
+// of X, one float per lane and k index.  ld(tile_r, tile_c, lane, slot)
+// returns an element of X.
+template <typename T, int D, typename Ld>
+__device__ __forceinline__ void row_frags(typename Mma<T>::Frag (&nf)[D / Mma<T>::KS], int tr, int lane, Ld ld) {
+  using M = Mma<T>;
+  const int g = lane >> 4, ar = lane & 15;
+#pragma unroll
+  for (int s = 0; s < D / M::KS; ++s) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int b = M::kidx(s, g, e);
+        nf[s][e] = (bf16)ld(tr, b >> 4, 16 * (ar >> 2) + (b & 15), ar & 3);
+      }
+    } else {
+      const int b = M::kidx(s, g, 0);
+      nf[s] = ld(tr, b >> 4, 16 * (ar >> 2) + (b & 15), ar & 3);
+    }
   }
 }
 
@@ -92,7 +99,18 @@ __device__ __forceinline__ float sum_groups(float x) {
   return x;
 }
 
-// The block a (head, item) pair walks: first [B,T,H] row and its chunks.
+// Stages the gate prefix: every wave scans, wave 0 writes it to LDS for the
+// others (visible after the caller's next barrier).  Returns the chunk's gate
+// sum.
+template <int C>
+__device__ __forceinline__ float stage_prefix(const float* gl, float* gp, int wv, int lane) {
+  const float G = chunk_scan<C>(lane < C ? gl[lane] : 0.f);
+  if (wv == 0 && lane < C) gp[lane] = G;
+  return __shfl(G, C - 1, 64);
+}
+
+// The block a workgroup walks: (block J, head) from a logical id, and the
+// [B,T,H] row of the block's first token.
 struct BlockOf {
   int J, bh, h, b;
   int64_t row;
@@ -105,231 +123,382 @@ struct BlockOf {
   }
 };
 
+// LDS of the two walks: two staging buffers (each: the q, k, v and dO tiles,
+// the gates, two more per-row values and the level weights [C][LS] of one
+// chunk, loaded straight into LDS one chunk ahead), per-chunk scratch, and
+// the chunk-level states when they fit.
+template <typename T, int D, int C, int MAXB, bool SLDS>
+struct WalkSmem {
+  typedef Tile<T, C, D> TL;
+  static constexpr int NW = C / 16;
+  static constexpr int TQ = 0, TK = TL::BYTES, TV = 2 * TL::BYTES, TD = 3 * TL::BYTES;
+  static constexpr int GOFF = 4 * TL::BYTES;   // gates [C]
+  static constexpr int R1OFF = GOFF + C * 4;   // a per-row value [C]
+  static constexpr int R2OFF = R1OFF + C * 4;  // another [C]
+  static constexpr int LOFF = R2OFF + C * 4;   // level weights [C][LS]
+  static constexpr int BUF = LOFF + C * kLevelsMax * 4;
+  static constexpr int GP = 2 * BUF;             // in-chunk prefix of the gates [C]
+  static constexpr int WT = GP + C * 4;          // per-token weight rows [MAXB][C]
+  static constexpr int XIN = WT + MAXB * C * 4;  // per-wave column sums [NW][C]
+  static constexpr int DOI = XIN + NW * C * 4;   // row sums [C]
+  static constexpr int DL = DOI + C * 4;         // dlambda of the chunk's rows [C][kLevelsMax]
+  static constexpr int ST = DL + C * kLevelsMax * 4;  // chunk-level states [MAXB] (padded layout)
+  static constexpr int BYTES = ST + (SLDS ? MAXB * PadState<D>::FLOATS * 4 : 0);
+};
+
+// Fragment registers of one state, the budget for the nodes a walk holds.
+template <typename T, int D>
+constexpr int state_frag_vgprs() {
+  return (D / 16) * (D / Mma<T>::KS) * (int)(sizeof(typename Mma<T>::Frag) / 4);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// ll_bwd_levels: one workgroup per (block J, head), C/16 waves, wave rt owns
-// the 16 target rows rt of each chunk and every level.  Walks the block's
-// chunks in order, keeping the chunk-level Fenwick states of (k, v) (states
-// of earlier chunks of the block, merged by the recurrent form's rule) in
-// fp32; the states of earlier blocks are the forward's Fenwick nodes.
-//   dlambda_t^l = sum_{s in bucket l of t} e^{G_t - G_s} (q_t . k_s)(dO_t . v_s)
-//     in-chunk levels: from the score tiles (q.k and dO.v per pair, exact
-//       products of the io values, fp32 sums);
-//     other levels:    e^{...} q_t^T S_l dO_t, the state read Z^T = S^T Q^T on
-//       the matrix cores and its rows dotted with dO in fp32.
-// Writes dlambda (every level of every row, zero where the bucket is empty),
-// the cross-chunk part of dO_t . o_t (sum over levels above the chunk of
-// lambda_t^l dlambda_t^l) and, into dlog_gate, the in-chunk pairs' share of
-// the gate gradient.
-template <typename T, int D, int C, int MAXB>
-__global__ void __launch_bounds__(64 * (C / 16)) ll_bwd_levels(BwdArgs a, BwdFwdNodes n, float* dOo, float* wstates) {
+// ll_bwd_fwalk: one workgroup per (block J, head), C/16 waves; wave rt owns the
+// target rows 16 rt .. 16 rt + 15 of every chunk.  Walks the block's chunks in
+// order, keeping the chunk-level states (S^T of the chunks of earlier levels
+// of the block, merged by the recurrent form's rule) in fp32; the states of
+// earlier blocks are the forward's Fenwick nodes of (v, k), the first MAXH of
+// them held in registers for the whole walk.  Per chunk:
+//   in-chunk levels 0..log2 C: the score tiles q.k and dO.v per pair (exact
+//     products of the io values, fp32 sums) give the dlambda bins, the
+//     in-chunk dq weights and the gate's in-chunk share;
+//   other levels: u = S dO_r on the matrix cores, dlambda = e^{..} q_r . u,
+//     dq_r += lambda_r^l e^{..} u.
+// Writes dlambda (every level, zero where no bucket exists), dq, the
+// cross-chunk part of dO . o and the gate's in-chunk share.
+template <typename T, int D, int C, int MAXB, int MAXH, bool SLDS>
+__global__ void __launch_bounds__(64 * (C / 16)) ll_bwd_fwalk(BwdArgs a, BwdFwdNodes n, BwdWork w) {
   using M = Mma<T>;
   typedef typename M::Frag Frag;
-  typedef BwdStage<T, D, C> SG;
-  constexpr int NW = C / 16, DT = D / 16, KSD = D / M::KS;
-  constexpr int LOGC = (C == 16) ? 4 : (C == 32) ? 5 : 6;
-  constexpr int SB = D * D;  // floats of one state
-  __shared__ __attribute__((aligned(1024))) char smem[SG::BYTES];
+  typedef WalkSmem<T, D, C, MAXB, SLDS> SM;
+  typedef Tile<T, C, D> TL;
+  typedef PadState<D> PS;
+  typedef typename std::conditional<sizeof(T) == 2, bf16x4, f32x4>::type Vec4;
+  constexpr int NW = C / 16, DT = D / 16, KSD = D / M::KS, KSC = C / M::KS, CT = C / 16, LOGC = logc_of(C);
+  constexpr int SB = D * D;
+  constexpr int NH = MAXH > 0 ? MAXH : 1;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, q16 = lane & 15;
-  const int rt = wv;  // this wave's 16 target rows
+  const int rt = wv;
+  const int r = 16 * rt + q16;  // this lane's target row
   BlockOf bk;
-  bk.set(blockIdx.x, a, n.nb, n.P, C);
+  bk.set(xcd_logical_id(blockIdx.x, gridDim.x), a, n.nb, n.P, C);
   const int logP = ilog2c(n.P);
-  // chunk-level states of the block: MAXB levels, fp32 in the tile layout
-  float* st = wstates + (int64_t)blockIdx.x * MAXB * SB;
+  const int LS = n.LS;
+  float* gp = reinterpret_cast<float*>(smem + SM::GP);
+  float* wt = reinterpret_cast<float*>(smem + SM::WT);
+  float* dl = reinterpret_cast<float*>(smem + SM::DL);  // dlambda of the chunk's rows [C][kLevelsMax]
+  float* stl = reinterpret_cast<float*>(smem + SM::ST);
+  float* stg = SLDS ? nullptr : w.scratch + (int64_t)blockIdx.x * MAXB * SB;
+
+  ChunkLoads<T, D, C, NW> cl;
+  cl.init(wv, lane, a.H, a.L, LS);
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    const int64_t row0 = bk.row + (int64_t)j * C * a.H;
+    char* buf = smem + (j & 1) * SM::BUF;
+    cl.tiles(a.q, row0, buf + SM::TQ, wv);
+    cl.tiles(a.k, row0, buf + SM::TK, wv);
+    cl.tiles(a.v, row0, buf + SM::TV, wv);
+    cl.tiles(a.dO, row0, buf + SM::TD, wv);
+    cl.gates(a.g, row0, reinterpret_cast<float*>(buf + SM::GOFF), wv, lane);
+    cl.lambda(a.lam, row0, a.L, reinterpret_cast<float*>(buf + SM::LOFF), wv, lane);
+  };
+  issue(0);
+
+  // Fenwick nodes of earlier blocks, one per set bit of J, most recent first
+  auto node_ptr = [&](int e) {
+    return (e & 1) ? n.F + ((int64_t)bk.bh * n.nF + (e >> 1)) * SB : n.S + ((int64_t)bk.bh * n.nb + e) * SB;
+  };
+  auto node_gamma = [&](int e) {
+    return (e & 1) ? n.GF[(int64_t)bk.bh * n.nF + (e >> 1)] : n.GS[(int64_t)bk.bh * n.nb + e];
+  };
+  Frag nh[NH][DT][KSD];
+  int hlv[NH];
+  float hdd[NH];
+  int rest_far = bk.J;
+  float dd_far = 0.f;
+#pragma unroll
+  for (int x = 0; x < MAXH; ++x) {
+    hlv[x] = -1;
+    hdd[x] = 0.f;
+    if (rest_far > 0) {
+      const int e = rest_far - 1;
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(node_ptr(e), SB * 4);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        col_frags<T, D>(nh[x][dt], dt, [&](int tr, int tc) { return load_state_tile<D>(rs, tr, tc, lane); });
+      hlv[x] = LOGC + 1 + logP + __ffs(rest_far) - 1;
+      hdd[x] = dd_far;
+      dd_far += node_gamma(e);
+      rest_far &= rest_far - 1;
+    }
+  }
+
   float sig[MAXB + 1];  // lazy log-scales of the chunk-level states
 #pragma unroll
   for (int m = 0; m <= MAXB; ++m) sig[m] = 0.f;
   float gw = 0.f;  // log-decay from the block start to the current chunk's start
-  float* gl = reinterpret_cast<float*>(smem + SG::G);
-  float* gp = reinterpret_cast<float*>(smem + SG::GP);
-  float* wt = reinterpret_cast<float*>(smem + SG::WT);
-  const float* ll = reinterpret_cast<const float*>(smem + SG::LAM);
-  const char* sq = smem + SG::A;   // q
-  const char* sk = smem + SG::B;   // k
-  const char* sv = smem + SG::X;   // v
-  const char* sdo = smem + SG::Y;  // dO
 
-  // A fragments (rows = state column n of column tile nt, k = d) of an fp32
-  // state in the tile layout
-  auto state_frags = [&](Frag (&nf)[KSD], __amdgpu_buffer_rsrc_t S, int nt) __attribute__((always_inline)) {
-    f32x4 t[DT];
+  // outputs of a chunk, stored during the next one (dlambda from LDS)
+  float odo = 0.f, odin = 0.f;
+  Vec4 odq[DT];
+  auto store_out = [&](int jj) __attribute__((always_inline)) {
+    const int64_t row0 = bk.row + (int64_t)jj * C * a.H;
+    const int64_t orow = row0 + (int64_t)r * a.H;
+    // lane group g writes levels g, g + 4, ...
+    for (int l = g4; l < a.L; l += 4) a.dlambda[orow * a.L + l] = l < kLevelsMax ? dl[r * kLevelsMax + l] : 0.f;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) t[dt] = load_state_tile<D>(S, dt, nt, lane);
-#pragma unroll
-    for (int s = 0; s < KSD; ++s) nf[s] = M::acc_frag(t, s);
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<Vec4*>(static_cast<T*>(a.dq) + orow * D + 16 * dt + 4 * g4) = odq[dt];
+    if (g4 == 0) w.dOo[orow] = odo;
+    if (wv == 0 && lane < C) w.din[row0 + (int64_t)lane * a.H] = odin;
   };
 
   for (int j = 0; j < n.P; ++j) {
-    const int64_t row0 = bk.row + (int64_t)j * C * a.H;
-    __syncthreads();  // the previous chunk's tiles and state writes are done everywhere
-    stage_tile<T, D, C>(a.q, row0, a.H, smem + SG::A, tid, 64 * NW);
-    stage_tile<T, D, C>(a.k, row0, a.H, smem + SG::B, tid, 64 * NW);
-    stage_tile<T, D, C>(a.v, row0, a.H, smem + SG::X, tid, 64 * NW);
-    stage_tile<T, D, C>(a.dO, row0, a.H, smem + SG::Y, tid, 64 * NW);
-    stage_gates<C>(a.g, a.lam, row0, a.H, a.L, n.LS, gl, reinterpret_cast<float*>(smem + SG::LAM), tid, 64 * NW);
-    __syncthreads();
-    const float gsum = stage_prefix<C>(gl, gp, wv, lane);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk j and stores of chunk j-2 are done
+    lds_barrier();                  // chunk j has landed everywhere; chunk j-1 is done with
+    if (j > 0) store_out(j - 1);
+    if (j + 1 < n.P) issue(j + 1);
+    const char* buf = smem + (j & 1) * SM::BUF;
+    const char* sq = buf + SM::TQ;
+    const char* sk = buf + SM::TK;
+    const char* sv = buf + SM::TV;
+    const char* sdo = buf + SM::TD;
+    const float* ll = reinterpret_cast<const float*>(buf + SM::LOFF);  // [C][LS]
+    const float gsum = stage_prefix<C>(reinterpret_cast<const float*>(buf + SM::GOFF), gp, wv, lane);
+    lds_barrier();  // also: the previous chunk's dlambda rows have been read
     // decay of each source row to the chunk's end, for this chunk's own state
     for (int x = tid; x < C; x += 64 * NW) wt[x] = __expf(gsum - gp[x]);
-    const int r = 16 * rt + q16;  // this lane's target row
+    // this wave's dlambda rows start at zero (levels no bucket reaches)
+    for (int x = lane; x < 16 * kLevelsMax; x += 64) dl[16 * rt * kLevelsMax + x] = 0.f;
     const float Gr = gp[r];
-    float lamr[LOGC + 1];  // in-chunk level weights of row r
+    const float* lr = ll + r * LS;  // level weights of row r
+    Frag qfr[KSD], dofr[KSD];       // rows r of q and dO (k = head dim)
 #pragma unroll
-    for (int l = 0; l <= LOGC; ++l) lamr[l] = ll[r * kLevelsMax + l];
+    for (int k = 0; k < KSD; ++k) {
+      qfr[k] = frag_row<T, C, D>(sq, r, k, g4);
+      dofr[k] = frag_row<T, C, D>(sdo, r, k, g4);
+    }
 
-    // --- in-chunk levels 0..LOGC: per pair (s, r), s <= r, level bit_length(r ^ s);
-    // the weighted pair terms are also summed per source (column) for the gate
+    // --- in-chunk levels 0..LOGC.  Lanes hold sources s = 16 ct + 4 (lane/16) + e
+    // of target r; a tile ct < rt lies at the one level 4 + bit_length(rt ^ ct),
+    // the diagonal tile at levels bit_length((r ^ s) % 16) <= 4.
     float bin[LOGC + 1];
 #pragma unroll
     for (int l = 0; l <= LOGC; ++l) bin[l] = 0.f;
-    float* xin = reinterpret_cast<float*>(smem + SG::XIN) + rt * C;
-    for (int ct = 0; ct <= rt; ++ct) {
+    f32x4 ptl[CT];  // in-chunk dq weights lambda_r^lev e^{G_r - G_s} (dO_r . v_s), rows s
+    float* xin = reinterpret_cast<float*>(smem + SM::XIN) + rt * C;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      ptl[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (ct > rt) continue;
       f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f}, y = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KSD; ++s) {
-        x = M::mma(frag_row<T, C, D>(sk, 16 * ct + q16, s, g4), frag_row<T, C, D>(sq, r, s, g4), x);
-        y = M::mma(frag_row<T, C, D>(sv, 16 * ct + q16, s, g4), frag_row<T, C, D>(sdo, r, s, g4), y);
+      for (int k = 0; k < KSD; ++k) {
+        x = M::mma(frag_row<T, C, D>(sk, 16 * ct + q16, k, g4), qfr[k], x);
+        y = M::mma(frag_row<T, C, D>(sv, 16 * ct + q16, k, g4), dofr[k], y);
       }
-      // lane: sources s = 16 ct + 4 (lane/16) + e of target r
       const f32x4 gs = *reinterpret_cast<const f32x4*>(gp + 16 * ct + 4 * g4);
       f32x4 col;
+      if (ct < rt) {
+        const int lev = 4 + 32 - __clz(rt ^ ct);
+        const float lam = lr[lev];
+        float sxy = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int s = 16 * ct + 4 * g4 + e;
-        col[e] = 0.f;
-        if (s <= r) {
-          const int lev = (s == r) ? 0 : 32 - __clz(r ^ s);
-          const float v = x[e] * y[e] * __expf(Gr - gs[e]);
+        for (int e = 0; e < 4; ++e) {
+          const float ey = y[e] * __expf(Gr - gs[e]);
+          sxy += x[e] * ey;
+          ptl[ct][e] = lam * ey;
+          col[e] = lam * x[e] * ey;
+        }
 #pragma unroll
-          for (int l = 0; l <= LOGC; ++l)
-            if (l == lev) {
-              bin[l] += v;
-              col[e] = lamr[l] * v;
-            }
+        for (int l = 5; l <= LOGC; ++l)
+          if (l == lev) bin[l] += sxy;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s4 = 4 * g4 + e;  // source within the tile
+          float ey = 0.f, lam = 0.f;
+          int lev = 0;
+          if (s4 <= q16) {
+            lev = 32 - __clz(q16 ^ s4);
+            lam = lr[lev];
+            ey = y[e] * __expf(Gr - gs[e]);
+          }
+          const float v = x[e] * ey;
+#pragma unroll
+          for (int l = 0; l <= 4; ++l)
+            if (l == lev) bin[l] += v;
+          ptl[ct][e] = lam * ey;
+          col[e] = lam * v;
         }
       }
-      // column sums over this wave's 16 targets (the lanes of a 16-lane group)
+      // column sums over this wave's 16 targets: a prefix within each 16-lane row, total at lane 15
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) col[e] += __shfl_xor(col[e], m, 64);
-      if (q16 == 0) *reinterpret_cast<f32x4*>(xin + 16 * ct + 4 * g4) = col;
+      for (int e = 0; e < 4; ++e) {
+        col[e] += dpp_f32<0x111, 0xf, true>(col[e]);
+        col[e] += dpp_f32<0x112, 0xf, true>(col[e]);
+        col[e] += dpp_f32<0x114, 0xf, true>(col[e]);
+        col[e] += dpp_f32<0x118, 0xf, true>(col[e]);
+      }
+      if (q16 == 15) *reinterpret_cast<f32x4*>(xin + 16 * ct + 4 * g4) = col;
     }
-    float dlam[kLevelsMax];
+    float rsum = 0.f;  // row sum of the in-chunk pair terms
 #pragma unroll
-    for (int l = 0; l < kLevelsMax; ++l) dlam[l] = 0.f;
+    for (int l = 0; l <= LOGC; ++l) {
+      const float v = sum_groups(bin[l]);
+      rsum += lr[l] * v;
+      if (g4 == 0) dl[r * kLevelsMax + l] = v;
+    }
+    if (g4 == 0) reinterpret_cast<float*>(smem + SM::DOI)[r] = rsum;
+
+    // --- in-chunk dq: dq^T[d][r] = sum_s k^T[d][s] P[s][r]
+    f32x4 dq[DT];
+    {
+      Frag pf[KSC];
 #pragma unroll
-    for (int l = 0; l <= LOGC; ++l) dlam[l] = sum_groups(bin[l]);
-    if (g4 == 0) {  // row sum of the in-chunk pair terms of row r
-      float rs = 0.f;
+      for (int k = 0; k < KSC; ++k) pf[k] = M::acc_frag(ptl, k);
 #pragma unroll
-      for (int l = 0; l <= LOGC; ++l) rs += lamr[l] * dlam[l];
-      reinterpret_cast<float*>(smem + SG::DOI)[r] = rs;
+      for (int dt = 0; dt < DT; ++dt) {
+        Frag kf[KSC];
+#pragma unroll
+        for (int k = 0; k < KSC; ++k) kf[k] = frag_col<T, C, D>(sk, 16 * dt, k, lane);
+        lds_wait(kf);
+        dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < KSC; ++k)
+          if (M::first_tile(k) <= rt) dq[dt] = M::mma(kf[k], pf[k], dq[dt]);
+      }
     }
 
-    // --- other levels: e^{G_r + D} q_r^T S dO_r for every non-empty level of the chunk
-    auto level_dot = [&](const float* S, float scale) __attribute__((always_inline)) {
-      // Z^T[n][r] = sum_d S[d][n] q[r][d]; lane: n = 16 nt + 4 (lane/16) + e, row r
-      Frag qf[KSD];
+    // --- other levels: u = S dO_r (lanes: rows d = 16 dt + 4 (lane/16) + e)
+    f32x4 qv[DT];  // q_r at those rows
 #pragma unroll
-      for (int s = 0; s < KSD; ++s) qf[s] = frag_row<T, C, D>(sq, r, s, g4);
-      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(S, SB * 4);
+    for (int dt = 0; dt < DT; ++dt) {
+      const T* p = reinterpret_cast<const T*>(sq + TL::off(r, 16 * dt + 4 * g4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[dt][e] = to_f32(p[e]);
+    }
+    odo = 0.f;
+    // one level: scale = e^{G_r + decay from the state's end to the chunk start}
+    auto level = [&](auto get, float scale, int lev) __attribute__((always_inline)) {
+      const float lamw = lr[lev];
       float acc = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < DT; ++nt) {
+      for (int dt = 0; dt < DT; ++dt) {
         Frag nf[KSD];
-        state_frags(nf, rs, nt);
+        get(dt, nf);
         f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KSD; ++s) z = M::mma(nf[s], qf[s], z);
-        const T* drow = reinterpret_cast<const T*>(sdo + Tile<T, C, D>::off(r, 16 * nt + 4 * g4));
+        for (int k = 0; k < KSD; ++k) z = M::mma(nf[k], dofr[k], z);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc += z[e] * to_f32(drow[e]);
+        for (int e = 0; e < 4; ++e) acc += z[e] * qv[dt][e];
+        dq[dt] += (lamw * scale) * z;
       }
-      return sum_groups(acc) * scale;
+      const float v = sum_groups(acc) * scale;
+      odo += lamw * v;
+      if (g4 == 0) dl[r * kLevelsMax + lev] = v;
     };
     // within-block levels LOGC+1 .. LOGC+logP: states of earlier chunks of the block
 #pragma unroll
     for (int m = 1; m <= MAXB; ++m)
-      if (m <= logP && ((j >> (m - 1)) & 1)) dlam[LOGC + m] = level_dot(st + (m - 1) * SB, __expf(Gr + sig[m]));
-    // earlier blocks: one Fenwick node per set bit of J, most recent first
+      if (m <= logP && ((j >> (m - 1)) & 1)) {
+        if constexpr (SLDS) {
+          const float* X = stl + (m - 1) * PS::FLOATS;
+          level(
+              [&](int dt, Frag(&nf)[KSD]) {
+                col_frags<T, D>(nf, dt, [&](int tr, int tc) {
+                  return *reinterpret_cast<const f32x4*>(X + PS::off(tr, tc, lane));
+                });
+              },
+              __expf(Gr + sig[m]), LOGC + m);
+        } else {
+          const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(stg + (m - 1) * SB, SB * 4);
+          level(
+              [&](int dt, Frag(&nf)[KSD]) {
+                col_frags<T, D>(nf, dt, [&](int tr, int tc) { return load_state_tile<D>(rs, tr, tc, lane); });
+              },
+              __expf(Gr + sig[m]), LOGC + m);
+        }
+      }
+    // earlier blocks: the nodes held in registers, then the rest from memory
+#pragma unroll
+    for (int x = 0; x < MAXH; ++x)
+      if (hlv[x] >= 0)
+        level(
+            [&](int dt, Frag(&nf)[KSD]) {
+#pragma unroll
+              for (int k = 0; k < KSD; ++k) nf[k] = nh[x][dt][k];
+            },
+            __expf(Gr + gw + hdd[x]), hlv[x]);
     {
-      int rest = bk.J;
-      float dd = 0.f;
+      int rest = rest_far;
+      float dd = dd_far;
       while (rest > 0) {
         const int e = rest - 1;
-        const int lev = LOGC + 1 + logP + __ffs(rest) - 1;
-        const float* node = (e & 1) ? n.F + ((int64_t)bk.bh * n.nF + (e >> 1)) * SB : n.S + ((int64_t)bk.bh * n.nb + e) * SB;
-        const float val = level_dot(node, __expf(Gr + gw + dd));
-#pragma unroll
-        for (int l = 0; l < kLevelsMax; ++l)
-          if (l == lev) dlam[l] = val;
-        dd += (e & 1) ? n.GF[(int64_t)bk.bh * n.nF + (e >> 1)] : n.GS[(int64_t)bk.bh * n.nb + e];
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(node_ptr(e), SB * 4);
+        level(
+            [&](int dt, Frag(&nf)[KSD]) {
+              col_frags<T, D>(nf, dt, [&](int tr, int tc) { return load_state_tile<D>(rs, tr, tc, lane); });
+            },
+            __expf(Gr + gw + dd), LOGC + 1 + logP + __ffs(rest) - 1);
+        dd += node_gamma(e);
         rest &= rest - 1;
       }
     }
-
-    // --- outputs of row r (lane group 0 writes)
-    if (g4 == 0) {
-      const int64_t orow = row0 + (int64_t)r * a.H;
-      const float* lr = ll + r * kLevelsMax;
-      float dot = 0.f;  // dO_r . o_r^x: the levels above the chunk
-      for (int l = 0; l < a.L; ++l) {
-        float v = 0.f;
 #pragma unroll
-        for (int x = 0; x < kLevelsMax; ++x)
-          if (x == l) v = dlam[x];
-        if (l > LOGC && l < n.LS) dot += lr[l] * v;
-        a.dlambda[orow * a.L + l] = l < n.LS ? v : 0.f;
-      }
-      dOo[orow] = dot;
-    }
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) odq[dt][e] = (T)dq[dt][e];
 
-    // --- this chunk's state K_w^T V (keys scaled by e^{G[C-1] - G_s}) and the
-    // merge rule of the chunk-level states (levels 1..c and the chunk become
-    // level c+1, c = ctz(j+1)); each wave makes the state tiles dt = wave,
-    // wave + NW, ... of every column tile
-    __syncthreads();  // every wave has read the states of this chunk
+    lds_barrier();  // column and row sums are in; every wave has read the states of this chunk
     // in-chunk share of the gate gradient: sum_{t >= p} (row sum t - column sum t)
     if (wv == 0) {
       float u = 0.f;
       if (lane < C) {
-        const float* xs = reinterpret_cast<const float*>(smem + SG::XIN);
-        u = reinterpret_cast<const float*>(smem + SG::DOI)[lane];
-        for (int w = lane / 16; w < NW; ++w) u -= xs[w * C + lane];  // waves of targets >= the column's tile
+        const float* xs = reinterpret_cast<const float*>(smem + SM::XIN);
+        u = reinterpret_cast<const float*>(smem + SM::DOI)[lane];
+        for (int v = lane / 16; v < NW; ++v) u -= xs[v * C + lane];  // waves of targets >= the column's tile
       }
       const float pre = chunk_scan<C>(u);
-      if (lane < C) a.dlog_gate[row0 + (int64_t)lane * a.H] = __shfl(pre, C - 1, 64) - pre + u;
+      odin = __shfl(pre, C - 1, 64) - pre + u;
     }
+
+    // --- this chunk's state and the merge rule of the chunk-level states
+    // (levels 1..c and the chunk become level c+1, c = ctz(j+1)), kept as S^T:
+    // tile (nt, dt) = sum_s e^{G[C-1] - G_s} v_s[n] k_s[d]; wave w makes the
+    // row tiles nt = w, w + NW, ...
 #pragma unroll
     for (int m = 1; m <= MAXB; ++m) sig[m] += gsum;
     gw += gsum;
     if (j + 1 < n.P) {
       const int c = __ffs(j + 1) - 1;
-      // per-lane decay of the source rows to the chunk's end, k-step order
-      for (int dt = wv; dt < DT; dt += NW) {
-        Frag kf[C / M::KS];
+      for (int nt = wv; nt < DT; nt += NW) {
+        Frag vf[KSC];
 #pragma unroll
-        for (int s = 0; s < C / M::KS; ++s) kf[s] = frag_col<T, C, D>(sk, 16 * dt, s, lane);
-        for (int nt = 0; nt < DT; ++nt) {
-          Frag vf[C / M::KS];
+        for (int k = 0; k < KSC; ++k) vf[k] = frag_col<T, C, D>(sv, 16 * nt, k, lane);
+        lds_wait(vf);
 #pragma unroll
-          for (int s = 0; s < C / M::KS; ++s) vf[s] = frag_col<T, C, D>(sv, 16 * nt, s, lane);
-          lds_wait(kf, vf);
+        for (int k = 0; k < KSC; ++k) vf[k] = scale_tokens<T>(vf[k], wt, k, g4);
+        for (int dt = 0; dt < DT; ++dt) {
+          Frag kf[KSC];
+#pragma unroll
+          for (int k = 0; k < KSC; ++k) kf[k] = frag_col<T, C, D>(sk, 16 * dt, k, lane);
+          lds_wait(kf);
           f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+          float* dst = SLDS ? stl + c * PS::FLOATS + PS::off(nt, dt, lane) : stg + c * SB + state_tile_offset<D>(nt, dt, lane);
 #pragma unroll
           for (int m = 1; m <= MAXB; ++m)
             if (m <= c) {
-              const f32x4 old = *reinterpret_cast<const f32x4*>(st + (m - 1) * SB + state_tile_offset<D>(dt, nt, lane));
-              acc += __expf(sig[m]) * old;
+              const float* src = SLDS ? stl + (m - 1) * PS::FLOATS + PS::off(nt, dt, lane)
+                                      : stg + (m - 1) * SB + state_tile_offset<D>(nt, dt, lane);
+              acc += __expf(sig[m]) * *reinterpret_cast<const f32x4*>(src);
             }
 #pragma unroll
-          for (int s = 0; s < C / M::KS; ++s) acc = M::mma(kf[s], scale_tokens<T>(vf[s], wt, s, g4), acc);
-          *reinterpret_cast<f32x4*>(st + c * SB + state_tile_offset<D>(dt, nt, lane)) = acc;
+          for (int k = 0; k < KSC; ++k) acc = M::mma(vf[k], kf[k], acc);
+          *reinterpret_cast<f32x4*>(dst) = acc;
         }
       }
 #pragma unroll
@@ -337,6 +506,8 @@ __global__ void __launch_bounds__(64 * (C / 16)) ll_bwd_levels(BwdArgs a, BwdFwd
         if (m == c + 1) sig[m] = 0.f;
     }
   }
+  lds_barrier();  // the last chunk's dlambda rows are in
+  store_out(n.P - 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -344,61 +515,79 @@ __global__ void __launch_bounds__(64 * (C / 16)) ll_bwd_levels(BwdArgs a, BwdFwd
 // levels), D/16 waves (one per 16 value columns).  For every block level b of
 // the group with bit b of J set (J lies in a right bucket of 2^b blocks), the
 // block's share of that bucket's state,
-//   W[J][b] = sum_{t in J} lambda_t^{l_b} e^{G_t - G_{J0-1}} kr_t vr_t^T,
-// l_b = log2(C P) + 1 + b, in the tile layout; (kr, vr) = (q, dO) for dv and
-// (dO, q) for dk.
+//   W[J][b] = sum_{t in J} lambda_t^{l_b} e^{G_t - G_{J0-1}} q_t dO_t^T,
+// l_b = log2(C P) + 1 + b, in the tile layout.  The chunks are loaded straight
+// into LDS one chunk ahead.
+template <typename T, int D, int C>
+struct RevSmem {
+  typedef Tile<T, C, D> TL;
+  static constexpr int TQ = 0, TD = TL::BYTES;
+  static constexpr int GOFF = 2 * TL::BYTES;
+  static constexpr int LOFF = GOFF + C * 4;
+  static constexpr int BUF = LOFF + C * kLevelsMax * 4;
+  static constexpr int GP = 2 * BUF;
+  static constexpr int WT = GP + C * 4;  // weight rows [NLB][C]
+};
+
 template <typename T, int D, int C, int NLB>
-__global__ void __launch_bounds__(64 * (D / 16)) ll_bwd_rev_state(BwdArgs a, BwdFwdNodes n, const void* kr,
-                                                                  const void* vr, float* W, int nbl) {
+__global__ void __launch_bounds__(64 * (D / 16)) ll_bwd_rev_state(BwdArgs a, BwdFwdNodes n, BwdWork w) {
   using M = Mma<T>;
   typedef typename M::Frag Frag;
-  typedef BwdStage<T, D, C> SG;
-  constexpr int NW = D / 16, DT = D / 16, KSC = C / M::KS;
-  constexpr int LOGC = (C == 16) ? 4 : (C == 32) ? 5 : 6;
+  typedef RevSmem<T, D, C> SM;
+  constexpr int NW = D / 16, DT = D / 16, KSC = C / M::KS, LOGC = logc_of(C);
   constexpr int SB = D * D;
-  __shared__ __attribute__((aligned(1024))) char smem[SG::BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[SM::WT + NLB * C * 4];
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4;
   BlockOf bk;
-  bk.set(blockIdx.x, a, n.nb, n.P, C);
+  bk.set(xcd_logical_id(blockIdx.x, gridDim.x), a, n.nb, n.P, C);
   const int logP = ilog2c(n.P);
+  const int nbl = w.nbl;
   const int b0 = blockIdx.y * NLB;  // first block level of this group
   // this group's levels that J takes part in (bit b0 + b of J set)
   const int bits = (bk.J >> b0) & ((1 << NLB) - 1) & ((1 << (nbl > b0 ? nbl - b0 : 0)) - 1);
   if (bits == 0) return;
+  const int LS = n.LS;
+  float* gp = reinterpret_cast<float*>(smem + SM::GP);
+  float* wt = reinterpret_cast<float*>(smem + SM::WT);
+  ChunkLoads<T, D, C, NW> cl;
+  cl.init(wv, lane, a.H, a.L, LS);
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    const int64_t row0 = bk.row + (int64_t)j * C * a.H;
+    char* buf = smem + (j & 1) * SM::BUF;
+    cl.tiles(a.q, row0, buf + SM::TQ, wv);
+    cl.tiles(a.dO, row0, buf + SM::TD, wv);
+    cl.gates(a.g, row0, reinterpret_cast<float*>(buf + SM::GOFF), wv, lane);
+    cl.lambda(a.lam, row0, a.L, reinterpret_cast<float*>(buf + SM::LOFF), wv, lane);
+  };
+  issue(0);
   f32x4 acc[NLB][DT];
 #pragma unroll
   for (int b = 0; b < NLB; ++b)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[b][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float* gl = reinterpret_cast<float*>(smem + SG::G);
-  float* gp = reinterpret_cast<float*>(smem + SG::GP);
-  float* wt = reinterpret_cast<float*>(smem + SG::WT);
-  const float* ll = reinterpret_cast<const float*>(smem + SG::LAM);
-  static_assert(NLB <= SG::NWT, "a weight row per block level");
   float pre = 0.f;  // G_{chunk start - 1} - G_{J0 - 1}
   for (int j = 0; j < n.P; ++j) {
-    const int64_t row0 = bk.row + (int64_t)j * C * a.H;
-    __syncthreads();
-    stage_tile<T, D, C>(kr, row0, a.H, smem + SG::A, tid, 64 * NW);
-    stage_tile<T, D, C>(vr, row0, a.H, smem + SG::B, tid, 64 * NW);
-    stage_gates<C>(a.g, a.lam, row0, a.H, a.L, n.LS, gl, reinterpret_cast<float*>(smem + SG::LAM), tid, 64 * NW);
-    __syncthreads();
-    const float gsum = stage_prefix<C>(gl, gp, wv, lane);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+    if (j + 1 < n.P) issue(j + 1);
+    const char* buf = smem + (j & 1) * SM::BUF;
+    const float* ll = reinterpret_cast<const float*>(buf + SM::LOFF);
+    const float gsum = stage_prefix<C>(reinterpret_cast<const float*>(buf + SM::GOFF), gp, wv, lane);
+    lds_barrier();
     // weight rows lambda_t^{l_b} e^{G_t - G_{J0-1}} of the block levels J lies in
     for (int x = tid; x < NLB * C; x += 64 * NW) {
       const int b = x / C, t = x % C;
-      if ((bits >> b) & 1) wt[x] = ll[t * kLevelsMax + LOGC + logP + 1 + b0 + b] * __expf(pre + gp[t]);
+      if ((bits >> b) & 1) wt[x] = ll[t * LS + LOGC + logP + 1 + b0 + b] * __expf(pre + gp[t]);
     }
-    __syncthreads();
+    lds_barrier();
     Frag kf[DT][KSC], vf[KSC];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int s = 0; s < KSC; ++s) kf[dt][s] = frag_col<T, C, D>(smem + SG::A, 16 * dt, s, lane);
+      for (int s = 0; s < KSC; ++s) kf[dt][s] = frag_col<T, C, D>(buf + SM::TQ, 16 * dt, s, lane);
 #pragma unroll
-    for (int s = 0; s < KSC; ++s) vf[s] = frag_col<T, C, D>(smem + SG::B, 16 * wv, s, lane);
+    for (int s = 0; s < KSC; ++s) vf[s] = frag_col<T, C, D>(buf + SM::TD, 16 * wv, s, lane);
     lds_wait(kf, vf);
 #pragma unroll
     for (int b = 0; b < NLB; ++b) {
@@ -415,7 +604,7 @@ __global__ void __launch_bounds__(64 * (D / 16)) ll_bwd_rev_state(BwdArgs a, Bwd
 #pragma unroll
   for (int b = 0; b < NLB; ++b) {
     if (!((bits >> b) & 1)) continue;
-    float* dst = W + (((int64_t)bk.bh * n.nb + bk.J) * nbl + b0 + b) * SB;
+    float* dst = w.W + (((int64_t)bk.bh * n.nb + bk.J) * nbl + b0 + b) * SB;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(dst + state_tile_offset<D>(dt, wv, lane)) = acc[b][dt];
   }
@@ -423,11 +612,13 @@ __global__ void __launch_bounds__(64 * (D / 16)) ll_bwd_rev_state(BwdArgs a, Bwd
 
 // ---------------------------------------------------------------------------
 // ll_bwd_rev_scan: for every head, block level b and right bucket X of 2^b
-// blocks (X = blocks x 2^b .. (x+1) 2^b - 1, x odd), the bucket state
+// blocks (blocks x 2^b .. (x+1) 2^b - 1, x odd), the bucket state
 //   R_X = sum_{J in X} e^{G_{J0-1} - G_{X0-1}} W[J][b],
-// written in place of W[x 2^b][b].  One thread per four state elements.
-__global__ void __launch_bounds__(256) ll_bwd_rev_scan(BwdFwdNodes n, int BH, int DD, float* W, int nbl) {
-  const int n4 = DD / 4;
+// written in place of W[x 2^b][b], and R_X^T at the same place of WT.  One
+// thread per four state elements.
+__global__ void __launch_bounds__(256) ll_bwd_rev_scan(BwdFwdNodes n, int BH, int D, BwdWork w) {
+  const int DD = D * D, n4 = DD / 4, DT = D / 16;
+  const int nbl = w.nbl;
   const int64_t total = (int64_t)BH * nbl * n.nb * n4;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     const int e4 = (int)(i % n4);
@@ -440,208 +631,358 @@ __global__ void __launch_bounds__(256) ll_bwd_rev_scan(BwdFwdNodes n, int BH, in
     f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
     float dec = 0.f;
     for (int J = first; J < first + (1 << b) && J < n.nb; ++J) {
-      const f32x4 w = reinterpret_cast<const f32x4*>(W + (((int64_t)bh * n.nb + J) * nbl + b) * DD)[e4];
-      sum += __expf(dec) * w;
+      const f32x4 v = reinterpret_cast<const f32x4*>(w.W + (((int64_t)bh * n.nb + J) * nbl + b) * DD)[e4];
+      sum += __expf(dec) * v;
       dec += n.GS[(int64_t)bh * n.nb + J];
     }
-    reinterpret_cast<f32x4*>(W + (((int64_t)bh * n.nb + first) * nbl + b) * DD)[e4] = sum;
+    const int64_t at = (((int64_t)bh * n.nb + first) * nbl + b) * DD;
+    reinterpret_cast<f32x4*>(w.W + at)[e4] = sum;
+    // e4: lane ln of tile (dt, nt), elements (16 dt + 4 (ln/16) + i, 16 nt + ln%16);
+    // transposed, element (x, y) goes to tile (x/16, y/16), lane 16 ((x%16)/4) + y%16, slot x%4
+    const int tile = e4 / 64, ln = e4 % 64;
+    const int dt = tile / DT, nt = tile % DT;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int dr = 4 * (ln / 16) + s, nr = ln % 16;  // (d, n) within the tile
+      w.WT[at + ((int64_t)(nt * DT + dt) * 64 + 16 * (nr / 4) + dr) * 4 + (nr % 4)] = sum[s];
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// ll_bwd_revread: one workgroup per (block J, head), C/16 waves, wave rt owns
-// the 16 source rows rt of each chunk and every output column.  Walks the
-// block's chunks from the last to the first:
-//   out_s = sum_{t >= s in chunk} P[t,s] vr_t,  P[t,s] = lambda_t^{lev} e^{G_t - G_s} (kr_t . qr_s)
-//         + sum over the buckets X after s: e^{G_{X0-1} - G_s} R_X^T qr_s
-// with (qr, kr, vr) = (k, q, dO) for dv and (v, dO, q) for dk.  Chunk-level
-// buckets are kept in fp32 (one per within-block level, built from the
-// chunks already walked); block-level buckets come from ll_bwd_rev_scan.
-// With xdot given, also writes xdot_s . (the buckets' part of out_s) in fp32:
-// v . dv^x, the cross-chunk part of v . dv (= k . dk).
-template <typename T, int D, int C, int MAXB>
-__global__ void __launch_bounds__(64 * (C / 16)) ll_bwd_revread(BwdArgs a, BwdFwdNodes n, const void* qr, const void* kr,
-                                                                const void* vr, const float* W, int nbl, void* out,
-                                                                const void* xdot, float* dot_out, float* rstates) {
+// ll_bwd_rwalk: one workgroup per (block J, head), C/16 waves; wave st owns the
+// source rows 16 st .. 16 st + 15 of every chunk.  Walks the block's chunks
+// from the last to the first:
+//   dv_s = sum_{t >= s in chunk} P1[t,s] dO_t + sum_X e^{G_{X0-1} - G_s} R_X^T k_s
+//   dk_s = sum_{t >= s in chunk} P2[t,s] q_t  + sum_X e^{G_{X0-1} - G_s} R_X v_s
+//   P1[t,s] = M[t,s] (q_t . k_s),  P2[t,s] = M[t,s] (dO_t . v_s)
+// over the buckets X after s.  Chunk-level buckets are built from the chunks
+// already walked and kept in fp32 (read both ways: R for dv, R^T for dk);
+// block-level buckets come from ll_bwd_rev_scan, the first MAXH held in
+// registers.  Also: v_s . dv_s^x from the buckets (before the in-chunk terms),
+// and the gate gradient of every row up to the later blocks' share:
+//   din_s + sum_{t >= s in the block} (dOo_t - v_t . dv_t^x),
+// with the block's total left in BT for ll_bwd_gate_add.
+template <typename T, int D, int C, int MAXB, int MAXH, bool SLDS>
+__global__ void __launch_bounds__(64 * (C / 16)) ll_bwd_rwalk(BwdArgs a, BwdFwdNodes n, BwdWork w) {
   using M = Mma<T>;
   typedef typename M::Frag Frag;
-  typedef BwdStage<T, D, C> SG;
+  typedef WalkSmem<T, D, C, MAXB, SLDS> SM;
   typedef Tile<T, C, D> TL;
+  typedef PadState<D> PS;
   typedef typename std::conditional<sizeof(T) == 2, bf16x4, f32x4>::type Vec4;
-  constexpr int NW = C / 16, CT = C / 16, DT = D / 16, KSD = D / M::KS, KSC = C / M::KS;
-  constexpr int LOGC = (C == 16) ? 4 : (C == 32) ? 5 : 6;
+  constexpr int NW = C / 16, DT = D / 16, KSD = D / M::KS, KSC = C / M::KS, CT = C / 16, LOGC = logc_of(C);
   constexpr int SB = D * D;
-  __shared__ __attribute__((aligned(1024))) char smem[SG::BYTES];
+  constexpr int NH = MAXH > 0 ? MAXH : 1;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, q16 = lane & 15;
-  const int st_ = wv;  // this wave's 16 source rows
+  const int s = 16 * wv + q16;  // this lane's source row
   BlockOf bk;
-  bk.set(blockIdx.x, a, n.nb, n.P, C);
+  bk.set(xcd_logical_id(blockIdx.x, gridDim.x), a, n.nb, n.P, C);
   const int logP = ilog2c(n.P);
-  float* Rm = rstates + (int64_t)blockIdx.x * MAXB * SB;  // chunk-level bucket states, fp32 tile layout
-  float sufX[MAXB + 1];  // gate sum of the walked chunks from each level's bucket start to the block end
-#pragma unroll
-  for (int m = 0; m <= MAXB; ++m) sufX[m] = 0.f;
-  float suf = 0.f;  // gate sum of the chunks after the current one, to the block end
-  float* gl = reinterpret_cast<float*>(smem + SG::G);
-  float* gp = reinterpret_cast<float*>(smem + SG::GP);
-  float* wt = reinterpret_cast<float*>(smem + SG::WT);
-  const float* ll = reinterpret_cast<const float*>(smem + SG::LAM);
-  static_assert(MAXB <= SG::NWT, "a weight row per chunk level");
-  const char* sq = smem + SG::A;  // qr (readers)
-  const char* sk = smem + SG::B;  // kr
-  const char* sv = smem + SG::X;  // vr
-  const char* sx = smem + SG::Y;  // xdot rows
+  const int LS = n.LS;
+  const int nbl = w.nbl;
+  float* gp = reinterpret_cast<float*>(smem + SM::GP);
+  float* wt = reinterpret_cast<float*>(smem + SM::WT);
+  float* ub = reinterpret_cast<float*>(smem + SM::XIN);  // per-row terms of the gate's suffix [C]
+  float* stl = reinterpret_cast<float*>(smem + SM::ST);
+  float* stg = SLDS ? nullptr : w.scratch + (int64_t)blockIdx.x * MAXB * SB;
 
-  // A fragments (rows = state column n of column tile nt, k = d) of an fp32 state
-  auto state_frags = [&](Frag (&nf)[KSD], __amdgpu_buffer_rsrc_t S, int nt) __attribute__((always_inline)) {
-    f32x4 t[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) t[dt] = load_state_tile<D>(S, dt, nt, lane);
-#pragma unroll
-    for (int s = 0; s < KSD; ++s) nf[s] = M::acc_frag(t, s);
+  ChunkLoads<T, D, C, NW> cl;
+  cl.init(wv, lane, a.H, a.L, LS);
+  auto issue = [&](int j, int bi) __attribute__((always_inline)) {
+    const int64_t row0 = bk.row + (int64_t)j * C * a.H;
+    char* buf = smem + bi * SM::BUF;
+    cl.tiles(a.q, row0, buf + SM::TQ, wv);
+    cl.tiles(a.k, row0, buf + SM::TK, wv);
+    cl.tiles(a.v, row0, buf + SM::TV, wv);
+    cl.tiles(a.dO, row0, buf + SM::TD, wv);
+    cl.gates(a.g, row0, reinterpret_cast<float*>(buf + SM::GOFF), wv, lane);
+    cl.gates(w.dOo, row0, reinterpret_cast<float*>(buf + SM::R1OFF), wv, lane);
+    cl.gates(w.din, row0, reinterpret_cast<float*>(buf + SM::R2OFF), wv, lane);
+    cl.lambda(a.lam, row0, a.L, reinterpret_cast<float*>(buf + SM::LOFF), wv, lane);
   };
+  issue(n.P - 1, 0);
 
-  // block gate sums of the blocks strictly between J and block x (exclusive)
+  // block-level buckets after J: the sibling after J's group of 2^b blocks
+  // (bit b of J clear), with the decay from the end of block J to its start
   auto gap_blocks = [&](int x) {
     float d = 0.f;
     for (int y = bk.J + 1; y < x; ++y) d += n.GS[(int64_t)bk.bh * n.nb + y];
     return d;
   };
+  auto bucket_at = [&](int b) { return (((int64_t)bk.bh * n.nb + (((bk.J >> b) + 1) << b)) * nbl + b) * SB; };
+  Frag hv[NH][DT][KSD], hk[NH][DT][KSD];  // rows n of R (for dv) and rows d of R (for dk)
+  float hgap[NH];
+  int nheld = 0, bfar = nbl;
+#pragma unroll
+  for (int x = 0; x < NH; ++x) hgap[x] = 0.f;
+  for (int b = 0; b < nbl; ++b) {
+    if ((bk.J >> b) & 1) continue;
+    const int first = ((bk.J >> b) + 1) << b;
+    if (first >= n.nb) continue;
+    if (nheld >= MAXH) {
+      bfar = b;
+      break;
+    }
+#pragma unroll
+    for (int x = 0; x < MAXH; ++x)
+      if (x == nheld) {
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(w.W + bucket_at(b), SB * 4);
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(w.WT + bucket_at(b), SB * 4);
+#pragma unroll
+        for (int y = 0; y < DT; ++y) {
+          col_frags<T, D>(hv[x][y], y, [&](int tr, int tc) { return load_state_tile<D>(rv, tr, tc, lane); });
+          col_frags<T, D>(hk[x][y], y, [&](int tr, int tc) { return load_state_tile<D>(rk, tr, tc, lane); });
+        }
+        hgap[x] = gap_blocks(first);
+      }
+    ++nheld;
+  }
 
-  for (int j = n.P - 1; j >= 0; --j) {
-    const int64_t row0 = bk.row + (int64_t)j * C * a.H;
-    __syncthreads();  // the previous chunk's tiles and bucket updates are done everywhere
-    stage_tile<T, D, C>(qr, row0, a.H, smem + SG::A, tid, 64 * NW);
-    stage_tile<T, D, C>(kr, row0, a.H, smem + SG::B, tid, 64 * NW);
-    stage_tile<T, D, C>(vr, row0, a.H, smem + SG::X, tid, 64 * NW);
-    if (xdot) stage_tile<T, D, C>(xdot, row0, a.H, smem + SG::Y, tid, 64 * NW);
-    stage_gates<C>(a.g, a.lam, row0, a.H, a.L, n.LS, gl, reinterpret_cast<float*>(smem + SG::LAM), tid, 64 * NW);
-    __syncthreads();
-    const float gsum = stage_prefix<C>(gl, gp, wv, lane);
-    __syncthreads();
+  float sufX[MAXB + 1];  // gate sum of the walked chunks from each level's bucket start to the block end
+#pragma unroll
+  for (int m = 0; m <= MAXB; ++m) sufX[m] = 0.f;
+  float suf = 0.f;     // gate sum of the chunks after the current one, to the block end
+  float bcarry = 0.f;  // sum of the gate's per-row terms of the walked chunks (wave 0)
+
+  Vec4 odv[DT], odk[DT];
+  float odg = 0.f;
+  auto store_out = [&](int jj) __attribute__((always_inline)) {
+    const int64_t row0 = bk.row + (int64_t)jj * C * a.H;
+    const int64_t orow = row0 + (int64_t)s * a.H;
+#pragma unroll
+    for (int x = 0; x < DT; ++x) {
+      *reinterpret_cast<Vec4*>(static_cast<T*>(a.dv) + orow * D + 16 * x + 4 * g4) = odv[x];
+      *reinterpret_cast<Vec4*>(static_cast<T*>(a.dk) + orow * D + 16 * x + 4 * g4) = odk[x];
+    }
+    if (wv == 0 && lane < C) a.dlog_gate[row0 + (int64_t)lane * a.H] = odg;
+  };
+
+  for (int t = 0; t < n.P; ++t) {
+    const int j = n.P - 1 - t;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk j and stores of chunk j+2 are done
+    lds_barrier();
+    if (t > 0) store_out(j + 1);
+    if (j > 0) issue(j - 1, (t + 1) & 1);
+    const char* buf = smem + (t & 1) * SM::BUF;
+    const char* sq = buf + SM::TQ;
+    const char* sk = buf + SM::TK;
+    const char* sv = buf + SM::TV;
+    const char* sdo = buf + SM::TD;
+    const float* ll = reinterpret_cast<const float*>(buf + SM::LOFF);
+    const float gsum = stage_prefix<C>(reinterpret_cast<const float*>(buf + SM::GOFF), gp, wv, lane);
+    lds_barrier();
     // weight rows lambda_t^{LOGC+m} e^{G_t} of the chunk-level buckets this chunk joins
     for (int x = tid; x < MAXB * C; x += 64 * NW) {
-      const int m = x / C + 1, t = x % C;
-      if (m <= logP && ((j >> (m - 1)) & 1)) wt[x] = ll[t * kLevelsMax + LOGC + m] * __expf(gp[t]);
+      const int m = x / C + 1, tk = x % C;
+      if (m <= logP && ((j >> (m - 1)) & 1)) wt[x] = ll[tk * LS + LOGC + m] * __expf(gp[tk]);
     }
-    const int s = 16 * st_ + q16;  // this lane's source row
     const float Gs = gp[s];
+    Frag kfs[KSD], vfs[KSD];  // rows s of k and v (k = head dim)
+#pragma unroll
+    for (int k = 0; k < KSD; ++k) {
+      kfs[k] = frag_row<T, C, D>(sk, s, k, g4);
+      vfs[k] = frag_row<T, C, D>(sv, s, k, g4);
+    }
 
-    // --- buckets after this chunk: Out^T[n][s] = sum_X e^{G_{X0-1} - G_s} R_X^T qr_s
-    f32x4 o[DT];
+    // --- buckets after this chunk.  Lanes: rows n of dv / rows d of dk = 16 x + 4 (lane/16) + e, column s
+    f32x4 ov[DT], ok[DT];
 #pragma unroll
-    for (int nt = 0; nt < DT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Frag qf[KSD];
+    for (int x = 0; x < DT; ++x) ov[x] = ok[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto bucket = [&](auto getv, auto getk, float scale) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < KSD; ++k) qf[k] = frag_row<T, C, D>(sq, s, k, g4);
-    auto bucket_read = [&](const float* R, float scale) __attribute__((always_inline)) {
-      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(R, SB * 4);
-#pragma unroll
-      for (int nt = 0; nt < DT; ++nt) {
+      for (int x = 0; x < DT; ++x) {
         Frag nf[KSD];
-        state_frags(nf, rs, nt);
+        getv(x, nf);
         f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < KSD; ++k) z = M::mma(nf[k], qf[k], z);
-        o[nt] += scale * z;
+        for (int k = 0; k < KSD; ++k) z = M::mma(nf[k], kfs[k], z);
+        ov[x] += scale * z;
+      }
+#pragma unroll
+      for (int x = 0; x < DT; ++x) {
+        Frag nf[KSD];
+        getk(x, nf);
+        f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < KSD; ++k) z = M::mma(nf[k], vfs[k], z);
+        ok[x] += scale * z;
       }
     };
     const float dec_end = gsum - Gs;  // G_{chunk end} - G_s
     // chunk-level buckets: the sibling after this chunk's group at level m (bit m-1 of j clear)
 #pragma unroll
     for (int m = 1; m <= MAXB; ++m)
-      if (m <= logP && !((j >> (m - 1)) & 1)) bucket_read(Rm + (m - 1) * SB, __expf(dec_end + suf - sufX[m]));
-    // block-level buckets: the sibling after J's group of 2^b blocks (bit b of J clear)
+      if (m <= logP && !((j >> (m - 1)) & 1)) {
+        const float sc = __expf(dec_end + suf - sufX[m]);
+        if constexpr (SLDS) {
+          const float* X = stl + (m - 1) * PS::FLOATS;
+          bucket(
+              [&](int x, Frag(&nf)[KSD]) {
+                col_frags<T, D>(nf, x, [&](int tr, int tc) {
+                  return *reinterpret_cast<const f32x4*>(X + PS::off(tr, tc, lane));
+                });
+              },
+              [&](int x, Frag(&nf)[KSD]) {
+                row_frags<T, D>(nf, x, lane, [&](int tr, int tc, int ln, int sl) { return X[PS::off(tr, tc, ln) + sl]; });
+              },
+              sc);
+        } else {
+          const float* X = stg + (m - 1) * SB;
+          const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(X, SB * 4);
+          bucket(
+              [&](int x, Frag(&nf)[KSD]) {
+                col_frags<T, D>(nf, x, [&](int tr, int tc) { return load_state_tile<D>(rs, tr, tc, lane); });
+              },
+              [&](int x, Frag(&nf)[KSD]) {
+                row_frags<T, D>(nf, x, lane, [&](int tr, int tc, int ln, int sl) {
+                  return __builtin_bit_cast(
+                      float, __builtin_amdgcn_raw_buffer_load_b32(rs, (state_tile_offset<D>(tr, tc, ln) + sl) * 4, 0, 0));
+                });
+              },
+              sc);
+        }
+      }
+    // block-level buckets: those held in registers, then any others from memory
     {
       const float base = dec_end + suf;  // to the end of block J
-      for (int b = 0; b < nbl; ++b) {
+#pragma unroll
+      for (int x = 0; x < MAXH; ++x)
+        if (x < nheld)
+          bucket(
+              [&](int y, Frag(&nf)[KSD]) {
+#pragma unroll
+                for (int k = 0; k < KSD; ++k) nf[k] = hv[x][y][k];
+              },
+              [&](int y, Frag(&nf)[KSD]) {
+#pragma unroll
+                for (int k = 0; k < KSD; ++k) nf[k] = hk[x][y][k];
+              },
+              __expf(base + hgap[x]));
+      for (int b = bfar; b < nbl; ++b) {
         if ((bk.J >> b) & 1) continue;
         const int first = ((bk.J >> b) + 1) << b;
         if (first >= n.nb) continue;
-        bucket_read(W + (((int64_t)bk.bh * n.nb + first) * nbl + b) * SB, __expf(base + gap_blocks(first)));
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(w.W + bucket_at(b), SB * 4);
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(w.WT + bucket_at(b), SB * 4);
+        bucket(
+            [&](int y, Frag(&nf)[KSD]) {
+              col_frags<T, D>(nf, y, [&](int tr, int tc) { return load_state_tile<D>(rv, tr, tc, lane); });
+            },
+            [&](int y, Frag(&nf)[KSD]) {
+              col_frags<T, D>(nf, y, [&](int tr, int tc) { return load_state_tile<D>(rk, tr, tc, lane); });
+            },
+            __expf(base + gap_blocks(first)));
       }
     }
 
-    // the cross-chunk part's dot with xdot_s, before the in-chunk terms join
-    float dot = 0.f;
-    if (xdot) {
+    // v_s . dv_s^x, the cross-chunk part, and the gate's per-row term dOo_s - v_s . dv_s^x
+    {
+      float dot = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < DT; ++nt) {
-        const T* xr = reinterpret_cast<const T*>(sx + TL::off(s, 16 * nt + 4 * g4));
+      for (int x = 0; x < DT; ++x) {
+        const T* vr = reinterpret_cast<const T*>(sv + TL::off(s, 16 * x + 4 * g4));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dot += o[nt][e] * to_f32(xr[e]);
+        for (int e = 0; e < 4; ++e) dot += ov[x][e] * to_f32(vr[e]);
       }
       dot = sum_groups(dot);
+      if (g4 == 0) ub[s] = reinterpret_cast<const float*>(buf + SM::R1OFF)[s] - dot;
     }
 
-    // --- in chunk: Out^T[n][s] = sum_t vr^T[n][t] P[t][s] for t >= s; P tiles with
-    // lanes holding rows t = 16 tt + 4 (lane/16) + e of column s (the k operand order)
-    f32x4 pt[CT];
+    // --- in chunk: P1, P2 tiles with lanes holding rows t = 16 tt + 4 (lane/16) + e of column s
+    {
+      f32x4 p1[CT], p2[CT];
 #pragma unroll
-    for (int tt = 0; tt < CT; ++tt) {
-      pt[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (tt < st_) continue;
-      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int tt = 0; tt < CT; ++tt) {
+        p1[tt] = p2[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (tt < wv) continue;
+        f32x4 x1 = f32x4{0.f, 0.f, 0.f, 0.f}, x2 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < KSD; ++k) x = M::mma(frag_row<T, C, D>(sk, 16 * tt + q16, k, g4), frag_row<T, C, D>(sq, s, k, g4), x);
-      const f32x4 gt = *reinterpret_cast<const f32x4*>(gp + 16 * tt + 4 * g4);
+        for (int k = 0; k < KSD; ++k) {
+          x1 = M::mma(frag_row<T, C, D>(sq, 16 * tt + q16, k, g4), kfs[k], x1);
+          x2 = M::mma(frag_row<T, C, D>(sdo, 16 * tt + q16, k, g4), vfs[k], x2);
+        }
+        const f32x4 gt = *reinterpret_cast<const f32x4*>(gp + 16 * tt + 4 * g4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tk = 16 * tt + 4 * g4 + e;
+          const int lev = (tk == s) ? 0 : 32 - __clz(tk ^ s);
+          const float wgt = (tk >= s) ? ll[tk * LS + lev] * __expf(gt[e] - Gs) : 0.f;
+          p1[tt][e] = x1[e] * wgt;
+          p2[tt][e] = x2[e] * wgt;
+        }
+      }
+      Frag pf1[KSC], pf2[KSC];
+#pragma unroll
+      for (int k = 0; k < KSC; ++k) {
+        pf1[k] = M::acc_frag(p1, k);
+        pf2[k] = M::acc_frag(p2, k);
+      }
+      // a k step whose accumulator tiles all lie before this wave's rows holds zeros
+      constexpr int TPK = (sizeof(T) == 2) ? 2 : 1;  // accumulator tiles a k step spans
+#pragma unroll
+      for (int x = 0; x < DT; ++x) {
+        Frag df[KSC], qf[KSC];
+#pragma unroll
+        for (int k = 0; k < KSC; ++k) {
+          df[k] = frag_col<T, C, D>(sdo, 16 * x, k, lane);
+          qf[k] = frag_col<T, C, D>(sq, 16 * x, k, lane);
+        }
+        lds_wait(df, qf);
+#pragma unroll
+        for (int k = 0; k < KSC; ++k)
+          if (M::first_tile(k) + TPK - 1 >= wv) {
+            ov[x] = M::mma(df[k], pf1[k], ov[x]);
+            ok[x] = M::mma(qf[k], pf2[k], ok[x]);
+          }
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < DT; ++x)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = 16 * tt + 4 * g4 + e;
-        const int lev = (t == s) ? 0 : 32 - __clz(t ^ s);
-        pt[tt][e] = (t >= s) ? x[e] * ll[t * kLevelsMax + lev] * __expf(gt[e] - Gs) : 0.f;
+        odv[x][e] = (T)ov[x][e];
+        odk[x][e] = (T)ok[x][e];
       }
-    }
-    Frag pf[KSC];
-#pragma unroll
-    for (int k = 0; k < KSC; ++k) pf[k] = M::acc_frag(pt, k);
-#pragma unroll
-    for (int nt = 0; nt < DT; ++nt) {
-      Frag vf[KSC];
-#pragma unroll
-      for (int k = 0; k < KSC; ++k) vf[k] = frag_col<T, C, D>(sv, 16 * nt, k, lane);
-      lds_wait(vf);
-#pragma unroll
-      for (int k = 0; k < KSC; ++k) o[nt] = M::mma(vf[k], pf[k], o[nt]);
-    }
 
-    // --- outputs of row s: lanes hold columns 16 nt + 4 (lane/16) + e
-    {
-      const int64_t orow = row0 + (int64_t)s * a.H;
-#pragma unroll
-      for (int nt = 0; nt < DT; ++nt) {
-        Vec4 ov;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (T)o[nt][e];
-        *reinterpret_cast<Vec4*>(static_cast<T*>(out) + orow * D + 16 * nt + 4 * g4) = ov;
-      }
-      if (xdot && g4 == 0) dot_out[orow] = dot;
+    lds_barrier();  // every wave has read the buckets; the gate's per-row terms are in
+    // the gate: din_s + the suffix of the per-row terms within the block
+    if (wv == 0) {
+      const float u = lane < C ? ub[lane] : 0.f;
+      const float pre = chunk_scan<C>(u);
+      const float tot = __shfl(pre, C - 1, 64);
+      if (lane < C) odg = reinterpret_cast<const float*>(buf + SM::R2OFF)[lane] + bcarry + tot - pre + u;
+      bcarry += tot;
     }
 
     // --- this chunk joins the chunk-level buckets it lies in (bit m-1 of j set):
-    // R_m = e^{g_j} R_m + sum_t lambda_t^{LOGC+m} e^{G_t} kr_t vr_t^T, a fresh
-    // bucket when j is its last chunk; each wave makes the tiles dt = wave, ...
-    __syncthreads();  // every wave has read the buckets
+    // R_m = e^{g_j} R_m + sum_t lambda_t^{LOGC+m} e^{G_t} q_t dO_t^T, a fresh
+    // bucket when j is its last chunk; wave w makes the tiles dt = w, w + NW, ...
     const float carry = __expf(gsum);
-    for (int dt = wv; dt < DT; dt += NW) {
-      Frag kf[KSC];
 #pragma unroll
-      for (int k = 0; k < KSC; ++k) kf[k] = frag_col<T, C, D>(sk, 16 * dt, k, lane);
-      for (int nt = 0; nt < DT; ++nt) {
-        Frag vf[KSC];
+    for (int m = 1; m <= MAXB; ++m) {
+      if (m > logP || !((j >> (m - 1)) & 1)) continue;
+      const float* wm = wt + (m - 1) * C;
+      const bool fresh = ((j + 1) & ((1 << (m - 1)) - 1)) == 0;
+      for (int dt = wv; dt < DT; dt += NW) {
+        Frag kf[KSC];
 #pragma unroll
-        for (int k = 0; k < KSC; ++k) vf[k] = frag_col<T, C, D>(sv, 16 * nt, k, lane);
-        lds_wait(kf, vf);
+        for (int k = 0; k < KSC; ++k) kf[k] = frag_col<T, C, D>(sq, 16 * dt, k, lane);
+        lds_wait(kf);
 #pragma unroll
-        for (int m = 1; m <= MAXB; ++m) {
-          if (m > logP || !((j >> (m - 1)) & 1)) continue;
-          const float* w = wt + (m - 1) * C;
-          float* dst = Rm + (m - 1) * SB + state_tile_offset<D>(dt, nt, lane);
-          const bool fresh = ((j + 1) & ((1 << (m - 1)) - 1)) == 0;
+        for (int k = 0; k < KSC; ++k) kf[k] = scale_tokens<T>(kf[k], wm, k, g4);
+        for (int nt = 0; nt < DT; ++nt) {
+          Frag vf[KSC];
+#pragma unroll
+          for (int k = 0; k < KSC; ++k) vf[k] = frag_col<T, C, D>(sdo, 16 * nt, k, lane);
+          lds_wait(vf);
+          float* dst = SLDS ? stl + (m - 1) * PS::FLOATS + PS::off(dt, nt, lane)
+                            : stg + (m - 1) * SB + state_tile_offset<D>(dt, nt, lane);
           f32x4 acc = fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : carry * *reinterpret_cast<const f32x4*>(dst);
 #pragma unroll
-          for (int k = 0; k < KSC; ++k) acc = M::mma(kf[k], scale_tokens<T>(vf[k], w, k, g4), acc);
+          for (int k = 0; k < KSC; ++k) acc = M::mma(kf[k], vf[k], acc);
           *reinterpret_cast<f32x4*>(dst) = acc;
         }
       }
@@ -651,64 +992,89 @@ __global__ void __launch_bounds__(64 * (C / 16)) ll_bwd_revread(BwdArgs a, BwdFw
     for (int m = 1; m <= MAXB; ++m)
       if (m <= logP && ((j >> (m - 1)) & 1)) sufX[m] = suf;
   }
+  store_out(0);
+  if (wv == 0 && lane == 0) w.BT[(int64_t)bk.bh * n.nb + bk.J] = bcarry;
 }
 
 // ---------------------------------------------------------------------------
-// ll_bwd_gate: one workgroup per head, adds to the in-chunk share in dlog_gate
-// the cross-chunk pairs' share sum_{t >= r} (dOo_t - xdv_t), walking the tokens
-// from the end in tiles of 256 with the running sum carried.
-__global__ void __launch_bounds__(256) ll_bwd_gate_suffix(BwdArgs a, const float* dOo, const float* xdv) {
-  __shared__ float sbuf[256];
-  const int bh = blockIdx.x, h = bh % a.H, b = bh / a.H;
-  const int tid = threadIdx.x;
-  float carry = 0.f;
-  for (int t0 = a.T - 256; t0 > -256; t0 -= 256) {
-    const int t = t0 + (255 - tid);  // thread 0 takes the latest token of the tile
-    const int64_t r = ((int64_t)b * a.T + t) * a.H + h;
-    sbuf[tid] = (t >= 0) ? dOo[r] - xdv[r] : 0.f;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const float add = tid >= off ? sbuf[tid - off] : 0.f;
-      __syncthreads();
-      sbuf[tid] += add;
-      __syncthreads();
-    }
-    if (t >= 0) a.dlog_gate[r] += carry + sbuf[tid];
-    carry += sbuf[255];
-    __syncthreads();
+// The gate's share from later blocks: BT[bh][J] becomes the sum of BT over the
+// blocks after J (one thread per head), then every row of block J gets it.
+__global__ void __launch_bounds__(256) ll_bwd_block_suffix(int BH, int nb, float* BT) {
+  const int bh = blockIdx.x * blockDim.x + threadIdx.x;
+  if (bh >= BH) return;
+  float acc = 0.f;
+  for (int J = nb - 1; J >= 0; --J) {
+    const float v = BT[(int64_t)bh * nb + J];
+    BT[(int64_t)bh * nb + J] = acc;
+    acc += v;
+  }
+}
+
+__global__ void __launch_bounds__(256) ll_bwd_gate_add(BwdArgs a, int nb, int block_tokens, const float* BT) {
+  const int64_t rows = (int64_t)a.B * a.T * a.H;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows; i += (int64_t)gridDim.x * blockDim.x) {
+    const int h = (int)(i % a.H);
+    const int64_t bt = i / a.H;
+    const int t = (int)(bt % a.T), b = (int)(bt / a.T);
+    a.dlog_gate[i] += BT[((int64_t)b * a.H + h) * nb + t / block_tokens];
   }
 }
 
 // ---------------------------------------------------------------------------
+// Raises a kernel's dynamic LDS allowance once (above 64 KiB it must be set).
+template <typename K>
+static hipError_t allow_lds(std::once_flag& once, hipError_t& result, K kern, int bytes) {
+  std::call_once(once, [&] {
+    result = bytes > 65536 ? hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, bytes)
+                           : hipSuccess;
+  });
+  return result;
+}
+
 template <typename T, int D, int C>
 static hipError_t launch_native_t(const BwdArgs& a, const BwdFwdNodes& n, const BwdWork& w, int pass, hipStream_t s) {
   constexpr int MAXB = max_block_depth(D);
+  constexpr bool SLDS = bwd_states_in_lds(D);  // chunk-level states in LDS (3 x 17 KiB at d = 64)
+  constexpr int FV = state_frag_vgprs<T, D>();
+  constexpr int HF = 64 / FV > 2 ? 2 : 64 / FV;  // forward walk: nodes held in registers
+  constexpr int HR = FV > 32 ? 0 : (64 / FV > 4 ? 4 : 64 / FV);  // reverse walk: buckets held, both ways
   constexpr int NLB = D >= 128 ? 4 : 8;  // block levels per rev_state workgroup: NLB x D/16 accumulator tiles
   const int grid = a.B * a.H * n.nb;
   if (pass == 0) {
-    hipLaunchKernelGGL((ll_bwd_levels<T, D, C, MAXB>), dim3(grid), dim3(64 * (C / 16)), 0, s, a, n, w.dOo, w.scratch);
-  } else if (pass == 1 || pass == 3) {
-    // the reverse bucket states of (kr, vr): (q, dO) for dv, (dO, q) for dk
-    const void* kr = pass == 1 ? a.q : a.dO;
-    const void* vr = pass == 1 ? a.dO : a.q;
+    auto kern = ll_bwd_fwalk<T, D, C, MAXB, HF, SLDS>;
+    constexpr int bytes = WalkSmem<T, D, C, MAXB, SLDS>::BYTES;
+    static std::once_flag once;
+    static hipError_t res = hipSuccess;
+    hipError_t e = allow_lds(once, res, kern, bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * (C / 16)), bytes, s, a, n, w);
+  } else if (pass == 1) {
     if (w.nbl == 0) return hipSuccess;  // one block per head: no block-level buckets
     hipLaunchKernelGGL((ll_bwd_rev_state<T, D, C, NLB>), dim3(grid, (w.nbl + NLB - 1) / NLB), dim3(64 * (D / 16)), 0,
-                       s, a, n, kr, vr, w.W, w.nbl);
+                       s, a, n, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t total = (int64_t)a.B * a.H * w.nbl * n.nb * (D * D / 4);
     const int sgrid = (int)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
-    hipLaunchKernelGGL(ll_bwd_rev_scan, dim3(sgrid), dim3(256), 0, s, n, a.B * a.H, D * D, w.W, w.nbl);
+    hipLaunchKernelGGL(ll_bwd_rev_scan, dim3(sgrid), dim3(256), 0, s, n, a.B * a.H, D, w);
   } else if (pass == 2) {
-    // dv: readers k, states of (q, dO), in-chunk values dO; v . dv for the gate
-    hipLaunchKernelGGL((ll_bwd_revread<T, D, C, MAXB>), dim3(grid), dim3(64 * (C / 16)), 0, s, a, n, a.k,
-                       a.q, a.dO, (const float*)w.W, w.nbl, a.dv, a.v, w.xdv, w.scratch);
-  } else if (pass == 4) {
-    // dk: readers v, states of (dO, q), in-chunk values q
-    hipLaunchKernelGGL((ll_bwd_revread<T, D, C, MAXB>), dim3(grid), dim3(64 * (C / 16)), 0, s, a, n, a.v,
-                       a.dO, a.q, (const float*)w.W, w.nbl, a.dk, (const void*)nullptr, (float*)nullptr, w.scratch);
+    auto kern = ll_bwd_rwalk<T, D, C, MAXB, HR, SLDS>;
+    constexpr int bytes = WalkSmem<T, D, C, MAXB, SLDS>::BYTES;
+    static std::once_flag once;
+    static hipError_t res = hipSuccess;
+    hipError_t e = allow_lds(once, res, kern, bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * (C / 16)), bytes, s, a, n, w);
   } else {
-    hipLaunchKernelGGL(ll_bwd_gate_suffix, dim3(a.B * a.H), dim3(256), 0, s, a, w.dOo, w.xdv);
+    if (n.nb == 1) return hipSuccess;  // no later blocks
+    const int BH = a.B * a.H;
+    hipLaunchKernelGGL(ll_bwd_block_suffix, dim3((BH + 255) / 256), dim3(256), 0, s, BH, n.nb, w.BT);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t rows = (int64_t)a.B * a.T * a.H;
+    const int ggrid = (int)((rows + 255) / 256 < 16384 ? (rows + 255) / 256 : 16384);
+    hipLaunchKernelGGL(ll_bwd_gate_add, dim3(ggrid), dim3(256), 0, s, a, n.nb, n.P * C, w.BT);
   }
   return hipGetLastError();
 }

@@ -79,6 +79,7 @@ struct BwdArgs {
   const float* g;
   const float* lam;
   const void* dO;
+  void* dq;
   void* dk;
   void* dv;
   float* dlog_gate;
@@ -97,11 +98,13 @@ struct BwdFwdNodes {
 
 // Scratch of the backward kernels.
 struct BwdWork {
-  float* dOo;      // [B,T,H] dO_t . o_t
-  float* xdv;      // [B,T,H] v_t . dv_t (= k_t . dk_t)
-  float* W;        // [B*H, nb, nbl, D*D] block shares of the reverse bucket states
+  float* dOo;      // [B,T,H] the cross-chunk part of dO_t . o_t
+  float* din;      // [B,T,H] the in-chunk pairs' share of the gate gradient
+  float* W;        // [B*H, nb, nbl, D*D] block shares of the reverse bucket states, then the bucket states
+  float* WT;       // [B*H, nb, nbl, D*D] the bucket states transposed (at each bucket's first block)
+  float* BT;       // [B*H, nb] per block: sum of dO.o - v.dv over its cross-chunk pairs, then the sum over later blocks
   int nbl;         // block levels: bit_length(nb - 1)
-  float* scratch;  // [B*H*nb, max_block_depth, D*D] chunk-level states of one walk
+  float* scratch;  // [B*H*nb, max_block_depth, D*D] chunk-level states of a walk, where they do not fit in LDS
 };
 
 // io: 0 = fp32, 1 = bf16.  Each returns hipSuccess or the launch error.
@@ -110,8 +113,9 @@ hipError_t launch_chunk_attn(int io, int D, int C, const PrefillArgs& a, hipStre
 hipError_t launch_fenwick_scan(int D, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_state_export(int D, int C, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prior_read(int io, int D, int C, const PrefillArgs& a, hipStream_t s);
-// pass: 0 levels (dlambda, dO.o), 1 reverse states of (q, dO), 2 dv, 3 reverse
-// states of (dO, q), 4 dk, 5 dlog_gate
+// pass: 0 the forward walk (dlambda, dq, the gate's in-chunk share; needs n
+// built from (v, k)), 1 the reverse bucket states, 2 the reverse walk (dv, dk),
+// 3 the gate's sum over later blocks
 hipError_t launch_bwd_native(int io, int D, int C, const BwdArgs& a, const BwdFwdNodes& n, const BwdWork& w, int pass,
                              hipStream_t s);
 hipError_t launch_ccq_fill(int64_t rows, int L, float* ones, float* zeros, hipStream_t s);
@@ -136,6 +140,10 @@ inline int ilog2_host(int x) {
 
 // largest within-block Fenwick depth the chunk kernels hold in registers
 constexpr int max_block_depth(int /*D*/) { return 3; }
+
+// Whether the backward walks keep their chunk-level states in LDS (else in
+// BwdWork::scratch).
+constexpr bool bwd_states_in_lds(int D) { return D <= 64; }
 
 // Whether the read takes the block-level Fenwick nodes from bf16 copies in
 // fragment order (PrefillArgs::N16): for bf16 io at head sizes where no node
