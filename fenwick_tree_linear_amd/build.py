@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libllattn.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.cpp", "chunk_attn.hip", "fenwick_scan.hip", "decode_step.hip", "gdn.hip", "lambda_mlp.hip", "prior_read.hip", "ccq.hip", "bwd_native.hip"]
+SOURCES = ["api.cpp", "chunk_attn.hip", "fenwick_scan.hip", "decode_step.hip", "gdn.hip", "lambda_mlp.hip", "prior_read.hip", "ccq.hip", "bwd_native.hip", "pad.hip"]
 ARCH = os.environ.get("LLATTN_ARCH", "gfx950")
 
 COMMON = [

@@ -57,15 +57,33 @@ int enum_value(const E& e) {
   return v;
 }
 
-// bf16 matrix-core steps contract 32 values: bf16 needs d >= 32 and C >= 32
-bool supported_head(int d, ll_dtype io) {
-  if (io == LL_BF16) return d == 32 || d == 64 || d == 128;
-  return d == 16 || d == 32 || d == 64;
+// Head sizes (each of dk and dv) and chunk sizes a caller may pass.
+bool accepted_head(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool accepted_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+
+// The square head size the kernels run a problem at: dk and dv zero-padded to
+// the larger, and bf16 d = 16 to the 32 values one bf16 matrix-core step
+// contracts (zero key columns add nothing to q.k; zero value columns give
+// output columns that are dropped).
+int run_head(int dk, int dv, ll_dtype io) {
+  const int d = dk > dv ? dk : dv;
+  return (io == LL_BF16 && d < 32) ? 32 : d;
 }
 
-bool supported_chunk(int c, ll_dtype io) {
-  if (io == LL_BF16) return c == 32 || c == 64;
-  return c == 16 || c == 32 || c == 64;
+// Chunks the kernels run natively for an io dtype.
+bool native_chunk(int c, ll_dtype io) { return io == LL_BF16 ? (c == 32 || c == 64) : accepted_chunk(c); }
+
+// The chunk the kernels run for a requested chunk C at run head size D.  The
+// read is the same sum whatever the chunk size, so: a bf16 step contracts 32
+// tokens (bf16 C = 16 runs 32-token chunks), and a C x D tile of the read must
+// fit its LDS stage (larger chunks run halved).  Gated DeltaNet's pseudo-value
+// pass runs the chunk it has for D (bf16: 32 or 64; fp32 at D = 128: 16).
+int run_chunk(int c, int D, ll_dtype io, ll_rule rule) {
+  const size_t esz = io == LL_BF16 ? 2 : 4;
+  if (io == LL_BF16 && c < 32) c = 32;
+  if (rule == LL_GATED_DELTANET) return (io == LL_F32 && D == 128) ? 16 : c;
+  while ((size_t)c * D * esz > (size_t)llattn::kAttnTileBytesMax && native_chunk(c / 2, io)) c /= 2;
+  return c;
 }
 
 constexpr int kMaxBlockChunks = 8;  // P <= 2^max_block_depth
@@ -73,14 +91,20 @@ constexpr int kMaxBlockChunks = 8;  // P <= 2^max_block_depth
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
-  int Cr;  // chunk size of the log-linear read (C, or smaller for Gated DeltaNet when a tile would not fit)
+  ll_problem r;  // the problem the kernels run: square head, run chunk and (padded) length
+  int Cr;        // chunk size of the log-linear read (r.C, or smaller for Gated DeltaNet when a tile would not fit)
   int P, nb, nF, LS;
   size_t s_off, gs_off, f_off, gf_off, n16_off;
   size_t w_off, up_off, u_off;  // Gated DeltaNet: W, U' and the pseudo-values U
+  // copies of the caller's tensors in the run shape, where it differs
+  bool pad_qk, pad_v, pad_t, pad_state;
+  size_t qp_off, kp_off, vp_off, op_off, gp_off, lp_off, bp_off, sin_off, sout_off;
   size_t bytes;
 };
 
-// Validates a prefill problem and derives the block decomposition.
+// Validates a prefill problem and derives the run problem, the block
+// decomposition and the workspace.  The workspace does not depend on
+// `exporting` (which only adds checks).
 ll_status plan_prefill(const ll_problem* p, bool exporting, Plan* out) {
   if (!p) return fail(LL_ERR_NULL, "problem is NULL");
   const int io_v = enum_value(p->io), rule_v = enum_value(p->rule);
@@ -98,61 +122,96 @@ ll_status plan_prefill(const ll_problem* p, bool exporting, Plan* out) {
   if (exporting && bit_length(p->T) > p->L - 1)
     return fail(LL_ERR_SHAPE, "exporting the state of [0,%d) needs at least %d levels, got L=%d", p->T,
                 bit_length(p->T) + 1, p->L);
-  if (p->dk != p->dv) return fail(LL_ERR_UNSUPPORTED, "dk=%d != dv=%d is not supported", p->dk, p->dv);
-  if (!supported_head(p->dk, p->io))
-    return fail(LL_ERR_UNSUPPORTED, "head size %d not supported for %s io", p->dk, p->io == LL_BF16 ? "bf16" : "fp32");
-  if (!supported_chunk(p->C, p->io))
-    return fail(LL_ERR_UNSUPPORTED, "chunk size C=%d not supported for %s io", p->C, p->io == LL_BF16 ? "bf16" : "fp32");
+  if (!accepted_head(p->dk) || !accepted_head(p->dv))
+    return fail(LL_ERR_UNSUPPORTED, "head sizes dk=%d, dv=%d: each must be 16, 32, 64 or 128", p->dk, p->dv);
+  if (!accepted_chunk(p->C)) return fail(LL_ERR_UNSUPPORTED, "chunk size C=%d not supported (16, 32 or 64)", p->C);
   const size_t esz = p->io == LL_BF16 ? 2 : 4;
-  int Cr = p->C;
-  if (p->rule == LL_GATED_DELTANET) {
-    // the pseudo-value pass works on chunks of C; the read may use smaller ones
-    while ((size_t)Cr * p->dk * esz > (size_t)llattn::kAttnTileBytesMax && supported_chunk(Cr / 2, p->io)) Cr /= 2;
+  ll_problem r = *p;
+  r.dk = r.dv = run_head(p->dk, p->dv, p->io);
+  r.C = run_chunk(p->C, r.dk, p->io, p->rule);
+  r.T = (p->T + r.C - 1) / r.C * r.C;
+  const int D = r.dk;
+  if (r.T != p->T) {
+    if (exporting)
+      return fail(LL_ERR_UNSUPPORTED, "exporting the state needs T a multiple of %d for %s io (T=%d)", r.C,
+                  p->io == LL_BF16 ? "bf16" : "fp32", p->T);
+    if (bit_length((int64_t)r.T - 1) + 1 > p->L)
+      return fail(LL_ERR_UNSUPPORTED, "T=%d runs padded to %d tokens (%d-token chunks), which needs L >= %d", p->T,
+                  r.T, r.C, bit_length((int64_t)r.T - 1) + 1);
   }
-  if ((size_t)Cr * p->dk * esz > (size_t)llattn::kAttnTileBytesMax)
-    return fail(LL_ERR_UNSUPPORTED, "a chunk tile of C=%d x d=%d %s values exceeds %d bytes", Cr, p->dk,
+  int Cr = r.C;
+  if (p->rule == LL_GATED_DELTANET) {
+    // the pseudo-value pass works on chunks of r.C; the read may use smaller ones
+    while ((size_t)Cr * D * esz > (size_t)llattn::kAttnTileBytesMax && native_chunk(Cr / 2, p->io)) Cr /= 2;
+  }
+  if ((size_t)Cr * D * esz > (size_t)llattn::kAttnTileBytesMax)
+    return fail(LL_ERR_UNSUPPORTED, "a chunk tile of C=%d x d=%d %s values exceeds %d bytes", Cr, D,
                 p->io == LL_BF16 ? "bf16" : "fp32", llattn::kAttnTileBytesMax);
-  if (need > llattn::kLevelsMax)
-    return fail(LL_ERR_UNSUPPORTED, "T=%d needs %d levels; at most %d are supported", p->T, need, llattn::kLevelsMax);
-  if ((int64_t)p->B * p->H * (p->T / p->C) > ((int64_t)1 << 31) - 1)
+  if (p->rule == LL_GATED_DELTANET && (size_t)r.C * D * esz > 2 * (size_t)llattn::kAttnTileBytesMax)
+    return fail(LL_ERR_UNSUPPORTED, "the Gated DeltaNet pass has no %s chunk of C=%d x d=%d",
+                p->io == LL_BF16 ? "bf16" : "fp32", r.C, D);
+  const int need_r = bit_length((int64_t)r.T - 1) + 1;
+  if (need_r > llattn::kLevelsMax)
+    return fail(LL_ERR_UNSUPPORTED, "T=%d needs %d levels; at most %d are supported", r.T, need_r, llattn::kLevelsMax);
+  if ((int64_t)p->B * p->H * (r.T / Cr) > ((int64_t)1 << 31) - 1)
     return fail(LL_ERR_UNSUPPORTED, "problem too large for one launch");
 
-  const int nc = p->T / Cr;
-  const int depth_cap = 1 << llattn::max_block_depth(p->dk);
+  const int nc = r.T / Cr;
+  const int depth_cap = 1 << llattn::max_block_depth(D);
   int P = nc & -nc;  // lowest set bit: blocks tile the chunks exactly
   if (P > kMaxBlockChunks) P = kMaxBlockChunks;
   if (P > depth_cap) P = depth_cap;
   Plan pl;
+  pl.r = r;
   pl.Cr = Cr;
   pl.P = P;
   pl.nb = nc / P;
   pl.nF = pl.nb / 2;
-  pl.LS = p->L < need ? p->L : need;
+  pl.LS = p->L < need_r ? p->L : need_r;
   const size_t bh = (size_t)p->B * p->H;
-  const size_t dd = (size_t)p->dk * p->dv;
+  const size_t dd = (size_t)D * D;
   size_t off = 0;
-  pl.s_off = off;
-  off = align256(off + bh * pl.nb * dd * sizeof(float));
-  pl.gs_off = off;
-  off = align256(off + bh * pl.nb * sizeof(float));
-  pl.f_off = off;
-  off = align256(off + bh * pl.nF * dd * sizeof(float));
-  pl.gf_off = off;
-  off = align256(off + bh * (pl.nF > 0 ? pl.nF : 1) * sizeof(float));
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  pl.s_off = take(bh * pl.nb * dd * sizeof(float));
+  pl.gs_off = take(bh * pl.nb * sizeof(float));
+  pl.f_off = take(bh * pl.nF * dd * sizeof(float));
+  pl.gf_off = take(bh * (pl.nF > 0 ? pl.nF : 1) * sizeof(float));
   pl.n16_off = 0;
-  if (llattn::node_copies(p->io == LL_BF16 ? 1 : 0, p->dk) && pl.nb > 1) {  // bf16 copies of the nodes the read takes
-    pl.n16_off = off;
-    off = align256(off + bh * pl.nb * dd * 2);
-  }
+  if (llattn::node_copies(p->io == LL_BF16 ? 1 : 0, D) && pl.nb > 1)  // bf16 copies of the nodes the read takes
+    pl.n16_off = take(bh * pl.nb * dd * 2);
+  const size_t rows_r = (size_t)p->B * r.T * p->H;
   pl.w_off = pl.up_off = pl.u_off = 0;
   if (p->rule == LL_GATED_DELTANET) {
-    const size_t rows = (size_t)p->B * p->T * p->H * p->dk * esz;
-    pl.w_off = off;
-    off = align256(off + rows);
-    pl.up_off = off;
-    off = align256(off + rows);
-    pl.u_off = off;
-    off = align256(off + rows);
+    pl.w_off = take(rows_r * D * esz);
+    pl.up_off = take(rows_r * D * esz);
+    pl.u_off = take(rows_r * D * esz);
+  }
+  pl.pad_t = r.T != p->T;
+  pl.pad_qk = p->dk != D || pl.pad_t;
+  pl.pad_v = p->dv != D || pl.pad_t;
+  pl.pad_state = p->dk != D || p->dv != D;
+  pl.qp_off = pl.kp_off = pl.vp_off = pl.op_off = pl.gp_off = pl.lp_off = pl.bp_off = pl.sin_off = pl.sout_off = 0;
+  if (pl.pad_qk) {
+    pl.qp_off = take(rows_r * D * esz);
+    pl.kp_off = take(rows_r * D * esz);
+  }
+  if (pl.pad_v) {
+    pl.vp_off = take(rows_r * D * esz);
+    pl.op_off = take(rows_r * D * esz);
+  }
+  if (pl.pad_t) {
+    pl.gp_off = take(rows_r * 4);
+    pl.lp_off = take(rows_r * p->L * 4);
+    pl.bp_off = take(rows_r * 4);
+  }
+  if (pl.pad_state) {
+    const size_t state_bytes = bh * p->L * (dd + 1) * 4;
+    pl.sin_off = take(state_bytes);
+    pl.sout_off = take(state_bytes);
   }
   pl.bytes = off;
   *out = pl;
@@ -301,54 +360,26 @@ ll_status scratch_of_current_device(void** out) {
   return LL_OK;
 }
 
-// Both prefill entry points: a segment at positions pos0 .. pos0 + T - 1 whose
-// earlier positions (if any) are summarised by state_in.
-// reuse_states: the workspace already holds the block states and Fenwick nodes
-// of this (k, v, log_gate) from the previous call (a Mamba-2 read with other
-// q or level weights); only the read runs.
-ll_status run_prefill(const ll_problem* p, int64_t pos0, const float* state_in, const void* q, const void* k,
-                      const void* v, const float* log_gate, const float* lambda, const float* beta, void* o,
-                      void* state_out, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                      bool reuse_states = false, bool noalloc = false) {
-  if (reuse_states && (p->rule != LL_MAMBA2 || pos0 != 0 || state_out))
-    return fail(LL_ERR_UNSUPPORTED, "reusing block states is only for a plain Mamba-2 read");
-  Plan pl;
-  ll_status st = plan_prefill(p, state_out != nullptr, &pl);
-  if (st != LL_OK) return st;
-  if (pos0 < 0) return fail(LL_ERR_POSITION, "pos0=%lld is negative", (long long)pos0);
-  if (pos0 > 0) {
-    if (!state_in) return fail(LL_ERR_NULL, "state_in must not be NULL when pos0 > 0");
-    if ((pos0 & -pos0) < p->T)
-      return fail(LL_ERR_POSITION, "pos0=%lld: the segment of T=%d tokens must fit below the lowest set bit of pos0",
-                  (long long)pos0, p->T);
-    if (pos0 > ((int64_t)1 << 61)) return fail(LL_ERR_POSITION, "pos0=%lld is too large", (long long)pos0);
-    const int64_t end = pos0 + p->T;
-    if (bit_length(end - 1) + 1 > p->L)
-      return fail(LL_ERR_SHAPE, "positions up to %lld need at least %d levels, got L=%d", (long long)(end - 1),
-                  bit_length(end - 1) + 1, p->L);
-    if (state_out && bit_length(end) > p->L - 1)
-      return fail(LL_ERR_SHAPE, "exporting the state of [0,%lld) needs at least %d levels, got L=%d", (long long)end,
-                  bit_length(end) + 1, p->L);
-  }
-  if (!k || !v || !log_gate) return fail(LL_ERR_NULL, "k, v and log_gate must not be NULL");
-  if (!o && !state_out) return fail(LL_ERR_NULL, "o and state_out are both NULL: nothing to compute");
-  if (o && (!q || !lambda)) return fail(LL_ERR_NULL, "q and lambda must not be NULL when o is requested");
-  if (p->rule == LL_GATED_DELTANET && !beta) return fail(LL_ERR_NULL, "beta must not be NULL for Gated DeltaNet");
-  if (noalloc) {
-    if (pl.bytes > LL_NOALLOC_SCRATCH_BYTES)
-      return fail(LL_ERR_WORKSPACE, "this problem needs %zu bytes of workspace; the allocation-free prefill has %zu",
-                  pl.bytes, (size_t)LL_NOALLOC_SCRATCH_BYTES);
-    // validation is over: only now touch the device, for the scratch address
-    st = scratch_of_current_device(&workspace);
-    if (st != LL_OK) return st;
-  } else {
-    if (workspace_bytes < pl.bytes)
-      return fail(LL_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes,
-                  pl.bytes);
-    if (pl.bytes > 0 && !workspace) return fail(LL_ERR_WORKSPACE, "workspace is NULL");
-  }
+// Copies between a caller's [B,T,H,d] (or [B,T,H]) tensor and its run shape.
+hipError_t pad_rows(int esz, const void* src, int B, int Ts, int H, int ds, void* dst, int Td, int dd, hipStream_t s) {
+  return llattn::launch_pad_copy(esz, src, dst, B, Ts, H, ds, Td, H, dd, s);
+}
 
+// A caller's decode-layout state [B,H,L,dk,dv] + sigma [B,H,L] and its run
+// shape [B,H,L,D,D] + sigma.
+hipError_t pad_state(const void* src, int dks, int dvs, void* dst, int dkd, int dvd, int64_t mats, hipStream_t s) {
+  hipError_t e = llattn::launch_pad_copy(4, src, dst, mats, dks, 1, dvs, dkd, 1, dvd, s);
+  if (e != hipSuccess) return e;
+  return llattn::launch_pad_copy(4, static_cast<const float*>(src) + mats * dks * dvs,
+                                 static_cast<float*>(dst) + mats * dkd * dvd, 1, 1, 1, (int)mats, 1, 1, (int)mats, s);
+}
+
+// The launch sequence of a validated prefill in its run shape.
+ll_status run_core(const Plan& pl, int64_t pos0, const float* state_in, const void* q, const void* k, const void* v,
+                   const float* log_gate, const float* lambda, const float* beta, void* o, void* state_out,
+                   void* workspace, hipStream_t stream, bool reuse_states) {
   char* ws = static_cast<char*>(workspace);
+  const ll_problem* p = &pl.r;
   PrefillArgs a;
   a.B = p->B;
   a.T = p->T;
@@ -411,6 +442,114 @@ ll_status run_prefill(const ll_problem* p, int64_t pos0, const float* state_in, 
   return ok();
 }
 
+
+// Both prefill entry points: a segment at positions pos0 .. pos0 + T - 1 whose
+// earlier positions (if any) are summarised by state_in.  A problem whose
+// shape the kernels do not run natively runs on copies in its run shape.
+// reuse_states: the workspace already holds the block states and Fenwick nodes
+// of this (k, v, log_gate) from the previous call (a Mamba-2 read with other
+// q or level weights); only the read runs.
+ll_status run_prefill(const ll_problem* p, int64_t pos0, const float* state_in, const void* q, const void* k,
+                      const void* v, const float* log_gate, const float* lambda, const float* beta, void* o,
+                      void* state_out, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                      bool reuse_states = false, bool noalloc = false) {
+  Plan pl;
+  ll_status st = plan_prefill(p, state_out != nullptr, &pl);
+  if (st != LL_OK) return st;
+  if (reuse_states && (p->rule != LL_MAMBA2 || pos0 != 0 || state_out || pl.pad_qk || pl.pad_v))
+    return fail(LL_ERR_UNSUPPORTED, "reusing block states is only for a plain Mamba-2 read in the run shape");
+  const ll_problem& r = pl.r;
+  if (pos0 < 0) return fail(LL_ERR_POSITION, "pos0=%lld is negative", (long long)pos0);
+  if (pos0 > 0) {
+    if (!state_in) return fail(LL_ERR_NULL, "state_in must not be NULL when pos0 > 0");
+    if ((pos0 & -pos0) < r.T)
+      return fail(LL_ERR_POSITION, "pos0=%lld: the segment of T=%d tokens must fit below the lowest set bit of pos0",
+                  (long long)pos0, r.T);
+    if (pos0 > ((int64_t)1 << 61)) return fail(LL_ERR_POSITION, "pos0=%lld is too large", (long long)pos0);
+    const int64_t end = pos0 + r.T;
+    if (bit_length(end - 1) + 1 > p->L)
+      return fail(LL_ERR_SHAPE, "positions up to %lld need at least %d levels, got L=%d", (long long)(end - 1),
+                  bit_length(end - 1) + 1, p->L);
+    if (state_out && bit_length(end) > p->L - 1)
+      return fail(LL_ERR_SHAPE, "exporting the state of [0,%lld) needs at least %d levels, got L=%d", (long long)end,
+                  bit_length(end) + 1, p->L);
+  }
+  if (!k || !v || !log_gate) return fail(LL_ERR_NULL, "k, v and log_gate must not be NULL");
+  if (!o && !state_out) return fail(LL_ERR_NULL, "o and state_out are both NULL: nothing to compute");
+  if (o && (!q || !lambda)) return fail(LL_ERR_NULL, "q and lambda must not be NULL when o is requested");
+  if (p->rule == LL_GATED_DELTANET && !beta) return fail(LL_ERR_NULL, "beta must not be NULL for Gated DeltaNet");
+  if (noalloc) {
+    if (pl.bytes > LL_NOALLOC_SCRATCH_BYTES)
+      return fail(LL_ERR_WORKSPACE, "this problem needs %zu bytes of workspace; the allocation-free prefill has %zu",
+                  pl.bytes, (size_t)LL_NOALLOC_SCRATCH_BYTES);
+    // validation is over: only now touch the device, for the scratch address
+    st = scratch_of_current_device(&workspace);
+    if (st != LL_OK) return st;
+  } else {
+    if (workspace_bytes < pl.bytes)
+      return fail(LL_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes,
+                  pl.bytes);
+    if (pl.bytes > 0 && !workspace) return fail(LL_ERR_WORKSPACE, "workspace is NULL");
+  }
+
+  // the caller's tensors in the run shape
+  char* ws = static_cast<char*>(workspace);
+  const int esz = p->io == LL_BF16 ? 2 : 4;
+  const int D = r.dk;
+  const int64_t mats = (int64_t)p->B * p->H * p->L;
+  const void *qr = q, *kr = k, *vr = v;
+  const float *gr = log_gate, *lr = lambda, *br = beta, *sr = state_in;
+  void* or_ = o;
+  void* sor = state_out;
+  hipError_t e = hipSuccess;
+  auto step = [&](auto fn) {
+    if (e == hipSuccess) e = fn();
+  };
+  if (pl.pad_qk) {
+    if (q) {
+      step([&] { return pad_rows(esz, q, p->B, p->T, p->H, p->dk, ws + pl.qp_off, r.T, D, stream); });
+      qr = ws + pl.qp_off;
+    }
+    step([&] { return pad_rows(esz, k, p->B, p->T, p->H, p->dk, ws + pl.kp_off, r.T, D, stream); });
+    kr = ws + pl.kp_off;
+  }
+  if (pl.pad_v) {
+    step([&] { return pad_rows(esz, v, p->B, p->T, p->H, p->dv, ws + pl.vp_off, r.T, D, stream); });
+    vr = ws + pl.vp_off;
+    if (o) or_ = ws + pl.op_off;
+  }
+  if (pl.pad_t) {
+    step([&] { return pad_rows(4, log_gate, p->B, p->T, p->H, 1, ws + pl.gp_off, r.T, 1, stream); });
+    gr = reinterpret_cast<const float*>(ws + pl.gp_off);
+    if (lambda) {
+      step([&] { return pad_rows(4, lambda, p->B, p->T, p->H, p->L, ws + pl.lp_off, r.T, p->L, stream); });
+      lr = reinterpret_cast<const float*>(ws + pl.lp_off);
+    }
+    if (beta) {
+      step([&] { return pad_rows(4, beta, p->B, p->T, p->H, 1, ws + pl.bp_off, r.T, 1, stream); });
+      br = reinterpret_cast<const float*>(ws + pl.bp_off);
+    }
+  }
+  if (pl.pad_state) {
+    if (pos0 > 0) {
+      step([&] { return pad_state(state_in, p->dk, p->dv, ws + pl.sin_off, D, D, mats, stream); });
+      sr = reinterpret_cast<const float*>(ws + pl.sin_off);
+    }
+    if (state_out) sor = ws + pl.sout_off;
+  }
+  if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+
+  st = run_core(pl, pos0, sr, qr, kr, vr, gr, lr, br, or_, sor, workspace, stream, reuse_states);
+  if (st != LL_OK) return st;
+
+  // the outputs in the caller's shape
+  if (o && or_ != o) step([&] { return pad_rows(esz, or_, p->B, r.T, p->H, D, o, p->T, p->dv, stream); });
+  if (state_out && sor != state_out)
+    step([&] { return pad_state(sor, D, D, state_out, p->dk, p->dv, mats, stream); });
+  if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 ll_status ll_attn_fwd(const ll_problem* p, const void* q, const void* k, const void* v, const float* log_gate,
@@ -455,12 +594,12 @@ ll_status check_decode(int B, int H, int dk, int dv, int L, ll_dtype io, ll_rule
   if (!q || !k || !v || !log_gate || !lambda || !o || !state)
     return fail(LL_ERR_NULL, "q, k, v, log_gate, lambda, o and state must not be NULL");
   if (rule == LL_GATED_DELTANET && !beta) return fail(LL_ERR_NULL, "beta must not be NULL for Gated DeltaNet");
-  if (dk != dv) return fail(LL_ERR_UNSUPPORTED, "dk=%d != dv=%d is not supported", dk, dv);
-  if (dk != 16 && dk != 32 && dk != 64 && dk != 128) return fail(LL_ERR_UNSUPPORTED, "head size %d not supported", dk);
+  if (!accepted_head(dk) || !accepted_head(dv))
+    return fail(LL_ERR_UNSUPPORTED, "head sizes dk=%d, dv=%d: each must be 16, 32, 64 or 128", dk, dv);
   return LL_OK;
 }
 
-ll_status launch_decode(int B, int H, int dk, int L, ll_dtype io, ll_rule rule, int64_t pos, const int64_t* pos_dev,
+ll_status launch_decode(int B, int H, int dk, int dv, int L, ll_dtype io, ll_rule rule, int64_t pos, const int64_t* pos_dev,
                         const void* q, const void* k, const void* v, const float* log_gate, const float* lambda,
                         const float* beta, void* o, void* state, hipStream_t stream) {
   DecodeArgs a;
@@ -478,7 +617,7 @@ ll_status launch_decode(int B, int H, int dk, int L, ll_dtype io, ll_rule rule, 
   a.o = o;
   a.state = static_cast<float*>(state);
   const int code = io == LL_BF16 ? 1 : 0;
-  hipError_t e = timed(K_DECODE_STEP, stream, [&] { return llattn::launch_decode_step(code, dk, a, stream); });
+  hipError_t e = timed(K_DECODE_STEP, stream, [&] { return llattn::launch_decode_step(code, dk, dv, a, stream); });
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -493,7 +632,7 @@ ll_status ll_decode_step(int B, int H, int dk, int dv, int L, ll_dtype io, ll_ru
   if (pos < 0) return fail(LL_ERR_POSITION, "pos=%lld is negative", (long long)pos);
   if (pos + 1 >= ((int64_t)1 << (L - 1)))
     return fail(LL_ERR_POSITION, "pos=%lld: the state of [0,pos+1) does not fit in L=%d levels", (long long)pos, L);
-  return launch_decode(B, H, dk, L, io, rule, pos, nullptr, q, k, v, log_gate, lambda, beta, o, state, stream);
+  return launch_decode(B, H, dk, dv, L, io, rule, pos, nullptr, q, k, v, log_gate, lambda, beta, o, state, stream);
 }
 
 ll_status ll_decode_step_ragged(int B, int H, int dk, int dv, int L, ll_dtype io, ll_rule rule, const int64_t* pos,
@@ -502,7 +641,7 @@ ll_status ll_decode_step_ragged(int B, int H, int dk, int dv, int L, ll_dtype io
   ll_status st = check_decode(B, H, dk, dv, L, io, rule, q, k, v, log_gate, lambda, beta, o, state);
   if (st != LL_OK) return st;
   if (!pos) return fail(LL_ERR_NULL, "pos must not be NULL");
-  return launch_decode(B, H, dk, L, io, rule, 0, pos, q, k, v, log_gate, lambda, beta, o, state, stream);
+  return launch_decode(B, H, dk, dv, L, io, rule, 0, pos, q, k, v, log_gate, lambda, beta, o, state, stream);
 }
 
 ll_status ll_lambda_mlp(int64_t rows, int L, int hidden, const float* d, const float* w1, const float* w2,
@@ -537,19 +676,22 @@ ll_status plan_ccq(int B, int T, int H, int dk, ll_dtype io, CcqPlan* out) {
   if (io_v != LL_F32 && io_v != LL_BF16) return fail(LL_ERR_DTYPE, "unknown io dtype %d", io_v);
   if (B < 1 || T < 1 || H < 1 || dk < 1)
     return fail(LL_ERR_SHAPE, "sizes must be positive (B=%d T=%d H=%d dk=%d)", B, T, H, dk);
-  if (!supported_head(dk, io))
-    return fail(LL_ERR_UNSUPPORTED, "head size %d not supported for %s io", dk, io == LL_BF16 ? "bf16" : "fp32");
+  if (!accepted_head(dk))
+    return fail(LL_ERR_UNSUPPORTED, "head size %d not supported (16, 32, 64 or 128)", dk);
   const size_t esz = io == LL_BF16 ? 2 : 4;
+  const int D = run_head(dk, dk, io);
   int C = 0;
   for (int c : {64, 32, 16})
-    if (!C && supported_chunk(c, io) && T % c == 0 && (size_t)c * dk * esz <= (size_t)llattn::kAttnTileBytesMax) C = c;
-  if (!C) return fail(LL_ERR_UNSUPPORTED, "T=%d is not a multiple of a supported chunk size for head size %d", T, dk);
+    if (!C && T % c == 0) C = c;
+  if (!C) return fail(LL_ERR_UNSUPPORTED, "T=%d is not a multiple of 16", T);
+  const int CW = run_chunk(C, D, io, LL_MAMBA2);
+  const int T_run = (T + CW - 1) / CW * CW;
   CcqPlan c;
   c.p.B = B;
   c.p.T = T;
   c.p.H = H;
   c.p.dk = c.p.dv = dk;
-  c.p.L = bit_length((int64_t)T - 1) + 1;
+  c.p.L = bit_length((int64_t)T_run - 1) + 1;  // levels for the run length (all weights are 1)
   if (c.p.L < 2) c.p.L = 2;
   c.p.C = C;
   c.p.io = io;
@@ -624,19 +766,33 @@ namespace {
 struct BwdPlan {
   Plan pl;
   int nbl;  // block levels: bit_length(nb - 1)
-  size_t fwd_off, doo_off, din_off, w_off, wt_off, bt_off, scratch_off, bytes;
+  size_t fwd_off, doo_off, din_off, w_off, bt_off, scratch_off;
+  // run-shape copies of dO and of the gradients, where the run shape differs
+  size_t dop_off, dqp_off, dkp_off, dvp_off, dgp_off, dlp_off;
+  size_t bytes;
 };
 
 ll_status plan_bwd(const ll_problem* p, BwdPlan* out) {
   Plan pl;
   ll_status st = plan_prefill(p, false, &pl);
   if (st != LL_OK) return st;
+  // fp32 runs 32-token chunks where 64 are asked for: the gradients do not
+  // depend on the chunk size, and the walks' fp32 fragments of 64 tokens do not
+  // fit two waves per SIMD
+  if (p->io == LL_F32 && pl.r.C == 64) {
+    ll_problem q = *p;
+    q.C = 32;
+    st = plan_prefill(&q, false, &pl);
+    if (st != LL_OK) return st;
+  }
   if (p->rule != LL_MAMBA2) return fail(LL_ERR_UNSUPPORTED, "the backward pass is implemented for the Mamba-2 write");
+  const ll_problem& r = pl.r;
   BwdPlan c;
   c.pl = pl;
   c.nbl = bit_length((int64_t)pl.nb - 1);
-  const size_t bh = (size_t)p->B * p->H, rows = (size_t)p->B * p->T * p->H;
-  const size_t dd = (size_t)p->dk * p->dv;
+  const size_t bh = (size_t)r.B * r.H, rows = (size_t)r.B * r.T * r.H;
+  const size_t dd = (size_t)r.dk * r.dv;
+  const size_t esz = p->io == LL_BF16 ? 2 : 4;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -647,10 +803,22 @@ ll_status plan_bwd(const ll_problem* p, BwdPlan* out) {
   c.doo_off = take(rows * 4);
   c.din_off = take(rows * 4);
   c.w_off = take(bh * pl.nb * (size_t)c.nbl * dd * 4);
-  c.wt_off = take(bh * pl.nb * (size_t)c.nbl * dd * 4);
   c.bt_off = take(bh * pl.nb * 4);
-  c.scratch_off = take(llattn::bwd_states_in_lds(p->dk) ? 0
-                                                        : bh * pl.nb * (size_t)llattn::max_block_depth(p->dk) * dd * 4);
+  c.scratch_off = take(llattn::bwd_states_in_lds(r.dk) ? 0
+                                                        : bh * pl.nb * (size_t)llattn::max_block_depth(r.dk) * dd * 4);
+  c.dop_off = c.dqp_off = c.dkp_off = c.dvp_off = c.dgp_off = c.dlp_off = 0;
+  if (pl.pad_qk) {
+    c.dqp_off = take(rows * r.dk * esz);
+    c.dkp_off = take(rows * r.dk * esz);
+  }
+  if (pl.pad_v) {
+    c.dop_off = take(rows * r.dv * esz);
+    c.dvp_off = take(rows * r.dv * esz);
+  }
+  if (pl.pad_t) {
+    c.dgp_off = take(rows * 4);
+    c.dlp_off = take(rows * (size_t)r.L * 4);
+  }
   c.bytes = off;
   *out = c;
   return LL_OK;
@@ -684,55 +852,91 @@ ll_status ll_attn_bwd(const ll_problem* p, const void* q, const void* k, const v
   if (!workspace) return fail(LL_ERR_WORKSPACE, "workspace is NULL");
   char* ws = static_cast<char*>(workspace);
   const Plan& pl = c.pl;
+  const ll_problem& r = pl.r;
+  char* fws = ws + c.fwd_off;  // the prefill workspace: block states, nodes and run-shape input copies
   const int io = p->io == LL_BF16 ? 1 : 0;
-  const int D = p->dk;
+  const int esz = io ? 2 : 4;
+  const int D = r.dk;
+  hipError_t e = hipSuccess;
+  auto step = [&](auto fn) {
+    if (e == hipSuccess) e = fn();
+  };
+
+  // the inputs in the run shape
+  const void *qr = q, *kr = k, *vr = v, *dor = dO;
+  const float *gr = log_gate, *lr = lambda;
+  void *dqr = dq, *dkr = dk, *dvr = dv;
+  float *dgr = dlog_gate, *dlr = dlambda;
+  if (pl.pad_qk) {
+    step([&] { return pad_rows(esz, q, p->B, p->T, p->H, p->dk, fws + pl.qp_off, r.T, D, stream); });
+    step([&] { return pad_rows(esz, k, p->B, p->T, p->H, p->dk, fws + pl.kp_off, r.T, D, stream); });
+    qr = fws + pl.qp_off;
+    kr = fws + pl.kp_off;
+    dqr = ws + c.dqp_off;
+    dkr = ws + c.dkp_off;
+  }
+  if (pl.pad_v) {
+    step([&] { return pad_rows(esz, v, p->B, p->T, p->H, p->dv, fws + pl.vp_off, r.T, D, stream); });
+    step([&] { return pad_rows(esz, dO, p->B, p->T, p->H, p->dv, ws + c.dop_off, r.T, D, stream); });
+    vr = fws + pl.vp_off;
+    dor = ws + c.dop_off;
+    dvr = ws + c.dvp_off;
+  }
+  if (pl.pad_t) {
+    step([&] { return pad_rows(4, log_gate, p->B, p->T, p->H, 1, fws + pl.gp_off, r.T, 1, stream); });
+    step([&] { return pad_rows(4, lambda, p->B, p->T, p->H, p->L, fws + pl.lp_off, r.T, p->L, stream); });
+    gr = reinterpret_cast<const float*>(fws + pl.gp_off);
+    lr = reinterpret_cast<const float*>(fws + pl.lp_off);
+    dgr = reinterpret_cast<float*>(ws + c.dgp_off);
+    dlr = reinterpret_cast<float*>(ws + c.dlp_off);
+  }
 
   // the forward's block states and Fenwick nodes of (v, k): the transposed
   // states of (k, v), which the forward walk reads as S dO
   PrefillArgs f;
-  f.B = p->B;
-  f.T = p->T;
-  f.H = p->H;
-  f.L = p->L;
+  f.B = r.B;
+  f.T = r.T;
+  f.H = r.H;
+  f.L = r.L;
   f.LS = pl.LS;
   f.P = pl.P;
   f.nb = pl.nb;
   f.nF = pl.nF;
   f.q = nullptr;
-  f.k = v;
-  f.v = k;
-  f.g = log_gate;
-  f.lam = lambda;
+  f.k = vr;
+  f.v = kr;
+  f.g = gr;
+  f.lam = lr;
   f.o = nullptr;
-  f.S = reinterpret_cast<float*>(ws + c.fwd_off + pl.s_off);
-  f.GS = reinterpret_cast<float*>(ws + c.fwd_off + pl.gs_off);
-  f.F = reinterpret_cast<float*>(ws + c.fwd_off + pl.f_off);
-  f.GF = reinterpret_cast<float*>(ws + c.fwd_off + pl.gf_off);
+  f.S = reinterpret_cast<float*>(fws + pl.s_off);
+  f.GS = reinterpret_cast<float*>(fws + pl.gs_off);
+  f.F = reinterpret_cast<float*>(fws + pl.f_off);
+  f.GF = reinterpret_cast<float*>(fws + pl.gf_off);
   f.N16 = nullptr;
   f.state = nullptr;
   f.state_in = nullptr;
   f.pos0 = 0;
-  hipError_t e = timed(K_BWD, stream, [&] { return llattn::launch_block_state(io, D, pl.Cr, f, stream); });
+  if (e == hipSuccess) e = timed(K_BWD, stream, [&] { return llattn::launch_block_state(io, D, pl.Cr, f, stream); });
   if (e == hipSuccess && pl.nb > 1) e = timed(K_BWD, stream, [&] { return llattn::launch_fenwick_scan(D, f, stream); });
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
 
   llattn::BwdArgs a;
-  a.B = p->B;
-  a.T = p->T;
-  a.H = p->H;
+  a.B = r.B;
+  a.T = r.T;
+  a.H = r.H;
   a.D = D;
-  a.L = p->L;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.g = log_gate;
-  a.lam = lambda;
-  a.dO = dO;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.dlog_gate = dlog_gate;
-  a.dlambda = dlambda;
+  a.L = r.L;
+  a.q = qr;
+  a.k = kr;
+  a.v = vr;
+  a.g = gr;
+  a.lam = lr;
+  a.dO = dor;
+  a.dq = dqr;
+  a.dk = dkr;
+  a.dv = dvr;
+  a.dlog_gate = dgr;
+  a.dlambda = dlr;
   llattn::BwdFwdNodes n;
   n.nb = pl.nb;
   n.nF = pl.nF;
@@ -746,13 +950,19 @@ ll_status ll_attn_bwd(const ll_problem* p, const void* q, const void* k, const v
   w.dOo = reinterpret_cast<float*>(ws + c.doo_off);
   w.din = reinterpret_cast<float*>(ws + c.din_off);
   w.W = reinterpret_cast<float*>(ws + c.w_off);
-  w.WT = reinterpret_cast<float*>(ws + c.wt_off);
   w.BT = reinterpret_cast<float*>(ws + c.bt_off);
   w.nbl = c.nbl;
   w.scratch = llattn::bwd_states_in_lds(D) ? nullptr : reinterpret_cast<float*>(ws + c.scratch_off);
   // the forward walk; the reverse bucket states; the reverse walk; the gate's later blocks
   for (int pass = 0; pass < 4 && e == hipSuccess; ++pass)
     e = timed(K_BWD, stream, [&] { return llattn::launch_bwd_native(io, D, pl.Cr, a, n, w, pass, stream); });
+
+  // the gradients in the caller's shape
+  if (dqr != dq) step([&] { return pad_rows(esz, dqr, p->B, r.T, p->H, D, dq, p->T, p->dk, stream); });
+  if (dkr != dk) step([&] { return pad_rows(esz, dkr, p->B, r.T, p->H, D, dk, p->T, p->dk, stream); });
+  if (dvr != dv) step([&] { return pad_rows(esz, dvr, p->B, r.T, p->H, D, dv, p->T, p->dv, stream); });
+  if (dgr != dlog_gate) step([&] { return pad_rows(4, dgr, p->B, r.T, p->H, 1, dlog_gate, p->T, 1, stream); });
+  if (dlr != dlambda) step([&] { return pad_rows(4, dlr, p->B, r.T, p->H, p->L, dlambda, p->T, p->L, stream); });
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -1110,10 +1110,14 @@ static hipError_t launch_native_t(const BwdArgs& a, const BwdFwdNodes& n, const 
   constexpr int MAXB = max_block_depth(D);
   constexpr bool SLDS = bwd_states_in_lds(D);  // chunk-level states in LDS (3 x 17 KiB at d = 64)
   constexpr int FV = state_frag_vgprs<T, D>();
-  constexpr int HF = 32 / FV > 2 ? 2 : 32 / FV;  // forward walk: nodes held in registers
-  constexpr int HR = 64 / FV > 2 ? 2 : 64 / FV;  // reverse walk: buckets held in registers
+  // held in registers for a whole walk (fewer for fp32 at C = 64: eight waves
+  // leave 256 registers per wave, and fp32 fragments of a state take more)
+  constexpr int HCAP = (sizeof(T) == 4 && C == 64) ? 1 : 2;
+  constexpr int HF = 32 / FV > HCAP ? HCAP : 32 / FV;  // forward walk: nodes
+  constexpr int HR = 64 / FV > HCAP ? HCAP : 64 / FV;  // reverse walk: buckets
   constexpr int NW = C / 16, DT = D / 16, NTW = (DT + NW - 1) / NW;
-  constexpr int NLBF = 8 / (NTW * DT) > 2 ? 2 : 8 / (NTW * DT);  // block levels whose shares the forward walk makes
+  // block levels whose shares the forward walk makes
+  constexpr int NLBF = 8 / (NTW * DT) > HCAP ? HCAP : 8 / (NTW * DT);
   constexpr int NLB = D >= 128 ? 4 : 8;  // block levels per rev_state workgroup: NLB x D/16 accumulator tiles
   const int grid = a.B * a.H * n.nb;
   if (pass == 0) {
@@ -1167,12 +1171,11 @@ hipError_t launch_bwd_native(int io, int D, int C, const BwdArgs& a, const BwdFw
   switch (D * 1000 + C) {
     case 16016: return launch_native_t<float, 16, 16>(a, n, w, pass, s);
     case 16032: return launch_native_t<float, 16, 32>(a, n, w, pass, s);
-    case 16064: return launch_native_t<float, 16, 64>(a, n, w, pass, s);
     case 32016: return launch_native_t<float, 32, 16>(a, n, w, pass, s);
     case 32032: return launch_native_t<float, 32, 32>(a, n, w, pass, s);
-    case 32064: return launch_native_t<float, 32, 64>(a, n, w, pass, s);
     case 64016: return launch_native_t<float, 64, 16>(a, n, w, pass, s);
     case 64032: return launch_native_t<float, 64, 32>(a, n, w, pass, s);
+    case 128016: return launch_native_t<float, 128, 16>(a, n, w, pass, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -181,6 +181,7 @@ static hipError_t launch_combine_t(int B, int T_, int H, int CS, const void* q, 
 #define LL_CCQ_DISPATCH(FN, ...)                                  \
   if (io == 1) {                                                  \
     switch (D) {                                                  \
+      case 16: return FN<bf16, 16>(__VA_ARGS__);                  \
       case 32: return FN<bf16, 32>(__VA_ARGS__);                  \
       case 64: return FN<bf16, 64>(__VA_ARGS__);                  \
       case 128: return FN<bf16, 128>(__VA_ARGS__);                \
@@ -190,6 +191,7 @@ static hipError_t launch_combine_t(int B, int T_, int H, int CS, const void* q, 
       case 16: return FN<float, 16>(__VA_ARGS__);                 \
       case 32: return FN<float, 32>(__VA_ARGS__);                 \
       case 64: return FN<float, 64>(__VA_ARGS__);                 \
+      case 128: return FN<float, 128>(__VA_ARGS__);               \
     }                                                             \
   }                                                               \
   return hipErrorInvalidValue;

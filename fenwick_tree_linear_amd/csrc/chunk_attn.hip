@@ -750,6 +750,9 @@ static hipError_t launch_attn_t(const PrefillArgs& a, hipStream_t s) {
       case 16: LL_DISPATCH_C_F32(FN, 16)                         \
       case 32: LL_DISPATCH_C_F32(FN, 32)                         \
       case 64: LL_DISPATCH_C_F32(FN, 64)                         \
+      case 128: /* a C x 128 fp32 tile fits at C = 16 only */    \
+        if (C == 16) return FN<float, 128, 16>(a, s);            \
+        return hipErrorInvalidValue;                             \
       default: return hipErrorInvalidValue;                      \
     }                                                            \
   }

@@ -25,33 +25,34 @@ namespace llattn {
 
 constexpr int kDecodeLevelsMax = 32;
 
-template <typename T, int D>
+template <typename T, int DK, int DV>
 __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
-  constexpr int NTH = (D * D / 4 < 256) ? D * D / 4 : 256;
-  constexpr int CG = D / 4;      // column groups of 4 floats
+  constexpr int NTH = (DK * DV / 4 < 256) ? DK * DV / 4 : 256;
+  constexpr int CG = DV / 4;     // column groups of 4 floats
   constexpr int RG = NTH / CG;   // row groups
-  constexpr int RPT = D / RG;    // rows per thread
+  constexpr int RPT = DK / RG;   // rows per thread
+  static_assert(RG * RPT == DK && NTH >= 64 && NTH >= DV, "a state row group per thread");
   // levels whose rows are in flight together (at most 20 f32x4 rows per
   // thread, so that four workgroups fit a CU: all heads of the 32K decode
   // workload in one round)
   constexpr int kDecodeBatch = RPT >= 20 ? 1 : (20 / RPT < 5 ? 20 / RPT : 5);
-  __shared__ float qs[D], ks[D], vs[D], us[D];
+  __shared__ float qs[DK], ks[DK], vs[DV], us[DV];
   __shared__ float lam[kDecodeLevelsMax], sig[kDecodeLevelsMax];
   __shared__ float qk_s;
-  __shared__ __attribute__((aligned(16))) float red[RG][D];
-  __shared__ __attribute__((aligned(16))) float redk[RG][D];  // Gated DeltaNet: the levels read by k
+  __shared__ __attribute__((aligned(16))) float red[RG][DV];
+  __shared__ __attribute__((aligned(16))) float redk[RG][DV];  // Gated DeltaNet: the levels read by k
 
   const int bh = blockIdx.x;
   const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
   const int L = a.L;
-  float* Sh = a.state + (int64_t)bh * L * D * D;
-  float* sigma = a.state + (int64_t)a.B * a.H * L * D * D + (int64_t)bh * L;
+  float* Sh = a.state + (int64_t)bh * L * DK * DV;
+  float* sigma = a.state + (int64_t)a.B * a.H * L * DK * DV + (int64_t)bh * L;
   // one position for the batch (checked by the host), or one per sequence
   // from device memory: a position whose successor state would not fit in L
   // levels (or a negative one) gives NaN outputs and leaves the state as it is
   const int64_t pos = a.pos_dev ? a.pos_dev[bh / a.H] : a.pos;
   if (pos < 0 || pos + 1 >= ((int64_t)1 << (L - 1))) {
-    for (int x = tid; x < D; x += NTH) static_cast<T*>(a.o)[(int64_t)bh * D + x] = from_f32<T>(__builtin_nanf(""));
+    for (int x = tid; x < DV; x += NTH) static_cast<T*>(a.o)[(int64_t)bh * DV + x] = from_f32<T>(__builtin_nanf(""));
     return;  // the whole workgroup: pos is the same for every thread
   }
   const int c = __ffsll((unsigned long long)(pos + 1)) - 1;
@@ -68,24 +69,24 @@ __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
     lv[u] = bits ? __ffsll((unsigned long long)bits) : 0;  // level = bit index + 1; 0 = none
     bits &= bits - 1;
     if (lv[u] == 0) continue;
-    const float* lev = Sh + (int64_t)lv[u] * D * D + 4 * cg;
+    const float* lev = Sh + (int64_t)lv[u] * DK * DV + 4 * cg;
 #pragma unroll
-    for (int rr = 0; rr < RPT; ++rr) rows[u][rr] = *reinterpret_cast<const f32x4*>(lev + (rr * RG + rg) * D);
+    for (int rr = 0; rr < RPT; ++rr) rows[u][rr] = *reinterpret_cast<const f32x4*>(lev + (rr * RG + rg) * DV);
   }
 
-  const T* q = static_cast<const T*>(a.q) + (int64_t)bh * D;
-  const T* k = static_cast<const T*>(a.k) + (int64_t)bh * D;
-  const T* v = static_cast<const T*>(a.v) + (int64_t)bh * D;
+  const T* q = static_cast<const T*>(a.q) + (int64_t)bh * DK;
+  const T* k = static_cast<const T*>(a.k) + (int64_t)bh * DK;
+  const T* v = static_cast<const T*>(a.v) + (int64_t)bh * DV;
   if (tid < 64) {
     // q.k by one wave: lane x holds q_x k_x (+ q_{x+64} k_{x+64}), then a butterfly
     float pk = 0.f;
-    for (int x = tid; x < D; x += 64) {
+    for (int x = tid; x < DK; x += 64) {
       const float qx = to_f32(q[x]), kx = to_f32(k[x]);
       qs[x] = qx;
       ks[x] = kx;
-      vs[x] = to_f32(v[x]);
       pk += qx * kx;
     }
+    for (int x = tid; x < DV; x += 64) vs[x] = to_f32(v[x]);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) pk += __shfl_xor(pk, m, 64);
     if (tid == 0) qk_s = pk;
@@ -127,16 +128,16 @@ __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
       lv[u] = bits ? __ffsll((unsigned long long)bits) : 0;
       bits &= bits - 1;
       if (lv[u] == 0) continue;
-      const float* lev = Sh + (int64_t)lv[u] * D * D + 4 * cg;
+      const float* lev = Sh + (int64_t)lv[u] * DK * DV + 4 * cg;
 #pragma unroll
-      for (int rr = 0; rr < RPT; ++rr) rows[u][rr] = *reinterpret_cast<const f32x4*>(lev + (rr * RG + rg) * D);
+      for (int rr = 0; rr < RPT; ++rr) rows[u][rr] = *reinterpret_cast<const f32x4*>(lev + (rr * RG + rg) * DV);
     }
   }
 
   *reinterpret_cast<f32x4*>(&red[rg][4 * cg]) = part;
   if (gdn) *reinterpret_cast<f32x4*>(&redk[rg][4 * cg]) = kpart;
   __syncthreads();
-  if (tid < D) {
+  if (tid < DV) {
     float acc = 0.f;
     for (int r = 0; r < RG; ++r) acc += red[r][tid];
     // the value this token writes: v, or for Gated DeltaNet its pseudo-value
@@ -148,45 +149,52 @@ __global__ void __launch_bounds__(256) ll_decode_step(DecodeArgs a) {
       u = a.beta[bh] * (vs[tid] - sk);
       us[tid] = u;
     }
-    static_cast<T*>(a.o)[(int64_t)bh * D + tid] = from_f32<T>(lam[0] * qk_s * u + acc);
+    static_cast<T*>(a.o)[(int64_t)bh * DV + tid] = from_f32<T>(lam[0] * qk_s * u + acc);
   }
   if (gdn) __syncthreads();
 
   // merge into level c+1 (c + 1 <= L - 1 by the position check above)
-  float* dst = Sh + (int64_t)(c + 1) * D * D + 4 * cg;
+  float* dst = Sh + (int64_t)(c + 1) * DK * DV + 4 * cg;
   const f32x4 vv = *reinterpret_cast<const f32x4*>(gdn ? &us[4 * cg] : &vs[4 * cg]);
 #pragma unroll
   for (int rr = 0; rr < RPT; ++rr) {
     const int d = rr * RG + rg;
-    *reinterpret_cast<f32x4*>(dst + d * D) = ks[d] * vv + msum[rr];
+    *reinterpret_cast<f32x4*>(dst + d * DV) = ks[d] * vv + msum[rr];
   }
   for (int x = tid; x < L; x += NTH) sigma[x] = (x == c + 1) ? 0.f : sig[x];
 }
 
-template <typename T, int D>
+template <typename T, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
-  constexpr int NTH = (D * D / 4 < 256) ? D * D / 4 : 256;
-  hipLaunchKernelGGL((ll_decode_step<T, D>), dim3(a.B * a.H), dim3(NTH), 0, s, a);
+  constexpr int NTH = (DK * DV / 4 < 256) ? DK * DV / 4 : 256;
+  hipLaunchKernelGGL((ll_decode_step<T, DK, DV>), dim3(a.B * a.H), dim3(NTH), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_step(int io, int D, const DecodeArgs& a, hipStream_t s) {
-  if (io == 1) {
-    switch (D) {
-      case 16: return launch_decode_t<bf16, 16>(a, s);
-      case 32: return launch_decode_t<bf16, 32>(a, s);
-      case 64: return launch_decode_t<bf16, 64>(a, s);
-      case 128: return launch_decode_t<bf16, 128>(a, s);
-    }
-  } else {
-    switch (D) {
-      case 16: return launch_decode_t<float, 16>(a, s);
-      case 32: return launch_decode_t<float, 32>(a, s);
-      case 64: return launch_decode_t<float, 64>(a, s);
-      case 128: return launch_decode_t<float, 128>(a, s);
-    }
+template <typename T, int DK>
+static hipError_t launch_decode_dv(int DV, const DecodeArgs& a, hipStream_t s) {
+  switch (DV) {
+    case 16: return launch_decode_t<T, DK, 16>(a, s);
+    case 32: return launch_decode_t<T, DK, 32>(a, s);
+    case 64: return launch_decode_t<T, DK, 64>(a, s);
+    case 128: return launch_decode_t<T, DK, 128>(a, s);
   }
   return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t launch_decode_dk(int DK, int DV, const DecodeArgs& a, hipStream_t s) {
+  switch (DK) {
+    case 16: return launch_decode_dv<T, 16>(DV, a, s);
+    case 32: return launch_decode_dv<T, 32>(DV, a, s);
+    case 64: return launch_decode_dv<T, 64>(DV, a, s);
+    case 128: return launch_decode_dv<T, 128>(DV, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_step(int io, int DK, int DV, const DecodeArgs& a, hipStream_t s) {
+  return io == 1 ? launch_decode_dk<bf16>(DK, DV, a, s) : launch_decode_dk<float>(DK, DV, a, s);
 }
 
 }  // namespace llattn

@@ -606,6 +606,7 @@ static hipError_t launch_gst_t(const GdnArgs& a, hipStream_t s) {
       case 64016: return FN<float, 64, 16>(a, s);                              \
       case 64032: return FN<float, 64, 32>(a, s);                              \
       case 64064: return FN<float, 64, 64>(a, s);                              \
+      case 128016: return FN<float, 128, 16>(a, s);                            \
       default: return hipErrorInvalidValue;                                    \
     }                                                                          \
   }
@@ -631,6 +632,7 @@ LL_GDN_INSTANCES(float, 32, 64)
 LL_GDN_INSTANCES(float, 64, 16)
 LL_GDN_INSTANCES(float, 64, 32)
 LL_GDN_INSTANCES(float, 64, 64)
+LL_GDN_INSTANCES(float, 128, 16)
 #undef LL_GDN_INSTANCES
 
 hipError_t launch_gdn_wy(int io, int D, int C, const GdnArgs& a, hipStream_t s) { LL_GDN_DISPATCH(launch_wy_t) }

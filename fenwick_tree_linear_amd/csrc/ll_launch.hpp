@@ -101,7 +101,6 @@ struct BwdWork {
   float* dOo;      // [B,T,H] the cross-chunk part of dO_t . o_t
   float* din;      // [B,T,H] the in-chunk pairs' share of the gate gradient
   float* W;        // [B*H, nb, nbl, D*D] block shares of the reverse bucket states, then the bucket states
-  float* WT;       // [B*H, nb, nbl, D*D] the bucket states transposed (at each bucket's first block)
   float* BT;       // [B*H, nb] per block: sum of dO.o - v.dv over its cross-chunk pairs, then the sum over later blocks
   int nbl;         // block levels: bit_length(nb - 1)
   float* scratch;  // [B*H*nb, max_block_depth, D*D] chunk-level states of a walk, where they do not fit in LDS
@@ -123,7 +122,10 @@ hipError_t launch_ccq_ksum(int io, int D, int B, int T, int H, int CS, const voi
 hipError_t launch_ccq_combine(int io, int D, int B, int T, int H, int CS, const void* q, const void* k,
                               const void* kkq, const float* csum, const float* w, const float* b, void* qc,
                               hipStream_t s);
-hipError_t launch_decode_step(int io, int D, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_step(int io, int DK, int DV, const DecodeArgs& a, hipStream_t s);
+// dst[i0][i1][i2][i3] = src[..] inside src's extents (s1, s2, s3), else 0; esz 2 or 4 bytes
+hipError_t launch_pad_copy(int esz, const void* src, void* dst, int64_t n0, int s1, int s2, int s3, int d1, int d2,
+                           int d3, hipStream_t s);
 hipError_t launch_gdn_wy(int io, int D, int C, const GdnArgs& a, hipStream_t s);
 hipError_t launch_gdn_state(int io, int D, int C, const GdnArgs& a, hipStream_t s);
 hipError_t launch_lambda_mlp(int64_t rows, int L, int hidden, const float* d, const float* w1, const float* w2,

@@ -163,6 +163,9 @@ hipError_t launch_prior_read(int io, int D, int C, const PrefillArgs& a, hipStre
       case 16: { LL_PRIOR_C(float, 16) }
       case 32: { LL_PRIOR_C(float, 32) }
       case 64: { LL_PRIOR_C(float, 64) }
+      case 128:  // a C x 128 fp32 tile fits at C = 16 only
+        if (C == 16) return launch_prior_t<float, 128, 16>(a, s);
+        break;
     }
   }
 #undef LL_PRIOR_C

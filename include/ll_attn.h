@@ -69,15 +69,22 @@ typedef enum { LL_MAMBA2 = 0, LL_GATED_DELTANET = 1 } ll_rule;
  *             two with T % C == 0.  The result does not depend on C beyond
  *             rounding.
  *   io      : dtype of q, k, v and o.  Gates, lambda, beta and states are fp32.
- * Implemented (LL_ERR_UNSUPPORTED otherwise): dk == dv, and
- *   bf16 io: dk in {32, 64, 128}, C in {32, 64};
- *   fp32 io: dk in {16, 32, 64},  C in {16, 32, 64};
- *   a chunk tile of C x dk values within 8 KiB (bf16: C = 64 with dk <= 64,
- *   C = 32 with any dk; fp32: C x dk <= 2048) -- for LL_GATED_DELTANET this
- *   binds the read only: the pseudo-value pass runs at C and the read at the
- *   largest supported chunk dividing C whose tile fits (bf16 dk = 128 with
- *   C = 64 reads at 32), so every (dk, C) pair listed above is accepted;
- *   T < 2^23.
+ * Accepted (LL_ERR_UNSUPPORTED otherwise): dk and dv each in {16, 32, 64,
+ *   128}, C in {16, 32, 64}, both io dtypes, T < 2^23.  The kernels run a
+ *   square head D and their own chunk, since the read is the same sum
+ *   whatever the head padding or the chunk size:
+ *   - D = max(dk, dv), and 32 for bf16 at 16: q and k (dk < D) or v (dv < D)
+ *     run on zero-padded copies in the workspace (zero key columns add nothing
+ *     to q.k; the padded output columns are dropped);
+ *   - bf16 runs chunks of at least 32 tokens (a bf16 matrix-core step
+ *     contracts 32 values); where T is not a multiple of the run chunk, the
+ *     inputs run zero-padded at the end (zero keys and values, no decay) and
+ *     need L covering the padded length; the state export then needs T a
+ *     multiple of the run chunk;
+ *   - a C x D tile of the read stays within 8 KiB: larger chunks run halved
+ *     (bf16 D = 128 at 32 tokens, fp32 D = 128 at 16).  For
+ *     LL_GATED_DELTANET the pseudo-value pass runs at the requested chunk
+ *     (fp32 D = 128: 16) and the read at the largest chunk that fits.
  */
 typedef struct {
   int B, T, H, dk, dv, L, C;
@@ -89,9 +96,10 @@ typedef struct {
  * Bytes of device workspace ll_attn_fwd needs for `p` (0 is possible).  The
  * workspace holds, per head, the decayed key-value state of every aligned span
  * of chunks and its Fenwick combination (chunk-parallel form, section 2.3);
- * for LL_GATED_DELTANET also three [B,T,H,dv] io-dtype row buffers: the
+ * for LL_GATED_DELTANET also three [B,T,H,D] io-dtype row buffers: the
  * per-chunk WY factors (I + L)^-1 diag(beta e^G) K and (I + L)^-1 diag(beta) V
- * and the pseudo-values u the read runs on.
+ * and the pseudo-values u the read runs on; and, for a problem not run in its
+ * own shape, the padded copies of the inputs, the output and the states.
  * Errors: LL_ERR_NULL, and every validation error of ll_attn_fwd.
  */
 ll_status ll_attn_fwd_workspace_bytes(const ll_problem* p, size_t* bytes);
@@ -253,8 +261,7 @@ ll_status ll_decode_step_ragged(int B, int H, int dk, int dv, int L, ll_dtype io
  * The running second moment comes from a chunk-parallel prefill with every
  * level weight 1 and no decay, the running key sum from a chunked fp32
  * prefix sum.  Implemented for the head sizes of ll_attn_fwd and T
- * a multiple of a supported chunk size (16 for fp32, 32 for bf16), T < 2^23
- * (LL_ERR_UNSUPPORTED otherwise).
+ * a multiple of 16, T < 2^23 (LL_ERR_UNSUPPORTED otherwise).
  */
 ll_status ll_ccq_query_workspace_bytes(int B, int T, int H, int dk, ll_dtype io, size_t* bytes);
 ll_status ll_ccq_query(int B, int T, int H, int dk, ll_dtype io, const void* q, const void* k, const float* w,

@@ -19,7 +19,8 @@ hipError_t launch_ccq_fill(int64_t, int, float*, float*, hipStream_t) { STUB; }
 hipError_t launch_ccq_ksum(int, int, int, int, int, int, const void*, float*, hipStream_t) { STUB; }
 hipError_t launch_ccq_combine(int, int, int, int, int, int, const void*, const void*, const void*, const float*,
                               const float*, const float*, void*, hipStream_t) { STUB; }
-hipError_t launch_decode_step(int, int, const DecodeArgs&, hipStream_t) { STUB; }
+hipError_t launch_decode_step(int, int, int, const DecodeArgs&, hipStream_t) { STUB; }
+hipError_t launch_pad_copy(int, const void*, void*, int64_t, int, int, int, int, int, int, hipStream_t) { STUB; }
 hipError_t launch_gdn_wy(int, int, int, const GdnArgs&, hipStream_t) { STUB; }
 hipError_t launch_gdn_state(int, int, int, const GdnArgs&, hipStream_t) { STUB; }
 hipError_t launch_lambda_mlp(int64_t, int, int, const float*, const float*, const float*, const float*, float*,

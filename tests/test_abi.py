@@ -72,6 +72,25 @@ def test_gdn_workspace_holds_three_row_buffers():
     assert F.ll_attn_fwd_workspace_bytes(prob(T=8192, L=14, dk=128, dv=128, rule=F.LL_GATED_DELTANET)) > 0
 
 
+@pytest.mark.parametrize("io", [F.LL_F32, F.LL_BF16])
+def test_full_shape_set_is_accepted(io):
+    """Every head size (dk and dv each in 16, 32, 64, 128, also unequal) and
+    chunk size (16, 32, 64) of the boundary is accepted by every prefill, the
+    backward (Mamba-2) and the decode; shapes the kernels do not run natively
+    run zero-padded to a square head, in bf16 32-token chunks, or in chunks
+    halved until a tile fits."""
+    for dk in (16, 32, 64, 128):
+        for dv in (16, 32, 64, 128):
+            for C in (16, 32, 64):
+                for rule in (F.LL_MAMBA2, F.LL_GATED_DELTANET):
+                    p = prob(B=1, T=256, H=2, dk=dk, dv=dv, L=9, C=C, io=io, rule=rule)
+                    assert F.ll_attn_fwd_workspace_bytes(p) > 0, (dk, dv, C, rule)
+                assert F.ll_attn_bwd_workspace_bytes(prob(B=1, T=256, H=2, dk=dk, dv=dv, L=9, C=C, io=io)) > 0
+            assert F.ll_decode_state_bytes(2, 3, dk, dv, 9) == 2 * 3 * 9 * (dk * dv + 1) * 4
+    # bf16 chunks of 16 with T not a multiple of 32 run padded to the next multiple
+    assert F.ll_attn_fwd_workspace_bytes(prob(B=1, T=48, H=2, L=7, C=16, io=io)) > 0
+
+
 def test_workspace_grows_with_problem():
     a = F.ll_attn_fwd_workspace_bytes(prob(T=2048, L=12))
     b = F.ll_attn_fwd_workspace_bytes(prob(T=4096, L=13))
@@ -83,12 +102,9 @@ def test_workspace_grows_with_problem():
     (dict(T=1000), "LL_ERR_SHAPE", "multiple"),
     (dict(C=48), "LL_ERR_SHAPE", "power of two"),
     (dict(C=128), "LL_ERR_UNSUPPORTED", "chunk"),
-    (dict(C=16), "LL_ERR_UNSUPPORTED", "chunk"),
-    (dict(dk=64, dv=32), "LL_ERR_UNSUPPORTED", "dk"),
     (dict(dk=48, dv=48), "LL_ERR_UNSUPPORTED", "head size"),
-    (dict(dk=16, dv=16), "LL_ERR_UNSUPPORTED", "head size"),
-    (dict(dk=128, dv=128), "LL_ERR_UNSUPPORTED", "exceeds"),
-    (dict(io=F.LL_F32, dk=64, dv=64, C=64), "LL_ERR_UNSUPPORTED", "exceeds"),
+    (dict(dk=64, dv=24), "LL_ERR_UNSUPPORTED", "head size"),
+    (dict(C=16, T=16, L=5), "LL_ERR_UNSUPPORTED", "L >= 6"),  # bf16 runs T = 16 padded to 32 tokens
     (dict(io=7), "LL_ERR_DTYPE", "dtype"),
     (dict(rule=5), "LL_ERR_UNSUPPORTED", "rule"),
     (dict(B=0), "LL_ERR_SHAPE", "positive"),
@@ -139,7 +155,7 @@ def test_decode_validation_before_any_launch():
         (dict(L=33, pos=5), "LL_ERR_UNSUPPORTED"),
         (dict(io=3), "LL_ERR_DTYPE"),
         (dict(rule=F.LL_GATED_DELTANET), "LL_ERR_NULL"),  # Gated DeltaNet needs beta
-        (dict(dk=64, dv=32), "LL_ERR_UNSUPPORTED"),
+        (dict(dk=64, dv=24), "LL_ERR_UNSUPPORTED"),
         (dict(state=None), "LL_ERR_NULL"),
         (dict(q=None), "LL_ERR_NULL"),
     ]
@@ -191,7 +207,7 @@ def test_ragged_decode_validation_before_any_launch():
         (dict(L=1), "LL_ERR_SHAPE"),
         (dict(io=3), "LL_ERR_DTYPE"),
         (dict(rule=F.LL_GATED_DELTANET), "LL_ERR_NULL"),
-        (dict(dk=64, dv=32), "LL_ERR_UNSUPPORTED"),
+        (dict(dk=64, dv=24), "LL_ERR_UNSUPPORTED"),
         (dict(dk=48, dv=48), "LL_ERR_UNSUPPORTED"),
         (dict(state=None), "LL_ERR_NULL"),
         (dict(o=None), "LL_ERR_NULL"),
@@ -252,12 +268,11 @@ def test_bwd_validation_before_any_launch():
     # reverse bucket states (4 blocks of 8 chunks per head: 2 block levels) and 3
     # chunk-level states per block, all fp32 64 x 64
     def need(T, L, nb, nbl):
-        # the forward's workspace, two fp32 values per row, the reverse bucket states and
-        # their transposes (one fp32 64 x 64 state per block and block level each) and
-        # one fp32 sum per block; at d = 64 the chunk-level states live in LDS
+        # the forward's workspace, two fp32 values per row, the reverse bucket states (one
+        # fp32 64 x 64 state per block and block level) and one fp32 sum per block; at
+        # d = 64 the chunk-level states live in LDS
         rows, heads, state = 2 * T * 16, 2 * 16, 64 * 64 * 4
-        return (F.ll_attn_fwd_workspace_bytes(prob(T=T, L=L)) + 2 * rows * 4 + heads * nb * 2 * nbl * state
-                + heads * nb * 4)
+        return F.ll_attn_fwd_workspace_bytes(prob(T=T, L=L)) + 2 * rows * 4 + heads * nb * nbl * state + heads * nb * 4
 
     assert need(2048, 12, 4, 2) <= n <= need(2048, 12, 4, 2) + 6 * 256  # 4 blocks of 8 chunks: 2 block levels
     m = F.ll_attn_bwd_workspace_bytes(prob(T=4096, L=13))  # 8 blocks: 3 block levels

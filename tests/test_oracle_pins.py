@@ -211,6 +211,18 @@ def test_direct_equals_recurrent(rule, T, L):
     assert rel_err(b, a) < 1e-12
 
 
+def test_zero_key_and_value_columns_change_nothing():
+    """Zero columns appended to q and k add nothing to any q.k, and zero columns
+    appended to v give zero output columns: the read at dk=3, dv=5 is the read
+    of the padded (6, 7) problem with its extra output columns dropped."""
+    q, k, v, g, lam, _ = tiny_inputs(T=29, dk=3, dv=5, L=6)
+    padc = lambda a, n: np.concatenate([a, np.zeros(a.shape[:-1] + (n,), np.float32)], axis=-1)
+    a = oracle.fwd_direct(q, k, v, g, lam)
+    b = oracle.fwd_direct(padc(q, 3), padc(k, 3), padc(v, 2), g, lam)
+    assert rel_err(b[..., :5], a) < 1e-12
+    assert np.max(np.abs(b[..., 5:])) == 0.0
+
+
 # --------------------------------------------------------- Gated DeltaNet pins
 
 def test_gdn_lambda_one_is_gated_delta_rule():
@@ -404,9 +416,11 @@ def test_lambda_mlp_acts_per_row():
 
 # ------------------------------------------------ backward (gradients)
 
-def _bwd_inputs(T=12, H=2, d=3, L=5, seed=0):
+def _bwd_inputs(T=12, H=2, d=3, L=5, seed=0, dv=None):
     rng = np.random.default_rng(seed)
-    q, k, v, dO = (rng.standard_normal((1, T, H, d)).astype(np.float32) for _ in range(4))
+    dv = d if dv is None else dv
+    q, k = (rng.standard_normal((1, T, H, d)).astype(np.float32) for _ in range(2))
+    v, dO = (rng.standard_normal((1, T, H, dv)).astype(np.float32) for _ in range(2))
     g = (-rng.uniform(0.01, 0.3, (1, T, H))).astype(np.float32)
     lam = rng.uniform(0.5, 1.5, (1, T, H, L)).astype(np.float32)
     return dict(q=q, k=k, v=v, log_gate=g, lam=lam), dO
@@ -417,13 +431,15 @@ def _loss(x, dO):
     return float(np.sum(o * dO.astype(np.float64)))
 
 
+@pytest.mark.parametrize("dv", [3, 5])
 @pytest.mark.parametrize("name", ["q", "k", "v", "lam", "log_gate"])
-def test_bwd_matches_finite_differences(name):
+def test_bwd_matches_finite_differences(name, dv):
     """Every gradient coordinate against a central difference of the forward
     oracle's loss sum(dO * o); the step actually taken in fp32 is used as the
     denominator.  The loss is linear in each single coordinate of q, k, v and
-    lambda (so the difference is exact up to rounding) and smooth in the gates."""
-    x, dO = _bwd_inputs()
+    lambda (so the difference is exact up to rounding) and smooth in the gates.
+    Square heads (dk = dv = 3) and unequal ones (dk = 3, dv = 5)."""
+    x, dO = _bwd_inputs(dv=dv)
     grads = oracle.bwd_direct(x["q"], x["k"], x["v"], x["log_gate"], x["lam"], dO)
     g = grads["d" + name if name != "lam" else "dlambda"]
     base = x[name]
