@@ -413,7 +413,9 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
     float sig[MAXB + 1];
     float gw = 0.f;  // log-decay from the start of block J to the current chunk
     auto node_of = [&](int e) {
-      return (e & 1) ? a.F + ((int64_t)bh * a.nF + (e >> 1)) * D * D : a.S + ((int64_t)bh * a.nb + e) * D * D;
+      const float* f = a.F + ((int64_t)bh * a.nF + (e >> 1)) * D * D;
+      const float* s = a.S + ((int64_t)bh * a.nb + e) * D * D;
+      return (e & 1) ? f : s;
     };
     // MFMA fragments of node e for this wave's columns: from the bf16 copies
     // in fragment order where they exist (one 16-byte load per fragment),
@@ -428,25 +430,41 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
       }
     };
     auto gamma_of = [&](int e) {
-      return (e & 1) ? a.GF[(int64_t)bh * a.nF + (e >> 1)] : a.GS[(int64_t)bh * a.nb + e];
+      const float* f = a.GF + (int64_t)bh * a.nF + (e >> 1);
+      const float* s = a.GS + (int64_t)bh * a.nb + e;
+      return *((e & 1) ? f : s);
     };
     auto start_item = [&]() __attribute__((always_inline)) {
       if (!first_item) read_at.next(a, C);
       first_item = false;
       bh = read_at.bh(a);
-      rest_far = read_at.J;
-      dd_far = 0.f;
+      // The held nodes: one per set bit of J, most recent first.  A slot past
+      // the last set bit repeats the first node and weighs nothing, so that
+      // every node and decay load goes out at once instead of each waiting
+      // for the one before.
+      const int J = read_at.J;
+      int ex[MAXH > 0 ? MAXH : 1];
+      rest_far = J;
 #pragma unroll
       for (int x = 0; x < MAXH; ++x) {
-        hlv[x] = -1;
-        hdd[x] = 0.f;
-        if (rest_far > 0) {
-          const int e = rest_far - 1;
-          load_node(hn[x], e);
-          hlv[x] = LOGC + 1 + logP + __ffs(rest_far) - 1;  // token level of the node
+        hlv[x] = rest_far > 0 ? LOGC + 1 + logP + __ffs(rest_far) - 1 : -1;  // token level of the node
+        ex[x] = rest_far > 0 ? rest_far - 1 : J - 1;
+        rest_far &= rest_far - 1;
+      }
+      dd_far = 0.f;
+#pragma unroll
+      for (int x = 0; x < MAXH; ++x) hdd[x] = 0.f;
+      if (MAXH > 0 && J > 0) {
+        float gm[MAXH > 0 ? MAXH : 1];
+#pragma unroll
+        for (int x = 0; x < MAXH; ++x) {
+          load_node(hn[x], ex[x]);
+          gm[x] = gamma_of(ex[x]);
+        }
+#pragma unroll
+        for (int x = 0; x < MAXH; ++x) {
           hdd[x] = dd_far;
-          dd_far += gamma_of(e);
-          rest_far &= rest_far - 1;
+          dd_far += hlv[x] >= 0 ? gm[x] : 0.f;
         }
       }
 #pragma unroll
@@ -666,12 +684,582 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
 }
 
 // ---------------------------------------------------------------------------
+// ll_chunk_attn_split: the same read for bf16 with two row groups, with the
+// work of a step divided by role instead of repeated per row group.
+//   readers (D/16 column tiles x 2 row groups): load the chunks, read out the
+//     intra-chunk product and every Fenwick level of their rows and columns,
+//     store o.
+//   makers (one per column tile): prepare the next chunk (masked scores and
+//     decay-scaled keys, each tile once) and merge this chunk into the
+//     within-block Fenwick states of their 16 columns, once for both row
+//     groups.  A merged state goes to LDS as bf16 MFMA fragments, which the
+//     readers take as they are.
+// A reader keeps no within-block state and a maker no output, so each fits
+// the register share of three waves per SIMD.
+template <int D, int C>
+struct SplitWaves {
+  static constexpr int NCT = D / 16;     // output column tiles
+  static constexpr int CT = C / 16;      // 16-row tiles of a chunk
+  static constexpr int NRW = 2 * NCT;    // reader waves
+  static constexpr int NMW = NCT;        // maker waves
+  static constexpr int NW = NRW + NMW;   // waves per workgroup
+  static constexpr int NRT = CT / 2;     // row tiles per reader
+  static_assert(CT == 2 || CT == 4, "two row groups of one or two row tiles");
+  // row group wr takes row tiles wr and CT-1-wr: the same share of the causal triangle
+  __host__ __device__ static constexpr int row_tile(int i, int wr) { return (i & 1) ? CT - 1 - wr : wr; }
+};
+
+// LDS of ll_chunk_attn_split (byte offsets): the chunk staging ring, masked
+// scores and decay-scaled keys of two chunk parities, the in-chunk prefix
+// arrays of two parities (one copy: every maker writes the same values), and
+// the within-block states as fragments [level][column tile][k step][lane].
+template <int D, int C, int MAXB>
+struct SplitLayout {
+  typedef Tile<bf16, C, D> TL;
+  typedef Tile<bf16, C, C> PT;
+  static constexpr int NS = 3;
+  static constexpr int FRAG_BYTES = 64 * 16;                           // one bf16 fragment of a wave
+  static constexpr int STATE_BYTES = MAXB * (D / 16) * (D / 32) * FRAG_BYTES;
+  int q, k, v, g, lraw, stage;
+  int p, kw, gw, st, total;
+  __host__ __device__ explicit SplitLayout(int LS) {
+    q = 0;
+    k = q + TL::BYTES;
+    v = k + TL::BYTES;
+    g = v + TL::BYTES;
+    lraw = g + C * 4;
+    stage = (lraw + C * LS * 4 + 255) & ~255;
+    p = NS * stage;
+    kw = p + 2 * PT::BYTES;
+    gw = kw + 2 * TL::BYTES;
+    st = (gw + 2 * 3 * C * 4 + 255) & ~255;
+    total = st + STATE_BYTES;
+  }
+};
+
+template <int D, int C, int MAXB, int MAXH>
+__global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_split(PrefillArgs a) {
+  typedef bf16 T;
+  using M = Mma<T>;
+  typedef typename M::Frag Frag;
+  typedef SplitLayout<D, C, MAXB> Lay;
+  typedef SplitWaves<D, C> W;
+  typedef Tile<T, C, D> TL;
+  typedef Tile<T, C, C> PT;
+  constexpr int NRW = W::NRW, NMW = W::NMW, NW = W::NW, NCT = W::NCT, NRT = W::NRT, CT = W::CT;
+  constexpr int DT = D / 16;
+  constexpr int KSD = D / M::KS, KSC = C / M::KS;
+  constexpr int LOGC = (C == 32) ? 5 : 6;
+  constexpr int NS = Lay::NS;
+  static_assert(NS == 3, "the staging ring is three buffers");
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  const int LS = a.LS;
+  const Lay lay(LS);
+  // the wave index is a scalar, so that every branch on it is a uniform jump
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, q16 = lane & 15;
+  const int wg = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int nitems = a.B * a.H * a.nb;
+  const int item0 = (int)((int64_t)wg * nitems / gridDim.x);
+  const int nsteps = ((int)((int64_t)(wg + 1) * nitems / gridDim.x) - item0) * a.P;
+  const int logP = ilog2c(a.P);
+  auto stage_of = [&](int t) { return smem + (t % NS) * lay.stage; };
+  // prefix arrays of step parity: G, e^{G[C-1]-G}, e^{G[end of 16-token tile]-G}
+  auto garr = [&](int t) { return reinterpret_cast<float*>(smem + lay.gw) + (t & 1) * 3 * C; };
+  // fragment s of the within-block state of level m (1..MAXB), column tile wc
+  auto state_frag = [&](int m, int wc, int s) {
+    return smem + lay.st + (((m - 1) * NCT + wc) * KSD + s) * Lay::FRAG_BYTES + lane * 16;
+  };
+
+  // masked-score tiles above the diagonal are never written: keep them zero
+  for (int x = tid * 16; x < 2 * PT::BYTES; x += 64 * NW * 16)
+    *reinterpret_cast<uint4*>(smem + lay.p + x) = uint4{0, 0, 0, 0};
+
+  // Preparation of chunk j for its read-out, in pieces that the waves share:
+  // the in-chunk prefix G of the log-gates (each preparing wave writes the
+  // same values), the masked scores
+  // P[r][s] = (q_r . k_s) lambda_r^(lev(r,s)) e^{G_r - G_s} for s <= r in
+  // 16x16 tiles (the diagonal ones by the makers, the ones below by the
+  // readers) and the keys scaled by e^{G[C-1] - G_s} (by the first row group
+  // of readers).  Below the diagonal the decay splits at the end e of the
+  // source tile, e^{G_r - G_e} e^{G_e - G_s}: both factors are at most one.
+  auto prefix = [&](int j) __attribute__((always_inline)) {
+    const char* st = stage_of(j);
+    float* gl = garr(j);
+    const float gscan = chunk_prefix<C>(reinterpret_cast<const float*>(st + lay.g), lane);
+    const float gsum = __shfl(gscan, C - 1, 64);
+    const float gend = __shfl(gscan, lane | 15, 64);
+    if (lane < C) {
+      gl[lane] = gscan;
+      gl[C + lane] = __expf(gsum - gscan);
+      gl[2 * C + lane] = __expf(gend - gscan);
+    }
+  };
+  // tile `item` of the causal tiles: the CT diagonal ones first, then the
+  // ones below the diagonal, o = rt (rt-1)/2 + ct for ct < rt
+  auto score_tile = [&](int j, int item) __attribute__((always_inline)) {
+    const char* st = stage_of(j);
+    const float* lraw = reinterpret_cast<const float*>(st + lay.lraw);
+    const float* gl = garr(j);
+    const float* es = gl + 2 * C;
+    char* pt = smem + lay.p + (j & 1) * PT::BYTES;
+    const bool diag = item < CT;
+    int rt = item, ct = item;
+    if (!diag) {
+      const int o = item - CT;
+      rt = 1;
+#pragma unroll
+      for (int u = 2; u < CT; ++u) rt += (o >= u * (u - 1) / 2) ? 1 : 0;
+      ct = o - rt * (rt - 1) / 2;
+    }
+    const int r = 16 * rt + q16;  // lane: row r, sources 16 ct + 4 (lane/16) .. + 3
+    const float* lr = lraw + r * LS;
+    Frag kf[KSD], qf[KSD];
+#pragma unroll
+    for (int s = 0; s < KSD; ++s) {
+      kf[s] = frag_row<T, C, D>(st + lay.k, 16 * ct + q16, s, g4);
+      qf[s] = frag_row<T, C, D>(st + lay.q, r, s, g4);
+    }
+    const float gr = gl[r];
+    f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x4 out;
+    if (diag) {
+      const f32x4 gs = *reinterpret_cast<const f32x4*>(gl + 16 * ct + 4 * g4);
+      float lam[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lam[e] = lr[32 - __clz(r ^ (16 * ct + 4 * g4 + e))];  // level of (r, s)
+#pragma unroll
+      for (int s = 0; s < KSD; ++s) x = M::mma(kf[s], qf[s], x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] = (T)((4 * g4 + e <= q16) ? x[e] * lam[e] * __expf(gr - gs[e]) : 0.f);
+    } else {
+      const f32x4 ess = *reinterpret_cast<const f32x4*>(es + 16 * ct + 4 * g4);
+      const float wrow = lr[4 + 32 - __clz(rt ^ ct)] * __expf(gr - gl[16 * ct + 15]);
+#pragma unroll
+      for (int s = 0; s < KSD; ++s) x = M::mma(kf[s], qf[s], x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] = (T)(x[e] * wrow * ess[e]);
+    }
+    *reinterpret_cast<bf16x4*>(pt + PT::off(r, 16 * ct + 4 * g4)) = out;
+  };
+  // decay-scaled keys: the same swizzled positions, each 16-byte piece of a
+  // row scaled by that row's weight; pieces x0, x0 + stride, ...
+  auto scaled_keys = [&](int j, int x0, int stride) __attribute__((always_inline)) {
+    const char* st = stage_of(j);
+    const float* wl = garr(j) + C;
+    char* kw = smem + lay.kw + (j & 1) * TL::BYTES;
+    for (int x = x0; x < TL::BYTES / 16; x += stride) {
+      const float w = wl[x / TL::NCH];
+      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(st + lay.k + x * 16);
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (T)((float)kv[e] * w);
+      *reinterpret_cast<bf16x8*>(kw + x * 16) = o;
+    }
+  };
+  constexpr int NBT = CT * (CT - 1) / 2;  // score tiles below the diagonal
+
+  if (wv >= NRW) {
+    // ------------------------------------------------------------ makers
+    const int mw = wv - NRW;  // column tile of the states this wave merges
+    // the diagonal score tiles of chunk j
+    auto prepare = [&](int j) __attribute__((always_inline)) {
+      prefix(j);
+#pragma unroll
+      for (int d = mw; d < CT; d += NMW) score_tile(j, d);
+#pragma unroll
+      for (int o = NCT + mw; o < NBT; o += 2 * NCT) score_tile(j, CT + o);
+    };
+
+    lds_barrier();  // the zeroed tiles are visible; the readers' first chunks landed
+    prepare(0);
+
+    // the within-block Fenwick states of this wave's 16 columns (levels
+    // 1..MAXB, fp32) and their log-scales
+    f32x4 nst[MAXB][DT];
+    float sig[MAXB + 1];
+    for (int t = 0; t < nsteps; ++t) {
+      const int j = t & (a.P - 1);
+      lds_barrier();  // step t prepared; the readers' loads of step t+1 landed
+      if (j == 0) {
+#pragma unroll
+        for (int m = 0; m < MAXB; ++m)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) nst[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m <= MAXB; ++m) sig[m] = 0.f;
+      }
+      // this chunk's decayed key-value state K_w^T V over the wave's columns
+      // (keys scaled by e^{G[C-1] - G_s}), merged by the Fenwick rule: levels
+      // 1..c and the chunk become level c+1, c = ctz(j+1)
+      const float gsum = garr(t)[C - 1];
+#pragma unroll
+      for (int m = 1; m <= MAXB; ++m) sig[m] += gsum;
+      if (j + 1 < a.P) {
+        const char* st = stage_of(t);
+        const char* kw = smem + lay.kw + (t & 1) * TL::BYTES;
+        Frag vf[KSC], kf[DT][KSC];
+#pragma unroll
+        for (int s = 0; s < KSC; ++s) vf[s] = frag_col<T, C, D>(st + lay.v, 16 * mw, s, lane);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int s = 0; s < KSC; ++s) kf[dt][s] = frag_col<T, C, D>(kw, 16 * dt, s, lane);
+        const int c = __ffs(j + 1) - 1;
+        f32x4 merged[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) merged[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 1; m <= MAXB; ++m) {
+          if (m <= c) {
+            const float sc = __expf(sig[m]);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) merged[dt] += sc * nst[m - 1][dt];
+          }
+        }
+        lds_wait(vf, kf);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int s = 0; s < KSC; ++s) merged[dt] = M::mma(kf[dt][s], vf[s], merged[dt]);
+#pragma unroll
+        for (int m = 1; m <= MAXB; ++m) {
+          if (m == c + 1) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) nst[m - 1][dt] = merged[dt];
+            sig[m] = 0.f;
+#pragma unroll
+            for (int s = 0; s < KSD; ++s) *reinterpret_cast<Frag*>(state_frag(m, mw, s)) = M::acc_frag(merged, s);
+          }
+        }
+      }
+      if (t + 1 < nsteps) prepare(t + 1);
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------- readers
+  const int wc = wv % NCT, wr = wv / NCT;
+  const int row_step = C * a.H;  // rows per chunk
+  // Steps are loaded, read out and stored in order, each by its own cursor
+  // over the items; a cursor moves on at the first chunk of every item after
+  // its first.
+  ItemWalk load_at, store_at, read_at;
+  load_at.start(item0, a, C);
+  store_at = load_at;
+  read_at = load_at;
+  auto row_in = [&](const ItemWalk& w, int t) { return w.row + (int64_t)((t & (a.P - 1)) * row_step); };
+  ChunkLoads<T, D, C, NRW> ld;
+  ld.init(wv, lane, a.H, a.L, LS);
+  // The loads of a step go out in three parts (q and gates, k and lambda, v),
+  // so that they can be spread between pieces of compute.
+  auto issue_part = [&](int j, int part) __attribute__((always_inline)) {
+    char* st = stage_of(j);
+    if (part == 0 && j > 0 && (j & (a.P - 1)) == 0) load_at.next(a, C);
+    const int64_t row0 = row_in(load_at, j);
+    if (part == 0) {
+      ld.tiles(a.q, row0, st + lay.q, wv);
+      ld.gates(a.g, row0, reinterpret_cast<float*>(st + lay.g), wv, lane);
+    } else if (part == 1) {
+      ld.tiles(a.k, row0, st + lay.k, wv);
+      ld.lambda(a.lam, row0, a.L, reinterpret_cast<float*>(st + lay.lraw), wv, lane);
+    } else {
+      ld.tiles(a.v, row0, st + lay.v, wv);
+    }
+  };
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    issue_part(j, 0);
+    issue_part(j, 1);
+    issue_part(j, 2);
+  };
+  issue(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  if (nsteps > 1) issue(1);
+  lds_barrier();  // step 0 has landed for every reader; the zeroed tiles are visible
+  // the first row group's share of preparing chunk j: the scaled keys and
+  // the score tiles below the diagonal that the makers do not take (the tiles
+  // below the diagonal alternate between the two in runs of NCT)
+  auto prepare = [&](int j) __attribute__((always_inline)) {
+    if (wv >= NCT) return;
+    prefix(j);
+#pragma unroll
+    for (int o = wv; o < NBT; o += 2 * NCT) score_tile(j, CT + o);
+    scaled_keys(j, tid, 64 * NCT);
+  };
+  prepare(0);
+
+  // The chunk loop, compiled once per row group so that every row-tile index
+  // in it is a constant.
+  auto run = [&](auto row_group) __attribute__((always_inline)) {
+    constexpr int WR = decltype(row_group)::value;
+    // Per item: the first MAXH Fenwick nodes of earlier blocks (most recent
+    // first) as A fragments of this wave's columns, with their level and
+    // decay offset; the log-scales of the within-block states.
+    Frag hn[MAXH > 0 ? MAXH : 1][KSD];
+    int hlv[MAXH > 0 ? MAXH : 1];
+    float hdd[MAXH > 0 ? MAXH : 1];
+    int rest_far = 0;  // set bits of J whose nodes are not held in registers
+    float dd_far = 0.f;
+    int bh = 0;
+    bool first_item = true;
+    float sig[MAXB + 1];
+    float gw = 0.f;  // log-decay from the start of block J to the current chunk
+    auto node_of = [&](int e) {
+      const float* f = a.F + ((int64_t)bh * a.nF + (e >> 1)) * D * D;
+      const float* s = a.S + ((int64_t)bh * a.nb + e) * D * D;
+      return (e & 1) ? f : s;
+    };
+    auto load_node = [&](Frag(&nf)[KSD], int e) __attribute__((always_inline)) {
+      node_frags<T, D>(nf, node_of(e), wc, lane);
+    };
+    auto gamma_of = [&](int e) {
+      const float* f = a.GF + (int64_t)bh * a.nF + (e >> 1);
+      const float* s = a.GS + (int64_t)bh * a.nb + e;
+      return *((e & 1) ? f : s);
+    };
+    auto start_item = [&]() __attribute__((always_inline)) {
+      if (!first_item) read_at.next(a, C);
+      first_item = false;
+      bh = read_at.bh(a);
+      // The held nodes: one per set bit of J, most recent first.  A slot past
+      // the last set bit repeats the first node and weighs nothing, so that
+      // every node and decay load goes out at once.
+      const int J = read_at.J;
+      int ex[MAXH > 0 ? MAXH : 1];
+      rest_far = J;
+#pragma unroll
+      for (int x = 0; x < MAXH; ++x) {
+        hlv[x] = rest_far > 0 ? LOGC + 1 + logP + __ffs(rest_far) - 1 : -1;  // token level of the node
+        ex[x] = rest_far > 0 ? rest_far - 1 : J - 1;
+        rest_far &= rest_far - 1;
+      }
+      dd_far = 0.f;
+#pragma unroll
+      for (int x = 0; x < MAXH; ++x) hdd[x] = 0.f;
+      if (MAXH > 0 && J > 0) {
+        float gm[MAXH > 0 ? MAXH : 1];
+#pragma unroll
+        for (int x = 0; x < MAXH; ++x) {
+          load_node(hn[x], ex[x]);
+          gm[x] = gamma_of(ex[x]);
+        }
+#pragma unroll
+        for (int x = 0; x < MAXH; ++x) {
+          hdd[x] = dd_far;
+          dd_far += hlv[x] >= 0 ? gm[x] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int m = 0; m <= MAXB; ++m) sig[m] = 0.f;
+      gw = 0.f;
+    };
+
+    // Output rows of a step leave during the following step.
+    bf16x4 ov[NRT];
+    auto store_out = [&](int jj) __attribute__((always_inline)) {
+      if (jj > 0 && (jj & (a.P - 1)) == 0) store_at.next(a, C);
+      const int64_t row0 = row_in(store_at, jj);
+#pragma unroll
+      for (int i = 0; i < NRT; ++i) {
+        const int r = 16 * W::row_tile(i, WR) + q16;  // lane: row r, columns 16 wc + 4 (lane/16) .. + 3
+        T* o = static_cast<T*>(a.o) + (row0 + (int64_t)r * a.H) * D + 16 * wc + 4 * g4;
+        *reinterpret_cast<bf16x4*>(o) = ov[i];
+      }
+    };
+
+    for (int t = 0; t < nsteps; ++t) {
+      const int j = t & (a.P - 1);    // chunk within the item's block
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of step t+1 and stores of step t-2 are done
+      lds_barrier();                  // step t prepared and step t+1 landed everywhere; step t-1 done
+      if (j == 0) start_item();       // node loads ahead of this step's other memory traffic
+      if (t > 0) store_out(t - 1);
+      if (t + 2 < nsteps) issue_part(t + 2, 0);
+
+      const char* st = stage_of(t);
+      const float* lraw = reinterpret_cast<const float*>(st + lay.lraw);
+      const float* gl = garr(t);
+      const float gsum = gl[C - 1];
+
+      // per row tile: Q fragments (index r, k = head dim), the row's lambda
+      // weights times e^{G_r} for every inter-chunk level this chunk reads
+      Frag qf[NRT][KSD];
+      const float* lr[NRT];
+      float egr[NRT], alw[NRT][MAXB], alh[NRT][MAXH > 0 ? MAXH : 1];
+#pragma unroll
+      for (int i = 0; i < NRT; ++i) {
+        const int r = 16 * W::row_tile(i, WR) + q16;
+#pragma unroll
+        for (int s = 0; s < KSD; ++s) qf[i][s] = frag_row<T, C, D>(st + lay.q, r, s, g4);
+        lr[i] = lraw + r * LS;
+        egr[i] = __expf(gl[r]);
+#pragma unroll
+        for (int m = 1; m <= MAXB; ++m) alw[i][m - 1] = lr[i][min(LOGC + m, LS - 1)] * egr[i];
+#pragma unroll
+        for (int x = 0; x < MAXH; ++x) alh[i][x] = lr[i][max(hlv[x], 0)] * egr[i];
+      }
+
+      // --- intra-chunk: O^T += V^T P^T
+      Frag vf[KSC];
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) vf[s] = frag_col<T, C, D>(st + lay.v, 16 * wc, s, lane);
+      const char* pt = smem + lay.p + (t & 1) * PT::BYTES;
+      Frag pf[NRT][KSC];
+#pragma unroll
+      for (int i = 0; i < NRT; ++i)
+#pragma unroll
+        for (int s = 0; s < KSC; ++s) pf[i][s] = frag_row<T, C, C>(pt, 16 * W::row_tile(i, WR) + q16, s, g4);
+      lds_wait(vf);
+      f32x4 oacc[NRT];
+#pragma unroll
+      for (int i = 0; i < NRT; ++i) {
+        oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KSC; ++s)
+          if (M::first_tile(s) <= W::row_tile(i, WR)) oacc[i] = M::mma(vf[s], pf[i][s], oacc[i]);
+      }
+
+      if (t + 2 < nsteps) {
+        issue_part(t + 2, 1);
+        issue_part(t + 2, 2);
+      }
+
+      // --- inter-chunk levels: O^T += diag(alpha) N^T Q^T, alpha_r = lambda_r^l e^{G_r} x scale.
+      // A level's product is weighted into O only when the next level comes
+      // (or at the end), so no level waits right away for its own products.
+      f32x4 pend[NRT];
+      float pal[NRT];
+#pragma unroll
+      for (int i = 0; i < NRT; ++i) {
+        pend[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        pal[i] = 0.f;
+      }
+      auto level_read = [&](const Frag(&nf)[KSD], const float(&al)[NRT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NRT; ++i) {
+          oacc[i] += pal[i] * pend[i];
+          pal[i] = al[i];
+          pend[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KSD; ++s) pend[i] = M::mma(nf[s], qf[i][s], pend[i]);
+        }
+      };
+      // within-block levels LOGC+1 .. LOGC+logP, from the makers' fragments
+#pragma unroll
+      for (int m = 1; m <= MAXB; ++m) {
+        if (m <= logP && ((j >> (m - 1)) & 1)) {
+          Frag nf[KSD];
+#pragma unroll
+          for (int s = 0; s < KSD; ++s) nf[s] = *reinterpret_cast<const Frag*>(state_frag(m, wc, s));
+          const float sc = __expf(sig[m]);
+          float al[NRT];
+#pragma unroll
+          for (int i = 0; i < NRT; ++i) al[i] = alw[i][m - 1] * sc;
+          level_read(nf, al);
+        }
+      }
+      // earlier blocks: one Fenwick node per set bit of J, most recent first
+#pragma unroll
+      for (int x = 0; x < MAXH; ++x) {
+        if (hlv[x] >= 0) {
+          const float sc = __expf(gw + hdd[x]);
+          float al[NRT];
+#pragma unroll
+          for (int i = 0; i < NRT; ++i) al[i] = alh[i][x] * sc;
+          level_read(hn[x], al);
+        }
+      }
+      {
+        int rest = rest_far;
+        float dd = dd_far;
+        while (rest > 0) {
+          const int e = rest - 1;
+          Frag nf[KSD];
+          load_node(nf, e);
+          const int lev = LOGC + 1 + logP + __ffs(rest) - 1;
+          const float sc = __expf(gw + dd);
+          float al[NRT];
+#pragma unroll
+          for (int i = 0; i < NRT; ++i) al[i] = lr[i][lev] * egr[i] * sc;
+          level_read(nf, al);
+          dd += gamma_of(e);
+          rest &= rest - 1;
+        }
+      }
+
+      // --- the output rows, stored during the next step
+#pragma unroll
+      for (int i = 0; i < NRT; ++i) {
+        oacc[i] += pal[i] * pend[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[i][e] = (T)oacc[i][e];
+      }
+
+      // the log-scales follow the makers' merge: every level decays by the
+      // chunk, the merged level c+1 starts afresh
+#pragma unroll
+      for (int m = 1; m <= MAXB; ++m) sig[m] += gsum;
+      gw += gsum;
+      if (j + 1 < a.P) {
+        const int c = __ffs(j + 1) - 1;
+#pragma unroll
+        for (int m = 1; m <= MAXB; ++m)
+          if (m == c + 1) sig[m] = 0.f;
+      }
+      if (t + 1 < nsteps) prepare(t + 1);
+    }
+    store_out(nsteps - 1);
+  };
+  if (wr == 0) {
+    run(std::integral_constant<int, 0>{});
+  } else {
+    run(std::integral_constant<int, 1>{});
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <typename T, int D, int C>
 static hipError_t launch_state_t(const PrefillArgs& a, hipStream_t s) {
   const int grid = a.B * a.H * a.nb;
   hipLaunchKernelGGL((ll_chunk_state<T, D, C>), dim3(grid), dim3(64 * (D / 16)), 0, s, a);
   return hipGetLastError();
 }
+
+// A persistent launch: as many workgroups as fit on the device at once, each
+// walking a run of consecutive (block, head) items.  Per kernel instance the
+// dynamic LDS allowed (above 64 KiB it must be raised explicitly) and the
+// number of workgroups that fit for that LDS size are kept under a lock
+// (calls may come from several threads).
+struct PersistentGrid {
+  std::mutex mu;
+  int configured = 0, slots = 0, slots_lds = -1;
+  hipError_t launch(const void* kern, int threads, int lds, const PrefillArgs& a, hipStream_t s) {
+    int grid_slots = 0;
+    {
+      std::lock_guard<std::mutex> lock(mu);
+      if (lds > configured) {
+        hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        configured = lds;
+      }
+      if (slots_lds != lds) {
+        int dev = 0, cus = 0, per_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds);
+        if (e != hipSuccess) return e;
+        slots = cus * (per_cu > 0 ? per_cu : 1);
+        slots_lds = lds;
+      }
+      grid_slots = slots;
+    }
+    const int items = a.B * a.H * a.nb;
+    const int grid = items < grid_slots ? items : grid_slots;
+    void* args[] = {const_cast<PrefillArgs*>(&a)};
+    hipError_t e = hipLaunchKernel(kern, dim3(grid), dim3(threads), args, lds, s);
+    return e != hipSuccess ? e : hipGetLastError();
+  }
+};
 
 template <typename T, int D, int C>
 static hipError_t launch_attn_t(const PrefillArgs& a, hipStream_t s) {
@@ -682,42 +1270,16 @@ static hipError_t launch_attn_t(const PrefillArgs& a, hipStream_t s) {
     // d = 128 the within-block nodes of 8-chunk blocks already fill the register budget, so
     // every earlier block's node is read from LDS (holding even one spills).
     constexpr int MAXH = (sizeof(T) == 2) ? (D <= 64 ? 5 : 0) : 0;
-    auto kern = ll_chunk_attn<T, D, C, max_block_depth(D), MAXH>;
-    const AttnLayout<T, D, C> lay(a.LS);
-    // Per kernel instance: the dynamic LDS allowed (above 64 KiB it must be
-    // raised explicitly) and the number of workgroups that fit the device at
-    // once for that LDS size, kept under a lock (calls may come from several
-    // threads).
-    static std::mutex mu;
-    static int configured = 0, slots = 0, slots_lds = -1;
-    int grid_slots = 0;
-    {
-      std::lock_guard<std::mutex> lock(mu);
-      if (lay.total > configured) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lay.total);
-        if (e != hipSuccess) return e;
-        configured = lay.total;
-      }
-      // persistent: as many workgroups as fit on the device at once, each
-      // walking a run of consecutive (block, head) items
-      if (slots_lds != lay.total) {
-        int dev = 0, cus = 0, per_cu = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e == hipSuccess)
-          e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
-                                                           64 * AttnWaves<D, C>::NW, lay.total);
-        if (e != hipSuccess) return e;
-        slots = cus * (per_cu > 0 ? per_cu : 1);
-        slots_lds = lay.total;
-      }
-      grid_slots = slots;
+    static PersistentGrid grid;
+    if constexpr (sizeof(T) == 2 && D <= 64 && C >= 32) {
+      auto kern = ll_chunk_attn_split<D, C, max_block_depth(D), MAXH>;
+      const SplitLayout<D, C, max_block_depth(D)> lay(a.LS);
+      return grid.launch(reinterpret_cast<const void*>(kern), 64 * SplitWaves<D, C>::NW, lay.total, a, s);
+    } else {
+      auto kern = ll_chunk_attn<T, D, C, max_block_depth(D), MAXH>;
+      const AttnLayout<T, D, C> lay(a.LS);
+      return grid.launch(reinterpret_cast<const void*>(kern), 64 * AttnWaves<D, C>::NW, lay.total, a, s);
     }
-    const int items = a.B * a.H * a.nb;
-    const int grid = items < grid_slots ? items : grid_slots;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * AttnWaves<D, C>::NW), lay.total, s, a);
-    return hipGetLastError();
   }
 }
 

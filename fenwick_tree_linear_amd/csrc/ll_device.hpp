@@ -298,27 +298,39 @@ struct ChunkLoads {
       lam_off[k] = (uint32_t)((r * H * L + (f - r * LS)) * 4);
     }
     gate_off = (uint32_t)(lane * H * 4);
+    h_ = H;
   }
-  __device__ __forceinline__ void tiles(const void* tensor, int64_t row0, char* lds, int wv) const {
-    const char* base = static_cast<const char*>(tensor) + row0 * D * (int64_t)sizeof(T);
+  // Every load goes through a buffer resource whose base is the chunk's first
+  // element, so the per-lane offsets above stay 32-bit registers and moving to
+  // another chunk is scalar work only.
+  int h_;
+  __device__ __forceinline__ void tiles_from(__amdgpu_buffer_rsrc_t rsrc, char* lds, int wv) const {
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
       const int i = wv + k * NW;
-      if (i < NINST) load_lds16(base + tile_off[k], lds + i * 1024);
+      if (i < NINST) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + i * 1024), 16, tile_off[k], 0, 0, 0);
     }
+  }
+  __device__ __forceinline__ void tiles(const void* tensor, int64_t row0, char* lds, int wv) const {
+    tiles_from(buffer_rsrc(static_cast<const char*>(tensor) + row0 * D * (int64_t)sizeof(T),
+                           (uint32_t)(((C - 1) * h_ + 1) * D * (int)sizeof(T))),
+               lds, wv);
   }
   __device__ __forceinline__ void gates(const float* g, int64_t row0, float* lds, int wv, int lane) const {
     if (wv == 0 && lane < C)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(g + row0) + gate_off, (lds_void*)lds, 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(g + row0, (uint32_t)(((C - 1) * h_ + 1) * 4)),
+                                               (lds_void*)lds, 4, gate_off, 0, 0, 0);
   }
-  __device__ __forceinline__ void lambda(const float* lam, int64_t row0, int L, float* lds, int wv, int lane) const {
-    const char* base = reinterpret_cast<const char*>(lam + row0 * L);
+  __device__ __forceinline__ void lambda_from(__amdgpu_buffer_rsrc_t rsrc, float* lds, int wv, int lane) const {
 #pragma unroll
     for (int k = 0; k < LPW; ++k) {
       const int first = (wv + k * NW) * 64;
       if (first < lam_n && first + lane < lam_n)
-        __builtin_amdgcn_global_load_lds(base + lam_off[k], (lds_void*)(lds + first), 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + first), 4, lam_off[k], 0, 0, 0);
     }
+  }
+  __device__ __forceinline__ void lambda(const float* lam, int64_t row0, int L, float* lds, int wv, int lane) const {
+    lambda_from(buffer_rsrc(lam + row0 * L, (uint32_t)(((C - 1) * h_ * L + lam_n / C) * 4)), lds, wv, lane);
   }
 };
 
