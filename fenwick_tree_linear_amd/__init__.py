@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     LLProblem,
     attn_bwd,
     attn_fwd,
+    attn_fwd_lambda_mlp,
     ccq_query,
     decode_state_tensor,
     lambda_mlp,
@@ -24,6 +25,8 @@ from .binding import (  # noqa: F401
     ll_attn_bwd_workspace_bytes,
     ll_attn_fwd,
     ll_attn_fwd_from_state,
+    ll_attn_fwd_lambda_mlp,
+    ll_attn_fwd_lambda_mlp_workspace_bytes,
     ll_attn_fwd_noalloc,
     ll_attn_fwd_workspace_bytes,
     ll_ccq_query,

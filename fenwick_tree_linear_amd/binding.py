@@ -73,9 +73,12 @@ def load_library() -> ctypes.CDLL:
     lib.ll_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(LLProblem), ctypes.POINTER(sz)]
     lib.ll_attn_bwd.argtypes = [ctypes.POINTER(LLProblem)] + [P] * 13 + [sz, P]
     lib.ll_decode_step_ragged.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
+    lib.ll_attn_fwd_lambda_mlp_workspace_bytes.argtypes = [ctypes.POINTER(LLProblem), i32, ctypes.POINTER(sz)]
+    lib.ll_attn_fwd_lambda_mlp.argtypes = [ctypes.POINTER(LLProblem), P, P, P, P, P, i32, P, P, P, P, P, P, P, sz, P]
     for fn in ("ll_attn_fwd_workspace_bytes", "ll_attn_fwd", "ll_decode_state_bytes", "ll_decode_step",
                "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp", "ll_attn_fwd_noalloc", "ll_decode_step_ragged", "ll_attn_fwd_from_state",
-               "ll_ccq_query_workspace_bytes", "ll_ccq_query", "ll_attn_bwd_workspace_bytes", "ll_attn_bwd"):
+               "ll_ccq_query_workspace_bytes", "ll_ccq_query", "ll_attn_bwd_workspace_bytes", "ll_attn_bwd",
+               "ll_attn_fwd_lambda_mlp_workspace_bytes", "ll_attn_fwd_lambda_mlp"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -221,6 +224,31 @@ def ll_attn_fwd_from_state(problem: LLProblem, pos0: int, state_in, q, k, v, log
                                                  workspace_bytes, _stream(stream)))
 
 
+def ll_attn_fwd_lambda_mlp_workspace_bytes(problem: LLProblem, hidden: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().ll_attn_fwd_lambda_mlp_workspace_bytes(None if problem is None else ctypes.byref(problem),
+                                                                 hidden, ctypes.byref(out)))
+    return out.value
+
+
+def ll_attn_fwd_lambda_mlp(problem: LLProblem, q, k, v, log_gate, d, hidden: int, w1, w2, bias, beta, o, state_out,
+                           workspace, workspace_bytes: int, stream=None) -> None:
+    p = problem
+    f32 = torch.float32
+    specs = []
+    if p:
+        specs = [s for s in _prefill_specs(p, q, k, v, log_gate, d, beta, o) if s[0] != "lambda"]
+        specs += [("d", d, p.B * p.T * p.H * p.L, f32), ("w1", w1, p.L * hidden, f32),
+                  ("w2", w2, hidden * p.L, f32), ("bias", bias, p.L, f32)]
+        if state_out is not None:
+            specs.append(("state_out", state_out, _state_elems(p.B, p.H, p.dk, p.dv, p.L), f32))
+    _validate(*specs, _workspace_spec(workspace, workspace_bytes))
+    _check(load_library().ll_attn_fwd_lambda_mlp(None if problem is None else ctypes.byref(problem), _ptr(q), _ptr(k),
+                                                 _ptr(v), _ptr(log_gate), _ptr(d), hidden, _ptr(w1), _ptr(w2),
+                                                 _ptr(bias), _ptr(beta), _ptr(o), _ptr(state_out), _ptr(workspace),
+                                                 workspace_bytes, _stream(stream)))
+
+
 def ll_decode_state_bytes(B: int, H: int, dk: int, dv: int, L: int) -> int:
     out = ctypes.c_size_t(0)
     _check(load_library().ll_decode_state_bytes(B, H, dk, dv, L, ctypes.byref(out)))
@@ -363,6 +391,27 @@ def lambda_mlp(d, w1, w2, bias, out=None, stream=None):
     lam = out if out is not None else torch.empty_like(d)
     ll_lambda_mlp(d.numel() // L, L, hidden, d, w1, w2, bias, lam, stream)
     return lam
+
+
+def attn_fwd_lambda_mlp(q, k, v, log_gate, d, w1, w2, bias, beta=None, C: int = 64, rule: int = LL_MAMBA2,
+                        want_state: bool = False, workspace=None, out=None, stream=None):
+    """The prefill with level weights softplus((d W1) W2 + b) made by the read
+    (``ll_attn_fwd_lambda_mlp``); returns ``o`` (and the exported state when
+    ``want_state``)."""
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    L, hidden = d.shape[-1], w1.shape[1]
+    prob = LLProblem(B, T, H, dk, dv, L, C, io_code(k.dtype), rule)
+    nbytes = ll_attn_fwd_lambda_mlp_workspace_bytes(prob, hidden)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
+    o = out if out is not None else torch.empty(B, T, H, dv, dtype=v.dtype, device=v.device)
+    st = None
+    if want_state:
+        st = torch.empty(ll_decode_state_bytes(B, H, dk, dv, L) // 4, dtype=torch.float32, device=k.device)
+    ll_attn_fwd_lambda_mlp(prob, q, k, v, log_gate, d, hidden, w1, w2, bias, beta, o, st, workspace,
+                           workspace.numel(), stream)
+    return (o, st) if want_state else o
 
 
 def ccq_query(q, k, w, b, out=None, workspace=None, stream=None):

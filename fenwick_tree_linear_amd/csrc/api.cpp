@@ -375,9 +375,15 @@ hipError_t pad_state(const void* src, int dks, int dvs, void* dst, int dkd, int 
 }
 
 // The launch sequence of a validated prefill in its run shape.
+// The level-weight MLP that the read runs itself (lambda then holds its input d).
+struct ReadMlp {
+  int hidden;
+  const float *w1, *w2, *bias;
+};
+
 ll_status run_core(const Plan& pl, int64_t pos0, const float* state_in, const void* q, const void* k, const void* v,
                    const float* log_gate, const float* lambda, const float* beta, void* o, void* state_out,
-                   void* workspace, hipStream_t stream, bool reuse_states) {
+                   void* workspace, hipStream_t stream, bool reuse_states, const ReadMlp* mlp = nullptr) {
   char* ws = static_cast<char*>(workspace);
   const ll_problem* p = &pl.r;
   PrefillArgs a;
@@ -404,6 +410,12 @@ ll_status run_core(const Plan& pl, int64_t pos0, const float* state_in, const vo
   a.state = static_cast<float*>(state_out);
   a.state_in = pos0 > 0 ? state_in : nullptr;
   a.pos0 = pos0;
+  if (mlp) {
+    a.w1 = mlp->w1;
+    a.w2 = mlp->w2;
+    a.mlp_bias = mlp->bias;
+    a.hidden = mlp->hidden;
+  }
   const int io = p->io == LL_BF16 ? 1 : 0;
   const int D = p->dk;
 
@@ -452,7 +464,7 @@ ll_status run_core(const Plan& pl, int64_t pos0, const float* state_in, const vo
 ll_status run_prefill(const ll_problem* p, int64_t pos0, const float* state_in, const void* q, const void* k,
                       const void* v, const float* log_gate, const float* lambda, const float* beta, void* o,
                       void* state_out, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                      bool reuse_states = false, bool noalloc = false) {
+                      bool reuse_states = false, bool noalloc = false, const ReadMlp* mlp = nullptr) {
   Plan pl;
   ll_status st = plan_prefill(p, state_out != nullptr, &pl);
   if (st != LL_OK) return st;
@@ -539,7 +551,7 @@ ll_status run_prefill(const ll_problem* p, int64_t pos0, const float* state_in, 
   }
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
 
-  st = run_core(pl, pos0, sr, qr, kr, vr, gr, lr, br, or_, sor, workspace, stream, reuse_states);
+  st = run_core(pl, pos0, sr, qr, kr, vr, gr, lr, br, or_, sor, workspace, stream, reuse_states, mlp);
   if (st != LL_OK) return st;
 
   // the outputs in the caller's shape
@@ -659,6 +671,66 @@ ll_status ll_lambda_mlp(int64_t rows, int L, int hidden, const float* d, const f
                        [&] { return llattn::launch_lambda_mlp(rows, L, hidden, d, w1, w2, bias, lambda, stream); });
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+namespace {
+
+// The prefill with its level weights from the MLP: whether the read makes
+// them itself, and the workspace (the prefill's, plus the weights when a
+// separate ll_lambda_mlp launch makes them).
+struct MlpPlan {
+  bool fused;
+  size_t lam_off, bytes;
+};
+
+ll_status plan_mlp_prefill(const ll_problem* p, int hidden, bool want_state, MlpPlan* mp) {
+  if (!p) return fail(LL_ERR_NULL, "problem is NULL");
+  if (hidden < 1) return fail(LL_ERR_SHAPE, "hidden=%d must be >= 1", hidden);
+  if (hidden > 64 || p->L > 32)
+    return fail(LL_ERR_UNSUPPORTED, "L=%d, hidden=%d: at most 32 levels and 64 hidden units are supported", p->L,
+                hidden);
+  Plan pl;
+  ll_status st = plan_prefill(p, want_state, &pl);
+  if (st != LL_OK) return st;
+  mp->fused = llattn::read_runs_mlp(pl.r.io == LL_BF16 ? 1 : 0, pl.r.dk, pl.Cr, p->L, hidden);
+  mp->lam_off = (pl.bytes + 255) & ~(size_t)255;
+  mp->bytes = mp->fused ? pl.bytes : mp->lam_off + (size_t)p->B * p->T * p->H * p->L * sizeof(float);
+  return LL_OK;
+}
+
+}  // namespace
+
+ll_status ll_attn_fwd_lambda_mlp_workspace_bytes(const ll_problem* p, int hidden, size_t* bytes) {
+  if (!bytes) return fail(LL_ERR_NULL, "bytes is NULL");
+  MlpPlan mp;
+  ll_status st = plan_mlp_prefill(p, hidden, false, &mp);  // the workspace does not depend on exporting
+  if (st != LL_OK) return st;
+  *bytes = mp.bytes;
+  return ok();
+}
+
+ll_status ll_attn_fwd_lambda_mlp(const ll_problem* p, const void* q, const void* k, const void* v,
+                                 const float* log_gate, const float* d, int hidden, const float* w1, const float* w2,
+                                 const float* bias, const float* beta, void* o, void* state_out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  MlpPlan mp;
+  ll_status st = plan_mlp_prefill(p, hidden, state_out != nullptr, &mp);
+  if (st != LL_OK) return st;
+  if (!o) return fail(LL_ERR_NULL, "o must not be NULL: the level weights only serve the read");
+  if (!d || !w1 || !w2 || !bias) return fail(LL_ERR_NULL, "d, w1, w2 and bias must not be NULL");
+  if (workspace_bytes < mp.bytes)
+    return fail(LL_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, mp.bytes);
+  if (mp.bytes > 0 && !workspace) return fail(LL_ERR_WORKSPACE, "workspace is NULL");
+  if (mp.fused) {
+    const ReadMlp mlp{hidden, w1, w2, bias};
+    return run_prefill(p, 0, nullptr, q, k, v, log_gate, d, beta, o, state_out, workspace, workspace_bytes, stream,
+                       false, false, &mlp);
+  }
+  // a read that does not run the MLP: the weights first, into the workspace
+  float* lam = reinterpret_cast<float*>(static_cast<char*>(workspace) + mp.lam_off);
+  st = ll_lambda_mlp((int64_t)p->B * p->T * p->H, p->L, hidden, d, w1, w2, bias, lam, stream);
+  if (st != LL_OK) return st;
+  return run_prefill(p, 0, nullptr, q, k, v, log_gate, lam, beta, o, state_out, workspace, mp.lam_off, stream);
 }
 
 namespace {

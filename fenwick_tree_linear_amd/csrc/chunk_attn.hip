@@ -683,6 +683,14 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
   }
 }
 
+// Waits until at most N of this wave's vector memory operations are
+// outstanding (they complete in issue order); the other counters are left.
+template <int N>
+__device__ __forceinline__ void wait_vmem_at_most() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ---------------------------------------------------------------------------
 // ll_chunk_attn_split: the same read for bf16 with two row groups, with the
 // work of a step divided by role instead of repeated per row group.
@@ -720,9 +728,13 @@ struct SplitLayout {
   static constexpr int NS = 3;
   static constexpr int FRAG_BYTES = 64 * 16;                           // one bf16 fragment of a wave
   static constexpr int STATE_BYTES = MAXB * (D / 16) * (D / 32) * FRAG_BYTES;
+  // with the level-weight MLP: its weights, zero-padded to 16 levels x 32
+  // hidden ([16][32] W1, [32][16] W2, [16] bias), and a ring of three chunks
+  // of its input [C][16] (levels past L unset)
+  static constexpr int MLP_W_BYTES = (16 * 32 + 32 * 16 + 16) * 4;
   int q, k, v, g, lraw, stage;
-  int p, kw, gw, st, total;
-  __host__ __device__ explicit SplitLayout(int LS) {
+  int p, kw, gw, st, mw, dr, total;
+  __host__ __device__ explicit SplitLayout(int LS, int mlp_levels = 0) {
     q = 0;
     k = q + TL::BYTES;
     v = k + TL::BYTES;
@@ -734,10 +746,15 @@ struct SplitLayout {
     gw = kw + 2 * TL::BYTES;
     st = (gw + 2 * 3 * C * 4 + 255) & ~255;
     total = st + STATE_BYTES;
+    mw = dr = total;
+    if (mlp_levels > 0) {
+      dr = mw + MLP_W_BYTES;
+      total = dr + 3 * C * 16 * 4;
+    }
   }
 };
 
-template <int D, int C, int MAXB, int MAXH>
+template <int D, int C, int MAXB, int MAXH, bool MLP>
 __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_split(PrefillArgs a) {
   typedef bf16 T;
   using M = Mma<T>;
@@ -755,7 +772,7 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int LS = a.LS;
-  const Lay lay(LS);
+  const Lay lay(LS, MLP ? a.L : 0);
   // the wave index is a scalar, so that every branch on it is a uniform jump
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, q16 = lane & 15;
@@ -860,6 +877,84 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
   };
   constexpr int NBT = CT * (CT - 1) / 2;  // score tiles below the diagonal
 
+  // The level-weight MLP of chunk j ("Adaptive memory decay for log-linear
+  // attention", section "Method", LambdaMLPSoftplus), 16 rows at a time, with
+  // the products, their order and the softplus of ll_lambda_mlp: layer 1
+  // transposed, h^T (hidden x rows) = W1^T d^T, so that a lane ends up holding
+  // its row of h in the k order of layer 2, z (rows x levels) = h W2, then
+  // lambda = softplus(z + b) into the chunk's level-weight rows.  The second
+  // row group of readers runs it (row tile rt by reader rt mod NCT of the
+  // group), at the end of their step; the makers load its input.
+  // The weights as MFMA fragments of this lane (zero in the padding): layer 1
+  // A = W1^T, step s of hidden tile n gives W1[4s + g][16n + c]; layer 2
+  // B = W2, step s gives W2[kidx(s, g)][c]; then the bias of level c.
+  struct MlpFrags {
+    float a1[2][4], b2[8], b;
+  };
+  auto mlp_frags = [&]() __attribute__((always_inline)) {
+    typedef Mma<float> MF;
+    const float* w = reinterpret_cast<const float*>(smem + lay.mw);
+    MlpFrags f;
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) f.a1[n][s] = w[(4 * s + g4) * 32 + 16 * n + q16];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) f.b2[s] = w[16 * 32 + MF::kidx(s, g4, 0) * 16 + q16];
+    f.b = w[16 * 32 + 32 * 16 + q16];
+    return f;
+  };
+  auto mlp_tile = [&](const MlpFrags& f, int j, int rt) __attribute__((always_inline)) {
+    typedef Mma<float> MF;
+    const float* drow = reinterpret_cast<const float*>(smem + lay.dr) + (j % 3) * C * 16 + (16 * rt + q16) * 16 + g4;
+    // (levels past L read the zeros the ring holds there)
+    float bd[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) bd[s] = drow[4 * s];
+    f32x4 h[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) h[n] = MF::mma(f.a1[n][s], bd[s], h[n]);
+    f32x4 zz[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) zz[s & 1] = MF::mma(MF::acc_frag(h, s), f.b2[s], zz[s & 1]);
+    const f32x4 z = zz[0] + zz[1];
+    float* lr = reinterpret_cast<float*>(stage_of(j) + lay.lraw);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (q16 < LS) lr[(16 * rt + 4 * g4 + i) * LS + q16] = softplus_f32(z[i] + f.b);
+  };
+  auto mlp_share = [&](int j) __attribute__((always_inline)) {
+    if (!MLP || wv < NCT || wv >= NRW) return;
+    const MlpFrags f = mlp_frags();  // read for each use: registers are scarce across the step
+#pragma unroll
+    for (int rt = 0; rt < CT; ++rt)
+      if (rt % NCT == wv - NCT) mlp_tile(f, j, rt);
+  };
+  if constexpr (MLP) {
+    // the levels past L of the input ring: zero, and never loaded
+    float* dring = reinterpret_cast<float*>(smem + lay.dr);
+    for (int x = tid; x < 3 * C * 16; x += 64 * NW)
+      if ((x & 15) >= a.L) dring[x] = 0.f;
+    // the MLP's weights into LDS, zero-padded
+    float* w = reinterpret_cast<float*>(smem + lay.mw);
+    for (int x = tid; x < 16 * 32 + 32 * 16 + 16; x += 64 * NW) {
+      float val = 0.f;
+      if (x < 16 * 32) {
+        const int k = x / 32, n = x % 32;
+        if (k < a.L && n < a.hidden) val = a.w1[k * a.hidden + n];
+      } else if (x < 16 * 32 + 32 * 16) {
+        const int k = (x - 16 * 32) / 16, n = (x - 16 * 32) % 16;
+        if (k < a.hidden && n < a.L) val = a.w2[k * a.L + n];
+      } else {
+        const int n = x - 16 * 32 - 32 * 16;
+        if (n < a.L) val = a.mlp_bias[n];
+      }
+      w[x] = val;
+    }
+  }
+
   if (wv >= NRW) {
     // ------------------------------------------------------------ makers
     const int mw = wv - NRW;  // column tile of the states this wave merges
@@ -872,7 +967,40 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
       for (int o = NCT + mw; o < NBT; o += 2 * NCT) score_tile(j, CT + o);
     };
 
+    // with the MLP: its input rows, four chunks ahead into a ring of three
+    // (chunk j in slot j % 3), loaded by the makers straight into LDS, 16
+    // levels a row: instruction u of maker mw takes rows 4 (mw + u NMW) ..
+    // + 3, lane l row + l / 16, level l % 16 (levels past L are not loaded).
+    // Chunk j is used at the end of step j - 2; its loads may stay in flight
+    // across the barrier of step j - 3.
+    ItemWalk dload_at;
+    dload_at.start(item0, a, C);
+    const uint32_t d_off = (uint32_t)(((mw * 4 + (lane >> 4)) * a.H * a.L + (lane & 15)) * 4);
+    const int d_step = NMW * 4 * a.H * a.L * 4;  // bytes between the rows of consecutive instructions
+    const uint32_t d_extent = (uint32_t)(((C - 1) * a.H * a.L + a.L) * 4);
+    auto load_d = [&](__amdgpu_buffer_rsrc_t r, char* lds) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < C * 16 / (64 * NMW); ++u)
+        if ((lane & 15) < a.L)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + (mw + u * NMW) * 256), 4, d_off, u * d_step, 0, 0);
+    };
+    auto issue_d = [&](int j) __attribute__((always_inline)) {
+      if (j > 0 && (j & (a.P - 1)) == 0) dload_at.next(a, C);
+      const float* rows = a.lam + (dload_at.row + (int64_t)((j & (a.P - 1)) * C * a.H)) * a.L;
+      load_d(buffer_rsrc(rows, d_extent), smem + lay.dr + (j % 3) * C * 16 * 4);
+    };
+    constexpr int ND = C * 16 / (64 * NMW);  // input loads of a chunk, per maker
+    if constexpr (MLP) {
+      issue_d(0);
+      if (nsteps > 1) issue_d(1);
+      __builtin_amdgcn_s_waitcnt(0);
+    }
     lds_barrier();  // the zeroed tiles are visible; the readers' first chunks landed
+    if constexpr (MLP) {
+      lds_barrier();  // the readers made the level weights of chunks 0 and 1
+      if (nsteps > 2) issue_d(2);
+      if (nsteps > 3) issue_d(3);
+    }
     prepare(0);
 
     // the within-block Fenwick states of this wave's 16 columns (levels
@@ -881,7 +1009,18 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
     float sig[MAXB + 1];
     for (int t = 0; t < nsteps; ++t) {
       const int j = t & (a.P - 1);
+      if constexpr (MLP) {
+        // this wave's input rows of chunk t+2 landed (those of t+3 may not have)
+        if (t + 3 < nsteps) {
+          wait_vmem_at_most<ND>();
+        } else {
+          __builtin_amdgcn_s_waitcnt(0);
+        }
+      }
       lds_barrier();  // step t prepared; the readers' loads of step t+1 landed
+      if constexpr (MLP) {
+        if (t + 4 < nsteps) issue_d(t + 4);
+      }
       if (j == 0) {
 #pragma unroll
         for (int m = 0; m < MAXB; ++m)
@@ -963,7 +1102,7 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
       ld.gates(a.g, row0, reinterpret_cast<float*>(st + lay.g), wv, lane);
     } else if (part == 1) {
       ld.tiles(a.k, row0, st + lay.k, wv);
-      ld.lambda(a.lam, row0, a.L, reinterpret_cast<float*>(st + lay.lraw), wv, lane);
+      if constexpr (!MLP) ld.lambda(a.lam, row0, a.L, reinterpret_cast<float*>(st + lay.lraw), wv, lane);
     } else {
       ld.tiles(a.v, row0, st + lay.v, wv);
     }
@@ -977,6 +1116,11 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
   __builtin_amdgcn_s_waitcnt(0);
   if (nsteps > 1) issue(1);
   lds_barrier();  // step 0 has landed for every reader; the zeroed tiles are visible
+  if constexpr (MLP) {
+    mlp_share(0);
+    if (nsteps > 1) mlp_share(1);
+    lds_barrier();  // the level weights of chunks 0 and 1 are made
+  }
   // the first row group's share of preparing chunk j: the scaled keys and
   // the score tiles below the diagonal that the makers do not take (the tiles
   // below the diagonal alternate between the two in runs of NCT)
@@ -1207,6 +1351,7 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
           if (m == c + 1) sig[m] = 0.f;
       }
       if (t + 1 < nsteps) prepare(t + 1);
+      if (t + 2 < nsteps) mlp_share(t + 2);
     }
     store_out(nsteps - 1);
   };
@@ -1272,10 +1417,18 @@ static hipError_t launch_attn_t(const PrefillArgs& a, hipStream_t s) {
     constexpr int MAXH = (sizeof(T) == 2) ? (D <= 64 ? 5 : 0) : 0;
     static PersistentGrid grid;
     if constexpr (sizeof(T) == 2 && D <= 64 && C >= 32) {
-      auto kern = ll_chunk_attn_split<D, C, max_block_depth(D), MAXH>;
+      if (a.w1) {
+        static PersistentGrid grid_mlp;
+        if (a.L > 16 || a.hidden < 1 || a.hidden > 32) return hipErrorInvalidValue;  // checked before launch
+        auto kern = ll_chunk_attn_split<D, C, max_block_depth(D), MAXH, true>;
+        const SplitLayout<D, C, max_block_depth(D)> lay(a.LS, a.L);
+        return grid_mlp.launch(reinterpret_cast<const void*>(kern), 64 * SplitWaves<D, C>::NW, lay.total, a, s);
+      }
+      auto kern = ll_chunk_attn_split<D, C, max_block_depth(D), MAXH, false>;
       const SplitLayout<D, C, max_block_depth(D)> lay(a.LS);
       return grid.launch(reinterpret_cast<const void*>(kern), 64 * SplitWaves<D, C>::NW, lay.total, a, s);
     } else {
+      if (a.w1) return hipErrorInvalidValue;  // the MLP runs inside the bf16 d <= 64 read only
       auto kern = ll_chunk_attn<T, D, C, max_block_depth(D), MAXH>;
       const AttnLayout<T, D, C> lay(a.LS);
       return grid.launch(reinterpret_cast<const void*>(kern), 64 * AttnWaves<D, C>::NW, lay.total, a, s);

@@ -12,7 +12,8 @@
 //   layer 1, transposed: h^T tile (16 hidden x 16 rows) = W1^T d^T, so that
 //     lane l ends up holding row l%16 of h at hidden indices 4(l/16)+i --
 //     exactly the k operand layout of layer 2 (no trip through LDS);
-//   layer 2: z tile (16 rows x 16 levels) = h W2, then + b and softplus.
+//   layer 2: z tile (16 rows x 16 levels) = h W2 (even and odd k steps in two
+//     accumulators, then summed), then + b and softplus.
 // W1 and W2 are loaded once per wave into fragment registers (zero where the
 // padding lies).
 #include "ll_device.hpp"
@@ -22,10 +23,6 @@ namespace llattn {
 
 constexpr int kMlpWaves = 4;  // waves (of 64 rows each) per workgroup
 
-// softplus(z) = log(1 + e^z), as max(z, 0) + log(1 + e^-|z|) so that large |z|
-// neither overflows nor cancels; rounding 1 + x (x in (0, 1]) to fp32 costs at
-// most 2^-24 in absolute terms, far below the weights' own size
-__device__ __forceinline__ float softplus_f32(float z) { return fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z))); }
 
 // LT = ceil(L / 16) level tiles, HT = ceil(hidden / 16) hidden tiles
 template <int LT, int HT>
@@ -105,13 +102,15 @@ __global__ void __launch_bounds__(64 * kMlpWaves) ll_lambda_mlp(int64_t rows, in
 #pragma unroll
       for (int n = 0; n < HT; ++n) h[n] = M::mma(a1[n][s], bd, h[n]);
     }
-    // layer 2: z (rows x levels) = h W2; lane l holds h[16rt + c][16n + 4g + i]
+    // layer 2: z (rows x levels) = h W2; lane l holds h[16rt + c][16n + 4g + i].
+    // The even and odd k steps go to two accumulators, summed at the end
+    // (two dependent chains of half the length).
 #pragma unroll
     for (int lt = 0; lt < LT; ++lt) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int s = 0; s < 4 * HT; ++s) acc = M::mma(M::acc_frag(h, s), b2[lt][s], acc);
-      z[rt][lt] = acc;
+      for (int s = 0; s < 4 * HT; ++s) acc[s & 1] = M::mma(M::acc_frag(h, s), b2[lt][s], acc[s & 1]);
+      z[rt][lt] = acc[0] + acc[1];
     }
   }
   __builtin_amdgcn_wave_barrier();  // the staged rows are read before they are overwritten

@@ -104,6 +104,11 @@ __device__ __forceinline__ float chunk_scan(float x) {
   return x;
 }
 
+// softplus(z) = log(1 + e^z), as max(z, 0) + log(1 + e^-|z|) so that large |z|
+// neither overflows nor cancels; rounding 1 + x (x in (0, 1]) to fp32 costs at
+// most 2^-24 in absolute terms, far below the weights' own size
+__device__ __forceinline__ float softplus_f32(float z) { return fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z))); }
+
 // ---------------------------------------------------------------- XCD order
 // Workgroup ids are dealt round-robin to the 8 XCDs of the chip; each XCD
 // has its own L2.  Renumber so that consecutive logical ids (the blocks of

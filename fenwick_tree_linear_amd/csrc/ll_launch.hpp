@@ -37,6 +37,13 @@ struct PrefillArgs {
   // segment in the decode layout, and the segment's first position (0: none)
   const float* state_in;
   int64_t pos0;
+  // The level-weight MLP run inside the read (ll_chunk_attn_split only): when
+  // w1 is set, lam holds the MLP's input d [B,T,H,L] instead of the weights,
+  // and the read makes lambda = softplus((d W1) W2 + b) per chunk.
+  const float* w1 = nullptr;  // [L, hidden]
+  const float* w2 = nullptr;  // [hidden, L]
+  const float* mlp_bias = nullptr;  // [L]
+  int hidden = 0;
 };
 
 struct DecodeArgs {
@@ -109,6 +116,11 @@ struct BwdWork {
 // io: 0 = fp32, 1 = bf16.  Each returns hipSuccess or the launch error.
 hipError_t launch_block_state(int io, int D, int C, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_chunk_attn(int io, int D, int C, const PrefillArgs& a, hipStream_t s);
+// Whether the read runs the level-weight MLP itself (PrefillArgs::w1): bf16 in
+// the run shape, square head D <= 64, chunk C >= 32, L <= 16, hidden <= 32.
+inline bool read_runs_mlp(int io, int D, int C, int L, int hidden) {
+  return io == 1 && D <= 64 && C >= 32 && L <= 16 && hidden >= 1 && hidden <= 32;
+}
 hipError_t launch_fenwick_scan(int D, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_state_export(int D, int C, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prior_read(int io, int D, int C, const PrefillArgs& a, hipStream_t s);

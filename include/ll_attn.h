@@ -230,6 +230,31 @@ ll_status ll_lambda_mlp(int64_t rows, int L, int hidden, const float* d, const f
                         const float* bias, float* lambda, hipStream_t stream);
 
 /*
+ * The chunk-parallel prefill with its level weights from the adaptive-decay
+ * MLP ("Adaptive memory decay for log-linear attention", section "Method",
+ * LambdaMLPSoftplus, and its "Complexity": the MLP acts on the O(log T) level
+ * axis of each token): ll_attn_fwd with lambda = softplus((d W1) W2 + b)
+ * taken from ll_lambda_mlp's arguments instead of a lambda tensor.
+ *   d [B,T,H,L] fp32, the per-level representation of each token and head
+ *   hidden, w1 [L, hidden], w2 [hidden, L], bias [L]: as ll_lambda_mlp
+ *   every other argument as ll_attn_fwd (o must not be NULL)
+ * For bf16 problems whose run shape has a head of at most 64 and chunks of at
+ * least 32, with L <= 16 and hidden <= 32, the read makes the weights of each
+ * chunk itself (fp32 matrix cores, the same products and order as
+ * ll_lambda_mlp) and never writes them to memory; otherwise ll_lambda_mlp
+ * writes them into the workspace first.  Either way the result is the same
+ * as ll_lambda_mlp followed by ll_attn_fwd.
+ * Workspace: ll_attn_fwd_lambda_mlp_workspace_bytes (the prefill's, plus
+ * B*T*H*L floats when the weights go through memory).  Errors as ll_attn_fwd
+ * and ll_lambda_mlp.
+ */
+ll_status ll_attn_fwd_lambda_mlp_workspace_bytes(const ll_problem* p, int hidden, size_t* bytes);
+ll_status ll_attn_fwd_lambda_mlp(const ll_problem* p, const void* q, const void* k, const void* v,
+                                 const float* log_gate, const float* d, int hidden, const float* w1, const float* w2,
+                                 const float* bias, const float* beta, void* o, void* state_out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The decode step for a batch whose sequences sit at different positions
  * (section 2.3, "inference", one token per sequence), for continuous batching:
  * as ll_decode_step, with

@@ -24,7 +24,9 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["ll_attn_bwd", "ll_attn_bwd_workspace_bytes", "ll_attn_fwd", "ll_attn_fwd_from_state", "ll_attn_fwd_noalloc", "ll_attn_fwd_workspace_bytes", "ll_ccq_query",
+        ["ll_attn_bwd", "ll_attn_bwd_workspace_bytes", "ll_attn_fwd", "ll_attn_fwd_from_state",
+         "ll_attn_fwd_lambda_mlp", "ll_attn_fwd_lambda_mlp_workspace_bytes", "ll_attn_fwd_noalloc",
+         "ll_attn_fwd_workspace_bytes", "ll_ccq_query",
          "ll_ccq_query_workspace_bytes", "ll_decode_state_bytes", "ll_decode_step", "ll_decode_step_ragged",
          "ll_kernel_timing_enable", "ll_kernel_timing_read", "ll_lambda_mlp", "ll_last_error"])
 
@@ -195,6 +197,42 @@ def test_lambda_mlp_validation_before_any_launch():
     for kw, name in cases:
         a = dict(good, **kw)
         st, msg = status_of(F.ll_lambda_mlp, *(a[k] for k in order), 0)
+        assert st == name, (kw, msg)
+
+
+def test_fused_mlp_prefill_workspace():
+    """The read makes the level weights itself for bf16 with a run head <= 64, run chunks >= 32,
+    L <= 16 and hidden <= 32: the workspace is then the prefill's.  Otherwise the weights of
+    every row go through the workspace after it (256-byte aligned)."""
+    for kw, hidden in [(dict(), 30), (dict(T=2048, L=12, dk=32, dv=16, C=16), 24)]:
+        p = prob(**kw)
+        assert F.ll_attn_fwd_lambda_mlp_workspace_bytes(p, hidden) == F.ll_attn_fwd_workspace_bytes(p)
+    for kw, hidden in [(dict(), 33), (dict(T=2048, L=17), 30), (dict(T=2048, L=12, io=F.LL_F32, C=32), 24),
+                       (dict(T=2048, L=12, dk=128, dv=128, C=32), 24)]:
+        p = prob(**kw)
+        base = (F.ll_attn_fwd_workspace_bytes(p) + 255) // 256 * 256
+        assert F.ll_attn_fwd_lambda_mlp_workspace_bytes(p, hidden) == base + p.B * p.T * p.H * p.L * 4, (kw, hidden)
+
+
+def test_fused_mlp_prefill_validation_before_any_launch():
+    D = DUMMY
+    p = prob(T=2048, L=12)
+    n = F.ll_attn_fwd_lambda_mlp_workspace_bytes(p, 24)
+    good = dict(p=p, q=D, k=D, v=D, g=D, d=D, hidden=24, w1=D, w2=D, bias=D, beta=None, o=D, st=None, ws=D, n=n)
+    cases = [
+        (dict(hidden=0), "LL_ERR_SHAPE"),
+        (dict(hidden=65), "LL_ERR_UNSUPPORTED"),
+        (dict(p=prob(T=2048, L=33)), "LL_ERR_UNSUPPORTED"),
+        (dict(o=None), "LL_ERR_NULL"),
+        (dict(d=None), "LL_ERR_NULL"),
+        (dict(w2=None), "LL_ERR_NULL"),
+        (dict(n=n - 1), "LL_ERR_WORKSPACE"),
+        (dict(p=prob(T=2048, L=12, C=48)), "LL_ERR_SHAPE"),
+    ]
+    order = ("p", "q", "k", "v", "g", "d", "hidden", "w1", "w2", "bias", "beta", "o", "st", "ws", "n")
+    for kw, name in cases:
+        a = dict(good, **kw)
+        st, msg = status_of(F.ll_attn_fwd_lambda_mlp, *(a[x] for x in order), 0)
         assert st == name, (kw, msg)
 
 
