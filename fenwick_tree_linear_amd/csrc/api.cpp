@@ -86,7 +86,7 @@ int run_chunk(int c, int D, ll_dtype io, ll_rule rule) {
   return c;
 }
 
-constexpr int kMaxBlockChunks = 8;  // P <= 2^max_block_depth
+constexpr int kMaxBlockChunks = 16;  // P <= 2^read_block_depth (or the depth a caller asks for)
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -105,7 +105,7 @@ struct Plan {
 // Validates a prefill problem and derives the run problem, the block
 // decomposition and the workspace.  The workspace does not depend on
 // `exporting` (which only adds checks).
-ll_status plan_prefill(const ll_problem* p, bool exporting, Plan* out) {
+ll_status plan_prefill(const ll_problem* p, bool exporting, Plan* out, int depth = -1) {
   if (!p) return fail(LL_ERR_NULL, "problem is NULL");
   const int io_v = enum_value(p->io), rule_v = enum_value(p->rule);
   if (io_v != LL_F32 && io_v != LL_BF16) return fail(LL_ERR_DTYPE, "unknown io dtype %d", io_v);
@@ -157,7 +157,7 @@ ll_status plan_prefill(const ll_problem* p, bool exporting, Plan* out) {
     return fail(LL_ERR_UNSUPPORTED, "problem too large for one launch");
 
   const int nc = r.T / Cr;
-  const int depth_cap = 1 << llattn::max_block_depth(D);
+  const int depth_cap = 1 << (depth >= 0 ? depth : llattn::read_block_depth(r.io == LL_BF16 ? 1 : 0, D, Cr));
   int P = nc & -nc;  // lowest set bit: blocks tile the chunks exactly
   if (P > kMaxBlockChunks) P = kMaxBlockChunks;
   if (P > depth_cap) P = depth_cap;
@@ -466,7 +466,8 @@ ll_status run_prefill(const ll_problem* p, int64_t pos0, const float* state_in, 
                       void* state_out, void* workspace, size_t workspace_bytes, hipStream_t stream,
                       bool reuse_states = false, bool noalloc = false, const ReadMlp* mlp = nullptr) {
   Plan pl;
-  ll_status st = plan_prefill(p, state_out != nullptr, &pl);
+  // the read that runs the MLP keeps blocks of at most 2^max_block_depth chunks
+  ll_status st = plan_prefill(p, state_out != nullptr, &pl, mlp ? llattn::max_block_depth(p ? p->dk : 0) : -1);
   if (st != LL_OK) return st;
   if (reuse_states && (p->rule != LL_MAMBA2 || pos0 != 0 || state_out || pl.pad_qk || pl.pad_v))
     return fail(LL_ERR_UNSUPPORTED, "reusing block states is only for a plain Mamba-2 read in the run shape");
@@ -689,10 +690,16 @@ ll_status plan_mlp_prefill(const ll_problem* p, int hidden, bool want_state, Mlp
   if (hidden > 64 || p->L > 32)
     return fail(LL_ERR_UNSUPPORTED, "L=%d, hidden=%d: at most 32 levels and 64 hidden units are supported", p->L,
                 hidden);
+  // planned as the read that runs the MLP (blocks of at most 2^max_block_depth
+  // chunks); a read that cannot runs the plain prefill after ll_lambda_mlp
   Plan pl;
-  ll_status st = plan_prefill(p, want_state, &pl);
+  ll_status st = plan_prefill(p, want_state, &pl, llattn::max_block_depth(p->dk));
   if (st != LL_OK) return st;
   mp->fused = llattn::read_runs_mlp(pl.r.io == LL_BF16 ? 1 : 0, pl.r.dk, pl.Cr, p->L, hidden);
+  if (!mp->fused) {
+    st = plan_prefill(p, want_state, &pl);
+    if (st != LL_OK) return st;
+  }
   mp->lam_off = (pl.bytes + 255) & ~(size_t)255;
   mp->bytes = mp->fused ? pl.bytes : mp->lam_off + (size_t)p->B * p->T * p->H * p->L * sizeof(float);
   return LL_OK;
@@ -846,7 +853,9 @@ struct BwdPlan {
 
 ll_status plan_bwd(const ll_problem* p, BwdPlan* out) {
   Plan pl;
-  ll_status st = plan_prefill(p, false, &pl);
+  // the backward's walks keep up to 2^max_block_depth chunks a block
+  const int depth = llattn::max_block_depth(p ? p->dk : 0);
+  ll_status st = plan_prefill(p, false, &pl, depth);
   if (st != LL_OK) return st;
   // fp32 runs 32-token chunks where 64 are asked for: the gradients do not
   // depend on the chunk size, and the walks' fp32 fragments of 64 tokens do not
@@ -854,7 +863,7 @@ ll_status plan_bwd(const ll_problem* p, BwdPlan* out) {
   if (p->io == LL_F32 && pl.r.C == 64) {
     ll_problem q = *p;
     q.C = 32;
-    st = plan_prefill(&q, false, &pl);
+    st = plan_prefill(&q, false, &pl, depth);
     if (st != LL_OK) return st;
   }
   if (p->rule != LL_MAMBA2) return fail(LL_ERR_UNSUPPORTED, "the backward pass is implemented for the Mamba-2 write");

@@ -1038,13 +1038,16 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
       if (j + 1 < a.P) {
         const char* st = stage_of(t);
         const char* kw = smem + lay.kw + (t & 1) * TL::BYTES;
-        Frag vf[KSC], kf[DT][KSC];
+        // the keys' fragments in groups of DG state row tiles, so that few
+        // registers hold them at once
+        constexpr int DG = DT >= 4 ? 2 : DT;
+        Frag vf[KSC], kf[DG][KSC];
 #pragma unroll
         for (int s = 0; s < KSC; ++s) vf[s] = frag_col<T, C, D>(st + lay.v, 16 * mw, s, lane);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        for (int u = 0; u < DG; ++u)
 #pragma unroll
-          for (int s = 0; s < KSC; ++s) kf[dt][s] = frag_col<T, C, D>(kw, 16 * dt, s, lane);
+          for (int s = 0; s < KSC; ++s) kf[u][s] = frag_col<T, C, D>(kw, 16 * u, s, lane);
         const int c = __ffs(j + 1) - 1;
         f32x4 merged[DT];
 #pragma unroll
@@ -1057,11 +1060,20 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
             for (int dt = 0; dt < DT; ++dt) merged[dt] += sc * nst[m - 1][dt];
           }
         }
-        lds_wait(vf, kf);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        for (int d0 = 0; d0 < DT; d0 += DG) {
+          lds_wait(vf, kf);
 #pragma unroll
-          for (int s = 0; s < KSC; ++s) merged[dt] = M::mma(kf[dt][s], vf[s], merged[dt]);
+          for (int u = 0; u < DG; ++u)
+#pragma unroll
+            for (int s = 0; s < KSC; ++s) merged[d0 + u] = M::mma(kf[u][s], vf[s], merged[d0 + u]);
+          if (d0 + DG < DT) {
+#pragma unroll
+            for (int u = 0; u < DG; ++u)
+#pragma unroll
+              for (int s = 0; s < KSC; ++s) kf[u][s] = frag_col<T, C, D>(kw, 16 * (d0 + DG + u), s, lane);
+          }
+        }
 #pragma unroll
         for (int m = 1; m <= MAXB; ++m) {
           if (m == c + 1) {
@@ -1416,19 +1428,26 @@ static hipError_t launch_attn_t(const PrefillArgs& a, hipStream_t s) {
     // every earlier block's node is read from LDS (holding even one spills).
     constexpr int MAXH = (sizeof(T) == 2) ? (D <= 64 ? 5 : 0) : 0;
     static PersistentGrid grid;
-    if constexpr (sizeof(T) == 2 && D <= 64 && C >= 32) {
+    if constexpr (read_split(sizeof(T) == 2 ? 1 : 0, D, C)) {
+      constexpr int MAXB = read_block_depth(1, D, C);
       if (a.w1) {
+        // with the MLP's ring and weights, four within-block levels do not fit
+        // LDS beside three staged chunks: blocks of at most 8 chunks
+        constexpr int MAXB_MLP = max_block_depth(D);
         static PersistentGrid grid_mlp;
+        if (a.P > (1 << MAXB_MLP)) return hipErrorInvalidValue;  // planned within the depth
         if (a.L > 16 || a.hidden < 1 || a.hidden > 32) return hipErrorInvalidValue;  // checked before launch
-        auto kern = ll_chunk_attn_split<D, C, max_block_depth(D), MAXH, true>;
-        const SplitLayout<D, C, max_block_depth(D)> lay(a.LS, a.L);
+        auto kern = ll_chunk_attn_split<D, C, MAXB_MLP, MAXH, true>;
+        const SplitLayout<D, C, MAXB_MLP> lay(a.LS, a.L);
         return grid_mlp.launch(reinterpret_cast<const void*>(kern), 64 * SplitWaves<D, C>::NW, lay.total, a, s);
       }
-      auto kern = ll_chunk_attn_split<D, C, max_block_depth(D), MAXH, false>;
-      const SplitLayout<D, C, max_block_depth(D)> lay(a.LS);
+      if (a.P > (1 << MAXB)) return hipErrorInvalidValue;  // planned within the depth
+      auto kern = ll_chunk_attn_split<D, C, MAXB, MAXH, false>;
+      const SplitLayout<D, C, MAXB> lay(a.LS);
       return grid.launch(reinterpret_cast<const void*>(kern), 64 * SplitWaves<D, C>::NW, lay.total, a, s);
     } else {
       if (a.w1) return hipErrorInvalidValue;  // the MLP runs inside the bf16 d <= 64 read only
+      if (a.P > (1 << max_block_depth(D))) return hipErrorInvalidValue;  // planned within the depth
       auto kern = ll_chunk_attn<T, D, C, max_block_depth(D), MAXH>;
       const AttnLayout<T, D, C> lay(a.LS);
       return grid.launch(reinterpret_cast<const void*>(kern), 64 * AttnWaves<D, C>::NW, lay.total, a, s);

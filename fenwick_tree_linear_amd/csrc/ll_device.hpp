@@ -285,7 +285,7 @@ struct ChunkLoads {
   static constexpr int TPW = (NINST + NW - 1) / NW;                        // tile instructions per wave
   static constexpr int LPW = (C * kLevelsMax + 64 * NW - 1) / (64 * NW);   // lambda instructions per wave, at most
   static_assert(TL::BYTES % 1024 == 0 && 1024 % TL::RB == 0, "tile must be whole 1 KiB instructions");
-  uint32_t tile_off[TPW], lam_off[LPW], gate_off;
+  uint32_t tile_off[TPW], lam_off[LPW];
   int lam_n;  // lambda floats per chunk, C * LS
 
   __device__ __forceinline__ void init(int wv, int lane, int H, int L, int LS) {
@@ -302,7 +302,6 @@ struct ChunkLoads {
       const int f = (wv + k * NW) * 64 + lane, r = f / LS;
       lam_off[k] = (uint32_t)((r * H * L + (f - r * LS)) * 4);
     }
-    gate_off = (uint32_t)(lane * H * 4);
     h_ = H;
   }
   // Every load goes through a buffer resource whose base is the chunk's first
@@ -322,9 +321,14 @@ struct ChunkLoads {
                lds, wv);
   }
   __device__ __forceinline__ void gates(const float* g, int64_t row0, float* lds, int wv, int lane) const {
-    if (wv == 0 && lane < C)
+    if (wv == 0 && lane < C) {
+      // the offset is formed here each time (an opaque copy of the lane keeps the
+      // compiler from hoisting it into a register held, or spilled, across a loop)
+      int l = lane;
+      asm volatile("" : "+v"(l));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(g + row0, (uint32_t)(((C - 1) * h_ + 1) * 4)),
-                                               (lds_void*)lds, 4, gate_off, 0, 0, 0);
+                                               (lds_void*)lds, 4, (uint32_t)(l * h_ * 4), 0, 0, 0);
+    }
   }
   __device__ __forceinline__ void lambda_from(__amdgpu_buffer_rsrc_t rsrc, float* lds, int wv, int lane) const {
 #pragma unroll

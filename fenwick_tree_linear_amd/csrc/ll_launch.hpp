@@ -116,11 +116,6 @@ struct BwdWork {
 // io: 0 = fp32, 1 = bf16.  Each returns hipSuccess or the launch error.
 hipError_t launch_block_state(int io, int D, int C, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_chunk_attn(int io, int D, int C, const PrefillArgs& a, hipStream_t s);
-// Whether the read runs the level-weight MLP itself (PrefillArgs::w1): bf16 in
-// the run shape, square head D <= 64, chunk C >= 32, L <= 16, hidden <= 32.
-inline bool read_runs_mlp(int io, int D, int C, int L, int hidden) {
-  return io == 1 && D <= 64 && C >= 32 && L <= 16 && hidden >= 1 && hidden <= 32;
-}
 hipError_t launch_fenwick_scan(int D, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_state_export(int D, int C, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prior_read(int io, int D, int C, const PrefillArgs& a, hipStream_t s);
@@ -154,6 +149,17 @@ inline int ilog2_host(int x) {
 
 // largest within-block Fenwick depth the chunk kernels hold in registers
 constexpr int max_block_depth(int /*D*/) { return 3; }
+// The reader/maker read (bf16, square head D <= 64, chunks of at least 32)
+// keeps four within-block levels, so its blocks hold up to 16 chunks; every
+// other read, that read when it runs the level-weight MLP, and the backward
+// up to 2^max_block_depth.
+constexpr bool read_split(int io, int D, int C) { return io == 1 && D <= 64 && C >= 32; }
+constexpr int read_block_depth(int io, int D, int C) { return read_split(io, D, C) ? 4 : max_block_depth(D); }
+// Whether the read runs the level-weight MLP itself (PrefillArgs::w1): bf16 in
+// the run shape, square head D <= 64, chunk C >= 32, L <= 16, hidden <= 32.
+inline bool read_runs_mlp(int io, int D, int C, int L, int hidden) {
+  return read_split(io, D, C) && L <= 16 && hidden >= 1 && hidden <= 32;
+}
 
 // Whether the backward walks keep their chunk-level states in LDS (else in
 // BwdWork::scratch).

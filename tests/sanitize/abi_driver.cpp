@@ -44,7 +44,7 @@ int main() {
   // passes validation; the stubbed launch fails
   expect(ll_attn_fwd(&p, d, d, d, f, f, nullptr, d, nullptr, d, bytes, nullptr), LL_ERR_HIP, "stubbed launch");
   ll_problem big = p;
-  big.B = 8;
+  big.B = 16;  // 16 x 16 heads x 16384 tokens: 100 MB of block states and nodes
   expect(ll_attn_fwd_noalloc(&big, d, d, d, f, f, nullptr, d, nullptr, nullptr), LL_ERR_WORKSPACE,
          "noalloc beyond the scratch");
   expect(ll_attn_fwd_from_state(&p, 3, f, d, d, d, f, f, nullptr, d, nullptr, d, bytes, nullptr), LL_ERR_POSITION,

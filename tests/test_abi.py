@@ -52,10 +52,11 @@ def status_of(fn, *args):
 
 
 def test_workspace_bytes_for_the_16k_prefill():
-    # 32 heads x 32 blocks of 8 chunks: 1024 block states + 512 Fenwick nodes
-    # of 64x64 fp32, plus their gate sums
+    # 32 heads x 16 blocks of 16 chunks (the bf16 d <= 64 read keeps four
+    # within-block levels): 512 block states + 256 Fenwick nodes of 64x64 fp32,
+    # plus their gate sums
     n = F.ll_attn_fwd_workspace_bytes(prob())
-    assert 1536 * 64 * 64 * 4 <= n <= 1536 * 64 * 64 * 4 + 4 * 4096 + 4 * 256
+    assert 768 * 64 * 64 * 4 <= n <= 768 * 64 * 64 * 4 + 4 * 4096 + 4 * 256
     assert n % 256 == 0
     # at d = 128 (bf16) the read takes the nodes from a bf16 copy of all of them:
     # 32 heads x 32 blocks of 8 chunks of 32 -> 1024 states, 512 nodes, 1024 copies
@@ -202,11 +203,16 @@ def test_lambda_mlp_validation_before_any_launch():
 
 def test_fused_mlp_prefill_workspace():
     """The read makes the level weights itself for bf16 with a run head <= 64, run chunks >= 32,
-    L <= 16 and hidden <= 32: the workspace is then the prefill's.  Otherwise the weights of
-    every row go through the workspace after it (256-byte aligned)."""
+    L <= 16 and hidden <= 32: the workspace is then a prefill's with blocks of at most 8 chunks
+    (that read keeps three within-block levels), no room for the weights.  Otherwise the weights
+    of every row go through the workspace after the plain prefill's (256-byte aligned)."""
     for kw, hidden in [(dict(), 30), (dict(T=2048, L=12, dk=32, dv=16, C=16), 24)]:
         p = prob(**kw)
-        assert F.ll_attn_fwd_lambda_mlp_workspace_bytes(p, hidden) == F.ll_attn_fwd_workspace_bytes(p)
+        n, plain = F.ll_attn_fwd_lambda_mlp_workspace_bytes(p, hidden), F.ll_attn_fwd_workspace_bytes(p)
+        assert plain <= n < plain + p.B * p.T * p.H * p.L * 4, (kw, n, plain)
+    # the 16K prefill: 32 heads x 32 blocks of 8 chunks, 1024 states + 512 nodes of 64 x 64 fp32
+    n = F.ll_attn_fwd_lambda_mlp_workspace_bytes(prob(), 30)
+    assert 1536 * 64 * 64 * 4 <= n <= 1536 * 64 * 64 * 4 + 4 * 4096 + 4 * 256
     for kw, hidden in [(dict(), 33), (dict(T=2048, L=17), 30), (dict(T=2048, L=12, io=F.LL_F32, C=32), 24),
                        (dict(T=2048, L=12, dk=128, dv=128, C=32), 24)]:
         p = prob(**kw)
@@ -306,11 +312,14 @@ def test_bwd_validation_before_any_launch():
     # reverse bucket states (4 blocks of 8 chunks per head: 2 block levels) and 3
     # chunk-level states per block, all fp32 64 x 64
     def need(T, L, nb, nbl):
-        # the forward's workspace, two fp32 values per row, the reverse bucket states (one
-        # fp32 64 x 64 state per block and block level) and one fp32 sum per block; at
+        # the block states and Fenwick nodes of (v, k) in blocks of 8 chunks (the backward's
+        # walks keep three chunk levels), two fp32 values per row, the reverse bucket states
+        # (one fp32 64 x 64 state per block and block level) and one fp32 sum per block; at
         # d = 64 the chunk-level states live in LDS
         rows, heads, state = 2 * T * 16, 2 * 16, 64 * 64 * 4
-        return F.ll_attn_fwd_workspace_bytes(prob(T=T, L=L)) + 2 * rows * 4 + heads * nb * nbl * state + heads * nb * 4
+        a256 = lambda x: (x + 255) // 256 * 256
+        fwd = a256(heads * nb * state) + a256(heads * nb * 4) + a256(heads * (nb // 2) * state) + a256(heads * max(nb // 2, 1) * 4)
+        return fwd + 2 * rows * 4 + heads * nb * nbl * state + heads * nb * 4
 
     assert need(2048, 12, 4, 2) <= n <= need(2048, 12, 4, 2) + 6 * 256  # 4 blocks of 8 chunks: 2 block levels
     m = F.ll_attn_bwd_workspace_bytes(prob(T=4096, L=13))  # 8 blocks: 3 block levels
@@ -334,7 +343,7 @@ def test_noalloc_validation_before_any_launch():
     problem whose workspace exceeds its 64 MiB scratch before touching the GPU."""
     d = DUMMY
     args = (d, d, d, d, d, None, d, None)
-    big = prob(B=8)  # 8 x 16 heads x 16384 tokens: 100 MB of block states and nodes
+    big = prob(B=16)  # 16 x 16 heads x 16384 tokens: 100 MB of block states and nodes
     assert F.ll_attn_fwd_workspace_bytes(prob()) <= 64 << 20
     assert F.ll_attn_fwd_workspace_bytes(big) > 64 << 20
     name, msg = status_of(F.ll_attn_fwd_noalloc, big, *args)
