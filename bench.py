@@ -698,9 +698,8 @@ def main() -> int:
     token_heads = w.B * w.T * w.H
     alg_bytes = algorithmic_bytes_per_token_head(w) * token_heads
     # ll_fenwick_scan: the block states it must read and the level >= 1 nodes it writes
-    # (blocks of 8 chunks: 32 per head, 16 nodes; 64 x 64 fp32 each)
-    nb = w.T // (w.C * 8)
-    scan_bytes = w.B * w.H * (nb + nb // 2) * w.dk * w.dv * 4
+    # (64 x 64 fp32 each): the workspace holds exactly those and their gate sums
+    scan_bytes = F.ll_attn_fwd_workspace_bytes(prob)
     t_scan = kt["ll_fenwick_scan"][0] / kt["ll_fenwick_scan"][1] * 1e-3
     scan = {"bytes": scan_bytes, "us": round(t_scan * 1e6, 2), "achieved_GBs": round(scan_bytes / t_scan / 1e9, 1),
             "frac": round(scan_bytes / t_scan / 1e9 / HBM_PEAK_GBS, 4)}

@@ -87,6 +87,9 @@ int run_chunk(int c, int D, ll_dtype io, ll_rule rule) {
 }
 
 constexpr int kMaxBlockChunks = 16;  // P <= 2^read_block_depth (or the depth a caller asks for)
+// Blocks per prefill below which blocks of 16 chunks would leave CUs of the
+// persistent read idle (the MI355X has 256): then blocks of 8.
+constexpr int64_t kReadBlocksMin = 256;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -161,6 +164,8 @@ ll_status plan_prefill(const ll_problem* p, bool exporting, Plan* out, int depth
   int P = nc & -nc;  // lowest set bit: blocks tile the chunks exactly
   if (P > kMaxBlockChunks) P = kMaxBlockChunks;
   if (P > depth_cap) P = depth_cap;
+  // blocks of more than 8 chunks only while they leave every CU a block to read
+  while (P > 8 && (int64_t)p->B * p->H * (nc / P) < kReadBlocksMin) P /= 2;
   Plan pl;
   pl.r = r;
   pl.Cr = Cr;
