@@ -1093,12 +1093,12 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
   // -------------------------------------------------------------- readers
   const int wc = wv % NCT, wr = wv / NCT;
   const int row_step = C * a.H;  // rows per chunk
-  // Steps are loaded, read out and stored in order, each by its own cursor
-  // over the items; a cursor moves on at the first chunk of every item after
-  // its first.
-  ItemWalk load_at, store_at, read_at;
+  // Steps are loaded and read out in order, each by its own cursor over the
+  // items; a cursor moves on at the first chunk of every item after its
+  // first.  A step's output rows leave during the next step, at the row the
+  // read cursor gave.
+  ItemWalk load_at, read_at;
   load_at.start(item0, a, C);
-  store_at = load_at;
   read_at = load_at;
   auto row_in = [&](const ItemWalk& w, int t) { return w.row + (int64_t)((t & (a.P - 1)) * row_step); };
   ChunkLoads<T, D, C, NRW> ld;
@@ -1151,16 +1151,20 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
     constexpr int WR = decltype(row_group)::value;
     // Per item: the first MAXH Fenwick nodes of earlier blocks (most recent
     // first) as A fragments of this wave's columns, with their level and
-    // decay offset; the log-scales of the within-block states.
+    // decay from their end to the start of block J (as a factor); the decay
+    // factors of the within-block states.  Decays of whole chunks are kept as
+    // running products of the chunks' e^{gate sum}.
     Frag hn[MAXH > 0 ? MAXH : 1][KSD];
-    int hlv[MAXH > 0 ? MAXH : 1];
-    float hdd[MAXH > 0 ? MAXH : 1];
+    int hlp = 0;  // the held nodes' token levels, five bits each (0: no node)
+    float ehd[MAXH > 0 ? MAXH : 1];
+    static_assert(MAXH * 5 <= 32 && kLevelsMax <= 32, "held levels packed in one word");
+    auto held_level = [&](int x) { return (hlp >> (5 * x)) & 31; };
     int rest_far = 0;  // set bits of J whose nodes are not held in registers
     float dd_far = 0.f;
     int bh = 0;
     bool first_item = true;
-    float sig[MAXB + 1];
-    float gw = 0.f;  // log-decay from the start of block J to the current chunk
+    float esig[MAXB + 1];
+    float egw = 1.f;  // decay from the start of block J to the current chunk
     auto node_of = [&](int e) {
       const float* f = a.F + ((int64_t)bh * a.nF + (e >> 1)) * D * D;
       const float* s = a.S + ((int64_t)bh * a.nb + e) * D * D;
@@ -1184,15 +1188,16 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
       const int J = read_at.J;
       int ex[MAXH > 0 ? MAXH : 1];
       rest_far = J;
+      hlp = 0;
 #pragma unroll
       for (int x = 0; x < MAXH; ++x) {
-        hlv[x] = rest_far > 0 ? LOGC + 1 + logP + __ffs(rest_far) - 1 : -1;  // token level of the node
+        if (rest_far > 0) hlp |= (LOGC + 1 + logP + __ffs(rest_far) - 1) << (5 * x);  // token level of the node
         ex[x] = rest_far > 0 ? rest_far - 1 : J - 1;
         rest_far &= rest_far - 1;
       }
       dd_far = 0.f;
 #pragma unroll
-      for (int x = 0; x < MAXH; ++x) hdd[x] = 0.f;
+      for (int x = 0; x < MAXH; ++x) ehd[x] = 1.f;
       if (MAXH > 0 && J > 0) {
         float gm[MAXH > 0 ? MAXH : 1];
 #pragma unroll
@@ -1202,20 +1207,20 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
         }
 #pragma unroll
         for (int x = 0; x < MAXH; ++x) {
-          hdd[x] = dd_far;
-          dd_far += hlv[x] >= 0 ? gm[x] : 0.f;
+          ehd[x] = __expf(dd_far);
+          dd_far += held_level(x) ? gm[x] : 0.f;
         }
       }
 #pragma unroll
-      for (int m = 0; m <= MAXB; ++m) sig[m] = 0.f;
-      gw = 0.f;
+      for (int m = 0; m <= MAXB; ++m) esig[m] = 1.f;
+      egw = 1.f;
     };
 
     // Output rows of a step leave during the following step.
     bf16x4 ov[NRT];
-    auto store_out = [&](int jj) __attribute__((always_inline)) {
-      if (jj > 0 && (jj & (a.P - 1)) == 0) store_at.next(a, C);
-      const int64_t row0 = row_in(store_at, jj);
+    int64_t out_row = 0;
+    auto store_out = [&]() __attribute__((always_inline)) {
+      const int64_t row0 = out_row;
 #pragma unroll
       for (int i = 0; i < NRT; ++i) {
         const int r = 16 * W::row_tile(i, WR) + q16;  // lane: row r, columns 16 wc + 4 (lane/16) .. + 3
@@ -1229,7 +1234,7 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
       __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of step t+1 and stores of step t-2 are done
       lds_barrier();                  // step t prepared and step t+1 landed everywhere; step t-1 done
       if (j == 0) start_item();       // node loads ahead of this step's other memory traffic
-      if (t > 0) store_out(t - 1);
+      if (t > 0) store_out();
       if (t + 2 < nsteps) issue_part(t + 2, 0);
 
       const char* st = stage_of(t);
@@ -1252,7 +1257,7 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
 #pragma unroll
         for (int m = 1; m <= MAXB; ++m) alw[i][m - 1] = lr[i][min(LOGC + m, LS - 1)] * egr[i];
 #pragma unroll
-        for (int x = 0; x < MAXH; ++x) alh[i][x] = lr[i][max(hlv[x], 0)] * egr[i];
+        for (int x = 0; x < MAXH; ++x) alh[i][x] = lr[i][held_level(x)] * egr[i];
       }
 
       // --- intra-chunk: O^T += V^T P^T
@@ -1307,7 +1312,7 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
           Frag nf[KSD];
 #pragma unroll
           for (int s = 0; s < KSD; ++s) nf[s] = *reinterpret_cast<const Frag*>(state_frag(m, wc, s));
-          const float sc = __expf(sig[m]);
+          const float sc = esig[m];
           float al[NRT];
 #pragma unroll
           for (int i = 0; i < NRT; ++i) al[i] = alw[i][m - 1] * sc;
@@ -1317,8 +1322,8 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
       // earlier blocks: one Fenwick node per set bit of J, most recent first
 #pragma unroll
       for (int x = 0; x < MAXH; ++x) {
-        if (hlv[x] >= 0) {
-          const float sc = __expf(gw + hdd[x]);
+        if (held_level(x)) {
+          const float sc = egw * ehd[x];
           float al[NRT];
 #pragma unroll
           for (int i = 0; i < NRT; ++i) al[i] = alh[i][x] * sc;
@@ -1333,7 +1338,7 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
           Frag nf[KSD];
           load_node(nf, e);
           const int lev = LOGC + 1 + logP + __ffs(rest) - 1;
-          const float sc = __expf(gw + dd);
+          const float sc = egw * __expf(dd);
           float al[NRT];
 #pragma unroll
           for (int i = 0; i < NRT; ++i) al[i] = lr[i][lev] * egr[i] * sc;
@@ -1344,6 +1349,7 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
       }
 
       // --- the output rows, stored during the next step
+      out_row = row_in(read_at, t);
 #pragma unroll
       for (int i = 0; i < NRT; ++i) {
         oacc[i] += pal[i] * pend[i];
@@ -1351,21 +1357,22 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
         for (int e = 0; e < 4; ++e) ov[i][e] = (T)oacc[i][e];
       }
 
-      // the log-scales follow the makers' merge: every level decays by the
+      // the decay factors follow the makers' merge: every level decays by the
       // chunk, the merged level c+1 starts afresh
+      const float egs = __expf(gsum);
 #pragma unroll
-      for (int m = 1; m <= MAXB; ++m) sig[m] += gsum;
-      gw += gsum;
+      for (int m = 1; m <= MAXB; ++m) esig[m] *= egs;
+      egw *= egs;
       if (j + 1 < a.P) {
         const int c = __ffs(j + 1) - 1;
 #pragma unroll
         for (int m = 1; m <= MAXB; ++m)
-          if (m == c + 1) sig[m] = 0.f;
+          if (m == c + 1) esig[m] = 1.f;
       }
       if (t + 1 < nsteps) prepare(t + 1);
       if (t + 2 < nsteps) mlp_share(t + 2);
     }
-    store_out(nsteps - 1);
+    store_out();
   };
   if (wr == 0) {
     run(std::integral_constant<int, 0>{});

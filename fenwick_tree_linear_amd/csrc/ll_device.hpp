@@ -334,8 +334,17 @@ struct ChunkLoads {
 #pragma unroll
     for (int k = 0; k < LPW; ++k) {
       const int first = (wv + k * NW) * 64;
-      if (first < lam_n && first + lane < lam_n)
+      if (first + 64 <= lam_n) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + first), 4, lam_off[k], 0, 0, 0);
+      } else if (first < lam_n) {
+        // the last, partial instruction (never at C = 64): its lane test is
+        // formed here, from a lane index made here, so that no mask is held
+        // (or spilled) across the caller's loop
+        int l;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+        if (l < lam_n - first)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + first), 4, lam_off[k], 0, 0, 0);
+      }
     }
   }
   __device__ __forceinline__ void lambda(const float* lam, int64_t row0, int L, float* lds, int wv, int lane) const {
