@@ -28,6 +28,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# The GPU raises its clocks over the first milliseconds of sustained work:
+# after 5 warm-up steps the 16K prefill step measured 0.12 ms, after 300 of
+# them 0.103 ms on the same box.  Before each timed section, settle() runs the
+# section's step untimed, in bursts of 10 with a wait after each, for
+# SETTLE_MS of wall time, so that the timed steps see the clocks a sustained
+# job runs at.
+SETTLE_MS = 100.0
+
+
+def settle(fn) -> int:
+    import torch
+
+    n = 0
+    t_end = time.perf_counter() + SETTLE_MS * 1e-3
+    while SETTLE_MS > 0 and time.perf_counter() < t_end:
+        for _ in range(10):
+            fn()
+        n += 10
+        torch.cuda.synchronize()
+    return n
+
+
 def algorithmic_bytes_per_token_head(w) -> int:
     """Compulsory HBM traffic of one token-head: read q, k, v, lambda, the
     log-gate, write o."""
@@ -132,6 +154,7 @@ def decode_bench(steps: int, cold_reps: int = 10) -> dict:
     def step(pos):
         F.ll_decode_step(w.B, w.H, w.dk, w.dv, w.L, F.LL_BF16, F.LL_MAMBA2, pos, q, k, v, g, lam, None, o, state, stream)
 
+    settle(lambda: step(w.T))
     for i in range(8):
         step(w.T + i)
     torch.cuda.synchronize()
@@ -206,6 +229,8 @@ def ragged_decode_bench(steps: int) -> dict:
                                 state, stream)
         pos.add_(1)
 
+    settle(lambda: F.ll_decode_step_ragged(w.B, w.H, w.dk, w.dv, w.L, F.LL_BF16, F.LL_MAMBA2, pos, q, k, v, g, lam,
+                                           None, o, state, stream))
     for _ in range(8):
         step()
     torch.cuda.synchronize()
@@ -259,6 +284,7 @@ def from_state_bench(reps: int) -> dict:
         F.ll_attn_fwd_from_state(prob0, T0, state, half["q"], half["k"], half["v"], half["log_gate"], half["lam"],
                                  None, o, None, ws, ws_bytes, stream)
 
+    settle(step)
     for _ in range(3):
         step()
     torch.cuda.synchronize()
@@ -298,6 +324,7 @@ def measured_peaks() -> dict:
     stream = torch.cuda.current_stream(dev)
 
     def median_ms(fn, reps=5):
+        settle(fn)
         fn()
         torch.cuda.synchronize()
         out = []
@@ -356,6 +383,7 @@ def ccq_bench(reps: int) -> dict:
         F.ll_attn_fwd(prob, qc, x["k"], x["v"], x["log_gate"], x["lam"], None, o, None, ws, ws_bytes, stream)
 
     def timed(fn, n):
+        settle(fn)
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
@@ -414,6 +442,7 @@ def bwd_bench(reps: int) -> dict:
                       bws_bytes, stream)
 
     def timed(fn, n):
+        settle(fn)
         for _ in range(2):
             fn()
         torch.cuda.synchronize()
@@ -462,6 +491,7 @@ def lambda_mlp_bench(reps: int) -> dict:
         F.ll_lambda_mlp(rows, L, hidden, m["d"], m["w1"], m["w2"], m["bias"], lam, stream)
 
     def timed(fn, n):
+        settle(fn)
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
@@ -528,6 +558,7 @@ def gdn_bench(steps: int) -> dict:
         F.ll_attn_fwd(prob, x["q"], x["k"], x["v"], x["log_gate"], x["lam"], x["beta"], o, None, ws, ws_bytes,
                       stream)
 
+    settle(step)
     for _ in range(3):
         step()
     torch.cuda.synchronize()
@@ -611,6 +642,9 @@ def main() -> int:
                     help="also time this many ll_lambda_mlp launches over the 16K workload's rows (0: skip)")
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="also time this many single steps with the last-level cache flushed before each (0: skip)")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="run the step untimed for this long before the warm-up steps, so that the timed steps "
+                         "see the GPU's clocks after they have ramped up under load (0: skip)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy and GEMM rates")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (calibrates HBM byte counters)")
@@ -648,6 +682,11 @@ def main() -> int:
         log(f"[bench] copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written")
         del src, dst
 
+    global SETTLE_MS
+    SETTLE_MS = args.settle_ms
+    settle_steps = settle(step)
+    if settle_steps:
+        log(f"[bench] settle: {settle_steps} untimed steps in {args.settle_ms:g} ms")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -664,6 +703,17 @@ def main() -> int:
     wall = time.perf_counter() - t0
     ms_per_step = start_ev.elapsed_time(stop_ev) / args.steps
     log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (events), wall {wall * 1e6 / args.steps:.1f} us/step")
+
+    # per-kernel durations: HIP events around every launch, on the launch stream,
+    # right after the timed steps (the same clocks)
+    F.ll_kernel_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = F.ll_kernel_timing_read()
+    F.ll_kernel_timing_enable(False)
+    kernels = {name: round(ms / n * 1e3, 2) for name, (ms, n) in kt.items()}
+    log(f"[bench] per-kernel average us: {kernels}")
 
     # cold: the 256 MB last-level cache flushed by writing a 512 MiB buffer
     # before each of a few individually timed steps (median reported)
@@ -685,16 +735,6 @@ def main() -> int:
                 "reps": len(cold_ms), "flush_bytes": 512 * 1024 * 1024}
         log(f"[bench] cold (last-level cache flushed): median {med * 1e3:.1f} us/step over {len(cold_ms)} steps")
 
-    # per-kernel durations: HIP events around every launch, on the launch stream
-    F.ll_kernel_timing_enable(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    kt = F.ll_kernel_timing_read()
-    F.ll_kernel_timing_enable(False)
-    kernels = {name: round(ms / n * 1e3, 2) for name, (ms, n) in kt.items()}
-    log(f"[bench] per-kernel average us: {kernels}")
-
     token_heads = w.B * w.T * w.H
     alg_bytes = algorithmic_bytes_per_token_head(w) * token_heads
     # ll_fenwick_scan: the block states it must read and the level >= 1 nodes it writes
@@ -715,6 +755,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "steps": settle_steps},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
