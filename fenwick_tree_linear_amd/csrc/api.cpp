@@ -471,8 +471,7 @@ ll_status run_prefill(const ll_problem* p, int64_t pos0, const float* state_in, 
                       void* state_out, void* workspace, size_t workspace_bytes, hipStream_t stream,
                       bool reuse_states = false, bool noalloc = false, const ReadMlp* mlp = nullptr) {
   Plan pl;
-  // the read that runs the MLP keeps blocks of at most 2^max_block_depth chunks
-  ll_status st = plan_prefill(p, state_out != nullptr, &pl, mlp ? llattn::max_block_depth(p ? p->dk : 0) : -1);
+  ll_status st = plan_prefill(p, state_out != nullptr, &pl);
   if (st != LL_OK) return st;
   if (reuse_states && (p->rule != LL_MAMBA2 || pos0 != 0 || state_out || pl.pad_qk || pl.pad_v))
     return fail(LL_ERR_UNSUPPORTED, "reusing block states is only for a plain Mamba-2 read in the run shape");
@@ -695,16 +694,12 @@ ll_status plan_mlp_prefill(const ll_problem* p, int hidden, bool want_state, Mlp
   if (hidden > 64 || p->L > 32)
     return fail(LL_ERR_UNSUPPORTED, "L=%d, hidden=%d: at most 32 levels and 64 hidden units are supported", p->L,
                 hidden);
-  // planned as the read that runs the MLP (blocks of at most 2^max_block_depth
-  // chunks); a read that cannot runs the plain prefill after ll_lambda_mlp
+  // the read that runs the MLP has the plain prefill's blocks; a read that
+  // cannot runs the plain prefill after ll_lambda_mlp
   Plan pl;
-  ll_status st = plan_prefill(p, want_state, &pl, llattn::max_block_depth(p->dk));
+  ll_status st = plan_prefill(p, want_state, &pl);
   if (st != LL_OK) return st;
   mp->fused = llattn::read_runs_mlp(pl.r.io == LL_BF16 ? 1 : 0, pl.r.dk, pl.Cr, p->L, hidden);
-  if (!mp->fused) {
-    st = plan_prefill(p, want_state, &pl);
-    if (st != LL_OK) return st;
-  }
   mp->lam_off = (pl.bytes + 255) & ~(size_t)255;
   mp->bytes = mp->fused ? pl.bytes : mp->lam_off + (size_t)p->B * p->T * p->H * p->L * sizeof(float);
   return LL_OK;

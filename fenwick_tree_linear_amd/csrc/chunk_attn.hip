@@ -683,14 +683,6 @@ __global__ void __launch_bounds__((64 * AttnWaves<D, C>::NW)) ll_chunk_attn(Pref
   }
 }
 
-// Waits until at most N of this wave's vector memory operations are
-// outstanding (they complete in issue order); the other counters are left.
-template <int N>
-__device__ __forceinline__ void wait_vmem_at_most() {
-  static_assert(N >= 0 && N < 64, "vmcnt holds six bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // ---------------------------------------------------------------------------
 // ll_chunk_attn_split: the same read for bf16 with two row groups, with the
 // work of a step divided by role instead of repeated per row group.
@@ -717,41 +709,15 @@ struct SplitWaves {
   __host__ __device__ static constexpr int row_tile(int i, int wr) { return (i & 1) ? CT - 1 - wr : wr; }
 };
 
-// LDS of ll_chunk_attn_split (byte offsets): the chunk staging ring, masked
-// scores and decay-scaled keys of two chunk parities, the in-chunk prefix
-// arrays of two parities (one copy: every maker writes the same values), and
-// the within-block states as fragments [level][column tile][k step][lane].
+// LDS of ll_chunk_attn_split: the offsets of SplitLds at this head, chunk and
+// within-block depth.
 template <int D, int C, int MAXB>
-struct SplitLayout {
+struct SplitLayout : SplitLds {
   typedef Tile<bf16, C, D> TL;
   typedef Tile<bf16, C, C> PT;
-  static constexpr int NS = 3;
-  static constexpr int FRAG_BYTES = 64 * 16;                           // one bf16 fragment of a wave
+  static_assert(TL::BYTES == C * D * 2 && PT::BYTES == C * C * 2, "tile sizes as SplitLds counts them");
   static constexpr int STATE_BYTES = MAXB * (D / 16) * (D / 32) * FRAG_BYTES;
-  // with the level-weight MLP: its weights, zero-padded to 16 levels x 32
-  // hidden ([16][32] W1, [32][16] W2, [16] bias), and a ring of three chunks
-  // of its input [C][16] (levels past L unset)
-  static constexpr int MLP_W_BYTES = (16 * 32 + 32 * 16 + 16) * 4;
-  int q, k, v, g, lraw, stage;
-  int p, kw, gw, st, mw, dr, total;
-  __host__ __device__ explicit SplitLayout(int LS, int mlp_levels = 0) {
-    q = 0;
-    k = q + TL::BYTES;
-    v = k + TL::BYTES;
-    g = v + TL::BYTES;
-    lraw = g + C * 4;
-    stage = (lraw + C * LS * 4 + 255) & ~255;
-    p = NS * stage;
-    kw = p + 2 * PT::BYTES;
-    gw = kw + 2 * TL::BYTES;
-    st = (gw + 2 * 3 * C * 4 + 255) & ~255;
-    total = st + STATE_BYTES;
-    mw = dr = total;
-    if (mlp_levels > 0) {
-      dr = mw + MLP_W_BYTES;
-      total = dr + 3 * C * 16 * 4;
-    }
-  }
+  __host__ __device__ explicit SplitLayout(int LS, int mlp_levels = 0) : SplitLds(D, C, MAXB, LS, mlp_levels > 0) {}
 };
 
 template <int D, int C, int MAXB, int MAXH, bool MLP>
@@ -861,12 +827,17 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
     *reinterpret_cast<bf16x4*>(pt + PT::off(r, 16 * ct + 4 * g4)) = out;
   };
   // decay-scaled keys: the same swizzled positions, each 16-byte piece of a
-  // row scaled by that row's weight; pieces x0, x0 + stride, ...
-  auto scaled_keys = [&](int j, int x0, int stride) __attribute__((always_inline)) {
+  // row scaled by that row's weight; pieces x0, x0 + STRIDE, ... (x0 < STRIDE,
+  // which divides the piece count: a fixed trip count)
+  auto scaled_keys = [&](int j, int x0, auto stride) __attribute__((always_inline)) {
+    constexpr int STRIDE = decltype(stride)::value;
+    static_assert((TL::BYTES / 16) % STRIDE == 0, "whole rounds of pieces");
     const char* st = stage_of(j);
     const float* wl = garr(j) + C;
     char* kw = smem + lay.kw + (j & 1) * TL::BYTES;
-    for (int x = x0; x < TL::BYTES / 16; x += stride) {
+#pragma unroll
+    for (int u = 0; u < TL::BYTES / 16 / STRIDE; ++u) {
+      const int x = x0 + u * STRIDE;
       const float w = wl[x / TL::NCH];
       const bf16x8 kv = *reinterpret_cast<const bf16x8*>(st + lay.k + x * 16);
       bf16x8 o;
@@ -878,52 +849,41 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
   constexpr int NBT = CT * (CT - 1) / 2;  // score tiles below the diagonal
 
   // The level-weight MLP of chunk j ("Adaptive memory decay for log-linear
-  // attention", section "Method", LambdaMLPSoftplus), 16 rows at a time, with
-  // the products, their order and the softplus of ll_lambda_mlp: layer 1
-  // transposed, h^T (hidden x rows) = W1^T d^T, so that a lane ends up holding
-  // its row of h in the k order of layer 2, z (rows x levels) = h W2, then
-  // lambda = softplus(z + b) into the chunk's level-weight rows.  The second
-  // row group of readers runs it (row tile rt by reader rt mod NCT of the
-  // group), at the end of their step; the makers load its input.
-  // The weights as MFMA fragments of this lane (zero in the padding): layer 1
-  // A = W1^T, step s of hidden tile n gives W1[4s + g][16n + c]; layer 2
-  // B = W2, step s gives W2[kidx(s, g)][c]; then the bias of level c.
+  // attention", section "Method", LambdaMLPSoftplus), 16 rows at a time, as
+  // in ll_lambda_mlp: lambda = softplus(d Wc + b) with the composite Wc = W1 W2
+  // (the two layers are linear), formed once per workgroup with the same
+  // operations, and the row product with the same k steps and accumulators,
+  // into the chunk's level-weight rows.  The second row group of readers runs
+  // it (row tile rt by reader rt mod NCT of the group), in the middle of their
+  // step, and loads its input.  This lane's fragments of Wc (step s:
+  // Wc[4s + g][c], zero past L) and the bias of level c:
   struct MlpFrags {
-    float a1[2][4], b2[8], b;
+    float b[4], bias;
   };
   auto mlp_frags = [&]() __attribute__((always_inline)) {
-    typedef Mma<float> MF;
     const float* w = reinterpret_cast<const float*>(smem + lay.mw);
     MlpFrags f;
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) f.a1[n][s] = w[(4 * s + g4) * 32 + 16 * n + q16];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) f.b2[s] = w[16 * 32 + MF::kidx(s, g4, 0) * 16 + q16];
-    f.b = w[16 * 32 + 32 * 16 + q16];
+    for (int s = 0; s < 4; ++s) f.b[s] = w[(4 * s + g4) * 16 + q16];
+    f.bias = w[16 * 16 + q16];
     return f;
   };
   auto mlp_tile = [&](const MlpFrags& f, int j, int rt) __attribute__((always_inline)) {
-    typedef Mma<float> MF;
-    const float* drow = reinterpret_cast<const float*>(smem + lay.dr) + (j % 3) * C * 16 + (16 * rt + q16) * 16 + g4;
+    // the lane's row and group from an opaque copy of the lane index, so that
+    // the addresses below are formed here rather than held across the step
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    const int g4 = l >> 4, q16 = l & 15;
+    const float* drow = reinterpret_cast<const float*>(smem + lay.dr) + (j % 2) * C * 16 + (16 * rt + q16) * 16 + g4;
     // (levels past L read the zeros the ring holds there)
     float bd[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) bd[s] = drow[4 * s];
-    f32x4 h[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int n = 0; n < 2; ++n) h[n] = MF::mma(f.a1[n][s], bd[s], h[n]);
-    f32x4 zz[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) zz[s & 1] = MF::mma(MF::acc_frag(h, s), f.b2[s], zz[s & 1]);
-    const f32x4 z = zz[0] + zz[1];
+    const f32x4 z = mlp_tile_product<4>(bd, f.b);
     float* lr = reinterpret_cast<float*>(stage_of(j) + lay.lraw);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (q16 < LS) lr[(16 * rt + 4 * g4 + i) * LS + q16] = softplus_f32(z[i] + f.b);
+      if (q16 < LS) lr[(16 * rt + 4 * g4 + i) * LS + q16] = softplus_f32(z[i] + f.bias);
   };
   auto mlp_share = [&](int j) __attribute__((always_inline)) {
     if (!MLP || wv < NCT || wv >= NRW) return;
@@ -935,24 +895,8 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
   if constexpr (MLP) {
     // the levels past L of the input ring: zero, and never loaded
     float* dring = reinterpret_cast<float*>(smem + lay.dr);
-    for (int x = tid; x < 3 * C * 16; x += 64 * NW)
+    for (int x = tid; x < 2 * C * 16; x += 64 * NW)
       if ((x & 15) >= a.L) dring[x] = 0.f;
-    // the MLP's weights into LDS, zero-padded
-    float* w = reinterpret_cast<float*>(smem + lay.mw);
-    for (int x = tid; x < 16 * 32 + 32 * 16 + 16; x += 64 * NW) {
-      float val = 0.f;
-      if (x < 16 * 32) {
-        const int k = x / 32, n = x % 32;
-        if (k < a.L && n < a.hidden) val = a.w1[k * a.hidden + n];
-      } else if (x < 16 * 32 + 32 * 16) {
-        const int k = (x - 16 * 32) / 16, n = (x - 16 * 32) % 16;
-        if (k < a.hidden && n < a.L) val = a.w2[k * a.L + n];
-      } else {
-        const int n = x - 16 * 32 - 32 * 16;
-        if (n < a.L) val = a.mlp_bias[n];
-      }
-      w[x] = val;
-    }
   }
 
   if (wv >= NRW) {
@@ -967,40 +911,15 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
       for (int o = NCT + mw; o < NBT; o += 2 * NCT) score_tile(j, CT + o);
     };
 
-    // with the MLP: its input rows, four chunks ahead into a ring of three
-    // (chunk j in slot j % 3), loaded by the makers straight into LDS, 16
-    // levels a row: instruction u of maker mw takes rows 4 (mw + u NMW) ..
-    // + 3, lane l row + l / 16, level l % 16 (levels past L are not loaded).
-    // Chunk j is used at the end of step j - 2; its loads may stay in flight
-    // across the barrier of step j - 3.
-    ItemWalk dload_at;
-    dload_at.start(item0, a, C);
-    const uint32_t d_off = (uint32_t)(((mw * 4 + (lane >> 4)) * a.H * a.L + (lane & 15)) * 4);
-    const int d_step = NMW * 4 * a.H * a.L * 4;  // bytes between the rows of consecutive instructions
-    const uint32_t d_extent = (uint32_t)(((C - 1) * a.H * a.L + a.L) * 4);
-    auto load_d = [&](__amdgpu_buffer_rsrc_t r, char* lds) __attribute__((always_inline)) {
-#pragma unroll
-      for (int u = 0; u < C * 16 / (64 * NMW); ++u)
-        if ((lane & 15) < a.L)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + (mw + u * NMW) * 256), 4, d_off, u * d_step, 0, 0);
-    };
-    auto issue_d = [&](int j) __attribute__((always_inline)) {
-      if (j > 0 && (j & (a.P - 1)) == 0) dload_at.next(a, C);
-      const float* rows = a.lam + (dload_at.row + (int64_t)((j & (a.P - 1)) * C * a.H)) * a.L;
-      load_d(buffer_rsrc(rows, d_extent), smem + lay.dr + (j % 3) * C * 16 * 4);
-    };
-    constexpr int ND = C * 16 / (64 * NMW);  // input loads of a chunk, per maker
     if constexpr (MLP) {
-      issue_d(0);
-      if (nsteps > 1) issue_d(1);
-      __builtin_amdgcn_s_waitcnt(0);
+      // Wc (16 x 16, zero past L) and the bias into LDS while the readers'
+      // first chunks load
+      float* w = reinterpret_cast<float*>(smem + lay.mw);
+      for (int x = tid - 64 * NRW; x < 16 * 16; x += 64 * NMW) w[x] = mlp_composite(a.w1, a.w2, a.L, a.hidden, x / 16, x % 16);
+      if (tid - 64 * NRW < 16) w[16 * 16 + lane] = lane < a.L ? a.mlp_bias[lane] : 0.f;
     }
     lds_barrier();  // the zeroed tiles are visible; the readers' first chunks landed
-    if constexpr (MLP) {
-      lds_barrier();  // the readers made the level weights of chunks 0 and 1
-      if (nsteps > 2) issue_d(2);
-      if (nsteps > 3) issue_d(3);
-    }
+    if constexpr (MLP) lds_barrier();  // the readers made the level weights of chunks 0 and 1
     prepare(0);
 
     // the within-block Fenwick states of this wave's 16 columns (levels
@@ -1009,18 +928,7 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
     float sig[MAXB + 1];
     for (int t = 0; t < nsteps; ++t) {
       const int j = t & (a.P - 1);
-      if constexpr (MLP) {
-        // this wave's input rows of chunk t+2 landed (those of t+3 may not have)
-        if (t + 3 < nsteps) {
-          wait_vmem_at_most<ND>();
-        } else {
-          __builtin_amdgcn_s_waitcnt(0);
-        }
-      }
       lds_barrier();  // step t prepared; the readers' loads of step t+1 landed
-      if constexpr (MLP) {
-        if (t + 4 < nsteps) issue_d(t + 4);
-      }
       if (j == 0) {
 #pragma unroll
         for (int m = 0; m < MAXB; ++m)
@@ -1124,13 +1032,45 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
     issue_part(j, 1);
     issue_part(j, 2);
   };
+  // With the MLP: the input rows of the tiles whose level weights this wave
+  // makes (second row group), loaded by the wave itself straight into LDS,
+  // one chunk ahead of its stage loads, into a ring of two chunks (chunk j in
+  // slot j % 2; chunk j is loaded during step j - 3 and used during step
+  // j - 2), 16 levels a row: instruction u of tile rt takes rows
+  // 16 rt + 4u .. + 3, lane l row + l / 16, level l % 16 (levels past L are
+  // not loaded).
+  ItemWalk dload_at = load_at;
+  auto issue_d = [&](int j) __attribute__((always_inline)) {
+    if (!MLP || wv < NCT) return;
+    if (j > 0 && (j & (a.P - 1)) == 0) dload_at.next(a, C);
+    const int64_t row0 = row_in(dload_at, j);
+    int l = lane;
+    asm volatile("" : "+v"(l));  // the lane offsets are formed here, not held across the step
+    const uint32_t off = (uint32_t)((((l >> 4) * a.H) * a.L + (l & 15)) * 4);
+#pragma unroll
+    for (int rt = 0; rt < CT; ++rt)
+      if (rt % NCT == wv - NCT) {
+        const __amdgpu_buffer_rsrc_t r =
+            buffer_rsrc(a.lam + (row0 + (int64_t)16 * rt * a.H) * a.L, (uint32_t)((15 * a.H * a.L + a.L) * 4));
+        char* dst = smem + lay.dr + (j % 2) * C * 16 * 4 + 16 * rt * 64;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if ((l & 15) < a.L)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + u * 256), 4, off, u * 4 * a.H * a.L * 4, 0, 0);
+      }
+  };
   issue(0);
+  if constexpr (MLP) {
+    issue_d(0);
+    if (nsteps > 1) issue_d(1);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   if (nsteps > 1) issue(1);
   lds_barrier();  // step 0 has landed for every reader; the zeroed tiles are visible
   if constexpr (MLP) {
     mlp_share(0);
     if (nsteps > 1) mlp_share(1);
+    if (nsteps > 2) issue_d(2);  // into the slot of chunk 0, whose weights are made
     lds_barrier();  // the level weights of chunks 0 and 1 are made
   }
   // the first row group's share of preparing chunk j: the scaled keys and
@@ -1141,7 +1081,7 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
     prefix(j);
 #pragma unroll
     for (int o = wv; o < NBT; o += 2 * NCT) score_tile(j, CT + o);
-    scaled_keys(j, tid, 64 * NCT);
+    scaled_keys(j, tid, std::integral_constant<int, 64 * NCT>{});
   };
   prepare(0);
 
@@ -1284,6 +1224,10 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
         issue_part(t + 2, 1);
         issue_part(t + 2, 2);
       }
+      if (t + 3 < nsteps) issue_d(t + 3);  // into the slot of chunk t+1, whose weights are made
+      // the level weights of chunk t+2 (its stage is being loaded, but not its
+      // weight rows), here so that their products overlap this step's reads
+      if (t + 2 < nsteps) mlp_share(t + 2);
 
       // --- inter-chunk levels: O^T += diag(alpha) N^T Q^T, alpha_r = lambda_r^l e^{G_r} x scale.
       // A level's product is weighted into O only when the next level comes
@@ -1370,7 +1314,6 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
           if (m == c + 1) esig[m] = 1.f;
       }
       if (t + 1 < nsteps) prepare(t + 1);
-      if (t + 2 < nsteps) mlp_share(t + 2);
     }
     store_out();
   };
@@ -1430,25 +1373,23 @@ static hipError_t launch_attn_t(const PrefillArgs& a, hipStream_t s) {
   if constexpr (C * D * (int)sizeof(T) > kAttnTileBytesMax) {
     return hipErrorInvalidValue;  // rejected by the shape checks before launch
   } else {
-    // Fenwick nodes of earlier blocks held in registers (5 cover up to 32 blocks per head).  At
-    // d = 128 the within-block nodes of 8-chunk blocks already fill the register budget, so
-    // every earlier block's node is read from LDS (holding even one spills).
-    constexpr int MAXH = (sizeof(T) == 2) ? (D <= 64 ? 5 : 0) : 0;
+    // Fenwick nodes of earlier blocks held in registers (4 cover up to 16 blocks per head; the
+    // nodes of further set bits are read at each chunk; a fifth held node costs the registers
+    // that keep the read's loop free of spills).  At d = 128 the within-block nodes of
+    // 8-chunk blocks already fill the register budget, so every earlier block's node is read
+    // from LDS (holding even one spills).
+    constexpr int MAXH = (sizeof(T) == 2) ? (D <= 64 ? 4 : 0) : 0;
     static PersistentGrid grid;
     if constexpr (read_split(sizeof(T) == 2 ? 1 : 0, D, C)) {
       constexpr int MAXB = read_block_depth(1, D, C);
+      if (a.P > (1 << MAXB)) return hipErrorInvalidValue;  // planned within the depth
       if (a.w1) {
-        // with the MLP's ring and weights, four within-block levels do not fit
-        // LDS beside three staged chunks: blocks of at most 8 chunks
-        constexpr int MAXB_MLP = max_block_depth(D);
+        if (a.L > 16 || a.hidden < 1) return hipErrorInvalidValue;  // checked before launch
         static PersistentGrid grid_mlp;
-        if (a.P > (1 << MAXB_MLP)) return hipErrorInvalidValue;  // planned within the depth
-        if (a.L > 16 || a.hidden < 1 || a.hidden > 32) return hipErrorInvalidValue;  // checked before launch
-        auto kern = ll_chunk_attn_split<D, C, MAXB_MLP, MAXH, true>;
-        const SplitLayout<D, C, MAXB_MLP> lay(a.LS, a.L);
+        auto kern = ll_chunk_attn_split<D, C, MAXB, MAXH, true>;
+        const SplitLayout<D, C, MAXB> lay(a.LS, a.L);
         return grid_mlp.launch(reinterpret_cast<const void*>(kern), 64 * SplitWaves<D, C>::NW, lay.total, a, s);
       }
-      if (a.P > (1 << MAXB)) return hipErrorInvalidValue;  // planned within the depth
       auto kern = ll_chunk_attn_split<D, C, MAXB, MAXH, false>;
       const SplitLayout<D, C, MAXB> lay(a.LS);
       return grid.launch(reinterpret_cast<const void*>(kern), 64 * SplitWaves<D, C>::NW, lay.total, a, s);

@@ -106,8 +106,37 @@ __device__ __forceinline__ float chunk_scan(float x) {
 
 // softplus(z) = log(1 + e^z), as max(z, 0) + log(1 + e^-|z|) so that large |z|
 // neither overflows nor cancels; rounding 1 + x (x in (0, 1]) to fp32 costs at
-// most 2^-24 in absolute terms, far below the weights' own size
-__device__ __forceinline__ float softplus_f32(float z) { return fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z))); }
+// most 2^-24 in absolute terms, far below the weights' own size.  The
+// logarithm's argument lies in (1, 2], so the hardware log2 (v_log_f32) serves
+// as is, times ln 2, without the range scaling a general logf needs.
+__device__ __forceinline__ float softplus_f32(float z) {
+  return fmaxf(z, 0.f) + 0.693147180559945309f * __builtin_amdgcn_logf(1.f + __expf(-fabsf(z)));
+}
+
+// The level-weight MLP ("Adaptive memory decay for log-linear attention",
+// section "Method", LambdaMLPSoftplus) has no activation between its two
+// linear layers: h = d W1, lambda = softplus(h W2 + b).  So lambda =
+// softplus(d Wc + b) with the composite Wc = W1 W2 (L x L): every kernel that
+// makes level weights forms Wc once, with these same fp32 operations, and
+// then one L x L product per row instead of the two layers.
+// Element (k, n) of Wc (zero past L), summed over the hidden units in order.
+__device__ __forceinline__ float mlp_composite(const float* w1, const float* w2, int L, int hidden, int k, int n) {
+  float acc = 0.f;
+  if (k < L && n < L)
+    for (int j = 0; j < hidden; ++j) acc = fmaf(w1[k * hidden + j], w2[j * L + n], acc);
+  return acc;
+}
+// One 16 x 16 tile of z = d Wc on the fp32 matrix cores over KSTEPS k steps of
+// four levels: a[s] = d[row l%16][4s + l/16], b[s] = Wc[4s + l/16][column
+// l%16]; the even and odd steps in two accumulators, then summed (two
+// dependent chains of half the length).  Lane l gets z[4(l/16) + i][l%16].
+template <int KSTEPS>
+__device__ __forceinline__ f32x4 mlp_tile_product(const float* a, const float* b) {
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) acc[s & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc[s & 1], 0, 0, 0);
+  return acc[0] + acc[1];
+}
 
 // ---------------------------------------------------------------- XCD order
 // Workgroup ids are dealt round-robin to the 8 XCDs of the chip; each XCD
@@ -284,8 +313,11 @@ struct ChunkLoads {
   static constexpr int NINST = TL::BYTES / 1024;
   static constexpr int TPW = (NINST + NW - 1) / NW;                        // tile instructions per wave
   static constexpr int LPW = (C * kLevelsMax + 64 * NW - 1) / (64 * NW);   // lambda instructions per wave, at most
+  // lambda instructions whose lane offsets are held: those of up to 16 staged
+  // levels; the others (more levels) form theirs at each use
+  static constexpr int LPH = (C * 16 + 64 * NW - 1) / (64 * NW) < LPW ? (C * 16 + 64 * NW - 1) / (64 * NW) : LPW;
   static_assert(TL::BYTES % 1024 == 0 && 1024 % TL::RB == 0, "tile must be whole 1 KiB instructions");
-  uint32_t tile_off[TPW], lam_off[LPW];
+  uint32_t tile_off[TPW], lam_off[LPH];
   int lam_n;  // lambda floats per chunk, C * LS
 
   __device__ __forceinline__ void init(int wv, int lane, int H, int L, int LS) {
@@ -298,11 +330,19 @@ struct ChunkLoads {
     }
     lam_n = C * LS;
 #pragma unroll
-    for (int k = 0; k < LPW; ++k) {
-      const int f = (wv + k * NW) * 64 + lane, r = f / LS;
-      lam_off[k] = (uint32_t)((r * H * L + (f - r * LS)) * 4);
-    }
+    for (int k = 0; k < LPH; ++k) lam_off[k] = lam_offset((wv + k * NW) * 64 + lane, H, L, LS);
     h_ = H;
+  }
+  // byte offset of float f of a chunk's staged [C][LS] rows in the [rows][L] tensor
+  __device__ __forceinline__ static uint32_t lam_offset(int f, int H, int L, int LS) {
+    const int r = f / LS;
+    return (uint32_t)((r * H * L + (f - r * LS)) * 4);
+  }
+  // a lane index formed where it is used (not held across the caller's loop)
+  __device__ __forceinline__ static int lane_here() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
   }
   // Every load goes through a buffer resource whose base is the chunk's first
   // element, so the per-lane offsets above stay 32-bit registers and moving to
@@ -330,25 +370,25 @@ struct ChunkLoads {
                                                (lds_void*)lds, 4, (uint32_t)(l * h_ * 4), 0, 0, 0);
     }
   }
-  __device__ __forceinline__ void lambda_from(__amdgpu_buffer_rsrc_t rsrc, float* lds, int wv, int lane) const {
+  __device__ __forceinline__ void lambda_from(__amdgpu_buffer_rsrc_t rsrc, float* lds, int wv, int L) const {
 #pragma unroll
     for (int k = 0; k < LPW; ++k) {
       const int first = (wv + k * NW) * 64;
-      if (first + 64 <= lam_n) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + first), 4, lam_off[k], 0, 0, 0);
-      } else if (first < lam_n) {
-        // the last, partial instruction (never at C = 64): its lane test is
-        // formed here, from a lane index made here, so that no mask is held
-        // (or spilled) across the caller's loop
-        int l;
-        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-        if (l < lam_n - first)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + first), 4, lam_off[k], 0, 0, 0);
+      if (first < lam_n) {
+        // the last, partial instruction (never at C = 64) and the offsets
+        // that are not held are formed here, from a lane index made here, so
+        // that no mask or offset is held (or spilled) across the caller's loop
+        const bool held = k < LPH, whole = first + 64 <= lam_n;
+        const int l = (held && whole) ? 0 : lane_here();
+        const uint32_t off = held ? lam_off[held ? k : 0] : lam_offset(first + l, h_, L, lam_n / C);
+        if (whole || l < lam_n - first)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + first), 4, off, 0, 0, 0);
       }
     }
   }
   __device__ __forceinline__ void lambda(const float* lam, int64_t row0, int L, float* lds, int wv, int lane) const {
-    lambda_from(buffer_rsrc(lam + row0 * L, (uint32_t)(((C - 1) * h_ * L + lam_n / C) * 4)), lds, wv, lane);
+    (void)lane;
+    lambda_from(buffer_rsrc(lam + row0 * L, (uint32_t)(((C - 1) * h_ * L + lam_n / C) * 4)), lds, wv, L);
   }
 };
 

@@ -150,16 +150,57 @@ inline int ilog2_host(int x) {
 // largest within-block Fenwick depth the chunk kernels hold in registers
 constexpr int max_block_depth(int /*D*/) { return 3; }
 // The reader/maker read (bf16, square head D <= 64, chunks of at least 32)
-// keeps four within-block levels, so its blocks hold up to 16 chunks; every
-// other read, that read when it runs the level-weight MLP, and the backward
-// up to 2^max_block_depth.
+// keeps four within-block levels, so its blocks hold up to 16 chunks (also
+// when it runs the level-weight MLP); every other read and the backward up to
+// 2^max_block_depth.
 constexpr bool read_split(int io, int D, int C) { return io == 1 && D <= 64 && C >= 32; }
 constexpr int read_block_depth(int io, int D, int C) { return read_split(io, D, C) ? 4 : max_block_depth(D); }
 // Whether the read runs the level-weight MLP itself (PrefillArgs::w1): bf16 in
-// the run shape, square head D <= 64, chunk C >= 32, L <= 16, hidden <= 32.
+// the run shape, square head D <= 64, chunk C >= 32, L <= 16 (any hidden size:
+// the read applies the composite W1 W2).
 inline bool read_runs_mlp(int io, int D, int C, int L, int hidden) {
-  return read_split(io, D, C) && L <= 16 && hidden >= 1 && hidden <= 32;
+  return read_split(io, D, C) && L <= 16 && hidden >= 1;
 }
+
+// LDS of the reader/maker read (bf16, head D, chunk C, within-block depth
+// maxb, LS staged levels), byte offsets: the chunk staging ring (three stages
+// of q, k and v tiles, gates and level-weight rows), the masked scores and the
+// decay-scaled keys of two chunk parities, the in-chunk prefix arrays of two
+// parities, the within-block states as bf16 MFMA fragments ([level][column
+// tile][k step][lane], 1 KiB each); with the level-weight MLP, its composite
+// weights and bias ([16][16], [16]) and a ring of two chunks of its input
+// [C][16].
+struct SplitLds {
+  static constexpr int NS = 3;
+  static constexpr int FRAG_BYTES = 64 * 16;
+  static constexpr int MLP_W_BYTES = (16 * 16 + 16) * 4;
+  int q = 0, k = 0, v = 0, g = 0, lraw = 0, stage = 0;
+  int p = 0, kw = 0, gw = 0, st = 0, mw = 0, dr = 0, total = 0;
+  __host__ __device__ constexpr SplitLds(int D, int C, int maxb, int LS, bool mlp) {
+    const int tile = C * D * 2, scores = C * C * 2;
+    q = 0;
+    k = q + tile;
+    v = k + tile;
+    g = v + tile;
+    lraw = g + C * 4;
+    stage = (lraw + C * LS * 4 + 255) & ~255;
+    p = NS * stage;
+    kw = p + 2 * scores;
+    gw = kw + 2 * tile;
+    st = (gw + 2 * 3 * C * 4 + 255) & ~255;
+    total = st + maxb * (D / 16) * (D / 32) * FRAG_BYTES;
+    mw = dr = total;
+    if (mlp) {
+      dr = mw + MLP_W_BYTES;
+      total = dr + 2 * C * 16 * 4;
+    }
+  }
+};
+constexpr int kLdsBytesMax = 160 * 1024;  // per workgroup on gfx950
+// The largest reader/maker reads fit: 24 staged levels without the MLP, 16
+// with it (the MLP takes L <= 16), both with four within-block levels.
+static_assert(SplitLds(64, 64, 4, kLevelsMax, false).total <= kLdsBytesMax, "the split read fits LDS");
+static_assert(SplitLds(64, 64, 4, 16, true).total <= kLdsBytesMax, "the split read with the MLP fits LDS");
 
 // Whether the backward walks keep their chunk-level states in LDS (else in
 // BwdWork::scratch).

@@ -223,7 +223,10 @@ ll_status ll_decode_step(int B, int H, int dk, int dv, int L, ll_dtype io, ll_ru
  *   bias   [L]              fp32
  *   lambda [rows, L]        fp32, written; must not overlap d
  * The page uses hidden = 2L; implemented for 1 <= L <= 32, 1 <= hidden <= 64
- * (LL_ERR_UNSUPPORTED otherwise).  Computed in fp32 on the matrix cores.
+ * (LL_ERR_UNSUPPORTED otherwise).  Computed in fp32: no activation lies between
+ * the two layers, so the kernel forms the composite Wc = W1 W2 (L x L) and then
+ * lambda = softplus(d Wc + b), one L x L product per row on the matrix cores
+ * (the result agrees with the two layers to fp32 rounding).
  * rows == 0 enqueues nothing (pointers may then be NULL).
  */
 ll_status ll_lambda_mlp(int64_t rows, int L, int hidden, const float* d, const float* w1, const float* w2,
@@ -239,11 +242,11 @@ ll_status ll_lambda_mlp(int64_t rows, int L, int hidden, const float* d, const f
  *   hidden, w1 [L, hidden], w2 [hidden, L], bias [L]: as ll_lambda_mlp
  *   every other argument as ll_attn_fwd (o must not be NULL)
  * For bf16 problems whose run shape has a head of at most 64 and chunks of at
- * least 32, with L <= 16 and hidden <= 32, the read makes the weights of each
- * chunk itself (fp32 matrix cores, the same products and order as
- * ll_lambda_mlp) and never writes them to memory; otherwise ll_lambda_mlp
- * writes them into the workspace first.  Either way the result is the same
- * as ll_lambda_mlp followed by ll_attn_fwd.
+ * least 32, with L <= 16, the read makes the weights of each chunk itself
+ * (the composite Wc and the fp32 products of ll_lambda_mlp, in the same order)
+ * and never writes them to memory; otherwise ll_lambda_mlp writes them into
+ * the workspace first.  Either way the result is that of ll_lambda_mlp
+ * followed by ll_attn_fwd, bit for bit (the same weights, the same blocks).
  * Workspace: ll_attn_fwd_lambda_mlp_workspace_bytes (the prefill's, plus
  * B*T*H*L floats when the weights go through memory).  Errors as ll_attn_fwd
  * and ll_lambda_mlp.

@@ -202,18 +202,18 @@ def test_lambda_mlp_validation_before_any_launch():
 
 
 def test_fused_mlp_prefill_workspace():
-    """The read makes the level weights itself for bf16 with a run head <= 64, run chunks >= 32,
-    L <= 16 and hidden <= 32: the workspace is then a prefill's with blocks of at most 8 chunks
-    (that read keeps three within-block levels), no room for the weights.  Otherwise the weights
-    of every row go through the workspace after the plain prefill's (256-byte aligned)."""
-    for kw, hidden in [(dict(), 30), (dict(T=2048, L=12, dk=32, dv=16, C=16), 24)]:
+    """The read makes the level weights itself for bf16 with a run head <= 64, run chunks >= 32
+    and L <= 16 (any hidden size), in the plain prefill's blocks: the workspace is then exactly a
+    prefill's.  Otherwise the weights of every row go through the workspace after the plain
+    prefill's (256-byte aligned)."""
+    for kw, hidden in [(dict(), 30), (dict(), 33), (dict(), 64), (dict(T=32768, L=16), 30),
+                       (dict(T=2048, L=12, dk=32, dv=16, C=16), 24)]:
         p = prob(**kw)
-        n, plain = F.ll_attn_fwd_lambda_mlp_workspace_bytes(p, hidden), F.ll_attn_fwd_workspace_bytes(p)
-        assert plain <= n < plain + p.B * p.T * p.H * p.L * 4, (kw, n, plain)
-    # the 16K prefill: 32 heads x 32 blocks of 8 chunks, 1024 states + 512 nodes of 64 x 64 fp32
+        assert F.ll_attn_fwd_lambda_mlp_workspace_bytes(p, hidden) == F.ll_attn_fwd_workspace_bytes(p), (kw, hidden)
+    # the 16K prefill: blocks of 16 chunks, 32 heads x 16 blocks, 512 states + 256 nodes of 64 x 64 fp32
     n = F.ll_attn_fwd_lambda_mlp_workspace_bytes(prob(), 30)
-    assert 1536 * 64 * 64 * 4 <= n <= 1536 * 64 * 64 * 4 + 4 * 4096 + 4 * 256
-    for kw, hidden in [(dict(), 33), (dict(T=2048, L=17), 30), (dict(T=2048, L=12, io=F.LL_F32, C=32), 24),
+    assert 768 * 64 * 64 * 4 <= n <= 768 * 64 * 64 * 4 + 4 * 4096 + 4 * 256
+    for kw, hidden in [(dict(T=2048, L=17), 30), (dict(T=2048, L=12, io=F.LL_F32, C=32), 24),
                        (dict(T=2048, L=12, dk=128, dv=128, C=32), 24)]:
         p = prob(**kw)
         base = (F.ll_attn_fwd_workspace_bytes(p) + 255) // 256 * 256

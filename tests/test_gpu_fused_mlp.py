@@ -5,13 +5,11 @@ log-linear attention", section "Method", LambdaMLPSoftplus).
 Two checks per case:
   - against the oracle: its own fp64 MLP, then its direct form, at the io
     tolerance;
-  - against ll_lambda_mlp followed by ll_attn_fwd on the same inputs.  The read
-    that makes the weights computes the same fp32 products in the same order as
-    ll_lambda_mlp, so where both calls also cut the sequence into the same
-    blocks (at most 8 chunks: the read that runs the MLP keeps blocks of at most
-    8 chunks, the plain bf16 read of up to 16) the outputs are equal bit for
-    bit; where the blocks differ they agree to the io tolerance; where the read
-    cannot make the weights the call runs the same launches (bit for bit).
+  - against ll_lambda_mlp followed by ll_attn_fwd on the same inputs: equal bit
+    for bit.  The read that makes the weights forms the composite W1 W2 and the
+    fp32 row products with the same operations in the same order as
+    ll_lambda_mlp and cuts the sequence into the plain read's blocks; where it
+    cannot make the weights the call runs those same launches.
 """
 
 import numpy as np
@@ -32,22 +30,16 @@ CASES = [
     ("bf16", 64, 64, 64, 960, 12, 24, W.MAMBA2),    # a last block of fewer chunks
     ("bf16", 32, 32, 32, 512, 10, 20, W.MAMBA2),    # d = 32, chunks of 32
     ("bf16", 32, 64, 64, 1024, 11, 22, W.MAMBA2),   # dk != dv (square head 64)
-    ("bf16", 64, 64, 16, 496, 10, 32, W.MAMBA2),    # chunks of 16 run as 32 (length padded); hidden at its fused limit
+    ("bf16", 64, 64, 16, 496, 10, 32, W.MAMBA2),    # chunks of 16 run as 32 (length padded)
     ("bf16", 64, 64, 64, 512, 16, 32, W.MAMBA2),    # L at its fused limit
+    ("bf16", 64, 64, 64, 4096, 16, 32, W.MAMBA2),   # L 16, 8 blocks
     ("bf16", 64, 64, 64, 1024, 11, 22, W.GATED_DELTANET),
-    ("bf16", 64, 64, 64, 1024, 11, 33, W.MAMBA2),   # hidden 33: ll_lambda_mlp first
+    ("bf16", 64, 64, 64, 1024, 11, 33, W.MAMBA2),   # hidden 33 (made by the read: any hidden size)
+    ("bf16", 64, 64, 64, 512, 12, 64, W.MAMBA2),    # hidden 64, the largest ll_lambda_mlp takes
+    ("bf16", 64, 64, 64, 512, 17, 34, W.MAMBA2),    # L 17: ll_lambda_mlp first
     ("bf16", 128, 128, 64, 512, 10, 20, W.MAMBA2),  # d = 128: ll_lambda_mlp first
     ("f32", 32, 32, 32, 512, 10, 20, W.MAMBA2),     # fp32: ll_lambda_mlp first
 ]
-
-
-def same_blocks(io, dk, dv, C, T, L, hidden):
-    """Whether the read that makes the weights and the plain read cut the sequence into the
-    same blocks: always, unless the former runs (bf16, run head <= 64, run chunk >= 32, L <= 16,
-    hidden <= 32) and the sequence has more than 8 run chunks."""
-    run_c = max(C, 32) if io == "bf16" else C
-    fused = io == "bf16" and max(dk, dv) <= 64 and L <= 16 and hidden <= 32
-    return not fused or -(-T // run_c) <= 8
 
 
 def fused_case(io, dk, dv, C, T, L, hidden, rule, B=1, H=3):
@@ -79,8 +71,7 @@ def test_fused_mlp_prefill(io, dk, dv, C, T, L, hidden, rule):
     err = rel_err(np32(o_fused), oracle_prefill(x))
     say(f"[fused mlp] {io} dk{dk} dv{dv} C{C} T{T} L{L} hidden {hidden} rule {rule}: rel err {err:.3e} "
         f"(tol {TOL[io]:g}); against ll_lambda_mlp + ll_attn_fwd: equal {same}, rel diff {two_err:.3e}")
-    if same_blocks(io, dk, dv, C, T, L, hidden):
-        assert same
+    assert same
     assert two_err <= TOL[io]
     assert err <= TOL[io]
 
@@ -88,15 +79,15 @@ def test_fused_mlp_prefill(io, dk, dv, C, T, L, hidden, rule):
 def test_fused_mlp_16k_workload():
     """The 16K prefill (B2 H16 T16384 d64 bf16, 15 levels, chunk 64) with its level weights
     from the MLP (hidden 2L = 30), which the read makes itself: every output against
-    ll_lambda_mlp + ll_attn_fwd (blocks of 8 and of 16 chunks: the io tolerance), and the last
-    256 tokens of every head against the oracle's direct form."""
+    ll_lambda_mlp + ll_attn_fwd (both in blocks of 16 chunks: bit for bit), and the last 256
+    tokens of every head against the oracle's direct form."""
     w = W.WORKLOADS["prefill-16k"]
     x = W.prefill_inputs(w, parts=("q", "k", "v", "log_gate"))
     m = W.lambda_mlp_inputs((w.B, w.T, w.H), w.L, seed=w.seed)
     o_fused, o_two = run_both(w, x, m, F.LL_MAMBA2)
     two_err = rel_err(np32(o_fused), np32(o_two))
     say(f"[fused mlp] 16K workload: rel diff against ll_lambda_mlp + ll_attn_fwd {two_err:.3e}")
-    assert two_err <= TOL["bf16"]
+    assert torch.equal(o_fused, o_two)
     lam_ref = oracle.lambda_mlp(np32(m["d"]), np32(m["w1"]), np32(m["w2"]), np32(m["bias"]))
     x["lam"] = torch.from_numpy(lam_ref.astype(np.float32))
     t_range = (w.T - 256, w.T)

@@ -1,11 +1,13 @@
 """GPU parity of the level-weight MLP (ll_lambda_mlp) against the oracle, and
 of a prefill whose level weights come from it.
 
-ll_lambda_mlp computes softplus((d W1) W2 + b) per row in fp32 on the matrix
-cores; the oracle computes it in fp64 ("Adaptive memory decay for log-linear
-attention", section "Method").  Tolerance: max|lambda - ref| / max|ref|
-<= 1e-5 (fp32 sums of at most 2 x 64 products of O(1) terms, plus the fp32
-exponential and logarithm of softplus, stay well below it).
+ll_lambda_mlp computes softplus(d (W1 W2) + b) per row in fp32, the composite
+W1 W2 first (no activation lies between the layers), the row product on the
+matrix cores; the oracle computes the two layers as written, softplus((d W1) W2
++ b), in fp64 ("Adaptive memory decay for log-linear attention", section
+"Method").  Tolerance: max|lambda - ref| / max|ref| <= 1e-5 (fp32 sums of at
+most 64 products for the composite and 32 for the row, of O(1) terms, plus the
+fp32 exponential and logarithm of softplus, stay well below it).
 """
 
 import numpy as np
