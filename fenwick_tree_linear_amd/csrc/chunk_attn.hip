@@ -1089,16 +1089,15 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
   // in it is a constant.
   auto run = [&](auto row_group) __attribute__((always_inline)) {
     constexpr int WR = decltype(row_group)::value;
-    // Per item: the first MAXH Fenwick nodes of earlier blocks (most recent
-    // first) as A fragments of this wave's columns, with their level and
-    // decay from their end to the start of block J (as a factor); the decay
-    // factors of the within-block states.  Decays of whole chunks are kept as
-    // running products of the chunks' e^{gate sum}.
+    // Per item: the Fenwick nodes of earlier blocks for bits 0 .. MAXH-1 of
+    // the block index J (slot b holds the node of bit b, at token level
+    // LOGC + 1 + logP + b, when that bit is set) as A fragments of this wave's
+    // columns, with their decay from their end to the start of block J (as a
+    // factor); the decay factors of the within-block states.  Decays of whole
+    // chunks are kept as running products of the chunks' e^{gate sum}.
     Frag hn[MAXH > 0 ? MAXH : 1][KSD];
-    int hlp = 0;  // the held nodes' token levels, five bits each (0: no node)
+    int hJ = 0;  // the block index of the item
     float ehd[MAXH > 0 ? MAXH : 1];
-    static_assert(MAXH * 5 <= 32 && kLevelsMax <= 32, "held levels packed in one word");
-    auto held_level = [&](int x) { return (hlp >> (5 * x)) & 31; };
     int rest_far = 0;  // set bits of J whose nodes are not held in registers
     float dd_far = 0.f;
     int bh = 0;
@@ -1122,33 +1121,30 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
       if (!first_item) read_at.next(a, C);
       first_item = false;
       bh = read_at.bh(a);
-      // The held nodes: one per set bit of J, most recent first.  A slot past
-      // the last set bit repeats the first node and weighs nothing, so that
-      // every node and decay load goes out at once.
+      // The held nodes: the node of set bit b of J covers the blocks from J
+      // with bits below b cleared, back by 2^b; index e = (J >> b << b) - 1.
+      // A slot whose bit is clear loads the node of the lowest set bit again
+      // and weighs nothing, so that every node and decay load goes out at once.
       const int J = read_at.J;
+      hJ = J;
       int ex[MAXH > 0 ? MAXH : 1];
-      rest_far = J;
-      hlp = 0;
 #pragma unroll
-      for (int x = 0; x < MAXH; ++x) {
-        if (rest_far > 0) hlp |= (LOGC + 1 + logP + __ffs(rest_far) - 1) << (5 * x);  // token level of the node
-        ex[x] = rest_far > 0 ? rest_far - 1 : J - 1;
-        rest_far &= rest_far - 1;
-      }
+      for (int b = 0; b < MAXH; ++b) ex[b] = ((J >> b) & 1) ? (J >> b << b) - 1 : J - 1;
+      rest_far = MAXH > 0 ? J >> MAXH << MAXH : J;
       dd_far = 0.f;
 #pragma unroll
-      for (int x = 0; x < MAXH; ++x) ehd[x] = 1.f;
+      for (int b = 0; b < MAXH; ++b) ehd[b] = 1.f;
       if (MAXH > 0 && J > 0) {
         float gm[MAXH > 0 ? MAXH : 1];
 #pragma unroll
-        for (int x = 0; x < MAXH; ++x) {
-          load_node(hn[x], ex[x]);
-          gm[x] = gamma_of(ex[x]);
+        for (int b = 0; b < MAXH; ++b) {
+          load_node(hn[b], ex[b]);
+          gm[b] = gamma_of(ex[b]);
         }
 #pragma unroll
-        for (int x = 0; x < MAXH; ++x) {
-          ehd[x] = __expf(dd_far);
-          dd_far += held_level(x) ? gm[x] : 0.f;
+        for (int b = 0; b < MAXH; ++b) {
+          ehd[b] = __expf(dd_far);
+          dd_far += ((J >> b) & 1) ? gm[b] : 0.f;
         }
       }
 #pragma unroll
@@ -1194,10 +1190,13 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
         for (int s = 0; s < KSD; ++s) qf[i][s] = frag_row<T, C, D>(st + lay.q, r, s, g4);
         lr[i] = lraw + r * LS;
         egr[i] = __expf(gl[r]);
+        // (levels LOGC+1 .. LOGC+logP+MAXH, contiguous in the row; the ones past
+        // the staged levels read the next row's, within LDS, and are never used)
 #pragma unroll
-        for (int m = 1; m <= MAXB; ++m) alw[i][m - 1] = lr[i][min(LOGC + m, LS - 1)] * egr[i];
+        for (int m = 1; m <= MAXB; ++m) alw[i][m - 1] = lr[i][LOGC + m] * egr[i];
+        const float* lrh = lr[i] + LOGC + 1 + logP;
 #pragma unroll
-        for (int x = 0; x < MAXH; ++x) alh[i][x] = lr[i][held_level(x)] * egr[i];
+        for (int b = 0; b < MAXH; ++b) alh[i][b] = lrh[b] * egr[i];
       }
 
       // --- intra-chunk: O^T += V^T P^T
@@ -1265,13 +1264,13 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
       }
       // earlier blocks: one Fenwick node per set bit of J, most recent first
 #pragma unroll
-      for (int x = 0; x < MAXH; ++x) {
-        if (held_level(x)) {
-          const float sc = egw * ehd[x];
+      for (int b = 0; b < MAXH; ++b) {
+        if ((hJ >> b) & 1) {
+          const float sc = egw * ehd[b];
           float al[NRT];
 #pragma unroll
-          for (int i = 0; i < NRT; ++i) al[i] = alh[i][x] * sc;
-          level_read(hn[x], al);
+          for (int i = 0; i < NRT; ++i) al[i] = alh[i][b] * sc;
+          level_read(hn[b], al);
         }
       }
       {
