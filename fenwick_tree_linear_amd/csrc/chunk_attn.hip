@@ -957,36 +957,35 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
 #pragma unroll
           for (int s = 0; s < KSC; ++s) kf[u][s] = frag_col<T, C, D>(kw, 16 * u, s, lane);
         const int c = __ffs(j + 1) - 1;
-        f32x4 merged[DT];
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) merged[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 1; m <= MAXB; ++m) {
-          if (m <= c) {
-            const float sc = __expf(sig[m]);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) merged[dt] += sc * nst[m - 1][dt];
-          }
-        }
-#pragma unroll
-        for (int d0 = 0; d0 < DT; d0 += DG) {
-          lds_wait(vf, kf);
-#pragma unroll
-          for (int u = 0; u < DG; ++u)
-#pragma unroll
-            for (int s = 0; s < KSC; ++s) merged[d0 + u] = M::mma(kf[u][s], vf[s], merged[d0 + u]);
-          if (d0 + DG < DT) {
-#pragma unroll
-            for (int u = 0; u < DG; ++u)
-#pragma unroll
-              for (int s = 0; s < KSC; ++s) kf[u][s] = frag_col<T, C, D>(kw, 16 * (d0 + DG + u), s, lane);
-          }
-        }
+        // Level c+1 is empty (bit c of j is clear): the merged state is formed
+        // in its registers, one copy of this code per level, so that no copy
+        // of the state is made.
 #pragma unroll
         for (int m = 1; m <= MAXB; ++m) {
           if (m == c + 1) {
+            f32x4(&merged)[DT] = nst[m - 1];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) nst[m - 1][dt] = merged[dt];
+            for (int dt = 0; dt < DT; ++dt) merged[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m2 = 1; m2 < m; ++m2) {
+              const float sc = __expf(sig[m2]);
+#pragma unroll
+              for (int dt = 0; dt < DT; ++dt) merged[dt] += sc * nst[m2 - 1][dt];
+            }
+#pragma unroll
+            for (int d0 = 0; d0 < DT; d0 += DG) {
+              lds_wait(vf, kf);
+#pragma unroll
+              for (int u = 0; u < DG; ++u)
+#pragma unroll
+                for (int s = 0; s < KSC; ++s) merged[d0 + u] = M::mma(kf[u][s], vf[s], merged[d0 + u]);
+              if (d0 + DG < DT) {
+#pragma unroll
+                for (int u = 0; u < DG; ++u)
+#pragma unroll
+                  for (int s = 0; s < KSC; ++s) kf[u][s] = frag_col<T, C, D>(kw, 16 * (d0 + DG + u), s, lane);
+              }
+            }
             sig[m] = 0.f;
 #pragma unroll
             for (int s = 0; s < KSD; ++s) *reinterpret_cast<Frag*>(state_frag(m, mw, s)) = M::acc_frag(merged, s);
