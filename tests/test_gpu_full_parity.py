@@ -53,6 +53,20 @@ def test_prefill_16k_every_output():
     assert err <= TOL["bf16"]
 
 
+def test_prefill_32k_far_nodes_every_output():
+    """B1 H8 T32768 d64 bf16, 16 levels, C=64: blocks of 16 chunks (8 heads x 32 blocks keep every
+    CU a block to read), so the block index J runs to 31 and its bit 4, past the four Fenwick
+    nodes the read holds in registers, is read from the workspace at every chunk.  Every output
+    against the oracle's recurrent form."""
+    w = W.Workload("prefill 32k, far nodes", W.MAMBA2, 1, 8, 32768, 64, 64, 16, 64, "bf16", 7)
+    x = W.prefill_inputs(w)
+    o = gpu_prefill(x, w.C, w.L)
+    ref = recurrent_ref(x)
+    err = rel_err(o, ref)
+    say(f"[full] PARITY {w.name}: all {o.size} outputs, rel err {err:.3e} (tol {TOL['bf16']:g})")
+    assert err <= TOL["bf16"]
+
+
 def test_gdn_8k_every_output():
     w = W.WORKLOADS["gdn-8k"]
     x = W.prefill_inputs(w)

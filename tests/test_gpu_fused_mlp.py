@@ -95,3 +95,16 @@ def test_fused_mlp_16k_workload():
     err = rel_err(np32(o_fused)[:, t_range[0]:t_range[1]], ref)
     say(f"[fused mlp] 16K workload: last 256 tokens rel err {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+def test_fused_mlp_32k_far_nodes():
+    """B1 H8 T32768 d64 bf16, 16 levels (the MLP's limit), hidden 2L: the read that makes the
+    weights in blocks of 16 chunks with block indices up to 31 (a Fenwick node past the four held
+    ones), against ll_lambda_mlp + ll_attn_fwd bit for bit."""
+    w = W.Workload("fused mlp 32k", W.MAMBA2, 1, 8, 32768, 64, 64, 16, 64, "bf16", 11)
+    x = W.prefill_inputs(w, parts=("q", "k", "v", "log_gate"))
+    m = W.lambda_mlp_inputs((w.B, w.T, w.H), w.L, seed=w.seed)
+    o_fused, o_two = run_both(w, x, m, F.LL_MAMBA2)
+    say(f"[fused mlp] 32K, 16 levels: equal {torch.equal(o_fused, o_two)}")
+    assert torch.isfinite(o_fused.float()).all()
+    assert torch.equal(o_fused, o_two)
