@@ -855,7 +855,7 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
   // operations, and the row product with the same k steps and accumulators,
   // into the chunk's level-weight rows.  The second row group of readers runs
   // it (row tile rt by reader rt mod NCT of the group), in the middle of their
-  // step, and loads its input.  This lane's fragments of Wc (step s:
+  // step.  This lane's fragments of Wc (step s:
   // Wc[4s + g][c], zero past L) and the bias of level c:
   struct MlpFrags {
     float b[4], bias;
@@ -884,6 +884,43 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (q16 < LS) lr[(16 * rt + 4 * g4 + i) * LS + q16] = softplus_f32(z[i] + f.bias);
+  };
+  // Its input rows (d) go straight into LDS, into a ring of two chunks (chunk
+  // j in slot j % 2), 16 levels a row: instruction u of row tile rt takes rows
+  // 16 rt + 4u .. + 3, lane l row + l / 16, level l % 16 (levels past L are
+  // not loaded).  With four makers, the makers of the last two column tiles
+  // (the lightest step) load them, a chunk at the top of each step for use in
+  // the next (chunk t+3 during step t, landed before the barrier of step t+1);
+  // otherwise each reader of the second row group loads its own tiles, one
+  // chunk ahead of its stage loads.
+  constexpr bool D_BY_MAKERS = NMW >= 4;
+  auto d_owner = [&](int rt) { return D_BY_MAKERS ? NRW + 2 + rt % 2 : NCT + rt % NCT; };
+  auto d_owns = [&]() {
+    bool o = false;
+#pragma unroll
+    for (int rt = 0; rt < CT; ++rt) o = o || wv == d_owner(rt);
+    return o;
+  };
+  ItemWalk dload_at;
+  dload_at.start(item0, a, C);
+  auto issue_d = [&](int j) __attribute__((always_inline)) {
+    if (!MLP || !d_owns()) return;
+    if (j > 0 && (j & (a.P - 1)) == 0) dload_at.next(a, C);
+    const int64_t row0 = dload_at.row + (int64_t)((j & (a.P - 1)) * C * a.H);
+    int l = lane;
+    asm volatile("" : "+v"(l));  // the lane offsets are formed here, not held across the step
+    const uint32_t off = (uint32_t)((((l >> 4) * a.H) * a.L + (l & 15)) * 4);
+#pragma unroll
+    for (int rt = 0; rt < CT; ++rt)
+      if (wv == d_owner(rt)) {
+        const __amdgpu_buffer_rsrc_t r =
+            buffer_rsrc(a.lam + (row0 + (int64_t)16 * rt * a.H) * a.L, (uint32_t)((15 * a.H * a.L + a.L) * 4));
+        char* dst = smem + lay.dr + (j % 2) * C * 16 * 4 + 16 * rt * 64;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if ((l & 15) < a.L)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + u * 256), 4, off, u * 4 * a.H * a.L * 4, 0, 0);
+      }
   };
   auto mlp_share = [&](int j) __attribute__((always_inline)) {
     if (!MLP || wv < NCT || wv >= NRW) return;
@@ -917,9 +954,15 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
       float* w = reinterpret_cast<float*>(smem + lay.mw);
       for (int x = tid - 64 * NRW; x < 16 * 16; x += 64 * NMW) w[x] = mlp_composite(a.w1, a.w2, a.L, a.hidden, x / 16, x % 16);
       if (tid - 64 * NRW < 16) w[16 * 16 + lane] = lane < a.L ? a.mlp_bias[lane] : 0.f;
+      issue_d(0);
+      if (nsteps > 1) issue_d(1);
+      __builtin_amdgcn_s_waitcnt(0);
     }
     lds_barrier();  // the zeroed tiles are visible; the readers' first chunks landed
-    if constexpr (MLP) lds_barrier();  // the readers made the level weights of chunks 0 and 1
+    if constexpr (MLP) {
+      lds_barrier();  // the readers made the level weights of chunks 0 and 1
+      if (nsteps > 2) issue_d(2);
+    }
     prepare(0);
 
     // the within-block Fenwick states of this wave's 16 columns (levels
@@ -928,7 +971,11 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
     float sig[MAXB + 1];
     for (int t = 0; t < nsteps; ++t) {
       const int j = t & (a.P - 1);
+      if constexpr (MLP && D_BY_MAKERS) __builtin_amdgcn_s_waitcnt(0);  // the MLP input of chunk t+2
       lds_barrier();  // step t prepared; the readers' loads of step t+1 landed
+      if constexpr (MLP) {
+        if (t + 3 < nsteps) issue_d(t + 3);  // into the slot of chunk t+1, whose weights are made
+      }
       if (j == 0) {
 #pragma unroll
         for (int m = 0; m < MAXB; ++m)
@@ -1031,33 +1078,6 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
     issue_part(j, 1);
     issue_part(j, 2);
   };
-  // With the MLP: the input rows of the tiles whose level weights this wave
-  // makes (second row group), loaded by the wave itself straight into LDS,
-  // one chunk ahead of its stage loads, into a ring of two chunks (chunk j in
-  // slot j % 2; chunk j is loaded during step j - 3 and used during step
-  // j - 2), 16 levels a row: instruction u of tile rt takes rows
-  // 16 rt + 4u .. + 3, lane l row + l / 16, level l % 16 (levels past L are
-  // not loaded).
-  ItemWalk dload_at = load_at;
-  auto issue_d = [&](int j) __attribute__((always_inline)) {
-    if (!MLP || wv < NCT) return;
-    if (j > 0 && (j & (a.P - 1)) == 0) dload_at.next(a, C);
-    const int64_t row0 = row_in(dload_at, j);
-    int l = lane;
-    asm volatile("" : "+v"(l));  // the lane offsets are formed here, not held across the step
-    const uint32_t off = (uint32_t)((((l >> 4) * a.H) * a.L + (l & 15)) * 4);
-#pragma unroll
-    for (int rt = 0; rt < CT; ++rt)
-      if (rt % NCT == wv - NCT) {
-        const __amdgpu_buffer_rsrc_t r =
-            buffer_rsrc(a.lam + (row0 + (int64_t)16 * rt * a.H) * a.L, (uint32_t)((15 * a.H * a.L + a.L) * 4));
-        char* dst = smem + lay.dr + (j % 2) * C * 16 * 4 + 16 * rt * 64;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if ((l & 15) < a.L)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + u * 256), 4, off, u * 4 * a.H * a.L * 4, 0, 0);
-      }
-  };
   issue(0);
   if constexpr (MLP) {
     issue_d(0);
@@ -1069,7 +1089,7 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
   if constexpr (MLP) {
     mlp_share(0);
     if (nsteps > 1) mlp_share(1);
-    if (nsteps > 2) issue_d(2);  // into the slot of chunk 0, whose weights are made
+    if (!D_BY_MAKERS && nsteps > 2) issue_d(2);  // into the slot of chunk 0, whose weights are made
     lds_barrier();  // the level weights of chunks 0 and 1 are made
   }
   // the first row group's share of preparing chunk j: the scaled keys and
