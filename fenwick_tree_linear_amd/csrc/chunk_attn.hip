@@ -856,7 +856,7 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
   // into the chunk's level-weight rows.  The second row group of readers runs
   // it (row tile rt by reader rt mod NCT of the group), in the middle of their
   // step.  This lane's fragments of Wc (step s:
-  // Wc[4s + g][c], zero past L) and the bias of level c:
+  // Wc[4g + s][c], zero past L) and the bias of level c:
   struct MlpFrags {
     float b[4], bias;
   };
@@ -864,7 +864,7 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
     const float* w = reinterpret_cast<const float*>(smem + lay.mw);
     MlpFrags f;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) f.b[s] = w[(4 * s + g4) * 16 + q16];
+    for (int s = 0; s < 4; ++s) f.b[s] = w[(4 * g4 + s) * 16 + q16];
     f.bias = w[16 * 16 + q16];
     return f;
   };
@@ -874,11 +874,11 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
     int l = lane;
     asm volatile("" : "+v"(l));
     const int g4 = l >> 4, q16 = l & 15;
-    const float* drow = reinterpret_cast<const float*>(smem + lay.dr) + (j % 2) * C * 16 + (16 * rt + q16) * 16 + g4;
-    // (levels past L read the zeros the ring holds there)
-    float bd[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) bd[s] = drow[4 * s];
+    // levels 4 g4 .. + 3 of the row, one 16-byte read (levels past L read the
+    // zeros the ring holds there)
+    const f32x4 dv = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(smem + lay.dr) + (j % 2) * C * 16 +
+                                                     (16 * rt + q16) * 16 + 4 * g4);
+    const float bd[4] = {dv[0], dv[1], dv[2], dv[3]};
     const f32x4 z = mlp_tile_product<4>(bd, f.b);
     float* lr = reinterpret_cast<float*>(stage_of(j) + lay.lraw);
 #pragma unroll

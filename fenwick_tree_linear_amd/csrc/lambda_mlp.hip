@@ -55,12 +55,12 @@ __global__ void __launch_bounds__(64 * kMlpWaves) ll_lambda_mlp(int64_t rows, in
   if (row0 >= rows) return;  // whole waves only; no workgroup barrier below
   const int nel = (rows - row0 < 64 ? (int)(rows - row0) : 64) * L;  // floats of this wave's rows
 
-  // this lane's fragments of Wc: level tile lt, step s gives Wc[4s + g][16lt + c]
+  // this lane's fragments of Wc: level tile lt, step s gives Wc[4 LT g + s][16lt + c]
   float bw[LT][4 * LT];
 #pragma unroll
   for (int lt = 0; lt < LT; ++lt)
 #pragma unroll
-    for (int s = 0; s < 4 * LT; ++s) bw[lt][s] = wc[(4 * s + g) * LP + 16 * lt + c];
+    for (int s = 0; s < 4 * LT; ++s) bw[lt][s] = wc[(4 * LT * g + s) * LP + 16 * lt + c];
   float bvec[LT];
 #pragma unroll
   for (int lt = 0; lt < LT; ++lt) bvec[lt] = 16 * lt + c < L ? bias[16 * lt + c] : 0.f;
@@ -89,11 +89,11 @@ __global__ void __launch_bounds__(64 * kMlpWaves) ll_lambda_mlp(int64_t rows, in
   f32x4 z[4][LT];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    // A operand: lane l = d[16rt + c][4s + g] (zero past L)
-    const float* drow = t + (16 * rt + c) * L + g;
+    // A operand: lane l = d[16rt + c][4 LT g + s] (zero past L)
+    const float* drow = t + (16 * rt + c) * L + 4 * LT * g;
     float a[4 * LT];
 #pragma unroll
-    for (int s = 0; s < 4 * LT; ++s) a[s] = 4 * s + g < L ? drow[4 * s] : 0.f;
+    for (int s = 0; s < 4 * LT; ++s) a[s] = 4 * LT * g + s < L ? drow[s] : 0.f;
 #pragma unroll
     for (int lt = 0; lt < LT; ++lt) z[rt][lt] = mlp_tile_product<4 * LT>(a, bw[lt]);
   }

@@ -127,9 +127,11 @@ __device__ __forceinline__ float mlp_composite(const float* w1, const float* w2,
   return acc;
 }
 // One 16 x 16 tile of z = d Wc on the fp32 matrix cores over KSTEPS k steps of
-// four levels: a[s] = d[row l%16][4s + l/16], b[s] = Wc[4s + l/16][column
-// l%16]; the even and odd steps in two accumulators, then summed (two
-// dependent chains of half the length).  Lane l gets z[4(l/16) + i][l%16].
+// four levels, lane group g = l/16 taking the KSTEPS consecutive levels from
+// KSTEPS g (so that a lane reads its row's levels as one run): a[s] =
+// d[row l%16][KSTEPS g + s], b[s] = Wc[KSTEPS g + s][column l%16]; the even
+// and odd steps in two accumulators, then summed (two dependent chains of half
+// the length).  Lane l gets z[4(l/16) + i][l%16].
 template <int KSTEPS>
 __device__ __forceinline__ f32x4 mlp_tile_product(const float* a, const float* b) {
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
