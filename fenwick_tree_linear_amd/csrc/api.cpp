@@ -415,6 +415,14 @@ ll_status run_core(const Plan& pl, int64_t pos0, const float* state_in, const vo
   a.state = static_cast<float*>(state_out);
   a.state_in = pos0 > 0 ? state_in : nullptr;
   a.pos0 = pos0;
+  const bool read_prior = llattn::read_takes_prior(p->io == LL_BF16 ? 1 : 0, p->dk, pl.Cr, pos0);
+  if (read_prior) {
+    // the read takes the levels of [0, pos0) too: stage up to level bit_length(pos0)
+    int bl = 0;
+    while ((pos0 >> bl) != 0) ++bl;
+    a.prior = state_in;
+    if (a.LS < bl + 1) a.LS = bl + 1 < p->L ? bl + 1 : p->L;
+  }
   if (mlp) {
     a.w1 = mlp->w1;
     a.w2 = mlp->w2;
@@ -451,7 +459,7 @@ ll_status run_core(const Plan& pl, int64_t pos0, const float* state_in, const vo
     e = timed(K_FENWICK_SCAN, stream, [&] { return llattn::launch_fenwick_scan(D, a, stream); });
   if (e == hipSuccess && o)
     e = timed(K_CHUNK_ATTN, stream, [&] { return llattn::launch_chunk_attn(io, D, C, a, stream); });
-  if (e == hipSuccess && o && pos0 > 0)
+  if (e == hipSuccess && o && pos0 > 0 && !read_prior)
     e = timed(K_PRIOR_READ, stream, [&] { return llattn::launch_prior_read(io, D, C, a, stream); });
   if (e == hipSuccess && state_out)
     e = timed(K_STATE_EXPORT, stream, [&] { return llattn::launch_state_export(D, C, a, stream); });

@@ -720,8 +720,9 @@ struct SplitLayout : SplitLds {
   __host__ __device__ explicit SplitLayout(int LS, int mlp_levels = 0) : SplitLds(D, C, MAXB, LS, mlp_levels > 0) {}
 };
 
-template <int D, int C, int MAXB, int MAXH, bool MLP>
+template <int D, int C, int MAXB, int MAXH, bool MLP, bool PRIOR = false>
 __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_split(PrefillArgs a) {
+  static_assert(!(MLP && PRIOR), "the read that makes its level weights starts sequences at position 0");
   typedef bf16 T;
   using M = Mma<T>;
   typedef typename M::Frag Frag;
@@ -1308,6 +1309,34 @@ __global__ void __launch_bounds__((64 * SplitWaves<D, C>::NW)) ll_chunk_attn_spl
           dd += gamma_of(e);
           rest &= rest - 1;
         }
+        // A segment that continues a sequence from the per-level states of
+        // [0, pos0) ("Log-Linear Attention", section 2.2): its tokens also
+        // read the bucket of each set bit b of pos0, at level b + 1, above
+        // every level inside the segment.  The states come in the decode
+        // layout (S_hat row-major, true state e^sigma S_hat, decayed through
+        // token pos0 - 1) and reach the row with the segment's gates before
+        // it: those of the earlier blocks (dd, now all of them), of this
+        // block's earlier chunks and of the row's chunk up to the row.
+        if (PRIOR) {
+          const float* sh = a.prior + (int64_t)bh * a.L * D * D;
+          const float* sgm = a.prior + (int64_t)a.B * a.H * a.L * D * D + (int64_t)bh * a.L;
+          uint64_t bits = (uint64_t)a.pos0;
+          while (bits) {
+            const int lev = __ffsll((unsigned long long)bits);  // bit index + 1
+            bits &= bits - 1;
+            const float* S = sh + (int64_t)lev * D * D + 16 * wc + q16;
+            Frag nf[KSD];
+#pragma unroll
+            for (int s2 = 0; s2 < KSD; ++s2)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) nf[s2][e] = (T)S[M::kidx(s2, g4, e) * D];
+            const float sc = egw * __expf(sgm[lev] + dd);
+            float al[NRT];
+#pragma unroll
+            for (int i = 0; i < NRT; ++i) al[i] = lr[i][lev] * egr[i] * sc;
+            level_read(nf, al);
+          }
+        }
       }
 
       // --- the output rows, stored during the next step
@@ -1402,11 +1431,18 @@ static hipError_t launch_attn_t(const PrefillArgs& a, hipStream_t s) {
       constexpr int MAXB = read_block_depth(1, D, C);
       if (a.P > (1 << MAXB)) return hipErrorInvalidValue;  // planned within the depth
       if (a.w1) {
-        if (a.L > 16 || a.hidden < 1) return hipErrorInvalidValue;  // checked before launch
+        if (a.L > 16 || a.hidden < 1 || a.prior) return hipErrorInvalidValue;  // checked before launch
         static PersistentGrid grid_mlp;
         auto kern = ll_chunk_attn_split<D, C, MAXB, MAXH, true>;
         const SplitLayout<D, C, MAXB> lay(a.LS, a.L);
         return grid_mlp.launch(reinterpret_cast<const void*>(kern), 64 * SplitWaves<D, C>::NW, lay.total, a, s);
+      }
+      if (a.prior) {
+        // a segment continuing a sequence: the read takes the earlier levels too
+        static PersistentGrid grid_prior;
+        auto kern = ll_chunk_attn_split<D, C, MAXB, MAXH, false, true>;
+        const SplitLayout<D, C, MAXB> lay(a.LS);
+        return grid_prior.launch(reinterpret_cast<const void*>(kern), 64 * SplitWaves<D, C>::NW, lay.total, a, s);
       }
       auto kern = ll_chunk_attn_split<D, C, MAXB, MAXH, false>;
       const SplitLayout<D, C, MAXB> lay(a.LS);

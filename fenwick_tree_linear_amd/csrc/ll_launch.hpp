@@ -37,6 +37,10 @@ struct PrefillArgs {
   // segment in the decode layout, and the segment's first position (0: none)
   const float* state_in;
   int64_t pos0;
+  // state_in when the read itself takes the levels of [0, pos0) (the
+  // reader/maker read, with those levels among the staged ones; else NULL and
+  // ll_prior_read adds them after the read)
+  const float* prior = nullptr;
   // The level-weight MLP run inside the read (ll_chunk_attn_split only): when
   // w1 is set, lam holds the MLP's input d [B,T,H,L] instead of the weights,
   // and the read makes lambda = softplus((d W1) W2 + b) per chunk.
@@ -155,6 +159,14 @@ constexpr int max_block_depth(int /*D*/) { return 3; }
 // 2^max_block_depth.
 constexpr bool read_split(int io, int D, int C) { return io == 1 && D <= 64 && C >= 32; }
 constexpr int read_block_depth(int io, int D, int C) { return read_split(io, D, C) ? 4 : max_block_depth(D); }
+// Whether the read takes the levels of [0, pos0) of a segment that continues a
+// sequence itself (the reader/maker read, while levels 0 .. bit_length(pos0)
+// can be staged), so that no ll_prior_read follows it.
+inline bool read_takes_prior(int io, int D, int C, int64_t pos0) {
+  int bl = 0;
+  while (bl < 63 && (pos0 >> bl) != 0) ++bl;
+  return pos0 > 0 && read_split(io, D, C) && bl + 1 <= kLevelsMax;
+}
 // Whether the read runs the level-weight MLP itself (PrefillArgs::w1): bf16 in
 // the run shape, square head D <= 64, chunk C >= 32, L <= 16 (any hidden size:
 // the read applies the composite W1 W2).
