@@ -10,22 +10,35 @@
 //   sum_{j<=t} (k_j . q_t) k_j   = prefill(q, k, v = k),
 // and the running key sum from a chunked prefix sum in fp32: per-chunk column
 // sums (ll_ccq_chunk_sum), their exclusive scan over the chunks of a head
-// (ll_ccq_chunk_scan), and within the chunk a running sum kept by the wave
-// that forms q_clean row by row (ll_ccq_combine).
+// (ll_ccq_chunk_scan), and within the chunk the key sums of its earlier groups
+// of 8 tokens plus a running sum over the group's own (ll_ccq_combine, one
+// wave per group).
 #include "ll_device.hpp"
 #include "ll_launch.hpp"
 
 namespace llattn {
 
-// Fills the inputs of the prefill: level weights 1 and log-gates 0.
-__global__ void __launch_bounds__(256) ll_ccq_fill(int64_t rows, int L, float* ones, float* zeros) {
+// Fills the inputs of the prefill: level weights 1 and log-gates 0.  VEC: the
+// buffers start on 16 bytes and take 4 values per store.
+template <bool VEC>
+__global__ void __launch_bounds__(256) ll_ccq_fill(int64_t n_ones, int64_t n_zeros, float* ones, float* zeros) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows * L; i += stride) ones[i] = 1.f;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows; i += stride) zeros[i] = 0.f;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (VEC) {
+    const float4 one4 = make_float4(1.f, 1.f, 1.f, 1.f), zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t i = i0; i < n_ones / 4; i += stride) reinterpret_cast<float4*>(ones)[i] = one4;
+    for (int64_t i = i0; i < n_zeros / 4; i += stride) reinterpret_cast<float4*>(zeros)[i] = zero4;
+    if (i0 < n_ones % 4) ones[n_ones / 4 * 4 + i0] = 1.f;
+    if (i0 < n_zeros % 4) zeros[n_zeros / 4 * 4 + i0] = 0.f;
+  } else {
+    for (int64_t i = i0; i < n_ones; i += stride) ones[i] = 1.f;
+    for (int64_t i = i0; i < n_zeros; i += stride) zeros[i] = 0.f;
+  }
 }
 
-// One wave per (b, h, chunk of CS tokens): the chunk's column sums of k,
-// csum[b][h][c][x] (fp32).
+// One wave per (b, h, chunk of CS tokens, CS a multiple of 16): the chunk's
+// column sums of k, csum[b][h][c][x] (fp32), 16 rows loaded per round.  Waves
+// go along the heads first (the rows in flight then cover every head).
 template <typename T, int D>
 __global__ void __launch_bounds__(256) ll_ccq_chunk_sum(int B, int T_, int H, int CS, const T* __restrict__ k,
                                                         float* __restrict__ csum) {
@@ -34,125 +47,218 @@ __global__ void __launch_bounds__(256) ll_ccq_chunk_sum(int B, int T_, int H, in
   const int nch = T_ / CS;
   const int64_t item = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   if (item >= (int64_t)B * H * nch) return;
-  const int c = (int)(item % nch);
-  const int bh = (int)(item / nch), h = bh % H, b = bh / H;
+  const int h = (int)(item % H);
+  const int64_t bc = item / H;
+  const int c = (int)(bc % nch), b = (int)(bc / nch);
   const int64_t row0 = ((int64_t)b * T_ + (int64_t)c * CS) * H + h;
+  const int64_t out = ((int64_t)b * H + h) * nch + c;
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int r = 0; r < CS; ++r) {
+  for (int r0 = 0; r0 < CS; r0 += 16) {
+    float kv[16][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int x = lane + 64 * e;
-      if (x < D) acc[e] += to_f32(k[(row0 + (int64_t)r * H) * D + x]);
-    }
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool in = lane * E < D;  // lanes past the last column read column 0 and add 0
+        const float v = to_f32(k[(row0 + (int64_t)(r0 + r) * H) * D + (in ? lane * E + e : 0)]);
+        kv[r][e] = in ? v : 0.f;
+      }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += kv[r][e];
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int x = lane + 64 * e;
-    if (x < D) csum[item * D + x] = acc[e];
+    const int x = lane * E + e;
+    if (x < D) csum[out * D + x] = acc[e];
   }
 }
 
-// One thread per (b, h, column): csum becomes, in place, the exclusive prefix
-// over the chunks of the head (the key sum of the tokens before the chunk).
-__global__ void __launch_bounds__(256) ll_ccq_chunk_scan(int64_t n_bh, int D, int nch, float* __restrict__ csum) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n_bh * D) return;
-  const int64_t bh = i / D;
-  const int x = (int)(i % D);
-  float* p = csum + bh * (int64_t)nch * D + x;
+// csum becomes, in place, the exclusive prefix over the chunks of each head
+// (the key sum of the tokens before the chunk).  One workgroup of 1024 threads
+// per (b, h): thread (s, x) takes column x of the s-th of 1024 / D runs of
+// consecutive chunks; run totals meet in LDS.
+template <int D>
+__global__ void __launch_bounds__(1024) ll_ccq_chunk_scan(int nch, float* __restrict__ csum) {
+  constexpr int S = 1024 / D;
+  __shared__ float tot[S][D];
+  const int x = threadIdx.x % D, s = threadIdx.x / D;
+  const int per = (nch + S - 1) / S;
+  const int c0 = s * per, c1 = min(nch, c0 + per);
+  float* p = csum + (int64_t)blockIdx.x * nch * D + x;
+  float sum = 0.f;
+  int c = c0;
+  for (; c + 16 <= c1; c += 16) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = p[(int64_t)(c + j) * D];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sum += v[j];
+  }
+  for (; c < c1; ++c) sum += p[(int64_t)c * D];
+  tot[s][x] = sum;
+  __syncthreads();
   float run = 0.f;
-  int c = 0;
-  for (; c + 8 <= nch; c += 8) {
-    float v[8];
+  for (int j = 0; j < s; ++j) run += tot[j][x];
+  c = c0;
+  for (; c + 16 <= c1; c += 16) {
+    float v[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = p[(int64_t)(c + j) * D];
+    for (int j = 0; j < 16; ++j) v[j] = p[(int64_t)(c + j) * D];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 16; ++j) {
       p[(int64_t)(c + j) * D] = run;
       run += v[j];
     }
   }
-  for (; c < nch; ++c) {
+  for (; c < c1; ++c) {
     const float v = p[(int64_t)c * D];
     p[(int64_t)c * D] = run;
     run += v;
   }
 }
 
-// One wave per (b, h, chunk): walks the chunk's tokens t in order, keeping
-// the running key sum (the chunk's exclusive prefix plus the tokens so far);
-// per token mu = ksum / (t+1), Sigma q = kkq / (t+1) - mu (mu . q),
-// gamma = sigmoid(w_h . q + b_h).
+// Sums v[r] (r = 0..G-1, G a power of two up to 64) over the 64 lanes of the
+// wave, halving the vector at each exchange (lanes with bit 5, 4, ... set keep
+// the upper half): lane l ends with the total of v[l >> (6 - log2 G)].  Both
+// halves are exchanged and the kept one chosen after the adds (a choice
+// between two array slots would become an indexed read of the array).
+template <int G>
+__device__ __forceinline__ float wave_sum_rows(const float (&v)[G], int lane) {
+  float a[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) a[i] = v[i];
+  int m = 32;
+#pragma unroll
+  for (int n = G; n > 1; n >>= 1, m >>= 1) {
+    const bool up = lane & m;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+      const float lo = a[i] + __shfl_xor(a[i], m, 64), hi = a[n / 2 + i] + __shfl_xor(a[n / 2 + i], m, 64);
+      a[i] = up ? hi : lo;
+    }
+  }
+#pragma unroll
+  for (; m >= 1; m >>= 1) a[0] += __shfl_xor(a[0], m, 64);
+  return a[0];
+}
+
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Tokens per wave of ll_ccq_combine (and their log2), waves per workgroup
+// (a workgroup holds whole chunks of up to 64 tokens).
+constexpr int kCombineLG = 3, kCombineG = 1 << kCombineLG, kCombineNW = 8;
+static_assert(64 / kCombineG <= kCombineNW, "a chunk of 64 tokens must fit one workgroup");
+
+// One wave per 8 tokens of a chunk (a chunk has 2, 4 or 8 such groups); a
+// workgroup of 8 waves holds the same chunk of 8 / (CS / 8) heads, and consecutive
+// workgroups go along the heads first, so that the waves in flight read rows
+// of every head ([B, T, H, D] puts a token's heads side by side; one head's
+// rows alone, 128 bytes every H * D elements, leave most HBM channels idle).  Lane l holds columns
+// l*E .. l*E+E-1.  Per token t: the running key sum (the chunk's exclusive
+// prefix, the key sums of the chunk's earlier groups from LDS, and the
+// group's tokens so far), mu = ksum / (t+1), Sigma q = kkq / (t+1) - mu (mu . q),
+// gamma = sigmoid(w_h . q + b_h).  The two dot products of the 8 tokens are
+// summed over the lanes together (wave_sum_rows), one token per 8 lanes, and
+// taken back from those lanes as wave-uniform values.
 template <typename T, int D>
-__global__ void __launch_bounds__(256) ll_ccq_combine(int B, int T_, int H, int CS, const T* __restrict__ q,
+__global__ void __launch_bounds__(64 * kCombineNW) ll_ccq_combine(int B, int T_, int H, int CS, const T* __restrict__ q,
                                                       const T* __restrict__ k, const T* __restrict__ kkq,
                                                       const float* __restrict__ csum, const float* __restrict__ w,
                                                       const float* __restrict__ b_, T* __restrict__ q_clean) {
-  constexpr int E = (D + 63) / 64;  // elements per lane
-  constexpr int RB = 8;             // rows loaded ahead
-  const int lane = threadIdx.x & 63;
-  const int nch = T_ / CS;
-  const int64_t item = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-  if (item >= (int64_t)B * H * nch) return;
-  const int c = (int)(item % nch);
-  const int bh = (int)(item / nch), h = bh % H, b = bh / H;
-  const int64_t row0 = ((int64_t)b * T_ + (int64_t)c * CS) * H + h;
-  float run[E], wv[E];
+  constexpr int E = (D + 63) / 64;
+  constexpr int G = kCombineG, NW = kCombineNW, LG = kCombineLG;
+  __shared__ float gsum[NW][64 * E];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int gpc = CS / G, nch = T_ / CS, hpw = NW / gpc;
+  const int nhb = (H + hpw - 1) / hpw;
+  const unsigned blk = blockIdx.x, bc = blk / (unsigned)nhb;
+  const int hb = (int)(blk % (unsigned)nhb);
+  const int c = (int)(bc % (unsigned)nch), bb = (int)(bc / (unsigned)nch);
+  const int sub = wv % gpc, hw = hb * hpw + wv / gpc;
+  const bool live = hw < H;
+  const int h = live ? hw : 0;
+  const int64_t chunk = ((int64_t)bb * H + h) * nch + c;
+  const int t0 = c * CS + sub * G;
+  const int64_t row0 = ((int64_t)bb * T_ + t0) * H + h;
+  // Every load is in bounds (a wave past the last head reads head 0, a lane
+  // past the last column reads column 0), so that none waits behind a branch;
+  // lanes past the last column then take zeros, and such waves store nothing.
+  const bool lane_in = lane * E < D;
+  const int xl = lane_in ? lane * E : 0;
+  float qv[G][E], kv[G][E], kq[G][E];
+#pragma unroll
+  for (int r = 0; r < G; ++r)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int64_t o = (row0 + (int64_t)r * H) * D + xl + e;
+      const float a = to_f32(q[o]), b = to_f32(k[o]), z = to_f32(kkq[o]);
+      qv[r][e] = lane_in ? a : 0.f;
+      kv[r][e] = lane_in ? b : 0.f;
+      kq[r][e] = lane_in ? z : 0.f;
+    }
+  float run[E], wx[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int x = lane + 64 * e;
-    run[e] = x < D ? csum[item * D + x] : 0.f;
-    wv[e] = x < D ? w[(int64_t)h * D + x] : 0.f;
+    const float a = csum[chunk * D + xl + e], b = w[(int64_t)h * D + xl + e];
+    run[e] = lane_in ? a : 0.f;
+    wx[e] = lane_in ? b : 0.f;
+    float g = 0.f;
+#pragma unroll
+    for (int r = 0; r < G; ++r) g += kv[r][e];
+    gsum[wv][lane * E + e] = g;
   }
-  const float bias = b_[h];
-  for (int r0 = 0; r0 < CS; r0 += RB) {
-    float qv[RB][E], kv[RB][E], kq[RB][E];
+  __syncthreads();
+  for (int s = 0; s < sub; ++s)
 #pragma unroll
-    for (int j = 0; j < RB; ++j)
+    for (int e = 0; e < E; ++e) run[e] += gsum[wv - sub + s][lane * E + e];
+  // The bias joins lane 0's share of w . q, so that its load goes out with
+  // the others rather than after the sums over the lanes.
+  const float bh_ = b_[h];
+  const float bias = lane == 0 ? bh_ : 0.f;
+  float mq[G], wq[G], run0[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int x = lane + 64 * e;
-        const int64_t o = (row0 + (int64_t)(r0 + j) * H) * D + x;
-        const bool in = x < D && r0 + j < CS;
-        qv[j][e] = in ? to_f32(q[o]) : 0.f;
-        kv[j][e] = in ? to_f32(k[o]) : 0.f;
-        kq[j][e] = in ? to_f32(kkq[o]) : 0.f;
-      }
+  for (int e = 0; e < E; ++e) run0[e] = run[e];
 #pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      if (r0 + j >= CS) break;
-      const int t = c * CS + r0 + j;
-      const float inv = 1.f / (float)(t + 1);
-      float mq = 0.f, wq = 0.f, mu[E];
+  for (int r = 0; r < G; ++r) {
+    const float inv = 1.f / (float)(t0 + r + 1);
+    mq[r] = 0.f;
+    wq[r] = bias;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        run[e] += kv[j][e];
-        mu[e] = run[e] * inv;
-        mq += mu[e] * qv[j][e];
-        wq += wv[e] * qv[j][e];
-      }
+    for (int e = 0; e < E; ++e) {
+      run[e] += kv[r][e];
+      mq[r] += run[e] * inv * qv[r][e];
+      wq[r] += wx[e] * qv[r][e];
+    }
+  }
+  const float mq_l = wave_sum_rows<G>(mq, lane);
+  const float gamma_l = 1.f / (1.f + __expf(-wave_sum_rows<G>(wq, lane)));
+  if (!live) return;
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        mq += __shfl_xor(mq, m, 64);
-        wq += __shfl_xor(wq, m, 64);
-      }
-      const float gamma = 1.f / (1.f + __expf(-(wq + bias)));
+  for (int r = 0; r < G; ++r) {
+    const float inv = 1.f / (float)(t0 + r + 1);
+    const float m = lane_value(mq_l, r << (6 - LG)), g = lane_value(gamma_l, r << (6 - LG));
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int x = lane + 64 * e;
-        if (x < D)
-          q_clean[(row0 + (int64_t)(r0 + j) * H) * D + x] = from_f32<T>(qv[j][e] - gamma * (kq[j][e] * inv - mu[e] * mq));
-      }
+    for (int e = 0; e < E; ++e) {
+      const int x = lane * E + e;
+      run0[e] += kv[r][e];  // the running key sum again, as in the first pass
+      if (x < D) q_clean[(row0 + (int64_t)r * H) * D + x] = from_f32<T>(qv[r][e] - g * (kq[r][e] * inv - run0[e] * inv * m));
     }
   }
 }
 
 hipError_t launch_ccq_fill(int64_t rows, int L, float* ones, float* zeros, hipStream_t s) {
   const int64_t n = rows * L;
-  const int grid = (int)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
-  hipLaunchKernelGGL(ll_ccq_fill, dim3(grid), dim3(256), 0, s, rows, L, ones, zeros);
+  const int grid = (int)((n / 4 + 255) / 256 < 8192 ? (n / 4 + 255) / 256 + 1 : 8192);
+  if ((reinterpret_cast<uintptr_t>(ones) | reinterpret_cast<uintptr_t>(zeros)) % 16 == 0)
+    hipLaunchKernelGGL(ll_ccq_fill<true>, dim3(grid), dim3(256), 0, s, n, rows, ones, zeros);
+  else
+    hipLaunchKernelGGL(ll_ccq_fill<false>, dim3(grid), dim3(256), 0, s, n, rows, ones, zeros);
   return hipGetLastError();
 }
 
@@ -162,17 +268,16 @@ static hipError_t launch_ksum_t(int B, int T_, int H, int CS, const void* k, flo
   hipLaunchKernelGGL((ll_ccq_chunk_sum<T, D>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, B, T_, H, CS,
                      static_cast<const T*>(k), csum);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  const int64_t n = (int64_t)B * H * D;
-  hipLaunchKernelGGL(ll_ccq_chunk_scan, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (int64_t)B * H, D,
-                     T_ / CS, csum);
+  hipLaunchKernelGGL(ll_ccq_chunk_scan<D>, dim3((unsigned)(B * H)), dim3(1024), 0, s, T_ / CS, csum);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t launch_combine_t(int B, int T_, int H, int CS, const void* q, const void* k, const void* kkq,
                                    const float* csum, const float* w, const float* b, void* qc, hipStream_t s) {
-  const int64_t items = (int64_t)B * H * (T_ / CS);
-  hipLaunchKernelGGL((ll_ccq_combine<T, D>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, B, T_, H, CS,
+  const int hpw = kCombineNW / (CS / kCombineG);
+  const int64_t blocks = (int64_t)B * (T_ / CS) * ((H + hpw - 1) / hpw);
+  hipLaunchKernelGGL((ll_ccq_combine<T, D>), dim3((unsigned)blocks), dim3(64 * kCombineNW), 0, s, B, T_, H, CS,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(kkq), csum, w, b,
                      static_cast<T*>(qc));
   return hipGetLastError();
