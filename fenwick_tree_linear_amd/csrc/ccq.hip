@@ -146,6 +146,33 @@ __device__ __forceinline__ float wave_sum_rows(const float (&v)[G], int lane) {
   return a[0];
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // a 16-byte piece of a row
+
+// Orders the wave's LDS accesses around it: what a lane wrote before is seen
+// by the other lanes of the wave after (a wave's LDS operations run in order;
+// this waits for them and keeps the compiler from moving memory accesses
+// across, without waiting for the wave's global loads in flight).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// 16-byte pieces of a G x D tile (one per lane and step, the last piece
+// again past the end) through the wave's LDS tile into one column per lane:
+// out[r][e] = tile[r][xl + e], or 0 on lanes past the last column.
+template <typename T, int D, int G, int E, int NL, int CPW>
+__device__ __forceinline__ void stage_columns(const u32x4 (&rr)[NL], u32x4* tw, const T* tile, int lane, int xl,
+                                              bool lane_in, float (&out)[G][E]) {
+#pragma unroll
+  for (int i = 0; i < NL; ++i) tw[min(lane + 64 * i, CPW - 1)] = rr[i];
+  wave_lds_sync();
+#pragma unroll
+  for (int r = 0; r < G; ++r)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float v = to_f32(tile[r * D + xl + e]);
+      out[r][e] = lane_in ? v : 0.f;
+    }
+  wave_lds_sync();
+}
+
 __device__ __forceinline__ float lane_value(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
@@ -163,7 +190,8 @@ static_assert(64 / kCombineG <= kCombineNW, "a chunk of 64 tokens must fit one w
 // l*E .. l*E+E-1.  Per token t: the running key sum (the chunk's exclusive
 // prefix, the key sums of the chunk's earlier groups from LDS, and the
 // group's tokens so far), mu = ksum / (t+1), Sigma q = kkq / (t+1) - mu (mu . q),
-// gamma = sigmoid(w_h . q + b_h).  The two dot products of the 8 tokens are
+// gamma = sigmoid(w_h . q + b_h).  Rows are read and written in 16-byte
+// pieces through an LDS tile per wave.  The two dot products of the 8 tokens are
 // summed over the lanes together (wave_sum_rows), one token per 8 lanes, and
 // taken back from those lanes as wave-uniform values.
 template <typename T, int D>
@@ -173,7 +201,10 @@ __global__ void __launch_bounds__(64 * kCombineNW) ll_ccq_combine(int B, int T_,
                                                       const float* __restrict__ b_, T* __restrict__ q_clean) {
   constexpr int E = (D + 63) / 64;
   constexpr int G = kCombineG, NW = kCombineNW, LG = kCombineLG;
+  constexpr int VW = 16 / (int)sizeof(T), LPR = D / VW, CPW = G * LPR, NL = (CPW + 63) / 64;
+  static_assert(D % VW == 0 && 64 % LPR == 0, "a row is a whole number of 16-byte pieces");
   __shared__ float gsum[NW][64 * E];
+  __shared__ __align__(16) T tile[NW][G * D];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int gpc = CS / G, nch = T_ / CS, hpw = NW / gpc;
   const int nhb = (H + hpw - 1) / hpw;
@@ -186,22 +217,29 @@ __global__ void __launch_bounds__(64 * kCombineNW) ll_ccq_combine(int B, int T_,
   const int64_t chunk = ((int64_t)bb * H + h) * nch + c;
   const int t0 = c * CS + sub * G;
   const int64_t row0 = ((int64_t)bb * T_ + t0) * H + h;
-  // Every load is in bounds (a wave past the last head reads head 0, a lane
-  // past the last column reads column 0), so that none waits behind a branch;
-  // lanes past the last column then take zeros, and such waves store nothing.
+  // The group's rows of q, k and kkq come in 16-byte pieces (piece p: row
+  // p / LPR, elements VW * (p % LPR) onward; a lane past the last piece takes
+  // the last one again) and are turned to one column per lane through the
+  // wave's LDS tile.  Every load is in bounds (a wave past the last head reads
+  // head 0, a lane past the last column reads column 0), so that none waits
+  // behind a branch; lanes past the last column then take zeros, and such
+  // waves store nothing.
   const bool lane_in = lane * E < D;
   const int xl = lane_in ? lane * E : 0;
+  u32x4 rq[NL], rk[NL], rz[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int pc = min(lane + 64 * i, CPW - 1);
+    const int64_t o = (row0 + (int64_t)(pc / LPR) * H) * D + (pc % LPR) * VW;
+    rq[i] = *reinterpret_cast<const u32x4*>(q + o);
+    rk[i] = *reinterpret_cast<const u32x4*>(k + o);
+    rz[i] = *reinterpret_cast<const u32x4*>(kkq + o);
+  }
+  u32x4* tw = reinterpret_cast<u32x4*>(&tile[wv][0]);
   float qv[G][E], kv[G][E], kq[G][E];
-#pragma unroll
-  for (int r = 0; r < G; ++r)
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int64_t o = (row0 + (int64_t)r * H) * D + xl + e;
-      const float a = to_f32(q[o]), b = to_f32(k[o]), z = to_f32(kkq[o]);
-      qv[r][e] = lane_in ? a : 0.f;
-      kv[r][e] = lane_in ? b : 0.f;
-      kq[r][e] = lane_in ? z : 0.f;
-    }
+  stage_columns<T, D, G, E, NL, CPW>(rq, tw, &tile[wv][0], lane, xl, lane_in, qv);
+  stage_columns<T, D, G, E, NL, CPW>(rk, tw, &tile[wv][0], lane, xl, lane_in, kv);
+  stage_columns<T, D, G, E, NL, CPW>(rz, tw, &tile[wv][0], lane, xl, lane_in, kq);
   float run[E], wx[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -245,10 +283,15 @@ __global__ void __launch_bounds__(64 * kCombineNW) ll_ccq_combine(int B, int T_,
     const float m = lane_value(mq_l, r << (6 - LG)), g = lane_value(gamma_l, r << (6 - LG));
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int x = lane * E + e;
       run0[e] += kv[r][e];  // the running key sum again, as in the first pass
-      if (x < D) q_clean[(row0 + (int64_t)r * H) * D + x] = from_f32<T>(qv[r][e] - g * (kq[r][e] * inv - run0[e] * inv * m));
+      if (lane_in) tile[wv][r * D + xl + e] = from_f32<T>(qv[r][e] - g * (kq[r][e] * inv - run0[e] * inv * m));
     }
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int pc = min(lane + 64 * i, CPW - 1);
+    *reinterpret_cast<u32x4*>(q_clean + (row0 + (int64_t)(pc / LPR) * H) * D + (pc % LPR) * VW) = tw[pc];
   }
 }
 
