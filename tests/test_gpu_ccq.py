@@ -76,3 +76,21 @@ def test_prefill_reads_with_the_contracted_query(io, d, C):
     err = rel_err(o, oracle_prefill(xr))
     say(f"[ccq] prefill {io} d{d} with contracted queries: rel err {err:.3e} (tol {TOL[io]:g})")
     assert err <= TOL[io]
+
+
+def test_ccq_16k_every_output():
+    """The 16K workload the benchmark times (B2 H16 T16384 d64 bf16, chunks of
+    64; the all-ones prefill then has 15 levels): every output against the
+    oracle, which runs the whole batch from its fp64 running sums."""
+    w = W.WORKLOADS["prefill-16k"]
+    x = W.prefill_inputs(w)
+    g = W.ccq_inputs(w.H, w.dk, seed=w.seed)
+    dev, gd = to_dev(x), to_dev(g)
+    qc = np32(F.ccq_query(dev["q"], dev["k"], gd["w"], gd["b"]))
+    torch.cuda.synchronize()
+    ref = oracle.ccq_query(np32(x["q"]), np32(x["k"]), np32(g["w"]), np32(g["b"]))
+    err = rel_err(qc, ref)
+    moved = rel_err(np32(x["q"]), ref)
+    say(f"[ccq] 16K workload, every output: rel err {err:.3e} (tol {TOL['bf16']:g}); contraction moves q by "
+        f"{moved:.2e}")
+    assert err <= TOL["bf16"]
