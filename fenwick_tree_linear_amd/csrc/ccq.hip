@@ -18,6 +18,40 @@
 
 namespace llattn {
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // a 16-byte piece of a row
+
+// The values of a 16-byte piece: 8 bf16 (element 2i in the low half of word
+// i) or 4 fp32.
+template <typename T>
+__device__ __forceinline__ void unpack_piece(u32x4 v, float (&f)[16 / sizeof(T)]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(v[i] << 16);
+      f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+  }
+}
+
+// A 16-byte piece from its values (bf16: rounded to nearest even).
+template <typename T>
+__device__ __forceinline__ u32x4 pack_piece(const float (&f)[16 / sizeof(T)]) {
+  u32x4 v;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = (unsigned)__builtin_bit_cast(unsigned short, (bf16)f[2 * i]) |
+             ((unsigned)__builtin_bit_cast(unsigned short, (bf16)f[2 * i + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
+  }
+  return v;
+}
+
 // Fills the inputs of the prefill: level weights 1 and log-gates 0.  VEC: the
 // buffers start on 16 bytes and take 4 values per store.
 template <bool VEC>
@@ -121,90 +155,34 @@ __global__ void __launch_bounds__(1024) ll_ccq_chunk_scan(int nch, float* __rest
   }
 }
 
-// Sums v[r] (r = 0..G-1, G a power of two up to 64) over the 64 lanes of the
-// wave, halving the vector at each exchange (lanes with bit 5, 4, ... set keep
-// the upper half): lane l ends with the total of v[l >> (6 - log2 G)].  Both
-// halves are exchanged and the kept one chosen after the adds (a choice
-// between two array slots would become an indexed read of the array).
-template <int G>
-__device__ __forceinline__ float wave_sum_rows(const float (&v)[G], int lane) {
-  float a[G];
-#pragma unroll
-  for (int i = 0; i < G; ++i) a[i] = v[i];
-  int m = 32;
-#pragma unroll
-  for (int n = G; n > 1; n >>= 1, m >>= 1) {
-    const bool up = lane & m;
-#pragma unroll
-    for (int i = 0; i < n / 2; ++i) {
-      const float lo = a[i] + __shfl_xor(a[i], m, 64), hi = a[n / 2 + i] + __shfl_xor(a[n / 2 + i], m, 64);
-      a[i] = up ? hi : lo;
-    }
-  }
-#pragma unroll
-  for (; m >= 1; m >>= 1) a[0] += __shfl_xor(a[0], m, 64);
-  return a[0];
-}
-
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // a 16-byte piece of a row
-
-// Orders the wave's LDS accesses around it: what a lane wrote before is seen
-// by the other lanes of the wave after (a wave's LDS operations run in order;
-// this waits for them and keeps the compiler from moving memory accesses
-// across, without waiting for the wave's global loads in flight).
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// 16-byte pieces of a G x D tile (one per lane and step, the last piece
-// again past the end) through the wave's LDS tile into one column per lane:
-// out[r][e] = tile[r][xl + e], or 0 on lanes past the last column.
-template <typename T, int D, int G, int E, int NL, int CPW>
-__device__ __forceinline__ void stage_columns(const u32x4 (&rr)[NL], u32x4* tw, const T* tile, int lane, int xl,
-                                              bool lane_in, float (&out)[G][E]) {
-#pragma unroll
-  for (int i = 0; i < NL; ++i) tw[min(lane + 64 * i, CPW - 1)] = rr[i];
-  wave_lds_sync();
-#pragma unroll
-  for (int r = 0; r < G; ++r)
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float v = to_f32(tile[r * D + xl + e]);
-      out[r][e] = lane_in ? v : 0.f;
-    }
-  wave_lds_sync();
-}
-
-__device__ __forceinline__ float lane_value(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
-// Tokens per wave of ll_ccq_combine (and their log2), waves per workgroup
-// (a workgroup holds whole chunks of up to 64 tokens).
-constexpr int kCombineLG = 3, kCombineG = 1 << kCombineLG, kCombineNW = 8;
+// Tokens per wave of ll_ccq_combine and waves per workgroup (a workgroup
+// holds whole chunks of up to 64 tokens).
+constexpr int kCombineG = 8, kCombineNW = 8;
 static_assert(64 / kCombineG <= kCombineNW, "a chunk of 64 tokens must fit one workgroup");
 
 // One wave per 8 tokens of a chunk (a chunk has 2, 4 or 8 such groups); a
-// workgroup of 8 waves holds the same chunk of 8 / (CS / 8) heads, and consecutive
-// workgroups go along the heads first, so that the waves in flight read rows
-// of every head ([B, T, H, D] puts a token's heads side by side; one head's
-// rows alone, 128 bytes every H * D elements, leave most HBM channels idle).  Lane l holds columns
-// l*E .. l*E+E-1.  Per token t: the running key sum (the chunk's exclusive
-// prefix, the key sums of the chunk's earlier groups from LDS, and the
-// group's tokens so far), mu = ksum / (t+1), Sigma q = kkq / (t+1) - mu (mu . q),
-// gamma = sigmoid(w_h . q + b_h).  Rows are read and written in 16-byte
-// pieces through an LDS tile per wave.  The two dot products of the 8 tokens are
-// summed over the lanes together (wave_sum_rows), one token per 8 lanes, and
-// taken back from those lanes as wave-uniform values.
+// workgroup of 8 waves holds the same chunk of 8 / (CS / 8) heads, and
+// consecutive workgroups go along the heads first, so that the waves in flight
+// read rows of every head ([B, T, H, D] puts a token's heads side by side; one
+// head's rows alone, 128 bytes every H * D elements, leave most HBM channels
+// idle).  Rows come whole in 16-byte pieces: lane l holds piece l % LPR (VW
+// elements) of row l / LPR of each load.  Per token t: the running key sum
+// (the chunk's exclusive prefix, the key sums of the chunk's earlier groups
+// from LDS, the earlier rows of the group by a scan over the lanes),
+// mu = ksum / (t+1), Sigma q = kkq / (t+1) - mu (mu . q), gamma =
+// sigmoid(w_h . q + b_h); the two dot products are summed over the LPR lanes
+// of the row.
 template <typename T, int D>
 __global__ void __launch_bounds__(64 * kCombineNW) ll_ccq_combine(int B, int T_, int H, int CS, const T* __restrict__ q,
                                                       const T* __restrict__ k, const T* __restrict__ kkq,
                                                       const float* __restrict__ csum, const float* __restrict__ w,
                                                       const float* __restrict__ b_, T* __restrict__ q_clean) {
-  constexpr int E = (D + 63) / 64;
-  constexpr int G = kCombineG, NW = kCombineNW, LG = kCombineLG;
-  constexpr int VW = 16 / (int)sizeof(T), LPR = D / VW, CPW = G * LPR, NL = (CPW + 63) / 64;
-  static_assert(D % VW == 0 && 64 % LPR == 0, "a row is a whole number of 16-byte pieces");
-  __shared__ float gsum[NW][64 * E];
-  __shared__ __align__(16) T tile[NW][G * D];
+  constexpr int G = kCombineG, NW = kCombineNW;
+  constexpr int VW = 16 / (int)sizeof(T), LPR = D / VW, RW = 64 / LPR;
+  constexpr int RL = RW < G ? RW : G;  // rows per load
+  constexpr int NL = G / RL;           // loads per tensor
+  static_assert(D % VW == 0 && 64 % LPR == 0 && G % RL == 0, "a row is a whole number of 16-byte pieces");
+  __shared__ float gsum[NW][D];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int gpc = CS / G, nch = T_ / CS, hpw = NW / gpc;
   const int nhb = (H + hpw - 1) / hpw;
@@ -217,81 +195,86 @@ __global__ void __launch_bounds__(64 * kCombineNW) ll_ccq_combine(int B, int T_,
   const int64_t chunk = ((int64_t)bb * H + h) * nch + c;
   const int t0 = c * CS + sub * G;
   const int64_t row0 = ((int64_t)bb * T_ + t0) * H + h;
-  // The group's rows of q, k and kkq come in 16-byte pieces (piece p: row
-  // p / LPR, elements VW * (p % LPR) onward; a lane past the last piece takes
-  // the last one again) and are turned to one column per lane through the
-  // wave's LDS tile.  Every load is in bounds (a wave past the last head reads
-  // head 0, a lane past the last column reads column 0), so that none waits
-  // behind a branch; lanes past the last column then take zeros, and such
-  // waves store nothing.
-  const bool lane_in = lane * E < D;
-  const int xl = lane_in ? lane * E : 0;
+  const int cp = lane % LPR, rl = lane / LPR;
+  // Every load is in bounds (a wave past the last head reads head 0, a lane
+  // past the last row of a load reads that row again), so that none waits
+  // behind a branch; such lanes and waves store nothing.
+  const bool lane_in = rl < RL;
+  const int rlc = lane_in ? rl : RL - 1;
   u32x4 rq[NL], rk[NL], rz[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const int pc = min(lane + 64 * i, CPW - 1);
-    const int64_t o = (row0 + (int64_t)(pc / LPR) * H) * D + (pc % LPR) * VW;
+    const int64_t o = (row0 + (int64_t)(i * RL + rlc) * H) * D + cp * VW;
     rq[i] = *reinterpret_cast<const u32x4*>(q + o);
     rk[i] = *reinterpret_cast<const u32x4*>(k + o);
     rz[i] = *reinterpret_cast<const u32x4*>(kkq + o);
   }
-  u32x4* tw = reinterpret_cast<u32x4*>(&tile[wv][0]);
-  float qv[G][E], kv[G][E], kq[G][E];
-  stage_columns<T, D, G, E, NL, CPW>(rq, tw, &tile[wv][0], lane, xl, lane_in, qv);
-  stage_columns<T, D, G, E, NL, CPW>(rk, tw, &tile[wv][0], lane, xl, lane_in, kv);
-  stage_columns<T, D, G, E, NL, CPW>(rz, tw, &tile[wv][0], lane, xl, lane_in, kq);
-  float run[E], wx[E];
+  float pre[VW], wx[VW];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const float a = csum[chunk * D + xl + e], b = w[(int64_t)h * D + xl + e];
-    run[e] = lane_in ? a : 0.f;
-    wx[e] = lane_in ? b : 0.f;
-    float g = 0.f;
-#pragma unroll
-    for (int r = 0; r < G; ++r) g += kv[r][e];
-    gsum[wv][lane * E + e] = g;
+  for (int e = 0; e < VW; ++e) {
+    pre[e] = csum[chunk * D + cp * VW + e];
+    wx[e] = w[(int64_t)h * D + cp * VW + e];
   }
-  __syncthreads();
-  for (int s = 0; s < sub; ++s)
+  const float bias = b_[h];
+  // k summed over the rows of each load up to the lane's own (a scan over the
+  // lanes, RL / 2, ..., 1 rows apart), and each load's total from its last row
+  float kc[NL][VW], gt[VW];
 #pragma unroll
-    for (int e = 0; e < E; ++e) run[e] += gsum[wv - sub + s][lane * E + e];
-  // The bias joins lane 0's share of w . q, so that its load goes out with
-  // the others rather than after the sums over the lanes.
-  const float bh_ = b_[h];
-  const float bias = lane == 0 ? bh_ : 0.f;
-  float mq[G], wq[G], run0[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) run0[e] = run[e];
-#pragma unroll
-  for (int r = 0; r < G; ++r) {
-    const float inv = 1.f / (float)(t0 + r + 1);
-    mq[r] = 0.f;
-    wq[r] = bias;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      run[e] += kv[r][e];
-      mq[r] += run[e] * inv * qv[r][e];
-      wq[r] += wx[e] * qv[r][e];
-    }
-  }
-  const float mq_l = wave_sum_rows<G>(mq, lane);
-  const float gamma_l = 1.f / (1.f + __expf(-wave_sum_rows<G>(wq, lane)));
-  if (!live) return;
-#pragma unroll
-  for (int r = 0; r < G; ++r) {
-    const float inv = 1.f / (float)(t0 + r + 1);
-    const float m = lane_value(mq_l, r << (6 - LG)), g = lane_value(gamma_l, r << (6 - LG));
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      run0[e] += kv[r][e];  // the running key sum again, as in the first pass
-      if (lane_in) tile[wv][r * D + xl + e] = from_f32<T>(qv[r][e] - g * (kq[r][e] * inv - run0[e] * inv * m));
-    }
-  }
-  wave_lds_sync();
+  for (int e = 0; e < VW; ++e) gt[e] = 0.f;
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const int pc = min(lane + 64 * i, CPW - 1);
-    *reinterpret_cast<u32x4*>(q_clean + (row0 + (int64_t)(pc / LPR) * H) * D + (pc % LPR) * VW) = tw[pc];
+    unpack_piece<T>(rk[i], kc[i]);
+#pragma unroll
+    for (int s = 1; s < RL; s <<= 1)
+#pragma unroll
+      for (int e = 0; e < VW; ++e) {
+        const float up = __shfl_up(kc[i][e], s * LPR, 64);
+        kc[i][e] = rl >= s ? kc[i][e] + up : kc[i][e];
+      }
+  }
+  float base[NL][VW];  // key sum of the group's rows before load i
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+#pragma unroll
+    for (int e = 0; e < VW; ++e) {
+      base[i][e] = gt[e];
+      gt[e] += __shfl(kc[i][e], (RL - 1) * LPR + cp, 64);
+    }
+  if (rl == 0)
+#pragma unroll
+    for (int e = 0; e < VW; ++e) gsum[wv][cp * VW + e] = gt[e];
+  __syncthreads();
+  float run0[VW];
+#pragma unroll
+  for (int e = 0; e < VW; ++e) run0[e] = pre[e];
+  for (int s = 0; s < sub; ++s)
+#pragma unroll
+    for (int e = 0; e < VW; ++e) run0[e] += gsum[wv - sub + s][cp * VW + e];
+  if (!live) return;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    float qv[VW], kq[VW], run[VW];
+    unpack_piece<T>(rq[i], qv);
+    unpack_piece<T>(rz[i], kq);
+    float a = 0.f, bq = 0.f;
+#pragma unroll
+    for (int e = 0; e < VW; ++e) {
+      run[e] = run0[e] + base[i][e] + kc[i][e];
+      a += run[e] * qv[e];
+      bq += wx[e] * qv[e];
+    }
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) {
+      a += __shfl_xor(a, m, 64);
+      bq += __shfl_xor(bq, m, 64);
+    }
+    const float inv = 1.f / (float)(t0 + i * RL + rlc + 1);
+    const float mq = a * inv, gamma = 1.f / (1.f + __expf(-(bq + bias)));
+    float out[VW];
+#pragma unroll
+    for (int e = 0; e < VW; ++e) out[e] = qv[e] - gamma * inv * (kq[e] - run[e] * mq);
+    if (lane_in)
+      *reinterpret_cast<u32x4*>(q_clean + (row0 + (int64_t)(i * RL + rl) * H) * D + cp * VW) = pack_piece<T>(out);
   }
 }
 
