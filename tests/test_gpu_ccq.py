@@ -26,6 +26,8 @@ SHAPES = [
     ("bf16", 2, 4, 2048, 64),
     ("bf16", 1, 2, 96, 32),    # chunks of 32
     ("bf16", 1, 2, 1024, 128),
+    ("f32", 1, 2, 256, 128),   # four 16-byte loads a tensor, two rows each
+    ("bf16", 2, 3, 128, 16),   # two lanes a row: a quarter of the lanes hold rows
 ]
 
 
