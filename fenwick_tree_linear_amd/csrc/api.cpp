@@ -829,14 +829,15 @@ ll_status ll_ccq_query(int B, int T, int H, int dk, ll_dtype io, const void* q, 
   void* kkq = ws + c.kkq_off;
   float* csum = reinterpret_cast<float*>(ws + c.csum_off);
   const int code = io == LL_BF16 ? 1 : 0;
-  hipError_t e = timed(K_CCQ, stream, [&] { return llattn::launch_ccq_fill((int64_t)B * T * H, c.p.L, ones, zeros, stream); });
+  // the prefill's inputs, and sum_{j<=t} k_j as chunk sums with their prefix over the chunks (the
+  // rest in the combine)
+  hipError_t e = timed(K_CCQ, stream, [&] {
+    return llattn::launch_ccq_prepare(code, dk, B, T, H, c.p.C, k, csum, (int64_t)B * T * H, c.p.L, ones, zeros, stream);
+  });
   if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   // sum_{j<=t} (k_j . q_t) k_j
   st = run_prefill(&c.p, 0, nullptr, q, k, k, zeros, ones, nullptr, kkq, nullptr, ws + c.fwd_off, c.fwd_bytes, stream);
   if (st != LL_OK) return st;
-  // sum_{j<=t} k_j: chunk sums and their prefix over the chunks, the rest in the combine
-  e = timed(K_CCQ, stream, [&] { return llattn::launch_ccq_ksum(code, dk, B, T, H, c.p.C, k, csum, stream); });
-  if (e != hipSuccess) return fail(LL_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   e = timed(K_CCQ, stream, [&] {
     return llattn::launch_ccq_combine(code, dk, B, T, H, c.p.C, q, k, kkq, csum, w, b, q_clean, stream);
   });

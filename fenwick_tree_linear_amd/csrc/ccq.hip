@@ -9,7 +9,8 @@
 // (the Fenwick buckets then add up to the plain prefix sum):
 //   sum_{j<=t} (k_j . q_t) k_j   = prefill(q, k, v = k),
 // and the running key sum from a chunked prefix sum in fp32: per-chunk column
-// sums (ll_ccq_chunk_sum), their exclusive scan over the chunks of a head
+// sums (ccq_chunk_sum, in ll_ccq_prepare beside the fill of the prefill's
+// inputs), their exclusive scan over the chunks of a head
 // (ll_ccq_chunk_scan), and within the chunk the key sums of its earlier groups
 // of 8 tokens plus a running sum over the group's own (ll_ccq_combine, one
 // wave per group).
@@ -52,12 +53,12 @@ __device__ __forceinline__ u32x4 pack_piece(const float (&f)[16 / sizeof(T)]) {
   return v;
 }
 
-// Fills the inputs of the prefill: level weights 1 and log-gates 0.  VEC: the
-// buffers start on 16 bytes and take 4 values per store.
+// Fills the inputs of the prefill: level weights 1 and log-gates 0, thread
+// i0 of a grid of `stride` threads.  VEC: the buffers start on 16 bytes and
+// take 4 values per store.
 template <bool VEC>
-__global__ void __launch_bounds__(256) ll_ccq_fill(int64_t n_ones, int64_t n_zeros, float* ones, float* zeros) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+__device__ __forceinline__ void ccq_fill(int64_t i0, int64_t stride, int64_t n_ones, int64_t n_zeros, float* ones,
+                                         float* zeros) {
   if (VEC) {
     const float4 one4 = make_float4(1.f, 1.f, 1.f, 1.f), zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int64_t i = i0; i < n_ones / 4; i += stride) reinterpret_cast<float4*>(ones)[i] = one4;
@@ -70,16 +71,16 @@ __global__ void __launch_bounds__(256) ll_ccq_fill(int64_t n_ones, int64_t n_zer
   }
 }
 
-// One wave per (b, h, chunk of CS tokens, CS a multiple of 16): the chunk's
-// column sums of k, csum[b][h][c][x] (fp32), 16 rows loaded per round.  Waves
-// go along the heads first (the rows in flight then cover every head).
+// Wave `item` of the chunk sums, one per (b, h, chunk of CS tokens, CS a
+// multiple of 16): the chunk's column sums of k, csum[b][h][c][x] (fp32), 16
+// rows loaded per round.  Items go along the heads first (the rows in flight
+// then cover every head).
 template <typename T, int D>
-__global__ void __launch_bounds__(256) ll_ccq_chunk_sum(int B, int T_, int H, int CS, const T* __restrict__ k,
-                                                        float* __restrict__ csum) {
+__device__ __forceinline__ void ccq_chunk_sum(int64_t item, int B, int T_, int H, int CS, const T* __restrict__ k,
+                                              float* __restrict__ csum) {
   constexpr int E = (D + 63) / 64;
   const int lane = threadIdx.x & 63;
   const int nch = T_ / CS;
-  const int64_t item = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   if (item >= (int64_t)B * H * nch) return;
   const int h = (int)(item % H);
   const int64_t bc = item / H;
@@ -108,6 +109,21 @@ __global__ void __launch_bounds__(256) ll_ccq_chunk_sum(int B, int T_, int H, in
   for (int e = 0; e < E; ++e) {
     const int x = lane * E + e;
     if (x < D) csum[out * D + x] = acc[e];
+  }
+}
+
+// The first sum_blocks workgroups take the chunk sums (four waves each), the
+// others the fill: the two are independent, and one launch lets the fill's
+// stores and the sums' loads overlap.
+template <typename T, int D, bool VEC>
+__global__ void __launch_bounds__(256) ll_ccq_prepare(int B, int T_, int H, int CS, const T* __restrict__ k,
+                                                      float* __restrict__ csum, int sum_blocks, int64_t n_ones,
+                                                      int64_t n_zeros, float* ones, float* zeros) {
+  if ((int)blockIdx.x < sum_blocks) {
+    ccq_chunk_sum<T, D>((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), B, T_, H, CS, k, csum);
+  } else {
+    ccq_fill<VEC>((int64_t)(blockIdx.x - sum_blocks) * blockDim.x + threadIdx.x,
+                  (int64_t)(gridDim.x - sum_blocks) * blockDim.x, n_ones, n_zeros, ones, zeros);
   }
 }
 
@@ -278,21 +294,19 @@ __global__ void __launch_bounds__(64 * kCombineNW) ll_ccq_combine(int B, int T_,
   }
 }
 
-hipError_t launch_ccq_fill(int64_t rows, int L, float* ones, float* zeros, hipStream_t s) {
-  const int64_t n = rows * L;
-  const int grid = (int)((n / 4 + 255) / 256 < 8192 ? (n / 4 + 255) / 256 + 1 : 8192);
-  if ((reinterpret_cast<uintptr_t>(ones) | reinterpret_cast<uintptr_t>(zeros)) % 16 == 0)
-    hipLaunchKernelGGL(ll_ccq_fill<true>, dim3(grid), dim3(256), 0, s, n, rows, ones, zeros);
-  else
-    hipLaunchKernelGGL(ll_ccq_fill<false>, dim3(grid), dim3(256), 0, s, n, rows, ones, zeros);
-  return hipGetLastError();
-}
-
 template <typename T, int D>
-static hipError_t launch_ksum_t(int B, int T_, int H, int CS, const void* k, float* csum, hipStream_t s) {
-  const int64_t items = (int64_t)B * H * (T_ / CS);
-  hipLaunchKernelGGL((ll_ccq_chunk_sum<T, D>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, B, T_, H, CS,
-                     static_cast<const T*>(k), csum);
+static hipError_t launch_prepare_t(int B, int T_, int H, int CS, const void* k, float* csum, int64_t rows, int L,
+                                   float* ones, float* zeros, hipStream_t s) {
+  const int64_t items = (int64_t)B * H * (T_ / CS), n = rows * L;
+  const int64_t sum_blocks = (items + 3) / 4, fill_blocks = (n / 4 + 255) / 256 < 8192 ? (n / 4 + 255) / 256 + 1 : 8192;
+  if (sum_blocks + fill_blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(sum_blocks + fill_blocks));
+  if ((reinterpret_cast<uintptr_t>(ones) | reinterpret_cast<uintptr_t>(zeros)) % 16 == 0)
+    hipLaunchKernelGGL((ll_ccq_prepare<T, D, true>), grid, dim3(256), 0, s, B, T_, H, CS, static_cast<const T*>(k),
+                       csum, (int)sum_blocks, n, rows, ones, zeros);
+  else
+    hipLaunchKernelGGL((ll_ccq_prepare<T, D, false>), grid, dim3(256), 0, s, B, T_, H, CS, static_cast<const T*>(k),
+                       csum, (int)sum_blocks, n, rows, ones, zeros);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL(ll_ccq_chunk_scan<D>, dim3((unsigned)(B * H)), dim3(1024), 0, s, T_ / CS, csum);
   return hipGetLastError();
@@ -327,8 +341,9 @@ static hipError_t launch_combine_t(int B, int T_, int H, int CS, const void* q, 
   }                                                               \
   return hipErrorInvalidValue;
 
-hipError_t launch_ccq_ksum(int io, int D, int B, int T_, int H, int CS, const void* k, float* csum, hipStream_t s) {
-  LL_CCQ_DISPATCH(launch_ksum_t, B, T_, H, CS, k, csum, s)
+hipError_t launch_ccq_prepare(int io, int D, int B, int T_, int H, int CS, const void* k, float* csum, int64_t rows,
+                              int L, float* ones, float* zeros, hipStream_t s) {
+  LL_CCQ_DISPATCH(launch_prepare_t, B, T_, H, CS, k, csum, rows, L, ones, zeros, s)
 }
 
 hipError_t launch_ccq_combine(int io, int D, int B, int T_, int H, int CS, const void* q, const void* k,

@@ -128,8 +128,10 @@ hipError_t launch_prior_read(int io, int D, int C, const PrefillArgs& a, hipStre
 // 3 the gate's sum over later blocks
 hipError_t launch_bwd_native(int io, int D, int C, const BwdArgs& a, const BwdFwdNodes& n, const BwdWork& w, int pass,
                              hipStream_t s);
-hipError_t launch_ccq_fill(int64_t rows, int L, float* ones, float* zeros, hipStream_t s);
-hipError_t launch_ccq_ksum(int io, int D, int B, int T, int H, int CS, const void* k, float* csum, hipStream_t s);
+// the prefill's level weights (1) and log-gates (0) for rows x L, and the
+// exclusive per-chunk key sums of each head in csum
+hipError_t launch_ccq_prepare(int io, int D, int B, int T, int H, int CS, const void* k, float* csum, int64_t rows,
+                              int L, float* ones, float* zeros, hipStream_t s);
 hipError_t launch_ccq_combine(int io, int D, int B, int T, int H, int CS, const void* q, const void* k,
                               const void* kkq, const float* csum, const float* w, const float* b, void* qc,
                               hipStream_t s);
