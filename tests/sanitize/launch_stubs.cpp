@@ -15,8 +15,8 @@ hipError_t launch_prior_read(int, int, int, const PrefillArgs&, hipStream_t) { S
 hipError_t launch_bwd_native(int, int, int, const BwdArgs&, const BwdFwdNodes&, const BwdWork&, int, hipStream_t) {
   STUB;
 }
-hipError_t launch_ccq_fill(int64_t, int, float*, float*, hipStream_t) { STUB; }
-hipError_t launch_ccq_ksum(int, int, int, int, int, int, const void*, float*, hipStream_t) { STUB; }
+hipError_t launch_ccq_prepare(int, int, int, int, int, int, const void*, float*, int64_t, int, float*, float*,
+                              hipStream_t) { STUB; }
 hipError_t launch_ccq_combine(int, int, int, int, int, int, const void*, const void*, const void*, const float*,
                               const float*, const float*, void*, hipStream_t) { STUB; }
 hipError_t launch_decode_step(int, int, int, const DecodeArgs&, hipStream_t) { STUB; }
